@@ -1,0 +1,197 @@
+// C ABI of libattnbwd.so (declared in include/attn_bwd.h): argument
+// validation, translation to the kernels' parameter block, and dispatch.
+//
+// Validation happens before any HIP call; a call that fails validation has
+// no effect on the device.
+#include <hip/hip_runtime.h>
+#include <math.h>
+#include <stdint.h>
+
+#include "../../include/attn_bwd.h"
+#include "kernels.h"
+
+using attn::Params;
+
+namespace {
+
+constexpr int kMaxHeadDim = 256;
+
+bool strides_ok(const int64_t* s) { return s[0] >= 0 && s[1] >= 0 && s[2] >= 0; }
+
+// Shape / mask checks shared by the forward and the backward.
+attn_status_t check_problem(const attn_problem_t* p) {
+  if (!p) return ATTN_EINVAL;
+  if (p->B < 0 || p->Hq <= 0 || p->Hk <= 0 || p->Sq < 0 || p->Sk < 0) return ATTN_EINVAL;
+  if (p->Hq % p->Hk != 0) return ATTN_EINVAL;
+  if (p->Dqk <= 0 || p->Dv <= 0 || p->Dqk > kMaxHeadDim || p->Dv > kMaxHeadDim) return ATTN_EINVAL;
+  if (!(p->scale > 0.f) || !isfinite(p->scale)) return ATTN_EINVAL;
+  if (p->in_dtype != ATTN_F32 && p->in_dtype != ATTN_BF16) return ATTN_EINVAL;
+  if (p->o_dtype != ATTN_F32 && p->o_dtype != ATTN_BF16) return ATTN_EINVAL;
+  if (p->mask != ATTN_MASK_NONE && p->mask != ATTN_MASK_TOP_LEFT && p->mask != ATTN_MASK_BOTTOM_RIGHT)
+    return ATTN_EINVAL;
+  if (p->window_left < -1 || p->window_right < 0 || p->num_sink_tokens < 0) return ATTN_EINVAL;
+  if (p->mask == ATTN_MASK_NONE && (p->window_left != -1 || p->window_right != 0 || p->num_sink_tokens != 0))
+    return ATTN_EINVAL;
+  if (p->q_offset < 0 || p->k_offset < 0 || p->sq_total < 0 || p->sk_total < 0) return ATTN_EINVAL;
+  const int64_t sq_t = p->sq_total ? p->sq_total : p->Sq;
+  const int64_t sk_t = p->sk_total ? p->sk_total : p->Sk;
+  if (p->q_offset + p->Sq > sq_t || p->k_offset + p->Sk > sk_t) return ATTN_EINVAL;
+  return ATTN_OK;
+}
+
+Params make_params(const attn_problem_t* p) {
+  Params k{};
+  k.B = p->B; k.Hq = p->Hq; k.Hk = p->Hk; k.G = p->Hq / p->Hk;
+  k.Sq = p->Sq; k.Sk = p->Sk; k.Dqk = p->Dqk; k.Dv = p->Dv;
+  k.scale = p->scale;
+  const int64_t sq_t = p->sq_total ? p->sq_total : p->Sq;
+  const int64_t sk_t = p->sk_total ? p->sk_total : p->Sk;
+  k.mask.kind = p->mask;
+  k.mask.wl = p->window_left;
+  k.mask.wr = p->window_right;
+  k.mask.n_sink = p->num_sink_tokens;
+  k.mask.q_off = p->q_offset;
+  k.mask.k_off = p->k_offset;
+  k.mask.diag = (p->mask == ATTN_MASK_BOTTOM_RIGHT) ? (sk_t - sq_t) : 0;
+  for (int i = 0; i < 3; ++i) {
+    k.q_str[i] = p->q_str[i]; k.k_str[i] = p->k_str[i]; k.v_str[i] = p->v_str[i];
+    k.o_str[i] = p->o_str[i]; k.do_str[i] = p->do_str[i]; k.dq_str[i] = p->dq_str[i];
+    k.dk_str[i] = p->dk_str[i]; k.dv_str[i] = p->dv_str[i];
+  }
+  k.bias_str[0] = p->bias_str[0];
+  k.bias_str[1] = p->bias_str[1];
+  return k;
+}
+
+attn_status_t hip_status(hipError_t e) { return e == hipSuccess ? ATTN_OK : ATTN_EHIP; }
+
+}  // namespace
+
+extern "C" {
+
+void attn_problem_init(attn_problem_t* p, int32_t B, int32_t Hq, int32_t Hk, int32_t Sq, int32_t Sk,
+                       int32_t Dqk, int32_t Dv) {
+  if (!p) return;
+  *p = attn_problem_t{};
+  p->B = B; p->Hq = Hq; p->Hk = Hk; p->Sq = Sq; p->Sk = Sk; p->Dqk = Dqk; p->Dv = Dv;
+  p->scale = Dqk > 0 ? 1.0f / sqrtf((float)Dqk) : 0.f;
+  p->in_dtype = ATTN_BF16;
+  p->o_dtype = ATTN_F32;
+  p->mask = ATTN_MASK_NONE;
+  p->window_left = -1;
+  p->window_right = 0;
+  p->num_sink_tokens = 0;
+  auto fill = [](int64_t* s, int64_t H, int64_t S, int64_t D) { s[0] = H * S * D; s[1] = S * D; s[2] = D; };
+  fill(p->q_str, Hq, Sq, Dqk);
+  fill(p->o_str, Hq, Sq, Dv);
+  fill(p->do_str, Hq, Sq, Dv);
+  fill(p->dq_str, Hq, Sq, Dqk);
+  fill(p->k_str, Hk, Sk, Dqk);
+  fill(p->dk_str, Hk, Sk, Dqk);
+  fill(p->v_str, Hk, Sk, Dv);
+  fill(p->dv_str, Hk, Sk, Dv);
+  p->bias_str[0] = (int64_t)Sq * Sk;
+  p->bias_str[1] = Sk;
+}
+
+const char* attn_status_string(attn_status_t s) {
+  switch (s) {
+    case ATTN_OK: return "ok";
+    case ATTN_EINVAL: return "invalid argument";
+    case ATTN_EUNSUPPORTED: return "unsupported problem";
+    case ATTN_EHIP: return "HIP runtime error";
+  }
+  return "unknown status";
+}
+
+attn_status_t attn_fwd_lse(const attn_problem_t* p, const void* q, const void* k, const void* v,
+                           const float* bias, const float* sinks, void* o, float* lse, void* stream) {
+  attn_status_t st = check_problem(p);
+  if (st != ATTN_OK) return st;
+  if (!strides_ok(p->q_str) || !strides_ok(p->k_str) || !strides_ok(p->v_str) || !strides_ok(p->o_str))
+    return ATTN_EINVAL;
+  const bool empty = p->B == 0 || p->Sq == 0;
+  if (!empty && (!q || !o || !lse)) return ATTN_EINVAL;
+  if (!empty && p->Sk > 0 && (!k || !v)) return ATTN_EINVAL;
+  if (bias && (p->bias_str[0] < 0 || p->bias_str[1] < 0)) return ATTN_EINVAL;
+  if (p->Dqk > attn::kSimtMaxD || p->Dv > attn::kSimtMaxD) return ATTN_EUNSUPPORTED;
+  if (empty) return ATTN_OK;
+  Params kp = make_params(p);
+  attn::FwdArgs a{q, k, v, bias, sinks, o, lse};
+  return hip_status(attn::launch_fwd_simt(kp, a, p->in_dtype == ATTN_BF16, p->o_dtype == ATTN_BF16,
+                                          (hipStream_t)stream));
+}
+
+attn_status_t attn_bwd_preprocess(const attn_problem_t* p, const void* o, const void* dout,
+                                  const float* lse, const float* sinks, float* delta, float* dsinks,
+                                  float* dq_zero, void* stream) {
+  attn_status_t st = check_problem(p);
+  if (st != ATTN_OK) return st;
+  if (!strides_ok(p->o_str) || !strides_ok(p->do_str)) return ATTN_EINVAL;
+  if (dq_zero && !strides_ok(p->dq_str)) return ATTN_EINVAL;
+  if ((sinks == nullptr) != (dsinks == nullptr)) return ATTN_EINVAL;
+  const bool empty = p->B == 0 || p->Sq == 0;
+  if (!empty && (!o || !dout || !delta)) return ATTN_EINVAL;
+  if (sinks && !empty && !lse) return ATTN_EINVAL;
+  hipStream_t s = (hipStream_t)stream;
+  if (!empty) {
+    hipError_t e = attn::launch_delta(o, p->o_dtype == ATTN_BF16, dout, p->in_dtype == ATTN_BF16, delta,
+                                      p->B, p->Hq, p->Sq, p->Dv, p->o_str, p->do_str, dq_zero, p->Dqk,
+                                      p->dq_str, s);
+    if (e != hipSuccess) return ATTN_EHIP;
+  }
+  if (sinks) return hip_status(attn::launch_dsinks(lse, delta, sinks, dsinks, p->B, p->Hq, p->Sq, s));
+  return ATTN_OK;
+}
+
+attn_status_t attn_bwd(const attn_problem_t* p, const void* q, const void* k, const void* v,
+                       const void* dout, const float* lse, const float* delta, const float* bias,
+                       float* dq, float* dk, float* dv, float* dbias, uint32_t flags, void* stream) {
+  attn_status_t st = check_problem(p);
+  if (st != ATTN_OK) return st;
+  if ((flags & ~(uint32_t)(ATTN_DETERMINISTIC | ATTN_ACCUMULATE_DQ)) != 0) return ATTN_EINVAL;
+  if (!strides_ok(p->q_str) || !strides_ok(p->k_str) || !strides_ok(p->v_str) || !strides_ok(p->do_str) ||
+      !strides_ok(p->dq_str) || !strides_ok(p->dk_str) || !strides_ok(p->dv_str))
+    return ATTN_EINVAL;
+  if (dbias && !bias) return ATTN_EINVAL;
+  if (bias && (p->bias_str[0] < 0 || p->bias_str[1] < 0)) return ATTN_EINVAL;
+  const bool no_rows = p->B == 0 || p->Sq == 0;
+  const bool no_keys = p->B == 0 || p->Sk == 0;
+  if (!no_rows && (!q || !dout || !lse || !delta || !dq)) return ATTN_EINVAL;
+  if (!no_keys && (!k || !v || !dk || !dv)) return ATTN_EINVAL;
+  if (p->in_dtype == ATTN_F32 && (p->Dqk > attn::kSimtMaxD || p->Dv > attn::kSimtMaxD))
+    return ATTN_EUNSUPPORTED;
+
+  Params kp = make_params(p);
+  attn::BwdArgs a{q, k, v, dout, lse, delta, bias, dq, dk, dv, dbias,
+                  (flags & ATTN_ACCUMULATE_DQ) ? 1 : 0, (flags & ATTN_DETERMINISTIC) ? 1 : 0};
+  hipStream_t s = (hipStream_t)stream;
+  if (p->in_dtype == ATTN_BF16) {
+    if (!attn::mfma_bwd_supported(kp)) {
+      if (p->Dqk > attn::kSimtMaxD || p->Dv > attn::kSimtMaxD) return ATTN_EUNSUPPORTED;
+    }
+  }
+  if (no_rows && no_keys) return ATTN_OK;
+  if (dbias && !no_rows && p->Sk > 0) {
+    if (attn::launch_zero_bias(dbias, p->Hq, p->Sq, p->Sk, p->bias_str, s) != hipSuccess) return ATTN_EHIP;
+  }
+  if (p->in_dtype == ATTN_BF16 && attn::mfma_bwd_supported(kp))
+    return hip_status(attn::launch_bwd_mfma(kp, a, s));
+  // fp32 inputs (and bf16 shapes the matrix-core kernels do not cover)
+  if (no_keys) {  // no keys: dK/dV are empty, dQ gets nothing added
+    if (!a.accumulate_dq) return hip_status(attn::launch_zero_rows(dq, p->B, p->Hq, p->Sq, p->Dqk, p->dq_str, s));
+    return ATTN_OK;
+  }
+  return hip_status(attn::launch_bwd_simt(kp, a, p->in_dtype == ATTN_BF16, s));
+}
+
+attn_status_t attn_lse_merge(int32_t B, int32_t H, int32_t Sq, int32_t Dv, float* o_acc, float* lse_acc,
+                             const float* o_part, const float* lse_part, void* stream) {
+  if (B < 0 || H < 0 || Sq < 0 || Dv <= 0) return ATTN_EINVAL;
+  const int64_t rows = (int64_t)B * H * Sq;
+  if (rows == 0) return ATTN_OK;
+  if (!o_acc || !lse_acc || !o_part || !lse_part) return ATTN_EINVAL;
+  return hip_status(attn::launch_lse_merge(rows, Dv, o_acc, lse_acc, o_part, lse_part, (hipStream_t)stream));
+}
+
+}  // extern "C"

@@ -1,0 +1,57 @@
+// Host-side launch entry points of the attention kernels (internal to the
+// library; the public ABI is include/attn_bwd.h).
+#pragma once
+
+#include "common.h"
+
+namespace attn {
+
+// Extra device pointers handed to the forward / backward kernels.
+struct FwdArgs {
+  const void* q;
+  const void* k;
+  const void* v;
+  const float* bias;   // nullable [Hq, Sq, Sk]
+  const float* sinks;  // nullable [Hq]
+  void* o;
+  float* lse;
+};
+
+struct BwdArgs {
+  const void* q;
+  const void* k;
+  const void* v;
+  const void* dout;
+  const float* lse;
+  const float* delta;
+  const float* bias;  // nullable
+  float* dq;
+  float* dk;
+  float* dv;
+  float* dbias;       // nullable
+  int accumulate_dq;  // add into dq instead of overwriting
+  int deterministic;
+};
+
+// delta = rowsum(dO * O); when dq_zero is non-null its rows are zeroed in the same pass.
+hipError_t launch_delta(const void* o, int o_bf16, const void* dout, int do_bf16, float* delta, int B,
+                        int H, int Sq, int Dv, const int64_t* os, const int64_t* ds, float* dq_zero,
+                        int Dqk, const int64_t* dqs, hipStream_t st);
+hipError_t launch_dsinks(const float* lse, const float* delta, const float* sinks, float* dsinks,
+                         int B, int H, int Sq, hipStream_t st);
+hipError_t launch_zero_rows(float* x, int B, int H, int S, int D, const int64_t* str, hipStream_t st);
+hipError_t launch_zero_bias(float* x, int H, int Sq, int Sk, const int64_t* str, hipStream_t st);
+hipError_t launch_lse_merge(int64_t rows, int Dv, float* o_acc, float* lse_acc, const float* o_part,
+                            const float* lse_part, hipStream_t st);
+
+// Plain fp32-arithmetic (no matrix cores) kernels: every dtype, head dims up
+// to kSimtMaxD.  The fp32 path, and the forward for every dtype.
+constexpr int kSimtMaxD = 128;
+hipError_t launch_fwd_simt(const Params& p, const FwdArgs& a, int in_bf16, int o_bf16, hipStream_t st);
+hipError_t launch_bwd_simt(const Params& p, const BwdArgs& a, int in_bf16, hipStream_t st);
+
+// bf16 matrix-core backward (gfx950 MFMA), head dims 64 and 128.
+bool mfma_bwd_supported(const Params& p);
+hipError_t launch_bwd_mfma(const Params& p, const BwdArgs& a, hipStream_t st);
+
+}  // namespace attn

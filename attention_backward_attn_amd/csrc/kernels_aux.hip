@@ -1,0 +1,233 @@
+// Memory-bound helper kernels: the backward preprocess (delta = rowsum(dO*O)
+// and the sink-logit gradient), zero fills, and the log-sum-exp merge.
+#include "kernels.h"
+
+namespace attn {
+
+// ---------------------------------------------------------------------------
+// delta[b,h,i] = sum_d dO[b,h,i,d] * O[b,h,i,d]
+// (CK FMHA example 34 cpu_bwd_gqa "D"; CANN sparse_flash_mla_grad Phase 2
+// SoftmaxGrad(dO, O)).  Each row is read by a group of TPR lanes, each lane
+// holding 8 contiguous elements; the group reduces with cross-lane shuffles.
+// ---------------------------------------------------------------------------
+// When dq is non-null the same lanes also zero dQ's row (Dqk floats).
+template <typename OT, typename DT, int TPR>
+__global__ __launch_bounds__(256) void k_delta_vec(const OT* __restrict__ o,
+                                                   const DT* __restrict__ dout,
+                                                   float* __restrict__ delta, int B, int H, int Sq,
+                                                   int Dv, int64_t ob, int64_t oh, int64_t os,
+                                                   int64_t db, int64_t dh, int64_t ds,
+                                                   float* __restrict__ dq, int Dqk, int64_t qb,
+                                                   int64_t qh, int64_t qs) {
+  const int64_t rows = (int64_t)B * H * Sq;
+  const int lane_in_row = threadIdx.x % TPR;
+  const int64_t row = ((int64_t)blockIdx.x * 256 + threadIdx.x) / TPR;
+  float acc = 0.f;
+  if (row < rows) {
+    const int i = (int)(row % Sq);
+    const int h = (int)((row / Sq) % H);
+    const int b = (int)(row / ((int64_t)Sq * H));
+    const OT* orow = o + b * ob + h * oh + i * os;
+    const DT* drow = dout + b * db + h * dh + i * ds;
+    for (int d0 = lane_in_row * 8; d0 < Dv; d0 += TPR * 8) {
+#pragma unroll
+      for (int e = 0; e < 8; ++e) acc += load_elem(orow, d0 + e) * load_elem(drow, d0 + e);
+    }
+    if (dq) {
+      float* qrow = dq + b * qb + h * qh + i * qs;
+      for (int d = lane_in_row; d < Dqk; d += TPR) qrow[d] = 0.f;
+    }
+  }
+#pragma unroll
+  for (int off = TPR / 2; off > 0; off >>= 1) acc += __shfl_xor(acc, off, TPR);
+  if (row < rows && lane_in_row == 0) delta[row] = acc;
+}
+
+// Scalar fallback for Dv not a multiple of 8: one thread per row.
+template <typename OT, typename DT>
+__global__ __launch_bounds__(256) void k_delta_scalar(const OT* __restrict__ o,
+                                                      const DT* __restrict__ dout,
+                                                      float* __restrict__ delta, int B, int H,
+                                                      int Sq, int Dv, int64_t ob, int64_t oh,
+                                                      int64_t os, int64_t db, int64_t dh,
+                                                      int64_t ds, float* __restrict__ dq, int Dqk,
+                                                      int64_t qb, int64_t qh, int64_t qs) {
+  const int64_t row = (int64_t)blockIdx.x * 256 + threadIdx.x;
+  if (row >= (int64_t)B * H * Sq) return;
+  const int i = (int)(row % Sq);
+  const int h = (int)((row / Sq) % H);
+  const int b = (int)(row / ((int64_t)Sq * H));
+  float acc = 0.f;
+  for (int d = 0; d < Dv; ++d)
+    acc += load_elem(o + b * ob + h * oh + i * os, d) * load_elem(dout + b * db + h * dh + i * ds, d);
+  delta[row] = acc;
+  if (dq)
+    for (int d = 0; d < Dqk; ++d) dq[b * qb + h * qh + i * qs + d] = 0.f;
+}
+
+// dsinks[h] = -sum_{b,i} exp(sink_h - lse[b,h,i]) * delta[b,h,i]
+// (CANN sparse_flash_mla_grad Phase 3 dSinks reduced over rows and batch).
+// One block per head; fixed-order strided partial sums and a fixed tree, so
+// the result does not depend on scheduling.
+__global__ __launch_bounds__(256) void k_dsinks(const float* __restrict__ lse,
+                                                const float* __restrict__ delta,
+                                                const float* __restrict__ sinks,
+                                                float* __restrict__ dsinks, int B, int H, int Sq) {
+  __shared__ float red[256];
+  const int h = blockIdx.x;
+  const float s = sinks[h];
+  float acc = 0.f;
+  for (int b = 0; b < B; ++b) {
+    const float* l = lse + ((int64_t)b * H + h) * Sq;
+    const float* d = delta + ((int64_t)b * H + h) * Sq;
+    for (int i = threadIdx.x; i < Sq; i += 256) {
+      const float li = l[i];
+      if (li != -INFINITY) acc += expf(s - li) * d[i];
+    }
+  }
+  red[threadIdx.x] = acc;
+  __syncthreads();
+  for (int w = 128; w > 0; w >>= 1) {
+    if (threadIdx.x < w) red[threadIdx.x] += red[threadIdx.x + w];
+    __syncthreads();
+  }
+  if (threadIdx.x == 0) dsinks[h] = -red[0];
+}
+
+// Zero rows of a strided [B, H, S, D] fp32 tensor (D contiguous).
+__global__ __launch_bounds__(256) void k_zero_rows(float* __restrict__ x, int B, int H, int S, int D,
+                                                   int64_t sb, int64_t sh, int64_t ss) {
+  const int64_t n = (int64_t)B * H * S * D;
+  for (int64_t e = (int64_t)blockIdx.x * 256 + threadIdx.x; e < n; e += (int64_t)gridDim.x * 256) {
+    const int d = (int)(e % D);
+    const int64_t r = e / D;
+    const int i = (int)(r % S);
+    const int h = (int)((r / S) % H);
+    const int b = (int)(r / ((int64_t)S * H));
+    x[b * sb + h * sh + i * ss + d] = 0.f;
+  }
+}
+
+// Zero a strided [H, Sq, Sk] fp32 tensor (Sk contiguous).
+__global__ __launch_bounds__(256) void k_zero_bias(float* __restrict__ x, int H, int Sq, int Sk,
+                                                   int64_t sh, int64_t si) {
+  const int64_t n = (int64_t)H * Sq * Sk;
+  for (int64_t e = (int64_t)blockIdx.x * 256 + threadIdx.x; e < n; e += (int64_t)gridDim.x * 256) {
+    const int j = (int)(e % Sk);
+    const int64_t r = e / Sk;
+    x[(r / Sq) * sh + (r % Sq) * si + j] = 0.f;
+  }
+}
+
+// ---------------------------------------------------------------------------
+// In-place merge of a partial (o, lse) into an accumulator ("Ring attention
+// for PyTorch", _ring_fwd): lse = logaddexp(lse_a, lse_b),
+// o = o_a e^{lse_a - lse} + o_b e^{lse_b - lse}; both empty -> o = 0, lse = -inf.
+// One block per row; every lane reads both lse values before lane 0 writes.
+// ---------------------------------------------------------------------------
+__global__ __launch_bounds__(128) void k_lse_merge(float* __restrict__ o_acc,
+                                                   float* __restrict__ lse_acc,
+                                                   const float* __restrict__ o_part,
+                                                   const float* __restrict__ lse_part, int Dv) {
+  const int64_t row = blockIdx.x;
+  const float la = lse_acc[row], lb = lse_part[row];
+  const float mx = fmaxf(la, lb);
+  float wa = 0.f, wb = 0.f, l = -INFINITY;
+  if (mx != -INFINITY) {
+    const float ea = expf(la - mx), eb = expf(lb - mx);
+    const float sum = ea + eb;
+    l = mx + logf(sum);
+    wa = ea / sum;
+    wb = eb / sum;
+  }
+  float* oa = o_acc + row * Dv;
+  const float* ob = o_part + row * Dv;
+  for (int d = threadIdx.x; d < Dv; d += 128) {
+    const float a = (wa != 0.f) ? oa[d] * wa : 0.f;
+    const float b = (wb != 0.f) ? ob[d] * wb : 0.f;
+    oa[d] = a + b;
+  }
+  __syncthreads();
+  if (threadIdx.x == 0) lse_acc[row] = l;
+}
+
+// ---------------------------------------------------------------------------
+// Host-side launchers
+// ---------------------------------------------------------------------------
+template <typename OT, typename DT>
+static hipError_t launch_delta_t(const void* o, const void* dout, float* delta, int B, int H, int Sq,
+                                 int Dv, const int64_t* os, const int64_t* ds, float* dq, int Dqk,
+                                 const int64_t* qs, hipStream_t st) {
+  const int64_t rows = (int64_t)B * H * Sq;
+  if (Dv % 8 == 0) {
+    const int tpr = Dv >= 128 ? 16 : (Dv >= 64 ? 8 : (Dv >= 32 ? 4 : (Dv >= 16 ? 2 : 1)));
+    const int64_t blocks = (rows * tpr + 255) / 256;
+#define ATTN_DELTA_LAUNCH(T)                                                                     \
+  hipLaunchKernelGGL((k_delta_vec<OT, DT, T>), dim3((unsigned)blocks), dim3(256), 0, st,           \
+                     (const OT*)o, (const DT*)dout, delta, B, H, Sq, Dv, os[0], os[1], os[2],      \
+                     ds[0], ds[1], ds[2], dq, Dqk, qs[0], qs[1], qs[2])
+    switch (tpr) {
+      case 16: ATTN_DELTA_LAUNCH(16); break;
+      case 8: ATTN_DELTA_LAUNCH(8); break;
+      case 4: ATTN_DELTA_LAUNCH(4); break;
+      case 2: ATTN_DELTA_LAUNCH(2); break;
+      default: ATTN_DELTA_LAUNCH(1); break;
+    }
+#undef ATTN_DELTA_LAUNCH
+  } else {
+    hipLaunchKernelGGL((k_delta_scalar<OT, DT>), dim3((unsigned)((rows + 255) / 256)), dim3(256), 0,
+                       st, (const OT*)o, (const DT*)dout, delta, B, H, Sq, Dv, os[0], os[1], os[2],
+                       ds[0], ds[1], ds[2], dq, Dqk, qs[0], qs[1], qs[2]);
+  }
+  return hipGetLastError();
+}
+
+hipError_t launch_delta(const void* o, int o_bf16, const void* dout, int do_bf16, float* delta, int B,
+                        int H, int Sq, int Dv, const int64_t* os, const int64_t* ds, float* dq_zero,
+                        int Dqk, const int64_t* qs, hipStream_t st) {
+  if (o_bf16 && do_bf16)
+    return launch_delta_t<unsigned short, unsigned short>(o, dout, delta, B, H, Sq, Dv, os, ds, dq_zero,
+                                                          Dqk, qs, st);
+  if (o_bf16)
+    return launch_delta_t<unsigned short, float>(o, dout, delta, B, H, Sq, Dv, os, ds, dq_zero, Dqk, qs, st);
+  if (do_bf16)
+    return launch_delta_t<float, unsigned short>(o, dout, delta, B, H, Sq, Dv, os, ds, dq_zero, Dqk, qs, st);
+  return launch_delta_t<float, float>(o, dout, delta, B, H, Sq, Dv, os, ds, dq_zero, Dqk, qs, st);
+}
+
+hipError_t launch_dsinks(const float* lse, const float* delta, const float* sinks, float* dsinks,
+                         int B, int H, int Sq, hipStream_t st) {
+  hipLaunchKernelGGL(k_dsinks, dim3(H), dim3(256), 0, st, lse, delta, sinks, dsinks, B, H, Sq);
+  return hipGetLastError();
+}
+
+static unsigned fill_blocks(int64_t n) {
+  int64_t b = (n + 255) / 256;
+  return (unsigned)(b > 16384 ? 16384 : (b < 1 ? 1 : b));
+}
+
+hipError_t launch_zero_rows(float* x, int B, int H, int S, int D, const int64_t* str, hipStream_t st) {
+  const int64_t n = (int64_t)B * H * S * D;
+  if (n == 0) return hipSuccess;
+  hipLaunchKernelGGL(k_zero_rows, dim3(fill_blocks(n)), dim3(256), 0, st, x, B, H, S, D, str[0],
+                     str[1], str[2]);
+  return hipGetLastError();
+}
+
+hipError_t launch_zero_bias(float* x, int H, int Sq, int Sk, const int64_t* str, hipStream_t st) {
+  const int64_t n = (int64_t)H * Sq * Sk;
+  if (n == 0) return hipSuccess;
+  hipLaunchKernelGGL(k_zero_bias, dim3(fill_blocks(n)), dim3(256), 0, st, x, H, Sq, Sk, str[0],
+                     str[1]);
+  return hipGetLastError();
+}
+
+hipError_t launch_lse_merge(int64_t rows, int Dv, float* o_acc, float* lse_acc, const float* o_part,
+                            const float* lse_part, hipStream_t st) {
+  if (rows == 0) return hipSuccess;
+  hipLaunchKernelGGL(k_lse_merge, dim3((unsigned)rows), dim3(128), 0, st, o_acc, lse_acc, o_part,
+                     lse_part, Dv);
+  return hipGetLastError();
+}
+
+}  // namespace attn

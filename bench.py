@@ -1,0 +1,236 @@
+#!/usr/bin/env python3
+"""Attention-backward throughput on one MI355X.
+
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME]
+
+A step is one whole backward of the workload on inputs already resident in
+HBM: ``attn_bwd_preprocess`` (delta = rowsum(dO * O), dQ zeroed in the same
+pass) followed by ``attn_bwd`` (dK, dV, dQ).  O and LSE come from the
+library's own forward before the timed region.  Throughput counts
+2 * (3 * Dqk + 2 * Dv) FLOPs per allowed (query, key) pair per query head --
+the five contractions -- and nothing for masked pairs or recomputation.
+
+Rank 0 prints one JSON line.  It also carries
+  * ``roofline`` for the dominant kernel (the main backward pass, timed alone
+    with HIP events on the stream it runs on),
+  * ``cpu_baseline``: the fp64 CPU oracle timed on a bounded sample of the
+    same workload (a subset of the KV head groups),
+  * extra timings (deterministic mode, the 4-chunk K/V split with the lse
+    merge, the forward).
+"""
+
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+PEAK_BF16_TFLOPS = 2516.6   # MI355X dense bf16 MFMA: 256 CU x 4096 FLOP/clk x 2.4 GHz
+PEAK_F32_TFLOPS = 157.3     # MI355X fp32 vector
+HBM_GBS = 8000.0
+
+
+def parse():
+    ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--workload", default=None, help="workload name (default: the headline workload)")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-extras", action="store_true", help="skip deterministic / chunked / forward timings")
+    ap.add_argument("--cpu-groups", type=int, default=8, help="KV head groups in the CPU oracle sample")
+    return ap.parse_args()
+
+
+def traffic_record(kernel_key: str):
+    """HBM bytes per launch of the dominant kernel from the committed
+    rocprofv3 counter summary, if it was taken on the current kernel source."""
+    path = os.path.join(ROOT, "profiles", "traffic.json")
+    if not os.path.exists(path):
+        return None
+    try:
+        with open(path) as f:
+            rec = json.load(f).get(kernel_key)
+        from attention_backward_attn_amd.build import source_digest
+        if rec and rec.get("source_digest") == source_digest():
+            return rec.get("bytes_per_launch")
+    except Exception:
+        return None
+    return None
+
+
+def cpu_baseline(w, x, groups: int):
+    """Time the fp64 oracle backward on KV groups [0, groups) of batch 0."""
+    import numpy as np
+
+    import oracle
+    from attention_backward_attn_amd.mask import backward_flops
+    try:
+        from threadpoolctl import threadpool_info
+        threads = max([i.get("num_threads", 1) for i in threadpool_info() if i.get("user_api") == "blas"] or [1])
+    except Exception:
+        threads = os.cpu_count()
+    groups = max(1, min(groups, w.Hk))
+    heads = slice(0, groups * w.G)
+    spec = oracle.MaskSpec(w.mask, w.window_left, w.window_right, w.num_sink)
+    q, do = x["q"][:1, heads], x["do"][:1, heads]
+    k, v = x["k"][:1, :groups], x["v"][:1, :groups]
+    bias = None if x["bias"] is None else x["bias"][heads]
+    sinks = None if x["sinks"] is None else x["sinks"][heads]
+    o, lse = oracle.forward(q, k, v, w.scale, spec, bias, sinks, row_block=1024)
+    o, lse = o.astype(np.float32), lse.astype(np.float32)
+    t0 = time.perf_counter()
+    oracle.backward(q, k, v, o, do, lse, w.scale, spec, bias, sinks, row_block=1024)
+    dt = time.perf_counter() - t0
+    flops = backward_flops(w.with_(B=1, Hq=groups * w.G, Hk=groups))
+    return {"value": flops / dt / 1e12, "unit": "TFLOP/s", "cores": threads, "kind": "oracle",
+            "sample": f"fp64 oracle backward (no forward), batch 0, KV groups 0..{groups - 1} "
+                      f"({groups * w.G} of {w.Hq} query heads), {dt:.2f} s; host cpu_count={os.cpu_count()}",
+            "seconds": dt}
+
+
+def main():
+    args = parse()
+    if args.gpus != 1:
+        print(f"bench.py runs on exactly one GPU; --gpus {args.gpus} is not supported "
+              "(this build has no multi-GPU path)", file=sys.stderr)
+        sys.exit(2)
+    import numpy as np
+    import torch
+
+    from attention_backward_attn_amd import binding as ab
+    from attention_backward_attn_amd.inputs import HEADLINE, WORKLOADS, make_inputs
+    from attention_backward_attn_amd.mask import allowed_pairs, backward_flops
+
+    if not torch.cuda.is_available():
+        print("bench.py needs a GPU", file=sys.stderr)
+        sys.exit(1)
+    w = WORKLOADS[args.workload or HEADLINE]
+    dev = torch.device("cuda:0")
+    x = make_inputs(w)
+    dt = torch.bfloat16 if w.dtype == "bf16" else torch.float32
+
+    def todev(a, t):
+        return None if a is None else torch.from_numpy(np.ascontiguousarray(a)).to(dev, t)
+
+    q, k, v, do = (todev(x[n], dt) for n in ("q", "k", "v", "do"))
+    bias, sinks = todev(x["bias"], torch.float32), todev(x["sinks"], torch.float32)
+    mask_kw = dict(mask=w.mask, window_left=w.window_left, window_right=w.window_right,
+                   num_sink_tokens=w.num_sink)
+    stream = torch.cuda.current_stream()
+    o, lse = ab.forward(q, k, v, bias=bias, sinks=sinks, scale=w.scale, stream=stream, **mask_kw)
+    dq = torch.empty(q.shape, device=dev, dtype=torch.float32)
+    dk = torch.empty(k.shape, device=dev, dtype=torch.float32)
+    dv = torch.empty(v.shape, device=dev, dtype=torch.float32)
+    delta = torch.empty(lse.shape, device=dev, dtype=torch.float32)
+    dsinks = torch.empty(w.Hq, device=dev, dtype=torch.float32) if sinks is not None else None
+    dbias = torch.empty(bias.shape, device=dev, dtype=torch.float32) if bias is not None else None
+    p = ab.make_problem(q, k, v, o=o, do=do, dq=dq, dk=dk, dv=dv, bias=bias, scale=w.scale, **mask_kw)
+
+    def step(flags, ev=None):
+        if ev is not None:
+            ev[0].record(stream)
+        ab.attn_bwd_preprocess(p, o, do, lse, sinks, delta, dsinks, dq, stream)
+        if ev is not None:
+            ev[1].record(stream)
+        ab.attn_bwd(p, q, k, v, do, lse, delta, bias, dq, dk, dv, dbias, flags | ab.ATTN_ACCUMULATE_DQ, stream)
+        if ev is not None:
+            ev[2].record(stream)
+
+    def timed(flags, steps, warmup):
+        for _ in range(warmup):
+            step(flags)
+        torch.cuda.synchronize()
+        evs = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(steps)]
+        t0 = time.perf_counter()
+        for i in range(steps):
+            step(flags, evs[i])
+        torch.cuda.synchronize()
+        wall = (time.perf_counter() - t0) / steps
+        pre = [e[0].elapsed_time(e[1]) for e in evs]
+        main_k = [e[1].elapsed_time(e[2]) for e in evs]
+        span = evs[0][0].elapsed_time(evs[-1][2]) / steps
+        return wall * 1e3, span, float(np.mean(pre)), float(np.mean(main_k)), float(np.median(main_k))
+
+    flops = backward_flops(w)
+    pairs = allowed_pairs(w.Sq, w.Sk, w.mask, w.window_left, w.window_right, w.num_sink)
+    wall_ms, span_ms, pre_ms, main_ms, main_med = timed(0, args.steps, args.warmup)
+    ms_per_step = span_ms
+    value = flops / (ms_per_step * 1e-3) / 1e12
+    achieved = flops / (main_ms * 1e-3) / 1e12
+    kernel_key = f"bwd_main:{w.name}"
+    out = {
+        "metric": "attention-backward TFLOP/s + % bf16 MFMA peak (GQA 32:8, S=4096, D=128, causal)",
+        "value": round(value, 2),
+        "unit": "TFLOP/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_per_step, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16" if w.dtype == "bf16" else "f32",
+        "data": "synthetic (seeded N(0,1) inputs; O/LSE from the library forward)",
+        "config": {"workload": w.name, "B": w.B, "Hq": w.Hq, "Hk": w.Hk, "Sq": w.Sq, "Sk": w.Sk,
+                   "D": w.Dqk, "mask": w.mask, "window_left": w.window_left, "num_sink": w.num_sink,
+                   "bias": w.bias, "sinks": w.sinks, "allowed_pairs_per_head": pairs,
+                   "counted_flop": flops, "timed": "attn_bwd_preprocess + attn_bwd (atomic dQ)"},
+        "pct_peak": round(100.0 * value / PEAK_BF16_TFLOPS, 2),
+        "wall_ms_per_step": round(wall_ms, 4),
+        "preprocess_ms": round(pre_ms, 4),
+        "roofline": {"bound": "mfma", "achieved": round(achieved, 2), "peak": PEAK_BF16_TFLOPS,
+                     "unit": "TFLOP/s", "frac": round(achieved / PEAK_BF16_TFLOPS, 4),
+                     "traffic": traffic_record(kernel_key), "kernel": "attn_bwd main pass",
+                     "kernel_ms_mean": round(main_ms, 4), "kernel_ms_median": round(main_med, 4)},
+    }
+    if not args.no_extras:
+        _, span_d, _, main_d, _ = timed(ab.ATTN_DETERMINISTIC, max(3, args.steps // 2), 2)
+        out["deterministic"] = {"ms_per_step": round(span_d, 4),
+                                "tflops": round(flops / (span_d * 1e-3) / 1e12, 2)}
+        # forward (input producer), timed for context
+        torch.cuda.synchronize()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record(stream)
+        for _ in range(3):
+            ab.forward(q, k, v, bias=bias, sinks=sinks, scale=w.scale, stream=stream, **mask_kw)
+        e1.record(stream)
+        torch.cuda.synchronize()
+        fwd_ms = e0.elapsed_time(e1) / 3
+        out["forward"] = {"ms": round(fwd_ms, 4),
+                          "tflops": round(2 * (w.Dqk + w.Dv) * pairs * w.B * w.Hq / (fwd_ms * 1e-3) / 1e12, 2)}
+        if w.kv_chunks > 1 and bias is None and sinks is None:
+            n, c = w.kv_chunks, w.Sk // w.kv_chunks
+            probs = [ab.make_problem(q, k[:, :, i * c:(i + 1) * c], v[:, :, i * c:(i + 1) * c], o=o, do=do, dq=dq,
+                                     dk=dk[:, :, i * c:(i + 1) * c], dv=dv[:, :, i * c:(i + 1) * c], scale=w.scale,
+                                     k_offset=i * c, sk_total=w.Sk, **mask_kw) for i in range(n)]
+
+            def chunked():
+                ab.attn_bwd_preprocess(p, o, do, lse, None, delta, None, dq, stream)
+                for i in range(n):
+                    sl = slice(i * c, (i + 1) * c)
+                    ab.attn_bwd(probs[i], q, k[:, :, sl], v[:, :, sl], do, lse, delta, None, dq, dk[:, :, sl],
+                                dv[:, :, sl], None, ab.ATTN_ACCUMULATE_DQ, stream)
+            for _ in range(2):
+                chunked()
+            torch.cuda.synchronize()
+            e0.record(stream)
+            for _ in range(5):
+                chunked()
+            e1.record(stream)
+            torch.cuda.synchronize()
+            ch_ms = e0.elapsed_time(e1) / 5
+            out["chunked_kv4"] = {"ms_per_step": round(ch_ms, 4), "tflops": round(flops / (ch_ms * 1e-3) / 1e12, 2)}
+    if not args.no_cpu_baseline:
+        out["cpu_baseline"] = cpu_baseline(w, x, args.cpu_groups)
+    print(json.dumps(out), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -1,0 +1,173 @@
+/*
+ * attn_bwd.h -- C ABI of the MI355X (gfx950) fused attention backward library
+ * (libattnbwd.so).
+ *
+ * Sources, cited by page title and section:
+ *  [GQA-BWD] CK FMHA dispatcher example 34, "Backward Pass with GQA": the CPU
+ *            backward reference (module docstring, cpu_bwd_gqa) and the
+ *            FmhaProblem fields batch, nhead_q, nhead_k, seqlen_q, seqlen_k,
+ *            hdim_q, hdim_v, scale.
+ *  [DBIAS]   CK FMHA dispatcher example 28, "Backward Bias Gradient (dbias)
+ *            FMHA": elementwise bias [H, Sq, Sk] broadcast over batch, dbias
+ *            summed over batch (cpu_attention_bwd_dbias); bias/dbias feature
+ *            flags of the backward kernel family.
+ *  [SFMG]    CANN ops-transformer sparse_flash_mla_grad: "Formula" Phase 2/3
+ *            (P, dP, dS, dQ, dKV, dSinks), "Prototype" (q, dout, attn_out,
+ *            softmax_lse, sinks, softmax_scale, window left/right with -1 as
+ *            unbounded), "Constraints" (consistent dtypes), "Deterministic
+ *            Computation" (determinism is opt-in), bottom-right rule in
+ *            "Example".
+ *  [SINK]    CK FMHA dispatcher example 22, "Sink Token Attention FMHA":
+ *            causal, causal + sink-token and sliding-window + sink-token masks.
+ *  [RING]    "Ring attention for PyTorch" gist: the forward returns (out, lse);
+ *            partial (o, lse) pairs are merged with logaddexp (_ring_fwd);
+ *            per-chunk backward against the global o and lse (_ring_bwd);
+ *            caller-allocated dq/dk/dv.
+ *
+ * Conventions shared by every entry point:
+ *  - Tensor pointers are DEVICE pointers owned by the caller; the library
+ *    keeps no state between calls and never allocates device memory.
+ *  - Layout: Q, dO, O, dQ are [B, Hq, S_q, D]; K, V, dK, dV are
+ *    [B, Hk, S_k, D]; the last dimension is contiguous and the other three
+ *    are given as element strides {b, h, s}.  LSE and delta are contiguous
+ *    fp32 [B, Hq, S_q].  bias and dbias are fp32 [Hq, S_q, S_k] shared over
+ *    the batch, strides {h, i} with j contiguous.  sinks / dsinks are fp32
+ *    [Hq].  Gradients are written in fp32.
+ *  - Query head h reads KV head h / (Hq / Hk) ([GQA-BWD]: K/V repeated along
+ *    the head axis, dK/dV summed back over each group).
+ *  - LSE is in natural-log units and is -inf for a row with no allowed key
+ *    and no sink; such a row has O = 0 and zero gradients.
+ *  - Every call validates its arguments on the host first and returns
+ *    ATTN_EINVAL / ATTN_EUNSUPPORTED without touching the GPU; HIP launch
+ *    errors return ATTN_EHIP.  Nothing is printed, no exception crosses the
+ *    ABI.  Calls are ordered on the given stream (NULL = the default stream)
+ *    and never synchronise the device.
+ */
+#ifndef ATTN_BWD_H
+#define ATTN_BWD_H
+
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+  ATTN_OK = 0,
+  ATTN_EINVAL = -1,        /* inconsistent or out-of-range argument          */
+  ATTN_EUNSUPPORTED = -2,  /* valid problem outside what the kernels cover   */
+  ATTN_EHIP = -3           /* a HIP launch or runtime call failed            */
+} attn_status_t;
+
+typedef enum { ATTN_F32 = 0, ATTN_BF16 = 1 } attn_dtype_t;
+
+/* Mask kinds ([SINK] make_causal_mask; [SFMG] "Example" bottom-right rule).
+ * With global indices i' = q_offset + i, j' = k_offset + j and
+ * delta = 0 (TOP_LEFT) or sk_total - sq_total (BOTTOM_RIGHT), a pair is
+ * allowed when
+ *     i' + delta - window_left <= j' <= i' + delta + window_right
+ *     (no lower bound when window_left < 0)
+ *  or j' < num_sink_tokens  (sink tokens are visible to every row).
+ * Plain causal is window_left = -1, window_right = 0; a sliding window of
+ * width W ([SINK] make_sliding_window_sink_mask) is window_left = W - 1,
+ * window_right = 0.  ATTN_MASK_NONE allows every pair; it requires
+ * window_left = -1, window_right = 0 and num_sink_tokens = 0. */
+typedef enum {
+  ATTN_MASK_NONE = 0,
+  ATTN_MASK_TOP_LEFT = 1,
+  ATTN_MASK_BOTTOM_RIGHT = 2
+} attn_mask_t;
+
+/* attn_bwd flags.
+ * ATTN_DETERMINISTIC: dQ comes from a separate query-block-parallel pass
+ *   that accumulates in registers (no atomics); dbias is accumulated over
+ *   the batch in a fixed order.  Two calls give bitwise identical results.
+ *   Without it dQ (and dbias) are accumulated with fp32 atomics, whose
+ *   order -- and so the low bits -- may vary between calls.
+ * ATTN_ACCUMULATE_DQ: add into dQ instead of overwriting it (chunked /
+ *   ring use, [RING] _ring_bwd "dq += dqa"). */
+enum { ATTN_DETERMINISTIC = 1u, ATTN_ACCUMULATE_DQ = 2u };
+
+/* Problem description ([GQA-BWD] FmhaProblem; [SFMG] "Prototype"). */
+typedef struct attn_problem {
+  int32_t B, Hq, Hk;        /* batch, query heads, KV heads; Hq % Hk == 0        */
+  int32_t Sq, Sk;           /* local sequence lengths (this call's rows / keys)  */
+  int32_t Dqk, Dv;          /* head dims of Q/K and of V/O                       */
+  float scale;              /* softmax scale, applied to Q K^T before bias       */
+  int32_t in_dtype;         /* attn_dtype_t of Q, K, V and dO                    */
+  int32_t o_dtype;          /* attn_dtype_t of O                                 */
+  int32_t mask;             /* attn_mask_t                                       */
+  int32_t window_left;      /* -1 = unbounded                                    */
+  int32_t window_right;     /* >= 0                                              */
+  int32_t num_sink_tokens;  /* keys with global index below this always visible  */
+  int64_t q_offset;         /* global index of local query row 0                 */
+  int64_t k_offset;         /* global index of local key 0                       */
+  int64_t sq_total;         /* global query length for bottom-right (0 => Sq)    */
+  int64_t sk_total;         /* global key length for bottom-right (0 => Sk)      */
+  int64_t q_str[3], k_str[3], v_str[3], o_str[3], do_str[3];  /* {b, h, s}      */
+  int64_t dq_str[3], dk_str[3], dv_str[3];                    /* {b, h, s}      */
+  int64_t bias_str[2];      /* {h, i} of bias and dbias                          */
+} attn_problem_t;
+
+/* Fill *p with contiguous [B, H, S, D] strides and defaults: scale =
+ * 1/sqrt(Dqk), dtypes bf16 (inputs) / fp32 (O), no mask, no window, no
+ * sinks, zero offsets, bias strides {Sq*Sk, Sk}. */
+void attn_problem_init(attn_problem_t* p, int32_t B, int32_t Hq, int32_t Hk, int32_t Sq,
+                       int32_t Sk, int32_t Dqk, int32_t Dv);
+
+/* Forward with log-sum-exp ([RING] _flash_fwd returns (out, lse); [GQA-BWD]
+ * cpu_fwd_with_intermediates; [DBIAS] cpu_attention_fwd_bias; [SINK]
+ * cpu_attention_fwd_masked).  S = scale * Q K^T + bias (masked pairs
+ * excluded); the optional sink logit of each query head joins the softmax
+ * normaliser without a value row.  Writes O (o_dtype, strides o_str) and
+ * LSE (fp32 [B, Hq, Sq]).
+ *   bias:  nullable fp32 [Hq, Sq, Sk];  sinks: nullable fp32 [Hq]. */
+attn_status_t attn_fwd_lse(const attn_problem_t* p, const void* q, const void* k,
+                           const void* v, const float* bias, const float* sinks, void* o,
+                           float* lse, void* stream);
+
+/* Backward preprocess ([GQA-BWD] cpu_bwd_gqa: D = rowsum(dO * O); [SFMG]
+ * Phase 2 SoftmaxGrad(dO, O) and Phase 3 dSinks).
+ *   delta[b,h,i] = sum_d dO[b,h,i,d] * O[b,h,i,d]               (fp32 [B,Hq,Sq])
+ *   if sinks: dsinks[h] = -sum_{b,i} exp(sinks[h] - lse[b,h,i]) * delta[b,h,i]
+ * dsinks is required iff sinks is given; it is overwritten.
+ * dq_zero is nullable: when given, the fp32 dQ buffer (strides dq_str) is
+ * zeroed in the same pass, so that a following attn_bwd with
+ * ATTN_ACCUMULATE_DQ produces dQ without a separate fill. */
+attn_status_t attn_bwd_preprocess(const attn_problem_t* p, const void* o, const void* dout,
+                                  const float* lse, const float* sinks, float* delta,
+                                  float* dsinks, float* dq_zero, void* stream);
+
+/* Backward main pass ([GQA-BWD] module docstring and cpu_bwd_gqa; [DBIAS]
+ * cpu_attention_bwd_dbias; [SFMG] Phase 2 and 3):
+ *   P = exp(S - LSE) on allowed pairs, dP = dO V^T, dS = P * (dP - delta),
+ *   dQ = scale * dS K,  dK = scale * dS^T Q,  dV = P^T dO  (dK, dV summed over
+ *   each KV head's query group), dbias = sum over batch of dS.
+ * dq is overwritten (or added into with ATTN_ACCUMULATE_DQ); dk, dv and
+ * dbias are overwritten.  bias is nullable; dbias is nullable and requires
+ * bias.  delta must come from attn_bwd_preprocess on the same O / dO.
+ * For a K/V chunk pass the chunk's K/V views with k_offset / sk_total and
+ * the GLOBAL O, LSE and delta ([RING] _ring_bwd). */
+attn_status_t attn_bwd(const attn_problem_t* p, const void* q, const void* k, const void* v,
+                       const void* dout, const float* lse, const float* delta,
+                       const float* bias, float* dq, float* dk, float* dv, float* dbias,
+                       uint32_t flags, void* stream);
+
+/* In-place log-sum-exp merge of a partial result into an accumulator
+ * ([RING] _ring_fwd):  lse = logaddexp(lse_acc, lse_part),
+ *   o_acc = o_acc * exp(lse_acc - lse) + o_part * exp(lse_part - lse).
+ * Both o buffers are contiguous fp32 [B, H, Sq, Dv], both lse buffers
+ * contiguous fp32 [B, H, Sq].  Where both lse are -inf the result is o = 0,
+ * lse = -inf. */
+attn_status_t attn_lse_merge(int32_t B, int32_t H, int32_t Sq, int32_t Dv, float* o_acc,
+                             float* lse_acc, const float* o_part, const float* lse_part,
+                             void* stream);
+
+/* Static description of a status code. */
+const char* attn_status_string(attn_status_t s);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* ATTN_BWD_H */

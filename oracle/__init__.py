@@ -41,5 +41,6 @@ from .attention import (  # noqa: F401
     lse_merge,
     dq_rows,
     dkdv_keys,
+    ds_rows,
     allowed_pair_count,
 )

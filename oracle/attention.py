@@ -268,6 +268,26 @@ def dq_rows(q, k, v, o, do, lse, scale, spec, b, h, rows, bias=None):
     return scale * (ds @ k[b, g, cols])
 
 
+def ds_rows(q, k, v, o, do, lse, scale, spec, b, h, rows, bias=None):
+    """dS[b, h, rows, :] over every key (0 where masked), the unscaled
+    gradient of the logits; dbias rows are its sum over the batch."""
+    q, k, v, o, do, lse, bias = (_f64(x) for x in (q, k, v, o, do, lse, bias))
+    Sq, Sk = q.shape[2], k.shape[2]
+    G = q.shape[1] // k.shape[1]
+    g = h // G
+    rows = np.asarray(rows)
+    out = np.zeros((rows.size, Sk))
+    cols, s, m = _block_logits(q[b, h, rows], k[b, g], h, rows, scale, spec, Sq, Sk, bias)
+    if cols.size == 0:
+        return out
+    l_i = lse[b, h, rows]
+    live = np.isfinite(l_i)
+    p = np.where(m & live[:, None], np.exp(s - np.where(live, l_i, 0.0)[:, None]), 0.0)
+    d_i = (do[b, h, rows] * o[b, h, rows]).sum(axis=-1)
+    out[:, cols] = p * (do[b, h, rows] @ v[b, g, cols].T - d_i[:, None])
+    return out
+
+
 def dkdv_keys(q, k, v, o, do, lse, scale, spec, b, g, keys, bias=None):
     """(dK, dV)[b, g, keys] alone: every query row of every query head in
     KV head g's group against the chosen keys (same definition as

@@ -1,0 +1,136 @@
+"""CPU-side checks of the C ABI: the library loads, exports every entry point
+declared in include/*.h, and rejects invalid arguments on the host before any
+HIP call (no GPU is touched by these tests)."""
+import ctypes
+import glob
+import os
+import re
+
+import pytest
+
+from attention_backward_attn_amd import binding as B
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+
+
+def declared_functions():
+    names = set()
+    for h in glob.glob(os.path.join(ROOT, "include", "*.h")):
+        text = open(h).read()
+        text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+        for m in re.finditer(r"\b(attn_[a-z0-9_]+)\s*\(", text):
+            names.add(m.group(1))
+    return sorted(names)
+
+
+def test_header_declares_entry_points():
+    names = declared_functions()
+    for n in ("attn_fwd_lse", "attn_bwd_preprocess", "attn_bwd", "attn_lse_merge"):
+        assert n in names
+
+
+@pytest.mark.parametrize("name", declared_functions())
+def test_library_exports(name):
+    L = B.lib()
+    assert hasattr(L, name), name
+    assert name in B.EXPORTED
+
+
+def problem(**kw):
+    p = B.attn_problem_t()
+    B.lib().attn_problem_init(ctypes.byref(p), 1, 4, 2, 64, 64, 64, 64)
+    for k, v in kw.items():
+        setattr(p, k, v)
+    return p
+
+
+def test_problem_init_defaults():
+    p = problem()
+    assert abs(p.scale - 0.125) < 1e-7
+    assert tuple(p.q_str) == (4 * 64 * 64, 64 * 64, 64)
+    assert tuple(p.k_str) == (2 * 64 * 64, 64 * 64, 64)
+    assert p.window_left == -1 and p.window_right == 0 and p.mask == 0
+    assert tuple(p.bias_str) == (64 * 64, 64)
+
+
+FAKE = ctypes.c_void_p(0x1000)  # never dereferenced: validation fails first
+
+
+BAD = [
+    dict(Hk=3),                 # Hq % Hk != 0
+    dict(Dqk=0),
+    dict(Dv=300),
+    dict(scale=0.0),
+    dict(scale=float("nan")),
+    dict(in_dtype=7),
+    dict(mask=5),
+    dict(window_left=-2),
+    dict(window_right=-1),
+    dict(num_sink_tokens=-1),
+    dict(window_left=3),        # window with mask NONE
+    dict(num_sink_tokens=2),    # sinks with mask NONE
+    dict(mask=1, q_offset=10, sq_total=32),   # offset + Sq beyond the global length
+    dict(mask=2, k_offset=-1),
+]
+
+
+@pytest.mark.parametrize("kw", BAD)
+def test_bwd_rejects_invalid_problem(kw):
+    p = problem(**kw)
+    s = B.lib().attn_bwd(ctypes.byref(p), FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, None, FAKE, FAKE, FAKE,
+                         None, 0, None)
+    assert s == B.ATTN_EINVAL
+
+
+@pytest.mark.parametrize("kw", BAD)
+def test_fwd_rejects_invalid_problem(kw):
+    p = problem(**kw)
+    s = B.lib().attn_fwd_lse(ctypes.byref(p), FAKE, FAKE, FAKE, None, None, FAKE, FAKE, None)
+    assert s in (B.ATTN_EINVAL, B.ATTN_EUNSUPPORTED)
+
+
+def test_bwd_rejects_null_pointers_and_flags():
+    p = problem()
+    L = B.lib()
+    assert L.attn_bwd(ctypes.byref(p), None, FAKE, FAKE, FAKE, FAKE, FAKE, None, FAKE, FAKE, FAKE, None,
+                      0, None) == B.ATTN_EINVAL
+    assert L.attn_bwd(ctypes.byref(p), FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, None, FAKE, None, FAKE, None,
+                      0, None) == B.ATTN_EINVAL
+    # dbias without bias
+    assert L.attn_bwd(ctypes.byref(p), FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, None, FAKE, FAKE, FAKE, FAKE,
+                      0, None) == B.ATTN_EINVAL
+    # unknown flag bit
+    assert L.attn_bwd(ctypes.byref(p), FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, None, FAKE, FAKE, FAKE, None,
+                      8, None) == B.ATTN_EINVAL
+    assert L.attn_bwd(None, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, None, FAKE, FAKE, FAKE, None, 0,
+                      None) == B.ATTN_EINVAL
+
+
+def test_preprocess_sinks_pairing():
+    p = problem()
+    L = B.lib()
+    # sinks without dsinks and the reverse
+    assert L.attn_bwd_preprocess(ctypes.byref(p), FAKE, FAKE, FAKE, FAKE, FAKE, None, None, None) == B.ATTN_EINVAL
+    assert L.attn_bwd_preprocess(ctypes.byref(p), FAKE, FAKE, FAKE, None, FAKE, FAKE, None, None) == B.ATTN_EINVAL
+
+
+def test_fp32_large_head_dim_unsupported():
+    p = problem(in_dtype=B.ATTN_F32, Dqk=192, Dv=192)
+    s = B.lib().attn_bwd(ctypes.byref(p), FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, None, FAKE, FAKE, FAKE,
+                         None, 0, None)
+    assert s == B.ATTN_EUNSUPPORTED
+
+
+def test_merge_validation_and_empty():
+    L = B.lib()
+    assert L.attn_lse_merge(1, 1, 4, 0, FAKE, FAKE, FAKE, FAKE, None) == B.ATTN_EINVAL
+    assert L.attn_lse_merge(-1, 1, 4, 8, FAKE, FAKE, FAKE, FAKE, None) == B.ATTN_EINVAL
+    assert L.attn_lse_merge(1, 1, 4, 8, None, FAKE, FAKE, FAKE, None) == B.ATTN_EINVAL
+    # zero rows: nothing to do, no device access
+    assert L.attn_lse_merge(0, 4, 4, 8, None, None, None, None, None) == B.ATTN_OK
+
+
+def test_status_strings():
+    assert B.status_string(B.ATTN_OK) == "ok"
+    assert "invalid" in B.status_string(B.ATTN_EINVAL)
+    assert "unsupported" in B.status_string(B.ATTN_EUNSUPPORTED)

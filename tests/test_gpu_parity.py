@@ -1,0 +1,334 @@
+"""GPU parity: the HIP library (through the C ABI) against the fp64 CPU oracle
+on the same seeded inputs.
+
+Tolerance (per output tensor): max|gpu - ref| <= tol * max|ref|, with
+tol = 1e-4 for fp32 inputs and 2e-2 for bf16 inputs (fp32 accumulation).
+The backward on both sides consumes the same fp32 O and LSE, produced by the
+oracle forward, so parity measures the backward kernels alone; the GPU
+forward is checked separately.
+"""
+import sys
+
+import numpy as np
+import pytest
+
+import oracle
+from oracle import MaskSpec
+from attention_backward_attn_amd.inputs import WORKLOADS, make_inputs, round_bf16
+
+torch = pytest.importorskip("torch")
+pytestmark = pytest.mark.gpu
+
+from attention_backward_attn_amd import binding as ab  # noqa: E402
+
+TOL = {"f32": 1e-4, "bf16": 2e-2}
+# Absolute floor for outputs whose reference is (nearly) all zeros -- e.g.
+# dQ when every row has a single key, where fp32 rounding of delta leaves
+# ~1e-7 * |dO| |V| behind.
+ATOL = 1e-5
+
+
+def say(msg):
+    print(msg, flush=True)
+    sys.stdout.flush()
+
+
+@pytest.fixture(scope="module", autouse=True)
+def _gpu():
+    if not torch.cuda.is_available():
+        pytest.fail("GPU tests need a visible GPU")
+    ab.lib()
+
+
+def dev(x, dtype):
+    return None if x is None else torch.from_numpy(np.ascontiguousarray(x)).to("cuda", dtype)
+
+
+def tdtype(name):
+    return torch.bfloat16 if name == "bf16" else torch.float32
+
+
+def check(name, got, ref, tol):
+    got = got.detach().float().cpu().numpy().astype(np.float64) if torch.is_tensor(got) else np.asarray(got)
+    ref = np.asarray(ref, dtype=np.float64)
+    assert got.shape == ref.shape, (name, got.shape, ref.shape)
+    assert np.isfinite(got).all(), f"{name}: non-finite values"
+    scale = np.abs(ref).max()
+    err = np.abs(got - ref).max()
+    assert err <= tol * scale + ATOL, f"{name}: max err {err:.3e} > {tol:g} * {scale:.3e} + {ATOL:g}"
+    return err / max(scale, 1e-30)
+
+
+def mask_kw(spec: MaskSpec):
+    return dict(mask=spec.kind, window_left=spec.window_left, window_right=spec.window_right,
+                num_sink_tokens=spec.num_sink, q_offset=spec.q_offset, k_offset=spec.k_offset,
+                sq_total=spec.sq_total or 0, sk_total=spec.sk_total or 0)
+
+
+def random_case(B, Hq, Hk, Sq, Sk, D, Dv, dtype, seed, bias, sinks):
+    rng = np.random.default_rng(seed)
+    f = (lambda a: round_bf16(a.astype(np.float32))) if dtype == "bf16" else (lambda a: a.astype(np.float32))
+    x = {"q": f(rng.standard_normal((B, Hq, Sq, D))), "k": f(rng.standard_normal((B, Hk, Sk, D))),
+         "v": f(rng.standard_normal((B, Hk, Sk, Dv))), "do": f(rng.standard_normal((B, Hq, Sq, Dv)))}
+    x["bias"] = rng.standard_normal((Hq, Sq, Sk)).astype(np.float32) if bias else None
+    x["sinks"] = rng.standard_normal(Hq).astype(np.float32) if sinks else None
+    return x
+
+
+def run_full_parity(x, dtype, spec, scale, flags=0):
+    """Oracle forward -> fp32 O/LSE -> GPU and oracle backward; compare all."""
+    o64, lse64 = oracle.forward(x["q"], x["k"], x["v"], scale, spec, x["bias"], x["sinks"])
+    o32, lse32 = o64.astype(np.float32), lse64.astype(np.float32)
+    ref = oracle.backward(x["q"], x["k"], x["v"], o32, x["do"], lse32, scale, spec, x["bias"], x["sinks"])
+    dt = tdtype(dtype)
+    q, k, v, do = (dev(x[n], dt) for n in ("q", "k", "v", "do"))
+    bias, sinks = dev(x["bias"], torch.float32), dev(x["sinks"], torch.float32)
+    o, lse = dev(o32, torch.float32), dev(lse32, torch.float32)
+    got = ab.backward(q, k, v, o, do, lse, bias=bias, sinks=sinks, want_dbias=bias is not None,
+                      flags=flags, scale=scale, **mask_kw(spec))
+    torch.cuda.synchronize()
+    tol = TOL[dtype]
+    errs = {}
+    for n in ("dq", "dk", "dv", "dbias", "dsinks"):
+        if ref[n] is not None:
+            errs[n] = check(n, got[n], ref[n], tol)
+    check("delta", got["delta"], ref["delta"], 1e-5)
+    return errs, got
+
+
+SMALL = [
+    # B, Hq, Hk, Sq, Sk, D, Dv, dtype, spec, bias, sinks
+    (1, 2, 2, 64, 64, 64, 64, "f32", MaskSpec("none"), False, False),
+    (2, 4, 2, 77, 77, 64, 64, "f32", MaskSpec("top_left"), True, True),
+    (1, 4, 4, 100, 130, 32, 48, "f32", MaskSpec("bottom_right"), False, False),
+    (2, 8, 2, 256, 256, 128, 128, "bf16", MaskSpec("top_left"), False, False),
+    (1, 8, 1, 300, 300, 128, 128, "bf16", MaskSpec("bottom_right"), False, False),
+    (2, 4, 4, 192, 320, 64, 64, "bf16", MaskSpec("none"), True, False),
+    (1, 16, 2, 384, 384, 128, 128, "bf16", MaskSpec("top_left", window_left=100, num_sink=4), False, True),
+    (1, 4, 1, 200, 333, 128, 128, "bf16", MaskSpec("bottom_right", window_left=63, window_right=5,
+                                                    num_sink=3), True, True),
+    (2, 2, 1, 257, 129, 64, 64, "bf16", MaskSpec("bottom_right"), False, False),   # empty rows
+    (1, 2, 2, 1, 513, 128, 128, "bf16", MaskSpec("none"), False, False),
+    (1, 8, 8, 129, 1, 64, 64, "bf16", MaskSpec("none"), False, False),
+]
+
+
+@pytest.mark.parametrize("case", SMALL, ids=lambda c: f"{c[7]}-B{c[0]}H{c[1]}:{c[2]}-S{c[3]}x{c[4]}-D{c[5]}-"
+                         f"{c[8].kind}{'-bias' if c[9] else ''}{'-sinks' if c[10] else ''}")
+@pytest.mark.parametrize("flags", [0, ab.ATTN_DETERMINISTIC], ids=["atomic", "determ"])
+def test_small_parity(case, flags):
+    B, Hq, Hk, Sq, Sk, D, Dv, dtype, spec, bias, sinks = case
+    say(f"[parity] {case} flags={flags}")
+    x = random_case(B, Hq, Hk, Sq, Sk, D, Dv, dtype, 100 + Sq + Sk, bias, sinks)
+    run_full_parity(x, dtype, spec, 1.0 / np.sqrt(D), flags)
+
+
+@pytest.mark.parametrize("name", ["mha_f32_s64", "gqa4_causal_tl_s1024"])
+def test_workload_full_parity(name):
+    w = WORKLOADS[name]
+    say(f"[workload full] {name}")
+    x = make_inputs(w)
+    spec = MaskSpec(w.mask, w.window_left, w.window_right, w.num_sink)
+    errs, _ = run_full_parity(x, w.dtype, spec, w.scale)
+    say(f"  rel errs {errs}")
+
+
+def sampled_workload(name, groups, rows_per_head=48, n_keys=48, flags=0):
+    """Full-size run of a workload; compare sampled outputs with the oracle.
+
+    The oracle forward runs for the query heads of the sampled KV groups
+    (every batch entry for bias workloads, whose dbias sums the batch); the
+    other heads take O/LSE from the GPU forward and are only checked for
+    finite values."""
+    w = WORKLOADS[name]
+    x = make_inputs(w)
+    spec = MaskSpec(w.mask, w.window_left, w.window_right, w.num_sink)
+    dt = tdtype(w.dtype)
+    q, k, v, do = (dev(x[n], dt) for n in ("q", "k", "v", "do"))
+    bias, sinks = dev(x["bias"], torch.float32), dev(x["sinks"], torch.float32)
+    say(f"[workload sampled] {name}: GPU forward")
+    o, lse = ab.forward(q, k, v, bias=bias, sinks=sinks, scale=w.scale, **mask_kw(spec))
+    torch.cuda.synchronize()
+    o_np = o.cpu().numpy()
+    lse_np = lse.cpu().numpy()
+    G = w.G
+    bs = range(w.B) if (w.bias or w.sinks) else [0]
+    for g in groups:
+        heads = list(range(g * G, (g + 1) * G))
+        for b in bs:
+            sl = (slice(b, b + 1), slice(heads[0], heads[-1] + 1))
+            bias_h = None if x["bias"] is None else x["bias"][heads[0]:heads[-1] + 1]
+            sinks_h = None if x["sinks"] is None else x["sinks"][heads[0]:heads[-1] + 1]
+            o64, l64 = oracle.forward(x["q"][sl], x["k"][b:b + 1, g:g + 1], x["v"][b:b + 1, g:g + 1],
+                                      w.scale, spec, bias_h, sinks_h, row_block=1024)
+            o_np[sl] = o64.astype(np.float32)
+            lse_np[sl] = l64.astype(np.float32)
+    o = dev(o_np, torch.float32)
+    lse = dev(lse_np, torch.float32)
+    say(f"[workload sampled] {name}: GPU backward flags={flags}")
+    got = ab.backward(q, k, v, o, do, lse, bias=bias, sinks=sinks, want_dbias=bias is not None,
+                      flags=flags, scale=w.scale, **mask_kw(spec))
+    torch.cuda.synchronize()
+    for key in ("dq", "dk", "dv"):
+        assert torch.isfinite(got[key]).all(), key
+    rng = np.random.default_rng(77)
+    tol = TOL[w.dtype]
+    errs = {}
+    for g in groups:
+        heads = list(range(g * G, (g + 1) * G))
+        b = 0
+        edge = [0, 1, 2, 3, 4, w.Sk // 4 - 1, w.Sk // 4, w.Sk // 2, w.Sk - 1]
+        keys = np.unique(np.concatenate([edge, rng.choice(w.Sk, n_keys, replace=False)]))
+        dk_ref, dv_ref = oracle.dkdv_keys(x["q"], x["k"], x["v"], o_np, x["do"], lse_np, w.scale, spec,
+                                          b, g, keys, x["bias"])
+        errs[f"dk[g{g}]"] = check("dk", got["dk"][b, g, keys], dk_ref, tol)
+        errs[f"dv[g{g}]"] = check("dv", got["dv"][b, g, keys], dv_ref, tol)
+        for h in heads[:2] + heads[-1:]:
+            rows = np.unique(np.concatenate([[0, 1, w.Sq - 1], rng.choice(w.Sq, rows_per_head, replace=False)]))
+            ref = oracle.dq_rows(x["q"], x["k"], x["v"], o_np, x["do"], lse_np, w.scale, spec, b, h, rows,
+                                 x["bias"])
+            errs[f"dq[h{h}]"] = check("dq", got["dq"][b, h, rows], ref, tol)
+            if w.bias:
+                rows_b = rows[:12]
+                ref_b = sum(oracle.ds_rows(x["q"], x["k"], x["v"], o_np, x["do"], lse_np, w.scale, spec, bb,
+                                           h, rows_b, x["bias"]) for bb in range(w.B))
+                errs[f"dbias[h{h}]"] = check("dbias", got["dbias"][h, rows_b], ref_b, tol)
+        if w.sinks:
+            ref_d, ref_s = oracle.preprocess(o_np[:, heads], x["do"][:, heads], lse_np[:, heads],
+                                             x["sinks"][heads])
+            errs[f"dsinks[g{g}]"] = check("dsinks", got["dsinks"][heads], ref_s, tol)
+            check("delta", got["delta"][:, heads], ref_d, 1e-5)
+    say(f"  rel errs {errs}")
+    return got, x, o_np, lse_np
+
+
+def test_headline_sampled():
+    sampled_workload("gqa4_causal_br_s4096", groups=[0, 7])
+
+
+def test_alibi_dbias_sampled():
+    sampled_workload("mha_alibi_dbias_s2048", groups=[0, 15], rows_per_head=16, n_keys=24)
+
+
+def test_window_sink_sampled():
+    sampled_workload("gqa8_swa1024_sink4_s8192", groups=[0], rows_per_head=32, n_keys=32)
+
+
+def test_dsinks_full_batch():
+    """dsinks sums over the batch: check it on a small multi-batch case."""
+    x = random_case(3, 8, 2, 160, 160, 64, 64, "bf16", 5, False, True)
+    run_full_parity(x, "bf16", MaskSpec("top_left", window_left=31, num_sink=2), 0.125)
+
+
+# ---------------------------------------------------------------------------
+FWD = [
+    (1, 2, 2, 64, 64, 64, 64, "f32", MaskSpec("none"), False, False),
+    (2, 8, 2, 200, 200, 128, 128, "bf16", MaskSpec("top_left", window_left=50, num_sink=3), True, True),
+    (1, 4, 1, 100, 260, 128, 64, "bf16", MaskSpec("bottom_right"), False, True),
+    (1, 2, 2, 90, 40, 64, 64, "bf16", MaskSpec("bottom_right"), False, False),  # empty rows
+]
+
+
+@pytest.mark.parametrize("case", FWD)
+def test_forward_parity(case):
+    B, Hq, Hk, Sq, Sk, D, Dv, dtype, spec, bias, sinks = case
+    say(f"[fwd] {case}")
+    x = random_case(B, Hq, Hk, Sq, Sk, D, Dv, dtype, 3, bias, sinks)
+    o_ref, lse_ref = oracle.forward(x["q"], x["k"], x["v"], 1 / np.sqrt(D), spec, x["bias"], x["sinks"])
+    dt = tdtype(dtype)
+    o, lse = ab.forward(dev(x["q"], dt), dev(x["k"], dt), dev(x["v"], dt), bias=dev(x["bias"], torch.float32),
+                        sinks=dev(x["sinks"], torch.float32), scale=1 / np.sqrt(D), **mask_kw(spec))
+    torch.cuda.synchronize()
+    check("o", o, o_ref, 1e-4)
+    lse_g = lse.cpu().numpy()
+    empty = np.isneginf(lse_ref)
+    assert (np.isneginf(lse_g) == empty).all()
+    np.testing.assert_allclose(lse_g[~empty], lse_ref[~empty], rtol=0, atol=1e-4)
+
+
+def test_lse_merge_parity():
+    say("[merge]")
+    rng = np.random.default_rng(12)
+    B, H, S, Dv = 2, 3, 70, 96
+    o_a, o_b = rng.standard_normal((B, H, S, Dv)).astype(np.float32), rng.standard_normal((B, H, S, Dv)).astype(np.float32)
+    l_a, l_b = rng.standard_normal((B, H, S)).astype(np.float32), rng.standard_normal((B, H, S)).astype(np.float32)
+    l_a[0, 0, :5] = -np.inf
+    o_a[0, 0, :5] = 0
+    l_b[0, 0, 3:8] = -np.inf
+    o_b[0, 0, 3:8] = 0
+    o_ref, l_ref = oracle.lse_merge(o_a, l_a, o_b, l_b)
+    oa, la = dev(o_a, torch.float32), dev(l_a, torch.float32)
+    ab.attn_lse_merge(oa, la, dev(o_b, torch.float32), dev(l_b, torch.float32))
+    torch.cuda.synchronize()
+    check("o", oa, o_ref, 1e-6)
+    lg = la.cpu().numpy()
+    assert (np.isneginf(lg) == np.isneginf(l_ref)).all()
+    fin = np.isfinite(l_ref)
+    np.testing.assert_allclose(lg[fin], l_ref[fin], atol=1e-6)
+
+
+def test_headline_chunked():
+    """The headline workload run as 4 K/V chunks of 1024: forward partials
+    joined by attn_lse_merge, then the backward of each chunk against the
+    global O / LSE / delta with dQ accumulated ("Ring attention for PyTorch",
+    _ring_fwd / _ring_bwd on one GPU).  Compared with the unchunked GPU run
+    and, on sampled outputs, with the oracle."""
+    w = WORKLOADS["gqa4_causal_br_s4096"]
+    x = make_inputs(w)
+    spec = MaskSpec(w.mask)
+    dt = torch.bfloat16
+    q, k, v, do = (dev(x[n], dt) for n in ("q", "k", "v", "do"))
+    say("[chunked] forward")
+    o_full, lse_full = ab.forward(q, k, v, scale=w.scale, mask=w.mask)
+    n, c = w.kv_chunks, w.Sk // w.kv_chunks
+    o = torch.zeros_like(o_full)
+    lse = torch.full_like(lse_full, -np.inf)
+    for i in range(n):
+        kc, vc = k[:, :, i * c:(i + 1) * c], v[:, :, i * c:(i + 1) * c]
+        o2, l2 = ab.forward(q, kc, vc, scale=w.scale, mask=w.mask, k_offset=i * c, sk_total=w.Sk)
+        ab.attn_lse_merge(o, lse, o2, l2)
+    torch.cuda.synchronize()
+    assert (lse == -np.inf).sum() == 0
+    check("o merged vs unchunked", o, o_full.cpu().numpy(), 1e-5)
+    # oracle forward on one group
+    o64, l64 = oracle.forward(x["q"][:, :4], x["k"][:, :1], x["v"][:, :1], w.scale, spec, row_block=1024)
+    check("o merged vs oracle", o[:, :4], o64, 1e-4)
+    say("[chunked] backward")
+    full = ab.backward(q, k, v, o, do, lse, scale=w.scale, mask=w.mask)
+    dq = torch.zeros_like(full["dq"])
+    delta = torch.empty_like(full["delta"])
+    dk = torch.empty_like(full["dk"])
+    dv = torch.empty_like(full["dv"])
+    p = ab.make_problem(q, k, v, o=o, do=do, dq=dq, dk=dk, dv=dv, scale=w.scale, mask=w.mask)
+    ab.attn_bwd_preprocess(p, o, do, lse, None, delta, None, None)
+    for i in range(n):
+        sl = slice(i * c, (i + 1) * c)
+        pc = ab.make_problem(q, k[:, :, sl], v[:, :, sl], o=o, do=do, dq=dq, dk=dk[:, :, sl], dv=dv[:, :, sl],
+                             scale=w.scale, mask=w.mask, k_offset=i * c, sk_total=w.Sk)
+        ab.attn_bwd(pc, q, k[:, :, sl], v[:, :, sl], do, lse, delta, None, dq, dk[:, :, sl], dv[:, :, sl],
+                    None, ab.ATTN_ACCUMULATE_DQ)
+    torch.cuda.synchronize()
+    for name, a, b in (("dq", dq, full["dq"]), ("dk", dk, full["dk"]), ("dv", dv, full["dv"])):
+        check(f"chunked {name} vs unchunked", a, b.cpu().numpy(), 1e-3)
+    # sampled oracle check on group 0 with the oracle's own O / LSE
+    rows = np.array([0, 1, 1023, 1024, 2047, 3000, 4095])
+    o_np, lse_np = o.cpu().numpy(), lse.cpu().numpy()
+    ref = oracle.dq_rows(x["q"], x["k"], x["v"], o_np, x["do"], lse_np, w.scale, spec, 0, 1, rows)
+    check("chunked dq vs oracle", dq[0, 1, rows], ref, 2e-2)
+
+
+def test_deterministic_is_bitwise_repeatable():
+    x = random_case(1, 8, 2, 512, 512, 128, 128, "bf16", 9, True, True)
+    spec = MaskSpec("top_left", window_left=200, num_sink=4)
+    dt = torch.bfloat16
+    q, k, v, do = (dev(x[n], dt) for n in ("q", "k", "v", "do"))
+    bias, sinks = dev(x["bias"], torch.float32), dev(x["sinks"], torch.float32)
+    o, lse = ab.forward(q, k, v, bias=bias, sinks=sinks, scale=1 / np.sqrt(128), **mask_kw(spec))
+    outs = []
+    for _ in range(3):
+        g = ab.backward(q, k, v, o, do, lse, bias=bias, sinks=sinks, want_dbias=True,
+                        flags=ab.ATTN_DETERMINISTIC, scale=1 / np.sqrt(128), **mask_kw(spec))
+        torch.cuda.synchronize()
+        outs.append({kk: vv.clone() for kk, vv in g.items() if vv is not None})
+    for kk in outs[0]:
+        assert torch.equal(outs[0][kk], outs[1][kk]) and torch.equal(outs[0][kk], outs[2][kk]), kk

@@ -208,6 +208,8 @@ def test_sampled_helpers_match_full_backward():
     dk, dv = oracle.dkdv_keys(q, k, v, o, do, lse, 0.3, spec, 0, 1, keys, bias)
     np.testing.assert_allclose(dk, g["dk"][0, 1, keys], atol=1e-13)
     np.testing.assert_allclose(dv, g["dv"][0, 1, keys], atol=1e-13)
+    dbias_rows = sum(oracle.ds_rows(q, k, v, o, do, lse, 0.3, spec, bb, 2, rows, bias) for bb in range(B))
+    np.testing.assert_allclose(dbias_rows, g["dbias"][2, rows], atol=1e-13)
 
 
 def test_planted_mistake_is_caught():
