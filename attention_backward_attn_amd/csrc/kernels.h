@@ -49,6 +49,8 @@ hipError_t launch_lse_merge(int64_t rows, int Dv, float* o_acc, float* lse_acc, 
 constexpr int kSimtMaxD = 128;
 hipError_t launch_fwd_simt(const Params& p, const FwdArgs& a, int in_bf16, int o_bf16, hipStream_t st);
 hipError_t launch_bwd_simt(const Params& p, const BwdArgs& a, int in_bf16, hipStream_t st);
+// dQ alone (query-parallel, no atomics); ACCUMULATE adds into dq.
+hipError_t launch_dq_simt(const Params& p, const BwdArgs& a, int in_bf16, hipStream_t st);
 
 // bf16 matrix-core backward (gfx950 MFMA), head dims 64 and 128.
 bool mfma_bwd_supported(const Params& p);

@@ -1,10 +1,579 @@
-// bf16 matrix-core backward (placeholder until the MFMA kernels land).
+// bf16 matrix-core (gfx950 MFMA) attention backward.
+//
+// Math (CK FMHA example 34 "Backward Pass with GQA", cpu_bwd_gqa and its
+// docstring; CANN sparse_flash_mla_grad "Formula" Phase 2 / 3; CK FMHA
+// example 28 cpu_attention_bwd_dbias):
+//   S = scale Q K^T (+ bias),  P = exp(S - LSE),  dP = dO V^T,
+//   dS = P (dP - delta),  dV = P^T dO,  dK = scale dS^T Q,  dQ = scale dS K,
+//   dbias = sum_b dS.
+//
+// Kernel k_dkdv: one workgroup per (128-key block, KV head[, batch]).
+//   Four waves; wave w owns keys [32 w, 32 w + 32) of the block and keeps
+//   K, V (and K^T for dQ) as MFMA operand fragments in registers, and dK, dV
+//   as fp32 accumulators in registers for the whole loop over the G query
+//   heads of the group and the 32-row query tiles that can see the block
+//   (no atomics for dK / dV).  Per tile: S and dP by v_mfma_f32_32x32x16_bf16
+//   with the K / V fragments as the B operand, so that the accumulator layout
+//   (one key per lane, 16 rows per lane) is directly the A operand of
+//   P^T dO and dS^T Q once the reduction index is permuted consistently on
+//   both operands.  dO^T / Q^T come from transposed LDS copies.  dS goes
+//   through LDS to form dQ = dS K for the tile (wave w: head-dim columns
+//   [32 w, 32 w + 32)), added into global dQ with fp32 atomics -- or left to
+//   the deterministic query-parallel kernel k_dq.
+//
+// MFMA 32x32x16 bf16 operand layout (lane l, r = 0..15):
+//   A[m][k]: lane holds m = l % 32, k = 8 (l / 32) + 0..7
+//   B[k][n]: lane holds n = l % 32, k = 8 (l / 32) + 0..7
+//   C[m][n]: lane holds n = l % 32, m = 8 (r / 4) + 4 (l / 32) + r % 4
 #include "kernels.h"
 
 namespace attn {
+namespace {
 
-bool mfma_bwd_supported(const Params&) { return false; }
+constexpr int BK = 128;       // keys per workgroup (k_dkdv)
+constexpr int BQ = 32;        // query rows per iteration (k_dkdv)
+constexpr int TP = 36;        // row length (elements) of the transposed tiles: 32 + 4 pad
+constexpr int NT = 256;       // threads per workgroup
 
-hipError_t launch_bwd_mfma(const Params&, const BwdArgs&, hipStream_t) { return hipErrorInvalidValue; }
+__device__ inline f32x16 mfma(bf16x8 a, bf16x8 b, f32x16 c) {
+  return __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c, 0, 0, 0);
+}
+
+__device__ inline bf16x8 as_bf16x8(u16x8 v) { return __builtin_bit_cast(bf16x8, v); }
+
+__device__ inline bf16x8 cat44(u16x4 lo, u16x4 hi) {
+  u16x8 v = {lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
+  return as_bf16x8(v);
+}
+
+// 8 fp32 accumulator values -> bf16x8 operand (round to nearest even).
+__device__ inline bf16x8 pack8(const float* x) {
+  bf16x8 r;
+#pragma unroll
+  for (int i = 0; i < 8; ++i) r[i] = (__bf16)x[i];
+  return r;
+}
+
+__device__ inline f32x16 zero16() {
+  f32x16 z;
+#pragma unroll
+  for (int i = 0; i < 16; ++i) z[i] = 0.f;
+  return z;
+}
+
+// Row (within a 32-row accumulator block) held by lane group lg in register r.
+__device__ inline int crow(int r, int lg) { return 8 * (r >> 2) + 4 * lg + (r & 3); }
+
+template <int D>
+struct SmemDKDV {
+  unsigned short q[2][BQ][D + 8];    // Q tile, row-major (A operand of S = Q K^T)
+  unsigned short dO[2][BQ][D + 8];   // dO tile, row-major (A operand of dP = dO V^T)
+  unsigned short qt[2][D][TP];       // Q^T (B operand of dK += dS^T Q)
+  unsigned short dOt[2][D][TP];      // dO^T (B operand of dV += P^T dO)
+  unsigned short ds[BQ][BK + 8];     // dS tile, row-major (A operand of dQ = dS K)
+  float lse2[2][BQ];                 // LSE * log2(e); +inf for rows without keys
+  float delta[2][BQ];
+};
+
+// Per-thread staging of one 32-row Q / dO tile: thread t < 2 * nch handles
+// rows 4 rg .. 4 rg + 3, columns 8 cc .. 8 cc + 7 of Q (t < nch) or dO.
+template <int D>
+struct Stage {
+  static constexpr int NCH = (BQ / 4) * (D / 8);
+  u16x8 v[4];
+  float lse, dl;
+
+  __device__ inline void load(const unsigned short* q, const unsigned short* dout, int64_t qs, int64_t ds,
+                              const float* lse_p, const float* dl_p, int64_t i0, int Sq) {
+    const int t = threadIdx.x;
+    if (t < 2 * NCH) {
+      const int c = t < NCH ? t : t - NCH;
+      const int rg = c / (D / 8), cc = c % (D / 8);
+      const unsigned short* base = t < NCH ? q : dout;
+      const int64_t st = t < NCH ? qs : ds;
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        const int64_t i = i0 + 4 * rg + e;
+        if (i < Sq) {
+          v[e] = *(const u16x8*)(base + i * st + 8 * cc);
+        } else {
+          v[e] = u16x8{0, 0, 0, 0, 0, 0, 0, 0};
+        }
+      }
+    }
+    if (t >= NT - BQ) {
+      const int r = t - (NT - BQ);
+      const int64_t i = i0 + r;
+      const float l = (i < Sq) ? lse_p[i] : -INFINITY;
+      lse = (l == -INFINITY) ? INFINITY : l * kLog2e;
+      dl = (i < Sq) ? dl_p[i] : 0.f;
+    }
+  }
+
+  __device__ inline void store(SmemDKDV<D>& sm, int buf) const {
+    const int t = threadIdx.x;
+    if (t < 2 * NCH) {
+      const int c = t < NCH ? t : t - NCH;
+      const int rg = c / (D / 8), cc = c % (D / 8);
+      unsigned short(*rowm)[D + 8] = t < NCH ? sm.q[buf] : sm.dO[buf];
+      unsigned short(*colm)[TP] = t < NCH ? sm.qt[buf] : sm.dOt[buf];
+#pragma unroll
+      for (int e = 0; e < 4; ++e) *(u16x8*)&rowm[4 * rg + e][8 * cc] = v[e];
+#pragma unroll
+      for (int k = 0; k < 8; ++k) {
+        u16x4 col = {v[0][k], v[1][k], v[2][k], v[3][k]};
+        *(u16x4*)&colm[8 * cc + k][4 * rg] = col;
+      }
+    }
+    if (t >= NT - BQ) {
+      const int r = t - (NT - BQ);
+      sm.lse2[buf][r] = lse;
+      sm.delta[buf][r] = dl;
+    }
+  }
+};
+
+template <int D, bool BIAS, bool DQ_ATOMIC, bool BLOOP>
+__global__ __launch_bounds__(NT, 1) void k_dkdv(Params p, BwdArgs a) {
+  static_assert(D == 64 || D == 128, "head dim");
+  constexpr int NS = D / 16;          // k-steps over the head dim
+  constexpr int NB = D / 32;          // 32-column blocks of the head dim
+  __shared__ __attribute__((aligned(16))) SmemDKDV<D> sm;
+
+  const int tid = threadIdx.x, w = tid >> 6, l = tid & 63, lr = l & 31, lg = l >> 5;
+  const int k0 = blockIdx.x * BK;
+  const int hk = blockIdx.y;
+  const int kw = k0 + 32 * w;         // first key of this wave
+  const int jkey = kw + lr;           // this lane's key (accumulator column of S / dP)
+  const int Sq = p.Sq, Sk = p.Sk;
+  const float scale_log2 = p.scale * kLog2e;
+
+  int64_t lo, hi;
+  p.mask.rows_for_keys(k0, min(k0 + BK, Sk), Sq, &lo, &hi);
+  const int64_t lo_al = lo & ~(int64_t)(BQ - 1);
+  const int nqb = hi > lo ? (int)((hi - lo_al + BQ - 1) / BQ) : 0;
+  const int n_it = p.G * nqb;
+  const bool wave_keys_in = kw + 32 <= Sk;
+  const bool dq_wave = DQ_ATOMIC && (w < NB);
+
+  const int b_begin = BLOOP ? 0 : blockIdx.z;
+  const int b_end = BLOOP ? p.B : b_begin + 1;
+  for (int b = b_begin; b < b_end; ++b) {
+    const unsigned short* kp = (const unsigned short*)a.k + b * p.k_str[0] + hk * p.k_str[1];
+    const unsigned short* vp = (const unsigned short*)a.v + b * p.v_str[0] + hk * p.v_str[1];
+    // K / V fragments of this wave's keys (B operands of S and dP).
+    bf16x8 kB[NS], vB[NS];
+#pragma unroll
+    for (int s = 0; s < NS; ++s) {
+      if (jkey < Sk) {
+        kB[s] = as_bf16x8(*(const u16x8*)(kp + (int64_t)jkey * p.k_str[2] + 16 * s + 8 * lg));
+        vB[s] = as_bf16x8(*(const u16x8*)(vp + (int64_t)jkey * p.v_str[2] + 16 * s + 8 * lg));
+      } else {
+        kB[s] = as_bf16x8(u16x8{0, 0, 0, 0, 0, 0, 0, 0});
+        vB[s] = kB[s];
+      }
+    }
+    // K^T fragments (B operand of dQ = dS K): keys 16 t + 8 lg + e, column 32 w + lr.
+    bf16x8 ktB[BK / 16];
+    if (dq_wave) {
+#pragma unroll
+      for (int t = 0; t < BK / 16; ++t) {
+        u16x8 u;
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+          const int j = k0 + 16 * t + 8 * lg + e;
+          u[e] = (j < Sk) ? kp[(int64_t)j * p.k_str[2] + 32 * w + lr] : (unsigned short)0;
+        }
+        ktB[t] = as_bf16x8(u);
+      }
+    }
+    f32x16 dk[NB], dv[NB];
+#pragma unroll
+    for (int n = 0; n < NB; ++n) { dk[n] = zero16(); dv[n] = zero16(); }
+
+    Stage<D> stg;
+    auto tile_ptrs = [&](int it, const unsigned short** q, const unsigned short** dout, const float** lse_p,
+                         const float** dl_p, int* h, int64_t* i0) {
+      *h = hk * p.G + it / nqb;
+      *i0 = lo_al + (int64_t)BQ * (it % nqb);
+      *q = (const unsigned short*)a.q + b * p.q_str[0] + *h * p.q_str[1];
+      *dout = (const unsigned short*)a.dout + b * p.do_str[0] + *h * p.do_str[1];
+      *lse_p = a.lse + ((int64_t)b * p.Hq + *h) * Sq;
+      *dl_p = a.delta + ((int64_t)b * p.Hq + *h) * Sq;
+    };
+    if (n_it > 0) {
+      const unsigned short *q, *dout;
+      const float *lse_p, *dl_p;
+      int h;
+      int64_t i0;
+      tile_ptrs(0, &q, &dout, &lse_p, &dl_p, &h, &i0);
+      __syncthreads();  // previous batch's readers of buffer 0 are done
+      stg.load(q, dout, p.q_str[2], p.do_str[2], lse_p, dl_p, i0, Sq);
+      stg.store(sm, 0);
+      __syncthreads();
+    }
+
+    for (int it = 0; it < n_it; ++it) {
+      const int cur = it & 1;
+      const unsigned short *q, *dout;
+      const float *lse_p, *dl_p;
+      int h;
+      int64_t i0;
+      tile_ptrs(it, &q, &dout, &lse_p, &dl_p, &h, &i0);
+      if (it + 1 < n_it) {
+        const unsigned short *q1, *d1;
+        const float *l1, *dl1;
+        int h1;
+        int64_t i1;
+        tile_ptrs(it + 1, &q1, &d1, &l1, &dl1, &h1, &i1);
+        stg.load(q1, d1, p.q_str[2], p.do_str[2], l1, dl1, i1, Sq);
+      }
+
+      // S = Q K^T and dP = dO V^T for rows i0..i0+31, this wave's 32 keys.
+      f32x16 sacc = zero16(), dpacc = zero16();
+#pragma unroll
+      for (int s = 0; s < NS; ++s) {
+        const bf16x8 qa = as_bf16x8(*(const u16x8*)&sm.q[cur][lr][16 * s + 8 * lg]);
+        const bf16x8 da = as_bf16x8(*(const u16x8*)&sm.dO[cur][lr][16 * s + 8 * lg]);
+        sacc = mfma(qa, kB[s], sacc);
+        dpacc = mfma(da, vB[s], dpacc);
+      }
+
+      // P = exp(S - LSE) on allowed pairs, dS = P (dP - delta).
+      const bool full = wave_keys_in && p.mask.tile_full(i0, i0 + BQ, kw, kw + 32);
+      float pv[16], dsv[16];
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        const int row = crow(r, lg);
+        const int64_t i = i0 + row;
+        float x = sacc[r] * scale_log2;
+        if (BIAS) {
+          if (i < Sq && jkey < Sk) x += a.bias[h * p.bias_str[0] + i * p.bias_str[1] + jkey] * kLog2e;
+        }
+        float pp = exp2f(x - sm.lse2[cur][row]);
+        if (!full && !(jkey < Sk && p.mask.allowed(i, jkey))) pp = 0.f;
+        pv[r] = pp;
+        dsv[r] = pp * (dpacc[r] - sm.delta[cur][row]);
+      }
+      if (BIAS && a.dbias) {
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+          const int64_t i = i0 + crow(r, lg);
+          if (i < Sq && jkey < Sk && pv[r] != 0.f) {
+            float* dst = a.dbias + h * p.bias_str[0] + i * p.bias_str[1] + jkey;
+            if (BLOOP)
+              *dst += dsv[r];
+            else
+              atomic_add_f32(dst, dsv[r]);
+          }
+        }
+      }
+      const bf16x8 pa0 = pack8(pv), pa1 = pack8(pv + 8);
+      const bf16x8 sa0 = pack8(dsv), sa1 = pack8(dsv + 8);
+
+      // dV += P^T dO and dK += dS^T Q (reduction over the 32 rows, permuted
+      // consistently with the accumulator layout of S).
+#pragma unroll
+      for (int n = 0; n < NB; ++n) {
+        const int d = 32 * n + lr;
+        const bf16x8 o0 = cat44(*(const u16x4*)&sm.dOt[cur][d][4 * lg], *(const u16x4*)&sm.dOt[cur][d][8 + 4 * lg]);
+        const bf16x8 o1 = cat44(*(const u16x4*)&sm.dOt[cur][d][16 + 4 * lg],
+                                *(const u16x4*)&sm.dOt[cur][d][24 + 4 * lg]);
+        dv[n] = mfma(pa0, o0, dv[n]);
+        dv[n] = mfma(pa1, o1, dv[n]);
+        const bf16x8 q0 = cat44(*(const u16x4*)&sm.qt[cur][d][4 * lg], *(const u16x4*)&sm.qt[cur][d][8 + 4 * lg]);
+        const bf16x8 q1 = cat44(*(const u16x4*)&sm.qt[cur][d][16 + 4 * lg], *(const u16x4*)&sm.qt[cur][d][24 + 4 * lg]);
+        dk[n] = mfma(sa0, q0, dk[n]);
+        dk[n] = mfma(sa1, q1, dk[n]);
+      }
+
+      if (DQ_ATOMIC) {
+        // dS (bf16) to LDS, row-major [row][key in block].
+        const __bf16* dsb = (const __bf16*)&sa0;
+        const __bf16* dsb1 = (const __bf16*)&sa1;
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+          const __bf16 v = r < 8 ? dsb[r] : dsb1[r - 8];
+          sm.ds[crow(r, lg)][32 * w + lr] = __builtin_bit_cast(unsigned short, v);
+        }
+        __syncthreads();
+        if (dq_wave) {
+          f32x16 qacc = zero16();
+#pragma unroll
+          for (int t = 0; t < BK / 16; ++t) {
+            const bf16x8 da = as_bf16x8(*(const u16x8*)&sm.ds[lr][16 * t + 8 * lg]);
+            qacc = mfma(da, ktB[t], qacc);
+          }
+          float* dq = a.dq + b * p.dq_str[0] + h * p.dq_str[1] + 32 * w + lr;
+#pragma unroll
+          for (int r = 0; r < 16; ++r) {
+            const int64_t i = i0 + crow(r, lg);
+            if (i >= lo && i < hi) atomic_add_f32(dq + i * p.dq_str[2], qacc[r] * p.scale);
+          }
+        }
+      }
+      if (it + 1 < n_it) stg.store(sm, cur ^ 1);
+      __syncthreads();
+    }
+
+    // Epilogue: dK * scale and dV for this wave's keys (complete group sums).
+    float* dkp = a.dk + b * p.dk_str[0] + hk * p.dk_str[1];
+    float* dvp = a.dv + b * p.dv_str[0] + hk * p.dv_str[1];
+#pragma unroll
+    for (int n = 0; n < NB; ++n) {
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        const int64_t j = kw + crow(r, lg);
+        if (j < Sk) {
+          dkp[j * p.dk_str[2] + 32 * n + lr] = dk[n][r] * p.scale;
+          dvp[j * p.dv_str[2] + 32 * n + lr] = dv[n][r];
+        }
+      }
+    }
+  }
+}
+
+template <int D, bool BIAS, bool DQ_ATOMIC, bool BLOOP>
+hipError_t launch_dkdv(const Params& p, const BwdArgs& a, hipStream_t st) {
+  const dim3 grid((p.Sk + BK - 1) / BK, p.Hk, BLOOP ? 1 : p.B);
+  hipLaunchKernelGGL((k_dkdv<D, BIAS, DQ_ATOMIC, BLOOP>), grid, dim3(NT), 0, st, p, a);
+  return hipGetLastError();
+}
+
+template <int D>
+hipError_t dispatch_dkdv(const Params& p, const BwdArgs& a, bool bias, bool dq_atomic, bool bloop,
+                         hipStream_t st) {
+  // the batch loop is only used with the deterministic (non-atomic) dQ pass
+  if (bias) {
+    if (dq_atomic) return launch_dkdv<D, true, true, false>(p, a, st);
+    return bloop ? launch_dkdv<D, true, false, true>(p, a, st) : launch_dkdv<D, true, false, false>(p, a, st);
+  }
+  if (dq_atomic) return launch_dkdv<D, false, true, false>(p, a, st);
+  return launch_dkdv<D, false, false, false>(p, a, st);
+}
+
+// ---------------------------------------------------------------------------
+// Kernel k_dq (deterministic dQ): one workgroup per (128-row query block,
+// query head, batch).  Wave w owns rows [32 w, 32 w + 32) and keeps Q and dO
+// as B-operand fragments in registers; per 32-key tile it forms
+// S^T = K Q^T and dP^T = V dO^T (keys on accumulator rows, one query row per
+// lane), so dS^T's accumulator layout is directly the A operand of
+// dQ = dS K with K^T from a transposed LDS copy.  dQ accumulates in registers
+// over every key tile the block can see -- no atomics.
+// ---------------------------------------------------------------------------
+constexpr int BQ3 = 128;   // query rows per workgroup (k_dq)
+constexpr int BK3 = 32;    // keys per iteration (k_dq)
+
+template <int D>
+struct SmemDQ {
+  unsigned short k[2][BK3][D + 8];   // K tile, row-major (A operand of S^T)
+  unsigned short v[2][BK3][D + 8];   // V tile, row-major (A operand of dP^T)
+  unsigned short kt[2][D][TP];       // K^T (B operand of dQ += dS K)
+};
+
+template <int D>
+struct StageKV {
+  static constexpr int NCH = (BK3 / 4) * (D / 8);
+  u16x8 v[4];
+
+  __device__ inline void load(const unsigned short* k, const unsigned short* vv, int64_t ks, int64_t vs,
+                              int64_t j0, int Sk) {
+    const int t = threadIdx.x;
+    if (t < 2 * NCH) {
+      const int c = t < NCH ? t : t - NCH;
+      const int rg = c / (D / 8), cc = c % (D / 8);
+      const unsigned short* base = t < NCH ? k : vv;
+      const int64_t st = t < NCH ? ks : vs;
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        const int64_t j = j0 + 4 * rg + e;
+        if (j < Sk)
+          v[e] = *(const u16x8*)(base + j * st + 8 * cc);
+        else
+          v[e] = u16x8{0, 0, 0, 0, 0, 0, 0, 0};
+      }
+    }
+  }
+
+  __device__ inline void store(SmemDQ<D>& sm, int buf) const {
+    const int t = threadIdx.x;
+    if (t < 2 * NCH) {
+      const int c = t < NCH ? t : t - NCH;
+      const int rg = c / (D / 8), cc = c % (D / 8);
+      unsigned short(*rowm)[D + 8] = t < NCH ? sm.k[buf] : sm.v[buf];
+#pragma unroll
+      for (int e = 0; e < 4; ++e) *(u16x8*)&rowm[4 * rg + e][8 * cc] = v[e];
+      if (t < NCH) {
+#pragma unroll
+        for (int k = 0; k < 8; ++k) {
+          u16x4 col = {v[0][k], v[1][k], v[2][k], v[3][k]};
+          *(u16x4*)&sm.kt[buf][8 * cc + k][4 * rg] = col;
+        }
+      }
+    }
+  }
+};
+
+template <int D, bool BIAS>
+__global__ __launch_bounds__(NT, 1) void k_dq(Params p, BwdArgs a) {
+  constexpr int NS = D / 16;
+  constexpr int NB = D / 32;
+  __shared__ __attribute__((aligned(16))) SmemDQ<D> sm;
+
+  const int tid = threadIdx.x, w = tid >> 6, l = tid & 63, lr = l & 31, lg = l >> 5;
+  const int i0 = blockIdx.x * BQ3;
+  const int h = blockIdx.y, b = blockIdx.z, g = h / p.G;
+  const int Sq = p.Sq, Sk = p.Sk;
+  const int64_t irow = i0 + 32 * w + lr;       // this lane's query row
+  const float scale_log2 = p.scale * kLog2e;
+
+  const unsigned short* q = (const unsigned short*)a.q + b * p.q_str[0] + h * p.q_str[1];
+  const unsigned short* dout = (const unsigned short*)a.dout + b * p.do_str[0] + h * p.do_str[1];
+  const unsigned short* kp = (const unsigned short*)a.k + b * p.k_str[0] + g * p.k_str[1];
+  const unsigned short* vp = (const unsigned short*)a.v + b * p.v_str[0] + g * p.v_str[1];
+
+  bf16x8 qB[NS], doB[NS];
+#pragma unroll
+  for (int s = 0; s < NS; ++s) {
+    if (irow < Sq) {
+      qB[s] = as_bf16x8(*(const u16x8*)(q + irow * p.q_str[2] + 16 * s + 8 * lg));
+      doB[s] = as_bf16x8(*(const u16x8*)(dout + irow * p.do_str[2] + 16 * s + 8 * lg));
+    } else {
+      qB[s] = as_bf16x8(u16x8{0, 0, 0, 0, 0, 0, 0, 0});
+      doB[s] = qB[s];
+    }
+  }
+  float lse2 = INFINITY, dl = 0.f;
+  if (irow < Sq) {
+    const float lv = a.lse[((int64_t)b * p.Hq + h) * Sq + irow];
+    lse2 = (lv == -INFINITY) ? INFINITY : lv * kLog2e;
+    dl = a.delta[((int64_t)b * p.Hq + h) * Sq + irow];
+  }
+
+  // key tiles: the sink tiles [0, a1) and the band tiles [a2, a3)
+  int64_t s_hi, b_lo, b_hi;
+  const int i1 = min(i0 + BQ3, Sq);
+  p.mask.keys_for_rows(i0, i1, Sk, &s_hi, &b_lo, &b_hi);
+  const int a1 = (int)((s_hi + BK3 - 1) / BK3);
+  int a2 = (int)(b_lo / BK3);
+  const int a3 = b_hi > b_lo ? (int)((b_hi + BK3 - 1) / BK3) : a2;
+  if (a2 < a1) a2 = a1;
+  const int n1 = a1, n2 = a3 > a2 ? a3 - a2 : 0;
+  const int n_it = i0 < Sq ? n1 + n2 : 0;
+  auto tile_of = [&](int it) { return (int64_t)BK3 * (it < n1 ? it : a2 + (it - n1)); };
+
+  f32x16 dq[NB];
+#pragma unroll
+  for (int n = 0; n < NB; ++n) dq[n] = zero16();
+
+  StageKV<D> stg;
+  if (n_it > 0) {
+    stg.load(kp, vp, p.k_str[2], p.v_str[2], tile_of(0), Sk);
+    stg.store(sm, 0);
+    __syncthreads();
+  }
+  for (int it = 0; it < n_it; ++it) {
+    const int cur = it & 1;
+    const int64_t j0 = tile_of(it);
+    if (it + 1 < n_it) stg.load(kp, vp, p.k_str[2], p.v_str[2], tile_of(it + 1), Sk);
+
+    f32x16 sacc = zero16(), dpacc = zero16();
+#pragma unroll
+    for (int s = 0; s < NS; ++s) {
+      const bf16x8 ka = as_bf16x8(*(const u16x8*)&sm.k[cur][lr][16 * s + 8 * lg]);
+      const bf16x8 va = as_bf16x8(*(const u16x8*)&sm.v[cur][lr][16 * s + 8 * lg]);
+      sacc = mfma(ka, qB[s], sacc);
+      dpacc = mfma(va, doB[s], dpacc);
+    }
+    const bool full = (j0 + BK3 <= Sk) && p.mask.tile_full(i0 + 32 * w, i0 + 32 * w + 32, j0, j0 + BK3);
+    float dsv[16];
+#pragma unroll
+    for (int r = 0; r < 16; ++r) {
+      const int64_t j = j0 + crow(r, lg);
+      float x = sacc[r] * scale_log2;
+      if (BIAS) {
+        if (irow < Sq && j < Sk) x += a.bias[h * p.bias_str[0] + irow * p.bias_str[1] + j] * kLog2e;
+      }
+      float pp = exp2f(x - lse2);
+      if (!full && !(j < Sk && p.mask.allowed(irow, j))) pp = 0.f;
+      dsv[r] = pp * (dpacc[r] - dl);
+    }
+    const bf16x8 sa0 = pack8(dsv), sa1 = pack8(dsv + 8);
+#pragma unroll
+    for (int n = 0; n < NB; ++n) {
+      const int d = 32 * n + lr;
+      const bf16x8 k0v = cat44(*(const u16x4*)&sm.kt[cur][d][4 * lg], *(const u16x4*)&sm.kt[cur][d][8 + 4 * lg]);
+      const bf16x8 k1v = cat44(*(const u16x4*)&sm.kt[cur][d][16 + 4 * lg],
+                               *(const u16x4*)&sm.kt[cur][d][24 + 4 * lg]);
+      dq[n] = mfma(sa0, k0v, dq[n]);
+      dq[n] = mfma(sa1, k1v, dq[n]);
+    }
+    if (it + 1 < n_it) stg.store(sm, cur ^ 1);
+    __syncthreads();
+  }
+
+  // dQ rows i0 + 32 w + crow(r, lg), columns 32 n + lr.
+  float* dqp = a.dq + b * p.dq_str[0] + h * p.dq_str[1];
+#pragma unroll
+  for (int n = 0; n < NB; ++n) {
+#pragma unroll
+    for (int r = 0; r < 16; ++r) {
+      const int64_t i = i0 + 32 * w + crow(r, lg);
+      if (i < Sq) {
+        float* dst = dqp + i * p.dq_str[2] + 32 * n + lr;
+        const float val = dq[n][r] * p.scale;
+        *dst = a.accumulate_dq ? *dst + val : val;
+      }
+    }
+  }
+}
+
+template <int D>
+hipError_t launch_dq(const Params& p, const BwdArgs& a, hipStream_t st) {
+  const dim3 grid((p.Sq + BQ3 - 1) / BQ3, p.Hq, p.B);
+  if (a.bias)
+    hipLaunchKernelGGL((k_dq<D, true>), grid, dim3(NT), 0, st, p, a);
+  else
+    hipLaunchKernelGGL((k_dq<D, false>), grid, dim3(NT), 0, st, p, a);
+  return hipGetLastError();
+}
+
+bool aligned16(const void* ptr) { return ((uintptr_t)ptr & 15u) == 0; }
+
+}  // namespace
+
+bool mfma_bwd_supported(const Params& p) {
+  if (p.Dqk != p.Dv || (p.Dqk != 64 && p.Dqk != 128)) return false;
+  // 16-byte row loads need every row stride to be a multiple of 8 elements
+  const int64_t* s[] = {p.q_str, p.k_str, p.v_str, p.do_str};
+  for (const int64_t* x : s)
+    for (int i = 0; i < 3; ++i)
+      if (x[i] % 8 != 0) return false;
+  return true;
+}
+
+hipError_t launch_bwd_mfma(const Params& p, const BwdArgs& a, hipStream_t st) {
+  if (!aligned16(a.q) || !aligned16(a.k) || !aligned16(a.v) || !aligned16(a.dout))
+    return launch_bwd_simt(p, a, 1, st);
+  const bool bias = a.bias != nullptr;
+  const bool dq_atomic = !a.deterministic;
+  // dbias summed over the batch in a fixed order: one workgroup walks the batch
+  const bool bloop = a.dbias != nullptr && a.deterministic;
+  hipError_t e = hipSuccess;
+  if (dq_atomic && !a.accumulate_dq) {
+    e = launch_zero_rows(a.dq, p.B, p.Hq, p.Sq, p.Dqk, p.dq_str, st);
+    if (e != hipSuccess) return e;
+  }
+  if (p.Sk > 0 && p.B > 0) {
+    e = p.Dqk == 64 ? dispatch_dkdv<64>(p, a, bias, dq_atomic, bloop, st)
+                    : dispatch_dkdv<128>(p, a, bias, dq_atomic, bloop, st);
+    if (e != hipSuccess) return e;
+  } else if (dq_atomic) {
+    return hipSuccess;
+  }
+  if (!dq_atomic && p.Sq > 0 && p.B > 0)
+    return p.Dqk == 64 ? launch_dq<64>(p, a, st) : launch_dq<128>(p, a, st);
+  return hipSuccess;
+}
 
 }  // namespace attn

@@ -336,6 +336,10 @@ hipError_t launch_bwd_simt(const Params& p, const BwdArgs& a, int in_bf16, hipSt
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
   }
+  return launch_dq_simt(p, a, in_bf16, st);
+}
+
+hipError_t launch_dq_simt(const Params& p, const BwdArgs& a, int in_bf16, hipStream_t st) {
   if (p.Sq > 0 && p.B > 0) {
     const dim3 grid((p.Sq + kT - 1) / kT, p.Hq, p.B);
     if (in_bf16)

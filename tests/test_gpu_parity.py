@@ -110,6 +110,9 @@ SMALL = [
     (2, 2, 1, 257, 129, 64, 64, "bf16", MaskSpec("bottom_right"), False, False),   # empty rows
     (1, 2, 2, 1, 513, 128, 128, "bf16", MaskSpec("none"), False, False),
     (1, 8, 8, 129, 1, 64, 64, "bf16", MaskSpec("none"), False, False),
+    (1, 4, 2, 96, 112, 128, 64, "bf16", MaskSpec("top_left"), False, True),      # Dqk != Dv
+    (3, 4, 4, 640, 640, 64, 64, "bf16", MaskSpec("none"), True, False),           # batch-ordered dbias
+    (1, 32, 8, 1100, 1100, 128, 128, "bf16", MaskSpec("bottom_right"), False, False),
 ]
 
 
