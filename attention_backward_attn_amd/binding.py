@@ -19,7 +19,7 @@ LIB_PATH = os.path.join(HERE, "libattnbwd.so")
 ATTN_OK, ATTN_EINVAL, ATTN_EUNSUPPORTED, ATTN_EHIP = 0, -1, -2, -3
 ATTN_F32, ATTN_BF16 = 0, 1
 MASKS = {"none": 0, "top_left": 1, "bottom_right": 2}
-ATTN_DETERMINISTIC, ATTN_ACCUMULATE_DQ = 1, 2
+ATTN_DETERMINISTIC, ATTN_ACCUMULATE_DQ, ATTN_ACCUMULATE_DKDV = 1, 2, 4
 
 EXPORTED = ("attn_problem_init", "attn_fwd_lse", "attn_bwd_preprocess", "attn_bwd",
             "attn_lse_merge", "attn_status_string")
@@ -66,7 +66,7 @@ def lib() -> ctypes.CDLL:
         L.attn_problem_init.restype = None
         L.attn_fwd_lse.argtypes = [P, vp, vp, vp, vp, vp, vp, vp, vp]
         L.attn_fwd_lse.restype = i32
-        L.attn_bwd_preprocess.argtypes = [P, vp, vp, vp, vp, vp, vp, vp, vp]
+        L.attn_bwd_preprocess.argtypes = [P, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp]
         L.attn_bwd_preprocess.restype = i32
         L.attn_bwd.argtypes = [P, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, ctypes.c_uint32, vp]
         L.attn_bwd.restype = i32
@@ -156,10 +156,12 @@ def attn_fwd_lse(p: attn_problem_t, q, k, v, bias, sinks, o, lse, stream=None):
                                               _ptr(sinks), _ptr(o), _ptr(lse), _stream(stream)))
 
 
-def attn_bwd_preprocess(p: attn_problem_t, o, do, lse, sinks, delta, dsinks, dq_zero=None, stream=None):
+def attn_bwd_preprocess(p: attn_problem_t, o, do, lse, sinks, delta, dsinks, dq_zero=None, dk_zero=None,
+                        dv_zero=None, stream=None):
     _check("attn_bwd_preprocess",
            lib().attn_bwd_preprocess(ctypes.byref(p), _ptr(o), _ptr(do), _ptr(lse), _ptr(sinks),
-                                     _ptr(delta), _ptr(dsinks), _ptr(dq_zero), _stream(stream)))
+                                     _ptr(delta), _ptr(dsinks), _ptr(dq_zero), _ptr(dk_zero), _ptr(dv_zero),
+                                     _stream(stream)))
 
 
 def attn_bwd(p: attn_problem_t, q, k, v, do, lse, delta, bias, dq, dk, dv, dbias, flags: int = 0,
@@ -206,6 +208,6 @@ def backward(q, k, v, o, do, lse, *, bias=None, sinks=None, want_dbias=False, fl
     dsinks = torch.empty(Hq, device=dev, dtype=torch.float32) if sinks is not None else None
     dbias = torch.empty(bias.shape, device=dev, dtype=torch.float32) if (want_dbias and bias is not None) else None
     p = make_problem(q, k, v, o=o, do=do, dq=dq, dk=dk, dv=dv, bias=bias, **mask_kw)
-    attn_bwd_preprocess(p, o, do, lse, sinks, delta, dsinks, None, stream)
+    attn_bwd_preprocess(p, o, do, lse, sinks, delta, dsinks, None, None, None, stream)
     attn_bwd(p, q, k, v, do, lse, delta, bias, dq, dk, dv, dbias, flags, stream)
     return {"dq": dq, "dk": dk, "dv": dv, "dbias": dbias, "dsinks": dsinks, "delta": delta}

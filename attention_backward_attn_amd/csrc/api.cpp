@@ -124,11 +124,12 @@ attn_status_t attn_fwd_lse(const attn_problem_t* p, const void* q, const void* k
 
 attn_status_t attn_bwd_preprocess(const attn_problem_t* p, const void* o, const void* dout,
                                   const float* lse, const float* sinks, float* delta, float* dsinks,
-                                  float* dq_zero, void* stream) {
+                                  float* dq_zero, float* dk_zero, float* dv_zero, void* stream) {
   attn_status_t st = check_problem(p);
   if (st != ATTN_OK) return st;
   if (!strides_ok(p->o_str) || !strides_ok(p->do_str)) return ATTN_EINVAL;
   if (dq_zero && !strides_ok(p->dq_str)) return ATTN_EINVAL;
+  if ((dk_zero && !strides_ok(p->dk_str)) || (dv_zero && !strides_ok(p->dv_str))) return ATTN_EINVAL;
   if ((sinks == nullptr) != (dsinks == nullptr)) return ATTN_EINVAL;
   const bool empty = p->B == 0 || p->Sq == 0;
   if (!empty && (!o || !dout || !delta)) return ATTN_EINVAL;
@@ -140,6 +141,13 @@ attn_status_t attn_bwd_preprocess(const attn_problem_t* p, const void* o, const 
                                       p->dq_str, s);
     if (e != hipSuccess) return ATTN_EHIP;
   }
+  if (dk_zero || dv_zero) {
+    attn::ZeroRows z[2];
+    int nz = 0;
+    if (dk_zero) z[nz++] = attn::ZeroRows{dk_zero, p->B, p->Hk, p->Sk, p->Dqk, {p->dk_str[0], p->dk_str[1], p->dk_str[2]}};
+    if (dv_zero) z[nz++] = attn::ZeroRows{dv_zero, p->B, p->Hk, p->Sk, p->Dv, {p->dv_str[0], p->dv_str[1], p->dv_str[2]}};
+    if (attn::launch_zero_multi(z, nz, s) != hipSuccess) return ATTN_EHIP;
+  }
   if (sinks) return hip_status(attn::launch_dsinks(lse, delta, sinks, dsinks, p->B, p->Hq, p->Sq, s));
   return ATTN_OK;
 }
@@ -149,7 +157,8 @@ attn_status_t attn_bwd(const attn_problem_t* p, const void* q, const void* k, co
                        float* dq, float* dk, float* dv, float* dbias, uint32_t flags, void* stream) {
   attn_status_t st = check_problem(p);
   if (st != ATTN_OK) return st;
-  if ((flags & ~(uint32_t)(ATTN_DETERMINISTIC | ATTN_ACCUMULATE_DQ)) != 0) return ATTN_EINVAL;
+  if ((flags & ~(uint32_t)(ATTN_DETERMINISTIC | ATTN_ACCUMULATE_DQ | ATTN_ACCUMULATE_DKDV)) != 0)
+    return ATTN_EINVAL;
   if (!strides_ok(p->q_str) || !strides_ok(p->k_str) || !strides_ok(p->v_str) || !strides_ok(p->do_str) ||
       !strides_ok(p->dq_str) || !strides_ok(p->dk_str) || !strides_ok(p->dv_str))
     return ATTN_EINVAL;
@@ -164,7 +173,8 @@ attn_status_t attn_bwd(const attn_problem_t* p, const void* q, const void* k, co
 
   Params kp = make_params(p);
   attn::BwdArgs a{q, k, v, dout, lse, delta, bias, dq, dk, dv, dbias,
-                  (flags & ATTN_ACCUMULATE_DQ) ? 1 : 0, (flags & ATTN_DETERMINISTIC) ? 1 : 0};
+                  (flags & ATTN_ACCUMULATE_DQ) ? 1 : 0, (flags & ATTN_DETERMINISTIC) ? 1 : 0,
+                  (flags & ATTN_ACCUMULATE_DKDV) ? 1 : 0};
   hipStream_t s = (hipStream_t)stream;
   if (p->in_dtype == ATTN_BF16) {
     if (!attn::mfma_bwd_supported(kp)) {

@@ -29,8 +29,16 @@ struct BwdArgs {
   float* dk;
   float* dv;
   float* dbias;       // nullable
-  int accumulate_dq;  // add into dq instead of overwriting
+  int accumulate_dq;    // add into dq instead of overwriting
   int deterministic;
+  int accumulate_dkdv;  // add into dk / dv instead of overwriting
+};
+
+// A strided [B, H, S, D] fp32 tensor (D contiguous) to be zeroed.
+struct ZeroRows {
+  float* p;
+  int B, H, S, D;
+  int64_t str[3];
 };
 
 // delta = rowsum(dO * O); when dq_zero is non-null its rows are zeroed in the same pass.
@@ -40,6 +48,8 @@ hipError_t launch_delta(const void* o, int o_bf16, const void* dout, int do_bf16
 hipError_t launch_dsinks(const float* lse, const float* delta, const float* sinks, float* dsinks,
                          int B, int H, int Sq, hipStream_t st);
 hipError_t launch_zero_rows(float* x, int B, int H, int S, int D, const int64_t* str, hipStream_t st);
+// Zero up to three tensors in one launch (n == 0: nothing is launched).
+hipError_t launch_zero_multi(const ZeroRows* z, int n, hipStream_t st);
 hipError_t launch_zero_bias(float* x, int H, int Sq, int Sk, const int64_t* str, hipStream_t st);
 hipError_t launch_lse_merge(int64_t rows, int Dv, float* o_acc, float* lse_acc, const float* o_part,
                             const float* lse_part, hipStream_t st);

@@ -94,6 +94,11 @@ __global__ __launch_bounds__(256) void k_dsinks(const float* __restrict__ lse,
   if (threadIdx.x == 0) dsinks[h] = -red[0];
 }
 
+static unsigned fill_blocks(int64_t n) {
+  int64_t b = (n + 255) / 256;
+  return (unsigned)(b > 16384 ? 16384 : (b < 1 ? 1 : b));
+}
+
 // Zero rows of a strided [B, H, S, D] fp32 tensor (D contiguous).
 __global__ __launch_bounds__(256) void k_zero_rows(float* __restrict__ x, int B, int H, int S, int D,
                                                    int64_t sb, int64_t sh, int64_t ss) {
@@ -106,6 +111,56 @@ __global__ __launch_bounds__(256) void k_zero_rows(float* __restrict__ x, int B,
     const int b = (int)(r / ((int64_t)S * H));
     x[b * sb + h * sh + i * ss + d] = 0.f;
   }
+}
+
+// Zero up to three strided row tensors: the flat element range of tensor k
+// starts at off[k]; rows of D % 4 == 0 tensors are written 4 floats at a time.
+struct ZeroMulti {
+  ZeroRows z[3];
+  int64_t off[4];  // element offsets (in units of 4-float groups where vec)
+  int vec[3];
+  int n;
+};
+
+__global__ __launch_bounds__(256) void k_zero_multi(ZeroMulti m) {
+  const int64_t total = m.off[m.n];
+  for (int64_t e = (int64_t)blockIdx.x * 256 + threadIdx.x; e < total; e += (int64_t)gridDim.x * 256) {
+    int k = 0;
+    while (k + 1 < m.n && e >= m.off[k + 1]) ++k;
+    const ZeroRows& z = m.z[k];
+    const int64_t x = e - m.off[k];
+    const int w = m.vec[k] ? z.D / 4 : z.D;
+    const int d = (int)(x % w);
+    const int64_t r = x / w;
+    const int i = (int)(r % z.S);
+    const int h = (int)((r / z.S) % z.H);
+    const int b = (int)(r / ((int64_t)z.S * z.H));
+    float* row = z.p + b * z.str[0] + h * z.str[1] + i * z.str[2];
+    if (m.vec[k])
+      *(float4*)(row + 4 * d) = make_float4(0.f, 0.f, 0.f, 0.f);
+    else
+      row[d] = 0.f;
+  }
+}
+
+hipError_t launch_zero_multi(const ZeroRows* z, int n, hipStream_t st) {
+  ZeroMulti m{};
+  int k = 0;
+  m.off[0] = 0;
+  for (int i = 0; i < n; ++i) {
+    const int64_t rows = (int64_t)z[i].B * z[i].H * z[i].S;
+    if (rows == 0 || z[i].D == 0) continue;
+    m.z[k] = z[i];
+    const bool aligned = ((uintptr_t)z[i].p % 16 == 0) && z[i].str[0] % 4 == 0 && z[i].str[1] % 4 == 0 &&
+                         z[i].str[2] % 4 == 0;
+    m.vec[k] = (z[i].D % 4 == 0 && aligned) ? 1 : 0;
+    m.off[k + 1] = m.off[k] + rows * (m.vec[k] ? z[i].D / 4 : z[i].D);
+    ++k;
+  }
+  m.n = k;
+  if (k == 0) return hipSuccess;
+  hipLaunchKernelGGL(k_zero_multi, dim3(fill_blocks(m.off[k])), dim3(256), 0, st, m);
+  return hipGetLastError();
 }
 
 // Zero a strided [H, Sq, Sk] fp32 tensor (Sk contiguous).
@@ -199,11 +254,6 @@ hipError_t launch_dsinks(const float* lse, const float* delta, const float* sink
                          int B, int H, int Sq, hipStream_t st) {
   hipLaunchKernelGGL(k_dsinks, dim3(H), dim3(256), 0, st, lse, delta, sinks, dsinks, B, H, Sq);
   return hipGetLastError();
-}
-
-static unsigned fill_blocks(int64_t n) {
-  int64_t b = (n + 255) / 256;
-  return (unsigned)(b > 16384 ? 16384 : (b < 1 ? 1 : b));
 }
 
 hipError_t launch_zero_rows(float* x, int B, int H, int S, int D, const int64_t* str, hipStream_t st) {

@@ -75,8 +75,12 @@ struct SmemDKDV {
   float delta[2][BQ];
 };
 
-// Per-thread staging of one 32-row Q / dO tile: thread t < 2 * nch handles
-// rows 4 rg .. 4 rg + 3, columns 8 cc .. 8 cc + 7 of Q (t < nch) or dO.
+// Per-thread staging of one 32-row Q / dO tile: thread t < 2 * NCH handles
+// rows 4 rg .. 4 rg + 3, columns 8 cc .. 8 cc + 7 of Q (t < NCH) or dO; the
+// last 32 threads carry the tile's LSE and delta.  load() only issues the
+// global loads (rows clamped into range, so no branches and no use of the
+// values); store() fixes up rows past the end and writes LDS.  This keeps
+// the loads in flight across the whole iteration that prefetches them.
 template <int D>
 struct Stage {
   static constexpr int NCH = (BQ / 4) * (D / 8);
@@ -93,263 +97,324 @@ struct Stage {
       const int64_t st = t < NCH ? qs : ds;
 #pragma unroll
       for (int e = 0; e < 4; ++e) {
-        const int64_t i = i0 + 4 * rg + e;
-        if (i < Sq) {
-          v[e] = *(const u16x8*)(base + i * st + 8 * cc);
-        } else {
-          v[e] = u16x8{0, 0, 0, 0, 0, 0, 0, 0};
-        }
+        const int64_t i = min(i0 + 4 * rg + e, (int64_t)Sq - 1);
+        v[e] = *(const u16x8*)(base + i * st + 8 * cc);
       }
     }
     if (t >= NT - BQ) {
-      const int r = t - (NT - BQ);
-      const int64_t i = i0 + r;
-      const float l = (i < Sq) ? lse_p[i] : -INFINITY;
-      lse = (l == -INFINITY) ? INFINITY : l * kLog2e;
-      dl = (i < Sq) ? dl_p[i] : 0.f;
+      const int64_t i = min(i0 + (t - (NT - BQ)), (int64_t)Sq - 1);
+      lse = lse_p[i];
+      dl = dl_p[i];
     }
   }
 
-  __device__ inline void store(SmemDKDV<D>& sm, int buf) const {
+  __device__ inline void store(SmemDKDV<D>& sm, int buf, int64_t i0, int Sq) const {
     const int t = threadIdx.x;
     if (t < 2 * NCH) {
       const int c = t < NCH ? t : t - NCH;
       const int rg = c / (D / 8), cc = c % (D / 8);
       unsigned short(*rowm)[D + 8] = t < NCH ? sm.q[buf] : sm.dO[buf];
       unsigned short(*colm)[TP] = t < NCH ? sm.qt[buf] : sm.dOt[buf];
+      u16x8 x[4];
 #pragma unroll
-      for (int e = 0; e < 4; ++e) *(u16x8*)&rowm[4 * rg + e][8 * cc] = v[e];
+      for (int e = 0; e < 4; ++e) {
+        const bool ok = i0 + 4 * rg + e < Sq;
+#pragma unroll
+        for (int k = 0; k < 8; ++k) x[e][k] = ok ? v[e][k] : (unsigned short)0;
+        *(u16x8*)&rowm[4 * rg + e][8 * cc] = x[e];
+      }
 #pragma unroll
       for (int k = 0; k < 8; ++k) {
-        u16x4 col = {v[0][k], v[1][k], v[2][k], v[3][k]};
+        u16x4 col = {x[0][k], x[1][k], x[2][k], x[3][k]};
         *(u16x4*)&colm[8 * cc + k][4 * rg] = col;
       }
     }
     if (t >= NT - BQ) {
       const int r = t - (NT - BQ);
-      sm.lse2[buf][r] = lse;
-      sm.delta[buf][r] = dl;
+      const bool ok = i0 + r < Sq;
+      sm.lse2[buf][r] = (!ok || lse == -INFINITY) ? INFINITY : lse * kLog2e;
+      sm.delta[buf][r] = ok ? dl : 0.f;
     }
   }
 };
 
+// How a dK/dV accumulator reaches global memory.
+enum : int { kStore = 0, kAtomicAdd = 1, kAddInto = 2 };
+
+// Work of one workgroup: key block(s) `kb0` (and `nkb - 1 - kb0` when
+// paired), query heads [h_begin, h_end) of KV head hk.
+//
+// Pairing: under a causal mask the number of query rows that see key block
+// kb falls linearly with kb, so block kb and block nkb-1-kb together cost the
+// same for every pair -- one pair per workgroup balances the grid.
+// Head split: the G query heads of a group may be split in two halves
+// handled by two workgroups; each adds its partial dK/dV into zeroed
+// outputs.  With exactly two addends onto zero the fp32 result does not
+// depend on their order, so the result stays deterministic.
 template <int D, bool BIAS, bool DQ_ATOMIC, bool BLOOP>
-__global__ __launch_bounds__(NT, 1) void k_dkdv(Params p, BwdArgs a) {
+__global__ __launch_bounds__(NT, 1) void k_dkdv(Params p, BwdArgs a, int pair, int hsplit, int out_mode) {
   static_assert(D == 64 || D == 128, "head dim");
   constexpr int NS = D / 16;          // k-steps over the head dim
   constexpr int NB = D / 32;          // 32-column blocks of the head dim
   __shared__ __attribute__((aligned(16))) SmemDKDV<D> sm;
 
   const int tid = threadIdx.x, w = tid >> 6, l = tid & 63, lr = l & 31, lg = l >> 5;
-  const int k0 = blockIdx.x * BK;
-  const int hk = blockIdx.y;
-  const int kw = k0 + 32 * w;         // first key of this wave
-  const int jkey = kw + lr;           // this lane's key (accumulator column of S / dP)
   const int Sq = p.Sq, Sk = p.Sk;
+  const int nkb = (Sk + BK - 1) / BK;
+  const int hk = blockIdx.y / hsplit;
+  const int part = blockIdx.y % hsplit;
+  const int gh = p.G / hsplit;                     // query heads handled here
+  const int h_begin = hk * p.G + part * gh;
   const float scale_log2 = p.scale * kLog2e;
-
-  int64_t lo, hi;
-  p.mask.rows_for_keys(k0, min(k0 + BK, Sk), Sq, &lo, &hi);
-  const int64_t lo_al = lo & ~(int64_t)(BQ - 1);
-  const int nqb = hi > lo ? (int)((hi - lo_al + BQ - 1) / BQ) : 0;
-  const int n_it = p.G * nqb;
-  const bool wave_keys_in = kw + 32 <= Sk;
   const bool dq_wave = DQ_ATOMIC && (w < NB);
+  const int kbx = blockIdx.x;
+  const int n_units = (pair && nkb - 1 - kbx != kbx) ? 2 : 1;
 
   const int b_begin = BLOOP ? 0 : blockIdx.z;
   const int b_end = BLOOP ? p.B : b_begin + 1;
   for (int b = b_begin; b < b_end; ++b) {
-    const unsigned short* kp = (const unsigned short*)a.k + b * p.k_str[0] + hk * p.k_str[1];
-    const unsigned short* vp = (const unsigned short*)a.v + b * p.v_str[0] + hk * p.v_str[1];
-    // K / V fragments of this wave's keys (B operands of S and dP).
-    bf16x8 kB[NS], vB[NS];
-#pragma unroll
-    for (int s = 0; s < NS; ++s) {
-      if (jkey < Sk) {
-        kB[s] = as_bf16x8(*(const u16x8*)(kp + (int64_t)jkey * p.k_str[2] + 16 * s + 8 * lg));
-        vB[s] = as_bf16x8(*(const u16x8*)(vp + (int64_t)jkey * p.v_str[2] + 16 * s + 8 * lg));
-      } else {
-        kB[s] = as_bf16x8(u16x8{0, 0, 0, 0, 0, 0, 0, 0});
-        vB[s] = kB[s];
-      }
-    }
-    // K^T fragments (B operand of dQ = dS K): keys 16 t + 8 lg + e, column 32 w + lr.
-    bf16x8 ktB[BK / 16];
-    if (dq_wave) {
-#pragma unroll
-      for (int t = 0; t < BK / 16; ++t) {
-        u16x8 u;
-#pragma unroll
-        for (int e = 0; e < 8; ++e) {
-          const int j = k0 + 16 * t + 8 * lg + e;
-          u[e] = (j < Sk) ? kp[(int64_t)j * p.k_str[2] + 32 * w + lr] : (unsigned short)0;
-        }
-        ktB[t] = as_bf16x8(u);
-      }
-    }
-    f32x16 dk[NB], dv[NB];
-#pragma unroll
-    for (int n = 0; n < NB; ++n) { dk[n] = zero16(); dv[n] = zero16(); }
+    for (int u = 0; u < n_units; ++u) {
+      const int kb = u == 0 ? kbx : nkb - 1 - kbx;
+      const int k0 = kb * BK;
+      const int kw = k0 + 32 * w;     // first key of this wave
+      const int jkey = kw + lr;       // this lane's key (accumulator column of S / dP)
+      const bool wave_keys_in = kw + 32 <= Sk;
+      int64_t lo, hi;
+      p.mask.rows_for_keys(k0, min(k0 + BK, Sk), Sq, &lo, &hi);
+      const int64_t lo_al = lo & ~(int64_t)(BQ - 1);
+      const int nqb = hi > lo ? (int)((hi - lo_al + BQ - 1) / BQ) : 0;
+      const int n_it = gh * nqb;
 
-    Stage<D> stg;
-    auto tile_ptrs = [&](int it, const unsigned short** q, const unsigned short** dout, const float** lse_p,
-                         const float** dl_p, int* h, int64_t* i0) {
-      *h = hk * p.G + it / nqb;
-      *i0 = lo_al + (int64_t)BQ * (it % nqb);
-      *q = (const unsigned short*)a.q + b * p.q_str[0] + *h * p.q_str[1];
-      *dout = (const unsigned short*)a.dout + b * p.do_str[0] + *h * p.do_str[1];
-      *lse_p = a.lse + ((int64_t)b * p.Hq + *h) * Sq;
-      *dl_p = a.delta + ((int64_t)b * p.Hq + *h) * Sq;
-    };
-    if (n_it > 0) {
-      const unsigned short *q, *dout;
-      const float *lse_p, *dl_p;
-      int h;
-      int64_t i0;
-      tile_ptrs(0, &q, &dout, &lse_p, &dl_p, &h, &i0);
-      __syncthreads();  // previous batch's readers of buffer 0 are done
-      stg.load(q, dout, p.q_str[2], p.do_str[2], lse_p, dl_p, i0, Sq);
-      stg.store(sm, 0);
-      __syncthreads();
-    }
-
-    for (int it = 0; it < n_it; ++it) {
-      const int cur = it & 1;
-      const unsigned short *q, *dout;
-      const float *lse_p, *dl_p;
-      int h;
-      int64_t i0;
-      tile_ptrs(it, &q, &dout, &lse_p, &dl_p, &h, &i0);
-      if (it + 1 < n_it) {
-        const unsigned short *q1, *d1;
-        const float *l1, *dl1;
-        int h1;
-        int64_t i1;
-        tile_ptrs(it + 1, &q1, &d1, &l1, &dl1, &h1, &i1);
-        stg.load(q1, d1, p.q_str[2], p.do_str[2], l1, dl1, i1, Sq);
-      }
-
-      // S = Q K^T and dP = dO V^T for rows i0..i0+31, this wave's 32 keys.
-      f32x16 sacc = zero16(), dpacc = zero16();
+      const unsigned short* kp = (const unsigned short*)a.k + b * p.k_str[0] + hk * p.k_str[1];
+      const unsigned short* vp = (const unsigned short*)a.v + b * p.v_str[0] + hk * p.v_str[1];
+      // K / V fragments of this wave's keys (B operands of S and dP).
+      bf16x8 kB[NS], vB[NS];
+      {
+        const int64_t jc = min(jkey, Sk - 1);
+        const bool ok = jkey < Sk;
 #pragma unroll
-      for (int s = 0; s < NS; ++s) {
-        const bf16x8 qa = as_bf16x8(*(const u16x8*)&sm.q[cur][lr][16 * s + 8 * lg]);
-        const bf16x8 da = as_bf16x8(*(const u16x8*)&sm.dO[cur][lr][16 * s + 8 * lg]);
-        sacc = mfma(qa, kB[s], sacc);
-        dpacc = mfma(da, vB[s], dpacc);
-      }
-
-      // P = exp(S - LSE) on allowed pairs, dS = P (dP - delta).
-      const bool full = wave_keys_in && p.mask.tile_full(i0, i0 + BQ, kw, kw + 32);
-      float pv[16], dsv[16];
+        for (int s = 0; s < NS; ++s) {
+          u16x8 kk = *(const u16x8*)(kp + jc * p.k_str[2] + 16 * s + 8 * lg);
+          u16x8 vv = *(const u16x8*)(vp + jc * p.v_str[2] + 16 * s + 8 * lg);
 #pragma unroll
-      for (int r = 0; r < 16; ++r) {
-        const int row = crow(r, lg);
-        const int64_t i = i0 + row;
-        float x = sacc[r] * scale_log2;
-        if (BIAS) {
-          if (i < Sq && jkey < Sk) x += a.bias[h * p.bias_str[0] + i * p.bias_str[1] + jkey] * kLog2e;
-        }
-        float pp = exp2f(x - sm.lse2[cur][row]);
-        if (!full && !(jkey < Sk && p.mask.allowed(i, jkey))) pp = 0.f;
-        pv[r] = pp;
-        dsv[r] = pp * (dpacc[r] - sm.delta[cur][row]);
-      }
-      if (BIAS && a.dbias) {
-#pragma unroll
-        for (int r = 0; r < 16; ++r) {
-          const int64_t i = i0 + crow(r, lg);
-          if (i < Sq && jkey < Sk && pv[r] != 0.f) {
-            float* dst = a.dbias + h * p.bias_str[0] + i * p.bias_str[1] + jkey;
-            if (BLOOP)
-              *dst += dsv[r];
-            else
-              atomic_add_f32(dst, dsv[r]);
+          for (int e = 0; e < 8; ++e) {
+            kk[e] = ok ? kk[e] : (unsigned short)0;
+            vv[e] = ok ? vv[e] : (unsigned short)0;
           }
+          kB[s] = as_bf16x8(kk);
+          vB[s] = as_bf16x8(vv);
         }
       }
-      const bf16x8 pa0 = pack8(pv), pa1 = pack8(pv + 8);
-      const bf16x8 sa0 = pack8(dsv), sa1 = pack8(dsv + 8);
-
-      // dV += P^T dO and dK += dS^T Q (reduction over the 32 rows, permuted
-      // consistently with the accumulator layout of S).
+      // K^T fragments (B operand of dQ = dS K): keys 16 t + 8 lg + e, column 32 w + lr.
+      bf16x8 ktB[BK / 16];
+      if (dq_wave) {
 #pragma unroll
-      for (int n = 0; n < NB; ++n) {
-        const int d = 32 * n + lr;
-        const bf16x8 o0 = cat44(*(const u16x4*)&sm.dOt[cur][d][4 * lg], *(const u16x4*)&sm.dOt[cur][d][8 + 4 * lg]);
-        const bf16x8 o1 = cat44(*(const u16x4*)&sm.dOt[cur][d][16 + 4 * lg],
-                                *(const u16x4*)&sm.dOt[cur][d][24 + 4 * lg]);
-        dv[n] = mfma(pa0, o0, dv[n]);
-        dv[n] = mfma(pa1, o1, dv[n]);
-        const bf16x8 q0 = cat44(*(const u16x4*)&sm.qt[cur][d][4 * lg], *(const u16x4*)&sm.qt[cur][d][8 + 4 * lg]);
-        const bf16x8 q1 = cat44(*(const u16x4*)&sm.qt[cur][d][16 + 4 * lg], *(const u16x4*)&sm.qt[cur][d][24 + 4 * lg]);
-        dk[n] = mfma(sa0, q0, dk[n]);
-        dk[n] = mfma(sa1, q1, dk[n]);
-      }
-
-      if (DQ_ATOMIC) {
-        // dS (bf16) to LDS, row-major [row][key in block].
-        const __bf16* dsb = (const __bf16*)&sa0;
-        const __bf16* dsb1 = (const __bf16*)&sa1;
+        for (int t = 0; t < BK / 16; ++t) {
+          u16x8 uu;
 #pragma unroll
-        for (int r = 0; r < 16; ++r) {
-          const __bf16 v = r < 8 ? dsb[r] : dsb1[r - 8];
-          sm.ds[crow(r, lg)][32 * w + lr] = __builtin_bit_cast(unsigned short, v);
+          for (int e = 0; e < 8; ++e) {
+            const int j = k0 + 16 * t + 8 * lg + e;
+            const unsigned short x = kp[(int64_t)min(j, Sk - 1) * p.k_str[2] + 32 * w + lr];
+            uu[e] = (j < Sk) ? x : (unsigned short)0;
+          }
+          ktB[t] = as_bf16x8(uu);
         }
+      }
+      f32x16 dk[NB], dv[NB];
+#pragma unroll
+      for (int n = 0; n < NB; ++n) { dk[n] = zero16(); dv[n] = zero16(); }
+
+      Stage<D> stg;
+      auto tile = [&](int it, int* h, int64_t* i0) {
+        *h = h_begin + it / nqb;
+        *i0 = lo_al + (int64_t)BQ * (it % nqb);
+      };
+      auto issue = [&](int it) {
+        int h;
+        int64_t i0;
+        tile(it, &h, &i0);
+        stg.load((const unsigned short*)a.q + b * p.q_str[0] + h * p.q_str[1],
+                 (const unsigned short*)a.dout + b * p.do_str[0] + h * p.do_str[1], p.q_str[2], p.do_str[2],
+                 a.lse + ((int64_t)b * p.Hq + h) * Sq, a.delta + ((int64_t)b * p.Hq + h) * Sq, i0, Sq);
+      };
+      if (n_it > 0) {
+        int h;
+        int64_t i0;
+        tile(0, &h, &i0);
+        issue(0);
+        __syncthreads();  // readers of buffer 0 from the previous unit are done
+        stg.store(sm, 0, i0, Sq);
         __syncthreads();
-        if (dq_wave) {
-          f32x16 qacc = zero16();
+      }
+
+      for (int it = 0; it < n_it; ++it) {
+        const int cur = it & 1;
+        int h;
+        int64_t i0;
+        tile(it, &h, &i0);
+        if (it + 1 < n_it) issue(it + 1);
+
+        // S = Q K^T and dP = dO V^T for rows i0..i0+31, this wave's 32 keys.
+        f32x16 sacc = zero16(), dpacc = zero16();
 #pragma unroll
-          for (int t = 0; t < BK / 16; ++t) {
-            const bf16x8 da = as_bf16x8(*(const u16x8*)&sm.ds[lr][16 * t + 8 * lg]);
-            qacc = mfma(da, ktB[t], qacc);
+        for (int s = 0; s < NS; ++s) {
+          const bf16x8 qa = as_bf16x8(*(const u16x8*)&sm.q[cur][lr][16 * s + 8 * lg]);
+          const bf16x8 da = as_bf16x8(*(const u16x8*)&sm.dO[cur][lr][16 * s + 8 * lg]);
+          sacc = mfma(qa, kB[s], sacc);
+          dpacc = mfma(da, vB[s], dpacc);
+        }
+
+        // P = exp(S - LSE) on allowed pairs, dS = P (dP - delta).
+        const bool full = wave_keys_in && p.mask.tile_full(i0, i0 + BQ, kw, kw + 32);
+        float pv[16], dsv[16];
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+          const int row = crow(r, lg);
+          const int64_t i = i0 + row;
+          float x = sacc[r] * scale_log2;
+          if (BIAS) {
+            if (i < Sq && jkey < Sk) x += a.bias[h * p.bias_str[0] + i * p.bias_str[1] + jkey] * kLog2e;
           }
-          float* dq = a.dq + b * p.dq_str[0] + h * p.dq_str[1] + 32 * w + lr;
+          float pp = exp2f(x - sm.lse2[cur][row]);
+          if (!full && !(jkey < Sk && p.mask.allowed(i, jkey))) pp = 0.f;
+          pv[r] = pp;
+          dsv[r] = pp * (dpacc[r] - sm.delta[cur][row]);
+        }
+        if (BIAS && a.dbias) {
 #pragma unroll
           for (int r = 0; r < 16; ++r) {
             const int64_t i = i0 + crow(r, lg);
-            if (i >= lo && i < hi) atomic_add_f32(dq + i * p.dq_str[2], qacc[r] * p.scale);
+            if (i < Sq && jkey < Sk && pv[r] != 0.f) {
+              float* dst = a.dbias + h * p.bias_str[0] + i * p.bias_str[1] + jkey;
+              if (BLOOP)
+                *dst += dsv[r];
+              else
+                atomic_add_f32(dst, dsv[r]);
+            }
           }
         }
-      }
-      if (it + 1 < n_it) stg.store(sm, cur ^ 1);
-      __syncthreads();
-    }
+        const bf16x8 pa0 = pack8(pv), pa1 = pack8(pv + 8);
+        const bf16x8 sa0 = pack8(dsv), sa1 = pack8(dsv + 8);
 
-    // Epilogue: dK * scale and dV for this wave's keys (complete group sums).
-    float* dkp = a.dk + b * p.dk_str[0] + hk * p.dk_str[1];
-    float* dvp = a.dv + b * p.dv_str[0] + hk * p.dv_str[1];
+        // dV += P^T dO and dK += dS^T Q (reduction over the 32 rows, permuted
+        // consistently with the accumulator layout of S).
 #pragma unroll
-    for (int n = 0; n < NB; ++n) {
+        for (int n = 0; n < NB; ++n) {
+          const int d = 32 * n + lr;
+          const bf16x8 o0 = cat44(*(const u16x4*)&sm.dOt[cur][d][4 * lg], *(const u16x4*)&sm.dOt[cur][d][8 + 4 * lg]);
+          const bf16x8 o1 = cat44(*(const u16x4*)&sm.dOt[cur][d][16 + 4 * lg],
+                                  *(const u16x4*)&sm.dOt[cur][d][24 + 4 * lg]);
+          dv[n] = mfma(pa0, o0, dv[n]);
+          dv[n] = mfma(pa1, o1, dv[n]);
+          const bf16x8 q0 = cat44(*(const u16x4*)&sm.qt[cur][d][4 * lg], *(const u16x4*)&sm.qt[cur][d][8 + 4 * lg]);
+          const bf16x8 q1 = cat44(*(const u16x4*)&sm.qt[cur][d][16 + 4 * lg],
+                                  *(const u16x4*)&sm.qt[cur][d][24 + 4 * lg]);
+          dk[n] = mfma(sa0, q0, dk[n]);
+          dk[n] = mfma(sa1, q1, dk[n]);
+        }
+
+        if (DQ_ATOMIC) {
+          // dS (bf16) to LDS, row-major [row][key in block].
 #pragma unroll
-      for (int r = 0; r < 16; ++r) {
-        const int64_t j = kw + crow(r, lg);
-        if (j < Sk) {
-          dkp[j * p.dk_str[2] + 32 * n + lr] = dk[n][r] * p.scale;
-          dvp[j * p.dv_str[2] + 32 * n + lr] = dv[n][r];
+          for (int r = 0; r < 16; ++r) {
+            const __bf16 vv = r < 8 ? sa0[r] : sa1[r - 8];
+            sm.ds[crow(r, lg)][32 * w + lr] = __builtin_bit_cast(unsigned short, vv);
+          }
+          __syncthreads();
+          if (dq_wave) {
+            f32x16 qacc = zero16();
+#pragma unroll
+            for (int t = 0; t < BK / 16; ++t) {
+              const bf16x8 da = as_bf16x8(*(const u16x8*)&sm.ds[lr][16 * t + 8 * lg]);
+              qacc = mfma(da, ktB[t], qacc);
+            }
+            float* dq = a.dq + b * p.dq_str[0] + h * p.dq_str[1] + 32 * w + lr;
+#pragma unroll
+            for (int r = 0; r < 16; ++r) {
+              const int64_t i = i0 + crow(r, lg);
+              if (i >= lo && i < hi) atomic_add_f32(dq + i * p.dq_str[2], qacc[r] * p.scale);
+            }
+          }
+        }
+        if (it + 1 < n_it) {
+          int h1;
+          int64_t i1;
+          tile(it + 1, &h1, &i1);
+          stg.store(sm, cur ^ 1, i1, Sq);
+        }
+        __syncthreads();
+      }
+
+      // Epilogue: dK * scale and dV for this wave's keys.
+      float* dkp = a.dk + b * p.dk_str[0] + hk * p.dk_str[1];
+      float* dvp = a.dv + b * p.dv_str[0] + hk * p.dv_str[1];
+#pragma unroll
+      for (int n = 0; n < NB; ++n) {
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+          const int64_t j = kw + crow(r, lg);
+          if (j < Sk) {
+            float* pk = dkp + j * p.dk_str[2] + 32 * n + lr;
+            float* pvv = dvp + j * p.dv_str[2] + 32 * n + lr;
+            if (out_mode == kAtomicAdd) {
+              atomic_add_f32(pk, dk[n][r] * p.scale);
+              atomic_add_f32(pvv, dv[n][r]);
+            } else if (out_mode == kAddInto) {
+              *pk += dk[n][r] * p.scale;
+              *pvv += dv[n][r];
+            } else {
+              *pk = dk[n][r] * p.scale;
+              *pvv = dv[n][r];
+            }
+          }
         }
       }
     }
   }
 }
 
+// Grid shape of k_dkdv for a problem (host side).
+struct DkdvPlan {
+  int pair, hsplit, out_mode;
+  dim3 grid;
+};
+
+DkdvPlan plan_dkdv(const Params& p, bool bloop, bool accumulate_dkdv, bool deterministic) {
+  DkdvPlan pl{};
+  const int nkb = (p.Sk + BK - 1) / BK;
+  // causal-like masks (no lower window bound): work per key block decreases
+  // monotonically, so complementary blocks pair up evenly
+  pl.pair = (p.mask.kind != kMaskNone && p.mask.wl < 0 && nkb > 1) ? 1 : 0;
+  const int xblocks = pl.pair ? (nkb + 1) / 2 : nkb;
+  const int64_t units = (int64_t)xblocks * p.Hk * (bloop ? 1 : p.B);
+  // Split the query heads of a group over two workgroups when the grid would
+  // not fill the chip twice over.  Two addends onto zeroed outputs sum in
+  // either order to the same fp32 value; adding two partials into existing
+  // values would not, so deterministic accumulation keeps one workgroup per
+  // key block.
+  pl.hsplit = (!bloop && !(accumulate_dkdv && deterministic) && p.G % 2 == 0 && units < 2 * 256) ? 2 : 1;
+  pl.out_mode = pl.hsplit > 1 ? kAtomicAdd : (accumulate_dkdv ? kAddInto : kStore);
+  pl.grid = dim3(xblocks, p.Hk * pl.hsplit, bloop ? 1 : p.B);
+  return pl;
+}
+
 template <int D, bool BIAS, bool DQ_ATOMIC, bool BLOOP>
-hipError_t launch_dkdv(const Params& p, const BwdArgs& a, hipStream_t st) {
-  const dim3 grid((p.Sk + BK - 1) / BK, p.Hk, BLOOP ? 1 : p.B);
-  hipLaunchKernelGGL((k_dkdv<D, BIAS, DQ_ATOMIC, BLOOP>), grid, dim3(NT), 0, st, p, a);
+hipError_t launch_dkdv(const Params& p, const BwdArgs& a, const DkdvPlan& pl, hipStream_t st) {
+  hipLaunchKernelGGL((k_dkdv<D, BIAS, DQ_ATOMIC, BLOOP>), pl.grid, dim3(NT), 0, st, p, a, pl.pair, pl.hsplit,
+                     pl.out_mode);
   return hipGetLastError();
 }
 
 template <int D>
-hipError_t dispatch_dkdv(const Params& p, const BwdArgs& a, bool bias, bool dq_atomic, bool bloop,
-                         hipStream_t st) {
+hipError_t dispatch_dkdv(const Params& p, const BwdArgs& a, const DkdvPlan& pl, bool bias, bool dq_atomic,
+                         bool bloop, hipStream_t st) {
   // the batch loop is only used with the deterministic (non-atomic) dQ pass
   if (bias) {
-    if (dq_atomic) return launch_dkdv<D, true, true, false>(p, a, st);
-    return bloop ? launch_dkdv<D, true, false, true>(p, a, st) : launch_dkdv<D, true, false, false>(p, a, st);
+    if (dq_atomic) return launch_dkdv<D, true, true, false>(p, a, pl, st);
+    return bloop ? launch_dkdv<D, true, false, true>(p, a, pl, st) : launch_dkdv<D, true, false, false>(p, a, pl, st);
   }
-  if (dq_atomic) return launch_dkdv<D, false, true, false>(p, a, st);
-  return launch_dkdv<D, false, false, false>(p, a, st);
+  if (dq_atomic) return launch_dkdv<D, false, true, false>(p, a, pl, st);
+  return launch_dkdv<D, false, false, false>(p, a, pl, st);
 }
 
 // ---------------------------------------------------------------------------
@@ -559,14 +624,20 @@ hipError_t launch_bwd_mfma(const Params& p, const BwdArgs& a, hipStream_t st) {
   const bool dq_atomic = !a.deterministic;
   // dbias summed over the batch in a fixed order: one workgroup walks the batch
   const bool bloop = a.dbias != nullptr && a.deterministic;
-  hipError_t e = hipSuccess;
-  if (dq_atomic && !a.accumulate_dq) {
-    e = launch_zero_rows(a.dq, p.B, p.Hq, p.Sq, p.Dqk, p.dq_str, st);
-    if (e != hipSuccess) return e;
+  const DkdvPlan pl = plan_dkdv(p, bloop, a.accumulate_dkdv != 0, a.deterministic != 0);
+  // one fill for every output that is accumulated into from zero
+  ZeroRows z[3];
+  int nz = 0;
+  if (dq_atomic && !a.accumulate_dq) z[nz++] = ZeroRows{a.dq, p.B, p.Hq, p.Sq, p.Dqk, {p.dq_str[0], p.dq_str[1], p.dq_str[2]}};
+  if (pl.out_mode == kAtomicAdd && !a.accumulate_dkdv && p.Sk > 0) {
+    z[nz++] = ZeroRows{a.dk, p.B, p.Hk, p.Sk, p.Dqk, {p.dk_str[0], p.dk_str[1], p.dk_str[2]}};
+    z[nz++] = ZeroRows{a.dv, p.B, p.Hk, p.Sk, p.Dv, {p.dv_str[0], p.dv_str[1], p.dv_str[2]}};
   }
+  hipError_t e = launch_zero_multi(z, nz, st);
+  if (e != hipSuccess) return e;
   if (p.Sk > 0 && p.B > 0) {
-    e = p.Dqk == 64 ? dispatch_dkdv<64>(p, a, bias, dq_atomic, bloop, st)
-                    : dispatch_dkdv<128>(p, a, bias, dq_atomic, bloop, st);
+    e = p.Dqk == 64 ? dispatch_dkdv<64>(p, a, pl, bias, dq_atomic, bloop, st)
+                    : dispatch_dkdv<128>(p, a, pl, bias, dq_atomic, bloop, st);
     if (e != hipSuccess) return e;
   } else if (dq_atomic) {
     return hipSuccess;

@@ -229,8 +229,8 @@ __global__ __launch_bounds__(kThreads) void k_dkdv_simt(Params p, BwdArgs a, int
 #pragma unroll
       for (int n = 0; n < kCols; ++n) {
         const int c = s + 4 * n;
-        if (c < p.Dqk) dkp[c] = dk[n] * p.scale;
-        if (c < p.Dv) dvp[c] = dv[n];
+        if (c < p.Dqk) dkp[c] = (a.accumulate_dkdv ? dkp[c] : 0.f) + dk[n] * p.scale;
+        if (c < p.Dv) dvp[c] = (a.accumulate_dkdv ? dvp[c] : 0.f) + dv[n];
       }
     }
   }

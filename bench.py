@@ -4,8 +4,9 @@
     python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME]
 
 A step is one whole backward of the workload on inputs already resident in
-HBM: ``attn_bwd_preprocess`` (delta = rowsum(dO * O), dQ zeroed in the same
-pass) followed by ``attn_bwd`` (dK, dV, dQ).  O and LSE come from the
+HBM: ``attn_bwd_preprocess`` (delta = rowsum(dO * O); dQ, dK, dV zeroed)
+followed by ``attn_bwd`` accumulating dK, dV, dQ (one kernel launch in the
+default atomic-dQ mode).  O and LSE come from the
 library's own forward before the timed region.  Throughput counts
 2 * (3 * Dqk + 2 * Dv) FLOPs per allowed (query, key) pair per query head --
 the five contractions -- and nothing for masked pairs or recomputation.
@@ -136,10 +137,11 @@ def main():
     def step(flags, ev=None):
         if ev is not None:
             ev[0].record(stream)
-        ab.attn_bwd_preprocess(p, o, do, lse, sinks, delta, dsinks, dq, stream)
+        ab.attn_bwd_preprocess(p, o, do, lse, sinks, delta, dsinks, dq, dk, dv, stream)
         if ev is not None:
             ev[1].record(stream)
-        ab.attn_bwd(p, q, k, v, do, lse, delta, bias, dq, dk, dv, dbias, flags | ab.ATTN_ACCUMULATE_DQ, stream)
+        ab.attn_bwd(p, q, k, v, do, lse, delta, bias, dq, dk, dv, dbias,
+                    flags | ab.ATTN_ACCUMULATE_DQ | ab.ATTN_ACCUMULATE_DKDV, stream)
         if ev is not None:
             ev[2].record(stream)
 
@@ -212,7 +214,7 @@ def main():
                                      k_offset=i * c, sk_total=w.Sk, **mask_kw) for i in range(n)]
 
             def chunked():
-                ab.attn_bwd_preprocess(p, o, do, lse, None, delta, None, dq, stream)
+                ab.attn_bwd_preprocess(p, o, do, lse, None, delta, None, dq, None, None, stream)
                 for i in range(n):
                     sl = slice(i * c, (i + 1) * c)
                     ab.attn_bwd(probs[i], q, k[:, :, sl], v[:, :, sl], do, lse, delta, None, dq, dk[:, :, sl],

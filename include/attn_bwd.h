@@ -85,8 +85,11 @@ typedef enum {
  *   Without it dQ (and dbias) are accumulated with fp32 atomics, whose
  *   order -- and so the low bits -- may vary between calls.
  * ATTN_ACCUMULATE_DQ: add into dQ instead of overwriting it (chunked /
- *   ring use, [RING] _ring_bwd "dq += dqa"). */
-enum { ATTN_DETERMINISTIC = 1u, ATTN_ACCUMULATE_DQ = 2u };
+ *   ring use, [RING] _ring_bwd accumulates dq over the K/V chunks).
+ * ATTN_ACCUMULATE_DKDV: add into dK and dV instead of overwriting them
+ *   ([RING] _ring_bwd adds each chunk's dk/dv into travelling
+ *   accumulators). */
+enum { ATTN_DETERMINISTIC = 1u, ATTN_ACCUMULATE_DQ = 2u, ATTN_ACCUMULATE_DKDV = 4u };
 
 /* Problem description ([GQA-BWD] FmhaProblem; [SFMG] "Prototype"). */
 typedef struct attn_problem {
@@ -131,12 +134,15 @@ attn_status_t attn_fwd_lse(const attn_problem_t* p, const void* q, const void* k
  *   delta[b,h,i] = sum_d dO[b,h,i,d] * O[b,h,i,d]               (fp32 [B,Hq,Sq])
  *   if sinks: dsinks[h] = -sum_{b,i} exp(sinks[h] - lse[b,h,i]) * delta[b,h,i]
  * dsinks is required iff sinks is given; it is overwritten.
- * dq_zero is nullable: when given, the fp32 dQ buffer (strides dq_str) is
- * zeroed in the same pass, so that a following attn_bwd with
- * ATTN_ACCUMULATE_DQ produces dQ without a separate fill. */
+ * dq_zero, dk_zero, dv_zero are nullable: each given fp32 gradient buffer
+ * (strides dq_str / dk_str / dv_str) is zeroed here -- dQ in the same pass
+ * as delta -- so that a following attn_bwd with ATTN_ACCUMULATE_DQ /
+ * ATTN_ACCUMULATE_DKDV accumulates into zeroed buffers without further
+ * fills. */
 attn_status_t attn_bwd_preprocess(const attn_problem_t* p, const void* o, const void* dout,
                                   const float* lse, const float* sinks, float* delta,
-                                  float* dsinks, float* dq_zero, void* stream);
+                                  float* dsinks, float* dq_zero, float* dk_zero, float* dv_zero,
+                                  void* stream);
 
 /* Backward main pass ([GQA-BWD] module docstring and cpu_bwd_gqa; [DBIAS]
  * cpu_attention_bwd_dbias; [SFMG] Phase 2 and 3):

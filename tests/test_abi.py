@@ -110,8 +110,8 @@ def test_preprocess_sinks_pairing():
     p = problem()
     L = B.lib()
     # sinks without dsinks and the reverse
-    assert L.attn_bwd_preprocess(ctypes.byref(p), FAKE, FAKE, FAKE, FAKE, FAKE, None, None, None) == B.ATTN_EINVAL
-    assert L.attn_bwd_preprocess(ctypes.byref(p), FAKE, FAKE, FAKE, None, FAKE, FAKE, None, None) == B.ATTN_EINVAL
+    assert L.attn_bwd_preprocess(ctypes.byref(p), FAKE, FAKE, FAKE, FAKE, FAKE, None, None, None, None, None) == B.ATTN_EINVAL
+    assert L.attn_bwd_preprocess(ctypes.byref(p), FAKE, FAKE, FAKE, None, FAKE, FAKE, None, None, None, None) == B.ATTN_EINVAL
 
 
 def test_fp32_large_head_dim_unsupported():

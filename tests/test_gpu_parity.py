@@ -303,7 +303,7 @@ def test_headline_chunked():
     dk = torch.empty_like(full["dk"])
     dv = torch.empty_like(full["dv"])
     p = ab.make_problem(q, k, v, o=o, do=do, dq=dq, dk=dk, dv=dv, scale=w.scale, mask=w.mask)
-    ab.attn_bwd_preprocess(p, o, do, lse, None, delta, None, None)
+    ab.attn_bwd_preprocess(p, o, do, lse, None, delta, None, None, None, None)
     for i in range(n):
         sl = slice(i * c, (i + 1) * c)
         pc = ab.make_problem(q, k[:, :, sl], v[:, :, sl], o=o, do=do, dq=dq, dk=dk[:, :, sl], dv=dv[:, :, sl],
@@ -335,3 +335,49 @@ def test_deterministic_is_bitwise_repeatable():
         outs.append({kk: vv.clone() for kk, vv in g.items() if vv is not None})
     for kk in outs[0]:
         assert torch.equal(outs[0][kk], outs[1][kk]) and torch.equal(outs[0][kk], outs[2][kk]), kk
+
+
+@pytest.mark.parametrize("flags", [0, ab.ATTN_DETERMINISTIC], ids=["atomic", "determ"])
+def test_accumulate_into_existing(flags):
+    """ATTN_ACCUMULATE_DQ / ATTN_ACCUMULATE_DKDV add into the caller's
+    buffers: start from random contents and compare with contents + oracle."""
+    x = random_case(1, 8, 2, 300, 300, 128, 128, "bf16", 21, False, False)
+    spec = MaskSpec("top_left")
+    scale = 1 / np.sqrt(128)
+    say(f"[accumulate] flags={flags}")
+    o64, lse64 = oracle.forward(x["q"], x["k"], x["v"], scale, spec)
+    o32, lse32 = o64.astype(np.float32), lse64.astype(np.float32)
+    ref = oracle.backward(x["q"], x["k"], x["v"], o32, x["do"], lse32, scale, spec)
+    dt = torch.bfloat16
+    q, k, v, do = (dev(x[n], dt) for n in ("q", "k", "v", "do"))
+    o, lse = dev(o32, torch.float32), dev(lse32, torch.float32)
+    rng = np.random.default_rng(3)
+    init = {n: rng.standard_normal(ref[n].shape).astype(np.float32) for n in ("dq", "dk", "dv")}
+    dq, dk, dv = (dev(init[n], torch.float32) for n in ("dq", "dk", "dv"))
+    delta = torch.empty_like(lse)
+    p = ab.make_problem(q, k, v, o=o, do=do, dq=dq, dk=dk, dv=dv, scale=scale, mask="top_left")
+    ab.attn_bwd_preprocess(p, o, do, lse, None, delta, None, None, None, None)
+    ab.attn_bwd(p, q, k, v, do, lse, delta, None, dq, dk, dv, None,
+                flags | ab.ATTN_ACCUMULATE_DQ | ab.ATTN_ACCUMULATE_DKDV)
+    torch.cuda.synchronize()
+    for n, t in (("dq", dq), ("dk", dk), ("dv", dv)):
+        got = t.cpu().numpy().astype(np.float64) - init[n]
+        check(n, got, ref[n], 2e-2)
+
+
+def test_preprocess_zeroes_gradients():
+    x = random_case(2, 4, 2, 130, 150, 64, 64, "bf16", 8, False, False)
+    dt = torch.bfloat16
+    q, k, v, do = (dev(x[n], dt) for n in ("q", "k", "v", "do"))
+    o = torch.randn(2, 4, 130, 64, device="cuda")
+    lse = torch.randn(2, 4, 130, device="cuda")
+    dq = torch.full((2, 4, 130, 64), 7.0, device="cuda")
+    dk = torch.full((2, 2, 150, 64), 7.0, device="cuda")
+    dv = torch.full((2, 2, 150, 64), 7.0, device="cuda")
+    delta = torch.empty_like(lse)
+    p = ab.make_problem(q, k, v, o=o, do=do, dq=dq, dk=dk, dv=dv)
+    ab.attn_bwd_preprocess(p, o, do, lse, None, delta, None, dq, dk, dv)
+    torch.cuda.synchronize()
+    assert (dq == 0).all() and (dk == 0).all() and (dv == 0).all()
+    ref = (do.float() * o).sum(-1)
+    assert torch.allclose(delta, ref, atol=1e-4, rtol=1e-5)
