@@ -36,6 +36,8 @@ attn_status_t check_problem(const attn_problem_t* p) {
   const int64_t sq_t = p->sq_total ? p->sq_total : p->Sq;
   const int64_t sk_t = p->sk_total ? p->sk_total : p->Sk;
   if (p->q_offset + p->Sq > sq_t || p->k_offset + p->Sk > sk_t) return ATTN_EINVAL;
+  // the kernels evaluate the mask in 32-bit global indices
+  if (sq_t >= (int64_t(1) << 30) || sk_t >= (int64_t(1) << 30)) return ATTN_EUNSUPPORTED;
   return ATTN_OK;
 }
 

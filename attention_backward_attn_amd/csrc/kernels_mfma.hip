@@ -16,7 +16,9 @@
 //   with the K / V fragments as the B operand, so that the accumulator layout
 //   (one key per lane, 16 rows per lane) is directly the A operand of
 //   P^T dO and dS^T Q once the reduction index is permuted consistently on
-//   both operands.  dO^T / Q^T come from transposed LDS copies.  dS goes
+//   both operands.  The B operands of those two products (dO and Q with the
+//   row index as the reduction index) are read from the same row-major LDS
+//   tiles with the gfx950 transposing read ds_read_b64_tr_b16.  dS goes
 //   through LDS to form dQ = dS K for the tile (wave w: head-dim columns
 //   [32 w, 32 w + 32)), added into global dQ with fp32 atomics -- or left to
 //   the deterministic query-parallel kernel k_dq.
@@ -32,8 +34,10 @@ namespace {
 
 constexpr int BK = 128;       // keys per workgroup (k_dkdv)
 constexpr int BQ = 32;        // query rows per iteration (k_dkdv)
-constexpr int TP = 36;        // row length (elements) of the transposed tiles: 32 + 4 pad
 constexpr int NT = 256;       // threads per workgroup
+
+typedef short s16x4 __attribute__((ext_vector_type(4)));
+typedef __attribute__((address_space(3))) s16x4 lds_s16x4;
 
 __device__ inline f32x16 mfma(bf16x8 a, bf16x8 b, f32x16 c) {
   return __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c, 0, 0, 0);
@@ -64,42 +68,82 @@ __device__ inline f32x16 zero16() {
 // Row (within a 32-row accumulator block) held by lane group lg in register r.
 __device__ inline int crow(int r, int lg) { return 8 * (r >> 2) + 4 * lg + (r & 3); }
 
+// Row-major bf16 tiles of D columns in LDS, 16-byte chunks XOR-swizzled per
+// row: chunk c of row r sits at chunk position c ^ swz(r).  The swizzle makes
+// both access patterns of the kernels conflict-free: 16 lanes reading the
+// same chunk of 16 consecutive rows (ds_read_b128, A operands), and the
+// transposing read of 4 consecutive rows x 4 consecutive chunks (both
+// 4-aligned) by 32 lanes (ds_read_b64_tr_b16, B operands).
+template <int D>
+__device__ inline int swz(int r) {
+  if constexpr (D == 128) return ((r & 3) << 2) | ((r >> 2) & 3);   // 16 chunks = 64 banks per row
+  else return (((r >> 1) & 1) << 2) | ((r >> 2) & 3);               // 8 chunks: two rows per 64 banks
+}
+
+// Element offset of (row, 8-aligned column) in a swizzled tile.
+template <int D>
+__device__ inline int swz_off(int row, int col) {
+  return row * D + (((col >> 3) ^ swz<D>(row)) << 3) + (col & 7);
+}
+
+// 8 contiguous bf16 of one row (A operand: row, columns col..col+7).
+template <int D>
+__device__ inline bf16x8 lds_row8(const unsigned short* tile, int row, int col) {
+  return as_bf16x8(*(const u16x8*)(tile + swz_off<D>(row, col)));
+}
+
+// B operand (reduction over the tile's rows) of v_mfma_f32_32x32x16_bf16 for
+// output columns [n0, n0 + 32) and tile rows r0 + {4 lg + 0..3, 8 + 4 lg + 0..3}
+// (the slot order of the S / dS accumulators): lane l receives
+// tile[r0 + 4 lg + slot][n0 + l % 32].  ds_read_b64_tr_b16 hands lane j of
+// each 16-lane group element j % 4 of the 8-byte chunk addressed by lane
+// 4 r + j / 4 of that group, so lane i addresses row r0 + 4 lg + i / 4,
+// columns n0 + 16 ((l / 16) % 2) + 4 (i % 4).
+template <int D>
+__device__ inline bf16x8 lds_colB(const unsigned short* tile, int r0, int n0, int l) {
+  const int j = l & 15, lg = l >> 5;
+  const int col = n0 + 16 * ((l >> 4) & 1) + 4 * (j & 3);
+  const int row = r0 + 4 * lg + (j >> 2);
+  const auto* base = (__attribute__((address_space(3))) const unsigned short*)tile;
+  const s16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(base + swz_off<D>(row, col)));
+  const s16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(base + swz_off<D>(row + 8, col)));
+  return cat44(__builtin_bit_cast(u16x4, lo), __builtin_bit_cast(u16x4, hi));
+}
+
 template <int D>
 struct SmemDKDV {
-  unsigned short q[2][BQ][D + 8];    // Q tile, row-major (A operand of S = Q K^T)
-  unsigned short dO[2][BQ][D + 8];   // dO tile, row-major (A operand of dP = dO V^T)
-  unsigned short qt[2][D][TP];       // Q^T (B operand of dK += dS^T Q)
-  unsigned short dOt[2][D][TP];      // dO^T (B operand of dV += P^T dO)
+  unsigned short q[2][BQ * D];       // Q tile, swizzled row-major
+  unsigned short dO[2][BQ * D];      // dO tile, swizzled row-major
   unsigned short ds[BQ][BK + 8];     // dS tile, row-major (A operand of dQ = dS K)
   float lse2[2][BQ];                 // LSE * log2(e); +inf for rows without keys
   float delta[2][BQ];
 };
 
-// Per-thread staging of one 32-row Q / dO tile: thread t < 2 * NCH handles
-// rows 4 rg .. 4 rg + 3, columns 8 cc .. 8 cc + 7 of Q (t < NCH) or dO; the
-// last 32 threads carry the tile's LSE and delta.  load() only issues the
-// global loads (rows clamped into range, so no branches and no use of the
-// values); store() fixes up rows past the end and writes LDS.  This keeps
-// the loads in flight across the whole iteration that prefetches them.
+// Per-thread staging of one 32-row Q / dO tile: the 2 x 32 x (D / 8)
+// 16-byte chunks are dealt round-robin to the threads (16 consecutive lanes
+// load one row's consecutive chunks); the last 32 threads carry the tile's
+// LSE and delta.  load() only issues the global loads (rows clamped into
+// range, so no branches and no use of the values); store() fixes up rows
+// past the end and writes LDS.  This keeps the loads in flight across the
+// whole iteration that prefetches them.
 template <int D>
 struct Stage {
-  static constexpr int NCH = (BQ / 4) * (D / 8);
-  u16x8 v[4];
+  static constexpr int NCR = D / 8;               // chunks per row
+  static constexpr int NCH = 2 * BQ * NCR;        // chunks per Q + dO tile
+  static constexpr int NR = NCH / NT;             // chunks per thread
+  u16x8 v[NR];
   float lse, dl;
 
   __device__ inline void load(const unsigned short* q, const unsigned short* dout, int64_t qs, int64_t ds,
                               const float* lse_p, const float* dl_p, int64_t i0, int Sq) {
     const int t = threadIdx.x;
-    if (t < 2 * NCH) {
-      const int c = t < NCH ? t : t - NCH;
-      const int rg = c / (D / 8), cc = c % (D / 8);
-      const unsigned short* base = t < NCH ? q : dout;
-      const int64_t st = t < NCH ? qs : ds;
 #pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        const int64_t i = min(i0 + 4 * rg + e, (int64_t)Sq - 1);
-        v[e] = *(const u16x8*)(base + i * st + 8 * cc);
-      }
+    for (int k = 0; k < NR; ++k) {
+      const int idx = t + NT * k;
+      const int tensor = idx / (BQ * NCR), rem = idx % (BQ * NCR);
+      const int row = rem / NCR, c = rem % NCR;
+      const int64_t i = min(i0 + row, (int64_t)Sq - 1);
+      v[k] = *(const u16x8*)((tensor == 0 ? q + i * qs : dout + i * ds) + 8 * c);
     }
     if (t >= NT - BQ) {
       const int64_t i = min(i0 + (t - (NT - BQ)), (int64_t)Sq - 1);
@@ -110,24 +154,17 @@ struct Stage {
 
   __device__ inline void store(SmemDKDV<D>& sm, int buf, int64_t i0, int Sq) const {
     const int t = threadIdx.x;
-    if (t < 2 * NCH) {
-      const int c = t < NCH ? t : t - NCH;
-      const int rg = c / (D / 8), cc = c % (D / 8);
-      unsigned short(*rowm)[D + 8] = t < NCH ? sm.q[buf] : sm.dO[buf];
-      unsigned short(*colm)[TP] = t < NCH ? sm.qt[buf] : sm.dOt[buf];
-      u16x8 x[4];
 #pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        const bool ok = i0 + 4 * rg + e < Sq;
+    for (int k = 0; k < NR; ++k) {
+      const int idx = t + NT * k;
+      const int tensor = idx / (BQ * NCR), rem = idx % (BQ * NCR);
+      const int row = rem / NCR, c = rem % NCR;
+      const bool ok = i0 + row < Sq;
+      u16x8 x;
 #pragma unroll
-        for (int k = 0; k < 8; ++k) x[e][k] = ok ? v[e][k] : (unsigned short)0;
-        *(u16x8*)&rowm[4 * rg + e][8 * cc] = x[e];
-      }
-#pragma unroll
-      for (int k = 0; k < 8; ++k) {
-        u16x4 col = {x[0][k], x[1][k], x[2][k], x[3][k]};
-        *(u16x4*)&colm[8 * cc + k][4 * rg] = col;
-      }
+      for (int e = 0; e < 8; ++e) x[e] = ok ? v[k][e] : (unsigned short)0;
+      unsigned short* tile = tensor == 0 ? sm.q[buf] : sm.dO[buf];
+      *(u16x8*)(tile + swz_off<D>(row, 8 * c)) = x;
     }
     if (t >= NT - BQ) {
       const int r = t - (NT - BQ);
@@ -225,66 +262,78 @@ __global__ __launch_bounds__(NT, 1) void k_dkdv(Params p, BwdArgs a, int pair, i
       for (int n = 0; n < NB; ++n) { dk[n] = zero16(); dv[n] = zero16(); }
 
       Stage<D> stg;
-      auto tile = [&](int it, int* h, int64_t* i0) {
-        *h = h_begin + it / nqb;
-        *i0 = lo_al + (int64_t)BQ * (it % nqb);
-      };
-      auto issue = [&](int it) {
-        int h;
-        int64_t i0;
-        tile(it, &h, &i0);
+      auto issue = [&](int h, int64_t i0) {
         stg.load((const unsigned short*)a.q + b * p.q_str[0] + h * p.q_str[1],
                  (const unsigned short*)a.dout + b * p.do_str[0] + h * p.do_str[1], p.q_str[2], p.do_str[2],
                  a.lse + ((int64_t)b * p.Hq + h) * Sq, a.delta + ((int64_t)b * p.Hq + h) * Sq, i0, Sq);
       };
+      // (head, row-tile) of the current iteration, advanced incrementally
+      int h = h_begin, qb = 0;
       if (n_it > 0) {
-        int h;
-        int64_t i0;
-        tile(0, &h, &i0);
-        issue(0);
+        issue(h, lo_al);
         __syncthreads();  // readers of buffer 0 from the previous unit are done
-        stg.store(sm, 0, i0, Sq);
+        stg.store(sm, 0, lo_al, Sq);
         __syncthreads();
       }
+      // mask in the form  t = j' - i' - diag:  allowed <=> lo_t <= t <= wr, or j' < n_sink
+      const int jg = jkey + (int)p.mask.k_off;
+      const bool key_ok = jkey < Sk;
+      const bool sink_key = jg < p.mask.n_sink;
+      const int lo_t = p.mask.wl < 0 ? -0x3fffffff : -p.mask.wl;
+      const int wr_t = p.mask.wr;
+      const bool no_mask = p.mask.kind == kMaskNone;
 
       for (int it = 0; it < n_it; ++it) {
         const int cur = it & 1;
-        int h;
-        int64_t i0;
-        tile(it, &h, &i0);
-        if (it + 1 < n_it) issue(it + 1);
+        const int64_t i0 = lo_al + (int64_t)BQ * qb;
+        int hn = h, qbn = qb + 1;
+        if (qbn == nqb) { qbn = 0; ++hn; }
+        if (it + 1 < n_it) issue(hn, lo_al + (int64_t)BQ * qbn);
+
+        // lse2 / delta of this lane's 16 rows: rows 8 m + 4 lg + 0..3
+        f32x4 L4[4], D4[4];
+#pragma unroll
+        for (int m = 0; m < 4; ++m) {
+          L4[m] = *(const f32x4*)&sm.lse2[cur][8 * m + 4 * lg];
+          D4[m] = *(const f32x4*)&sm.delta[cur][8 * m + 4 * lg];
+        }
 
         // S = Q K^T and dP = dO V^T for rows i0..i0+31, this wave's 32 keys.
         f32x16 sacc = zero16(), dpacc = zero16();
 #pragma unroll
         for (int s = 0; s < NS; ++s) {
-          const bf16x8 qa = as_bf16x8(*(const u16x8*)&sm.q[cur][lr][16 * s + 8 * lg]);
-          const bf16x8 da = as_bf16x8(*(const u16x8*)&sm.dO[cur][lr][16 * s + 8 * lg]);
+          const bf16x8 qa = lds_row8<D>(sm.q[cur], lr, 16 * s + 8 * lg);
+          const bf16x8 da = lds_row8<D>(sm.dO[cur], lr, 16 * s + 8 * lg);
           sacc = mfma(qa, kB[s], sacc);
           dpacc = mfma(da, vB[s], dpacc);
         }
+        // B fragments of the first head-dim block for dV / dK (independent of P)
+        bf16x8 o0 = lds_colB<D>(sm.dO[cur], 0, 0, l), o1 = lds_colB<D>(sm.dO[cur], 16, 0, l);
+        bf16x8 q0 = lds_colB<D>(sm.q[cur], 0, 0, l), q1 = lds_colB<D>(sm.q[cur], 16, 0, l);
 
-        // P = exp(S - LSE) on allowed pairs, dS = P (dP - delta).
+        // P = exp(S - LSE) on allowed pairs, dS = P (dP - delta); branch-free.
         const bool full = wave_keys_in && p.mask.tile_full(i0, i0 + BQ, kw, kw + 32);
+        const int tb = jg - (int)(i0 + p.mask.q_off) - (int)p.mask.diag - 4 * lg;
         float pv[16], dsv[16];
 #pragma unroll
         for (int r = 0; r < 16; ++r) {
-          const int row = crow(r, lg);
-          const int64_t i = i0 + row;
-          float x = sacc[r] * scale_log2;
+          const int c = 8 * (r >> 2) + (r & 3);
+          const int t = tb - c;
+          const bool ok = full || (key_ok && (no_mask || (t <= wr_t && t >= lo_t) || sink_key));
+          float x = sacc[r] * scale_log2 - L4[r >> 2][r & 3];
           if (BIAS) {
-            if (i < Sq && jkey < Sk) x += a.bias[h * p.bias_str[0] + i * p.bias_str[1] + jkey] * kLog2e;
+            const int64_t i = i0 + 4 * lg + c;
+            if (i < Sq && key_ok) x += a.bias[h * p.bias_str[0] + i * p.bias_str[1] + jkey] * kLog2e;
           }
-          float pp = exp2f(x - sm.lse2[cur][row]);
-          if (!full && !(jkey < Sk && p.mask.allowed(i, jkey))) pp = 0.f;
+          const float pp = ok ? __builtin_amdgcn_exp2f(x) : 0.f;
           pv[r] = pp;
-          dsv[r] = pp * (dpacc[r] - sm.delta[cur][row]);
+          dsv[r] = pp * (dpacc[r] - D4[r >> 2][r & 3]);
         }
         if (BIAS && a.dbias) {
 #pragma unroll
           for (int r = 0; r < 16; ++r) {
             const int64_t i = i0 + crow(r, lg);
-            if (i < Sq && jkey < Sk && pv[r] != 0.f) {
+            if (i < Sq && key_ok && pv[r] != 0.f) {
               float* dst = a.dbias + h * p.bias_str[0] + i * p.bias_str[1] + jkey;
               if (BLOOP)
                 *dst += dsv[r];
@@ -297,20 +346,23 @@ __global__ __launch_bounds__(NT, 1) void k_dkdv(Params p, BwdArgs a, int pair, i
         const bf16x8 sa0 = pack8(dsv), sa1 = pack8(dsv + 8);
 
         // dV += P^T dO and dK += dS^T Q (reduction over the 32 rows, permuted
-        // consistently with the accumulator layout of S).
+        // consistently with the accumulator layout of S); the fragments of
+        // block n + 1 are read while block n multiplies.
 #pragma unroll
         for (int n = 0; n < NB; ++n) {
-          const int d = 32 * n + lr;
-          const bf16x8 o0 = cat44(*(const u16x4*)&sm.dOt[cur][d][4 * lg], *(const u16x4*)&sm.dOt[cur][d][8 + 4 * lg]);
-          const bf16x8 o1 = cat44(*(const u16x4*)&sm.dOt[cur][d][16 + 4 * lg],
-                                  *(const u16x4*)&sm.dOt[cur][d][24 + 4 * lg]);
+          bf16x8 o0n = o0, o1n = o1, q0n = q0, q1n = q1;
+          if (n + 1 < NB) {
+            const int n0 = 32 * (n + 1);
+            o0n = lds_colB<D>(sm.dO[cur], 0, n0, l);
+            o1n = lds_colB<D>(sm.dO[cur], 16, n0, l);
+            q0n = lds_colB<D>(sm.q[cur], 0, n0, l);
+            q1n = lds_colB<D>(sm.q[cur], 16, n0, l);
+          }
           dv[n] = mfma(pa0, o0, dv[n]);
-          dv[n] = mfma(pa1, o1, dv[n]);
-          const bf16x8 q0 = cat44(*(const u16x4*)&sm.qt[cur][d][4 * lg], *(const u16x4*)&sm.qt[cur][d][8 + 4 * lg]);
-          const bf16x8 q1 = cat44(*(const u16x4*)&sm.qt[cur][d][16 + 4 * lg],
-                                  *(const u16x4*)&sm.qt[cur][d][24 + 4 * lg]);
           dk[n] = mfma(sa0, q0, dk[n]);
+          dv[n] = mfma(pa1, o1, dv[n]);
           dk[n] = mfma(sa1, q1, dk[n]);
+          o0 = o0n; o1 = o1n; q0 = q0n; q1 = q1n;
         }
 
         if (DQ_ATOMIC) {
@@ -322,27 +374,30 @@ __global__ __launch_bounds__(NT, 1) void k_dkdv(Params p, BwdArgs a, int pair, i
           }
           __syncthreads();
           if (dq_wave) {
-            f32x16 qacc = zero16();
+            bf16x8 dsa[BK / 16];
 #pragma unroll
-            for (int t = 0; t < BK / 16; ++t) {
-              const bf16x8 da = as_bf16x8(*(const u16x8*)&sm.ds[lr][16 * t + 8 * lg]);
-              qacc = mfma(da, ktB[t], qacc);
+            for (int t = 0; t < BK / 16; ++t) dsa[t] = as_bf16x8(*(const u16x8*)&sm.ds[lr][16 * t + 8 * lg]);
+            f32x16 qacc0 = zero16(), qacc1 = zero16();
+#pragma unroll
+            for (int t = 0; t < BK / 16; t += 2) {
+              qacc0 = mfma(dsa[t], ktB[t], qacc0);
+              qacc1 = mfma(dsa[t + 1], ktB[t + 1], qacc1);
             }
-            float* dq = a.dq + b * p.dq_str[0] + h * p.dq_str[1] + 32 * w + lr;
+            // row i0 + 4 lg + c, column 32 w + lr: 32-bit offsets from a uniform base
+            float* dqb = a.dq + b * p.dq_str[0] + h * p.dq_str[1] + i0 * p.dq_str[2];
+            const int rs = (int)p.dq_str[2];
+            const int64_t rows_left = Sq - i0;
 #pragma unroll
             for (int r = 0; r < 16; ++r) {
-              const int64_t i = i0 + crow(r, lg);
-              if (i >= lo && i < hi) atomic_add_f32(dq + i * p.dq_str[2], qacc[r] * p.scale);
+              const int c = 4 * lg + 8 * (r >> 2) + (r & 3);
+              if (c < rows_left) atomic_add_f32(dqb + (c * rs + 32 * w + lr), (qacc0[r] + qacc1[r]) * p.scale);
             }
           }
         }
-        if (it + 1 < n_it) {
-          int h1;
-          int64_t i1;
-          tile(it + 1, &h1, &i1);
-          stg.store(sm, cur ^ 1, i1, Sq);
-        }
+        if (it + 1 < n_it) stg.store(sm, cur ^ 1, lo_al + (int64_t)BQ * qbn, Sq);
         __syncthreads();
+        h = hn;
+        qb = qbn;
       }
 
       // Epilogue: dK * scale and dV for this wave's keys.
@@ -431,50 +486,43 @@ constexpr int BK3 = 32;    // keys per iteration (k_dq)
 
 template <int D>
 struct SmemDQ {
-  unsigned short k[2][BK3][D + 8];   // K tile, row-major (A operand of S^T)
-  unsigned short v[2][BK3][D + 8];   // V tile, row-major (A operand of dP^T)
-  unsigned short kt[2][D][TP];       // K^T (B operand of dQ += dS K)
+  unsigned short k[2][BK3 * D];      // K tile, swizzled row-major
+  unsigned short v[2][BK3 * D];      // V tile, swizzled row-major
 };
 
+// Staging of one 32-key K / V tile (same dealing of 16-byte chunks as Stage).
 template <int D>
 struct StageKV {
-  static constexpr int NCH = (BK3 / 4) * (D / 8);
-  u16x8 v[4];
+  static constexpr int NCR = D / 8;
+  static constexpr int NCH = 2 * BK3 * NCR;
+  static constexpr int NR = NCH / NT;
+  u16x8 v[NR];
 
   __device__ inline void load(const unsigned short* k, const unsigned short* vv, int64_t ks, int64_t vs,
                               int64_t j0, int Sk) {
     const int t = threadIdx.x;
-    if (t < 2 * NCH) {
-      const int c = t < NCH ? t : t - NCH;
-      const int rg = c / (D / 8), cc = c % (D / 8);
-      const unsigned short* base = t < NCH ? k : vv;
-      const int64_t st = t < NCH ? ks : vs;
 #pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        const int64_t j = j0 + 4 * rg + e;
-        if (j < Sk)
-          v[e] = *(const u16x8*)(base + j * st + 8 * cc);
-        else
-          v[e] = u16x8{0, 0, 0, 0, 0, 0, 0, 0};
-      }
+    for (int m = 0; m < NR; ++m) {
+      const int idx = t + NT * m;
+      const int tensor = idx / (BK3 * NCR), rem = idx % (BK3 * NCR);
+      const int row = rem / NCR, c = rem % NCR;
+      const int64_t j = min(j0 + row, (int64_t)Sk - 1);
+      v[m] = *(const u16x8*)((tensor == 0 ? k + j * ks : vv + j * vs) + 8 * c);
     }
   }
 
-  __device__ inline void store(SmemDQ<D>& sm, int buf) const {
+  __device__ inline void store(SmemDQ<D>& sm, int buf, int64_t j0, int Sk) const {
     const int t = threadIdx.x;
-    if (t < 2 * NCH) {
-      const int c = t < NCH ? t : t - NCH;
-      const int rg = c / (D / 8), cc = c % (D / 8);
-      unsigned short(*rowm)[D + 8] = t < NCH ? sm.k[buf] : sm.v[buf];
 #pragma unroll
-      for (int e = 0; e < 4; ++e) *(u16x8*)&rowm[4 * rg + e][8 * cc] = v[e];
-      if (t < NCH) {
+    for (int m = 0; m < NR; ++m) {
+      const int idx = t + NT * m;
+      const int tensor = idx / (BK3 * NCR), rem = idx % (BK3 * NCR);
+      const int row = rem / NCR, c = rem % NCR;
+      const bool ok = j0 + row < Sk;
+      u16x8 x;
 #pragma unroll
-        for (int k = 0; k < 8; ++k) {
-          u16x4 col = {v[0][k], v[1][k], v[2][k], v[3][k]};
-          *(u16x4*)&sm.kt[buf][8 * cc + k][4 * rg] = col;
-        }
-      }
+      for (int e = 0; e < 8; ++e) x[e] = ok ? v[m][e] : (unsigned short)0;
+      *(u16x8*)((tensor == 0 ? sm.k[buf] : sm.v[buf]) + swz_off<D>(row, 8 * c)) = x;
     }
   }
 };
@@ -534,7 +582,7 @@ __global__ __launch_bounds__(NT, 1) void k_dq(Params p, BwdArgs a) {
   StageKV<D> stg;
   if (n_it > 0) {
     stg.load(kp, vp, p.k_str[2], p.v_str[2], tile_of(0), Sk);
-    stg.store(sm, 0);
+    stg.store(sm, 0, tile_of(0), Sk);
     __syncthreads();
   }
   for (int it = 0; it < n_it; ++it) {
@@ -545,8 +593,8 @@ __global__ __launch_bounds__(NT, 1) void k_dq(Params p, BwdArgs a) {
     f32x16 sacc = zero16(), dpacc = zero16();
 #pragma unroll
     for (int s = 0; s < NS; ++s) {
-      const bf16x8 ka = as_bf16x8(*(const u16x8*)&sm.k[cur][lr][16 * s + 8 * lg]);
-      const bf16x8 va = as_bf16x8(*(const u16x8*)&sm.v[cur][lr][16 * s + 8 * lg]);
+      const bf16x8 ka = lds_row8<D>(sm.k[cur], lr, 16 * s + 8 * lg);
+      const bf16x8 va = lds_row8<D>(sm.v[cur], lr, 16 * s + 8 * lg);
       sacc = mfma(ka, qB[s], sacc);
       dpacc = mfma(va, doB[s], dpacc);
     }
@@ -566,14 +614,12 @@ __global__ __launch_bounds__(NT, 1) void k_dq(Params p, BwdArgs a) {
     const bf16x8 sa0 = pack8(dsv), sa1 = pack8(dsv + 8);
 #pragma unroll
     for (int n = 0; n < NB; ++n) {
-      const int d = 32 * n + lr;
-      const bf16x8 k0v = cat44(*(const u16x4*)&sm.kt[cur][d][4 * lg], *(const u16x4*)&sm.kt[cur][d][8 + 4 * lg]);
-      const bf16x8 k1v = cat44(*(const u16x4*)&sm.kt[cur][d][16 + 4 * lg],
-                               *(const u16x4*)&sm.kt[cur][d][24 + 4 * lg]);
+      const bf16x8 k0v = lds_colB<D>(sm.k[cur], 0, 32 * n, l);
+      const bf16x8 k1v = lds_colB<D>(sm.k[cur], 16, 32 * n, l);
       dq[n] = mfma(sa0, k0v, dq[n]);
       dq[n] = mfma(sa1, k1v, dq[n]);
     }
-    if (it + 1 < n_it) stg.store(sm, cur ^ 1);
+    if (it + 1 < n_it) stg.store(sm, cur ^ 1, tile_of(it + 1), Sk);
     __syncthreads();
   }
 
