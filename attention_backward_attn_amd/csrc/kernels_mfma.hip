@@ -58,6 +58,14 @@ __device__ inline bf16x8 pack8(const float* x) {
   return r;
 }
 
+// Wait for every outstanding vector-memory load (vmcnt = 0; expcnt and
+// lgkmcnt left at their maxima).  Issued once after the register-resident
+// fragments are loaded, ahead of a loop: otherwise the compiler's wait
+// counting carries those loads into the loop body, and each use there waits
+// for the vmcnt of older operations -- including the previous iteration's
+// dQ atomics.
+__device__ inline void wait_vm_loads() { __builtin_amdgcn_s_waitcnt(0x0F70); }
+
 __device__ inline f32x16 zero16() {
   f32x16 z;
 #pragma unroll
@@ -110,11 +118,24 @@ __device__ inline bf16x8 lds_colB(const unsigned short* tile, int r0, int n0, in
   return cat44(__builtin_bit_cast(u16x4, lo), __builtin_bit_cast(u16x4, hi));
 }
 
+// dS^T tile: row = key (BK rows of BQ = 32 bf16, 64 bytes), 8-byte slots
+// XOR-swizzled by key: slot c of key row k sits at slot c ^ ((k >> 2) & 7).
+// Conflict-free for the 32 lanes that write 8 bytes of 32 consecutive keys,
+// and for the transposing read of 4 consecutive keys x 32 rows.
+__device__ inline int dst_off(int key, int col) {
+  return key * BQ + ((((col >> 2) ^ (key >> 2)) & 7) << 2);
+}
+
+__device__ inline u16x4 lds_tr4(const unsigned short* base, int off) {
+  const auto* b = (__attribute__((address_space(3))) const unsigned short*)base;
+  return __builtin_bit_cast(u16x4, __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(b + off)));
+}
+
 template <int D>
 struct SmemDKDV {
   unsigned short q[2][BQ * D];       // Q tile, swizzled row-major
   unsigned short dO[2][BQ * D];      // dO tile, swizzled row-major
-  unsigned short ds[BQ][BK + 8];     // dS tile, row-major (A operand of dQ = dS K)
+  unsigned short dst[BK * BQ];       // dS^T tile [key][row], 8-byte slots swizzled (dst_off)
   float lse2[2][BQ];                 // LSE * log2(e); +inf for rows without keys
   float delta[2][BQ];
 };
@@ -159,12 +180,10 @@ struct Stage {
       const int idx = t + NT * k;
       const int tensor = idx / (BQ * NCR), rem = idx % (BQ * NCR);
       const int row = rem / NCR, c = rem % NCR;
-      const bool ok = i0 + row < Sq;
-      u16x8 x;
-#pragma unroll
-      for (int e = 0; e < 8; ++e) x[e] = ok ? v[k][e] : (unsigned short)0;
+      // rows past the end hold a copy of the last row: finite, and their
+      // LSE of +inf makes every P (and dS) of the row zero
       unsigned short* tile = tensor == 0 ? sm.q[buf] : sm.dO[buf];
-      *(u16x8*)(tile + swz_off<D>(row, 8 * c)) = x;
+      *(u16x8*)(tile + swz_off<D>(row, 8 * c)) = v[k];
     }
     if (t >= NT - BQ) {
       const int r = t - (NT - BQ);
@@ -206,6 +225,10 @@ __global__ __launch_bounds__(NT, 1) void k_dkdv(Params p, BwdArgs a, int pair, i
   const bool dq_wave = DQ_ATOMIC && (w < NB);
   const int kbx = blockIdx.x;
   const int n_units = (pair && nkb - 1 - kbx != kbx) ? 2 : 1;
+  const bool no_mask = p.mask.kind == kMaskNone;
+  // mask as t = j' - i' - diag:  allowed <=> lo_t <= t <= wr, or j' < n_sink
+  const int lo_t = p.mask.wl < 0 ? -0x3fffffff : -p.mask.wl;
+  const int wr_t = p.mask.wr;
 
   const int b_begin = BLOOP ? 0 : blockIdx.z;
   const int b_end = BLOOP ? p.B : b_begin + 1;
@@ -216,33 +239,32 @@ __global__ __launch_bounds__(NT, 1) void k_dkdv(Params p, BwdArgs a, int pair, i
       const int kw = k0 + 32 * w;     // first key of this wave
       const int jkey = kw + lr;       // this lane's key (accumulator column of S / dP)
       const bool wave_keys_in = kw + 32 <= Sk;
-      int64_t lo, hi;
-      p.mask.rows_for_keys(k0, min(k0 + BK, Sk), Sq, &lo, &hi);
-      const int64_t lo_al = lo & ~(int64_t)(BQ - 1);
-      const int nqb = hi > lo ? (int)((hi - lo_al + BQ - 1) / BQ) : 0;
+      const bool key_ok = jkey < Sk;
+      const int jg = jkey + (int)p.mask.k_off;
+      const bool sink_key = jg < p.mask.n_sink;
+      int64_t lo64, hi64;
+      p.mask.rows_for_keys(k0, min(k0 + BK, Sk), Sq, &lo64, &hi64);
+      const int lo = (int)lo64, hi = (int)hi64;
+      const int lo_al = lo & ~(BQ - 1);
+      const int nqb = hi > lo ? (hi - lo_al + BQ - 1) / BQ : 0;
       const int n_it = gh * nqb;
 
       const unsigned short* kp = (const unsigned short*)a.k + b * p.k_str[0] + hk * p.k_str[1];
       const unsigned short* vp = (const unsigned short*)a.v + b * p.v_str[0] + hk * p.v_str[1];
-      // K / V fragments of this wave's keys (B operands of S and dP).
+      // K / V fragments of this wave's keys (B operands of S and dP); keys
+      // past the end read the last key (finite; their P is forced to 0).
       bf16x8 kB[NS], vB[NS];
       {
         const int64_t jc = min(jkey, Sk - 1);
-        const bool ok = jkey < Sk;
 #pragma unroll
         for (int s = 0; s < NS; ++s) {
-          u16x8 kk = *(const u16x8*)(kp + jc * p.k_str[2] + 16 * s + 8 * lg);
-          u16x8 vv = *(const u16x8*)(vp + jc * p.v_str[2] + 16 * s + 8 * lg);
-#pragma unroll
-          for (int e = 0; e < 8; ++e) {
-            kk[e] = ok ? kk[e] : (unsigned short)0;
-            vv[e] = ok ? vv[e] : (unsigned short)0;
-          }
-          kB[s] = as_bf16x8(kk);
-          vB[s] = as_bf16x8(vv);
+          kB[s] = as_bf16x8(*(const u16x8*)(kp + jc * p.k_str[2] + 16 * s + 8 * lg));
+          vB[s] = as_bf16x8(*(const u16x8*)(vp + jc * p.v_str[2] + 16 * s + 8 * lg));
         }
       }
-      // K^T fragments (B operand of dQ = dS K): keys 16 t + 8 lg + e, column 32 w + lr.
+      // K fragments for dQ = dS K (B operand, head-dim column 32 w + lr) in
+      // the key order of the dS^T transposing read: slot e of step t is key
+      // 16 t + 8 (e / 4) + 4 lg + e % 4.
       bf16x8 ktB[BK / 16];
       if (dq_wave) {
 #pragma unroll
@@ -250,9 +272,8 @@ __global__ __launch_bounds__(NT, 1) void k_dkdv(Params p, BwdArgs a, int pair, i
           u16x8 uu;
 #pragma unroll
           for (int e = 0; e < 8; ++e) {
-            const int j = k0 + 16 * t + 8 * lg + e;
-            const unsigned short x = kp[(int64_t)min(j, Sk - 1) * p.k_str[2] + 32 * w + lr];
-            uu[e] = (j < Sk) ? x : (unsigned short)0;
+            const int j = k0 + 16 * t + 8 * (e >> 2) + 4 * lg + (e & 3);
+            uu[e] = kp[(int64_t)min(j, Sk - 1) * p.k_str[2] + 32 * w + lr];
           }
           ktB[t] = as_bf16x8(uu);
         }
@@ -260,9 +281,10 @@ __global__ __launch_bounds__(NT, 1) void k_dkdv(Params p, BwdArgs a, int pair, i
       f32x16 dk[NB], dv[NB];
 #pragma unroll
       for (int n = 0; n < NB; ++n) { dk[n] = zero16(); dv[n] = zero16(); }
+      wait_vm_loads();
 
       Stage<D> stg;
-      auto issue = [&](int h, int64_t i0) {
+      auto issue = [&](int h, int i0) {
         stg.load((const unsigned short*)a.q + b * p.q_str[0] + h * p.q_str[1],
                  (const unsigned short*)a.dout + b * p.do_str[0] + h * p.do_str[1], p.q_str[2], p.do_str[2],
                  a.lse + ((int64_t)b * p.Hq + h) * Sq, a.delta + ((int64_t)b * p.Hq + h) * Sq, i0, Sq);
@@ -275,28 +297,13 @@ __global__ __launch_bounds__(NT, 1) void k_dkdv(Params p, BwdArgs a, int pair, i
         stg.store(sm, 0, lo_al, Sq);
         __syncthreads();
       }
-      // mask in the form  t = j' - i' - diag:  allowed <=> lo_t <= t <= wr, or j' < n_sink
-      const int jg = jkey + (int)p.mask.k_off;
-      const bool key_ok = jkey < Sk;
-      const bool sink_key = jg < p.mask.n_sink;
-      const int lo_t = p.mask.wl < 0 ? -0x3fffffff : -p.mask.wl;
-      const int wr_t = p.mask.wr;
-      const bool no_mask = p.mask.kind == kMaskNone;
 
       for (int it = 0; it < n_it; ++it) {
         const int cur = it & 1;
-        const int64_t i0 = lo_al + (int64_t)BQ * qb;
+        const int i0 = lo_al + BQ * qb;
         int hn = h, qbn = qb + 1;
         if (qbn == nqb) { qbn = 0; ++hn; }
-        if (it + 1 < n_it) issue(hn, lo_al + (int64_t)BQ * qbn);
-
-        // lse2 / delta of this lane's 16 rows: rows 8 m + 4 lg + 0..3
-        f32x4 L4[4], D4[4];
-#pragma unroll
-        for (int m = 0; m < 4; ++m) {
-          L4[m] = *(const f32x4*)&sm.lse2[cur][8 * m + 4 * lg];
-          D4[m] = *(const f32x4*)&sm.delta[cur][8 * m + 4 * lg];
-        }
+        if (it + 1 < n_it) issue(hn, lo_al + BQ * qbn);
 
         // S = Q K^T and dP = dO V^T for rows i0..i0+31, this wave's 32 keys.
         f32x16 sacc = zero16(), dpacc = zero16();
@@ -310,31 +317,51 @@ __global__ __launch_bounds__(NT, 1) void k_dkdv(Params p, BwdArgs a, int pair, i
         // B fragments of the first head-dim block for dV / dK (independent of P)
         bf16x8 o0 = lds_colB<D>(sm.dO[cur], 0, 0, l), o1 = lds_colB<D>(sm.dO[cur], 16, 0, l);
         bf16x8 q0 = lds_colB<D>(sm.q[cur], 0, 0, l), q1 = lds_colB<D>(sm.q[cur], 16, 0, l);
-
-        // P = exp(S - LSE) on allowed pairs, dS = P (dP - delta); branch-free.
-        const bool full = wave_keys_in && p.mask.tile_full(i0, i0 + BQ, kw, kw + 32);
-        const int tb = jg - (int)(i0 + p.mask.q_off) - (int)p.mask.diag - 4 * lg;
-        float pv[16], dsv[16];
+        // LSE (log2 units) and delta of this lane's 16 rows: rows 8 m + 4 lg + 0..3
+        f32x4 L4[4], D4[4];
 #pragma unroll
-        for (int r = 0; r < 16; ++r) {
-          const int c = 8 * (r >> 2) + (r & 3);
-          const int t = tb - c;
-          const bool ok = full || (key_ok && (no_mask || (t <= wr_t && t >= lo_t) || sink_key));
-          float x = sacc[r] * scale_log2 - L4[r >> 2][r & 3];
-          if (BIAS) {
-            const int64_t i = i0 + 4 * lg + c;
-            if (i < Sq && key_ok) x += a.bias[h * p.bias_str[0] + i * p.bias_str[1] + jkey] * kLog2e;
+        for (int m = 0; m < 4; ++m) {
+          L4[m] = *(const f32x4*)&sm.lse2[cur][8 * m + 4 * lg];
+          D4[m] = *(const f32x4*)&sm.delta[cur][8 * m + 4 * lg];
+        }
+
+        // P = exp(S - LSE) on allowed pairs, dS = P (dP - delta).  Tiles that
+        // are entirely allowed (the bulk under causal masks) skip the mask.
+        const bool full = wave_keys_in && p.mask.tile_full(i0, i0 + BQ, kw, kw + 32);
+        float pv[16], dsv[16];
+        if (full) {
+#pragma unroll
+          for (int r = 0; r < 16; ++r) {
+            float x = fmaf(sacc[r], scale_log2, -L4[r >> 2][r & 3]);
+            if (BIAS) {
+              const int i = i0 + 4 * lg + 8 * (r >> 2) + (r & 3);
+              if (i < Sq) x += a.bias[h * p.bias_str[0] + (int64_t)i * p.bias_str[1] + jkey] * kLog2e;
+            }
+            pv[r] = __builtin_amdgcn_exp2f(x);
+            dsv[r] = pv[r] * (dpacc[r] - D4[r >> 2][r & 3]);
           }
-          const float pp = ok ? __builtin_amdgcn_exp2f(x) : 0.f;
-          pv[r] = pp;
-          dsv[r] = pp * (dpacc[r] - D4[r >> 2][r & 3]);
+        } else {
+          const int tb = jg - (i0 + (int)p.mask.q_off) - (int)p.mask.diag - 4 * lg;
+#pragma unroll
+          for (int r = 0; r < 16; ++r) {
+            const int c = 8 * (r >> 2) + (r & 3);
+            const int t = tb - c;
+            const bool ok = key_ok && (no_mask || (t <= wr_t && t >= lo_t) || sink_key);
+            float x = fmaf(sacc[r], scale_log2, -L4[r >> 2][r & 3]);
+            if (BIAS) {
+              const int i = i0 + 4 * lg + c;
+              if (i < Sq && key_ok) x += a.bias[h * p.bias_str[0] + (int64_t)i * p.bias_str[1] + jkey] * kLog2e;
+            }
+            pv[r] = ok ? __builtin_amdgcn_exp2f(x) : 0.f;
+            dsv[r] = pv[r] * (dpacc[r] - D4[r >> 2][r & 3]);
+          }
         }
         if (BIAS && a.dbias) {
 #pragma unroll
           for (int r = 0; r < 16; ++r) {
-            const int64_t i = i0 + crow(r, lg);
+            const int i = i0 + crow(r, lg);
             if (i < Sq && key_ok && pv[r] != 0.f) {
-              float* dst = a.dbias + h * p.bias_str[0] + i * p.bias_str[1] + jkey;
+              float* dst = a.dbias + h * p.bias_str[0] + (int64_t)i * p.bias_str[1] + jkey;
               if (BLOOP)
                 *dst += dsv[r];
               else
@@ -342,6 +369,9 @@ __global__ __launch_bounds__(NT, 1) void k_dkdv(Params p, BwdArgs a, int pair, i
             }
           }
         }
+        // the softmax scale of dK and dQ is folded into the dS operand
+#pragma unroll
+        for (int r = 0; r < 16; ++r) dsv[r] *= p.scale;
         const bf16x8 pa0 = pack8(pv), pa1 = pack8(pv + 8);
         const bf16x8 sa0 = pack8(dsv), sa1 = pack8(dsv + 8);
 
@@ -366,41 +396,45 @@ __global__ __launch_bounds__(NT, 1) void k_dkdv(Params p, BwdArgs a, int pair, i
         }
 
         if (DQ_ATOMIC) {
-          // dS (bf16) to LDS, row-major [row][key in block].
-#pragma unroll
-          for (int r = 0; r < 16; ++r) {
-            const __bf16 vv = r < 8 ? sa0[r] : sa1[r - 8];
-            sm.ds[crow(r, lg)][32 * w + lr] = __builtin_bit_cast(unsigned short, vv);
+          // dS^T to LDS: this lane's key row, query rows 8 m + 4 lg + 0..3.
+          {
+            const u16x8 s0 = __builtin_bit_cast(u16x8, sa0), s1 = __builtin_bit_cast(u16x8, sa1);
+            const int key = 32 * w + lr;
+            *(u16x4*)&sm.dst[dst_off(key, 4 * lg)] = u16x4{s0[0], s0[1], s0[2], s0[3]};
+            *(u16x4*)&sm.dst[dst_off(key, 8 + 4 * lg)] = u16x4{s0[4], s0[5], s0[6], s0[7]};
+            *(u16x4*)&sm.dst[dst_off(key, 16 + 4 * lg)] = u16x4{s1[0], s1[1], s1[2], s1[3]};
+            *(u16x4*)&sm.dst[dst_off(key, 24 + 4 * lg)] = u16x4{s1[4], s1[5], s1[6], s1[7]};
           }
           __syncthreads();
           if (dq_wave) {
-            bf16x8 dsa[BK / 16];
+            // A operand of dQ = dS K: rows l % 32, keys 16 t + {4 lg + 0..3, 8 + 4 lg + 0..3}
+            const int j = l & 15;
+            const int rcol = 16 * ((l >> 4) & 1) + 4 * (j & 3);
+            f32x16 qacc = zero16();
 #pragma unroll
-            for (int t = 0; t < BK / 16; ++t) dsa[t] = as_bf16x8(*(const u16x8*)&sm.ds[lr][16 * t + 8 * lg]);
-            f32x16 qacc0 = zero16(), qacc1 = zero16();
-#pragma unroll
-            for (int t = 0; t < BK / 16; t += 2) {
-              qacc0 = mfma(dsa[t], ktB[t], qacc0);
-              qacc1 = mfma(dsa[t + 1], ktB[t + 1], qacc1);
+            for (int t = 0; t < BK / 16; ++t) {
+              const int key = 16 * t + 4 * lg + (j >> 2);
+              const bf16x8 da = cat44(lds_tr4(sm.dst, dst_off(key, rcol)), lds_tr4(sm.dst, dst_off(key + 8, rcol)));
+              qacc = mfma(da, ktB[t], qacc);
             }
             // row i0 + 4 lg + c, column 32 w + lr: 32-bit offsets from a uniform base
-            float* dqb = a.dq + b * p.dq_str[0] + h * p.dq_str[1] + i0 * p.dq_str[2];
+            float* dqb = a.dq + b * p.dq_str[0] + h * p.dq_str[1] + (int64_t)i0 * p.dq_str[2] + 32 * w + lr;
             const int rs = (int)p.dq_str[2];
-            const int64_t rows_left = Sq - i0;
+            const int rows_left = Sq - i0;
 #pragma unroll
             for (int r = 0; r < 16; ++r) {
               const int c = 4 * lg + 8 * (r >> 2) + (r & 3);
-              if (c < rows_left) atomic_add_f32(dqb + (c * rs + 32 * w + lr), (qacc0[r] + qacc1[r]) * p.scale);
+              if (c < rows_left) atomic_add_f32(dqb + c * rs, qacc[r]);
             }
           }
         }
-        if (it + 1 < n_it) stg.store(sm, cur ^ 1, lo_al + (int64_t)BQ * qbn, Sq);
+        if (it + 1 < n_it) stg.store(sm, cur ^ 1, lo_al + BQ * qbn, Sq);
         __syncthreads();
         h = hn;
         qb = qbn;
       }
 
-      // Epilogue: dK * scale and dV for this wave's keys.
+      // Epilogue: dK (already scaled through dS) and dV for this wave's keys.
       float* dkp = a.dk + b * p.dk_str[0] + hk * p.dk_str[1];
       float* dvp = a.dv + b * p.dv_str[0] + hk * p.dv_str[1];
 #pragma unroll
@@ -412,13 +446,13 @@ __global__ __launch_bounds__(NT, 1) void k_dkdv(Params p, BwdArgs a, int pair, i
             float* pk = dkp + j * p.dk_str[2] + 32 * n + lr;
             float* pvv = dvp + j * p.dv_str[2] + 32 * n + lr;
             if (out_mode == kAtomicAdd) {
-              atomic_add_f32(pk, dk[n][r] * p.scale);
+              atomic_add_f32(pk, dk[n][r]);
               atomic_add_f32(pvv, dv[n][r]);
             } else if (out_mode == kAddInto) {
-              *pk += dk[n][r] * p.scale;
+              *pk += dk[n][r];
               *pvv += dv[n][r];
             } else {
-              *pk = dk[n][r] * p.scale;
+              *pk = dk[n][r];
               *pvv = dv[n][r];
             }
           }
@@ -562,6 +596,7 @@ __global__ __launch_bounds__(NT, 1) void k_dq(Params p, BwdArgs a) {
     lse2 = (lv == -INFINITY) ? INFINITY : lv * kLog2e;
     dl = a.delta[((int64_t)b * p.Hq + h) * Sq + irow];
   }
+  wait_vm_loads();
 
   // key tiles: the sink tiles [0, a1) and the band tiles [a2, a3)
   int64_t s_hi, b_lo, b_hi;
