@@ -76,77 +76,66 @@ __device__ inline f32x16 zero16() {
 // Row (within a 32-row accumulator block) held by lane group lg in register r.
 __device__ inline int crow(int r, int lg) { return 8 * (r >> 2) + 4 * lg + (r & 3); }
 
-// Row-major bf16 tiles of D columns in LDS, 16-byte chunks XOR-swizzled per
-// row: chunk c of row r sits at chunk position c ^ swz(r).  The swizzle makes
-// both access patterns of the kernels conflict-free: 16 lanes reading the
-// same chunk of 16 consecutive rows (ds_read_b128, A operands), and the
-// transposing read of 4 consecutive rows x 4 consecutive chunks (both
-// 4-aligned) by 32 lanes (ds_read_b64_tr_b16, B operands).
+// LDS layouts.  Every tile is row-major bf16 with a padded row stride, and
+// each access pattern gets a copy whose padding makes it bank-conflict-free
+// with per-lane addresses of the form  lane_base + compile-time offset:
+//   * "row" copies, stride D + 8: 16 lanes read 16 bytes of the same columns
+//     of 16 consecutive rows (A operands, ds_read_b128) -- consecutive rows
+//     start 4 banks apart;
+//   * "tr" copies, stride D + 32: 32 lanes read 4 consecutive rows x 64 bytes
+//     with the transposing ds_read_b64_tr_b16 (B operands whose reduction
+//     index is the tile row) -- consecutive rows start 16 banks apart.
 template <int D>
-__device__ inline int swz(int r) {
-  if constexpr (D == 128) return ((r & 3) << 2) | ((r >> 2) & 3);   // 16 chunks = 64 banks per row
-  else return (((r >> 1) & 1) << 2) | ((r >> 2) & 3);               // 8 chunks: two rows per 64 banks
+struct Lay {
+  static constexpr int R = D + 8;    // row-copy stride (elements)
+  static constexpr int T = D + 32;   // tr-copy stride (elements)
+};
+
+__device__ inline bf16x8 lds_b128(const unsigned short* tile, int off) {
+  return as_bf16x8(*(const u16x8*)(tile + off));
 }
 
-// Element offset of (row, 8-aligned column) in a swizzled tile.
-template <int D>
-__device__ inline int swz_off(int row, int col) {
-  return row * D + (((col >> 3) ^ swz<D>(row)) << 3) + (col & 7);
-}
-
-// 8 contiguous bf16 of one row (A operand: row, columns col..col+7).
-template <int D>
-__device__ inline bf16x8 lds_row8(const unsigned short* tile, int row, int col) {
-  return as_bf16x8(*(const u16x8*)(tile + swz_off<D>(row, col)));
-}
-
-// B operand (reduction over the tile's rows) of v_mfma_f32_32x32x16_bf16 for
-// output columns [n0, n0 + 32) and tile rows r0 + {4 lg + 0..3, 8 + 4 lg + 0..3}
-// (the slot order of the S / dS accumulators): lane l receives
-// tile[r0 + 4 lg + slot][n0 + l % 32].  ds_read_b64_tr_b16 hands lane j of
-// each 16-lane group element j % 4 of the 8-byte chunk addressed by lane
-// 4 r + j / 4 of that group, so lane i addresses row r0 + 4 lg + i / 4,
-// columns n0 + 16 ((l / 16) % 2) + 4 (i % 4).
-template <int D>
-__device__ inline bf16x8 lds_colB(const unsigned short* tile, int r0, int n0, int l) {
-  const int j = l & 15, lg = l >> 5;
-  const int col = n0 + 16 * ((l >> 4) & 1) + 4 * (j & 3);
-  const int row = r0 + 4 * lg + (j >> 2);
-  const auto* base = (__attribute__((address_space(3))) const unsigned short*)tile;
-  const s16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(base + swz_off<D>(row, col)));
-  const s16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(base + swz_off<D>(row + 8, col)));
-  return cat44(__builtin_bit_cast(u16x4, lo), __builtin_bit_cast(u16x4, hi));
-}
-
-// dS^T tile: row = key (BK rows of BQ = 32 bf16, 64 bytes), 8-byte slots
-// XOR-swizzled by key: slot c of key row k sits at slot c ^ ((k >> 2) & 7).
-// Conflict-free for the 32 lanes that write 8 bytes of 32 consecutive keys,
-// and for the transposing read of 4 consecutive keys x 32 rows.
-__device__ inline int dst_off(int key, int col) {
-  return key * BQ + ((((col >> 2) ^ (key >> 2)) & 7) << 2);
-}
-
-__device__ inline u16x4 lds_tr4(const unsigned short* base, int off) {
-  const auto* b = (__attribute__((address_space(3))) const unsigned short*)base;
+__device__ inline u16x4 lds_tr4(const unsigned short* tile, int off) {
+  const auto* b = (__attribute__((address_space(3))) const unsigned short*)tile;
   return __builtin_bit_cast(u16x4, __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(b + off)));
+}
+
+// Transposing-read lane base for a tile of stride `stride`: ds_read_b64_tr_b16
+// hands lane j of each 16-lane group element j % 4 of the 8-byte chunk
+// addressed by lane 4 r + j / 4 of that group.  Lane l therefore addresses
+// row 4 (l / 32) + (l % 16) / 4, column 16 ((l / 16) % 2) + 4 (l % 4); the
+// read at  base + r0 * stride + n0  (and + 8 rows) yields the B operand of a
+// 32x32x16 MFMA whose reduction slots are tile rows
+// r0 + {4 lg + 0..3, 8 + 4 lg + 0..3} -- the slot order of the S / dS
+// accumulators -- and whose output column is n0 + l % 32.
+__device__ inline int tr_base(int l, int stride) {
+  const int j = l & 15;
+  return (4 * (l >> 5) + (j >> 2)) * stride + 16 * ((l >> 4) & 1) + 4 * (j & 3);
+}
+
+__device__ inline bf16x8 lds_trB(const unsigned short* tile, int base, int r0, int n0, int stride) {
+  return cat44(lds_tr4(tile, base + r0 * stride + n0), lds_tr4(tile, base + (r0 + 8) * stride + n0));
 }
 
 template <int D>
 struct SmemDKDV {
-  unsigned short q[2][BQ * D];       // Q tile, swizzled row-major
-  unsigned short dO[2][BQ * D];      // dO tile, swizzled row-major
-  unsigned short dst[BK * BQ];       // dS^T tile [key][row], 8-byte slots swizzled (dst_off)
-  float lse2[2][BQ];                 // LSE * log2(e); +inf for rows without keys
-  float delta[2][BQ];
+  unsigned short qr[2][BQ * Lay<D>::R];   // Q tile, row copy  (A of S = Q K^T)
+  unsigned short dr[2][BQ * Lay<D>::R];   // dO tile, row copy (A of dP = dO V^T)
+  unsigned short qt[2][BQ * Lay<D>::T];   // Q tile, tr copy   (B of dK += dS^T Q)
+  unsigned short dt[2][BQ * Lay<D>::T];   // dO tile, tr copy  (B of dV += P^T dO)
+  unsigned short kt[BK * Lay<D>::T];      // K block, tr copy  (B of dQ = dS K)
+  unsigned short dst[2][BK * BQ];         // dS^T tiles [key][row] (A of dQ, tr reads)
+  float lse2[2][BQ];                      // LSE * log2(e); +inf for rows without keys
+  float dls[2][BQ];                       // delta * scale
 };
 
 // Per-thread staging of one 32-row Q / dO tile: the 2 x 32 x (D / 8)
 // 16-byte chunks are dealt round-robin to the threads (16 consecutive lanes
 // load one row's consecutive chunks); the last 32 threads carry the tile's
 // LSE and delta.  load() only issues the global loads (rows clamped into
-// range, so no branches and no use of the values); store() fixes up rows
-// past the end and writes LDS.  This keeps the loads in flight across the
-// whole iteration that prefetches them.
+// range, so no branches and no use of the values) and store() writes both
+// LDS copies.  Rows past the end hold a copy of the last row: finite, and
+// their LSE of +inf makes every P (and dS) of the row zero.
 template <int D>
 struct Stage {
   static constexpr int NCR = D / 8;               // chunks per row
@@ -156,40 +145,38 @@ struct Stage {
   float lse, dl;
 
   __device__ inline void load(const unsigned short* q, const unsigned short* dout, int64_t qs, int64_t ds,
-                              const float* lse_p, const float* dl_p, int64_t i0, int Sq) {
+                              const float* lse_p, const float* dl_p, int i0, int Sq) {
     const int t = threadIdx.x;
 #pragma unroll
     for (int k = 0; k < NR; ++k) {
       const int idx = t + NT * k;
       const int tensor = idx / (BQ * NCR), rem = idx % (BQ * NCR);
       const int row = rem / NCR, c = rem % NCR;
-      const int64_t i = min(i0 + row, (int64_t)Sq - 1);
+      const int64_t i = min(i0 + row, Sq - 1);
       v[k] = *(const u16x8*)((tensor == 0 ? q + i * qs : dout + i * ds) + 8 * c);
     }
     if (t >= NT - BQ) {
-      const int64_t i = min(i0 + (t - (NT - BQ)), (int64_t)Sq - 1);
+      const int64_t i = min(i0 + (t - (NT - BQ)), Sq - 1);
       lse = lse_p[i];
       dl = dl_p[i];
     }
   }
 
-  __device__ inline void store(SmemDKDV<D>& sm, int buf, int64_t i0, int Sq) const {
+  __device__ inline void store(SmemDKDV<D>& sm, int buf, int i0, int Sq, float scale) const {
     const int t = threadIdx.x;
 #pragma unroll
     for (int k = 0; k < NR; ++k) {
       const int idx = t + NT * k;
       const int tensor = idx / (BQ * NCR), rem = idx % (BQ * NCR);
       const int row = rem / NCR, c = rem % NCR;
-      // rows past the end hold a copy of the last row: finite, and their
-      // LSE of +inf makes every P (and dS) of the row zero
-      unsigned short* tile = tensor == 0 ? sm.q[buf] : sm.dO[buf];
-      *(u16x8*)(tile + swz_off<D>(row, 8 * c)) = v[k];
+      *(u16x8*)((tensor == 0 ? sm.qr[buf] : sm.dr[buf]) + row * Lay<D>::R + 8 * c) = v[k];
+      *(u16x8*)((tensor == 0 ? sm.qt[buf] : sm.dt[buf]) + row * Lay<D>::T + 8 * c) = v[k];
     }
     if (t >= NT - BQ) {
       const int r = t - (NT - BQ);
       const bool ok = i0 + r < Sq;
       sm.lse2[buf][r] = (!ok || lse == -INFINITY) ? INFINITY : lse * kLog2e;
-      sm.delta[buf][r] = ok ? dl : 0.f;
+      sm.dls[buf][r] = ok ? dl * scale : 0.f;
     }
   }
 };
@@ -212,6 +199,7 @@ __global__ __launch_bounds__(NT, 1) void k_dkdv(Params p, BwdArgs a, int pair, i
   static_assert(D == 64 || D == 128, "head dim");
   constexpr int NS = D / 16;          // k-steps over the head dim
   constexpr int NB = D / 32;          // 32-column blocks of the head dim
+  constexpr int R = Lay<D>::R, T = Lay<D>::T;
   __shared__ __attribute__((aligned(16))) SmemDKDV<D> sm;
 
   const int tid = threadIdx.x, w = tid >> 6, l = tid & 63, lr = l & 31, lg = l >> 5;
@@ -221,7 +209,7 @@ __global__ __launch_bounds__(NT, 1) void k_dkdv(Params p, BwdArgs a, int pair, i
   const int part = blockIdx.y % hsplit;
   const int gh = p.G / hsplit;                     // query heads handled here
   const int h_begin = hk * p.G + part * gh;
-  const float scale_log2 = p.scale * kLog2e;
+  const float scale = p.scale, scale_log2 = p.scale * kLog2e;
   const bool dq_wave = DQ_ATOMIC && (w < NB);
   const int kbx = blockIdx.x;
   const int n_units = (pair && nkb - 1 - kbx != kbx) ? 2 : 1;
@@ -229,6 +217,11 @@ __global__ __launch_bounds__(NT, 1) void k_dkdv(Params p, BwdArgs a, int pair, i
   // mask as t = j' - i' - diag:  allowed <=> lo_t <= t <= wr, or j' < n_sink
   const int lo_t = p.mask.wl < 0 ? -0x3fffffff : -p.mask.wl;
   const int wr_t = p.mask.wr;
+  // per-lane LDS bases
+  const int rowA = lr * R + 8 * lg;            // row-copy A operands: + 16 s
+  const int trQ = tr_base(l, T);               // tr-copy B operands
+  const int trS = tr_base(l, BQ);              // dS^T tr reads (row stride 32)
+  const int dsw = (32 * w + lr) * BQ + 4 * lg; // dS^T writes: + 8 m
 
   const int b_begin = BLOOP ? 0 : blockIdx.z;
   const int b_end = BLOOP ? p.B : b_begin + 1;
@@ -262,20 +255,16 @@ __global__ __launch_bounds__(NT, 1) void k_dkdv(Params p, BwdArgs a, int pair, i
           vB[s] = as_bf16x8(*(const u16x8*)(vp + jc * p.v_str[2] + 16 * s + 8 * lg));
         }
       }
-      // K fragments for dQ = dS K (B operand, head-dim column 32 w + lr) in
-      // the key order of the dS^T transposing read: slot e of step t is key
-      // 16 t + 8 (e / 4) + 4 lg + e % 4.
-      bf16x8 ktB[BK / 16];
-      if (dq_wave) {
+      __syncthreads();  // readers of the previous unit's LDS tiles are done
+      if (DQ_ATOMIC) {
+        // the K block's tr copy (B operand of dQ = dS K)
+        constexpr int NCR = D / 8;
 #pragma unroll
-        for (int t = 0; t < BK / 16; ++t) {
-          u16x8 uu;
-#pragma unroll
-          for (int e = 0; e < 8; ++e) {
-            const int j = k0 + 16 * t + 8 * (e >> 2) + 4 * lg + (e & 3);
-            uu[e] = kp[(int64_t)min(j, Sk - 1) * p.k_str[2] + 32 * w + lr];
-          }
-          ktB[t] = as_bf16x8(uu);
+        for (int m = 0; m < BK * NCR / NT; ++m) {
+          const int idx = tid + NT * m;
+          const int row = idx / NCR, c = idx % NCR;
+          const int64_t j = min(k0 + row, Sk - 1);
+          *(u16x8*)(sm.kt + row * T + 8 * c) = *(const u16x8*)(kp + j * p.k_str[2] + 8 * c);
         }
       }
       f32x16 dk[NB], dv[NB];
@@ -289,12 +278,43 @@ __global__ __launch_bounds__(NT, 1) void k_dkdv(Params p, BwdArgs a, int pair, i
                  (const unsigned short*)a.dout + b * p.do_str[0] + h * p.do_str[1], p.q_str[2], p.do_str[2],
                  a.lse + ((int64_t)b * p.Hq + h) * Sq, a.delta + ((int64_t)b * p.Hq + h) * Sq, i0, Sq);
       };
+      // dQ += dS K for the tile (head hh, rows ii..ii+31) whose dS^T sits in
+      // buffer buf: wave w < NB produces head-dim columns [32 w, 32 w + 32)
+      // and adds them to global dQ with fp32 atomics.
+      auto dq_tile = [&](int buf, int hh, int ii) {
+        if (!dq_wave) return;
+        f32x16 qacc = zero16();
+#pragma unroll
+        for (int t0 = 0; t0 < BK / 16; t0 += 4) {
+          bf16x8 sA[4], kT[4];
+#pragma unroll
+          for (int t = 0; t < 4; ++t) {
+            sA[t] = lds_trB(sm.dst[buf], trS, 16 * (t0 + t), 0, BQ);
+            kT[t] = lds_trB(sm.kt, trQ, 16 * (t0 + t), 32 * w, T);
+          }
+#pragma unroll
+          for (int t = 0; t < 4; ++t) qacc = mfma(sA[t], kT[t], qacc);
+        }
+        // row ii + 4 lg + c, column 32 w + lr: 32-bit offsets from a uniform base
+        float* dqb = a.dq + b * p.dq_str[0] + hh * p.dq_str[1] + (int64_t)ii * p.dq_str[2] + 32 * w + lr;
+        const int rs = (int)p.dq_str[2];
+        const int rows_left = Sq - ii;
+        if (rows_left >= BQ) {
+#pragma unroll
+          for (int r = 0; r < 16; ++r) atomic_add_f32(dqb + (4 * lg + 8 * (r >> 2) + (r & 3)) * rs, qacc[r]);
+        } else {
+#pragma unroll
+          for (int r = 0; r < 16; ++r) {
+            const int c = 4 * lg + 8 * (r >> 2) + (r & 3);
+            if (c < rows_left) atomic_add_f32(dqb + c * rs, qacc[r]);
+          }
+        }
+      };
       // (head, row-tile) of the current iteration, advanced incrementally
       int h = h_begin, qb = 0;
       if (n_it > 0) {
         issue(h, lo_al);
-        __syncthreads();  // readers of buffer 0 from the previous unit are done
-        stg.store(sm, 0, lo_al, Sq);
+        stg.store(sm, 0, lo_al, Sq, scale);
         __syncthreads();
       }
 
@@ -306,27 +326,47 @@ __global__ __launch_bounds__(NT, 1) void k_dkdv(Params p, BwdArgs a, int pair, i
         if (it + 1 < n_it) issue(hn, lo_al + BQ * qbn);
 
         // S = Q K^T and dP = dO V^T for rows i0..i0+31, this wave's 32 keys.
+        // The A operands are read from LDS in bulk ahead of the products, so
+        // the read latency is paid once rather than once per product.
         f32x16 sacc = zero16(), dpacc = zero16();
+        {
+          bf16x8 qa[NS], da[NS];
 #pragma unroll
-        for (int s = 0; s < NS; ++s) {
-          const bf16x8 qa = lds_row8<D>(sm.q[cur], lr, 16 * s + 8 * lg);
-          const bf16x8 da = lds_row8<D>(sm.dO[cur], lr, 16 * s + 8 * lg);
-          sacc = mfma(qa, kB[s], sacc);
-          dpacc = mfma(da, vB[s], dpacc);
+          for (int s = 0; s < NS; ++s) {
+            qa[s] = lds_b128(sm.qr[cur], rowA + 16 * s);
+            da[s] = lds_b128(sm.dr[cur], rowA + 16 * s);
+          }
+#pragma unroll
+          for (int s = 0; s < NS; ++s) {
+            sacc = mfma(qa[s], kB[s], sacc);
+            dpacc = mfma(da[s], vB[s], dpacc);
+          }
         }
-        // B fragments of the first head-dim block for dV / dK (independent of P)
-        bf16x8 o0 = lds_colB<D>(sm.dO[cur], 0, 0, l), o1 = lds_colB<D>(sm.dO[cur], 16, 0, l);
-        bf16x8 q0 = lds_colB<D>(sm.q[cur], 0, 0, l), q1 = lds_colB<D>(sm.q[cur], 16, 0, l);
-        // LSE (log2 units) and delta of this lane's 16 rows: rows 8 m + 4 lg + 0..3
+        // B operands of dV += P^T dO and dK += dS^T Q for the first two
+        // head-dim blocks (independent of P): their reads overlap the
+        // elementwise step below; the rest are read while those multiply.
+        constexpr int NPF = NB < 2 ? NB : 2;
+        bf16x8 oB[NB][2], qB[NB][2];
+#pragma unroll
+        for (int n = 0; n < NPF; ++n) {
+#pragma unroll
+          for (int hf = 0; hf < 2; ++hf) {
+            oB[n][hf] = lds_trB(sm.dt[cur], trQ, 16 * hf, 32 * n, T);
+            qB[n][hf] = lds_trB(sm.qt[cur], trQ, 16 * hf, 32 * n, T);
+          }
+        }
+        // LSE (log2 units) and delta * scale of this lane's 16 rows: rows 8 m + 4 lg + 0..3
         f32x4 L4[4], D4[4];
 #pragma unroll
         for (int m = 0; m < 4; ++m) {
           L4[m] = *(const f32x4*)&sm.lse2[cur][8 * m + 4 * lg];
-          D4[m] = *(const f32x4*)&sm.delta[cur][8 * m + 4 * lg];
+          D4[m] = *(const f32x4*)&sm.dls[cur][8 * m + 4 * lg];
         }
 
-        // P = exp(S - LSE) on allowed pairs, dS = P (dP - delta).  Tiles that
-        // are entirely allowed (the bulk under causal masks) skip the mask.
+        // P = exp(S - LSE) on allowed pairs; dS = P (dP - delta), carried
+        // pre-multiplied by the softmax scale (the factor of dK and dQ).
+        // Tiles that are entirely allowed (the bulk under causal masks) skip
+        // the mask.
         const bool full = wave_keys_in && p.mask.tile_full(i0, i0 + BQ, kw, kw + 32);
         float pv[16], dsv[16];
         if (full) {
@@ -338,7 +378,7 @@ __global__ __launch_bounds__(NT, 1) void k_dkdv(Params p, BwdArgs a, int pair, i
               if (i < Sq) x += a.bias[h * p.bias_str[0] + (int64_t)i * p.bias_str[1] + jkey] * kLog2e;
             }
             pv[r] = __builtin_amdgcn_exp2f(x);
-            dsv[r] = pv[r] * (dpacc[r] - D4[r >> 2][r & 3]);
+            dsv[r] = pv[r] * fmaf(dpacc[r], scale, -D4[r >> 2][r & 3]);
           }
         } else {
           const int tb = jg - (i0 + (int)p.mask.q_off) - (int)p.mask.diag - 4 * lg;
@@ -353,88 +393,66 @@ __global__ __launch_bounds__(NT, 1) void k_dkdv(Params p, BwdArgs a, int pair, i
               if (i < Sq && key_ok) x += a.bias[h * p.bias_str[0] + (int64_t)i * p.bias_str[1] + jkey] * kLog2e;
             }
             pv[r] = ok ? __builtin_amdgcn_exp2f(x) : 0.f;
-            dsv[r] = pv[r] * (dpacc[r] - D4[r >> 2][r & 3]);
+            dsv[r] = pv[r] * fmaf(dpacc[r], scale, -D4[r >> 2][r & 3]);
           }
         }
         if (BIAS && a.dbias) {
+          // dbias takes the unscaled dS
+          const float inv_scale = 1.f / scale;
 #pragma unroll
           for (int r = 0; r < 16; ++r) {
             const int i = i0 + crow(r, lg);
             if (i < Sq && key_ok && pv[r] != 0.f) {
               float* dst = a.dbias + h * p.bias_str[0] + (int64_t)i * p.bias_str[1] + jkey;
               if (BLOOP)
-                *dst += dsv[r];
+                *dst += dsv[r] * inv_scale;
               else
-                atomic_add_f32(dst, dsv[r]);
+                atomic_add_f32(dst, dsv[r] * inv_scale);
             }
           }
         }
-        // the softmax scale of dK and dQ is folded into the dS operand
-#pragma unroll
-        for (int r = 0; r < 16; ++r) dsv[r] *= p.scale;
         const bf16x8 pa0 = pack8(pv), pa1 = pack8(pv + 8);
         const bf16x8 sa0 = pack8(dsv), sa1 = pack8(dsv + 8);
 
         // dV += P^T dO and dK += dS^T Q (reduction over the 32 rows, permuted
-        // consistently with the accumulator layout of S); the fragments of
-        // block n + 1 are read while block n multiplies.
+        // consistently with the accumulator layout of S).
+#pragma unroll
+        for (int n = NPF; n < NB; ++n) {
+#pragma unroll
+          for (int hf = 0; hf < 2; ++hf) {
+            oB[n][hf] = lds_trB(sm.dt[cur], trQ, 16 * hf, 32 * n, T);
+            qB[n][hf] = lds_trB(sm.qt[cur], trQ, 16 * hf, 32 * n, T);
+          }
+        }
 #pragma unroll
         for (int n = 0; n < NB; ++n) {
-          bf16x8 o0n = o0, o1n = o1, q0n = q0, q1n = q1;
-          if (n + 1 < NB) {
-            const int n0 = 32 * (n + 1);
-            o0n = lds_colB<D>(sm.dO[cur], 0, n0, l);
-            o1n = lds_colB<D>(sm.dO[cur], 16, n0, l);
-            q0n = lds_colB<D>(sm.q[cur], 0, n0, l);
-            q1n = lds_colB<D>(sm.q[cur], 16, n0, l);
-          }
-          dv[n] = mfma(pa0, o0, dv[n]);
-          dk[n] = mfma(sa0, q0, dk[n]);
-          dv[n] = mfma(pa1, o1, dv[n]);
-          dk[n] = mfma(sa1, q1, dk[n]);
-          o0 = o0n; o1 = o1n; q0 = q0n; q1 = q1n;
+          dv[n] = mfma(pa0, oB[n][0], dv[n]);
+          dk[n] = mfma(sa0, qB[n][0], dk[n]);
+          dv[n] = mfma(pa1, oB[n][1], dv[n]);
+          dk[n] = mfma(sa1, qB[n][1], dk[n]);
         }
 
         if (DQ_ATOMIC) {
-          // dS^T to LDS: this lane's key row, query rows 8 m + 4 lg + 0..3.
-          {
-            const u16x8 s0 = __builtin_bit_cast(u16x8, sa0), s1 = __builtin_bit_cast(u16x8, sa1);
-            const int key = 32 * w + lr;
-            *(u16x4*)&sm.dst[dst_off(key, 4 * lg)] = u16x4{s0[0], s0[1], s0[2], s0[3]};
-            *(u16x4*)&sm.dst[dst_off(key, 8 + 4 * lg)] = u16x4{s0[4], s0[5], s0[6], s0[7]};
-            *(u16x4*)&sm.dst[dst_off(key, 16 + 4 * lg)] = u16x4{s1[0], s1[1], s1[2], s1[3]};
-            *(u16x4*)&sm.dst[dst_off(key, 24 + 4 * lg)] = u16x4{s1[4], s1[5], s1[6], s1[7]};
-          }
-          __syncthreads();
-          if (dq_wave) {
-            // A operand of dQ = dS K: rows l % 32, keys 16 t + {4 lg + 0..3, 8 + 4 lg + 0..3}
-            const int j = l & 15;
-            const int rcol = 16 * ((l >> 4) & 1) + 4 * (j & 3);
-            f32x16 qacc = zero16();
-#pragma unroll
-            for (int t = 0; t < BK / 16; ++t) {
-              const int key = 16 * t + 4 * lg + (j >> 2);
-              const bf16x8 da = cat44(lds_tr4(sm.dst, dst_off(key, rcol)), lds_tr4(sm.dst, dst_off(key + 8, rcol)));
-              qacc = mfma(da, ktB[t], qacc);
-            }
-            // row i0 + 4 lg + c, column 32 w + lr: 32-bit offsets from a uniform base
-            float* dqb = a.dq + b * p.dq_str[0] + h * p.dq_str[1] + (int64_t)i0 * p.dq_str[2] + 32 * w + lr;
-            const int rs = (int)p.dq_str[2];
-            const int rows_left = Sq - i0;
-#pragma unroll
-            for (int r = 0; r < 16; ++r) {
-              const int c = 4 * lg + 8 * (r >> 2) + (r & 3);
-              if (c < rows_left) atomic_add_f32(dqb + c * rs, qacc[r]);
-            }
-          }
+          // dS^T of this tile to LDS (this lane's key row, query rows
+          // 8 m + 4 lg + 0..3); its dQ product runs after the barrier that
+          // ends this iteration.
+          const u16x8 s0 = __builtin_bit_cast(u16x8, sa0), s1 = __builtin_bit_cast(u16x8, sa1);
+          unsigned short* dt = sm.dst[cur];
+          *(u16x4*)&dt[dsw] = u16x4{s0[0], s0[1], s0[2], s0[3]};
+          *(u16x4*)&dt[dsw + 8] = u16x4{s0[4], s0[5], s0[6], s0[7]};
+          *(u16x4*)&dt[dsw + 16] = u16x4{s1[0], s1[1], s1[2], s1[3]};
+          *(u16x4*)&dt[dsw + 24] = u16x4{s1[4], s1[5], s1[6], s1[7]};
         }
-        if (it + 1 < n_it) stg.store(sm, cur ^ 1, lo_al + BQ * qbn, Sq);
+        if (it + 1 < n_it) stg.store(sm, cur ^ 1, lo_al + BQ * qbn, Sq, scale);
         __syncthreads();
+        // dQ of this tile, from the dS^T the barrier just published; the
+        // buffer is rewritten two iterations later, after another barrier
+        if (DQ_ATOMIC) dq_tile(cur, h, i0);
         h = hn;
         qb = qbn;
       }
 
-      // Epilogue: dK (already scaled through dS) and dV for this wave's keys.
+      // Epilogue: dK (scaled through dS) and dV for this wave's keys.
       float* dkp = a.dk + b * p.dk_str[0] + hk * p.dk_str[1];
       float* dvp = a.dv + b * p.dv_str[0] + hk * p.dv_str[1];
 #pragma unroll
@@ -520,8 +538,9 @@ constexpr int BK3 = 32;    // keys per iteration (k_dq)
 
 template <int D>
 struct SmemDQ {
-  unsigned short k[2][BK3 * D];      // K tile, swizzled row-major
-  unsigned short v[2][BK3 * D];      // V tile, swizzled row-major
+  unsigned short kr[2][BK3 * Lay<D>::R];   // K tile, row copy (A of S^T = K Q^T)
+  unsigned short vr[2][BK3 * Lay<D>::R];   // V tile, row copy (A of dP^T = V dO^T)
+  unsigned short kt[2][BK3 * Lay<D>::T];   // K tile, tr copy  (B of dQ += dS K)
 };
 
 // Staging of one 32-key K / V tile (same dealing of 16-byte chunks as Stage).
@@ -545,34 +564,39 @@ struct StageKV {
     }
   }
 
-  __device__ inline void store(SmemDQ<D>& sm, int buf, int64_t j0, int Sk) const {
+  // keys past the end hold the last key: finite, and masked to P = 0
+  __device__ inline void store(SmemDQ<D>& sm, int buf) const {
     const int t = threadIdx.x;
 #pragma unroll
     for (int m = 0; m < NR; ++m) {
       const int idx = t + NT * m;
       const int tensor = idx / (BK3 * NCR), rem = idx % (BK3 * NCR);
       const int row = rem / NCR, c = rem % NCR;
-      const bool ok = j0 + row < Sk;
-      u16x8 x;
-#pragma unroll
-      for (int e = 0; e < 8; ++e) x[e] = ok ? v[m][e] : (unsigned short)0;
-      *(u16x8*)((tensor == 0 ? sm.k[buf] : sm.v[buf]) + swz_off<D>(row, 8 * c)) = x;
+      if (tensor == 0) {
+        *(u16x8*)(sm.kr[buf] + row * Lay<D>::R + 8 * c) = v[m];
+        *(u16x8*)(sm.kt[buf] + row * Lay<D>::T + 8 * c) = v[m];
+      } else {
+        *(u16x8*)(sm.vr[buf] + row * Lay<D>::R + 8 * c) = v[m];
+      }
     }
   }
 };
 
 template <int D, bool BIAS>
-__global__ __launch_bounds__(NT, 1) void k_dq(Params p, BwdArgs a) {
+__global__ __launch_bounds__(NT, 2) void k_dq(Params p, BwdArgs a) {
   constexpr int NS = D / 16;
   constexpr int NB = D / 32;
+  constexpr int R = Lay<D>::R, T = Lay<D>::T;
   __shared__ __attribute__((aligned(16))) SmemDQ<D> sm;
 
   const int tid = threadIdx.x, w = tid >> 6, l = tid & 63, lr = l & 31, lg = l >> 5;
   const int i0 = blockIdx.x * BQ3;
   const int h = blockIdx.y, b = blockIdx.z, g = h / p.G;
   const int Sq = p.Sq, Sk = p.Sk;
-  const int64_t irow = i0 + 32 * w + lr;       // this lane's query row
-  const float scale_log2 = p.scale * kLog2e;
+  const int irow = i0 + 32 * w + lr;           // this lane's query row
+  const float scale = p.scale, scale_log2 = p.scale * kLog2e;
+  const int rowA = lr * R + 8 * lg;
+  const int trK = tr_base(l, T);
 
   const unsigned short* q = (const unsigned short*)a.q + b * p.q_str[0] + h * p.q_str[1];
   const unsigned short* dout = (const unsigned short*)a.dout + b * p.do_str[0] + h * p.do_str[1];
@@ -580,21 +604,19 @@ __global__ __launch_bounds__(NT, 1) void k_dq(Params p, BwdArgs a) {
   const unsigned short* vp = (const unsigned short*)a.v + b * p.v_str[0] + g * p.v_str[1];
 
   bf16x8 qB[NS], doB[NS];
+  {
+    const int64_t ic = min(irow, Sq - 1);
 #pragma unroll
-  for (int s = 0; s < NS; ++s) {
-    if (irow < Sq) {
-      qB[s] = as_bf16x8(*(const u16x8*)(q + irow * p.q_str[2] + 16 * s + 8 * lg));
-      doB[s] = as_bf16x8(*(const u16x8*)(dout + irow * p.do_str[2] + 16 * s + 8 * lg));
-    } else {
-      qB[s] = as_bf16x8(u16x8{0, 0, 0, 0, 0, 0, 0, 0});
-      doB[s] = qB[s];
+    for (int s = 0; s < NS; ++s) {
+      qB[s] = as_bf16x8(*(const u16x8*)(q + ic * p.q_str[2] + 16 * s + 8 * lg));
+      doB[s] = as_bf16x8(*(const u16x8*)(dout + ic * p.do_str[2] + 16 * s + 8 * lg));
     }
   }
-  float lse2 = INFINITY, dl = 0.f;
+  float lse2 = INFINITY, dls = 0.f;
   if (irow < Sq) {
     const float lv = a.lse[((int64_t)b * p.Hq + h) * Sq + irow];
     lse2 = (lv == -INFINITY) ? INFINITY : lv * kLog2e;
-    dl = a.delta[((int64_t)b * p.Hq + h) * Sq + irow];
+    dls = a.delta[((int64_t)b * p.Hq + h) * Sq + irow] * scale;
   }
   wait_vm_loads();
 
@@ -609,6 +631,9 @@ __global__ __launch_bounds__(NT, 1) void k_dq(Params p, BwdArgs a) {
   const int n1 = a1, n2 = a3 > a2 ? a3 - a2 : 0;
   const int n_it = i0 < Sq ? n1 + n2 : 0;
   auto tile_of = [&](int it) { return (int64_t)BK3 * (it < n1 ? it : a2 + (it - n1)); };
+  const bool no_mask = p.mask.kind == kMaskNone;
+  const int lo_t = p.mask.wl < 0 ? -0x3fffffff : -p.mask.wl;
+  const int wr_t = p.mask.wr;
 
   f32x16 dq[NB];
 #pragma unroll
@@ -617,48 +642,52 @@ __global__ __launch_bounds__(NT, 1) void k_dq(Params p, BwdArgs a) {
   StageKV<D> stg;
   if (n_it > 0) {
     stg.load(kp, vp, p.k_str[2], p.v_str[2], tile_of(0), Sk);
-    stg.store(sm, 0, tile_of(0), Sk);
+    stg.store(sm, 0);
     __syncthreads();
   }
   for (int it = 0; it < n_it; ++it) {
     const int cur = it & 1;
-    const int64_t j0 = tile_of(it);
+    const int j0 = (int)tile_of(it);
     if (it + 1 < n_it) stg.load(kp, vp, p.k_str[2], p.v_str[2], tile_of(it + 1), Sk);
 
+    // S^T = K Q^T and dP^T = V dO^T: keys on accumulator rows, this lane's row on the column
     f32x16 sacc = zero16(), dpacc = zero16();
 #pragma unroll
     for (int s = 0; s < NS; ++s) {
-      const bf16x8 ka = lds_row8<D>(sm.k[cur], lr, 16 * s + 8 * lg);
-      const bf16x8 va = lds_row8<D>(sm.v[cur], lr, 16 * s + 8 * lg);
-      sacc = mfma(ka, qB[s], sacc);
-      dpacc = mfma(va, doB[s], dpacc);
+      sacc = mfma(lds_b128(sm.kr[cur], rowA + 16 * s), qB[s], sacc);
+      dpacc = mfma(lds_b128(sm.vr[cur], rowA + 16 * s), doB[s], dpacc);
     }
     const bool full = (j0 + BK3 <= Sk) && p.mask.tile_full(i0 + 32 * w, i0 + 32 * w + 32, j0, j0 + BK3);
+    // t = j' - i' - diag for key j0 + 4 lg + c
+    const int tb = j0 + (int)p.mask.k_off + 4 * lg - (irow + (int)p.mask.q_off) - (int)p.mask.diag;
     float dsv[16];
 #pragma unroll
     for (int r = 0; r < 16; ++r) {
-      const int64_t j = j0 + crow(r, lg);
-      float x = sacc[r] * scale_log2;
+      const int c = 8 * (r >> 2) + (r & 3);
+      const int j = j0 + 4 * lg + c;
+      float x = fmaf(sacc[r], scale_log2, -lse2);
       if (BIAS) {
-        if (irow < Sq && j < Sk) x += a.bias[h * p.bias_str[0] + irow * p.bias_str[1] + j] * kLog2e;
+        if (irow < Sq && j < Sk) x += a.bias[h * p.bias_str[0] + (int64_t)irow * p.bias_str[1] + j] * kLog2e;
       }
-      float pp = exp2f(x - lse2);
-      if (!full && !(j < Sk && p.mask.allowed(irow, j))) pp = 0.f;
-      dsv[r] = pp * (dpacc[r] - dl);
+      float pp = __builtin_amdgcn_exp2f(x);
+      if (!full) {
+        const int t = tb + c;
+        const bool ok = j < Sk && (no_mask || (t <= wr_t && t >= lo_t) || (j + (int)p.mask.k_off) < p.mask.n_sink);
+        pp = ok ? pp : 0.f;
+      }
+      dsv[r] = pp * fmaf(dpacc[r], scale, -dls);
     }
     const bf16x8 sa0 = pack8(dsv), sa1 = pack8(dsv + 8);
 #pragma unroll
     for (int n = 0; n < NB; ++n) {
-      const bf16x8 k0v = lds_colB<D>(sm.k[cur], 0, 32 * n, l);
-      const bf16x8 k1v = lds_colB<D>(sm.k[cur], 16, 32 * n, l);
-      dq[n] = mfma(sa0, k0v, dq[n]);
-      dq[n] = mfma(sa1, k1v, dq[n]);
+      dq[n] = mfma(sa0, lds_trB(sm.kt[cur], trK, 0, 32 * n, T), dq[n]);
+      dq[n] = mfma(sa1, lds_trB(sm.kt[cur], trK, 16, 32 * n, T), dq[n]);
     }
-    if (it + 1 < n_it) stg.store(sm, cur ^ 1, tile_of(it + 1), Sk);
+    if (it + 1 < n_it) stg.store(sm, cur ^ 1);
     __syncthreads();
   }
 
-  // dQ rows i0 + 32 w + crow(r, lg), columns 32 n + lr.
+  // dQ rows i0 + 32 w + crow(r, lg), columns 32 n + lr (already scaled through dS).
   float* dqp = a.dq + b * p.dq_str[0] + h * p.dq_str[1];
 #pragma unroll
   for (int n = 0; n < NB; ++n) {
@@ -667,8 +696,7 @@ __global__ __launch_bounds__(NT, 1) void k_dq(Params p, BwdArgs a) {
       const int64_t i = i0 + 32 * w + crow(r, lg);
       if (i < Sq) {
         float* dst = dqp + i * p.dq_str[2] + 32 * n + lr;
-        const float val = dq[n][r] * p.scale;
-        *dst = a.accumulate_dq ? *dst + val : val;
+        *dst = a.accumulate_dq ? *dst + dq[n][r] : dq[n][r];
       }
     }
   }
