@@ -27,6 +27,8 @@
 //   A[m][k]: lane holds m = l % 32, k = 8 (l / 32) + 0..7
 //   B[k][n]: lane holds n = l % 32, k = 8 (l / 32) + 0..7
 //   C[m][n]: lane holds n = l % 32, m = 8 (r / 4) + 4 (l / 32) + r % 4
+#include <algorithm>
+
 #include "kernels.h"
 
 namespace attn {
@@ -184,18 +186,29 @@ struct Stage {
 // How a dK/dV accumulator reaches global memory.
 enum : int { kStore = 0, kAtomicAdd = 1, kAddInto = 2 };
 
-// Work of one workgroup: key block(s) `kb0` (and `nkb - 1 - kb0` when
-// paired), query heads [h_begin, h_end) of KV head hk.
+// How the key blocks of a KV head are dealt to workgroups.
 //
+// A unit is one key block of one KV head; its work is the list of
+// (query head of the group, 32-row query tile) iterations that can see it.
 // Pairing: under a causal mask the number of query rows that see key block
 // kb falls linearly with kb, so block kb and block nkb-1-kb together cost the
 // same for every pair -- one pair per workgroup balances the grid.
-// Head split: the G query heads of a group may be split in two halves
-// handled by two workgroups; each adds its partial dK/dV into zeroed
-// outputs.  With exactly two addends onto zero the fp32 result does not
-// depend on their order, so the result stays deterministic.
+// Splitting: a unit's iteration list may be cut into `nsplit` contiguous
+// parts handled by separate workgroups, each adding its partial dK/dV into
+// zeroed outputs.  With exactly two addends onto zero the fp32 result does
+// not depend on their order, so a two-way split stays deterministic.
+// Sink block: with sink tokens under a sliding window, key block 0 is seen by
+// every query row while the others see only a band; it gets `nsplit0` parts,
+// dealt first (blockIdx.x < nsplit0).
+struct DkdvGrid {
+  int pair;      // complementary key blocks per workgroup
+  int nsplit;    // parts per unit (blockIdx.y = hk * nsplit + part)
+  int nsplit0;   // parts of key block 0 (1 = no separate treatment)
+  int out_mode;  // kStore / kAtomicAdd / kAddInto
+};
+
 template <int D, bool BIAS, bool DQ_ATOMIC, bool BLOOP>
-__global__ __launch_bounds__(NT, 1) void k_dkdv(Params p, BwdArgs a, int pair, int hsplit, int out_mode) {
+__global__ __launch_bounds__(NT, 1) void k_dkdv(Params p, BwdArgs a, DkdvGrid gd) {
   static_assert(D == 64 || D == 128, "head dim");
   constexpr int NS = D / 16;          // k-steps over the head dim
   constexpr int NB = D / 32;          // 32-column blocks of the head dim
@@ -205,14 +218,23 @@ __global__ __launch_bounds__(NT, 1) void k_dkdv(Params p, BwdArgs a, int pair, i
   const int tid = threadIdx.x, w = tid >> 6, l = tid & 63, lr = l & 31, lg = l >> 5;
   const int Sq = p.Sq, Sk = p.Sk;
   const int nkb = (Sk + BK - 1) / BK;
-  const int hk = blockIdx.y / hsplit;
-  const int part = blockIdx.y % hsplit;
-  const int gh = p.G / hsplit;                     // query heads handled here
-  const int h_begin = hk * p.G + part * gh;
+  const int hk = blockIdx.y / gd.nsplit;
+  int part = blockIdx.y % gd.nsplit, nparts = gd.nsplit;
+  int kbx = blockIdx.x;
+  if (gd.nsplit0 > 1) {
+    if (kbx < gd.nsplit0) {
+      part = kbx * gd.nsplit + part;
+      nparts = gd.nsplit0 * gd.nsplit;
+      kbx = 0;
+    } else {
+      kbx -= gd.nsplit0 - 1;
+    }
+  }
+  const int h_begin = hk * p.G;
   const float scale = p.scale, scale_log2 = p.scale * kLog2e;
   const bool dq_wave = DQ_ATOMIC && (w < NB);
-  const int kbx = blockIdx.x;
-  const int n_units = (pair && nkb - 1 - kbx != kbx) ? 2 : 1;
+  const int n_units = (gd.pair && nkb - 1 - kbx != kbx) ? 2 : 1;
+  const int out_mode = gd.out_mode;
   const bool no_mask = p.mask.kind == kMaskNone;
   // mask as t = j' - i' - diag:  allowed <=> lo_t <= t <= wr, or j' < n_sink
   const int lo_t = p.mask.wl < 0 ? -0x3fffffff : -p.mask.wl;
@@ -240,7 +262,10 @@ __global__ __launch_bounds__(NT, 1) void k_dkdv(Params p, BwdArgs a, int pair, i
       const int lo = (int)lo64, hi = (int)hi64;
       const int lo_al = lo & ~(BQ - 1);
       const int nqb = hi > lo ? (hi - lo_al + BQ - 1) / BQ : 0;
-      const int n_it = gh * nqb;
+      // this part's slice [it_lo, it_hi) of the unit's G * nqb iterations
+      const int n_all = p.G * nqb;
+      const int it_lo = (int)((int64_t)n_all * part / nparts);
+      const int n_it = (int)((int64_t)n_all * (part + 1) / nparts) - it_lo;
 
       const unsigned short* kp = (const unsigned short*)a.k + b * p.k_str[0] + hk * p.k_str[1];
       const unsigned short* vp = (const unsigned short*)a.v + b * p.v_str[0] + hk * p.v_str[1];
@@ -311,10 +336,10 @@ __global__ __launch_bounds__(NT, 1) void k_dkdv(Params p, BwdArgs a, int pair, i
         }
       };
       // (head, row-tile) of the current iteration, advanced incrementally
-      int h = h_begin, qb = 0;
+      int h = h_begin + (nqb > 0 ? it_lo / nqb : 0), qb = nqb > 0 ? it_lo % nqb : 0;
       if (n_it > 0) {
-        issue(h, lo_al);
-        stg.store(sm, 0, lo_al, Sq, scale);
+        issue(h, lo_al + BQ * qb);
+        stg.store(sm, 0, lo_al + BQ * qb, Sq, scale);
         __syncthreads();
       }
 
@@ -482,33 +507,46 @@ __global__ __launch_bounds__(NT, 1) void k_dkdv(Params p, BwdArgs a, int pair, i
 
 // Grid shape of k_dkdv for a problem (host side).
 struct DkdvPlan {
-  int pair, hsplit, out_mode;
+  DkdvGrid g;
   dim3 grid;
 };
 
 DkdvPlan plan_dkdv(const Params& p, bool bloop, bool accumulate_dkdv, bool deterministic) {
   DkdvPlan pl{};
   const int nkb = (p.Sk + BK - 1) / BK;
+  const Mask& m = p.mask;
   // causal-like masks (no lower window bound): work per key block decreases
   // monotonically, so complementary blocks pair up evenly
-  pl.pair = (p.mask.kind != kMaskNone && p.mask.wl < 0 && nkb > 1) ? 1 : 0;
-  const int xblocks = pl.pair ? (nkb + 1) / 2 : nkb;
+  pl.g.pair = (m.kind != kMaskNone && m.wl < 0 && nkb > 1) ? 1 : 0;
+  const int xblocks = pl.g.pair ? (nkb + 1) / 2 : nkb;
   const int64_t units = (int64_t)xblocks * p.Hk * (bloop ? 1 : p.B);
-  // Split the query heads of a group over two workgroups when the grid would
-  // not fill the chip twice over.  Two addends onto zeroed outputs sum in
-  // either order to the same fp32 value; adding two partials into existing
-  // values would not, so deterministic accumulation keeps one workgroup per
-  // key block.
-  pl.hsplit = (!bloop && !(accumulate_dkdv && deterministic) && p.G % 2 == 0 && units < 2 * 256) ? 2 : 1;
-  pl.out_mode = pl.hsplit > 1 ? kAtomicAdd : (accumulate_dkdv ? kAddInto : kStore);
-  pl.grid = dim3(xblocks, p.Hk * pl.hsplit, bloop ? 1 : p.B);
+  // Partial dK/dV go through atomic adds onto zeroed outputs: never with the
+  // batch loop (its dbias is ordered), and only two-way when the result must
+  // be deterministic -- two partials into existing values would not be.
+  const bool can_split = !bloop && !(accumulate_dkdv && deterministic);
+  const int max_parts = deterministic ? 2 : 8;
+  pl.g.nsplit = (can_split && p.G % 2 == 0 && units < 2 * 256) ? 2 : 1;
+  // the sink key block under a sliding window sees every row
+  const bool sink_block = m.kind != kMaskNone && m.wl >= 0 && m.n_sink > m.k_off && nkb > 1;
+  pl.g.nsplit0 = 1;
+  if (can_split && sink_block) {
+    int64_t lo, hi, lo1, hi1;
+    m.rows_for_keys(0, std::min(BK, p.Sk), p.Sq, &lo, &hi);
+    m.rows_for_keys(BK, std::min(2 * BK, p.Sk), p.Sq, &lo1, &hi1);
+    const int64_t ratio = (hi1 > lo1) ? (hi - lo + (hi1 - lo1) - 1) / (hi1 - lo1) : 1;
+    int ns0 = 1;
+    while (ns0 * pl.g.nsplit < max_parts && ns0 < ratio) ns0 *= 2;
+    pl.g.nsplit0 = ns0;
+  }
+  const int nparts_max = pl.g.nsplit * pl.g.nsplit0;
+  pl.g.out_mode = nparts_max > 1 ? kAtomicAdd : (accumulate_dkdv ? kAddInto : kStore);
+  pl.grid = dim3(xblocks + pl.g.nsplit0 - 1, p.Hk * pl.g.nsplit, bloop ? 1 : p.B);
   return pl;
 }
 
 template <int D, bool BIAS, bool DQ_ATOMIC, bool BLOOP>
 hipError_t launch_dkdv(const Params& p, const BwdArgs& a, const DkdvPlan& pl, hipStream_t st) {
-  hipLaunchKernelGGL((k_dkdv<D, BIAS, DQ_ATOMIC, BLOOP>), pl.grid, dim3(NT), 0, st, p, a, pl.pair, pl.hsplit,
-                     pl.out_mode);
+  hipLaunchKernelGGL((k_dkdv<D, BIAS, DQ_ATOMIC, BLOOP>), pl.grid, dim3(NT), 0, st, p, a, pl.g);
   return hipGetLastError();
 }
 
@@ -738,7 +776,7 @@ hipError_t launch_bwd_mfma(const Params& p, const BwdArgs& a, hipStream_t st) {
   ZeroRows z[3];
   int nz = 0;
   if (dq_atomic && !a.accumulate_dq) z[nz++] = ZeroRows{a.dq, p.B, p.Hq, p.Sq, p.Dqk, {p.dq_str[0], p.dq_str[1], p.dq_str[2]}};
-  if (pl.out_mode == kAtomicAdd && !a.accumulate_dkdv && p.Sk > 0) {
+  if (pl.g.out_mode == kAtomicAdd && !a.accumulate_dkdv && p.Sk > 0) {
     z[nz++] = ZeroRows{a.dk, p.B, p.Hk, p.Sk, p.Dqk, {p.dk_str[0], p.dk_str[1], p.dk_str[2]}};
     z[nz++] = ZeroRows{a.dv, p.B, p.Hk, p.Sk, p.Dv, {p.dv_str[0], p.dv_str[1], p.dv_str[2]}};
   }

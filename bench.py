@@ -135,13 +135,21 @@ def main():
     p = ab.make_problem(q, k, v, o=o, do=do, dq=dq, dk=dk, dv=dv, bias=bias, scale=w.scale, **mask_kw)
 
     def step(flags, ev=None):
+        # Atomic mode: the preprocess zeroes dQ/dK/dV and attn_bwd accumulates
+        # into them, so the timed attn_bwd call is the main kernel alone.
+        # Deterministic mode: attn_bwd overwrites its outputs itself (zeroing
+        # only what a two-way split needs).
+        determ = bool(flags & ab.ATTN_DETERMINISTIC)
         if ev is not None:
             ev[0].record(stream)
-        ab.attn_bwd_preprocess(p, o, do, lse, sinks, delta, dsinks, dq, dk, dv, stream)
+        if determ:
+            ab.attn_bwd_preprocess(p, o, do, lse, sinks, delta, dsinks, None, None, None, stream)
+        else:
+            ab.attn_bwd_preprocess(p, o, do, lse, sinks, delta, dsinks, dq, dk, dv, stream)
         if ev is not None:
             ev[1].record(stream)
-        ab.attn_bwd(p, q, k, v, do, lse, delta, bias, dq, dk, dv, dbias,
-                    flags | ab.ATTN_ACCUMULATE_DQ | ab.ATTN_ACCUMULATE_DKDV, stream)
+        extra = 0 if determ else (ab.ATTN_ACCUMULATE_DQ | ab.ATTN_ACCUMULATE_DKDV)
+        ab.attn_bwd(p, q, k, v, do, lse, delta, bias, dq, dk, dv, dbias, flags | extra, stream)
         if ev is not None:
             ev[2].record(stream)
 
