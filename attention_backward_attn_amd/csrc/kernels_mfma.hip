@@ -349,6 +349,24 @@ __global__ __launch_bounds__(NT, 1) void k_dkdv(Params p, BwdArgs a, DkdvGrid gd
         int hn = h, qbn = qb + 1;
         if (qbn == nqb) { qbn = 0; ++hn; }
         if (it + 1 < n_it) issue(hn, lo_al + BQ * qbn);
+        // bias (and, past the first batch entry, the running dbias) of this
+        // lane's 16 pairs: loads issued now, used after the products below
+        float bpre[BIAS ? 16 : 1], dbpre[BIAS ? 16 : 1];
+        if (BIAS) {
+          const int64_t jc = min(jkey, Sk - 1);
+#pragma unroll
+          for (int r = 0; r < 16; ++r) {
+            const int64_t i = min(i0 + crow(r, lg), Sq - 1);
+            bpre[r] = a.bias[h * p.bias_str[0] + i * p.bias_str[1] + jc];
+          }
+          if (BLOOP && a.dbias && b > b_begin) {
+#pragma unroll
+            for (int r = 0; r < 16; ++r) {
+              const int64_t i = min(i0 + crow(r, lg), Sq - 1);
+              dbpre[r] = a.dbias[h * p.bias_str[0] + i * p.bias_str[1] + jc];
+            }
+          }
+        }
 
         // S = Q K^T and dP = dO V^T for rows i0..i0+31, this wave's 32 keys.
         // The A operands are read from LDS in bulk ahead of the products, so
@@ -398,10 +416,7 @@ __global__ __launch_bounds__(NT, 1) void k_dkdv(Params p, BwdArgs a, DkdvGrid gd
 #pragma unroll
           for (int r = 0; r < 16; ++r) {
             float x = fmaf(sacc[r], scale_log2, -L4[r >> 2][r & 3]);
-            if (BIAS) {
-              const int i = i0 + 4 * lg + 8 * (r >> 2) + (r & 3);
-              if (i < Sq) x += a.bias[h * p.bias_str[0] + (int64_t)i * p.bias_str[1] + jkey] * kLog2e;
-            }
+            if (BIAS) x = fmaf(bpre[r], kLog2e, x);
             pv[r] = __builtin_amdgcn_exp2f(x);
             dsv[r] = pv[r] * fmaf(dpacc[r], scale, -D4[r >> 2][r & 3]);
           }
@@ -413,25 +428,23 @@ __global__ __launch_bounds__(NT, 1) void k_dkdv(Params p, BwdArgs a, DkdvGrid gd
             const int t = tb - c;
             const bool ok = key_ok && (no_mask || (t <= wr_t && t >= lo_t) || sink_key);
             float x = fmaf(sacc[r], scale_log2, -L4[r >> 2][r & 3]);
-            if (BIAS) {
-              const int i = i0 + 4 * lg + c;
-              if (i < Sq && key_ok) x += a.bias[h * p.bias_str[0] + (int64_t)i * p.bias_str[1] + jkey] * kLog2e;
-            }
+            if (BIAS) x = fmaf(bpre[r], kLog2e, x);
             pv[r] = ok ? __builtin_amdgcn_exp2f(x) : 0.f;
             dsv[r] = pv[r] * fmaf(dpacc[r], scale, -D4[r >> 2][r & 3]);
           }
         }
         if (BIAS && a.dbias) {
-          // dbias takes the unscaled dS
+          // dbias takes the unscaled dS; with the batch loop the first entry
+          // stores (rows and keys inside the problem) and later ones add
           const float inv_scale = 1.f / scale;
 #pragma unroll
           for (int r = 0; r < 16; ++r) {
             const int i = i0 + crow(r, lg);
-            if (i < Sq && key_ok && pv[r] != 0.f) {
+            if (i < Sq && key_ok) {
               float* dst = a.dbias + h * p.bias_str[0] + (int64_t)i * p.bias_str[1] + jkey;
               if (BLOOP)
-                *dst += dsv[r] * inv_scale;
-              else
+                *dst = (b > b_begin ? dbpre[r] : 0.f) + dsv[r] * inv_scale;
+              else if (pv[r] != 0.f)
                 atomic_add_f32(dst, dsv[r] * inv_scale);
             }
           }
@@ -574,23 +587,30 @@ hipError_t dispatch_dkdv(const Params& p, const BwdArgs& a, const DkdvPlan& pl, 
 constexpr int BQ3 = 128;   // query rows per workgroup (k_dq)
 constexpr int BK3 = 32;    // keys per iteration (k_dq)
 
-template <int D>
+constexpr int BSTR = BK3 + 4;   // bias tile row stride (floats): 16 lanes reading 16 rows hit distinct banks
+
+template <int D, bool BIAS>
 struct SmemDQ {
   unsigned short kr[2][BK3 * Lay<D>::R];   // K tile, row copy (A of S^T = K Q^T)
   unsigned short vr[2][BK3 * Lay<D>::R];   // V tile, row copy (A of dP^T = V dO^T)
   unsigned short kt[2][BK3 * Lay<D>::T];   // K tile, tr copy  (B of dQ += dS K)
+  float bias[BIAS ? 2 : 1][BIAS ? BQ3 * BSTR : 1];   // bias[h][i0 + r][j0 + c], row-major padded
 };
 
-// Staging of one 32-key K / V tile (same dealing of 16-byte chunks as Stage).
-template <int D>
+// Staging of one 32-key K / V tile (same dealing of 16-byte chunks as
+// Stage) and, with a bias, of the [128 rows x 32 keys] fp32 bias tile
+// (8 lanes per row, 16 bytes each: coalesced along the keys).
+template <int D, bool BIAS>
 struct StageKV {
   static constexpr int NCR = D / 8;
   static constexpr int NCH = 2 * BK3 * NCR;
   static constexpr int NR = NCH / NT;
+  static constexpr int NBI = BIAS ? BQ3 * BK3 / 4 / NT : 0;   // float4 bias chunks per thread
   u16x8 v[NR];
+  f32x4 bv[BIAS ? NBI : 1];
 
   __device__ inline void load(const unsigned short* k, const unsigned short* vv, int64_t ks, int64_t vs,
-                              int64_t j0, int Sk) {
+                              int64_t j0, int Sk, const float* bias_h, int64_t bstr, int i0, int Sq) {
     const int t = threadIdx.x;
 #pragma unroll
     for (int m = 0; m < NR; ++m) {
@@ -600,10 +620,20 @@ struct StageKV {
       const int64_t j = min(j0 + row, (int64_t)Sk - 1);
       v[m] = *(const u16x8*)((tensor == 0 ? k + j * ks : vv + j * vs) + 8 * c);
     }
+    if (BIAS) {
+#pragma unroll
+      for (int m = 0; m < NBI; ++m) {
+        const int idx = t + NT * m;
+        const int row = idx / (BK3 / 4), c4 = idx % (BK3 / 4);
+        const int64_t i = min(i0 + row, Sq - 1);
+        const int64_t j = min(j0 + 4 * c4, (int64_t)Sk - 4);   // Sk % 4 == 0 for the vector path
+        bv[m] = *(const f32x4*)(bias_h + i * bstr + j);
+      }
+    }
   }
 
   // keys past the end hold the last key: finite, and masked to P = 0
-  __device__ inline void store(SmemDQ<D>& sm, int buf) const {
+  __device__ inline void store(SmemDQ<D, BIAS>& sm, int buf) const {
     const int t = threadIdx.x;
 #pragma unroll
     for (int m = 0; m < NR; ++m) {
@@ -617,6 +647,14 @@ struct StageKV {
         *(u16x8*)(sm.vr[buf] + row * Lay<D>::R + 8 * c) = v[m];
       }
     }
+    if (BIAS) {
+#pragma unroll
+      for (int m = 0; m < NBI; ++m) {
+        const int idx = t + NT * m;
+        const int row = idx / (BK3 / 4), c4 = idx % (BK3 / 4);
+        *(f32x4*)&sm.bias[buf][row * BSTR + 4 * c4] = bv[m];
+      }
+    }
   }
 };
 
@@ -625,7 +663,7 @@ __global__ __launch_bounds__(NT, 2) void k_dq(Params p, BwdArgs a) {
   constexpr int NS = D / 16;
   constexpr int NB = D / 32;
   constexpr int R = Lay<D>::R, T = Lay<D>::T;
-  __shared__ __attribute__((aligned(16))) SmemDQ<D> sm;
+  __shared__ __attribute__((aligned(16))) SmemDQ<D, BIAS> sm;
 
   const int tid = threadIdx.x, w = tid >> 6, l = tid & 63, lr = l & 31, lg = l >> 5;
   const int i0 = blockIdx.x * BQ3;
@@ -677,16 +715,17 @@ __global__ __launch_bounds__(NT, 2) void k_dq(Params p, BwdArgs a) {
 #pragma unroll
   for (int n = 0; n < NB; ++n) dq[n] = zero16();
 
-  StageKV<D> stg;
+  const float* bias_h = BIAS ? a.bias + h * p.bias_str[0] : nullptr;
+  StageKV<D, BIAS> stg;
   if (n_it > 0) {
-    stg.load(kp, vp, p.k_str[2], p.v_str[2], tile_of(0), Sk);
+    stg.load(kp, vp, p.k_str[2], p.v_str[2], tile_of(0), Sk, bias_h, p.bias_str[1], i0, Sq);
     stg.store(sm, 0);
     __syncthreads();
   }
   for (int it = 0; it < n_it; ++it) {
     const int cur = it & 1;
     const int j0 = (int)tile_of(it);
-    if (it + 1 < n_it) stg.load(kp, vp, p.k_str[2], p.v_str[2], tile_of(it + 1), Sk);
+    if (it + 1 < n_it) stg.load(kp, vp, p.k_str[2], p.v_str[2], tile_of(it + 1), Sk, bias_h, p.bias_str[1], i0, Sq);
 
     // S^T = K Q^T and dP^T = V dO^T: keys on accumulator rows, this lane's row on the column
     f32x16 sacc = zero16(), dpacc = zero16();
@@ -704,9 +743,7 @@ __global__ __launch_bounds__(NT, 2) void k_dq(Params p, BwdArgs a) {
       const int c = 8 * (r >> 2) + (r & 3);
       const int j = j0 + 4 * lg + c;
       float x = fmaf(sacc[r], scale_log2, -lse2);
-      if (BIAS) {
-        if (irow < Sq && j < Sk) x += a.bias[h * p.bias_str[0] + (int64_t)irow * p.bias_str[1] + j] * kLog2e;
-      }
+      if (BIAS) x = fmaf(sm.bias[cur][(32 * w + lr) * BSTR + 4 * lg + c], kLog2e, x);
       float pp = __builtin_amdgcn_exp2f(x);
       if (!full) {
         const int t = tb + c;
@@ -767,10 +804,15 @@ bool mfma_bwd_supported(const Params& p) {
 hipError_t launch_bwd_mfma(const Params& p, const BwdArgs& a, hipStream_t st) {
   if (!aligned16(a.q) || !aligned16(a.k) || !aligned16(a.v) || !aligned16(a.dout))
     return launch_bwd_simt(p, a, 1, st);
+  // bias tiles are staged 16 bytes at a time
+  if (a.bias && (!aligned16(a.bias) || p.Sk % 4 != 0 || p.bias_str[0] % 4 != 0 || p.bias_str[1] % 4 != 0))
+    return launch_bwd_simt(p, a, 1, st);
   const bool bias = a.bias != nullptr;
-  const bool dq_atomic = !a.deterministic;
-  // dbias summed over the batch in a fixed order: one workgroup walks the batch
-  const bool bloop = a.dbias != nullptr && a.deterministic;
+  // Bias problems take dQ from the query-parallel pass (its bias tiles are
+  // staged through LDS); dbias is summed over the batch in a fixed order by
+  // one workgroup per key block walking the batch -- no atomics either way.
+  const bool dq_atomic = !a.deterministic && !bias;
+  const bool bloop = a.dbias != nullptr;
   const DkdvPlan pl = plan_dkdv(p, bloop, a.accumulate_dkdv != 0, a.deterministic != 0);
   // one fill for every output that is accumulated into from zero
   ZeroRows z[3];
