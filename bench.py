@@ -46,7 +46,22 @@ def parse():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-extras", action="store_true", help="skip deterministic / chunked / forward timings")
     ap.add_argument("--cpu-groups", type=int, default=8, help="KV head groups in the CPU oracle sample")
+    ap.add_argument("--calibrate-copy", action="store_true",
+                    help="only run a plain 256 MiB device-to-device copy (HBM counter calibration)")
     return ap.parse_args()
+
+
+def calibrate_copy():
+    """A plain copy of known size: its FETCH_SIZE / WRITE_SIZE counter
+    readings calibrate the counters of the attention kernels."""
+    import torch
+    n = 256 * 1024 * 1024 // 4
+    src = torch.ones(n, device="cuda:0", dtype=torch.float32)
+    dst = torch.empty_like(src)
+    for _ in range(3):
+        dst.copy_(src)
+    torch.cuda.synchronize()
+    print(json.dumps({"calibrate_copy_bytes_read": n * 4, "calibrate_copy_bytes_written": n * 4, "launches": 3}))
 
 
 def traffic_record(kernel_key: str):
@@ -98,6 +113,9 @@ def cpu_baseline(w, x, groups: int):
 
 def main():
     args = parse()
+    if args.calibrate_copy:
+        calibrate_copy()
+        return
     if args.gpus != 1:
         print(f"bench.py runs on exactly one GPU; --gpus {args.gpus} is not supported "
               "(this build has no multi-GPU path)", file=sys.stderr)
