@@ -120,8 +120,10 @@ attn_status_t attn_fwd_lse(const attn_problem_t* p, const void* q, const void* k
   if (empty) return ATTN_OK;
   Params kp = make_params(p);
   attn::FwdArgs a{q, k, v, bias, sinks, o, lse};
-  return hip_status(attn::launch_fwd_simt(kp, a, p->in_dtype == ATTN_BF16, p->o_dtype == ATTN_BF16,
-                                          (hipStream_t)stream));
+  const bool o_bf16 = p->o_dtype == ATTN_BF16;
+  if (p->in_dtype == ATTN_BF16 && attn::mfma_fwd_supported(kp, a, o_bf16))
+    return hip_status(attn::launch_fwd_mfma(kp, a, o_bf16, (hipStream_t)stream));
+  return hip_status(attn::launch_fwd_simt(kp, a, p->in_dtype == ATTN_BF16, o_bf16, (hipStream_t)stream));
 }
 
 attn_status_t attn_bwd_preprocess(const attn_problem_t* p, const void* o, const void* dout,

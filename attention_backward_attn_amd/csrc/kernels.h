@@ -62,6 +62,11 @@ hipError_t launch_bwd_simt(const Params& p, const BwdArgs& a, int in_bf16, hipSt
 // dQ alone (query-parallel, no atomics); ACCUMULATE adds into dq.
 hipError_t launch_dq_simt(const Params& p, const BwdArgs& a, int in_bf16, hipStream_t st);
 
+// bf16 matrix-core forward (gfx950 MFMA), head dims 64 and 128 (Dqk == Dv),
+// 16-byte aligned operands; O in fp32 or bf16.
+bool mfma_fwd_supported(const Params& p, const FwdArgs& a, bool o_bf16);
+hipError_t launch_fwd_mfma(const Params& p, const FwdArgs& a, bool o_bf16, hipStream_t st);
+
 // bf16 matrix-core backward (gfx950 MFMA), head dims 64 and 128.
 bool mfma_bwd_supported(const Params& p);
 hipError_t launch_bwd_mfma(const Params& p, const BwdArgs& a, hipStream_t st);

@@ -30,94 +30,21 @@
 #include <algorithm>
 
 #include "kernels.h"
+#include "mfma_util.h"
 
 namespace attn {
 namespace {
 
+using namespace mfma_util;
+
 constexpr int BK = 128;       // keys per workgroup (k_dkdv)
+#ifndef ATTN_MIN_WORKGROUPS
+#define ATTN_MIN_WORKGROUPS 256
+#endif
+constexpr int64_t kMinWorkgroups = ATTN_MIN_WORKGROUPS;   // split target of the dK/dV grid
 constexpr int BQ = 32;        // query rows per iteration (k_dkdv)
 constexpr int NT = 256;       // threads per workgroup
 
-typedef short s16x4 __attribute__((ext_vector_type(4)));
-typedef __attribute__((address_space(3))) s16x4 lds_s16x4;
-
-__device__ inline f32x16 mfma(bf16x8 a, bf16x8 b, f32x16 c) {
-  return __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c, 0, 0, 0);
-}
-
-__device__ inline bf16x8 as_bf16x8(u16x8 v) { return __builtin_bit_cast(bf16x8, v); }
-
-__device__ inline bf16x8 cat44(u16x4 lo, u16x4 hi) {
-  u16x8 v = {lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
-  return as_bf16x8(v);
-}
-
-// 8 fp32 accumulator values -> bf16x8 operand (round to nearest even).
-__device__ inline bf16x8 pack8(const float* x) {
-  bf16x8 r;
-#pragma unroll
-  for (int i = 0; i < 8; ++i) r[i] = (__bf16)x[i];
-  return r;
-}
-
-// Wait for every outstanding vector-memory load (vmcnt = 0; expcnt and
-// lgkmcnt left at their maxima).  Issued once after the register-resident
-// fragments are loaded, ahead of a loop: otherwise the compiler's wait
-// counting carries those loads into the loop body, and each use there waits
-// for the vmcnt of older operations -- including the previous iteration's
-// dQ atomics.
-__device__ inline void wait_vm_loads() { __builtin_amdgcn_s_waitcnt(0x0F70); }
-
-__device__ inline f32x16 zero16() {
-  f32x16 z;
-#pragma unroll
-  for (int i = 0; i < 16; ++i) z[i] = 0.f;
-  return z;
-}
-
-// Row (within a 32-row accumulator block) held by lane group lg in register r.
-__device__ inline int crow(int r, int lg) { return 8 * (r >> 2) + 4 * lg + (r & 3); }
-
-// LDS layouts.  Every tile is row-major bf16 with a padded row stride, and
-// each access pattern gets a copy whose padding makes it bank-conflict-free
-// with per-lane addresses of the form  lane_base + compile-time offset:
-//   * "row" copies, stride D + 8: 16 lanes read 16 bytes of the same columns
-//     of 16 consecutive rows (A operands, ds_read_b128) -- consecutive rows
-//     start 4 banks apart;
-//   * "tr" copies, stride D + 32: 32 lanes read 4 consecutive rows x 64 bytes
-//     with the transposing ds_read_b64_tr_b16 (B operands whose reduction
-//     index is the tile row) -- consecutive rows start 16 banks apart.
-template <int D>
-struct Lay {
-  static constexpr int R = D + 8;    // row-copy stride (elements)
-  static constexpr int T = D + 32;   // tr-copy stride (elements)
-};
-
-__device__ inline bf16x8 lds_b128(const unsigned short* tile, int off) {
-  return as_bf16x8(*(const u16x8*)(tile + off));
-}
-
-__device__ inline u16x4 lds_tr4(const unsigned short* tile, int off) {
-  const auto* b = (__attribute__((address_space(3))) const unsigned short*)tile;
-  return __builtin_bit_cast(u16x4, __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(b + off)));
-}
-
-// Transposing-read lane base for a tile of stride `stride`: ds_read_b64_tr_b16
-// hands lane j of each 16-lane group element j % 4 of the 8-byte chunk
-// addressed by lane 4 r + j / 4 of that group.  Lane l therefore addresses
-// row 4 (l / 32) + (l % 16) / 4, column 16 ((l / 16) % 2) + 4 (l % 4); the
-// read at  base + r0 * stride + n0  (and + 8 rows) yields the B operand of a
-// 32x32x16 MFMA whose reduction slots are tile rows
-// r0 + {4 lg + 0..3, 8 + 4 lg + 0..3} -- the slot order of the S / dS
-// accumulators -- and whose output column is n0 + l % 32.
-__device__ inline int tr_base(int l, int stride) {
-  const int j = l & 15;
-  return (4 * (l >> 5) + (j >> 2)) * stride + 16 * ((l >> 4) & 1) + 4 * (j & 3);
-}
-
-__device__ inline bf16x8 lds_trB(const unsigned short* tile, int base, int r0, int n0, int stride) {
-  return cat44(lds_tr4(tile, base + r0 * stride + n0), lds_tr4(tile, base + (r0 + 8) * stride + n0));
-}
 
 template <int D>
 struct SmemDKDV {
@@ -537,14 +464,22 @@ DkdvPlan plan_dkdv(const Params& p, bool bloop, bool accumulate_dkdv, bool deter
   // batch loop (its dbias is ordered), and only two-way when the result must
   // be deterministic -- two partials into existing values would not be.
   const bool can_split = !bloop && !(accumulate_dkdv && deterministic);
-  const int max_parts = deterministic ? 2 : 8;
-  pl.g.nsplit = (can_split && p.G % 2 == 0 && units < 2 * 256) ? 2 : 1;
+  const int max_parts = deterministic ? 2 : 16;
+  // Split until the grid covers the chip once (one workgroup per CU at one
+  // wave per SIMD), keeping at least a few iterations per part; more parts
+  // cost more dK/dV atomics than they gain in balance.
+  int64_t lo, hi;
+  m.rows_for_keys(0, std::min(BK, p.Sk), p.Sq, &lo, &hi);
+  const int64_t iters = (int64_t)p.G * ((hi - lo + BQ - 1) / BQ + 1);   // about one unit's, paired or not
+  int ns = 1;
+  if (can_split)
+    while (ns < max_parts && units * ns < kMinWorkgroups && iters >= 8 * 2 * ns) ns *= 2;
+  pl.g.nsplit = ns;
   // the sink key block under a sliding window sees every row
   const bool sink_block = m.kind != kMaskNone && m.wl >= 0 && m.n_sink > m.k_off && nkb > 1;
   pl.g.nsplit0 = 1;
   if (can_split && sink_block) {
-    int64_t lo, hi, lo1, hi1;
-    m.rows_for_keys(0, std::min(BK, p.Sk), p.Sq, &lo, &hi);
+    int64_t lo1, hi1;
     m.rows_for_keys(BK, std::min(2 * BK, p.Sk), p.Sq, &lo1, &hi1);
     const int64_t ratio = (hi1 > lo1) ? (hi - lo + (hi1 - lo1) - 1) / (hi1 - lo1) : 1;
     int ns0 = 1;

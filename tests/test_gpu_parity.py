@@ -227,26 +227,49 @@ def test_dsinks_full_batch():
 FWD = [
     (1, 2, 2, 64, 64, 64, 64, "f32", MaskSpec("none"), False, False),
     (2, 8, 2, 200, 200, 128, 128, "bf16", MaskSpec("top_left", window_left=50, num_sink=3), True, True),
-    (1, 4, 1, 100, 260, 128, 64, "bf16", MaskSpec("bottom_right"), False, True),
-    (1, 2, 2, 90, 40, 64, 64, "bf16", MaskSpec("bottom_right"), False, False),  # empty rows
+    (1, 4, 1, 100, 260, 128, 64, "bf16", MaskSpec("bottom_right"), False, True),    # Dqk != Dv
+    (1, 2, 2, 90, 40, 64, 64, "bf16", MaskSpec("bottom_right"), False, False),       # empty rows
+    (1, 8, 2, 1100, 1100, 128, 128, "bf16", MaskSpec("bottom_right"), False, False),
+    (2, 4, 4, 300, 260, 64, 64, "bf16", MaskSpec("none"), True, False),
+    (1, 4, 2, 333, 333, 64, 64, "bf16", MaskSpec("top_left", window_left=40, num_sink=2), False, True),
+    (1, 4, 1, 130, 700, 128, 128, "bf16", MaskSpec("bottom_right", window_left=63, window_right=5,
+                                                    num_sink=3), True, True),
+    (1, 2, 2, 50, 1, 128, 128, "bf16", MaskSpec("none"), False, False),              # one key
+    (1, 2, 1, 70, 20, 64, 64, "bf16", MaskSpec("top_left", window_left=3), False, False),  # empty rows, window
 ]
 
 
-@pytest.mark.parametrize("case", FWD)
-def test_forward_parity(case):
+def fwd_case(case, o_dtype=None):
     B, Hq, Hk, Sq, Sk, D, Dv, dtype, spec, bias, sinks = case
-    say(f"[fwd] {case}")
     x = random_case(B, Hq, Hk, Sq, Sk, D, Dv, dtype, 3, bias, sinks)
     o_ref, lse_ref = oracle.forward(x["q"], x["k"], x["v"], 1 / np.sqrt(D), spec, x["bias"], x["sinks"])
     dt = tdtype(dtype)
     o, lse = ab.forward(dev(x["q"], dt), dev(x["k"], dt), dev(x["v"], dt), bias=dev(x["bias"], torch.float32),
-                        sinks=dev(x["sinks"], torch.float32), scale=1 / np.sqrt(D), **mask_kw(spec))
+                        sinks=dev(x["sinks"], torch.float32), scale=1 / np.sqrt(D), o_dtype=o_dtype,
+                        **mask_kw(spec))
     torch.cuda.synchronize()
-    check("o", o, o_ref, 1e-4)
     lse_g = lse.cpu().numpy()
     empty = np.isneginf(lse_ref)
     assert (np.isneginf(lse_g) == empty).all()
     np.testing.assert_allclose(lse_g[~empty], lse_ref[~empty], rtol=0, atol=1e-4)
+    assert (o.cpu()[torch.from_numpy(empty)] == 0).all(), "rows without keys must be zero"
+    return o, o_ref
+
+
+@pytest.mark.parametrize("case", FWD)
+def test_forward_parity(case):
+    say(f"[fwd] {case}")
+    o, o_ref = fwd_case(case)
+    # bf16 inputs: P is a bf16 matrix-core operand
+    check("o", o, o_ref, 1e-4 if case[7] == "f32" else TOL["bf16"])
+
+
+def test_forward_bf16_output():
+    case = FWD[4]
+    say(f"[fwd bf16 O] {case}")
+    o, o_ref = fwd_case(case, o_dtype=torch.bfloat16)
+    assert o.dtype == torch.bfloat16
+    check("o", o, o_ref, TOL["bf16"])
 
 
 def test_lse_merge_parity():
@@ -292,10 +315,11 @@ def test_headline_chunked():
         ab.attn_lse_merge(o, lse, o2, l2)
     torch.cuda.synchronize()
     assert (lse == -np.inf).sum() == 0
-    check("o merged vs unchunked", o, o_full.cpu().numpy(), 1e-5)
+    # each chunk rounds its own P to bf16 as a matrix-core operand
+    check("o merged vs unchunked", o, o_full.cpu().numpy(), TOL["bf16"])
     # oracle forward on one group
     o64, l64 = oracle.forward(x["q"][:, :4], x["k"][:, :1], x["v"][:, :1], w.scale, spec, row_block=1024)
-    check("o merged vs oracle", o[:, :4], o64, 1e-4)
+    check("o merged vs oracle", o[:, :4], o64, TOL["bf16"])
     say("[chunked] backward")
     full = ab.backward(q, k, v, o, do, lse, scale=w.scale, mask=w.mask)
     dq = torch.zeros_like(full["dq"])
