@@ -111,8 +111,9 @@ __global__ __launch_bounds__(NTF, 2) void k_fwd(Params p, FwdArgs a) {
   __shared__ __attribute__((aligned(16))) SmemFwd<D, KT, BIAS> sm;
 
   const int tid = threadIdx.x, w = tid >> 6, l = tid & 63, lr = l & 31, lg = l >> 5;
-  const int i0 = blockIdx.x * BQF;
-  const int h = blockIdx.y, b = blockIdx.z, g = h / p.G;
+  const BlockXYZ blk = xcd_block();
+  const int i0 = blk.x * BQF;
+  const int h = blk.y, b = blk.z, g = h / p.G;
   const int Sq = p.Sq, Sk = p.Sk;
   const int irow = i0 + 32 * w + lr;   // this lane's query row
   const float scale_log2 = p.scale * kLog2e;

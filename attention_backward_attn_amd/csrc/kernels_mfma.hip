@@ -7,21 +7,23 @@
 //   dS = P (dP - delta),  dV = P^T dO,  dK = scale dS^T Q,  dQ = scale dS K,
 //   dbias = sum_b dS.
 //
-// Kernel k_dkdv: one workgroup per (128-key block, KV head[, batch]).
-//   Four waves; wave w owns keys [32 w, 32 w + 32) of the block and keeps
-//   K, V (and K^T for dQ) as MFMA operand fragments in registers, and dK, dV
-//   as fp32 accumulators in registers for the whole loop over the G query
-//   heads of the group and the 32-row query tiles that can see the block
-//   (no atomics for dK / dV).  Per tile: S and dP by v_mfma_f32_32x32x16_bf16
-//   with the K / V fragments as the B operand, so that the accumulator layout
-//   (one key per lane, 16 rows per lane) is directly the A operand of
-//   P^T dO and dS^T Q once the reduction index is permuted consistently on
-//   both operands.  The B operands of those two products (dO and Q with the
-//   row index as the reduction index) are read from the same row-major LDS
-//   tiles with the gfx950 transposing read ds_read_b64_tr_b16.  dS goes
-//   through LDS to form dQ = dS K for the tile (wave w: head-dim columns
-//   [32 w, 32 w + 32)), added into global dQ with fp32 atomics -- or left to
-//   the deterministic query-parallel kernel k_dq.
+// The backward runs as two passes, neither with atomic dQ updates:
+//   * dK / dV by key blocks: one workgroup per (128-key block, KV head,
+//     batch) loops over the G query heads of the group and the 32-row query
+//     tiles that can see the block, keeping dK and dV for its keys in
+//     registers (GQA group sums without atomics).  k_dkdv2 splits each
+//     32-key slice between a pair of waves on one SIMD (two waves per SIMD);
+//     k_dkdv, one wave per 32 keys, serves problems with a bias and walks the
+//     batch so that dbias is summed in a fixed order.
+//   * dQ by query blocks: k_dq, one workgroup per (128-row block, query
+//     head, batch), recomputes S and dP per key tile and keeps dQ in
+//     registers.
+// In every kernel S (or S^T) comes out of v_mfma_f32_32x32x16_bf16 with one
+// row or key per lane, and that accumulator layout is used directly as the
+// operand of the next product once the reduction index is permuted the same
+// way on both operands; the other operand is read from row-major LDS tiles,
+// with the gfx950 transposing read ds_read_b64_tr_b16 where the tile row is
+// the reduction index.
 //
 // MFMA 32x32x16 bf16 operand layout (lane l, r = 0..15):
 //   A[m][k]: lane holds m = l % 32, k = 8 (l / 32) + 0..7
@@ -52,8 +54,6 @@ struct SmemDKDV {
   unsigned short dr[2][BQ * Lay<D>::R];   // dO tile, row copy (A of dP = dO V^T)
   unsigned short qt[2][BQ * Lay<D>::T];   // Q tile, tr copy   (B of dK += dS^T Q)
   unsigned short dt[2][BQ * Lay<D>::T];   // dO tile, tr copy  (B of dV += P^T dO)
-  unsigned short kt[BK * Lay<D>::T];      // K block, tr copy  (B of dQ = dS K)
-  unsigned short dst[2][BK * BQ];         // dS^T tiles [key][row] (A of dQ, tr reads)
   float lse2[2][BQ];                      // LSE * log2(e); +inf for rows without keys
   float dls[2][BQ];                       // delta * scale
 };
@@ -126,15 +126,22 @@ enum : int { kStore = 0, kAtomicAdd = 1, kAddInto = 2 };
 // not depend on their order, so a two-way split stays deterministic.
 // Sink block: with sink tokens under a sliding window, key block 0 is seen by
 // every query row while the others see only a band; it gets `nsplit0` parts,
-// dealt first (blockIdx.x < nsplit0).
+// dealt first (logical block x < nsplit0).
 struct DkdvGrid {
   int pair;      // complementary key blocks per workgroup
-  int nsplit;    // parts per unit (blockIdx.y = hk * nsplit + part)
+  int nsplit;    // parts per unit (logical block y = hk * nsplit + part)
   int nsplit0;   // parts of key block 0 (1 = no separate treatment)
   int out_mode;  // kStore / kAtomicAdd / kAddInto
 };
 
-template <int D, bool BIAS, bool DQ_ATOMIC, bool BLOOP>
+// Kernel k_dkdv (problems with a bias): four waves, wave w owns keys
+// [32 w, 32 w + 32) of the block with K / V fragments and dK / dV
+// accumulators in registers; per tile S and dP with the fragments as the B
+// operand, the bias added to S, P and dS elementwise, then dV += P^T dO and
+// dK += dS^T Q.  With dbias the workgroup walks the batch: the first entry
+// stores dS, later ones add to it, so the sum over the batch has a fixed
+// order.
+template <int D, bool BIAS, bool BLOOP>
 __global__ __launch_bounds__(NT, 1) void k_dkdv(Params p, BwdArgs a, DkdvGrid gd) {
   static_assert(D == 64 || D == 128, "head dim");
   constexpr int NS = D / 16;          // k-steps over the head dim
@@ -145,9 +152,10 @@ __global__ __launch_bounds__(NT, 1) void k_dkdv(Params p, BwdArgs a, DkdvGrid gd
   const int tid = threadIdx.x, w = tid >> 6, l = tid & 63, lr = l & 31, lg = l >> 5;
   const int Sq = p.Sq, Sk = p.Sk;
   const int nkb = (Sk + BK - 1) / BK;
-  const int hk = blockIdx.y / gd.nsplit;
-  int part = blockIdx.y % gd.nsplit, nparts = gd.nsplit;
-  int kbx = blockIdx.x;
+  const BlockXYZ blk = xcd_block();
+  const int hk = blk.y / gd.nsplit;
+  int part = blk.y % gd.nsplit, nparts = gd.nsplit;
+  int kbx = blk.x;
   if (gd.nsplit0 > 1) {
     if (kbx < gd.nsplit0) {
       part = kbx * gd.nsplit + part;
@@ -159,7 +167,6 @@ __global__ __launch_bounds__(NT, 1) void k_dkdv(Params p, BwdArgs a, DkdvGrid gd
   }
   const int h_begin = hk * p.G;
   const float scale = p.scale, scale_log2 = p.scale * kLog2e;
-  const bool dq_wave = DQ_ATOMIC && (w < NB);
   const int n_units = (gd.pair && nkb - 1 - kbx != kbx) ? 2 : 1;
   const int out_mode = gd.out_mode;
   const bool no_mask = p.mask.kind == kMaskNone;
@@ -169,10 +176,8 @@ __global__ __launch_bounds__(NT, 1) void k_dkdv(Params p, BwdArgs a, DkdvGrid gd
   // per-lane LDS bases
   const int rowA = lr * R + 8 * lg;            // row-copy A operands: + 16 s
   const int trQ = tr_base(l, T);               // tr-copy B operands
-  const int trS = tr_base(l, BQ);              // dS^T tr reads (row stride 32)
-  const int dsw = (32 * w + lr) * BQ + 4 * lg; // dS^T writes: + 8 m
 
-  const int b_begin = BLOOP ? 0 : blockIdx.z;
+  const int b_begin = BLOOP ? 0 : blk.z;
   const int b_end = BLOOP ? p.B : b_begin + 1;
   for (int b = b_begin; b < b_end; ++b) {
     for (int u = 0; u < n_units; ++u) {
@@ -208,17 +213,6 @@ __global__ __launch_bounds__(NT, 1) void k_dkdv(Params p, BwdArgs a, DkdvGrid gd
         }
       }
       __syncthreads();  // readers of the previous unit's LDS tiles are done
-      if (DQ_ATOMIC) {
-        // the K block's tr copy (B operand of dQ = dS K)
-        constexpr int NCR = D / 8;
-#pragma unroll
-        for (int m = 0; m < BK * NCR / NT; ++m) {
-          const int idx = tid + NT * m;
-          const int row = idx / NCR, c = idx % NCR;
-          const int64_t j = min(k0 + row, Sk - 1);
-          *(u16x8*)(sm.kt + row * T + 8 * c) = *(const u16x8*)(kp + j * p.k_str[2] + 8 * c);
-        }
-      }
       f32x16 dk[NB], dv[NB];
 #pragma unroll
       for (int n = 0; n < NB; ++n) { dk[n] = zero16(); dv[n] = zero16(); }
@@ -229,38 +223,6 @@ __global__ __launch_bounds__(NT, 1) void k_dkdv(Params p, BwdArgs a, DkdvGrid gd
         stg.load((const unsigned short*)a.q + b * p.q_str[0] + h * p.q_str[1],
                  (const unsigned short*)a.dout + b * p.do_str[0] + h * p.do_str[1], p.q_str[2], p.do_str[2],
                  a.lse + ((int64_t)b * p.Hq + h) * Sq, a.delta + ((int64_t)b * p.Hq + h) * Sq, i0, Sq);
-      };
-      // dQ += dS K for the tile (head hh, rows ii..ii+31) whose dS^T sits in
-      // buffer buf: wave w < NB produces head-dim columns [32 w, 32 w + 32)
-      // and adds them to global dQ with fp32 atomics.
-      auto dq_tile = [&](int buf, int hh, int ii) {
-        if (!dq_wave) return;
-        f32x16 qacc = zero16();
-#pragma unroll
-        for (int t0 = 0; t0 < BK / 16; t0 += 4) {
-          bf16x8 sA[4], kT[4];
-#pragma unroll
-          for (int t = 0; t < 4; ++t) {
-            sA[t] = lds_trB(sm.dst[buf], trS, 16 * (t0 + t), 0, BQ);
-            kT[t] = lds_trB(sm.kt, trQ, 16 * (t0 + t), 32 * w, T);
-          }
-#pragma unroll
-          for (int t = 0; t < 4; ++t) qacc = mfma(sA[t], kT[t], qacc);
-        }
-        // row ii + 4 lg + c, column 32 w + lr: 32-bit offsets from a uniform base
-        float* dqb = a.dq + b * p.dq_str[0] + hh * p.dq_str[1] + (int64_t)ii * p.dq_str[2] + 32 * w + lr;
-        const int rs = (int)p.dq_str[2];
-        const int rows_left = Sq - ii;
-        if (rows_left >= BQ) {
-#pragma unroll
-          for (int r = 0; r < 16; ++r) atomic_add_f32(dqb + (4 * lg + 8 * (r >> 2) + (r & 3)) * rs, qacc[r]);
-        } else {
-#pragma unroll
-          for (int r = 0; r < 16; ++r) {
-            const int c = 4 * lg + 8 * (r >> 2) + (r & 3);
-            if (c < rows_left) atomic_add_f32(dqb + c * rs, qacc[r]);
-          }
-        }
       };
       // (head, row-tile) of the current iteration, advanced incrementally
       int h = h_begin + (nqb > 0 ? it_lo / nqb : 0), qb = nqb > 0 ? it_lo % nqb : 0;
@@ -397,22 +359,8 @@ __global__ __launch_bounds__(NT, 1) void k_dkdv(Params p, BwdArgs a, DkdvGrid gd
           dk[n] = mfma(sa1, qB[n][1], dk[n]);
         }
 
-        if (DQ_ATOMIC) {
-          // dS^T of this tile to LDS (this lane's key row, query rows
-          // 8 m + 4 lg + 0..3); its dQ product runs after the barrier that
-          // ends this iteration.
-          const u16x8 s0 = __builtin_bit_cast(u16x8, sa0), s1 = __builtin_bit_cast(u16x8, sa1);
-          unsigned short* dt = sm.dst[cur];
-          *(u16x4*)&dt[dsw] = u16x4{s0[0], s0[1], s0[2], s0[3]};
-          *(u16x4*)&dt[dsw + 8] = u16x4{s0[4], s0[5], s0[6], s0[7]};
-          *(u16x4*)&dt[dsw + 16] = u16x4{s1[0], s1[1], s1[2], s1[3]};
-          *(u16x4*)&dt[dsw + 24] = u16x4{s1[4], s1[5], s1[6], s1[7]};
-        }
         if (it + 1 < n_it) stg.store(sm, cur ^ 1, lo_al + BQ * qbn, Sq, scale);
         __syncthreads();
-        // dQ of this tile, from the dS^T the barrier just published; the
-        // buffer is rewritten two iterations later, after another barrier
-        if (DQ_ATOMIC) dq_tile(cur, h, i0);
         h = hn;
         qb = qbn;
       }
@@ -438,6 +386,290 @@ __global__ __launch_bounds__(NT, 1) void k_dkdv(Params p, BwdArgs a, DkdvGrid gd
               *pk = dk[n][r];
               *pvv = dv[n][r];
             }
+          }
+        }
+      }
+    }
+  }
+}
+
+// ---------------------------------------------------------------------------
+// Kernel k_dkdv2: dK / dV without dQ (dQ from k_dq), two waves per SIMD.
+// One workgroup of eight waves per unit, as for k_dkdv.  Waves w and w + 4
+// form a pair that owns keys [32 (w % 4), 32 (w % 4) + 32) of the block and
+// splits the head dim of dK / dV between them: the "S" wave (w < 4) keeps
+// the keys' K fragments, forms S = Q K^T and P, and accumulates dK / dV
+// columns [0, D / 2); the "dP" wave keeps V, forms dP = dO V^T and
+// dS = P (dP - delta), and accumulates columns [D / 2, D).  P (bf16, as the
+// MFMA operand of dV) and dS are handed to the partner through LDS in the
+// accumulator's own lane order.  Per tile: barrier X publishes P (and ends
+// every read of the tile two steps back), barrier Y publishes dS and the
+// next tile.  The pair sits on one SIMD, so one wave's exponentials and
+// LDS waits overlap the other's matrix products.
+// ---------------------------------------------------------------------------
+constexpr int NT2 = 512;
+
+template <int D>
+struct SmemDKDV2 {
+  unsigned short qr[2][BQ * Lay<D>::R];   // Q tile, row copy  (A of S = Q K^T)
+  unsigned short dr[2][BQ * Lay<D>::R];   // dO tile, row copy (A of dP = dO V^T)
+  unsigned short qt[2][BQ * Lay<D>::T];   // Q tile, tr copy   (B of dK += dS^T Q)
+  unsigned short dt[2][BQ * Lay<D>::T];   // dO tile, tr copy  (B of dV += P^T dO)
+  u16x8 px[4][2][64];                     // P of pair w % 4: [operand half][lane]
+  u16x8 sx[4][2][64];                     // dS of pair w % 4
+  float lse2[2][BQ];                      // LSE * log2(e); +inf for rows without keys
+  float dls[2][BQ];                       // delta * scale
+};
+
+// Staging of one 32-row Q / dO tile by 512 threads (as Stage).
+template <int D>
+struct Stage2 {
+  static constexpr int NCR = D / 8;
+  static constexpr int NCH = 2 * BQ * NCR;
+  static constexpr int NR = NCH / NT2;
+  static_assert(NCH % NT2 == 0, "chunks per thread");
+  u16x8 v[NR];
+  float lse, dl;
+
+  __device__ inline void load(const unsigned short* q, const unsigned short* dout, int64_t qs, int64_t ds,
+                              const float* lse_p, const float* dl_p, int i0, int Sq) {
+    const int t = threadIdx.x;
+#pragma unroll
+    for (int k = 0; k < NR; ++k) {
+      const int idx = t + NT2 * k;
+      const int tensor = idx / (BQ * NCR), rem = idx % (BQ * NCR);
+      const int row = rem / NCR, c = rem % NCR;
+      const int64_t i = min(i0 + row, Sq - 1);
+      v[k] = *(const u16x8*)((tensor == 0 ? q + i * qs : dout + i * ds) + 8 * c);
+    }
+    if (t >= NT2 - BQ) {
+      const int64_t i = min(i0 + (t - (NT2 - BQ)), Sq - 1);
+      lse = lse_p[i];
+      dl = dl_p[i];
+    }
+  }
+
+  __device__ inline void store(SmemDKDV2<D>& sm, int buf, int i0, int Sq, float scale) const {
+    const int t = threadIdx.x;
+#pragma unroll
+    for (int k = 0; k < NR; ++k) {
+      const int idx = t + NT2 * k;
+      const int tensor = idx / (BQ * NCR), rem = idx % (BQ * NCR);
+      const int row = rem / NCR, c = rem % NCR;
+      *(u16x8*)((tensor == 0 ? sm.qr[buf] : sm.dr[buf]) + row * Lay<D>::R + 8 * c) = v[k];
+      *(u16x8*)((tensor == 0 ? sm.qt[buf] : sm.dt[buf]) + row * Lay<D>::T + 8 * c) = v[k];
+    }
+    if (t >= NT2 - BQ) {
+      const int r = t - (NT2 - BQ);
+      const bool ok = i0 + r < Sq;
+      sm.lse2[buf][r] = (!ok || lse == -INFINITY) ? INFINITY : lse * kLog2e;
+      sm.dls[buf][r] = ok ? dl * scale : 0.f;
+    }
+  }
+};
+
+template <int D>
+__global__ __launch_bounds__(NT2) void k_dkdv2(Params p, BwdArgs a, DkdvGrid gd) {
+  static_assert(D == 64 || D == 128, "head dim");
+  constexpr int NS = D / 16;          // k-steps over the head dim
+  constexpr int NH = D / 64;          // 32-column blocks of this wave's half of the head dim
+  constexpr int R = Lay<D>::R, T = Lay<D>::T;
+  __shared__ __attribute__((aligned(16))) SmemDKDV2<D> sm;
+
+  const int tid = threadIdx.x, w = tid >> 6, l = tid & 63, lr = l & 31, lg = l >> 5;
+  const int pr = w & 3;               // pair: keys [32 pr, 32 pr + 32) of the block
+  const bool sw = w < 4;              // S wave (else dP wave)
+  const int cb = sw ? 0 : D / 2;      // first dK / dV column of this wave
+  const int Sq = p.Sq, Sk = p.Sk;
+  const int nkb = (Sk + BK - 1) / BK;
+  const BlockXYZ blk = xcd_block();
+  const int hk = blk.y / gd.nsplit;
+  int part = blk.y % gd.nsplit, nparts = gd.nsplit;
+  int kbx = blk.x;
+  if (gd.nsplit0 > 1) {
+    if (kbx < gd.nsplit0) {
+      part = kbx * gd.nsplit + part;
+      nparts = gd.nsplit0 * gd.nsplit;
+      kbx = 0;
+    } else {
+      kbx -= gd.nsplit0 - 1;
+    }
+  }
+  const int h_begin = hk * p.G;
+  const float scale = p.scale, scale_log2 = p.scale * kLog2e;
+  const int n_units = (gd.pair && nkb - 1 - kbx != kbx) ? 2 : 1;
+  const int out_mode = gd.out_mode;
+  const bool no_mask = p.mask.kind == kMaskNone;
+  const int lo_t = p.mask.wl < 0 ? -0x3fffffff : -p.mask.wl;
+  const int wr_t = p.mask.wr;
+  const int rowA = lr * R + 8 * lg;
+  const int trQ = tr_base(l, T);
+  const int b = blk.z;
+
+  for (int u = 0; u < n_units; ++u) {
+    const int kb = u == 0 ? kbx : nkb - 1 - kbx;
+    const int k0 = kb * BK;
+    const int kw = k0 + 32 * pr;
+    const int jkey = kw + lr;
+    const bool wave_keys_in = kw + 32 <= Sk;
+    const bool key_ok = jkey < Sk;
+    const int jg = jkey + (int)p.mask.k_off;
+    const bool sink_key = jg < p.mask.n_sink;
+    int64_t lo64, hi64;
+    p.mask.rows_for_keys(k0, min(k0 + BK, Sk), Sq, &lo64, &hi64);
+    const int lo = (int)lo64, hi = (int)hi64;
+    const int lo_al = lo & ~(BQ - 1);
+    const int nqb = hi > lo ? (hi - lo_al + BQ - 1) / BQ : 0;
+    const int n_all = p.G * nqb;
+    const int it_lo = (int)((int64_t)n_all * part / nparts);
+    const int n_it = (int)((int64_t)n_all * (part + 1) / nparts) - it_lo;
+
+    // K (S wave) or V (dP wave) fragments of this pair's keys: B operands
+    bf16x8 fB[NS];
+    {
+      const unsigned short* src = sw ? (const unsigned short*)a.k + b * p.k_str[0] + hk * p.k_str[1]
+                                     : (const unsigned short*)a.v + b * p.v_str[0] + hk * p.v_str[1];
+      const int64_t rs = sw ? p.k_str[2] : p.v_str[2];
+      const int64_t jc = min(jkey, Sk - 1);
+#pragma unroll
+      for (int s = 0; s < NS; ++s) fB[s] = as_bf16x8(*(const u16x8*)(src + jc * rs + 16 * s + 8 * lg));
+    }
+    f32x16 dk[NH], dv[NH];
+#pragma unroll
+    for (int n = 0; n < NH; ++n) { dk[n] = zero16(); dv[n] = zero16(); }
+    __syncthreads();  // readers of the previous unit's LDS tiles are done
+    wait_vm_loads();
+
+    Stage2<D> stg;
+    auto issue = [&](int h, int i0) {
+      stg.load((const unsigned short*)a.q + b * p.q_str[0] + h * p.q_str[1],
+               (const unsigned short*)a.dout + b * p.do_str[0] + h * p.do_str[1], p.q_str[2], p.do_str[2],
+               a.lse + ((int64_t)b * p.Hq + h) * Sq, a.delta + ((int64_t)b * p.Hq + h) * Sq, i0, Sq);
+    };
+    int h = h_begin + (nqb > 0 ? it_lo / nqb : 0), qb = nqb > 0 ? it_lo % nqb : 0;
+    if (n_it > 0) {
+      issue(h, lo_al + BQ * qb);
+      stg.store(sm, 0, lo_al + BQ * qb, Sq, scale);
+      __syncthreads();
+    }
+
+    for (int it = 0; it < n_it; ++it) {
+      const int cur = it & 1;
+      const int i0 = lo_al + BQ * qb;
+      int hn = h, qbn = qb + 1;
+      if (qbn == nqb) { qbn = 0; ++hn; }
+      if (it + 1 < n_it) issue(hn, lo_al + BQ * qbn);
+
+      // S = Q K^T (S wave) or dP = dO V^T (dP wave): rows i0..i0+31, the pair's keys
+      f32x16 acc = zero16();
+      {
+        const unsigned short* src = sw ? sm.qr[cur] : sm.dr[cur];
+        bf16x8 xa[NS];
+#pragma unroll
+        for (int s = 0; s < NS; ++s) xa[s] = lds_b128(src, rowA + 16 * s);
+#pragma unroll
+        for (int s = 0; s < NS; ++s) acc = mfma(xa[s], fB[s], acc);
+      }
+      // dO B operands of this wave's dV columns (independent of P)
+      bf16x8 oB[NH][2];
+#pragma unroll
+      for (int n = 0; n < NH; ++n) {
+        oB[n][0] = lds_trB(sm.dt[cur], trQ, 0, cb + 32 * n, T);
+        oB[n][1] = lds_trB(sm.dt[cur], trQ, 16, cb + 32 * n, T);
+      }
+      bf16x8 pa0, pa1;
+      if (sw) {
+        f32x4 L4[4];
+#pragma unroll
+        for (int m = 0; m < 4; ++m) L4[m] = *(const f32x4*)&sm.lse2[cur][8 * m + 4 * lg];
+        const bool full = wave_keys_in && p.mask.tile_full(i0, i0 + BQ, kw, kw + 32);
+        float pv[16];
+        if (full) {
+#pragma unroll
+          for (int r = 0; r < 16; ++r)
+            pv[r] = __builtin_amdgcn_exp2f(fmaf(acc[r], scale_log2, -L4[r >> 2][r & 3]));
+        } else {
+          const int tb = jg - (i0 + (int)p.mask.q_off) - (int)p.mask.diag - 4 * lg;
+#pragma unroll
+          for (int r = 0; r < 16; ++r) {
+            const int c = 8 * (r >> 2) + (r & 3);
+            const int t = tb - c;
+            const bool ok = key_ok && (no_mask || (t <= wr_t && t >= lo_t) || sink_key);
+            const float x = fmaf(acc[r], scale_log2, -L4[r >> 2][r & 3]);
+            pv[r] = ok ? __builtin_amdgcn_exp2f(x) : 0.f;
+          }
+        }
+        pa0 = pack8(pv);
+        pa1 = pack8(pv + 8);
+        sm.px[pr][0][l] = __builtin_bit_cast(u16x8, pa0);
+        sm.px[pr][1][l] = __builtin_bit_cast(u16x8, pa1);
+      }
+      __syncthreads();  // X: P published
+      if (!sw) {
+        f32x4 D4[4];
+#pragma unroll
+        for (int m = 0; m < 4; ++m) D4[m] = *(const f32x4*)&sm.dls[cur][8 * m + 4 * lg];
+        const u16x8 p0 = sm.px[pr][0][l], p1 = sm.px[pr][1][l];
+        pa0 = __builtin_bit_cast(bf16x8, p0);
+        pa1 = __builtin_bit_cast(bf16x8, p1);
+        // dS = P (dP - delta), pre-multiplied by the softmax scale
+        float dsv[16];
+#pragma unroll
+        for (int r = 0; r < 8; ++r) {
+          dsv[r] = bf16_to_f32(p0[r]) * fmaf(acc[r], scale, -D4[r >> 2][r & 3]);
+          dsv[r + 8] = bf16_to_f32(p1[r]) * fmaf(acc[r + 8], scale, -D4[(r + 8) >> 2][r & 3]);
+        }
+        const bf16x8 sa0 = pack8(dsv), sa1 = pack8(dsv + 8);
+        sm.sx[pr][0][l] = __builtin_bit_cast(u16x8, sa0);
+        sm.sx[pr][1][l] = __builtin_bit_cast(u16x8, sa1);
+#pragma unroll
+        for (int n = 0; n < NH; ++n) {
+          const bf16x8 q0 = lds_trB(sm.qt[cur], trQ, 0, cb + 32 * n, T);
+          const bf16x8 q1 = lds_trB(sm.qt[cur], trQ, 16, cb + 32 * n, T);
+          dk[n] = mfma(sa0, q0, dk[n]);
+          dk[n] = mfma(sa1, q1, dk[n]);
+        }
+      }
+#pragma unroll
+      for (int n = 0; n < NH; ++n) {
+        dv[n] = mfma(pa0, oB[n][0], dv[n]);
+        dv[n] = mfma(pa1, oB[n][1], dv[n]);
+      }
+      if (it + 1 < n_it) stg.store(sm, cur ^ 1, lo_al + BQ * qbn, Sq, scale);
+      __syncthreads();  // Y: dS and the next tile published
+      if (sw) {
+        const bf16x8 sa0 = __builtin_bit_cast(bf16x8, sm.sx[pr][0][l]);
+        const bf16x8 sa1 = __builtin_bit_cast(bf16x8, sm.sx[pr][1][l]);
+#pragma unroll
+        for (int n = 0; n < NH; ++n) {
+          dk[n] = mfma(sa0, lds_trB(sm.qt[cur], trQ, 0, cb + 32 * n, T), dk[n]);
+          dk[n] = mfma(sa1, lds_trB(sm.qt[cur], trQ, 16, cb + 32 * n, T), dk[n]);
+        }
+      }
+      h = hn;
+      qb = qbn;
+    }
+
+    // Epilogue: this wave's dK (scaled through dS) and dV columns.
+    float* dkp = a.dk + b * p.dk_str[0] + hk * p.dk_str[1];
+    float* dvp = a.dv + b * p.dv_str[0] + hk * p.dv_str[1];
+#pragma unroll
+    for (int n = 0; n < NH; ++n) {
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        const int64_t j = kw + crow(r, lg);
+        if (j < Sk) {
+          float* pk = dkp + j * p.dk_str[2] + cb + 32 * n + lr;
+          float* pvv = dvp + j * p.dv_str[2] + cb + 32 * n + lr;
+          if (out_mode == kAtomicAdd) {
+            atomic_add_f32(pk, dk[n][r]);
+            atomic_add_f32(pvv, dv[n][r]);
+          } else if (out_mode == kAddInto) {
+            *pk += dk[n][r];
+            *pvv += dv[n][r];
+          } else {
+            *pk = dk[n][r];
+            *pvv = dv[n][r];
           }
         }
       }
@@ -492,26 +724,24 @@ DkdvPlan plan_dkdv(const Params& p, bool bloop, bool accumulate_dkdv, bool deter
   return pl;
 }
 
-template <int D, bool BIAS, bool DQ_ATOMIC, bool BLOOP>
+template <int D, bool BIAS, bool BLOOP>
 hipError_t launch_dkdv(const Params& p, const BwdArgs& a, const DkdvPlan& pl, hipStream_t st) {
-  hipLaunchKernelGGL((k_dkdv<D, BIAS, DQ_ATOMIC, BLOOP>), pl.grid, dim3(NT), 0, st, p, a, pl.g);
+  hipLaunchKernelGGL((k_dkdv<D, BIAS, BLOOP>), pl.grid, dim3(NT), 0, st, p, a, pl.g);
   return hipGetLastError();
 }
 
 template <int D>
-hipError_t dispatch_dkdv(const Params& p, const BwdArgs& a, const DkdvPlan& pl, bool bias, bool dq_atomic,
-                         bool bloop, hipStream_t st) {
-  // the batch loop is only used with the deterministic (non-atomic) dQ pass
-  if (bias) {
-    if (dq_atomic) return launch_dkdv<D, true, true, false>(p, a, pl, st);
-    return bloop ? launch_dkdv<D, true, false, true>(p, a, pl, st) : launch_dkdv<D, true, false, false>(p, a, pl, st);
+hipError_t dispatch_dkdv(const Params& p, const BwdArgs& a, const DkdvPlan& pl, bool bias, bool bloop,
+                         hipStream_t st) {
+  if (!bias) {
+    hipLaunchKernelGGL((k_dkdv2<D>), pl.grid, dim3(NT2), 0, st, p, a, pl.g);
+    return hipGetLastError();
   }
-  if (dq_atomic) return launch_dkdv<D, false, true, false>(p, a, pl, st);
-  return launch_dkdv<D, false, false, false>(p, a, pl, st);
+  return bloop ? launch_dkdv<D, true, true>(p, a, pl, st) : launch_dkdv<D, true, false>(p, a, pl, st);
 }
 
 // ---------------------------------------------------------------------------
-// Kernel k_dq (deterministic dQ): one workgroup per (128-row query block,
+// Kernel k_dq (dQ): one workgroup per (128-row query block,
 // query head, batch).  Wave w owns rows [32 w, 32 w + 32) and keeps Q and dO
 // as B-operand fragments in registers; per 32-key tile it forms
 // S^T = K Q^T and dP^T = V dO^T (keys on accumulator rows, one query row per
@@ -601,8 +831,9 @@ __global__ __launch_bounds__(NT, 2) void k_dq(Params p, BwdArgs a) {
   __shared__ __attribute__((aligned(16))) SmemDQ<D, BIAS> sm;
 
   const int tid = threadIdx.x, w = tid >> 6, l = tid & 63, lr = l & 31, lg = l >> 5;
-  const int i0 = blockIdx.x * BQ3;
-  const int h = blockIdx.y, b = blockIdx.z, g = h / p.G;
+  const BlockXYZ blk = xcd_block();
+  const int i0 = blk.x * BQ3;
+  const int h = blk.y, b = blk.z, g = h / p.G;
   const int Sq = p.Sq, Sk = p.Sk;
   const int irow = i0 + 32 * w + lr;           // this lane's query row
   const float scale = p.scale, scale_log2 = p.scale * kLog2e;
@@ -743,31 +974,24 @@ hipError_t launch_bwd_mfma(const Params& p, const BwdArgs& a, hipStream_t st) {
   if (a.bias && (!aligned16(a.bias) || p.Sk % 4 != 0 || p.bias_str[0] % 4 != 0 || p.bias_str[1] % 4 != 0))
     return launch_bwd_simt(p, a, 1, st);
   const bool bias = a.bias != nullptr;
-  // Bias problems take dQ from the query-parallel pass (its bias tiles are
-  // staged through LDS); dbias is summed over the batch in a fixed order by
-  // one workgroup per key block walking the batch -- no atomics either way.
-  const bool dq_atomic = !a.deterministic && !bias;
+  // dK / dV by key blocks (k_dkdv2; k_dkdv with a bias, where dbias is
+  // summed over the batch in a fixed order by one workgroup per key block
+  // walking the batch), then dQ by query blocks (k_dq): no dQ atomics.
   const bool bloop = a.dbias != nullptr;
   const DkdvPlan pl = plan_dkdv(p, bloop, a.accumulate_dkdv != 0, a.deterministic != 0);
-  // one fill for every output that is accumulated into from zero
-  ZeroRows z[3];
-  int nz = 0;
-  if (dq_atomic && !a.accumulate_dq) z[nz++] = ZeroRows{a.dq, p.B, p.Hq, p.Sq, p.Dqk, {p.dq_str[0], p.dq_str[1], p.dq_str[2]}};
+  // split parts add into zeroed dK / dV
   if (pl.g.out_mode == kAtomicAdd && !a.accumulate_dkdv && p.Sk > 0) {
-    z[nz++] = ZeroRows{a.dk, p.B, p.Hk, p.Sk, p.Dqk, {p.dk_str[0], p.dk_str[1], p.dk_str[2]}};
-    z[nz++] = ZeroRows{a.dv, p.B, p.Hk, p.Sk, p.Dv, {p.dv_str[0], p.dv_str[1], p.dv_str[2]}};
-  }
-  hipError_t e = launch_zero_multi(z, nz, st);
-  if (e != hipSuccess) return e;
-  if (p.Sk > 0 && p.B > 0) {
-    e = p.Dqk == 64 ? dispatch_dkdv<64>(p, a, pl, bias, dq_atomic, bloop, st)
-                    : dispatch_dkdv<128>(p, a, pl, bias, dq_atomic, bloop, st);
+    ZeroRows z[2] = {ZeroRows{a.dk, p.B, p.Hk, p.Sk, p.Dqk, {p.dk_str[0], p.dk_str[1], p.dk_str[2]}},
+                     ZeroRows{a.dv, p.B, p.Hk, p.Sk, p.Dv, {p.dv_str[0], p.dv_str[1], p.dv_str[2]}}};
+    hipError_t e = launch_zero_multi(z, 2, st);
     if (e != hipSuccess) return e;
-  } else if (dq_atomic) {
-    return hipSuccess;
   }
-  if (!dq_atomic && p.Sq > 0 && p.B > 0)
-    return p.Dqk == 64 ? launch_dq<64>(p, a, st) : launch_dq<128>(p, a, st);
+  if (p.Sk > 0 && p.B > 0) {
+    hipError_t e = p.Dqk == 64 ? dispatch_dkdv<64>(p, a, pl, bias, bloop, st)
+                               : dispatch_dkdv<128>(p, a, pl, bias, bloop, st);
+    if (e != hipSuccess) return e;
+  }
+  if (p.Sq > 0 && p.B > 0) return p.Dqk == 64 ? launch_dq<64>(p, a, st) : launch_dq<128>(p, a, st);
   return hipSuccess;
 }
 

@@ -94,5 +94,38 @@ __device__ inline bf16x8 lds_trB(const unsigned short* tile, int base, int r0, i
   return cat44(lds_tr4(tile, base + r0 * stride + n0), lds_tr4(tile, base + (r0 + 8) * stride + n0));
 }
 
+// The hardware deals a launch's workgroups to the eight XCDs round-robin by
+// linear workgroup id.  Renumbering them so that each XCD receives one
+// contiguous range of logical ids (x fastest, then y, then z) keeps the
+// workgroups that share a KV head -- and so its K / V or Q / dO rows -- on
+// one XCD and in its L2.
+struct BlockXYZ {
+  int x, y, z;
+};
+
+__device__ inline BlockXYZ xcd_block() {
+  const int nx = gridDim.x, ny = gridDim.y;
+  const int n = nx * ny * gridDim.z;
+  const int id = blockIdx.x + nx * (blockIdx.y + ny * blockIdx.z);
+  const int q = n >> 3, r = n & 7, k = id & 7;
+  const int L = k * q + min(k, r) + (id >> 3);
+  const int yz = L / nx;
+  return {L - yz * nx, yz % ny, yz / ny};
+}
+
+// Raw buffer resource over [base, base + bytes): a load at an offset past the
+// end returns zero without touching memory, so ragged tiles need no clamping.
+__device__ inline __amdgpu_buffer_rsrc_t buf_rsrc(const void* base, int bytes) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, bytes, 0x00020000);
+}
+
+__device__ inline u16x8 buf_load16(__amdgpu_buffer_rsrc_t r, int off) {
+  return __builtin_bit_cast(u16x8, __builtin_amdgcn_raw_buffer_load_b128(r, off, 0, 0));
+}
+
+__device__ inline float buf_load_f32(__amdgpu_buffer_rsrc_t r, int off) {
+  return __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(r, off, 0, 0));
+}
+
 }  // namespace mfma_util
 }  // namespace attn

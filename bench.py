@@ -4,16 +4,17 @@
     python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME]
 
 A step is one whole backward of the workload on inputs already resident in
-HBM: ``attn_bwd_preprocess`` (delta = rowsum(dO * O); dQ, dK, dV zeroed)
-followed by ``attn_bwd`` accumulating dK, dV, dQ (one kernel launch in the
-default atomic-dQ mode).  O and LSE come from the
-library's own forward before the timed region.  Throughput counts
+HBM: ``attn_bwd_preprocess`` (delta = rowsum(dO * O)) followed by
+``attn_bwd`` (the dK / dV pass by key blocks, then the dQ pass by query
+blocks), writing dQ, dK, dV.  O and LSE come from the library's own forward
+before the timed region.  Throughput counts
 2 * (3 * Dqk + 2 * Dv) FLOPs per allowed (query, key) pair per query head --
 the five contractions -- and nothing for masked pairs or recomputation.
 
 Rank 0 prints one JSON line.  It also carries
-  * ``roofline`` for the dominant kernel (the main backward pass, timed alone
-    with HIP events on the stream it runs on),
+  * ``roofline`` for the main backward call (``attn_bwd``: its two kernels,
+    timed together with HIP events on the stream they run on; the
+    rocprofv3 summary lists each),
   * ``cpu_baseline``: the fp64 CPU oracle timed on a bounded sample of the
     same workload (a subset of the KV head groups),
   * extra timings (deterministic mode, the 4-chunk K/V split with the lse
@@ -153,21 +154,14 @@ def main():
     p = ab.make_problem(q, k, v, o=o, do=do, dq=dq, dk=dk, dv=dv, bias=bias, scale=w.scale, **mask_kw)
 
     def step(flags, ev=None):
-        # Atomic mode: the preprocess zeroes dQ/dK/dV and attn_bwd accumulates
-        # into them, so the timed attn_bwd call is the main kernel alone.
-        # Deterministic mode: attn_bwd overwrites its outputs itself (zeroing
-        # only what a two-way split needs).
-        determ = bool(flags & ab.ATTN_DETERMINISTIC)
+        # attn_bwd overwrites dQ, dK, dV (and dbias); it zeroes by itself
+        # whatever its split parts add into.
         if ev is not None:
             ev[0].record(stream)
-        if determ:
-            ab.attn_bwd_preprocess(p, o, do, lse, sinks, delta, dsinks, None, None, None, stream)
-        else:
-            ab.attn_bwd_preprocess(p, o, do, lse, sinks, delta, dsinks, dq, dk, dv, stream)
+        ab.attn_bwd_preprocess(p, o, do, lse, sinks, delta, dsinks, None, None, None, stream)
         if ev is not None:
             ev[1].record(stream)
-        extra = 0 if determ else (ab.ATTN_ACCUMULATE_DQ | ab.ATTN_ACCUMULATE_DKDV)
-        ab.attn_bwd(p, q, k, v, do, lse, delta, bias, dq, dk, dv, dbias, flags | extra, stream)
+        ab.attn_bwd(p, q, k, v, do, lse, delta, bias, dq, dk, dv, dbias, flags, stream)
         if ev is not None:
             ev[2].record(stream)
 
@@ -209,13 +203,13 @@ def main():
         "config": {"workload": w.name, "B": w.B, "Hq": w.Hq, "Hk": w.Hk, "Sq": w.Sq, "Sk": w.Sk,
                    "D": w.Dqk, "mask": w.mask, "window_left": w.window_left, "num_sink": w.num_sink,
                    "bias": w.bias, "sinks": w.sinks, "allowed_pairs_per_head": pairs,
-                   "counted_flop": flops, "timed": "attn_bwd_preprocess + attn_bwd (atomic dQ)"},
+                   "counted_flop": flops, "timed": "attn_bwd_preprocess + attn_bwd (dK/dV pass + dQ pass)"},
         "pct_peak": round(100.0 * value / PEAK_BF16_TFLOPS, 2),
         "wall_ms_per_step": round(wall_ms, 4),
         "preprocess_ms": round(pre_ms, 4),
         "roofline": {"bound": "mfma", "achieved": round(achieved, 2), "peak": PEAK_BF16_TFLOPS,
                      "unit": "TFLOP/s", "frac": round(achieved / PEAK_BF16_TFLOPS, 4),
-                     "traffic": traffic_record(kernel_key), "kernel": "attn_bwd main pass",
+                     "traffic": traffic_record(kernel_key), "kernel": "attn_bwd (k_dkdv2/k_dkdv + k_dq)",
                      "kernel_ms_mean": round(main_ms, 4), "kernel_ms_median": round(main_med, 4)},
     }
     if not args.no_extras:
