@@ -110,9 +110,12 @@ __global__ __launch_bounds__(NTF, 2) void k_fwd(Params p, FwdArgs a) {
   constexpr int R = Lay<D>::R, T = Lay<D>::T, BS = KT + 4;
   __shared__ __attribute__((aligned(16))) SmemFwd<D, KT, BIAS> sm;
 
-  const int tid = threadIdx.x, w = tid >> 6, l = tid & 63, lr = l & 31, lg = l >> 5;
+  const int tid = threadIdx.x, l = tid & 63, lr = l & 31, lg = l >> 5;
+  const int w = __builtin_amdgcn_readfirstlane(tid >> 6);   // wave-uniform
   const BlockXYZ blk = xcd_block();
-  const int i0 = blk.x * BQF;
+  // under a causal mask later row blocks see more keys: deal them first
+  const bool heavy_last = p.mask.kind != kMaskNone && p.mask.wl < 0;
+  const int i0 = (heavy_last ? (int)gridDim.x - 1 - blk.x : blk.x) * BQF;
   const int h = blk.y, b = blk.z, g = h / p.G;
   const int Sq = p.Sq, Sk = p.Sk;
   const int irow = i0 + 32 * w + lr;   // this lane's query row
@@ -182,22 +185,29 @@ __global__ __launch_bounds__(NTF, 2) void k_fwd(Params p, FwdArgs a) {
     // t = j' - i' - diag for key j0 + 4 lg + c
     const int tb = j0 + (int)p.mask.k_off + 4 * lg - (irow + (int)p.mask.q_off) - (int)p.mask.diag;
     float mt = -INFINITY;
-#pragma unroll
-    for (int hh = 0; hh < NH; ++hh) {
-#pragma unroll
-      for (int r = 0; r < 16; ++r) {
-        const int c = 32 * hh + 8 * (r >> 2) + (r & 3);
-        float x = sacc[hh][r] * scale_log2;
-        if (BIAS) x = fmaf(sm.bias[cur][(32 * w + lr) * BS + 4 * lg + c], kLog2e, x);
-        if (!full) {
-          const int j = j0 + 4 * lg + c;
-          const int t = tb + c;
-          const bool ok = j < Sk && (no_mask || (t <= wr_t && t >= lo_t) || (j + (int)p.mask.k_off) < p.mask.n_sink);
-          x = ok ? x : -INFINITY;
-        }
-        sacc[hh][r] = x;
-        mt = fmaxf(mt, x);
+    auto elem = [&](int hh, int r, bool masked) {
+      const int c = 32 * hh + 8 * (r >> 2) + (r & 3);
+      float x = sacc[hh][r] * scale_log2;
+      if (BIAS) x = fmaf(sm.bias[cur][(32 * w + lr) * BS + 4 * lg + c], kLog2e, x);
+      if (masked) {
+        const int j = j0 + 4 * lg + c;
+        const int t = tb + c;
+        const bool ok = (j < Sk) & (no_mask | ((t <= wr_t) & (t >= lo_t)) | ((j + (int)p.mask.k_off) < p.mask.n_sink));
+        x = ok ? x : -INFINITY;
       }
+      sacc[hh][r] = x;
+      mt = fmaxf(mt, x);
+    };
+    if (full) {
+#pragma unroll
+      for (int hh = 0; hh < NH; ++hh)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) elem(hh, r, false);
+    } else {
+#pragma unroll
+      for (int hh = 0; hh < NH; ++hh)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) elem(hh, r, true);
     }
     mt = fmaxf(mt, __shfl_xor(mt, 32));
     const float mn = fmaxf(m, mt);

@@ -149,7 +149,8 @@ __global__ __launch_bounds__(NT, 1) void k_dkdv(Params p, BwdArgs a, DkdvGrid gd
   constexpr int R = Lay<D>::R, T = Lay<D>::T;
   __shared__ __attribute__((aligned(16))) SmemDKDV<D> sm;
 
-  const int tid = threadIdx.x, w = tid >> 6, l = tid & 63, lr = l & 31, lg = l >> 5;
+  const int tid = threadIdx.x, l = tid & 63, lr = l & 31, lg = l >> 5;
+  const int w = __builtin_amdgcn_readfirstlane(tid >> 6);   // wave-uniform
   const int Sq = p.Sq, Sk = p.Sk;
   const int nkb = (Sk + BK - 1) / BK;
   const BlockXYZ blk = xcd_block();
@@ -315,10 +316,11 @@ __global__ __launch_bounds__(NT, 1) void k_dkdv(Params p, BwdArgs a, DkdvGrid gd
           for (int r = 0; r < 16; ++r) {
             const int c = 8 * (r >> 2) + (r & 3);
             const int t = tb - c;
-            const bool ok = key_ok && (no_mask || (t <= wr_t && t >= lo_t) || sink_key);
+            const bool ok = key_ok & (no_mask | ((t <= wr_t) & (t >= lo_t)) | sink_key);
             float x = fmaf(sacc[r], scale_log2, -L4[r >> 2][r & 3]);
             if (BIAS) x = fmaf(bpre[r], kLog2e, x);
-            pv[r] = ok ? __builtin_amdgcn_exp2f(x) : 0.f;
+            const float ex = __builtin_amdgcn_exp2f(x);
+            pv[r] = ok ? ex : 0.f;
             dsv[r] = pv[r] * fmaf(dpacc[r], scale, -D4[r >> 2][r & 3]);
           }
         }
@@ -476,7 +478,8 @@ __global__ __launch_bounds__(NT2) void k_dkdv2(Params p, BwdArgs a, DkdvGrid gd)
   constexpr int R = Lay<D>::R, T = Lay<D>::T;
   __shared__ __attribute__((aligned(16))) SmemDKDV2<D> sm;
 
-  const int tid = threadIdx.x, w = tid >> 6, l = tid & 63, lr = l & 31, lg = l >> 5;
+  const int tid = threadIdx.x, l = tid & 63, lr = l & 31, lg = l >> 5;
+  const int w = __builtin_amdgcn_readfirstlane(tid >> 6);   // wave-uniform
   const int pr = w & 3;               // pair: keys [32 pr, 32 pr + 32) of the block
   const bool sw = w < 4;              // S wave (else dP wave)
   const int cb = sw ? 0 : D / 2;      // first dK / dV column of this wave
@@ -594,9 +597,9 @@ __global__ __launch_bounds__(NT2) void k_dkdv2(Params p, BwdArgs a, DkdvGrid gd)
           for (int r = 0; r < 16; ++r) {
             const int c = 8 * (r >> 2) + (r & 3);
             const int t = tb - c;
-            const bool ok = key_ok && (no_mask || (t <= wr_t && t >= lo_t) || sink_key);
-            const float x = fmaf(acc[r], scale_log2, -L4[r >> 2][r & 3]);
-            pv[r] = ok ? __builtin_amdgcn_exp2f(x) : 0.f;
+            const bool ok = key_ok & (no_mask | ((t <= wr_t) & (t >= lo_t)) | sink_key);
+            const float ex = __builtin_amdgcn_exp2f(fmaf(acc[r], scale_log2, -L4[r >> 2][r & 3]));
+            pv[r] = ok ? ex : 0.f;
           }
         }
         pa0 = pack8(pv);
@@ -830,9 +833,12 @@ __global__ __launch_bounds__(NT, 2) void k_dq(Params p, BwdArgs a) {
   constexpr int R = Lay<D>::R, T = Lay<D>::T;
   __shared__ __attribute__((aligned(16))) SmemDQ<D, BIAS> sm;
 
-  const int tid = threadIdx.x, w = tid >> 6, l = tid & 63, lr = l & 31, lg = l >> 5;
+  const int tid = threadIdx.x, l = tid & 63, lr = l & 31, lg = l >> 5;
+  const int w = __builtin_amdgcn_readfirstlane(tid >> 6);   // wave-uniform
   const BlockXYZ blk = xcd_block();
-  const int i0 = blk.x * BQ3;
+  // under a causal mask later row blocks see more keys: deal them first
+  const bool heavy_last = p.mask.kind != kMaskNone && p.mask.wl < 0;
+  const int i0 = (heavy_last ? (int)gridDim.x - 1 - blk.x : blk.x) * BQ3;
   const int h = blk.y, b = blk.z, g = h / p.G;
   const int Sq = p.Sq, Sk = p.Sk;
   const int irow = i0 + 32 * w + lr;           // this lane's query row
@@ -904,19 +910,25 @@ __global__ __launch_bounds__(NT, 2) void k_dq(Params p, BwdArgs a) {
     // t = j' - i' - diag for key j0 + 4 lg + c
     const int tb = j0 + (int)p.mask.k_off + 4 * lg - (irow + (int)p.mask.q_off) - (int)p.mask.diag;
     float dsv[16];
-#pragma unroll
-    for (int r = 0; r < 16; ++r) {
+    auto elem = [&](int r, bool masked) {
       const int c = 8 * (r >> 2) + (r & 3);
-      const int j = j0 + 4 * lg + c;
       float x = fmaf(sacc[r], scale_log2, -lse2);
       if (BIAS) x = fmaf(sm.bias[cur][(32 * w + lr) * BSTR + 4 * lg + c], kLog2e, x);
       float pp = __builtin_amdgcn_exp2f(x);
-      if (!full) {
+      if (masked) {
+        const int j = j0 + 4 * lg + c;
         const int t = tb + c;
-        const bool ok = j < Sk && (no_mask || (t <= wr_t && t >= lo_t) || (j + (int)p.mask.k_off) < p.mask.n_sink);
+        const bool ok = (j < Sk) & (no_mask | ((t <= wr_t) & (t >= lo_t)) | ((j + (int)p.mask.k_off) < p.mask.n_sink));
         pp = ok ? pp : 0.f;
       }
       dsv[r] = pp * fmaf(dpacc[r], scale, -dls);
+    };
+    if (full) {
+#pragma unroll
+      for (int r = 0; r < 16; ++r) elem(r, false);
+    } else {
+#pragma unroll
+      for (int r = 0; r < 16; ++r) elem(r, true);
     }
     const bf16x8 sa0 = pack8(dsv), sa1 = pack8(dsv + 8);
 #pragma unroll
