@@ -423,44 +423,53 @@ struct SmemDKDV2 {
   float dls[2][BQ];                       // delta * scale
 };
 
-// Staging of one 32-row Q / dO tile by 512 threads (as Stage).
+// Staging of one 32-row Q / dO tile by 512 threads.  Each thread owns fixed
+// 16-byte chunk slots (the tensor of a slot is the same for a whole wave)
+// and fetches them with buffer loads whose resource covers the tile's rows
+// only: rows past the end read as zero, and the per-thread offsets never
+// change.  The last 32 threads keep the tile's LSE and delta.
 template <int D>
 struct Stage2 {
   static constexpr int NCR = D / 8;
   static constexpr int NCH = 2 * BQ * NCR;
   static constexpr int NR = NCH / NT2;
-  static_assert(NCH % NT2 == 0, "chunks per thread");
+  static_assert(NCH % NT2 == 0 && (BQ * NCR) % 64 == 0, "chunks per thread, one tensor per wave");
   u16x8 v[NR];
   float lse, dl;
+  int voff[NR], lrow[NR], ltr[NR];
+  bool tdo[NR];   // slot holds dO (else Q)
 
-  __device__ inline void load(const unsigned short* q, const unsigned short* dout, int64_t qs, int64_t ds,
-                              const float* lse_p, const float* dl_p, int i0, int Sq) {
-    const int t = threadIdx.x;
+  __device__ inline void init(int w, int q_rb, int d_rb) {
 #pragma unroll
     for (int k = 0; k < NR; ++k) {
-      const int idx = t + NT2 * k;
-      const int tensor = idx / (BQ * NCR), rem = idx % (BQ * NCR);
+      tdo[k] = (64 * w + NT2 * k) / (BQ * NCR) != 0;
+      const int rem = (threadIdx.x + NT2 * k) % (BQ * NCR);
       const int row = rem / NCR, c = rem % NCR;
-      const int64_t i = min(i0 + row, Sq - 1);
-      v[k] = *(const u16x8*)((tensor == 0 ? q + i * qs : dout + i * ds) + 8 * c);
-    }
-    if (t >= NT2 - BQ) {
-      const int64_t i = min(i0 + (t - (NT2 - BQ)), Sq - 1);
-      lse = lse_p[i];
-      dl = dl_p[i];
+      voff[k] = row * (tdo[k] ? d_rb : q_rb) + 16 * c;
+      lrow[k] = row * Lay<D>::R + 8 * c;
+      ltr[k] = row * Lay<D>::T + 8 * c;
     }
   }
 
+  // q_t / d_t / l_t / dl_t point at the tile's first row; rows = rows inside the problem
+  __device__ inline void load(const unsigned short* q_t, const unsigned short* d_t, int q_rb, int d_rb,
+                              const float* l_t, const float* dl_t, int rows) {
+    const __amdgpu_buffer_rsrc_t rq = buf_rsrc(q_t, rows * q_rb);
+    const __amdgpu_buffer_rsrc_t rd = buf_rsrc(d_t, rows * d_rb);
+#pragma unroll
+    for (int k = 0; k < NR; ++k) v[k] = buf_load16(tdo[k] ? rd : rq, voff[k]);
+    const int r = 4 * (threadIdx.x & (BQ - 1));
+    lse = buf_load_f32(buf_rsrc(l_t, rows * 4), r);
+    dl = buf_load_f32(buf_rsrc(dl_t, rows * 4), r);
+  }
+
   __device__ inline void store(SmemDKDV2<D>& sm, int buf, int i0, int Sq, float scale) const {
-    const int t = threadIdx.x;
 #pragma unroll
     for (int k = 0; k < NR; ++k) {
-      const int idx = t + NT2 * k;
-      const int tensor = idx / (BQ * NCR), rem = idx % (BQ * NCR);
-      const int row = rem / NCR, c = rem % NCR;
-      *(u16x8*)((tensor == 0 ? sm.qr[buf] : sm.dr[buf]) + row * Lay<D>::R + 8 * c) = v[k];
-      *(u16x8*)((tensor == 0 ? sm.qt[buf] : sm.dt[buf]) + row * Lay<D>::T + 8 * c) = v[k];
+      *(u16x8*)((tdo[k] ? sm.dr[buf] : sm.qr[buf]) + lrow[k]) = v[k];
+      *(u16x8*)((tdo[k] ? sm.dt[buf] : sm.qt[buf]) + ltr[k]) = v[k];
     }
+    const int t = threadIdx.x;
     if (t >= NT2 - BQ) {
       const int r = t - (NT2 - BQ);
       const bool ok = i0 + r < Sq;
@@ -544,10 +553,13 @@ __global__ __launch_bounds__(NT2) void k_dkdv2(Params p, BwdArgs a, DkdvGrid gd)
     wait_vm_loads();
 
     Stage2<D> stg;
+    const int q_rb = 2 * (int)p.q_str[2], d_rb = 2 * (int)p.do_str[2];
+    stg.init(w, q_rb, d_rb);
     auto issue = [&](int h, int i0) {
-      stg.load((const unsigned short*)a.q + b * p.q_str[0] + h * p.q_str[1],
-               (const unsigned short*)a.dout + b * p.do_str[0] + h * p.do_str[1], p.q_str[2], p.do_str[2],
-               a.lse + ((int64_t)b * p.Hq + h) * Sq, a.delta + ((int64_t)b * p.Hq + h) * Sq, i0, Sq);
+      const int64_t rb = ((int64_t)b * p.Hq + h) * Sq + i0;
+      stg.load((const unsigned short*)a.q + b * p.q_str[0] + h * p.q_str[1] + (int64_t)i0 * p.q_str[2],
+               (const unsigned short*)a.dout + b * p.do_str[0] + h * p.do_str[1] + (int64_t)i0 * p.do_str[2],
+               q_rb, d_rb, a.lse + rb, a.delta + rb, min(Sq - i0, BQ));
     };
     int h = h_begin + (nqb > 0 ? it_lo / nqb : 0), qb = nqb > 0 ? it_lo % nqb : 0;
     if (n_it > 0) {
@@ -765,63 +777,75 @@ struct SmemDQ {
   float bias[BIAS ? 2 : 1][BIAS ? BQ3 * BSTR : 1];   // bias[h][i0 + r][j0 + c], row-major padded
 };
 
-// Staging of one 32-key K / V tile (same dealing of 16-byte chunks as
-// Stage) and, with a bias, of the [128 rows x 32 keys] fp32 bias tile
-// (8 lanes per row, 16 bytes each: coalesced along the keys).
+// Staging of one 32-key K / V tile and, with a bias, of the [128 rows x 32
+// keys] fp32 bias tile (8 lanes per row, 16 bytes each: coalesced along the
+// keys).  Fixed per-thread 16-byte slots fetched with buffer loads whose
+// resource ends at the tile's last valid element: keys (and bias rows) past
+// the end read as zero and are masked to P = 0.
 template <int D, bool BIAS>
 struct StageKV {
   static constexpr int NCR = D / 8;
   static constexpr int NCH = 2 * BK3 * NCR;
   static constexpr int NR = NCH / NT;
   static constexpr int NBI = BIAS ? BQ3 * BK3 / 4 / NT : 0;   // float4 bias chunks per thread
+  static_assert((BK3 * NCR) % NT == 0, "one tensor per chunk slot");
   u16x8 v[NR];
   f32x4 bv[BIAS ? NBI : 1];
+  int voff[NR], lrow[NR], ltr[NR];
+  int boff[BIAS ? NBI : 1], bl[BIAS ? NBI : 1];
 
-  __device__ inline void load(const unsigned short* k, const unsigned short* vv, int64_t ks, int64_t vs,
-                              int64_t j0, int Sk, const float* bias_h, int64_t bstr, int i0, int Sq) {
+  static constexpr bool is_v(int m) { return (NT * m) / (BK3 * NCR) != 0; }
+
+  __device__ inline void init(int k_rb, int v_rb, int b_rb) {
     const int t = threadIdx.x;
 #pragma unroll
     for (int m = 0; m < NR; ++m) {
-      const int idx = t + NT * m;
-      const int tensor = idx / (BK3 * NCR), rem = idx % (BK3 * NCR);
+      const int rem = (t + NT * m) % (BK3 * NCR);
       const int row = rem / NCR, c = rem % NCR;
-      const int64_t j = min(j0 + row, (int64_t)Sk - 1);
-      v[m] = *(const u16x8*)((tensor == 0 ? k + j * ks : vv + j * vs) + 8 * c);
+      voff[m] = row * (is_v(m) ? v_rb : k_rb) + 16 * c;
+      lrow[m] = row * Lay<D>::R + 8 * c;
+      ltr[m] = row * Lay<D>::T + 8 * c;
     }
     if (BIAS) {
 #pragma unroll
       for (int m = 0; m < NBI; ++m) {
         const int idx = t + NT * m;
         const int row = idx / (BK3 / 4), c4 = idx % (BK3 / 4);
-        const int64_t i = min(i0 + row, Sq - 1);
-        const int64_t j = min(j0 + 4 * c4, (int64_t)Sk - 4);   // Sk % 4 == 0 for the vector path
-        bv[m] = *(const f32x4*)(bias_h + i * bstr + j);
+        boff[m] = row * b_rb + 16 * c4;
+        bl[m] = row * BSTR + 4 * c4;
       }
     }
   }
 
-  // keys past the end hold the last key: finite, and masked to P = 0
+  // k_t / v_t: first key of the tile; keys = keys inside the problem;
+  // b_t: bias of (first row, first key), b_bytes: bytes up to its last valid element
+  __device__ inline void load(const unsigned short* k_t, const unsigned short* v_t, int k_rb, int v_rb, int keys,
+                              const float* b_t, int b_bytes) {
+    const __amdgpu_buffer_rsrc_t rk = buf_rsrc(k_t, keys * k_rb);
+    const __amdgpu_buffer_rsrc_t rv = buf_rsrc(v_t, keys * v_rb);
+#pragma unroll
+    for (int m = 0; m < NR; ++m) v[m] = buf_load16(is_v(m) ? rv : rk, voff[m]);
+    if (BIAS) {
+      const __amdgpu_buffer_rsrc_t rb = buf_rsrc(b_t, b_bytes);
+#pragma unroll
+      for (int m = 0; m < NBI; ++m)
+        bv[m] = __builtin_bit_cast(f32x4, __builtin_amdgcn_raw_buffer_load_b128(rb, boff[m], 0, 0));
+    }
+  }
+
   __device__ inline void store(SmemDQ<D, BIAS>& sm, int buf) const {
-    const int t = threadIdx.x;
 #pragma unroll
     for (int m = 0; m < NR; ++m) {
-      const int idx = t + NT * m;
-      const int tensor = idx / (BK3 * NCR), rem = idx % (BK3 * NCR);
-      const int row = rem / NCR, c = rem % NCR;
-      if (tensor == 0) {
-        *(u16x8*)(sm.kr[buf] + row * Lay<D>::R + 8 * c) = v[m];
-        *(u16x8*)(sm.kt[buf] + row * Lay<D>::T + 8 * c) = v[m];
+      if (is_v(m)) {
+        *(u16x8*)(sm.vr[buf] + lrow[m]) = v[m];
       } else {
-        *(u16x8*)(sm.vr[buf] + row * Lay<D>::R + 8 * c) = v[m];
+        *(u16x8*)(sm.kr[buf] + lrow[m]) = v[m];
+        *(u16x8*)(sm.kt[buf] + ltr[m]) = v[m];
       }
     }
     if (BIAS) {
 #pragma unroll
-      for (int m = 0; m < NBI; ++m) {
-        const int idx = t + NT * m;
-        const int row = idx / (BK3 / 4), c4 = idx % (BK3 / 4);
-        *(f32x4*)&sm.bias[buf][row * BSTR + 4 * c4] = bv[m];
-      }
+      for (int m = 0; m < NBI; ++m) *(f32x4*)&sm.bias[buf][bl[m]] = bv[m];
     }
   }
 };
@@ -888,16 +912,25 @@ __global__ __launch_bounds__(NT, 2) void k_dq(Params p, BwdArgs a) {
   for (int n = 0; n < NB; ++n) dq[n] = zero16();
 
   const float* bias_h = BIAS ? a.bias + h * p.bias_str[0] : nullptr;
+  const int k_rb = 2 * (int)p.k_str[2], v_rb = 2 * (int)p.v_str[2], b_rb = 4 * (int)p.bias_str[1];
+  const int brows = min(Sq - i0, BQ3);
   StageKV<D, BIAS> stg;
+  stg.init(k_rb, v_rb, b_rb);
+  auto issue = [&](int it) {
+    const int j0 = (int)tile_of(it);
+    const int keys = min(Sk - j0, BK3);
+    stg.load(kp + (int64_t)j0 * p.k_str[2], vp + (int64_t)j0 * p.v_str[2], k_rb, v_rb, keys,
+             BIAS ? bias_h + (int64_t)i0 * p.bias_str[1] + j0 : nullptr, (brows - 1) * b_rb + 4 * keys);
+  };
   if (n_it > 0) {
-    stg.load(kp, vp, p.k_str[2], p.v_str[2], tile_of(0), Sk, bias_h, p.bias_str[1], i0, Sq);
+    issue(0);
     stg.store(sm, 0);
     __syncthreads();
   }
   for (int it = 0; it < n_it; ++it) {
     const int cur = it & 1;
     const int j0 = (int)tile_of(it);
-    if (it + 1 < n_it) stg.load(kp, vp, p.k_str[2], p.v_str[2], tile_of(it + 1), Sk, bias_h, p.bias_str[1], i0, Sq);
+    if (it + 1 < n_it) issue(it + 1);
 
     // S^T = K Q^T and dP^T = V dO^T: keys on accumulator rows, this lane's row on the column
     f32x16 sacc = zero16(), dpacc = zero16();

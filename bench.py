@@ -11,6 +11,9 @@ before the timed region.  Throughput counts
 2 * (3 * Dqk + 2 * Dv) FLOPs per allowed (query, key) pair per query head --
 the five contractions -- and nothing for masked pairs or recomputation.
 
+Before the W warmup steps the step runs untimed for ``--settle-ms``
+(default 500 ms) so that the timed steps see the GPU's steady clock.
+
 Rank 0 prints one JSON line.  It also carries
   * ``roofline`` for the main backward call (``attn_bwd``: its two kernels,
     timed together with HIP events on the stream they run on; the
@@ -43,6 +46,8 @@ def parse():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--settle-ms", type=float, default=500.0,
+                    help="untimed load before the warmup steps, to reach the steady GPU clock")
     ap.add_argument("--workload", default=None, help="workload name (default: the headline workload)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-extras", action="store_true", help="skip deterministic / chunked / forward timings")
@@ -182,6 +187,18 @@ def main():
 
     flops = backward_flops(w)
     pairs = allowed_pairs(w.Sq, w.Sk, w.mask, w.window_left, w.window_right, w.num_sink)
+    # Clock settle: the GPU takes a few hundred milliseconds of load to reach
+    # its steady clock; run the step (untimed) for that long before the
+    # warmup steps, so the timed steps see the steady state.
+    settle_s = args.settle_ms * 1e-3
+    t_end = time.perf_counter() + settle_s
+    n_settle = 0
+    while time.perf_counter() < t_end:
+        step(0)
+        n_settle += 1
+        if n_settle % 8 == 0:
+            torch.cuda.synchronize()
+    torch.cuda.synchronize()
     wall_ms, span_ms, pre_ms, main_ms, main_med = timed(0, args.steps, args.warmup)
     ms_per_step = span_ms
     value = flops / (ms_per_step * 1e-3) / 1e12
@@ -207,6 +224,7 @@ def main():
         "pct_peak": round(100.0 * value / PEAK_BF16_TFLOPS, 2),
         "wall_ms_per_step": round(wall_ms, 4),
         "preprocess_ms": round(pre_ms, 4),
+        "clock_settle": {"ms": args.settle_ms, "steps": n_settle},
         "roofline": {"bound": "mfma", "achieved": round(achieved, 2), "peak": PEAK_BF16_TFLOPS,
                      "unit": "TFLOP/s", "frac": round(achieved / PEAK_BF16_TFLOPS, 4),
                      "traffic": traffic_record(kernel_key), "kernel": "attn_bwd (k_dkdv2/k_dkdv + k_dq)",
