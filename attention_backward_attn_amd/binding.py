@@ -46,6 +46,8 @@ class attn_problem_t(ctypes.Structure):
         ("o_str", ctypes.c_int64 * 3), ("do_str", ctypes.c_int64 * 3),
         ("dq_str", ctypes.c_int64 * 3), ("dk_str", ctypes.c_int64 * 3), ("dv_str", ctypes.c_int64 * 3),
         ("bias_str", ctypes.c_int64 * 2),
+        ("cu_seqlens_q", ctypes.c_void_p), ("cu_seqlens_k", ctypes.c_void_p),
+        ("total_q", ctypes.c_int64), ("total_k", ctypes.c_int64),
     ]
 
 
@@ -106,6 +108,15 @@ def _strides3(t):
     return tuple(t.stride()[:3])
 
 
+def _strides_packed(t):
+    """{b, h, s} strides of a packed [T, H, D] tensor (the b stride is unused)."""
+    if t is None:
+        return (0, 0, 0)
+    if t.stride(-1) != 1:
+        raise ValueError("the last dimension must be contiguous")
+    return (0, t.stride(1), t.stride(0))
+
+
 def _dtype_code(t) -> int:
     import torch
     if t.dtype == torch.float32:
@@ -118,12 +129,28 @@ def _dtype_code(t) -> int:
 def make_problem(q, k, v, *, o=None, do=None, dq=None, dk=None, dv=None, bias=None,
                  scale: Optional[float] = None, mask: str = "none", window_left: int = -1,
                  window_right: int = 0, num_sink_tokens: int = 0, q_offset: int = 0,
-                 k_offset: int = 0, sq_total: int = 0, sk_total: int = 0) -> attn_problem_t:
-    """Problem descriptor from tensors in [B, H, S, D] layout."""
-    B, Hq, Sq, Dqk = q.shape
-    Hk, Sk, Dv = k.shape[1], k.shape[2], v.shape[3]
+                 k_offset: int = 0, sq_total: int = 0, sk_total: int = 0,
+                 cu_seqlens_q=None, cu_seqlens_k=None, max_seqlen_q: int = 0,
+                 max_seqlen_k: int = 0) -> attn_problem_t:
+    """Problem descriptor from tensors in [B, H, S, D] layout, or -- with
+    cu_seqlens_q / cu_seqlens_k (int32 device tensors of B + 1 prefix sums)
+    -- from packed [T, H, D] tensors of a variable-length batch (TND)."""
+    packed = cu_seqlens_q is not None
+    if packed:
+        if cu_seqlens_k is None or q.dim() != 3:
+            raise ValueError("a packed batch needs cu_seqlens_q, cu_seqlens_k and [T, H, D] tensors")
+        B = cu_seqlens_q.numel() - 1
+        Hq, Dqk = q.shape[1], q.shape[2]
+        Hk, Dv = k.shape[1], v.shape[2]
+        Sq, Sk = max_seqlen_q, max_seqlen_k
+    else:
+        B, Hq, Sq, Dqk = q.shape
+        Hk, Sk, Dv = k.shape[1], k.shape[2], v.shape[3]
     p = attn_problem_t()
     lib().attn_problem_init(ctypes.byref(p), B, Hq, Hk, Sq, Sk, Dqk, Dv)
+    if packed:
+        p.cu_seqlens_q, p.cu_seqlens_k = _ptr(cu_seqlens_q), _ptr(cu_seqlens_k)
+        p.total_q, p.total_k = q.shape[0], k.shape[0]
     if scale is not None:
         p.scale = float(scale)
     p.in_dtype = _dtype_code(q)
@@ -131,19 +158,20 @@ def make_problem(q, k, v, *, o=None, do=None, dq=None, dk=None, dv=None, bias=No
     p.mask = MASKS[mask]
     p.window_left, p.window_right, p.num_sink_tokens = window_left, window_right, num_sink_tokens
     p.q_offset, p.k_offset, p.sq_total, p.sk_total = q_offset, k_offset, sq_total, sk_total
-    p.q_str[:] = _strides3(q)
-    p.k_str[:] = _strides3(k)
-    p.v_str[:] = _strides3(v)
+    st = _strides_packed if packed else _strides3
+    p.q_str[:] = st(q)
+    p.k_str[:] = st(k)
+    p.v_str[:] = st(v)
     if o is not None:
-        p.o_str[:] = _strides3(o)
+        p.o_str[:] = st(o)
     if do is not None:
-        p.do_str[:] = _strides3(do)
+        p.do_str[:] = st(do)
     if dq is not None:
-        p.dq_str[:] = _strides3(dq)
+        p.dq_str[:] = st(dq)
     if dk is not None:
-        p.dk_str[:] = _strides3(dk)
+        p.dk_str[:] = st(dk)
     if dv is not None:
-        p.dv_str[:] = _strides3(dv)
+        p.dv_str[:] = st(dv)
     if bias is not None:
         if bias.stride(-1) != 1:
             raise ValueError("bias: the key dimension must be contiguous")
@@ -184,10 +212,16 @@ def attn_lse_merge(o_acc, lse_acc, o_part, lse_part, stream=None):
 # Convenience wrappers that allocate outputs with torch (device memory only).
 # ---------------------------------------------------------------------------
 def forward(q, k, v, *, bias=None, sinks=None, o_dtype=None, stream=None, **mask_kw):
-    """(O, LSE) of attention; O in ``o_dtype`` (default fp32)."""
+    """(O, LSE) of attention; O in ``o_dtype`` (default fp32).  With
+    cu_seqlens_q / cu_seqlens_k (packed [T, H, D] tensors) O is packed too
+    and LSE is [B, Hq, max_seqlen_q]."""
     import torch
-    B, Hq, Sq, _ = q.shape
-    o = torch.empty(B, Hq, Sq, v.shape[3], device=q.device, dtype=o_dtype or torch.float32)
+    if mask_kw.get("cu_seqlens_q") is not None:
+        B, Hq, Sq = mask_kw["cu_seqlens_q"].numel() - 1, q.shape[1], mask_kw["max_seqlen_q"]
+        o = torch.empty(q.shape[0], Hq, v.shape[2], device=q.device, dtype=o_dtype or torch.float32)
+    else:
+        B, Hq, Sq, _ = q.shape
+        o = torch.empty(B, Hq, Sq, v.shape[3], device=q.device, dtype=o_dtype or torch.float32)
     lse = torch.empty(B, Hq, Sq, device=q.device, dtype=torch.float32)
     p = make_problem(q, k, v, o=o, bias=bias, **mask_kw)
     attn_fwd_lse(p, q, k, v, bias, sinks, o, lse, stream)
@@ -199,9 +233,12 @@ def backward(q, k, v, o, do, lse, *, bias=None, sinks=None, want_dbias=False, fl
     """Full backward: preprocess then the main pass.  Returns a dict with
     dq, dk, dv (fp32), dbias and dsinks (or None) and delta."""
     import torch
-    B, Hq, Sq, Dqk = q.shape
     dev = q.device
-    dq = torch.empty(B, Hq, Sq, Dqk, device=dev, dtype=torch.float32) if dq is None else dq
+    if mask_kw.get("cu_seqlens_q") is not None:
+        B, Hq, Sq = mask_kw["cu_seqlens_q"].numel() - 1, q.shape[1], mask_kw["max_seqlen_q"]
+    else:
+        B, Hq, Sq, _ = q.shape
+    dq = torch.empty(q.shape, device=dev, dtype=torch.float32) if dq is None else dq
     dk = torch.empty(k.shape, device=dev, dtype=torch.float32)
     dv = torch.empty(v.shape, device=dev, dtype=torch.float32)
     delta = torch.empty(B, Hq, Sq, device=dev, dtype=torch.float32)

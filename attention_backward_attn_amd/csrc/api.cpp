@@ -38,8 +38,18 @@ attn_status_t check_problem(const attn_problem_t* p) {
   if (p->q_offset + p->Sq > sq_t || p->k_offset + p->Sk > sk_t) return ATTN_EINVAL;
   // the kernels evaluate the mask in 32-bit global indices
   if (sq_t >= (int64_t(1) << 30) || sk_t >= (int64_t(1) << 30)) return ATTN_EUNSUPPORTED;
+  if ((p->cu_seqlens_q == nullptr) != (p->cu_seqlens_k == nullptr)) return ATTN_EINVAL;
+  if (p->cu_seqlens_q) {
+    if (p->q_offset || p->k_offset || p->sq_total || p->sk_total) return ATTN_EINVAL;
+    if (p->total_q < 0 || p->total_k < 0) return ATTN_EINVAL;
+    if (p->total_q >= (int64_t(1) << 31) || p->total_k >= (int64_t(1) << 31)) return ATTN_EUNSUPPORTED;
+  }
   return ATTN_OK;
 }
+
+bool packed(const attn_problem_t* p) { return p->cu_seqlens_q != nullptr; }
+
+bool aligned16(const void* x) { return ((uintptr_t)x & 15u) == 0; }
 
 Params make_params(const attn_problem_t* p) {
   Params k{};
@@ -62,7 +72,18 @@ Params make_params(const attn_problem_t* p) {
   }
   k.bias_str[0] = p->bias_str[0];
   k.bias_str[1] = p->bias_str[1];
+  k.cu_q = p->cu_seqlens_q;
+  k.cu_k = p->cu_seqlens_k;
+  k.tot_q = p->total_q;
+  k.tot_k = p->total_k;
   return k;
+}
+
+// dK / dV (or any k-side tensor) as rows to zero: [B, H, Sk] dense, or the
+// packed rows [total_k] of a variable-length batch.
+attn::ZeroRows ksite_rows(const attn_problem_t* p, float* x, int D, const int64_t* str) {
+  if (packed(p)) return attn::ZeroRows{x, 1, p->Hk, (int)p->total_k, D, {0, str[1], str[2]}};
+  return attn::ZeroRows{x, p->B, p->Hk, p->Sk, D, {str[0], str[1], str[2]}};
 }
 
 attn_status_t hip_status(hipError_t e) { return e == hipSuccess ? ATTN_OK : ATTN_EHIP; }
@@ -121,8 +142,9 @@ attn_status_t attn_fwd_lse(const attn_problem_t* p, const void* q, const void* k
   Params kp = make_params(p);
   attn::FwdArgs a{q, k, v, bias, sinks, o, lse};
   const bool o_bf16 = p->o_dtype == ATTN_BF16;
-  if (p->in_dtype == ATTN_BF16 && attn::mfma_fwd_supported(kp, a, o_bf16))
-    return hip_status(attn::launch_fwd_mfma(kp, a, o_bf16, (hipStream_t)stream));
+  const bool mfma = p->in_dtype == ATTN_BF16 && attn::mfma_fwd_supported(kp, a, o_bf16);
+  if (packed(p) && (!mfma || bias)) return ATTN_EUNSUPPORTED;
+  if (mfma) return hip_status(attn::launch_fwd_mfma(kp, a, o_bf16, (hipStream_t)stream));
   return hip_status(attn::launch_fwd_simt(kp, a, p->in_dtype == ATTN_BF16, o_bf16, (hipStream_t)stream));
 }
 
@@ -139,20 +161,21 @@ attn_status_t attn_bwd_preprocess(const attn_problem_t* p, const void* o, const 
   if (!empty && (!o || !dout || !delta)) return ATTN_EINVAL;
   if (sinks && !empty && !lse) return ATTN_EINVAL;
   hipStream_t s = (hipStream_t)stream;
+  const attn::Packed pk{p->cu_seqlens_q, p->total_q};
   if (!empty) {
     hipError_t e = attn::launch_delta(o, p->o_dtype == ATTN_BF16, dout, p->in_dtype == ATTN_BF16, delta,
                                       p->B, p->Hq, p->Sq, p->Dv, p->o_str, p->do_str, dq_zero, p->Dqk,
-                                      p->dq_str, s);
+                                      p->dq_str, pk, s);
     if (e != hipSuccess) return ATTN_EHIP;
   }
   if (dk_zero || dv_zero) {
     attn::ZeroRows z[2];
     int nz = 0;
-    if (dk_zero) z[nz++] = attn::ZeroRows{dk_zero, p->B, p->Hk, p->Sk, p->Dqk, {p->dk_str[0], p->dk_str[1], p->dk_str[2]}};
-    if (dv_zero) z[nz++] = attn::ZeroRows{dv_zero, p->B, p->Hk, p->Sk, p->Dv, {p->dv_str[0], p->dv_str[1], p->dv_str[2]}};
+    if (dk_zero) z[nz++] = ksite_rows(p, dk_zero, p->Dqk, p->dk_str);
+    if (dv_zero) z[nz++] = ksite_rows(p, dv_zero, p->Dv, p->dv_str);
     if (attn::launch_zero_multi(z, nz, s) != hipSuccess) return ATTN_EHIP;
   }
-  if (sinks) return hip_status(attn::launch_dsinks(lse, delta, sinks, dsinks, p->B, p->Hq, p->Sq, s));
+  if (sinks) return hip_status(attn::launch_dsinks(lse, delta, sinks, dsinks, p->B, p->Hq, p->Sq, pk, s));
   return ATTN_OK;
 }
 
@@ -185,6 +208,10 @@ attn_status_t attn_bwd(const attn_problem_t* p, const void* q, const void* k, co
       if (p->Dqk > attn::kSimtMaxD || p->Dv > attn::kSimtMaxD) return ATTN_EUNSUPPORTED;
     }
   }
+  // a packed batch runs on the matrix-core kernels only
+  if (packed(p) && (bias || p->in_dtype != ATTN_BF16 || !attn::mfma_bwd_supported(kp) || !aligned16(q) ||
+                    !aligned16(k) || !aligned16(v) || !aligned16(dout)))
+    return ATTN_EUNSUPPORTED;
   if (no_rows && no_keys) return ATTN_OK;
   if (dbias && !no_rows && p->Sk > 0) {
     if (attn::launch_zero_bias(dbias, p->Hq, p->Sq, p->Sk, p->bias_str, s) != hipSuccess) return ATTN_EHIP;

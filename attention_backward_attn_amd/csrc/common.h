@@ -81,7 +81,52 @@ struct Params {
   Mask mask;
   int64_t q_str[3], k_str[3], v_str[3], o_str[3], do_str[3], dq_str[3], dk_str[3], dv_str[3];
   int64_t bias_str[2];
+  // variable-length packed batch (null: dense): prefix sums of the rows of
+  // each sequence along the s index, and the packed row counts
+  const int* cu_q;
+  const int* cu_k;
+  int64_t tot_q, tot_k;
 };
+
+// Sequence b of the batch: where its query rows and keys start along the s
+// index (dense batch: 0, with the b strides locating it), its lengths, and
+// the mask with its own bottom-right offset.  Packed offsets and lengths are
+// clamped to the packed row counts and to the maxima Sq / Sk, so no access
+// leaves the tensors whatever the prefix sums hold.
+struct SeqView {
+  int64_t q_row0, k_row0;
+  int Sq, Sk;
+  bool packed;
+  Mask mask;
+
+  // element offset of the sequence's (head 0, row 0) in a q-side / k-side tensor
+  __device__ inline int64_t q_off(const int64_t* str, int b) const { return packed ? q_row0 * str[2] : b * str[0]; }
+  __device__ inline int64_t k_off(const int64_t* str, int b) const { return packed ? k_row0 * str[2] : b * str[0]; }
+};
+
+__device__ inline SeqView seq_view(const Params& p, int b) {
+  SeqView s;
+  s.mask = p.mask;
+  s.packed = p.cu_q != nullptr;
+  if (!s.packed) {
+    s.q_row0 = 0;
+    s.k_row0 = 0;
+    s.Sq = p.Sq;
+    s.Sk = p.Sk;
+    return s;
+  }
+  int64_t q0 = p.cu_q[b], q1 = p.cu_q[b + 1], k0 = p.cu_k[b], k1 = p.cu_k[b + 1];
+  q0 = q0 < 0 ? 0 : (q0 > p.tot_q ? p.tot_q : q0);
+  k0 = k0 < 0 ? 0 : (k0 > p.tot_k ? p.tot_k : k0);
+  q1 = q1 < q0 ? q0 : (q1 > p.tot_q ? p.tot_q : q1);
+  k1 = k1 < k0 ? k0 : (k1 > p.tot_k ? p.tot_k : k1);
+  s.q_row0 = q0;
+  s.k_row0 = k0;
+  s.Sq = (int)(q1 - q0 < p.Sq ? q1 - q0 : p.Sq);
+  s.Sk = (int)(k1 - k0 < p.Sk ? k1 - k0 : p.Sk);
+  if (s.mask.kind == kMaskBottomRight) s.mask.diag = s.Sk - s.Sq;
+  return s;
+}
 
 __device__ inline float bf16_to_f32(unsigned short u) {
   return __uint_as_float(((unsigned int)u) << 16);

@@ -41,12 +41,20 @@ struct ZeroRows {
   int64_t str[3];
 };
 
-// delta = rowsum(dO * O); when dq_zero is non-null its rows are zeroed in the same pass.
+// Query rows of a variable-length packed batch (cu == nullptr: dense):
+// prefix sums of the sequences' rows along the s index and their count.
+struct Packed {
+  const int* cu;
+  int64_t tot;
+};
+
+// delta = rowsum(dO * O); when dq_zero is non-null its rows are zeroed in the
+// same pass.  Packed batch: delta rows past a sequence's length are 0.
 hipError_t launch_delta(const void* o, int o_bf16, const void* dout, int do_bf16, float* delta, int B,
                         int H, int Sq, int Dv, const int64_t* os, const int64_t* ds, float* dq_zero,
-                        int Dqk, const int64_t* dqs, hipStream_t st);
+                        int Dqk, const int64_t* dqs, Packed pk, hipStream_t st);
 hipError_t launch_dsinks(const float* lse, const float* delta, const float* sinks, float* dsinks,
-                         int B, int H, int Sq, hipStream_t st);
+                         int B, int H, int Sq, Packed pk, hipStream_t st);
 hipError_t launch_zero_rows(float* x, int B, int H, int S, int D, const int64_t* str, hipStream_t st);
 // Zero up to three tensors in one launch (n == 0: nothing is launched).
 hipError_t launch_zero_multi(const ZeroRows* z, int n, hipStream_t st);

@@ -4,6 +4,16 @@
 
 namespace attn {
 
+// Length and first packed row of sequence b (clamped as in seq_view).
+__device__ inline int packed_seq(const Packed& pk, int b, int Smax, int64_t* row0) {
+  int64_t q0 = pk.cu[b], q1 = pk.cu[b + 1];
+  q0 = q0 < 0 ? 0 : (q0 > pk.tot ? pk.tot : q0);
+  q1 = q1 < q0 ? q0 : (q1 > pk.tot ? pk.tot : q1);
+  *row0 = q0;
+  return (int)(q1 - q0 < Smax ? q1 - q0 : Smax);
+}
+
+
 // ---------------------------------------------------------------------------
 // delta[b,h,i] = sum_d dO[b,h,i,d] * O[b,h,i,d]
 // (CK FMHA example 34 cpu_bwd_gqa "D"; CANN sparse_flash_mla_grad Phase 2
@@ -18,29 +28,41 @@ __global__ __launch_bounds__(256) void k_delta_vec(const OT* __restrict__ o,
                                                    int Dv, int64_t ob, int64_t oh, int64_t os,
                                                    int64_t db, int64_t dh, int64_t ds,
                                                    float* __restrict__ dq, int Dqk, int64_t qb,
-                                                   int64_t qh, int64_t qs) {
+                                                   int64_t qh, int64_t qs, Packed pk) {
   const int64_t rows = (int64_t)B * H * Sq;
   const int lane_in_row = threadIdx.x % TPR;
   const int64_t row = ((int64_t)blockIdx.x * 256 + threadIdx.x) / TPR;
   float acc = 0.f;
-  if (row < rows) {
-    const int i = (int)(row % Sq);
-    const int h = (int)((row / Sq) % H);
-    const int b = (int)(row / ((int64_t)Sq * H));
-    const OT* orow = o + b * ob + h * oh + i * os;
-    const DT* drow = dout + b * db + h * dh + i * ds;
+  bool live = row < rows;
+  const int i = live ? (int)(row % Sq) : 0;
+  const int h = live ? (int)((row / Sq) % H) : 0;
+  const int b = live ? (int)(row / ((int64_t)Sq * H)) : 0;
+  // dense: (b, i) through the b stride; packed: packed row r0 + i of sequence b
+  int64_t ro = 0, rd = 0, rq = 0;
+  if (live) {
+    if (pk.cu) {
+      int64_t r0;
+      live = i < packed_seq(pk, b, Sq, &r0);
+      ro = (r0 + i) * os; rd = (r0 + i) * ds; rq = (r0 + i) * qs;
+    } else {
+      ro = b * ob + i * os; rd = b * db + i * ds; rq = b * qb + i * qs;
+    }
+  }
+  if (live) {
+    const OT* orow = o + ro + h * oh;
+    const DT* drow = dout + rd + h * dh;
     for (int d0 = lane_in_row * 8; d0 < Dv; d0 += TPR * 8) {
 #pragma unroll
       for (int e = 0; e < 8; ++e) acc += load_elem(orow, d0 + e) * load_elem(drow, d0 + e);
     }
     if (dq) {
-      float* qrow = dq + b * qb + h * qh + i * qs;
+      float* qrow = dq + rq + h * qh;
       for (int d = lane_in_row; d < Dqk; d += TPR) qrow[d] = 0.f;
     }
   }
 #pragma unroll
   for (int off = TPR / 2; off > 0; off >>= 1) acc += __shfl_xor(acc, off, TPR);
-  if (row < rows && lane_in_row == 0) delta[row] = acc;
+  if (row < rows && lane_in_row == 0) delta[row] = acc;   // 0 past a packed sequence's length
 }
 
 // Scalar fallback for Dv not a multiple of 8: one thread per row.
@@ -51,18 +73,26 @@ __global__ __launch_bounds__(256) void k_delta_scalar(const OT* __restrict__ o,
                                                       int Sq, int Dv, int64_t ob, int64_t oh,
                                                       int64_t os, int64_t db, int64_t dh,
                                                       int64_t ds, float* __restrict__ dq, int Dqk,
-                                                      int64_t qb, int64_t qh, int64_t qs) {
+                                                      int64_t qb, int64_t qh, int64_t qs, Packed pk) {
   const int64_t row = (int64_t)blockIdx.x * 256 + threadIdx.x;
   if (row >= (int64_t)B * H * Sq) return;
   const int i = (int)(row % Sq);
   const int h = (int)((row / Sq) % H);
   const int b = (int)(row / ((int64_t)Sq * H));
+  int64_t ro = b * ob + i * os, rd = b * db + i * ds, rq = b * qb + i * qs;
+  if (pk.cu) {
+    int64_t r0;
+    if (i >= packed_seq(pk, b, Sq, &r0)) {
+      delta[row] = 0.f;
+      return;
+    }
+    ro = (r0 + i) * os; rd = (r0 + i) * ds; rq = (r0 + i) * qs;
+  }
   float acc = 0.f;
-  for (int d = 0; d < Dv; ++d)
-    acc += load_elem(o + b * ob + h * oh + i * os, d) * load_elem(dout + b * db + h * dh + i * ds, d);
+  for (int d = 0; d < Dv; ++d) acc += load_elem(o + ro + h * oh, d) * load_elem(dout + rd + h * dh, d);
   delta[row] = acc;
   if (dq)
-    for (int d = 0; d < Dqk; ++d) dq[b * qb + h * qh + i * qs + d] = 0.f;
+    for (int d = 0; d < Dqk; ++d) dq[rq + h * qh + d] = 0.f;
 }
 
 // dsinks[h] = -sum_{b,i} exp(sink_h - lse[b,h,i]) * delta[b,h,i]
@@ -72,7 +102,8 @@ __global__ __launch_bounds__(256) void k_delta_scalar(const OT* __restrict__ o,
 __global__ __launch_bounds__(256) void k_dsinks(const float* __restrict__ lse,
                                                 const float* __restrict__ delta,
                                                 const float* __restrict__ sinks,
-                                                float* __restrict__ dsinks, int B, int H, int Sq) {
+                                                float* __restrict__ dsinks, int B, int H, int Sq,
+                                                Packed pk) {
   __shared__ float red[256];
   const int h = blockIdx.x;
   const float s = sinks[h];
@@ -80,7 +111,9 @@ __global__ __launch_bounds__(256) void k_dsinks(const float* __restrict__ lse,
   for (int b = 0; b < B; ++b) {
     const float* l = lse + ((int64_t)b * H + h) * Sq;
     const float* d = delta + ((int64_t)b * H + h) * Sq;
-    for (int i = threadIdx.x; i < Sq; i += 256) {
+    int64_t r0;
+    const int n = pk.cu ? packed_seq(pk, b, Sq, &r0) : Sq;   // rows of this sequence
+    for (int i = threadIdx.x; i < n; i += 256) {
       const float li = l[i];
       if (li != -INFINITY) acc += expf(s - li) * d[i];
     }
@@ -212,7 +245,7 @@ __global__ __launch_bounds__(128) void k_lse_merge(float* __restrict__ o_acc,
 template <typename OT, typename DT>
 static hipError_t launch_delta_t(const void* o, const void* dout, float* delta, int B, int H, int Sq,
                                  int Dv, const int64_t* os, const int64_t* ds, float* dq, int Dqk,
-                                 const int64_t* qs, hipStream_t st) {
+                                 const int64_t* qs, Packed pk, hipStream_t st) {
   const int64_t rows = (int64_t)B * H * Sq;
   if (Dv % 8 == 0) {
     const int tpr = Dv >= 128 ? 16 : (Dv >= 64 ? 8 : (Dv >= 32 ? 4 : (Dv >= 16 ? 2 : 1)));
@@ -220,7 +253,7 @@ static hipError_t launch_delta_t(const void* o, const void* dout, float* delta, 
 #define ATTN_DELTA_LAUNCH(T)                                                                     \
   hipLaunchKernelGGL((k_delta_vec<OT, DT, T>), dim3((unsigned)blocks), dim3(256), 0, st,           \
                      (const OT*)o, (const DT*)dout, delta, B, H, Sq, Dv, os[0], os[1], os[2],      \
-                     ds[0], ds[1], ds[2], dq, Dqk, qs[0], qs[1], qs[2])
+                     ds[0], ds[1], ds[2], dq, Dqk, qs[0], qs[1], qs[2], pk)
     switch (tpr) {
       case 16: ATTN_DELTA_LAUNCH(16); break;
       case 8: ATTN_DELTA_LAUNCH(8); break;
@@ -232,27 +265,27 @@ static hipError_t launch_delta_t(const void* o, const void* dout, float* delta, 
   } else {
     hipLaunchKernelGGL((k_delta_scalar<OT, DT>), dim3((unsigned)((rows + 255) / 256)), dim3(256), 0,
                        st, (const OT*)o, (const DT*)dout, delta, B, H, Sq, Dv, os[0], os[1], os[2],
-                       ds[0], ds[1], ds[2], dq, Dqk, qs[0], qs[1], qs[2]);
+                       ds[0], ds[1], ds[2], dq, Dqk, qs[0], qs[1], qs[2], pk);
   }
   return hipGetLastError();
 }
 
 hipError_t launch_delta(const void* o, int o_bf16, const void* dout, int do_bf16, float* delta, int B,
                         int H, int Sq, int Dv, const int64_t* os, const int64_t* ds, float* dq_zero,
-                        int Dqk, const int64_t* qs, hipStream_t st) {
+                        int Dqk, const int64_t* qs, Packed pk, hipStream_t st) {
   if (o_bf16 && do_bf16)
     return launch_delta_t<unsigned short, unsigned short>(o, dout, delta, B, H, Sq, Dv, os, ds, dq_zero,
-                                                          Dqk, qs, st);
+                                                          Dqk, qs, pk, st);
   if (o_bf16)
-    return launch_delta_t<unsigned short, float>(o, dout, delta, B, H, Sq, Dv, os, ds, dq_zero, Dqk, qs, st);
+    return launch_delta_t<unsigned short, float>(o, dout, delta, B, H, Sq, Dv, os, ds, dq_zero, Dqk, qs, pk, st);
   if (do_bf16)
-    return launch_delta_t<float, unsigned short>(o, dout, delta, B, H, Sq, Dv, os, ds, dq_zero, Dqk, qs, st);
-  return launch_delta_t<float, float>(o, dout, delta, B, H, Sq, Dv, os, ds, dq_zero, Dqk, qs, st);
+    return launch_delta_t<float, unsigned short>(o, dout, delta, B, H, Sq, Dv, os, ds, dq_zero, Dqk, qs, pk, st);
+  return launch_delta_t<float, float>(o, dout, delta, B, H, Sq, Dv, os, ds, dq_zero, Dqk, qs, pk, st);
 }
 
 hipError_t launch_dsinks(const float* lse, const float* delta, const float* sinks, float* dsinks,
-                         int B, int H, int Sq, hipStream_t st) {
-  hipLaunchKernelGGL(k_dsinks, dim3(H), dim3(256), 0, st, lse, delta, sinks, dsinks, B, H, Sq);
+                         int B, int H, int Sq, Packed pk, hipStream_t st) {
+  hipLaunchKernelGGL(k_dsinks, dim3(H), dim3(256), 0, st, lse, delta, sinks, dsinks, B, H, Sq, pk);
   return hipGetLastError();
 }
 

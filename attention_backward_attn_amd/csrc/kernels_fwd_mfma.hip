@@ -117,15 +117,18 @@ __global__ __launch_bounds__(NTF, 2) void k_fwd(Params p, FwdArgs a) {
   const bool heavy_last = p.mask.kind != kMaskNone && p.mask.wl < 0;
   const int i0 = (heavy_last ? (int)gridDim.x - 1 - blk.x : blk.x) * BQF;
   const int h = blk.y, b = blk.z, g = h / p.G;
-  const int Sq = p.Sq, Sk = p.Sk;
+  const SeqView sv = seq_view(p, b);   // this batch entry (or packed sequence)
+  const Mask& msk = sv.mask;
+  const int Sq = sv.Sq, Sk = sv.Sk;
+  if (i0 >= Sq) return;   // past this sequence's rows (uniform across the workgroup)
   const int irow = i0 + 32 * w + lr;   // this lane's query row
   const float scale_log2 = p.scale * kLog2e;
   const int rowA = lr * R + 8 * lg;
   const int trV = tr_base(l, T);
 
-  const unsigned short* q = (const unsigned short*)a.q + b * p.q_str[0] + h * p.q_str[1];
-  const unsigned short* kp = (const unsigned short*)a.k + b * p.k_str[0] + g * p.k_str[1];
-  const unsigned short* vp = (const unsigned short*)a.v + b * p.v_str[0] + g * p.v_str[1];
+  const unsigned short* q = (const unsigned short*)a.q + sv.q_off(p.q_str, b) + h * p.q_str[1];
+  const unsigned short* kp = (const unsigned short*)a.k + sv.k_off(p.k_str, b) + g * p.k_str[1];
+  const unsigned short* vp = (const unsigned short*)a.v + sv.k_off(p.v_str, b) + g * p.v_str[1];
 
   bf16x8 qB[NS];
   {
@@ -145,7 +148,7 @@ __global__ __launch_bounds__(NTF, 2) void k_fwd(Params p, FwdArgs a) {
   // key tiles: the sink tiles, then the band tiles of the block's rows
   int64_t s_hi, b_lo, b_hi;
   const int i1 = min(i0 + BQF, Sq);
-  p.mask.keys_for_rows(i0, i1, Sk, &s_hi, &b_lo, &b_hi);
+  msk.keys_for_rows(i0, i1, Sk, &s_hi, &b_lo, &b_hi);
   const int a1 = (int)((s_hi + KT - 1) / KT);
   int a2 = (int)(b_lo / KT);
   const int a3 = b_hi > b_lo ? (int)((b_hi + KT - 1) / KT) : a2;
@@ -153,9 +156,9 @@ __global__ __launch_bounds__(NTF, 2) void k_fwd(Params p, FwdArgs a) {
   const int n1 = a1, n2 = a3 > a2 ? a3 - a2 : 0;
   const int n_it = (i0 < Sq && Sk > 0) ? n1 + n2 : 0;
   auto tile_of = [&](int it) { return (int64_t)KT * (it < n1 ? it : a2 + (it - n1)); };
-  const bool no_mask = p.mask.kind == kMaskNone;
-  const int lo_t = p.mask.wl < 0 ? -0x3fffffff : -p.mask.wl;
-  const int wr_t = p.mask.wr;
+  const bool no_mask = msk.kind == kMaskNone;
+  const int lo_t = msk.wl < 0 ? -0x3fffffff : -msk.wl;
+  const int wr_t = msk.wr;
 
   f32x16 o[NB];
 #pragma unroll
@@ -181,9 +184,9 @@ __global__ __launch_bounds__(NTF, 2) void k_fwd(Params p, FwdArgs a) {
       for (int s = 0; s < NS; ++s)
         sacc[hh] = mfma(lds_b128(sm.kr[cur], rowA + 32 * hh * R + 16 * s), qB[s], sacc[hh]);
     }
-    const bool full = (j0 + KT <= Sk) && p.mask.tile_full(i0 + 32 * w, i0 + 32 * w + 32, j0, j0 + KT);
+    const bool full = (j0 + KT <= Sk) && msk.tile_full(i0 + 32 * w, i0 + 32 * w + 32, j0, j0 + KT);
     // t = j' - i' - diag for key j0 + 4 lg + c
-    const int tb = j0 + (int)p.mask.k_off + 4 * lg - (irow + (int)p.mask.q_off) - (int)p.mask.diag;
+    const int tb = j0 + (int)msk.k_off + 4 * lg - (irow + (int)msk.q_off) - (int)msk.diag;
     float mt = -INFINITY;
     auto elem = [&](int hh, int r, bool masked) {
       const int c = 32 * hh + 8 * (r >> 2) + (r & 3);
@@ -192,7 +195,7 @@ __global__ __launch_bounds__(NTF, 2) void k_fwd(Params p, FwdArgs a) {
       if (masked) {
         const int j = j0 + 4 * lg + c;
         const int t = tb + c;
-        const bool ok = (j < Sk) & (no_mask | ((t <= wr_t) & (t >= lo_t)) | ((j + (int)p.mask.k_off) < p.mask.n_sink));
+        const bool ok = (j < Sk) & (no_mask | ((t <= wr_t) & (t >= lo_t)) | ((j + (int)msk.k_off) < msk.n_sink));
         x = ok ? x : -INFINITY;
       }
       sacc[hh][r] = x;
@@ -244,7 +247,7 @@ __global__ __launch_bounds__(NTF, 2) void k_fwd(Params p, FwdArgs a) {
   if (irow < Sq) {
     const bool live = ltot > 0.f;
     const float inv = live ? 1.f / ltot : 0.f;
-    OT* op = (OT*)a.o + b * p.o_str[0] + h * p.o_str[1] + (int64_t)irow * p.o_str[2];
+    OT* op = (OT*)a.o + sv.q_off(p.o_str, b) + h * p.o_str[1] + (int64_t)irow * p.o_str[2];
 #pragma unroll
     for (int n = 0; n < NB; ++n) {
 #pragma unroll
@@ -256,7 +259,7 @@ __global__ __launch_bounds__(NTF, 2) void k_fwd(Params p, FwdArgs a) {
       }
     }
     if (lg == 0)
-      a.lse[((int64_t)b * p.Hq + h) * Sq + irow] =
+      a.lse[((int64_t)b * p.Hq + h) * p.Sq + irow] =
           live ? (m + log2f(ltot)) * 0.6931471805599453f : -INFINITY;
   }
 }

@@ -492,9 +492,12 @@ __global__ __launch_bounds__(NT2) void k_dkdv2(Params p, BwdArgs a, DkdvGrid gd)
   const int pr = w & 3;               // pair: keys [32 pr, 32 pr + 32) of the block
   const bool sw = w < 4;              // S wave (else dP wave)
   const int cb = sw ? 0 : D / 2;      // first dK / dV column of this wave
-  const int Sq = p.Sq, Sk = p.Sk;
-  const int nkb = (Sk + BK - 1) / BK;
   const BlockXYZ blk = xcd_block();
+  const int b = blk.z;
+  const SeqView sv = seq_view(p, b);   // this batch entry (or packed sequence)
+  const Mask& msk = sv.mask;
+  const int Sq = sv.Sq, Sk = sv.Sk;
+  const int nkb = (Sk + BK - 1) / BK;
   const int hk = blk.y / gd.nsplit;
   int part = blk.y % gd.nsplit, nparts = gd.nsplit;
   int kbx = blk.x;
@@ -509,14 +512,15 @@ __global__ __launch_bounds__(NT2) void k_dkdv2(Params p, BwdArgs a, DkdvGrid gd)
   }
   const int h_begin = hk * p.G;
   const float scale = p.scale, scale_log2 = p.scale * kLog2e;
-  const int n_units = (gd.pair && nkb - 1 - kbx != kbx) ? 2 : 1;
+  // key blocks of this sequence (a packed batch's grid covers the longest)
+  const bool unit_in = gd.pair ? 2 * kbx < nkb : kbx < nkb;
+  const int n_units = !unit_in ? 0 : ((gd.pair && nkb - 1 - kbx != kbx) ? 2 : 1);
   const int out_mode = gd.out_mode;
-  const bool no_mask = p.mask.kind == kMaskNone;
-  const int lo_t = p.mask.wl < 0 ? -0x3fffffff : -p.mask.wl;
-  const int wr_t = p.mask.wr;
+  const bool no_mask = msk.kind == kMaskNone;
+  const int lo_t = msk.wl < 0 ? -0x3fffffff : -msk.wl;
+  const int wr_t = msk.wr;
   const int rowA = lr * R + 8 * lg;
   const int trQ = tr_base(l, T);
-  const int b = blk.z;
 
   for (int u = 0; u < n_units; ++u) {
     const int kb = u == 0 ? kbx : nkb - 1 - kbx;
@@ -525,10 +529,10 @@ __global__ __launch_bounds__(NT2) void k_dkdv2(Params p, BwdArgs a, DkdvGrid gd)
     const int jkey = kw + lr;
     const bool wave_keys_in = kw + 32 <= Sk;
     const bool key_ok = jkey < Sk;
-    const int jg = jkey + (int)p.mask.k_off;
-    const bool sink_key = jg < p.mask.n_sink;
+    const int jg = jkey + (int)msk.k_off;
+    const bool sink_key = jg < msk.n_sink;
     int64_t lo64, hi64;
-    p.mask.rows_for_keys(k0, min(k0 + BK, Sk), Sq, &lo64, &hi64);
+    msk.rows_for_keys(k0, min(k0 + BK, Sk), Sq, &lo64, &hi64);
     const int lo = (int)lo64, hi = (int)hi64;
     const int lo_al = lo & ~(BQ - 1);
     const int nqb = hi > lo ? (hi - lo_al + BQ - 1) / BQ : 0;
@@ -539,8 +543,8 @@ __global__ __launch_bounds__(NT2) void k_dkdv2(Params p, BwdArgs a, DkdvGrid gd)
     // K (S wave) or V (dP wave) fragments of this pair's keys: B operands
     bf16x8 fB[NS];
     {
-      const unsigned short* src = sw ? (const unsigned short*)a.k + b * p.k_str[0] + hk * p.k_str[1]
-                                     : (const unsigned short*)a.v + b * p.v_str[0] + hk * p.v_str[1];
+      const unsigned short* src = sw ? (const unsigned short*)a.k + sv.k_off(p.k_str, b) + hk * p.k_str[1]
+                                     : (const unsigned short*)a.v + sv.k_off(p.v_str, b) + hk * p.v_str[1];
       const int64_t rs = sw ? p.k_str[2] : p.v_str[2];
       const int64_t jc = min(jkey, Sk - 1);
 #pragma unroll
@@ -556,9 +560,9 @@ __global__ __launch_bounds__(NT2) void k_dkdv2(Params p, BwdArgs a, DkdvGrid gd)
     const int q_rb = 2 * (int)p.q_str[2], d_rb = 2 * (int)p.do_str[2];
     stg.init(w, q_rb, d_rb);
     auto issue = [&](int h, int i0) {
-      const int64_t rb = ((int64_t)b * p.Hq + h) * Sq + i0;
-      stg.load((const unsigned short*)a.q + b * p.q_str[0] + h * p.q_str[1] + (int64_t)i0 * p.q_str[2],
-               (const unsigned short*)a.dout + b * p.do_str[0] + h * p.do_str[1] + (int64_t)i0 * p.do_str[2],
+      const int64_t rb = ((int64_t)b * p.Hq + h) * p.Sq + i0;
+      stg.load((const unsigned short*)a.q + sv.q_off(p.q_str, b) + h * p.q_str[1] + (int64_t)i0 * p.q_str[2],
+               (const unsigned short*)a.dout + sv.q_off(p.do_str, b) + h * p.do_str[1] + (int64_t)i0 * p.do_str[2],
                q_rb, d_rb, a.lse + rb, a.delta + rb, min(Sq - i0, BQ));
     };
     int h = h_begin + (nqb > 0 ? it_lo / nqb : 0), qb = nqb > 0 ? it_lo % nqb : 0;
@@ -597,14 +601,14 @@ __global__ __launch_bounds__(NT2) void k_dkdv2(Params p, BwdArgs a, DkdvGrid gd)
         f32x4 L4[4];
 #pragma unroll
         for (int m = 0; m < 4; ++m) L4[m] = *(const f32x4*)&sm.lse2[cur][8 * m + 4 * lg];
-        const bool full = wave_keys_in && p.mask.tile_full(i0, i0 + BQ, kw, kw + 32);
+        const bool full = wave_keys_in && msk.tile_full(i0, i0 + BQ, kw, kw + 32);
         float pv[16];
         if (full) {
 #pragma unroll
           for (int r = 0; r < 16; ++r)
             pv[r] = __builtin_amdgcn_exp2f(fmaf(acc[r], scale_log2, -L4[r >> 2][r & 3]));
         } else {
-          const int tb = jg - (i0 + (int)p.mask.q_off) - (int)p.mask.diag - 4 * lg;
+          const int tb = jg - (i0 + (int)msk.q_off) - (int)msk.diag - 4 * lg;
 #pragma unroll
           for (int r = 0; r < 16; ++r) {
             const int c = 8 * (r >> 2) + (r & 3);
@@ -666,8 +670,8 @@ __global__ __launch_bounds__(NT2) void k_dkdv2(Params p, BwdArgs a, DkdvGrid gd)
     }
 
     // Epilogue: this wave's dK (scaled through dS) and dV columns.
-    float* dkp = a.dk + b * p.dk_str[0] + hk * p.dk_str[1];
-    float* dvp = a.dv + b * p.dv_str[0] + hk * p.dv_str[1];
+    float* dkp = a.dk + sv.k_off(p.dk_str, b) + hk * p.dk_str[1];
+    float* dvp = a.dv + sv.k_off(p.dv_str, b) + hk * p.dv_str[1];
 #pragma unroll
     for (int n = 0; n < NH; ++n) {
 #pragma unroll
@@ -864,16 +868,19 @@ __global__ __launch_bounds__(NT, 2) void k_dq(Params p, BwdArgs a) {
   const bool heavy_last = p.mask.kind != kMaskNone && p.mask.wl < 0;
   const int i0 = (heavy_last ? (int)gridDim.x - 1 - blk.x : blk.x) * BQ3;
   const int h = blk.y, b = blk.z, g = h / p.G;
-  const int Sq = p.Sq, Sk = p.Sk;
+  const SeqView sv = seq_view(p, b);   // this batch entry (or packed sequence)
+  const Mask& msk = sv.mask;
+  const int Sq = sv.Sq, Sk = sv.Sk;
+  if (i0 >= Sq) return;   // past this sequence's rows (uniform across the workgroup)
   const int irow = i0 + 32 * w + lr;           // this lane's query row
   const float scale = p.scale, scale_log2 = p.scale * kLog2e;
   const int rowA = lr * R + 8 * lg;
   const int trK = tr_base(l, T);
 
-  const unsigned short* q = (const unsigned short*)a.q + b * p.q_str[0] + h * p.q_str[1];
-  const unsigned short* dout = (const unsigned short*)a.dout + b * p.do_str[0] + h * p.do_str[1];
-  const unsigned short* kp = (const unsigned short*)a.k + b * p.k_str[0] + g * p.k_str[1];
-  const unsigned short* vp = (const unsigned short*)a.v + b * p.v_str[0] + g * p.v_str[1];
+  const unsigned short* q = (const unsigned short*)a.q + sv.q_off(p.q_str, b) + h * p.q_str[1];
+  const unsigned short* dout = (const unsigned short*)a.dout + sv.q_off(p.do_str, b) + h * p.do_str[1];
+  const unsigned short* kp = (const unsigned short*)a.k + sv.k_off(p.k_str, b) + g * p.k_str[1];
+  const unsigned short* vp = (const unsigned short*)a.v + sv.k_off(p.v_str, b) + g * p.v_str[1];
 
   bf16x8 qB[NS], doB[NS];
   {
@@ -886,16 +893,16 @@ __global__ __launch_bounds__(NT, 2) void k_dq(Params p, BwdArgs a) {
   }
   float lse2 = INFINITY, dls = 0.f;
   if (irow < Sq) {
-    const float lv = a.lse[((int64_t)b * p.Hq + h) * Sq + irow];
+    const float lv = a.lse[((int64_t)b * p.Hq + h) * p.Sq + irow];
     lse2 = (lv == -INFINITY) ? INFINITY : lv * kLog2e;
-    dls = a.delta[((int64_t)b * p.Hq + h) * Sq + irow] * scale;
+    dls = a.delta[((int64_t)b * p.Hq + h) * p.Sq + irow] * scale;
   }
   wait_vm_loads();
 
   // key tiles: the sink tiles [0, a1) and the band tiles [a2, a3)
   int64_t s_hi, b_lo, b_hi;
   const int i1 = min(i0 + BQ3, Sq);
-  p.mask.keys_for_rows(i0, i1, Sk, &s_hi, &b_lo, &b_hi);
+  msk.keys_for_rows(i0, i1, Sk, &s_hi, &b_lo, &b_hi);
   const int a1 = (int)((s_hi + BK3 - 1) / BK3);
   int a2 = (int)(b_lo / BK3);
   const int a3 = b_hi > b_lo ? (int)((b_hi + BK3 - 1) / BK3) : a2;
@@ -903,9 +910,9 @@ __global__ __launch_bounds__(NT, 2) void k_dq(Params p, BwdArgs a) {
   const int n1 = a1, n2 = a3 > a2 ? a3 - a2 : 0;
   const int n_it = i0 < Sq ? n1 + n2 : 0;
   auto tile_of = [&](int it) { return (int64_t)BK3 * (it < n1 ? it : a2 + (it - n1)); };
-  const bool no_mask = p.mask.kind == kMaskNone;
-  const int lo_t = p.mask.wl < 0 ? -0x3fffffff : -p.mask.wl;
-  const int wr_t = p.mask.wr;
+  const bool no_mask = msk.kind == kMaskNone;
+  const int lo_t = msk.wl < 0 ? -0x3fffffff : -msk.wl;
+  const int wr_t = msk.wr;
 
   f32x16 dq[NB];
 #pragma unroll
@@ -939,9 +946,9 @@ __global__ __launch_bounds__(NT, 2) void k_dq(Params p, BwdArgs a) {
       sacc = mfma(lds_b128(sm.kr[cur], rowA + 16 * s), qB[s], sacc);
       dpacc = mfma(lds_b128(sm.vr[cur], rowA + 16 * s), doB[s], dpacc);
     }
-    const bool full = (j0 + BK3 <= Sk) && p.mask.tile_full(i0 + 32 * w, i0 + 32 * w + 32, j0, j0 + BK3);
+    const bool full = (j0 + BK3 <= Sk) && msk.tile_full(i0 + 32 * w, i0 + 32 * w + 32, j0, j0 + BK3);
     // t = j' - i' - diag for key j0 + 4 lg + c
-    const int tb = j0 + (int)p.mask.k_off + 4 * lg - (irow + (int)p.mask.q_off) - (int)p.mask.diag;
+    const int tb = j0 + (int)msk.k_off + 4 * lg - (irow + (int)msk.q_off) - (int)msk.diag;
     float dsv[16];
     auto elem = [&](int r, bool masked) {
       const int c = 8 * (r >> 2) + (r & 3);
@@ -951,7 +958,7 @@ __global__ __launch_bounds__(NT, 2) void k_dq(Params p, BwdArgs a) {
       if (masked) {
         const int j = j0 + 4 * lg + c;
         const int t = tb + c;
-        const bool ok = (j < Sk) & (no_mask | ((t <= wr_t) & (t >= lo_t)) | ((j + (int)p.mask.k_off) < p.mask.n_sink));
+        const bool ok = (j < Sk) & (no_mask | ((t <= wr_t) & (t >= lo_t)) | ((j + (int)msk.k_off) < msk.n_sink));
         pp = ok ? pp : 0.f;
       }
       dsv[r] = pp * fmaf(dpacc[r], scale, -dls);
@@ -974,7 +981,7 @@ __global__ __launch_bounds__(NT, 2) void k_dq(Params p, BwdArgs a) {
   }
 
   // dQ rows i0 + 32 w + crow(r, lg), columns 32 n + lr (already scaled through dS).
-  float* dqp = a.dq + b * p.dq_str[0] + h * p.dq_str[1];
+  float* dqp = a.dq + sv.q_off(p.dq_str, b) + h * p.dq_str[1];
 #pragma unroll
   for (int n = 0; n < NB; ++n) {
 #pragma unroll
@@ -1026,8 +1033,11 @@ hipError_t launch_bwd_mfma(const Params& p, const BwdArgs& a, hipStream_t st) {
   const DkdvPlan pl = plan_dkdv(p, bloop, a.accumulate_dkdv != 0, a.deterministic != 0);
   // split parts add into zeroed dK / dV
   if (pl.g.out_mode == kAtomicAdd && !a.accumulate_dkdv && p.Sk > 0) {
-    ZeroRows z[2] = {ZeroRows{a.dk, p.B, p.Hk, p.Sk, p.Dqk, {p.dk_str[0], p.dk_str[1], p.dk_str[2]}},
-                     ZeroRows{a.dv, p.B, p.Hk, p.Sk, p.Dv, {p.dv_str[0], p.dv_str[1], p.dv_str[2]}}};
+    // dense [B, Hk, Sk] or the packed rows of a variable-length batch
+    const bool pk = p.cu_k != nullptr;
+    const int zb = pk ? 1 : p.B, zs = pk ? (int)p.tot_k : p.Sk;
+    ZeroRows z[2] = {ZeroRows{a.dk, zb, p.Hk, zs, p.Dqk, {pk ? 0 : p.dk_str[0], p.dk_str[1], p.dk_str[2]}},
+                     ZeroRows{a.dv, zb, p.Hk, zs, p.Dv, {pk ? 0 : p.dv_str[0], p.dv_str[1], p.dv_str[2]}}};
     hipError_t e = launch_zero_multi(z, 2, st);
     if (e != hipSuccess) return e;
   }

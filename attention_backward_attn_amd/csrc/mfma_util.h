@@ -96,21 +96,22 @@ __device__ inline bf16x8 lds_trB(const unsigned short* tile, int base, int r0, i
 
 // The hardware deals a launch's workgroups to the eight XCDs round-robin by
 // linear workgroup id.  Renumbering them so that each XCD receives one
-// contiguous range of logical ids (x fastest, then y, then z) keeps the
-// workgroups that share a KV head -- and so its K / V or Q / dO rows -- on
-// one XCD and in its L2.
+// contiguous range of logical ids (x fastest, then z, then y) keeps the
+// workgroups of one head -- which share its K / V or Q / dO rows -- on one
+// XCD and in its L2, while every XCD gets a share of every batch entry (or
+// packed sequence, whose sizes may differ) so the XCDs stay balanced.
 struct BlockXYZ {
   int x, y, z;
 };
 
 __device__ inline BlockXYZ xcd_block() {
-  const int nx = gridDim.x, ny = gridDim.y;
-  const int n = nx * ny * gridDim.z;
+  const int nx = gridDim.x, ny = gridDim.y, nz = gridDim.z;
+  const int n = nx * ny * nz;
   const int id = blockIdx.x + nx * (blockIdx.y + ny * blockIdx.z);
   const int q = n >> 3, r = n & 7, k = id & 7;
   const int L = k * q + min(k, r) + (id >> 3);
-  const int yz = L / nx;
-  return {L - yz * nx, yz % ny, yz / ny};
+  const int zy = L / nx;
+  return {L - zy * nx, zy / nz, zy % nz};
 }
 
 // Raw buffer resource over [base, base + bytes): a load at an offset past the

@@ -121,3 +121,49 @@ def make_inputs(w: Workload, seed: Optional[int] = None) -> dict:
     if w.bias == "alibi":
         out["bias"] = alibi_bias(w.Hq, w.Sq, w.Sk)
     return out
+
+
+@dataclass(frozen=True)
+class VarlenWorkload:
+    """A packed batch of sequences of different lengths (TND layout with
+    cumulative sequence lengths).  Self-attention: each sequence's keys are
+    its own rows.  Lengths are drawn uniformly from [min_len, max_len] with
+    the seed, then rounded down to multiples of 8."""
+    name: str
+    n_seq: int
+    min_len: int
+    max_len: int
+    Hq: int
+    Hk: int
+    D: int
+    mask: str
+    seed: int
+
+    @property
+    def scale(self) -> float:
+        return 1.0 / float(np.sqrt(self.D))
+
+    def lengths(self) -> np.ndarray:
+        rng = np.random.default_rng(self.seed)
+        return (rng.integers(self.min_len, self.max_len + 1, self.n_seq) // 8 * 8).astype(np.int64)
+
+    def cu_seqlens(self) -> np.ndarray:
+        return np.concatenate([[0], np.cumsum(self.lengths())]).astype(np.int32)
+
+
+VARLEN_WORKLOADS = {
+    "varlen16_gqa4_causal_br": VarlenWorkload("varlen16_gqa4_causal_br", n_seq=16, min_len=256,
+                                              max_len=4096, Hq=32, Hk=8, D=128, mask="bottom_right",
+                                              seed=1006),
+}
+
+
+def make_varlen_inputs(w: VarlenWorkload) -> dict:
+    """Packed q, do [T, Hq, D] and k, v [T, Hk, D] (bf16-rounded float32) and
+    the prefix sums of the sequence lengths."""
+    cu = w.cu_seqlens()
+    T = int(cu[-1])
+    rng = np.random.default_rng(w.seed + 1)
+    draw = lambda *s: round_bf16(rng.standard_normal(s).astype(np.float32))
+    return {"q": draw(T, w.Hq, w.D), "k": draw(T, w.Hk, w.D), "v": draw(T, w.Hk, w.D),
+            "do": draw(T, w.Hq, w.D), "cu_seqlens": cu}

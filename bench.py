@@ -87,6 +87,50 @@ def traffic_record(kernel_key: str):
     return None
 
 
+def bench_varlen(stream, name: str = "varlen16_gqa4_causal_br", steps: int = 10):
+    """Backward of a packed variable-length batch (TND with cumulative
+    sequence lengths): preprocess + attn_bwd per step, counted FLOPs summed
+    over the sequences."""
+    import numpy as np
+    import torch
+
+    from attention_backward_attn_amd import binding as ab
+    from attention_backward_attn_amd.inputs import VARLEN_WORKLOADS, make_varlen_inputs
+    from attention_backward_attn_amd.mask import allowed_pairs
+    w = VARLEN_WORKLOADS[name]
+    x = make_varlen_inputs(w)
+    dev = torch.device("cuda:0")
+    q, k, v, do = (torch.from_numpy(x[n]).to(dev, torch.bfloat16) for n in ("q", "k", "v", "do"))
+    cu = torch.from_numpy(x["cu_seqlens"]).to(dev)
+    lens = np.diff(x["cu_seqlens"])
+    kw = dict(mask=w.mask, cu_seqlens_q=cu, cu_seqlens_k=cu, max_seqlen_q=int(lens.max()),
+              max_seqlen_k=int(lens.max()))
+    o, lse = ab.forward(q, k, v, scale=w.scale, stream=stream, **kw)
+    dq = torch.empty(q.shape, device=dev)
+    dk = torch.empty(k.shape, device=dev)
+    dv = torch.empty(v.shape, device=dev)
+    delta = torch.empty(lse.shape, device=dev)
+    p = ab.make_problem(q, k, v, o=o, do=do, dq=dq, dk=dk, dv=dv, scale=w.scale, **kw)
+
+    def step():
+        ab.attn_bwd_preprocess(p, o, do, lse, None, delta, None, None, None, None, stream)
+        ab.attn_bwd(p, q, k, v, do, lse, delta, None, dq, dk, dv, None, 0, stream)
+    for _ in range(3):
+        step()
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record(stream)
+    for _ in range(steps):
+        step()
+    e1.record(stream)
+    torch.cuda.synchronize()
+    ms = e0.elapsed_time(e1) / steps
+    pairs = sum(allowed_pairs(int(n), int(n), w.mask) for n in lens)
+    flops = 10.0 * w.D * pairs * w.Hq
+    return {"workload": name, "tokens": int(lens.sum()), "n_seq": int(len(lens)), "ms_per_step": round(ms, 4),
+            "tflops": round(flops / (ms * 1e-3) / 1e12, 2)}
+
+
 def cpu_baseline(w, x, groups: int):
     """Time the fp64 oracle backward on KV groups [0, groups) of batch 0."""
     import numpy as np
@@ -267,6 +311,8 @@ def main():
             torch.cuda.synchronize()
             ch_ms = e0.elapsed_time(e1) / 5
             out["chunked_kv4"] = {"ms_per_step": round(ch_ms, 4), "tflops": round(flops / (ch_ms * 1e-3) / 1e12, 2)}
+        if w.name == HEADLINE:
+            out["varlen"] = bench_varlen(stream)
     if not args.no_cpu_baseline:
         out["cpu_baseline"] = cpu_baseline(w, x, args.cpu_groups)
     print(json.dumps(out), flush=True)

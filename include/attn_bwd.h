@@ -79,11 +79,11 @@ typedef enum {
 } attn_mask_t;
 
 /* attn_bwd flags.
- * ATTN_DETERMINISTIC: dQ comes from a separate query-block-parallel pass
- *   that accumulates in registers (no atomics); dbias is accumulated over
- *   the batch in a fixed order.  Two calls give bitwise identical results.
- *   Without it dQ (and dbias) are accumulated with fp32 atomics, whose
- *   order -- and so the low bits -- may vary between calls.
+ * ATTN_DETERMINISTIC: two calls give bitwise identical results.  dQ always
+ *   comes from a query-block-parallel pass that accumulates in registers,
+ *   and dbias is summed over the batch in a fixed order; without the flag a
+ *   block of dK / dV may be split into more than two parts whose fp32 adds
+ *   into the output can come in any order, so the low bits may vary.
  * ATTN_ACCUMULATE_DQ: add into dQ instead of overwriting it (chunked /
  *   ring use, [RING] _ring_bwd accumulates dq over the K/V chunks).
  * ATTN_ACCUMULATE_DKDV: add into dK and dV instead of overwriting them
@@ -110,6 +110,24 @@ typedef struct attn_problem {
   int64_t q_str[3], k_str[3], v_str[3], o_str[3], do_str[3];  /* {b, h, s}      */
   int64_t dq_str[3], dk_str[3], dv_str[3];                    /* {b, h, s}      */
   int64_t bias_str[2];      /* {h, i} of bias and dbias                          */
+  /* Variable-length packed batch ([SFMG] "Prototype": TND layout with
+   * cumulative sequence lengths).  Both null: dense batch.  Otherwise device
+   * arrays of B + 1 non-decreasing int32 prefix sums: sequence b owns the
+   * packed query rows [cu_seqlens_q[b], cu_seqlens_q[b+1]) and keys
+   * [cu_seqlens_k[b], cu_seqlens_k[b+1]) along the s index of every q-side
+   * (Q, O, dO, dQ) and k-side (K, V, dK, dV) tensor, whose b strides are
+   * then unused (e.g. TND: strides {0, D, H * D}).  Sq and Sk are the
+   * longest lengths; total_q and total_k the packed row counts of the
+   * tensors.  Offsets and lengths read from the arrays are clamped to those
+   * counts and maxima, so no access leaves the tensors.  The bottom-right
+   * mask is aligned per sequence.  LSE and delta stay [B, Hq, Sq]: rows past
+   * a sequence's length are not written by the forward, delta is 0 there.
+   * Requires bf16 inputs with Dqk == Dv in {64, 128}, no bias, and zero
+   * q_offset / k_offset / sq_total / sk_total (else ATTN_EUNSUPPORTED or
+   * ATTN_EINVAL).  Zero-filled by attn_problem_init. */
+  const int32_t* cu_seqlens_q;
+  const int32_t* cu_seqlens_k;
+  int64_t total_q, total_k;
 } attn_problem_t;
 
 /* Fill *p with contiguous [B, H, S, D] strides and defaults: scale =

@@ -43,4 +43,6 @@ from .attention import (  # noqa: F401
     dkdv_keys,
     ds_rows,
     allowed_pair_count,
+    forward_varlen,
+    backward_varlen,
 )

@@ -28,6 +28,10 @@ How each function is pinned (tests/test_oracle_*.py):
                     sum_j dV = sum_i dO, sinks shift invariance); GQA ==
                     expanded MHA ([GQA-BWD]); Sk = 1 special case
 ``preprocess``      the same FD pins (it is the D / dsinks part of backward)
+``forward_varlen``  equal-length packed batch == the dense batch; each
+``backward_varlen`` sequence == the dense oracle on that sequence alone
+                    (a sequence's rows never see another's keys); empty
+                    sequences contribute nothing
 ``lse_merge``       merged chunk forwards equal the unchunked forward;
                     identity with an empty partial; commutativity
 ``dq_rows`` /       equality with the corresponding rows / keys of
@@ -328,3 +332,57 @@ def lse_merge(o_a, lse_a, o_b, lse_b):
     wb = np.where(live & np.isfinite(lse_b), np.exp(np.where(np.isfinite(lse_b), lse_b, 0.0) - safe), 0.0)
     o = o_a * wa[..., None] + o_b * wb[..., None]
     return o, lse
+
+
+def _unpack(x, c0, c1):
+    """Rows [c0, c1) of a packed [T, H, D] tensor as a [1, H, c1 - c0, D] batch."""
+    return x[c0:c1].transpose(1, 0, 2)[None]
+
+
+def forward_varlen(q, k, v, cu_q, cu_k, max_q: int, scale: float, spec: MaskSpec = MaskSpec(),
+                   sinks=None):
+    """Forward of a variable-length packed batch ([SFMG] "Prototype": TND
+    layout with cumulative sequence lengths).  q: [Tq, Hq, D], k / v:
+    [Tk, Hk, D]; sequence b owns rows cu_q[b]..cu_q[b+1] and keys
+    cu_k[b]..cu_k[b+1], and attends to its own keys only, with masks aligned
+    on its own lengths.  Returns packed O [Tq, Hq, Dv] and LSE [B, Hq, max_q]
+    (rows past a sequence's length stay -inf)."""
+    q, k, v = _f64(q), _f64(k), _f64(v)
+    B = len(cu_q) - 1
+    o = np.zeros((q.shape[0], q.shape[1], v.shape[2]))
+    lse = np.full((B, q.shape[1], max_q), NEG_INF)
+    for b in range(B):
+        q0, q1, k0, k1 = cu_q[b], cu_q[b + 1], cu_k[b], cu_k[b + 1]
+        if q1 == q0:
+            continue
+        ob, lb = forward(_unpack(q, q0, q1), _unpack(k, k0, k1), _unpack(v, k0, k1), scale, spec, None, sinks)
+        o[q0:q1] = ob[0].transpose(1, 0, 2)
+        lse[b, :, :q1 - q0] = lb[0]
+    return o, lse
+
+
+def backward_varlen(q, k, v, o, do, lse, cu_q, cu_k, scale: float, spec: MaskSpec = MaskSpec(),
+                    sinks=None):
+    """Backward of a variable-length packed batch: each sequence is the dense
+    problem on its own rows and keys (see ``forward_varlen``).  Packed dq
+    [Tq, Hq, Dqk], dk / dv [Tk, Hk, D]; delta [B, Hq, max_q] (0 past a
+    sequence's length); dsinks summed over every sequence's rows."""
+    q, k, v, o, do, lse = _f64(q), _f64(k), _f64(v), _f64(o), _f64(do), _f64(lse)
+    B = len(cu_q) - 1
+    dq, dk, dv = np.zeros_like(q), np.zeros(k.shape), np.zeros(v.shape)
+    delta = np.zeros(lse.shape)
+    dsinks = None if sinks is None else np.zeros(q.shape[1])
+    for b in range(B):
+        q0, q1, k0, k1 = cu_q[b], cu_q[b + 1], cu_k[b], cu_k[b + 1]
+        if q1 == q0 and k1 == k0:
+            continue
+        n = q1 - q0
+        g = backward(_unpack(q, q0, q1), _unpack(k, k0, k1), _unpack(v, k0, k1), _unpack(o, q0, q1),
+                     _unpack(do, q0, q1), lse[b:b + 1, :, :n], scale, spec, None, sinks)
+        dq[q0:q1] = g["dq"][0].transpose(1, 0, 2)
+        dk[k0:k1] = g["dk"][0].transpose(1, 0, 2)
+        dv[k0:k1] = g["dv"][0].transpose(1, 0, 2)
+        delta[b, :, :n] = g["delta"][0]
+        if dsinks is not None and n > 0:
+            dsinks += g["dsinks"]
+    return {"dq": dq, "dk": dk, "dv": dv, "dsinks": dsinks, "delta": delta}

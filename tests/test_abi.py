@@ -71,6 +71,9 @@ BAD = [
     dict(num_sink_tokens=2),    # sinks with mask NONE
     dict(mask=1, q_offset=10, sq_total=32),   # offset + Sq beyond the global length
     dict(mask=2, k_offset=-1),
+    dict(cu_seqlens_q=0x1000),                                  # packed batch needs both prefix sums
+    dict(cu_seqlens_q=0x1000, cu_seqlens_k=0x1000, mask=2, sq_total=128),   # no offsets with a packed batch
+    dict(cu_seqlens_q=0x1000, cu_seqlens_k=0x1000, total_q=-1),
 ]
 
 
@@ -87,6 +90,17 @@ def test_fwd_rejects_invalid_problem(kw):
     p = problem(**kw)
     s = B.lib().attn_fwd_lse(ctypes.byref(p), FAKE, FAKE, FAKE, None, None, FAKE, FAKE, None)
     assert s in (B.ATTN_EINVAL, B.ATTN_EUNSUPPORTED)
+
+
+def test_packed_batch_unsupported_cases():
+    # fp32 inputs and a bias are not covered by the packed-batch kernels;
+    # the call fails before any HIP call
+    for kw in (dict(in_dtype=0), dict()):
+        p = problem(cu_seqlens_q=0x1000, cu_seqlens_k=0x1000, total_q=64, total_k=64, **kw)
+        bias = FAKE if not kw else None
+        s = B.lib().attn_bwd(ctypes.byref(p), FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, bias, FAKE, FAKE, FAKE,
+                             None, 0, None)
+        assert s == B.ATTN_EUNSUPPORTED, kw
 
 
 def test_bwd_rejects_null_pointers_and_flags():
