@@ -397,30 +397,33 @@ __global__ __launch_bounds__(NT, 1) void k_dkdv(Params p, BwdArgs a, DkdvGrid gd
 
 // ---------------------------------------------------------------------------
 // Kernel k_dkdv2: dK / dV without dQ (dQ from k_dq), two waves per SIMD.
-// One workgroup of eight waves per unit, as for k_dkdv.  Waves w and w + 4
-// form a pair that owns keys [32 (w % 4), 32 (w % 4) + 32) of the block and
-// splits the head dim of dK / dV between them: the "S" wave (w < 4) keeps
-// the keys' K fragments, forms S = Q K^T and P, and accumulates dK / dV
-// columns [0, D / 2); the "dP" wave keeps V, forms dP = dO V^T and
-// dS = P (dP - delta), and accumulates columns [D / 2, D).  P (bf16, as the
-// MFMA operand of dV) and dS are handed to the partner through LDS in the
-// accumulator's own lane order.  Per tile: barrier X publishes P (and ends
-// every read of the tile two steps back), barrier Y publishes dS and the
-// next tile.  The pair sits on one SIMD, so one wave's exponentials and
-// LDS waits overlap the other's matrix products.
+// One workgroup of eight waves per unit.  Waves w and w + 4 form a pair on
+// one SIMD that owns keys [32 (w % 4), 32 (w % 4) + 32) of the block: the
+// "S" wave keeps the keys' K fragments, forms S = Q K^T and P and
+// accumulates all of dV; the "dP" wave keeps V, forms dP = dO V^T and
+// dS = P (dP - delta) and accumulates all of dK.  P (bf16, in the
+// accumulator's own lane order) is the only value handed across, through
+// LDS.  One barrier per 32-row query tile: before barrier t the S wave
+// publishes P(t) and the dP wave has formed dP(t); after it the S wave adds
+// P(t)^T dO(t) into dV and goes on to S(t + 1), while the dP wave forms
+// dS(t), adds dS(t)^T Q(t) into dK and goes on to dP(t + 1) -- so each
+// wave's exponentials or dS arithmetic run under its partner's products.
+// Q / dO tiles are staged through three LDS buffers: the tile stored after
+// barrier t is first read after barrier t + 1, and the buffer it replaces
+// was last read before barrier t.
 // ---------------------------------------------------------------------------
 constexpr int NT2 = 512;
+constexpr int NB2 = 3;   // Q / dO staging buffers
 
 template <int D>
 struct SmemDKDV2 {
-  unsigned short qr[2][BQ * Lay<D>::R];   // Q tile, row copy  (A of S = Q K^T)
-  unsigned short dr[2][BQ * Lay<D>::R];   // dO tile, row copy (A of dP = dO V^T)
-  unsigned short qt[2][BQ * Lay<D>::T];   // Q tile, tr copy   (B of dK += dS^T Q)
-  unsigned short dt[2][BQ * Lay<D>::T];   // dO tile, tr copy  (B of dV += P^T dO)
-  u16x8 px[4][2][64];                     // P of pair w % 4: [operand half][lane]
-  u16x8 sx[4][2][64];                     // dS of pair w % 4
-  float lse2[2][BQ];                      // LSE * log2(e); +inf for rows without keys
-  float dls[2][BQ];                       // delta * scale
+  unsigned short qr[NB2][BQ * Lay<D>::R];   // Q tile, row copy  (A of S = Q K^T)
+  unsigned short dr[NB2][BQ * Lay<D>::R];   // dO tile, row copy (A of dP = dO V^T)
+  unsigned short qt[NB2][BQ * Lay<D>::T];   // Q tile, tr copy   (B of dK += dS^T Q)
+  unsigned short dt[NB2][BQ * Lay<D>::T];   // dO tile, tr copy  (B of dV += P^T dO)
+  u16x8 px[2][4][2][64];                    // P by tile parity, pair w % 4: [operand half][lane]
+  float lse2[NB2][BQ];                      // LSE * log2(e); +inf for rows without keys
+  float dls[NB2][BQ];                       // delta * scale
 };
 
 // Staging of one 32-row Q / dO tile by 512 threads.  Each thread owns fixed
@@ -463,7 +466,8 @@ struct Stage2 {
     dl = buf_load_f32(buf_rsrc(dl_t, rows * 4), r);
   }
 
-  __device__ inline void store(SmemDKDV2<D>& sm, int buf, int i0, int Sq, float scale) const {
+  // rows = rows of the tile inside the problem (the rest hold zeros)
+  __device__ inline void store(SmemDKDV2<D>& sm, int buf, int rows, float scale) const {
 #pragma unroll
     for (int k = 0; k < NR; ++k) {
       *(u16x8*)((tdo[k] ? sm.dr[buf] : sm.qr[buf]) + lrow[k]) = v[k];
@@ -472,9 +476,35 @@ struct Stage2 {
     const int t = threadIdx.x;
     if (t >= NT2 - BQ) {
       const int r = t - (NT2 - BQ);
-      const bool ok = i0 + r < Sq;
+      const bool ok = r < rows;
       sm.lse2[buf][r] = (!ok || lse == -INFINITY) ? INFINITY : lse * kLog2e;
       sm.dls[buf][r] = ok ? dl * scale : 0.f;
+    }
+  }
+};
+
+// Walk over the (query head, 32-row tile) sequence of one unit part, with
+// running tile pointers: a step adds one tile's rows, a head change adds the
+// head stride less the rows walked.
+struct TileWalk {
+  const unsigned short *q, *d;
+  const float *l, *dl;
+  int qb, nqb, i0, lo_al;
+  int64_t q_step, d_step, q_wrap, d_wrap, l_wrap;
+
+  __device__ inline void next() {
+    q += q_step;
+    d += d_step;
+    l += BQ;
+    dl += BQ;
+    i0 += BQ;
+    if (++qb == nqb) {
+      qb = 0;
+      i0 = lo_al;
+      q += q_wrap;
+      d += d_wrap;
+      l += l_wrap;
+      dl += l_wrap;
     }
   }
 };
@@ -483,7 +513,7 @@ template <int D>
 __global__ __launch_bounds__(NT2) void k_dkdv2(Params p, BwdArgs a, DkdvGrid gd) {
   static_assert(D == 64 || D == 128, "head dim");
   constexpr int NS = D / 16;          // k-steps over the head dim
-  constexpr int NH = D / 64;          // 32-column blocks of this wave's half of the head dim
+  constexpr int NC = D / 32;          // 32-column blocks of dK / dV
   constexpr int R = Lay<D>::R, T = Lay<D>::T;
   __shared__ __attribute__((aligned(16))) SmemDKDV2<D> sm;
 
@@ -491,7 +521,6 @@ __global__ __launch_bounds__(NT2) void k_dkdv2(Params p, BwdArgs a, DkdvGrid gd)
   const int w = __builtin_amdgcn_readfirstlane(tid >> 6);   // wave-uniform
   const int pr = w & 3;               // pair: keys [32 pr, 32 pr + 32) of the block
   const bool sw = w < 4;              // S wave (else dP wave)
-  const int cb = sw ? 0 : D / 2;      // first dK / dV column of this wave
   const BlockXYZ blk = xcd_block();
   const int b = blk.z;
   const SeqView sv = seq_view(p, b);   // this batch entry (or packed sequence)
@@ -521,13 +550,13 @@ __global__ __launch_bounds__(NT2) void k_dkdv2(Params p, BwdArgs a, DkdvGrid gd)
   const int wr_t = msk.wr;
   const int rowA = lr * R + 8 * lg;
   const int trQ = tr_base(l, T);
+  const int q_rb = 2 * (int)p.q_str[2], d_rb = 2 * (int)p.do_str[2];
 
   for (int u = 0; u < n_units; ++u) {
     const int kb = u == 0 ? kbx : nkb - 1 - kbx;
     const int k0 = kb * BK;
     const int kw = k0 + 32 * pr;
     const int jkey = kw + lr;
-    const bool wave_keys_in = kw + 32 <= Sk;
     const bool key_ok = jkey < Sk;
     const int jg = jkey + (int)msk.k_off;
     const bool sink_key = jg < msk.n_sink;
@@ -539,6 +568,16 @@ __global__ __launch_bounds__(NT2) void k_dkdv2(Params p, BwdArgs a, DkdvGrid gd)
     const int n_all = p.G * nqb;
     const int it_lo = (int)((int64_t)n_all * part / nparts);
     const int n_it = (int)((int64_t)n_all * (part + 1) / nparts) - it_lo;
+    // tiles [i0, i0 + 32) in which every row sees all 32 keys of this wave:
+    // i0 >= full_a and i0 + 31 <= full_c
+    int full_a = -0x3fffffff, full_c = 0x3fffffff;
+    if (kw + 32 > Sk) {
+      full_a = 0x3fffffff;
+    } else if (!no_mask && kw + 31 + msk.k_off >= msk.n_sink) {
+      const int64_t base = (int64_t)kw + msk.k_off - msk.q_off - msk.diag;
+      full_a = (int)max<int64_t>(min<int64_t>(base + 31 - msk.wr, 0x3fffffff), -0x3fffffff);
+      if (msk.wl >= 0) full_c = (int)max<int64_t>(min<int64_t>(base + msk.wl, 0x3fffffff), -0x3fffffff);
+    }
 
     // K (S wave) or V (dP wave) fragments of this pair's keys: B operands
     bf16x8 fB[NS];
@@ -550,146 +589,182 @@ __global__ __launch_bounds__(NT2) void k_dkdv2(Params p, BwdArgs a, DkdvGrid gd)
 #pragma unroll
       for (int s = 0; s < NS; ++s) fB[s] = as_bf16x8(*(const u16x8*)(src + jc * rs + 16 * s + 8 * lg));
     }
-    f32x16 dk[NH], dv[NH];
+    f32x16 og[NC];   // dV (S wave) or dK (dP wave), columns 32 n + lane
 #pragma unroll
-    for (int n = 0; n < NH; ++n) { dk[n] = zero16(); dv[n] = zero16(); }
+    for (int n = 0; n < NC; ++n) og[n] = zero16();
     __syncthreads();  // readers of the previous unit's LDS tiles are done
     wait_vm_loads();
+    if (n_it <= 0) continue;
+
+    // tile walks: `ld` runs ahead with the loads, `fr` is the tile whose
+    // S / dP is formed next
+    TileWalk ld;
+    {
+      const int h0 = h_begin + it_lo / nqb, qb0 = it_lo % nqb;
+      const int i00 = lo_al + BQ * qb0;
+      ld.q = (const unsigned short*)a.q + sv.q_off(p.q_str, b) + h0 * p.q_str[1] + (int64_t)i00 * p.q_str[2];
+      ld.d = (const unsigned short*)a.dout + sv.q_off(p.do_str, b) + h0 * p.do_str[1] +
+             (int64_t)i00 * p.do_str[2];
+      const int64_t rb = ((int64_t)b * p.Hq + h0) * p.Sq + i00;
+      ld.l = a.lse + rb;
+      ld.dl = a.delta + rb;
+      ld.qb = qb0;
+      ld.nqb = nqb;
+      ld.i0 = i00;
+      ld.lo_al = lo_al;
+      ld.q_step = BQ * p.q_str[2];
+      ld.d_step = BQ * p.do_str[2];
+      ld.q_wrap = p.q_str[1] - nqb * ld.q_step;
+      ld.d_wrap = p.do_str[1] - nqb * ld.d_step;
+      ld.l_wrap = (int64_t)p.Sq - (int64_t)nqb * BQ;
+    }
+    int fr_i0 = ld.i0, fr_qb = ld.qb;
+    auto fr_next = [&]() {
+      fr_i0 += BQ;
+      if (++fr_qb == nqb) { fr_qb = 0; fr_i0 = lo_al; }
+    };
 
     Stage2<D> stg;
-    const int q_rb = 2 * (int)p.q_str[2], d_rb = 2 * (int)p.do_str[2];
     stg.init(w, q_rb, d_rb);
-    auto issue = [&](int h, int i0) {
-      const int64_t rb = ((int64_t)b * p.Hq + h) * p.Sq + i0;
-      stg.load((const unsigned short*)a.q + sv.q_off(p.q_str, b) + h * p.q_str[1] + (int64_t)i0 * p.q_str[2],
-               (const unsigned short*)a.dout + sv.q_off(p.do_str, b) + h * p.do_str[1] + (int64_t)i0 * p.do_str[2],
-               q_rb, d_rb, a.lse + rb, a.delta + rb, min(Sq - i0, BQ));
+    int held_rows = 0;   // rows of the tile whose loads are in stg
+    auto issue = [&]() {
+      held_rows = min(Sq - ld.i0, BQ);
+      stg.load(ld.q, ld.d, q_rb, d_rb, ld.l, ld.dl, held_rows);
+      ld.next();
     };
-    int h = h_begin + (nqb > 0 ? it_lo / nqb : 0), qb = nqb > 0 ? it_lo % nqb : 0;
-    if (n_it > 0) {
-      issue(h, lo_al + BQ * qb);
-      stg.store(sm, 0, lo_al + BQ * qb, Sq, scale);
-      __syncthreads();
+    // prologue: tiles 0 and 1 into buffers 0 and 1, tile 2 into registers
+    issue();
+    stg.store(sm, 0, held_rows, scale);
+    if (n_it > 1) {
+      issue();
+      stg.store(sm, 1, held_rows, scale);
     }
+    if (n_it > 2) issue();
+    __syncthreads();
 
-    for (int it = 0; it < n_it; ++it) {
-      const int cur = it & 1;
-      const int i0 = lo_al + BQ * qb;
-      int hn = h, qbn = qb + 1;
-      if (qbn == nqb) { qbn = 0; ++hn; }
-      if (it + 1 < n_it) issue(hn, lo_al + BQ * qbn);
+    // Per-lane key window of the masked exponentials: key lane jg is allowed
+    // for row i when  jg - i - q_off - diag  lies in [lo_l, lo_l + span]
+    // (all offsets for a sink key or no mask, none for a key past the end).
+    int lo_l = lo_t, span = wr_t - lo_t;
+    if (no_mask | sink_key) { lo_l = -0x3fffffff; span = 0x7ffffffe; }
+    if (!key_ok) { lo_l = 0x3fffffff; span = 0; }
+    const int tb0 = jg - (int)msk.q_off - (int)msk.diag - 4 * lg - lo_l;
 
-      // S = Q K^T (S wave) or dP = dO V^T (dP wave): rows i0..i0+31, the pair's keys
-      f32x16 acc = zero16();
-      {
-        const unsigned short* src = sw ? sm.qr[cur] : sm.dr[cur];
-        bf16x8 xa[NS];
+    // S = Q K^T (S wave) or dP = dO V^T (dP wave) of the tile in buffer `buf`
+    f32x16 acc;
+    auto front_mm = [&](int buf) {
+      const unsigned short* src = lds_opaque((sw ? sm.qr[buf] : sm.dr[buf]) + rowA);
+      bf16x8 xa[NS];
 #pragma unroll
-        for (int s = 0; s < NS; ++s) xa[s] = lds_b128(src, rowA + 16 * s);
+      for (int s = 0; s < NS; ++s) xa[s] = lds_b128(src, 16 * s);
+      acc = zero16();
 #pragma unroll
-        for (int s = 0; s < NS; ++s) acc = mfma(xa[s], fB[s], acc);
-      }
-      // dO B operands of this wave's dV columns (independent of P)
-      bf16x8 oB[NH][2];
+      for (int s = 0; s < NS; ++s) acc = mfma(xa[s], fB[s], acc);
+    };
+    // S wave: P of tile `fr` (rows from buffer `buf`), published in P buffer `pbuf`
+    bf16x8 pa0, pa1;
+    auto front_p = [&](int buf, int pbuf) {
+      f32x4 L4[4];
 #pragma unroll
-      for (int n = 0; n < NH; ++n) {
-        oB[n][0] = lds_trB(sm.dt[cur], trQ, 0, cb + 32 * n, T);
-        oB[n][1] = lds_trB(sm.dt[cur], trQ, 16, cb + 32 * n, T);
-      }
-      bf16x8 pa0, pa1;
-      if (sw) {
-        f32x4 L4[4];
+      for (int m = 0; m < 4; ++m) L4[m] = *(const f32x4*)&sm.lse2[buf][8 * m + 4 * lg];
+      const int i0 = fr_i0;
+      float pv[16];
+      if (i0 >= full_a && i0 + BQ - 1 <= full_c) {
 #pragma unroll
-        for (int m = 0; m < 4; ++m) L4[m] = *(const f32x4*)&sm.lse2[cur][8 * m + 4 * lg];
-        const bool full = wave_keys_in && msk.tile_full(i0, i0 + BQ, kw, kw + 32);
-        float pv[16];
-        if (full) {
+        for (int r = 0; r < 16; ++r)
+          pv[r] = __builtin_amdgcn_exp2f(fmaf(acc[r], scale_log2, -L4[r >> 2][r & 3]));
+      } else {
+        const int tb = tb0 - i0;
 #pragma unroll
-          for (int r = 0; r < 16; ++r)
-            pv[r] = __builtin_amdgcn_exp2f(fmaf(acc[r], scale_log2, -L4[r >> 2][r & 3]));
-        } else {
-          const int tb = jg - (i0 + (int)msk.q_off) - (int)msk.diag - 4 * lg;
-#pragma unroll
-          for (int r = 0; r < 16; ++r) {
-            const int c = 8 * (r >> 2) + (r & 3);
-            const int t = tb - c;
-            const bool ok = key_ok & (no_mask | ((t <= wr_t) & (t >= lo_t)) | sink_key);
-            const float ex = __builtin_amdgcn_exp2f(fmaf(acc[r], scale_log2, -L4[r >> 2][r & 3]));
-            pv[r] = ok ? ex : 0.f;
-          }
+        for (int r = 0; r < 16; ++r) {
+          const unsigned int tt = (unsigned int)(tb - (8 * (r >> 2) + (r & 3)));
+          const float ex = __builtin_amdgcn_exp2f(fmaf(acc[r], scale_log2, -L4[r >> 2][r & 3]));
+          pv[r] = tt <= (unsigned int)span ? ex : 0.f;
         }
-        pa0 = pack8(pv);
-        pa1 = pack8(pv + 8);
-        sm.px[pr][0][l] = __builtin_bit_cast(u16x8, pa0);
-        sm.px[pr][1][l] = __builtin_bit_cast(u16x8, pa1);
       }
-      __syncthreads();  // X: P published
+      pa0 = pack8(pv);
+      pa1 = pack8(pv + 8);
+      sm.px[pbuf][pr][0][l] = __builtin_bit_cast(u16x8, pa0);
+      sm.px[pbuf][pr][1][l] = __builtin_bit_cast(u16x8, pa1);
+    };
+    front_mm(0);
+    if (sw) front_p(0, 0);
+    fr_next();
+
+    for (int t = 0; t < n_it; ++t) {
+      const int buf = t % NB2, nbuf = (t + 1) % NB2;
+      __syncthreads();  // P(t) published; tile t - 1's buffers free; tile t + 1 stored
+      if (t + 2 < n_it) {
+        stg.store(sm, (t + 2) % NB2, held_rows, scale);
+        if (t + 3 < n_it) issue();
+      }
+      // S wave: dV += P(t)^T dO(t).  dP wave: dS(t) = P(t) (dP(t) - delta),
+      // pre-multiplied by the softmax scale, and dK += dS(t)^T Q(t).  One
+      // product loop for both, so the accumulators keep their registers.
+      bf16x8 A0 = pa0, A1 = pa1;
       if (!sw) {
         f32x4 D4[4];
 #pragma unroll
-        for (int m = 0; m < 4; ++m) D4[m] = *(const f32x4*)&sm.dls[cur][8 * m + 4 * lg];
-        const u16x8 p0 = sm.px[pr][0][l], p1 = sm.px[pr][1][l];
-        pa0 = __builtin_bit_cast(bf16x8, p0);
-        pa1 = __builtin_bit_cast(bf16x8, p1);
-        // dS = P (dP - delta), pre-multiplied by the softmax scale
+        for (int m = 0; m < 4; ++m) D4[m] = *(const f32x4*)&sm.dls[buf][8 * m + 4 * lg];
+        const u16x8 p0 = sm.px[t & 1][pr][0][l], p1 = sm.px[t & 1][pr][1][l];
         float dsv[16];
 #pragma unroll
         for (int r = 0; r < 8; ++r) {
           dsv[r] = bf16_to_f32(p0[r]) * fmaf(acc[r], scale, -D4[r >> 2][r & 3]);
           dsv[r + 8] = bf16_to_f32(p1[r]) * fmaf(acc[r + 8], scale, -D4[(r + 8) >> 2][r & 3]);
         }
-        const bf16x8 sa0 = pack8(dsv), sa1 = pack8(dsv + 8);
-        sm.sx[pr][0][l] = __builtin_bit_cast(u16x8, sa0);
-        sm.sx[pr][1][l] = __builtin_bit_cast(u16x8, sa1);
+        A0 = pack8(dsv);
+        A1 = pack8(dsv + 8);
+      }
+      // The products of tile t and S / dP of tile t + 1 form one scheduling
+      // region, with every operand read issued ahead of the product that
+      // uses it (on the last tile the second half reads a stale buffer and
+      // its result is dropped).
+      {
+        const unsigned short* bt = lds_opaque((sw ? sm.dt[buf] : sm.qt[buf]) + trQ);
+        bf16x8 bq[2 * NC];
 #pragma unroll
-        for (int n = 0; n < NH; ++n) {
-          const bf16x8 q0 = lds_trB(sm.qt[cur], trQ, 0, cb + 32 * n, T);
-          const bf16x8 q1 = lds_trB(sm.qt[cur], trQ, 16, cb + 32 * n, T);
-          dk[n] = mfma(sa0, q0, dk[n]);
-          dk[n] = mfma(sa1, q1, dk[n]);
+        for (int i = 0; i < 2 * NC; ++i) bq[i] = lds_trB(bt, 0, 16 * (i & 1), 32 * (i >> 1), T);
+#pragma unroll
+        for (int i = 0; i < 2 * NC; ++i) og[i >> 1] = mfma((i & 1) ? A1 : A0, bq[i], og[i >> 1]);
+        front_mm(nbuf);
+        // reads of 4 B operands ahead, then one product per further read
+        __builtin_amdgcn_sched_group_barrier(0x100, 8, 0);
+#pragma unroll
+        for (int i = 0; i < 2 * NC - 4; ++i) {
+          __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+          __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
         }
-      }
 #pragma unroll
-      for (int n = 0; n < NH; ++n) {
-        dv[n] = mfma(pa0, oB[n][0], dv[n]);
-        dv[n] = mfma(pa1, oB[n][1], dv[n]);
-      }
-      if (it + 1 < n_it) stg.store(sm, cur ^ 1, lo_al + BQ * qbn, Sq, scale);
-      __syncthreads();  // Y: dS and the next tile published
-      if (sw) {
-        const bf16x8 sa0 = __builtin_bit_cast(bf16x8, sm.sx[pr][0][l]);
-        const bf16x8 sa1 = __builtin_bit_cast(bf16x8, sm.sx[pr][1][l]);
-#pragma unroll
-        for (int n = 0; n < NH; ++n) {
-          dk[n] = mfma(sa0, lds_trB(sm.qt[cur], trQ, 0, cb + 32 * n, T), dk[n]);
-          dk[n] = mfma(sa1, lds_trB(sm.qt[cur], trQ, 16, cb + 32 * n, T), dk[n]);
+        for (int i = 0; i < 4; ++i) {
+          __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+          __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
         }
+#pragma unroll
+        for (int i = 0; i < NS - 4; ++i) {
+          __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+          __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+        }
+        __builtin_amdgcn_sched_group_barrier(0x008, 4, 0);
       }
-      h = hn;
-      qb = qbn;
+      if (sw && t + 1 < n_it) front_p(nbuf, (t + 1) & 1);
+      fr_next();
     }
 
-    // Epilogue: this wave's dK (scaled through dS) and dV columns.
-    float* dkp = a.dk + sv.k_off(p.dk_str, b) + hk * p.dk_str[1];
-    float* dvp = a.dv + sv.k_off(p.dv_str, b) + hk * p.dv_str[1];
+    // Epilogue: dV (S wave) or dK (dP wave, scaled through dS) of this pair's keys.
+    float* op = sw ? a.dv + sv.k_off(p.dv_str, b) + hk * p.dv_str[1]
+                   : a.dk + sv.k_off(p.dk_str, b) + hk * p.dk_str[1];
+    const int64_t os = sw ? p.dv_str[2] : p.dk_str[2];
 #pragma unroll
-    for (int n = 0; n < NH; ++n) {
+    for (int n = 0; n < NC; ++n) {
 #pragma unroll
       for (int r = 0; r < 16; ++r) {
         const int64_t j = kw + crow(r, lg);
         if (j < Sk) {
-          float* pk = dkp + j * p.dk_str[2] + cb + 32 * n + lr;
-          float* pvv = dvp + j * p.dv_str[2] + cb + 32 * n + lr;
-          if (out_mode == kAtomicAdd) {
-            atomic_add_f32(pk, dk[n][r]);
-            atomic_add_f32(pvv, dv[n][r]);
-          } else if (out_mode == kAddInto) {
-            *pk += dk[n][r];
-            *pvv += dv[n][r];
-          } else {
-            *pk = dk[n][r];
-            *pvv = dv[n][r];
-          }
+          float* po = op + j * os + 32 * n + lr;
+          if (out_mode == kAtomicAdd) atomic_add_f32(po, og[n][r]);
+          else if (out_mode == kAddInto) *po += og[n][r];
+          else *po = og[n][r];
         }
       }
     }

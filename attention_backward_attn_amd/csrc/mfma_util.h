@@ -94,6 +94,17 @@ __device__ inline bf16x8 lds_trB(const unsigned short* tile, int base, int r0, i
   return cat44(lds_tr4(tile, base + r0 * stride + n0), lds_tr4(tile, base + (r0 + 8) * stride + n0));
 }
 
+// The same LDS address passed through a register the compiler cannot see
+// into: reads at  opaque(p) + constant  then keep one address register and
+// fold the constant into the instruction's offset field, instead of one
+// hoisted address register per constant.
+__device__ inline const unsigned short* lds_opaque(const unsigned short* p) {
+  const auto* p3 = (__attribute__((address_space(3))) const unsigned short*)p;
+  unsigned int a = (unsigned int)(size_t)p3;
+  asm volatile("" : "+v"(a));
+  return (const unsigned short*)(__attribute__((address_space(3))) const unsigned short*)(size_t)a;
+}
+
 // The hardware deals a launch's workgroups to the eight XCDs round-robin by
 // linear workgroup id.  Renumbering them so that each XCD receives one
 // contiguous range of logical ids (x fastest, then z, then y) keeps the
