@@ -413,72 +413,60 @@ __global__ __launch_bounds__(NT, 1) void k_dkdv(Params p, BwdArgs a, DkdvGrid gd
 // was last read before barrier t.
 // ---------------------------------------------------------------------------
 constexpr int NT2 = 512;
-constexpr int NB2 = 3;   // Q / dO staging buffers
+constexpr int NB2 = 4;   // Q / dO tile buffers
 
 template <int D>
-struct SmemDKDV2 {
-  unsigned short qr[NB2][BQ * Lay<D>::R];   // Q tile, row copy  (A of S = Q K^T)
-  unsigned short dr[NB2][BQ * Lay<D>::R];   // dO tile, row copy (A of dP = dO V^T)
-  unsigned short qt[NB2][BQ * Lay<D>::T];   // Q tile, tr copy   (B of dK += dS^T Q)
-  unsigned short dt[NB2][BQ * Lay<D>::T];   // dO tile, tr copy  (B of dV += P^T dO)
-  u16x8 px[2][4][2][64];                    // P by tile parity, pair w % 4: [operand half][lane]
-  float lse2[NB2][BQ];                      // LSE * log2(e); +inf for rows without keys
-  float dls[NB2][BQ];                       // delta * scale
+struct __attribute__((aligned(1024))) SmemDKDV2 {
+  unsigned char q[NB2][BQ * 2 * D];   // Q tile, swizzled (A of S = Q K^T; tr B of dK += dS^T Q)
+  unsigned char d[NB2][BQ * 2 * D];   // dO tile, swizzled (A of dP = dO V^T; tr B of dV += P^T dO)
+  float lse[NB2][2 * BQ];             // LSE of the tile's rows (second half: padding)
+  float dl[NB2][2 * BQ];              // delta of the tile's rows (second half: padding)
+  u16x8 px[2][4][2][64];              // P by tile parity, pair w % 4: [operand half][lane]
 };
 
-// Staging of one 32-row Q / dO tile by 512 threads.  Each thread owns fixed
-// 16-byte chunk slots (the tensor of a slot is the same for a whole wave)
-// and fetches them with buffer loads whose resource covers the tile's rows
-// only: rows past the end read as zero, and the per-thread offsets never
-// change.  The last 32 threads keep the tile's LSE and delta.
+// Staging of one 32-row Q / dO tile straight from global memory into LDS:
+// wave w issues CR / 8 64-lane loads, each filling 1 KB (64 / CR rows) of
+// one tensor's tile in the swizzled layout, so every lane has one fixed
+// source offset per load; wave 0 also loads the tile's LSE and delta.  The
+// buffer resources span the tile's rows inside the problem: rows past the
+// end arrive as zeros.
 template <int D>
-struct Stage2 {
-  static constexpr int NCR = D / 8;
-  static constexpr int NCH = 2 * BQ * NCR;
-  static constexpr int NR = NCH / NT2;
-  static_assert(NCH % NT2 == 0 && (BQ * NCR) % 64 == 0, "chunks per thread, one tensor per wave");
-  u16x8 v[NR];
-  float lse, dl;
-  int voff[NR], lrow[NR], ltr[NR];
-  bool tdo[NR];   // slot holds dO (else Q)
+struct StageDma {
+  static constexpr int CR = D / 8;
+  static constexpr int NI = CR / 8;   // Q / dO loads per wave per tile
+  static_assert(NI >= 1 && (2 * BQ * CR) % (64 * NI) == 0, "loads per wave");
+  int voff[NI];
+  unsigned int dst0[NI];   // LDS byte offset of each load in buffer 0
+  bool is_d;               // this wave loads dO (else Q)
+  bool rows_too;           // wave 0: also the LSE / delta rows
+  int n_loads;             // loads per tile of this wave
 
-  __device__ inline void init(int w, int q_rb, int d_rb) {
+  __device__ inline void init(int w, int l, int q_rb, int d_rb) {
 #pragma unroll
-    for (int k = 0; k < NR; ++k) {
-      tdo[k] = (64 * w + NT2 * k) / (BQ * NCR) != 0;
-      const int rem = (threadIdx.x + NT2 * k) % (BQ * NCR);
-      const int row = rem / NCR, c = rem % NCR;
-      voff[k] = row * (tdo[k] ? d_rb : q_rb) + 16 * c;
-      lrow[k] = row * Lay<D>::R + 8 * c;
-      ltr[k] = row * Lay<D>::T + 8 * c;
+    for (int k = 0; k < NI; ++k) {
+      const int gi = w * NI + k;   // load index over both tiles
+      is_d = gi >= BQ * CR / 64;
+      const int slot = gi % (BQ * CR / 64);
+      const int row = (64 * slot + l) / CR;
+      voff[k] = row * (is_d ? d_rb : q_rb) + 16 * ((l % CR) ^ Swz<D>::f(row));
+      dst0[k] = (is_d ? offsetof(SmemDKDV2<D>, d) : offsetof(SmemDKDV2<D>, q)) + 1024 * slot;
     }
+    rows_too = w == 0;
+    n_loads = NI + (rows_too ? 2 : 0);
   }
 
-  // q_t / d_t / l_t / dl_t point at the tile's first row; rows = rows inside the problem
-  __device__ inline void load(const unsigned short* q_t, const unsigned short* d_t, int q_rb, int d_rb,
-                              const float* l_t, const float* dl_t, int rows) {
-    const __amdgpu_buffer_rsrc_t rq = buf_rsrc(q_t, rows * q_rb);
-    const __amdgpu_buffer_rsrc_t rd = buf_rsrc(d_t, rows * d_rb);
+  // q_t / d_t / l_t / dl_t: the tile's first row; rows: rows inside the problem
+  __device__ inline void issue(unsigned int sm_base, int buf, const unsigned short* q_t, const unsigned short* d_t,
+                               int q_rb, int d_rb, const float* l_t, const float* dl_t, int rows, int l) {
+    const __amdgpu_buffer_rsrc_t rs = is_d ? buf_rsrc(d_t, rows * d_rb) : buf_rsrc(q_t, rows * q_rb);
 #pragma unroll
-    for (int k = 0; k < NR; ++k) v[k] = buf_load16(tdo[k] ? rd : rq, voff[k]);
-    const int r = 4 * (threadIdx.x & (BQ - 1));
-    lse = buf_load_f32(buf_rsrc(l_t, rows * 4), r);
-    dl = buf_load_f32(buf_rsrc(dl_t, rows * 4), r);
-  }
-
-  // rows = rows of the tile inside the problem (the rest hold zeros)
-  __device__ inline void store(SmemDKDV2<D>& sm, int buf, int rows, float scale) const {
-#pragma unroll
-    for (int k = 0; k < NR; ++k) {
-      *(u16x8*)((tdo[k] ? sm.dr[buf] : sm.qr[buf]) + lrow[k]) = v[k];
-      *(u16x8*)((tdo[k] ? sm.dt[buf] : sm.qt[buf]) + ltr[k]) = v[k];
-    }
-    const int t = threadIdx.x;
-    if (t >= NT2 - BQ) {
-      const int r = t - (NT2 - BQ);
-      const bool ok = r < rows;
-      sm.lse2[buf][r] = (!ok || lse == -INFINITY) ? INFINITY : lse * kLog2e;
-      sm.dls[buf][r] = ok ? dl * scale : 0.f;
+    for (int k = 0; k < NI; ++k)
+      lds_dma16(rs, __builtin_amdgcn_readfirstlane(sm_base + dst0[k] + buf * (BQ * 2 * D)), voff[k]);
+    if (rows_too) {
+      lds_dma4(buf_rsrc(l_t, rows * 4),
+               __builtin_amdgcn_readfirstlane(sm_base + offsetof(SmemDKDV2<D>, lse) + buf * (8 * BQ)), 4 * l);
+      lds_dma4(buf_rsrc(dl_t, rows * 4),
+               __builtin_amdgcn_readfirstlane(sm_base + offsetof(SmemDKDV2<D>, dl) + buf * (8 * BQ)), 4 * l);
     }
   }
 };
@@ -514,8 +502,8 @@ __global__ __launch_bounds__(NT2) void k_dkdv2(Params p, BwdArgs a, DkdvGrid gd)
   static_assert(D == 64 || D == 128, "head dim");
   constexpr int NS = D / 16;          // k-steps over the head dim
   constexpr int NC = D / 32;          // 32-column blocks of dK / dV
-  constexpr int R = Lay<D>::R, T = Lay<D>::T;
-  __shared__ __attribute__((aligned(16))) SmemDKDV2<D> sm;
+  constexpr int RB = Swz<D>::RB;
+  __shared__ SmemDKDV2<D> sm;
 
   const int tid = threadIdx.x, l = tid & 63, lr = l & 31, lg = l >> 5;
   const int w = __builtin_amdgcn_readfirstlane(tid >> 6);   // wave-uniform
@@ -548,9 +536,11 @@ __global__ __launch_bounds__(NT2) void k_dkdv2(Params p, BwdArgs a, DkdvGrid gd)
   const bool no_mask = msk.kind == kMaskNone;
   const int lo_t = msk.wl < 0 ? -0x3fffffff : -msk.wl;
   const int wr_t = msk.wr;
-  const int rowA = lr * R + 8 * lg;
-  const int trQ = tr_base(l, T);
+  const int a_lane = Swz<D>::a_lane(l), t_lane = Swz<D>::t_lane(l);
   const int q_rb = 2 * (int)p.q_str[2], d_rb = 2 * (int)p.do_str[2];
+  StageDma<D> stg;
+  stg.init(w, l, q_rb, d_rb);
+  const unsigned int sm_base = lds_addr(&sm);
 
   for (int u = 0; u < n_units; ++u) {
     const int kb = u == 0 ? kbx : nkb - 1 - kbx;
@@ -623,23 +613,20 @@ __global__ __launch_bounds__(NT2) void k_dkdv2(Params p, BwdArgs a, DkdvGrid gd)
       fr_i0 += BQ;
       if (++fr_qb == nqb) { fr_qb = 0; fr_i0 = lo_al; }
     };
-
-    Stage2<D> stg;
-    stg.init(w, q_rb, d_rb);
-    int held_rows = 0;   // rows of the tile whose loads are in stg
-    auto issue = [&]() {
-      held_rows = min(Sq - ld.i0, BQ);
-      stg.load(ld.q, ld.d, q_rb, d_rb, ld.l, ld.dl, held_rows);
+    auto issue = [&](int buf) {
+      stg.issue(sm_base, buf, ld.q, ld.d, q_rb, d_rb, ld.l, ld.dl, min(Sq - ld.i0, BQ), l);
       ld.next();
     };
-    // prologue: tiles 0 and 1 into buffers 0 and 1, tile 2 into registers
-    issue();
-    stg.store(sm, 0, held_rows, scale);
-    if (n_it > 1) {
-      issue();
-      stg.store(sm, 1, held_rows, scale);
+    // Prologue: tiles 0, 1 and 2 in flight; 0 and 1 complete before the
+    // first barrier.
+    issue(0);
+    if (n_it > 1) issue(1);
+    if (n_it > 2) {
+      issue(2);
+      wait_vm(stg.n_loads);
+    } else {
+      wait_vm(0);
     }
-    if (n_it > 2) issue();
     __syncthreads();
 
     // Per-lane key window of the masked exponentials: key lane jg is allowed
@@ -650,23 +637,37 @@ __global__ __launch_bounds__(NT2) void k_dkdv2(Params p, BwdArgs a, DkdvGrid gd)
     if (!key_ok) { lo_l = 0x3fffffff; span = 0; }
     const int tb0 = jg - (int)msk.q_off - (int)msk.diag - 4 * lg - lo_l;
 
+    // A-operand tile of this wave (Q for the S wave, dO for the dP wave) and
+    // B-operand tile of its dV / dK products (dO, resp. Q), buffer `buf`
+    auto a_tile = [&](int buf) { return lds_addr(sw ? sm.q[buf] : sm.d[buf]) + a_lane; };
+    auto b_tile = [&](int buf) { return lds_addr(sw ? sm.d[buf] : sm.q[buf]) + t_lane; };
+
     // S = Q K^T (S wave) or dP = dO V^T (dP wave) of the tile in buffer `buf`
     f32x16 acc;
     auto front_mm = [&](int buf) {
-      const unsigned short* src = lds_opaque((sw ? sm.qr[buf] : sm.dr[buf]) + rowA);
+      const unsigned int ab = a_tile(buf);
       bf16x8 xa[NS];
 #pragma unroll
-      for (int s = 0; s < NS; ++s) xa[s] = lds_b128(src, 16 * s);
+      for (int s = 0; s < NS; ++s) xa[s] = lds_b128_at(ab ^ (32 * s));
       acc = zero16();
 #pragma unroll
       for (int s = 0; s < NS; ++s) acc = mfma(xa[s], fB[s], acc);
     };
-    // S wave: P of tile `fr` (rows from buffer `buf`), published in P buffer `pbuf`
-    bf16x8 pa0, pa1;
-    auto front_p = [&](int buf, int pbuf) {
-      f32x4 L4[4];
+    // LSE * log2(e) (S wave: of the next tile) or delta * scale (dP wave: of
+    // the current one) of the rows this lane holds in the accumulator.  Rows
+    // past the end read zeros: their Q / dO rows are zero as well, so they
+    // add nothing to dV or dK.  A row without keys (LSE = -inf) only occurs
+    // in masked tiles, where its P is zero by the mask.
+    f32x4 RV[4];
+    auto row_vals = [&](int buf) {
+      const float* v = sw ? sm.lse[buf] : sm.dl[buf];
+      const float c = sw ? kLog2e : scale;
 #pragma unroll
-      for (int m = 0; m < 4; ++m) L4[m] = *(const f32x4*)&sm.lse2[buf][8 * m + 4 * lg];
+      for (int m = 0; m < 4; ++m) RV[m] = *(const f32x4*)&v[8 * m + 4 * lg] * c;
+    };
+    // S wave: P of tile `fr`, published in P buffer `pbuf`
+    bf16x8 pa0, pa1;
+    auto front_p = [&](const f32x4* L4, int pbuf) {
       const int i0 = fr_i0;
       float pv[16];
       if (i0 >= full_a && i0 + BQ - 1 <= full_c) {
@@ -688,67 +689,67 @@ __global__ __launch_bounds__(NT2) void k_dkdv2(Params p, BwdArgs a, DkdvGrid gd)
       sm.px[pbuf][pr][1][l] = __builtin_bit_cast(u16x8, pa1);
     };
     front_mm(0);
-    if (sw) front_p(0, 0);
+    row_vals(0);
+    if (sw) front_p(RV, 0);
     fr_next();
 
     for (int t = 0; t < n_it; ++t) {
       const int buf = t % NB2, nbuf = (t + 1) % NB2;
-      __syncthreads();  // P(t) published; tile t - 1's buffers free; tile t + 1 stored
-      if (t + 2 < n_it) {
-        stg.store(sm, (t + 2) % NB2, held_rows, scale);
-        if (t + 3 < n_it) issue();
-      }
+      __syncthreads();  // P(t) published; tile t + 1 complete; tile t - 1's buffer free
+      // the loads of tile t + 3, into tile t - 1's buffer
+      const bool more = t + 3 < n_it;
+      if (more) issue((t + 3) % NB2);
       // S wave: dV += P(t)^T dO(t).  dP wave: dS(t) = P(t) (dP(t) - delta),
       // pre-multiplied by the softmax scale, and dK += dS(t)^T Q(t).  One
       // product loop for both, so the accumulators keep their registers.
       bf16x8 A0 = pa0, A1 = pa1;
       if (!sw) {
-        f32x4 D4[4];
-#pragma unroll
-        for (int m = 0; m < 4; ++m) D4[m] = *(const f32x4*)&sm.dls[buf][8 * m + 4 * lg];
         const u16x8 p0 = sm.px[t & 1][pr][0][l], p1 = sm.px[t & 1][pr][1][l];
         float dsv[16];
 #pragma unroll
         for (int r = 0; r < 8; ++r) {
-          dsv[r] = bf16_to_f32(p0[r]) * fmaf(acc[r], scale, -D4[r >> 2][r & 3]);
-          dsv[r + 8] = bf16_to_f32(p1[r]) * fmaf(acc[r + 8], scale, -D4[(r + 8) >> 2][r & 3]);
+          dsv[r] = bf16_to_f32(p0[r]) * fmaf(acc[r], scale, -RV[r >> 2][r & 3]);
+          dsv[r + 8] = bf16_to_f32(p1[r]) * fmaf(acc[r + 8], scale, -RV[(r + 8) >> 2][r & 3]);
         }
         A0 = pack8(dsv);
         A1 = pack8(dsv + 8);
       }
-      // The products of tile t and S / dP of tile t + 1 form one scheduling
-      // region, with every operand read issued ahead of the product that
-      // uses it (on the last tile the second half reads a stale buffer and
-      // its result is dropped).
+      // One scheduling region: the products of tile t, S / dP of tile t + 1
+      // and the LSE / delta rows of tile t + 1.  Every operand read is issued
+      // ahead of the product that uses it; the dependent S / dP chain
+      // alternates with the independent dV / dK accumulators.  On the last
+      // tile the S / dP half reads a stale buffer and its result is dropped.
       {
-        const unsigned short* bt = lds_opaque((sw ? sm.dt[buf] : sm.qt[buf]) + trQ);
-        bf16x8 bq[2 * NC];
+        const unsigned int bt = b_tile(buf), ab = a_tile(nbuf);
+        static_assert(2 * NC == NS, "one dV / dK product per S / dP product");
+        constexpr int AHEAD = 3;   // product pairs whose operands are in flight
+        bf16x8 bq[NS], xa[NS];
+        // product pair i: dV / dK accumulator i % NC with rows 16 (i / NC) of
+        // the tile, and step i of the S / dP chain
+        auto read_pair = [&](int i) {
+          const int n = i % NC, r0 = 16 * (i / NC);
+          const unsigned int x0 = bt ^ (64 * n), x1 = bt ^ (64 * n + 32);
+          bq[i] = cat44(lds_tr4_at(x0 + r0 * RB), lds_tr4_at(x1 + (r0 + 8) * RB));
+          xa[i] = lds_b128_at(ab ^ (32 * i));
+        };
 #pragma unroll
-        for (int i = 0; i < 2 * NC; ++i) bq[i] = lds_trB(bt, 0, 16 * (i & 1), 32 * (i >> 1), T);
+        for (int i = 0; i < AHEAD; ++i) read_pair(i);
+        acc = zero16();
+        __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
-        for (int i = 0; i < 2 * NC; ++i) og[i >> 1] = mfma((i & 1) ? A1 : A0, bq[i], og[i >> 1]);
-        front_mm(nbuf);
-        // reads of 4 B operands ahead, then one product per further read
-        __builtin_amdgcn_sched_group_barrier(0x100, 8, 0);
-#pragma unroll
-        for (int i = 0; i < 2 * NC - 4; ++i) {
-          __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
-          __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
+        for (int i = 0; i < NS; ++i) {
+          og[i % NC] = mfma(i < NC ? A0 : A1, bq[i], og[i % NC]);
+          acc = mfma(xa[i], fB[i], acc);
+          if (i + AHEAD < NS) read_pair(i + AHEAD);
+          if (i == NS - 3) row_vals(nbuf);
+          __builtin_amdgcn_sched_barrier(0);
         }
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
-          __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
-        }
-#pragma unroll
-        for (int i = 0; i < NS - 4; ++i) {
-          __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
-          __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
-        }
-        __builtin_amdgcn_sched_group_barrier(0x008, 4, 0);
       }
-      if (sw && t + 1 < n_it) front_p(nbuf, (t + 1) & 1);
+      if (sw && t + 1 < n_it) front_p(RV, (t + 1) & 1);
       fr_next();
+      // tile t + 2 complete before the next barrier (tile t + 3's loads may
+      // stay in flight)
+      wait_vm(more ? stg.n_loads : 0);
     }
 
     // Epilogue: dV (S wave) or dK (dP wave, scaled through dS) of this pair's keys.

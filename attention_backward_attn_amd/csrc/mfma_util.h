@@ -105,6 +105,78 @@ __device__ inline const unsigned short* lds_opaque(const unsigned short* p) {
   return (const unsigned short*)(__attribute__((address_space(3))) const unsigned short*)(size_t)a;
 }
 
+// Swizzled tile layout: rows of D bf16 with no padding, and the 16-byte
+// chunk c of row r stored at chunk position c ^ swz(r).  For both operand
+// read patterns -- one chunk of 16 consecutive rows (ds_read_b128) and four
+// chunks of four consecutive rows (ds_read_b64_tr_b16) -- the units read
+// together fall into distinct bank groups, so one copy of a tile serves both
+// (measured on gfx950 at the speed of the best padded layout of each
+// pattern).  For r0 a multiple of 8, swz(r0 + r) = swz(r) ^ ((r0 / 4) % 4),
+// which keeps every operand address a lane base XOR a constant.
+template <int D>
+struct Swz {
+  static constexpr int RB = 2 * D;   // row bytes
+  static constexpr int CR = D / 8;   // 16-byte chunks per row
+  __host__ __device__ static constexpr int f(int r) {
+    return D == 128 ? 4 * (r & 3) + ((r >> 2) & 3) : 4 * ((r >> 1) & 1) + ((r >> 2) & 3);
+  }
+  __host__ __device__ static constexpr int off(int r, int c) { return r * RB + ((c ^ f(r)) << 4); }
+  // A-operand lane base: row l % 32, chunk l / 32 (k-step s reads base ^ 32 s)
+  __device__ static int a_lane(int l) { return off(l & 31, l >> 5); }
+  // transposing-read lane base (see tr_base): row 4 (l / 32) + (l % 16) / 4,
+  // chunk 2 ((l / 16) % 2) + (l % 4) / 2, byte 8 (l % 2) of the chunk.
+  // Rows r0..r0+3 (r0 a multiple of 8) of 32-column block n0 read at
+  // (base ^ 16 K) + r0 RB with K = n0 / 8 ^ (r0 / 4) % 4.
+  __device__ static int t_lane(int l) {
+    const int r = 4 * (l >> 5) + ((l & 15) >> 2);
+    return off(r, 2 * ((l >> 4) & 1) + ((l & 3) >> 1)) + 8 * (l & 1);
+  }
+};
+
+typedef __attribute__((address_space(3))) u16x8 lds_u16x8;
+
+__device__ inline bf16x8 lds_b128_at(unsigned int addr) {
+  return as_bf16x8(*(const lds_u16x8*)(size_t)addr);
+}
+
+__device__ inline u16x4 lds_tr4_at(unsigned int addr) {
+  return __builtin_bit_cast(u16x4, __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(size_t)addr));
+}
+
+// Byte address of an LDS object, opaque to the compiler (see lds_opaque).
+__device__ inline unsigned int lds_addr(const void* p) {
+  unsigned int a = (unsigned int)(size_t)(const __attribute__((address_space(3))) char*)p;
+  asm volatile("" : "+v"(a));
+  return a;
+}
+
+// 16-byte (dwordx4) or 4-byte (dword) load from a buffer straight into LDS:
+// lane l writes to lds + size * l (lds: wave-uniform byte address in M0).
+// Issued as inline assembly, which the compiler does not count: the caller
+// waits for completion (vmcnt) itself.  The compiler would otherwise make
+// every transposing LDS read wait for all such loads in flight.
+__device__ inline void lds_dma16(__amdgpu_buffer_rsrc_t r, unsigned int lds, int voff) {
+  asm volatile("buffer_load_dwordx4 %0, %1, 0 offen lds" ::"v"(voff), "s"(r), "{m0}"(lds) : "memory");
+}
+__device__ inline void lds_dma4(__amdgpu_buffer_rsrc_t r, unsigned int lds, int voff) {
+  asm volatile("buffer_load_dword %0, %1, 0 offen lds" ::"v"(voff), "s"(r), "{m0}"(lds) : "memory");
+}
+
+// Wait until at most n vector-memory operations of this wave are in flight
+// (vmcnt; expcnt and lgkmcnt left at their maxima).
+__device__ inline void wait_vm(int n) {
+  switch (n) {
+    case 0: __builtin_amdgcn_s_waitcnt(0x0F70); break;
+    case 1: __builtin_amdgcn_s_waitcnt(0x0F71); break;
+    case 2: __builtin_amdgcn_s_waitcnt(0x0F72); break;
+    case 3: __builtin_amdgcn_s_waitcnt(0x0F73); break;
+    case 4: __builtin_amdgcn_s_waitcnt(0x0F74); break;
+    case 5: __builtin_amdgcn_s_waitcnt(0x0F75); break;
+    case 6: __builtin_amdgcn_s_waitcnt(0x0F76); break;
+    default: __builtin_amdgcn_s_waitcnt(0x0F70); break;
+  }
+}
+
 // The hardware deals a launch's workgroups to the eight XCDs round-robin by
 // linear workgroup id.  Renumbering them so that each XCD receives one
 // contiguous range of logical ids (x fastest, then z, then y) keeps the
