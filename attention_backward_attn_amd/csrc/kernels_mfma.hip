@@ -30,6 +30,7 @@
 //   B[k][n]: lane holds n = l % 32, k = 8 (l / 32) + 0..7
 //   C[m][n]: lane holds n = l % 32, m = 8 (r / 4) + 4 (l / 32) + r % 4
 #include <algorithm>
+#include <type_traits>
 
 #include "kernels.h"
 #include "mfma_util.h"
@@ -413,7 +414,7 @@ __global__ __launch_bounds__(NT, 1) void k_dkdv(Params p, BwdArgs a, DkdvGrid gd
 // was last read before barrier t.
 // ---------------------------------------------------------------------------
 constexpr int NT2 = 512;
-constexpr int NB2 = 4;   // Q / dO tile buffers
+constexpr int NB2 = 5;   // Q / dO tile buffers
 
 template <int D>
 struct __attribute__((aligned(1024))) SmemDKDV2 {
@@ -421,7 +422,7 @@ struct __attribute__((aligned(1024))) SmemDKDV2 {
   unsigned char d[NB2][BQ * 2 * D];   // dO tile, swizzled (A of dP = dO V^T; tr B of dV += P^T dO)
   float lse[NB2][2 * BQ];             // LSE of the tile's rows (second half: padding)
   float dl[NB2][2 * BQ];              // delta of the tile's rows (second half: padding)
-  u16x8 px[2][4][2][64];              // P by tile parity, pair w % 4: [operand half][lane]
+  f32x4 px[2][4][4][64];              // P (fp32) by tile parity, pair w % 4: [4 values][lane]
 };
 
 // Staging of one 32-row Q / dO tile straight from global memory into LDS:
@@ -579,9 +580,6 @@ __global__ __launch_bounds__(NT2) void k_dkdv2(Params p, BwdArgs a, DkdvGrid gd)
 #pragma unroll
       for (int s = 0; s < NS; ++s) fB[s] = as_bf16x8(*(const u16x8*)(src + jc * rs + 16 * s + 8 * lg));
     }
-    f32x16 og[NC];   // dV (S wave) or dK (dP wave), columns 32 n + lane
-#pragma unroll
-    for (int n = 0; n < NC; ++n) og[n] = zero16();
     __syncthreads();  // readers of the previous unit's LDS tiles are done
     wait_vm_loads();
     if (n_it <= 0) continue;
@@ -608,7 +606,7 @@ __global__ __launch_bounds__(NT2) void k_dkdv2(Params p, BwdArgs a, DkdvGrid gd)
       ld.d_wrap = p.do_str[1] - nqb * ld.d_step;
       ld.l_wrap = (int64_t)p.Sq - (int64_t)nqb * BQ;
     }
-    int fr_i0 = ld.i0, fr_qb = ld.qb;
+    int fr_i0 = ld.i0, fr_qb = ld.qb;   // tile whose P the S wave forms next
     auto fr_next = [&]() {
       fr_i0 += BQ;
       if (++fr_qb == nqb) { fr_qb = 0; fr_i0 = lo_al; }
@@ -617,16 +615,30 @@ __global__ __launch_bounds__(NT2) void k_dkdv2(Params p, BwdArgs a, DkdvGrid gd)
       stg.issue(sm_base, buf, ld.q, ld.d, q_rb, d_rb, ld.l, ld.dl, min(Sq - ld.i0, BQ), l);
       ld.next();
     };
-    // Prologue: tiles 0, 1 and 2 in flight; 0 and 1 complete before the
-    // first barrier.
+    // Prologue: tiles 0..3 in flight; 0..2 complete before the first barrier.
     issue(0);
-    if (n_it > 1) issue(1);
-    if (n_it > 2) {
-      issue(2);
+#pragma unroll
+    for (int j = 1; j < NB2 - 2; ++j)
+      if (n_it > j) issue(j);
+    if (n_it > NB2 - 2) {
+      issue(NB2 - 2);
       wait_vm(stg.n_loads);
     } else {
       wait_vm(0);
     }
+    __syncthreads();
+    // Wave 0 turns the raw LSE / delta rows of a complete tile into
+    // LSE * log2(e) (+inf for a row without keys) and delta * scale, in place.
+    // Rows past the end hold zeros (P = 1 there, against zero Q / dO rows).
+    auto prep_rows = [&](int buf) {
+      if (w == 0) {
+        float* x = (l < BQ ? sm.lse[buf] : sm.dl[buf]) + (l & (BQ - 1));
+        const float v = *x;
+        *x = l < BQ ? (v == -INFINITY ? INFINITY : v * kLog2e) : v * scale;
+      }
+    };
+    prep_rows(0);
+    if (n_it > 1) prep_rows(1);
     __syncthreads();
 
     // Per-lane key window of the masked exponentials: key lane jg is allowed
@@ -637,138 +649,181 @@ __global__ __launch_bounds__(NT2) void k_dkdv2(Params p, BwdArgs a, DkdvGrid gd)
     if (!key_ok) { lo_l = 0x3fffffff; span = 0; }
     const int tb0 = jg - (int)msk.q_off - (int)msk.diag - 4 * lg - lo_l;
 
-    // A-operand tile of this wave (Q for the S wave, dO for the dP wave) and
-    // B-operand tile of its dV / dK products (dO, resp. Q), buffer `buf`
-    auto a_tile = [&](int buf) { return lds_addr(sw ? sm.q[buf] : sm.d[buf]) + a_lane; };
-    auto b_tile = [&](int buf) { return lds_addr(sw ? sm.d[buf] : sm.q[buf]) + t_lane; };
+    constexpr int TS = BQ * 2 * D;   // tile bytes
+    // LSE * log2(e) or delta * scale of the rows this lane holds in the accumulator
+    auto row_vals = [&](f32x4* x, const float* v) {
+#pragma unroll
+      for (int m = 0; m < 4; ++m) x[m] = *(const f32x4*)&v[8 * m + 4 * lg];
+    };
+    constexpr int EPS = 16 / NS;   // accumulator elements handled per chain step
+    constexpr int AHEAD = 2;       // chain steps whose operands are in flight
 
-    // S = Q K^T (S wave) or dP = dO V^T (dP wave) of the tile in buffer `buf`
-    f32x16 acc;
-    auto front_mm = [&](int buf) {
-      const unsigned int ab = a_tile(buf);
-      bf16x8 xa[NS];
+    // Each role runs its own copy of the loop, so that its accumulators never
+    // cross a branch.  Per query tile t (one barrier):
+    //   S wave:  dV += P(t)^T dO(t);  S(t + 2) = Q K^T;  P(t + 1) = exp2(S(t + 1) - LSE)
+    //   dP wave: dS(t) = P(t) (dP(t) - delta);  dP(t + 1) = dO V^T;  dK += dS(t)^T Q(t)
+    // The exponentials and dS arithmetic run between the products of the
+    // same wave; P(t + 1) (fp32) is published before barrier t + 1.  The
+    // loop is unrolled over the tile buffers, so every operand read is a
+    // per-lane register plus a constant offset.
+    auto run = [&](auto role) {
+      constexpr bool SW = decltype(role)::value;
+      f32x16 og[NC];   // dV (S wave) or dK (dP wave), columns 32 n + lane
 #pragma unroll
-      for (int s = 0; s < NS; ++s) xa[s] = lds_b128_at(ab ^ (32 * s));
-      acc = zero16();
+      for (int n = 0; n < NC; ++n) og[n] = zero16();
+      // operand read addresses in tile buffer 0
+      const unsigned int a_t0 = sm_base + (SW ? offsetof(SmemDKDV2<D>, q) : offsetof(SmemDKDV2<D>, d));
+      const unsigned int b_t0 = sm_base + (SW ? offsetof(SmemDKDV2<D>, d) : offsetof(SmemDKDV2<D>, q));
+      unsigned int ar[NS], br[NC];
 #pragma unroll
-      for (int s = 0; s < NS; ++s) acc = mfma(xa[s], fB[s], acc);
-    };
-    // LSE * log2(e) (S wave: of the next tile) or delta * scale (dP wave: of
-    // the current one) of the rows this lane holds in the accumulator.  Rows
-    // past the end read zeros: their Q / dO rows are zero as well, so they
-    // add nothing to dV or dK.  A row without keys (LSE = -inf) only occurs
-    // in masked tiles, where its P is zero by the mask.
-    f32x4 RV[4];
-    auto row_vals = [&](int buf) {
-      const float* v = sw ? sm.lse[buf] : sm.dl[buf];
-      const float c = sw ? kLog2e : scale;
+      for (int s = 0; s < NS; ++s) ar[s] = a_t0 + (a_lane ^ (32 * s));
 #pragma unroll
-      for (int m = 0; m < 4; ++m) RV[m] = *(const f32x4*)&v[8 * m + 4 * lg] * c;
-    };
-    // S wave: P of tile `fr`, published in P buffer `pbuf`
-    bf16x8 pa0, pa1;
-    auto front_p = [&](const f32x4* L4, int pbuf) {
-      const int i0 = fr_i0;
+      for (int n = 0; n < NC; ++n) br[n] = b_t0 + (t_lane ^ (64 * n));
+      // A of chain step s, and B of dV / dK product i (accumulator i % NC,
+      // tile rows 16 (i / NC) ...), in tile buffer j (a constant)
+      auto read_a = [&](int j, int s) { return lds_b128_at(ar[s] + j * TS); };
+      auto read_b = [&](int j, int i) {
+        const int n = i % NC, r0 = 16 * (i / NC);
+        // (tile buffers are 1 KB aligned: the XOR only touches address bits 5..7)
+        return cat44(lds_tr4_at(br[n] + j * TS + r0 * RB), lds_tr4_at((br[n] ^ 32) + j * TS + (r0 + 8) * RB));
+      };
+      auto chain = [&](int j) {   // S or dP of the tile in buffer j, in one go
+        bf16x8 xa[NS];
+#pragma unroll
+        for (int s = 0; s < NS; ++s) xa[s] = read_a(j, s);
+        f32x16 c = zero16();
+#pragma unroll
+        for (int s = 0; s < NS; ++s) c = mfma(xa[s], fB[s], c);
+        return c;
+      };
+      f32x16 acc = chain(0);   // S(0) / dP(0)
+      bf16x8 pa0, pa1;         // S wave: P of the current tile
       float pv[16];
-      if (i0 >= full_a && i0 + BQ - 1 <= full_c) {
+      // S wave: mask P of tile fr (in pv), keep it as operands, publish it
+      auto publish = [&](int pbuf) {
+        const int i0 = fr_i0;
+        if (!(i0 >= full_a && i0 + BQ - 1 <= full_c)) {
+          const int tb = tb0 - i0;
 #pragma unroll
-        for (int r = 0; r < 16; ++r)
-          pv[r] = __builtin_amdgcn_exp2f(fmaf(acc[r], scale_log2, -L4[r >> 2][r & 3]));
-      } else {
-        const int tb = tb0 - i0;
+          for (int r = 0; r < 16; ++r) {
+            const unsigned int tt = (unsigned int)(tb - (8 * (r >> 2) + (r & 3)));
+            pv[r] = tt <= (unsigned int)span ? pv[r] : 0.f;
+          }
+        }
+        pa0 = pack8(pv);
+        pa1 = pack8(pv + 8);
+#pragma unroll
+        for (int k = 0; k < 4; ++k)
+          sm.px[pbuf][pr][k][l] = f32x4{pv[4 * k], pv[4 * k + 1], pv[4 * k + 2], pv[4 * k + 3]};
+      };
+      if (SW) {
+        f32x4 L4[4];
+        row_vals(L4, sm.lse[0]);
+#pragma unroll
+        for (int r = 0; r < 16; ++r) pv[r] = __builtin_amdgcn_exp2f(fmaf(acc[r], scale_log2, -L4[r >> 2][r & 3]));
+        publish(0);
+        fr_next();
+        acc = chain(1);   // S(1) (stale when there is no tile 1; then unused)
+      }
+
+      // one tile: t the tile index, j = t % NB2 (a constant)
+      auto tile = [&](int t, auto jc) {
+        constexpr int j = decltype(jc)::value;
+        constexpr int j1 = (j + 1) % NB2, j2 = (j + 2) % NB2;
+        __syncthreads();  // P(t) published; tile t + 2 complete, its rows prepared; tile t - 1's buffer free
+        const bool more = t + NB2 - 1 < n_it;
+        if (more) issue((j + NB2 - 1) % NB2);
+        if (t + 2 < n_it) prep_rows(j2);   // complete since the barrier; first read after the next one
+        bf16x8 bq[NS], xa[NS];
+        f32x16 accn = zero16();
+        if (SW) {
+          // region: dV(t) products, S(t + 2) chain, exponentials of S(t + 1)
+          f32x4 L4[4];
+          row_vals(L4, sm.lse[j1]);
+#pragma unroll
+          for (int i = 0; i < AHEAD; ++i) { bq[i] = read_b(j, i); xa[i] = read_a(j2, i); }
+          __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+          for (int i = 0; i < NS; ++i) {
+            og[i % NC] = mfma(i < NC ? pa0 : pa1, bq[i], og[i % NC]);
+            accn = mfma(xa[i], fB[i], accn);
+#pragma unroll
+            for (int e = 0; e < EPS; ++e) {
+              const int r = EPS * i + e;
+              pv[r] = __builtin_amdgcn_exp2f(fmaf(acc[r], scale_log2, -L4[r >> 2][r & 3]));
+            }
+            if (i + AHEAD < NS) { bq[i + AHEAD] = read_b(j, i + AHEAD); xa[i + AHEAD] = read_a(j2, i + AHEAD); }
+            __builtin_amdgcn_sched_barrier(0);
+          }
+          // (unconditional, so the exponentials stay among the products; past
+          // the last tile it writes an unread P buffer)
+          publish((t + 1) & 1);
+          fr_next();
+        } else {
+          // region: dS(t) arithmetic, dP(t + 1) chain, dK(t) products
+          f32x4 D4[4], P4[4];
+          row_vals(D4, sm.dl[j]);
+#pragma unroll
+          for (int k = 0; k < 4; ++k) P4[k] = sm.px[t & 1][pr][k][l];
+#pragma unroll
+          for (int i = 0; i < AHEAD; ++i) { bq[i] = read_b(j, i); xa[i] = read_a(j1, i); }
+          __builtin_amdgcn_sched_barrier(0);
+          float dsv[16];
+          bf16x8 A0, A1;
+#pragma unroll
+          for (int i = 0; i < NS; ++i) {
+            accn = mfma(xa[i], fB[i], accn);
+            if (i >= NS / 2) og[(i - NS / 2) % NC] = mfma(A0, bq[i - NS / 2], og[(i - NS / 2) % NC]);
+#pragma unroll
+            for (int e = 0; e < EPS; ++e) {
+              const int r = EPS * i + e;
+              dsv[r] = P4[r >> 2][r & 3] * fmaf(acc[r], scale, -D4[r >> 2][r & 3]);
+            }
+            if (i == NS / 2 - 1) A0 = pack8(dsv);
+            if (i + AHEAD < NS) { bq[i + AHEAD] = read_b(j, i + AHEAD); xa[i + AHEAD] = read_a(j1, i + AHEAD); }
+            __builtin_amdgcn_sched_barrier(0);
+          }
+          A1 = pack8(dsv + 8);
+#pragma unroll
+          for (int i = NS / 2; i < NS; ++i) og[i % NC] = mfma(A1, bq[i], og[i % NC]);
+        }
+        acc = accn;
+        // tile t + 3 complete before the next barrier (tile t + 4 may stay in flight)
+        wait_vm(more ? stg.n_loads : 0);
+      };
+      static_assert(NB2 == 5, "tile loop unrolled over five buffers");
+      for (int t0 = 0; t0 < n_it; t0 += NB2) {
+        tile(t0, std::integral_constant<int, 0>{});
+        if (t0 + 1 >= n_it) break;
+        tile(t0 + 1, std::integral_constant<int, 1>{});
+        if (t0 + 2 >= n_it) break;
+        tile(t0 + 2, std::integral_constant<int, 2>{});
+        if (t0 + 3 >= n_it) break;
+        tile(t0 + 3, std::integral_constant<int, 3>{});
+        if (t0 + 4 >= n_it) break;
+        tile(t0 + 4, std::integral_constant<int, 4>{});
+      }
+
+      // Epilogue: dV (S wave) or dK (dP wave, scaled through dS) of this pair's keys.
+      float* op = SW ? a.dv + sv.k_off(p.dv_str, b) + hk * p.dv_str[1]
+                     : a.dk + sv.k_off(p.dk_str, b) + hk * p.dk_str[1];
+      const int64_t os = SW ? p.dv_str[2] : p.dk_str[2];
+#pragma unroll
+      for (int n = 0; n < NC; ++n) {
 #pragma unroll
         for (int r = 0; r < 16; ++r) {
-          const unsigned int tt = (unsigned int)(tb - (8 * (r >> 2) + (r & 3)));
-          const float ex = __builtin_amdgcn_exp2f(fmaf(acc[r], scale_log2, -L4[r >> 2][r & 3]));
-          pv[r] = tt <= (unsigned int)span ? ex : 0.f;
+          const int64_t j = kw + crow(r, lg);
+          if (j < Sk) {
+            float* po = op + j * os + 32 * n + lr;
+            if (out_mode == kAtomicAdd) atomic_add_f32(po, og[n][r]);
+            else if (out_mode == kAddInto) *po += og[n][r];
+            else *po = og[n][r];
+          }
         }
       }
-      pa0 = pack8(pv);
-      pa1 = pack8(pv + 8);
-      sm.px[pbuf][pr][0][l] = __builtin_bit_cast(u16x8, pa0);
-      sm.px[pbuf][pr][1][l] = __builtin_bit_cast(u16x8, pa1);
     };
-    front_mm(0);
-    row_vals(0);
-    if (sw) front_p(RV, 0);
-    fr_next();
-
-    for (int t = 0; t < n_it; ++t) {
-      const int buf = t % NB2, nbuf = (t + 1) % NB2;
-      __syncthreads();  // P(t) published; tile t + 1 complete; tile t - 1's buffer free
-      // the loads of tile t + 3, into tile t - 1's buffer
-      const bool more = t + 3 < n_it;
-      if (more) issue((t + 3) % NB2);
-      // S wave: dV += P(t)^T dO(t).  dP wave: dS(t) = P(t) (dP(t) - delta),
-      // pre-multiplied by the softmax scale, and dK += dS(t)^T Q(t).  One
-      // product loop for both, so the accumulators keep their registers.
-      bf16x8 A0 = pa0, A1 = pa1;
-      if (!sw) {
-        const u16x8 p0 = sm.px[t & 1][pr][0][l], p1 = sm.px[t & 1][pr][1][l];
-        float dsv[16];
-#pragma unroll
-        for (int r = 0; r < 8; ++r) {
-          dsv[r] = bf16_to_f32(p0[r]) * fmaf(acc[r], scale, -RV[r >> 2][r & 3]);
-          dsv[r + 8] = bf16_to_f32(p1[r]) * fmaf(acc[r + 8], scale, -RV[(r + 8) >> 2][r & 3]);
-        }
-        A0 = pack8(dsv);
-        A1 = pack8(dsv + 8);
-      }
-      // One scheduling region: the products of tile t, S / dP of tile t + 1
-      // and the LSE / delta rows of tile t + 1.  Every operand read is issued
-      // ahead of the product that uses it; the dependent S / dP chain
-      // alternates with the independent dV / dK accumulators.  On the last
-      // tile the S / dP half reads a stale buffer and its result is dropped.
-      {
-        const unsigned int bt = b_tile(buf), ab = a_tile(nbuf);
-        static_assert(2 * NC == NS, "one dV / dK product per S / dP product");
-        constexpr int AHEAD = 3;   // product pairs whose operands are in flight
-        bf16x8 bq[NS], xa[NS];
-        // product pair i: dV / dK accumulator i % NC with rows 16 (i / NC) of
-        // the tile, and step i of the S / dP chain
-        auto read_pair = [&](int i) {
-          const int n = i % NC, r0 = 16 * (i / NC);
-          const unsigned int x0 = bt ^ (64 * n), x1 = bt ^ (64 * n + 32);
-          bq[i] = cat44(lds_tr4_at(x0 + r0 * RB), lds_tr4_at(x1 + (r0 + 8) * RB));
-          xa[i] = lds_b128_at(ab ^ (32 * i));
-        };
-#pragma unroll
-        for (int i = 0; i < AHEAD; ++i) read_pair(i);
-        acc = zero16();
-        __builtin_amdgcn_sched_barrier(0);
-#pragma unroll
-        for (int i = 0; i < NS; ++i) {
-          og[i % NC] = mfma(i < NC ? A0 : A1, bq[i], og[i % NC]);
-          acc = mfma(xa[i], fB[i], acc);
-          if (i + AHEAD < NS) read_pair(i + AHEAD);
-          if (i == NS - 3) row_vals(nbuf);
-          __builtin_amdgcn_sched_barrier(0);
-        }
-      }
-      if (sw && t + 1 < n_it) front_p(RV, (t + 1) & 1);
-      fr_next();
-      // tile t + 2 complete before the next barrier (tile t + 3's loads may
-      // stay in flight)
-      wait_vm(more ? stg.n_loads : 0);
-    }
-
-    // Epilogue: dV (S wave) or dK (dP wave, scaled through dS) of this pair's keys.
-    float* op = sw ? a.dv + sv.k_off(p.dv_str, b) + hk * p.dv_str[1]
-                   : a.dk + sv.k_off(p.dk_str, b) + hk * p.dk_str[1];
-    const int64_t os = sw ? p.dv_str[2] : p.dk_str[2];
-#pragma unroll
-    for (int n = 0; n < NC; ++n) {
-#pragma unroll
-      for (int r = 0; r < 16; ++r) {
-        const int64_t j = kw + crow(r, lg);
-        if (j < Sk) {
-          float* po = op + j * os + 32 * n + lr;
-          if (out_mode == kAtomicAdd) atomic_add_f32(po, og[n][r]);
-          else if (out_mode == kAddInto) *po += og[n][r];
-          else *po = og[n][r];
-        }
-      }
-    }
+    if (sw) run(std::true_type{});
+    else run(std::false_type{});
   }
 }
 
