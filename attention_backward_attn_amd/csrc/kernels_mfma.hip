@@ -1126,13 +1126,248 @@ __global__ __launch_bounds__(NT, 2) void k_dq(Params p, BwdArgs a) {
   }
 }
 
+// ---------------------------------------------------------------------------
+// Kernel k_dq2 (dQ without a bias): one workgroup of four waves per
+// (128-row query block, query head, batch), two workgroups per CU.  Wave w
+// owns rows [32 w, 32 w + 32) and keeps Q and dO as B-operand fragments in
+// registers.  The 32-key K / V tiles come straight from global memory into
+// four LDS buffers (XOR-swizzled, one copy per tile serving the row reads of
+// S^T = K Q^T, dP^T = V dO^T and the transposing reads of dQ += dS K), two
+// tiles ahead of use.  Per key tile t (one barrier): the S^T / dP^T chains
+// of tile t + 1 run between the exponentials and dS arithmetic of tile t,
+// then dS(t) K(t) goes into dQ; the loop is unrolled over the buffers so
+// every operand read is a lane register plus a constant offset.
+// ---------------------------------------------------------------------------
+constexpr int NBQ = 4;   // K / V tile buffers (k_dq2)
+
+template <int D>
+struct __attribute__((aligned(1024))) SmemDQ2 {
+  unsigned char k[NBQ][BK3 * 2 * D];   // K tile, swizzled
+  unsigned char v[NBQ][BK3 * 2 * D];   // V tile, swizzled
+};
+
+template <int D>
+__global__ __launch_bounds__(NT, 2) void k_dq2(Params p, BwdArgs a) {
+  constexpr int NS = D / 16;   // k-steps over the head dim
+  constexpr int NC = D / 32;   // 32-column blocks of dQ
+  constexpr int RB = Swz<D>::RB, CR = Swz<D>::CR;
+  constexpr int TS = BK3 * 2 * D;   // tile bytes
+  constexpr int PER_T = BK3 * CR / 64;   // 1 KB loads per tile
+  constexpr int NI = 2 * PER_T / 4;      // loads per wave per K + V tile pair
+  static_assert(NI >= 1 && PER_T % NI == 0, "loads per wave");
+  __shared__ SmemDQ2<D> sm;
+
+  const int tid = threadIdx.x, l = tid & 63, lr = l & 31, lg = l >> 5;
+  const int w = __builtin_amdgcn_readfirstlane(tid >> 6);   // wave-uniform
+  const BlockXYZ blk = xcd_block();
+  // under a causal mask later row blocks see more keys: deal them first
+  const bool heavy_last = p.mask.kind != kMaskNone && p.mask.wl < 0;
+  const int i0 = (heavy_last ? (int)gridDim.x - 1 - blk.x : blk.x) * BQ3;
+  const int h = blk.y, b = blk.z, g = h / p.G;
+  const SeqView sv = seq_view(p, b);   // this batch entry (or packed sequence)
+  const Mask& msk = sv.mask;
+  const int Sq = sv.Sq, Sk = sv.Sk;
+  if (i0 >= Sq) return;   // past this sequence's rows (uniform across the workgroup)
+  const int irow = i0 + 32 * w + lr;           // this lane's query row
+  const float scale = p.scale, scale_log2 = p.scale * kLog2e;
+
+  const unsigned short* q = (const unsigned short*)a.q + sv.q_off(p.q_str, b) + h * p.q_str[1];
+  const unsigned short* dout = (const unsigned short*)a.dout + sv.q_off(p.do_str, b) + h * p.do_str[1];
+  const unsigned short* kp = (const unsigned short*)a.k + sv.k_off(p.k_str, b) + g * p.k_str[1];
+  const unsigned short* vp = (const unsigned short*)a.v + sv.k_off(p.v_str, b) + g * p.v_str[1];
+
+  bf16x8 qB[NS], doB[NS];
+  {
+    const int64_t ic = min(irow, Sq - 1);
+#pragma unroll
+    for (int s = 0; s < NS; ++s) {
+      qB[s] = as_bf16x8(*(const u16x8*)(q + ic * p.q_str[2] + 16 * s + 8 * lg));
+      doB[s] = as_bf16x8(*(const u16x8*)(dout + ic * p.do_str[2] + 16 * s + 8 * lg));
+    }
+  }
+  float lse2 = INFINITY, dls = 0.f;
+  if (irow < Sq) {
+    const float lv = a.lse[((int64_t)b * p.Hq + h) * p.Sq + irow];
+    lse2 = (lv == -INFINITY) ? INFINITY : lv * kLog2e;
+    dls = a.delta[((int64_t)b * p.Hq + h) * p.Sq + irow] * scale;
+  }
+  wait_vm_loads();
+
+  // key tiles: the sink tiles [0, a1) and the band tiles [a2, a3)
+  int64_t s_hi, b_lo, b_hi;
+  const int i1 = min(i0 + BQ3, Sq);
+  msk.keys_for_rows(i0, i1, Sk, &s_hi, &b_lo, &b_hi);
+  const int a1 = (int)((s_hi + BK3 - 1) / BK3);
+  int a2 = (int)(b_lo / BK3);
+  const int a3 = b_hi > b_lo ? (int)((b_hi + BK3 - 1) / BK3) : a2;
+  if (a2 < a1) a2 = a1;
+  const int n1 = a1, n2 = a3 > a2 ? a3 - a2 : 0;
+  const int n_it = n1 + n2;
+  auto tile_of = [&](int it) { return BK3 * (it < n1 ? it : a2 + (it - n1)); };
+  // this wave's rows: a tile [j0, j0 + 32) is full when every key is
+  // allowed for all 32 rows
+  const int wr0 = i0 + 32 * w;
+  // per-lane key window of the masked tiles: key j is allowed for this
+  // lane's row when  j + k_off - (irow + q_off) - diag  lies in [lo_l, lo_l + span]
+  const bool no_mask = msk.kind == kMaskNone;
+  int lo_l = msk.wl < 0 ? -0x3fffffff : -msk.wl, span = msk.wr - lo_l;
+  if (no_mask) { lo_l = -0x3fffffff; span = 0x7ffffffe; }
+  const int tq = (int)msk.k_off - (irow + (int)msk.q_off) - (int)msk.diag + 4 * lg - lo_l;
+  const int sink_lim = (int)min<int64_t>(max<int64_t>(msk.n_sink - msk.k_off, 0), 0x3fffffff);   // keys below are sinks
+
+  // staging: wave w issues NI 1 KB loads of the K (waves 0, 1) or V tile
+  const int k_rb = 2 * (int)p.k_str[2], v_rb = 2 * (int)p.v_str[2];
+  const bool ld_v = w * NI >= PER_T;
+  int voff[NI];
+  unsigned int dst0[NI];
+  const unsigned int sm_base = lds_addr(&sm);
+#pragma unroll
+  for (int k = 0; k < NI; ++k) {
+    const int slot = (w * NI + k) % PER_T;
+    const int row = (64 * slot + l) / CR;
+    voff[k] = row * (ld_v ? v_rb : k_rb) + 16 * ((l % CR) ^ Swz<D>::f(row));
+    dst0[k] = sm_base + (ld_v ? offsetof(SmemDQ2<D>, v) : offsetof(SmemDQ2<D>, k)) + 1024 * slot;
+  }
+  auto issue = [&](int it, int buf) {
+    const int j0 = tile_of(it);
+    const int keys = min(Sk - j0, BK3);
+    const __amdgpu_buffer_rsrc_t rs = ld_v ? buf_rsrc(vp + (int64_t)j0 * p.v_str[2], keys * v_rb)
+                                           : buf_rsrc(kp + (int64_t)j0 * p.k_str[2], keys * k_rb);
+#pragma unroll
+    for (int k = 0; k < NI; ++k) lds_dma16(rs, __builtin_amdgcn_readfirstlane(dst0[k] + buf * TS), voff[k]);
+  };
+
+  f32x16 dq[NC];
+#pragma unroll
+  for (int n = 0; n < NC; ++n) dq[n] = zero16();
+
+  if (n_it > 0) {
+    // K tile buffer 3 zeroed (read by the zero dQ products ahead of tile 0)
+#pragma unroll
+    for (int k = 0; k < TS / (16 * NT); ++k) *(u16x8*)&sm.k[NBQ - 1][16 * (tid + NT * k)] = u16x8{0, 0, 0, 0, 0, 0, 0, 0};
+    // tiles 0 and 1 in flight; 0 complete before the first barrier
+    issue(0, 0);
+    if (n_it > 1) {
+      issue(1, 1);
+      wait_vm(NI);
+    } else {
+      wait_vm(0);
+    }
+
+    // operand read addresses in tile buffer 0
+    const int a_lane = Swz<D>::a_lane(l), t_lane = Swz<D>::t_lane(l);
+    const unsigned int k_t0 = sm_base + offsetof(SmemDQ2<D>, k), v_t0 = sm_base + offsetof(SmemDQ2<D>, v);
+    unsigned int br[NC];
+#pragma unroll
+    for (int n = 0; n < NC; ++n) br[n] = k_t0 + (t_lane ^ (64 * n));
+    const unsigned int ka = k_t0 + a_lane, va = v_t0 + a_lane;
+    // K / V rows of chain step s and K^T of dQ product i in tile buffer j (a
+    // constant; the buffers are 1 KB aligned, so the XOR stays in the row)
+    auto read_k = [&](int j, int s) { return lds_b128_at((ka ^ (32 * s)) + j * TS); };
+    auto read_v = [&](int j, int s) { return lds_b128_at((va ^ (32 * s)) + j * TS); };
+    auto read_kt = [&](int j, int i) {
+      const int n = i % NC, r0 = 16 * (i / NC);
+      return cat44(lds_tr4_at(br[n] + j * TS + r0 * RB), lds_tr4_at((br[n] ^ 32) + j * TS + (r0 + 8) * RB));
+    };
+    constexpr int AHEAD = 2;
+    // dS of the previous tile (dQ operands); before the first tile zeros,
+    // against the K tile buffer 3 zeroed in the prologue
+    bf16x8 A0 = as_bf16x8(u16x8{0, 0, 0, 0, 0, 0, 0, 0}), A1 = A0;
+
+    // tile t in buffer j: the S^T / dP^T chains of tile t among the dQ
+    // products of tile t - 1 (when DQ), then the exponentials and dS
+    // arithmetic of tile t
+    auto tile = [&](int t, int j, bool full) {
+      const int jp = (j + NBQ - 1) % NBQ;
+      constexpr bool DQ = true;
+      bf16x8 xk[NS], xv[NS], bq[NS];
+      f32x16 sacc = zero16(), pacc = zero16();
+#pragma unroll
+      for (int i = 0; i < AHEAD; ++i) {
+        xk[i] = read_k(j, i);
+        xv[i] = read_v(j, i);
+        if (DQ) bq[i] = read_kt(jp, i);
+      }
+      __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+      for (int i = 0; i < NS; ++i) {
+        sacc = mfma(xk[i], qB[i], sacc);
+        if (DQ) dq[i % NC] = mfma(i < NC ? A0 : A1, bq[i], dq[i % NC]);
+        pacc = mfma(xv[i], doB[i], pacc);
+        if (i + AHEAD < NS) {
+          xk[i + AHEAD] = read_k(j, i + AHEAD);
+          xv[i + AHEAD] = read_v(j, i + AHEAD);
+          if (DQ) bq[i + AHEAD] = read_kt(jp, i + AHEAD);
+        }
+        __builtin_amdgcn_sched_barrier(0);
+      }
+      const int j0 = tile_of(t);
+      const int tb = tq + j0;   // window offset of key j0 + 4 lg for this lane's row
+      float pp[16], dsv[16];
+#pragma unroll
+      for (int r = 0; r < 16; ++r) pp[r] = __builtin_amdgcn_exp2f(fmaf(sacc[r], scale_log2, -lse2));
+      if (!full) {   // (the branch touches P only)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+          const int c = 8 * (r >> 2) + (r & 3);
+          const int jj = j0 + 4 * lg + c;
+          const bool ok = (jj < Sk) & (((unsigned int)(tb + c) <= (unsigned int)span) | (jj < sink_lim));
+          pp[r] = ok ? pp[r] : 0.f;
+        }
+      }
+#pragma unroll
+      for (int r = 0; r < 16; ++r) dsv[r] = pp[r] * fmaf(pacc[r], scale, -dls);
+      A0 = pack8(dsv);
+      A1 = pack8(dsv + 8);
+    };
+    auto step = [&](int t) {
+      const int j = t % NBQ;
+      __syncthreads();  // tile t complete; tile t - 2's buffer free
+      const bool more = t + 2 < n_it;
+      if (more) issue(t + 2, (j + 2) % NBQ);
+      const int j0 = tile_of(t);
+      const bool full = (j0 + BK3 <= Sk) && msk.tile_full(wr0, wr0 + 32, j0, j0 + BK3);
+      tile(t, j, full);
+      // tile t + 1 complete before the next barrier (tile t + 2 may stay in flight)
+      wait_vm(more ? NI : 0);
+    };
+    for (int t = 0; t < n_it; ++t) step(t);
+    // the dQ products of the last tile
+    {
+      const unsigned int jb = ((n_it - 1) % NBQ) * TS;
+      bf16x8 bq[NS];
+#pragma unroll
+      for (int i = 0; i < NS; ++i) {
+        const int n = i % NC, r0 = 16 * (i / NC);
+        bq[i] = cat44(lds_tr4_at(br[n] + jb + r0 * RB), lds_tr4_at((br[n] ^ 32) + jb + (r0 + 8) * RB));
+      }
+#pragma unroll
+      for (int i = 0; i < NS; ++i) dq[i % NC] = mfma(i < NC ? A0 : A1, bq[i], dq[i % NC]);
+    }
+  }
+
+  // dQ rows i0 + 32 w + crow(r, lg), columns 32 n + lr (already scaled through dS).
+  float* dqp = a.dq + sv.q_off(p.dq_str, b) + h * p.dq_str[1];
+#pragma unroll
+  for (int n = 0; n < NC; ++n) {
+#pragma unroll
+    for (int r = 0; r < 16; ++r) {
+      const int64_t i = i0 + 32 * w + crow(r, lg);
+      if (i < Sq) {
+        float* dst = dqp + i * p.dq_str[2] + 32 * n + lr;
+        *dst = a.accumulate_dq ? *dst + dq[n][r] : dq[n][r];
+      }
+    }
+  }
+}
+
 template <int D>
 hipError_t launch_dq(const Params& p, const BwdArgs& a, hipStream_t st) {
   const dim3 grid((p.Sq + BQ3 - 1) / BQ3, p.Hq, p.B);
   if (a.bias)
     hipLaunchKernelGGL((k_dq<D, true>), grid, dim3(NT), 0, st, p, a);
   else
-    hipLaunchKernelGGL((k_dq<D, false>), grid, dim3(NT), 0, st, p, a);
+    hipLaunchKernelGGL((k_dq2<D>), grid, dim3(NT), 0, st, p, a);
   return hipGetLastError();
 }
 
