@@ -1331,7 +1331,70 @@ __global__ __launch_bounds__(NT, 2) void k_dq2(Params p, BwdArgs a) {
       // tile t + 1 complete before the next barrier (tile t + 2 may stay in flight)
       wait_vm(more ? NI : 0);
     };
-    for (int t = 0; t < n_it; ++t) step(t);
+    auto tilec = [&](int t, auto jc, bool full) {
+      constexpr int j = decltype(jc)::value, jp = (j + NBQ - 1) % NBQ;
+      constexpr bool DQ = true;
+      bf16x8 xk[NS], xv[NS], bq[NS];
+      f32x16 sacc = zero16(), pacc = zero16();
+#pragma unroll
+      for (int i = 0; i < AHEAD; ++i) {
+        xk[i] = read_k(j, i);
+        xv[i] = read_v(j, i);
+        if (DQ) bq[i] = read_kt(jp, i);
+      }
+      __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+      for (int i = 0; i < NS; ++i) {
+        sacc = mfma(xk[i], qB[i], sacc);
+        if (DQ) dq[i % NC] = mfma(i < NC ? A0 : A1, bq[i], dq[i % NC]);
+        pacc = mfma(xv[i], doB[i], pacc);
+        if (i + AHEAD < NS) {
+          xk[i + AHEAD] = read_k(j, i + AHEAD);
+          xv[i + AHEAD] = read_v(j, i + AHEAD);
+          if (DQ) bq[i + AHEAD] = read_kt(jp, i + AHEAD);
+        }
+        __builtin_amdgcn_sched_barrier(0);
+      }
+      const int j0 = tile_of(t);
+      const int tb = tq + j0;   // window offset of key j0 + 4 lg for this lane's row
+      float pp[16], dsv[16];
+#pragma unroll
+      for (int r = 0; r < 16; ++r) pp[r] = __builtin_amdgcn_exp2f(fmaf(sacc[r], scale_log2, -lse2));
+      if (!full) {   // (the branch touches P only)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+          const int c = 8 * (r >> 2) + (r & 3);
+          const int jj = j0 + 4 * lg + c;
+          const bool ok = (jj < Sk) & (((unsigned int)(tb + c) <= (unsigned int)span) | (jj < sink_lim));
+          pp[r] = ok ? pp[r] : 0.f;
+        }
+      }
+#pragma unroll
+      for (int r = 0; r < 16; ++r) dsv[r] = pp[r] * fmaf(pacc[r], scale, -dls);
+      A0 = pack8(dsv);
+      A1 = pack8(dsv + 8);
+    };
+    auto stepc = [&](int t, auto jc) {
+      constexpr int j = decltype(jc)::value;
+      __syncthreads();  // tile t complete; tile t - 2's buffer free
+      const bool more = t + 2 < n_it;
+      if (more) issue(t + 2, (j + 2) % NBQ);
+      const int j0 = tile_of(t);
+      const bool full = (j0 + BK3 <= Sk) && msk.tile_full(wr0, wr0 + 32, j0, j0 + BK3);
+      tilec(t, jc, full);
+      // tile t + 1 complete before the next barrier (tile t + 2 may stay in flight)
+      wait_vm(more ? NI : 0);
+    };
+    // main loop unrolled over the four buffers (constant read offsets), then
+    // the remaining tiles
+    int t = 0;
+    for (; t + NBQ <= n_it; t += NBQ) {
+      stepc(t, std::integral_constant<int, 0>{});
+      stepc(t + 1, std::integral_constant<int, 1>{});
+      stepc(t + 2, std::integral_constant<int, 2>{});
+      stepc(t + 3, std::integral_constant<int, 3>{});
+    }
+    for (; t < n_it; ++t) step(t);
     // the dQ products of the last tile
     {
       const unsigned int jb = ((n_it - 1) % NBQ) * TS;
