@@ -1214,13 +1214,21 @@ __global__ __launch_bounds__(NT, 2) void k_dq2(Params p, BwdArgs a) {
   if (no_mask) { lo_l = -0x3fffffff; span = 0x7ffffffe; }
   const int tq = (int)msk.k_off - (irow + (int)msk.q_off) - (int)msk.diag + 4 * lg - lo_l;
   const int sink_lim = (int)min<int64_t>(max<int64_t>(msk.n_sink - msk.k_off, 0), 0x3fffffff);   // keys below are sinks
+  // tile [j0, j0 + 32) full for this wave's 32 rows: every key inside the
+  // problem and allowed for every row (all sinks, or inside the band)
+  auto clamp_i = [](int64_t x) { return (int)max<int64_t>(min<int64_t>(x, 0x3fffffff), -0x3fffffff); };
+  const int64_t band = (int64_t)wr0 + msk.q_off + msk.diag - msk.k_off;
+  const int fl_hi = no_mask ? 0x3fffffff : clamp_i(band + msk.wr - 31);
+  const int fl_lo = (no_mask || msk.wl < 0) ? -0x3fffffff : clamp_i(band + 31 - msk.wl);
+  const int fl_sink = no_mask ? -0x3fffffff : clamp_i((int64_t)msk.n_sink - 31 - msk.k_off);
+  auto tile_full = [&](int j0) { return (j0 + BK3 <= Sk) & ((j0 < fl_sink) | ((j0 <= fl_hi) & (j0 >= fl_lo))); };
 
   // staging: wave w issues NI 1 KB loads of the K (waves 0, 1) or V tile
   const int k_rb = 2 * (int)p.k_str[2], v_rb = 2 * (int)p.v_str[2];
   const bool ld_v = w * NI >= PER_T;
   int voff[NI];
   unsigned int dst0[NI];
-  const unsigned int sm_base = lds_addr(&sm);
+  const unsigned int sm_base = __builtin_amdgcn_readfirstlane(lds_addr(&sm));
 #pragma unroll
   for (int k = 0; k < NI; ++k) {
     const int slot = (w * NI + k) % PER_T;
@@ -1325,42 +1333,50 @@ __global__ __launch_bounds__(NT, 2) void k_dq2(Params p, BwdArgs a) {
       __syncthreads();  // tile t complete; tile t - 2's buffer free
       const bool more = t + 2 < n_it;
       if (more) issue(t + 2, (j + 2) % NBQ);
-      const int j0 = tile_of(t);
-      const bool full = (j0 + BK3 <= Sk) && msk.tile_full(wr0, wr0 + 32, j0, j0 + BK3);
-      tile(t, j, full);
+      tile(t, j, tile_full(tile_of(t)));
       // tile t + 1 complete before the next barrier (tile t + 2 may stay in flight)
       wait_vm(more ? NI : 0);
     };
     auto tilec = [&](int t, auto jc, bool full) {
       constexpr int j = decltype(jc)::value, jp = (j + NBQ - 1) % NBQ;
-      constexpr bool DQ = true;
-      bf16x8 xk[NS], xv[NS], bq[NS];
+      // region 1: the S^T / dP^T chains of tile t (two independent chains)
       f32x16 sacc = zero16(), pacc = zero16();
+      {
+        bf16x8 xk[NS], xv[NS];
 #pragma unroll
-      for (int i = 0; i < AHEAD; ++i) {
-        xk[i] = read_k(j, i);
-        xv[i] = read_v(j, i);
-        if (DQ) bq[i] = read_kt(jp, i);
-      }
-      __builtin_amdgcn_sched_barrier(0);
-#pragma unroll
-      for (int i = 0; i < NS; ++i) {
-        sacc = mfma(xk[i], qB[i], sacc);
-        if (DQ) dq[i % NC] = mfma(i < NC ? A0 : A1, bq[i], dq[i % NC]);
-        pacc = mfma(xv[i], doB[i], pacc);
-        if (i + AHEAD < NS) {
-          xk[i + AHEAD] = read_k(j, i + AHEAD);
-          xv[i + AHEAD] = read_v(j, i + AHEAD);
-          if (DQ) bq[i + AHEAD] = read_kt(jp, i + AHEAD);
-        }
+        for (int i = 0; i < AHEAD; ++i) { xk[i] = read_k(j, i); xv[i] = read_v(j, i); }
         __builtin_amdgcn_sched_barrier(0);
-      }
-      const int j0 = tile_of(t);
-      const int tb = tq + j0;   // window offset of key j0 + 4 lg for this lane's row
-      float pp[16], dsv[16];
 #pragma unroll
-      for (int r = 0; r < 16; ++r) pp[r] = __builtin_amdgcn_exp2f(fmaf(sacc[r], scale_log2, -lse2));
+        for (int i = 0; i < NS; ++i) {
+          sacc = mfma(xk[i], qB[i], sacc);
+          pacc = mfma(xv[i], doB[i], pacc);
+          if (i + AHEAD < NS) { xk[i + AHEAD] = read_k(j, i + AHEAD); xv[i + AHEAD] = read_v(j, i + AHEAD); }
+          __builtin_amdgcn_sched_barrier(0);
+        }
+      }
+      // region 2: the dQ products of tile t - 1 among the exponentials of tile t
+      float pp[16], dsv[16];
+      {
+        constexpr int EPS = 16 / NS;
+        bf16x8 bq[NS];
+#pragma unroll
+        for (int i = 0; i < AHEAD; ++i) bq[i] = read_kt(jp, i);
+        __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+        for (int i = 0; i < NS; ++i) {
+          dq[i % NC] = mfma(i < NC ? A0 : A1, bq[i], dq[i % NC]);
+#pragma unroll
+          for (int e = 0; e < EPS; ++e) {
+            const int r = EPS * i + e;
+            pp[r] = __builtin_amdgcn_exp2f(fmaf(sacc[r], scale_log2, -lse2));
+          }
+          if (i + AHEAD < NS) bq[i + AHEAD] = read_kt(jp, i + AHEAD);
+          __builtin_amdgcn_sched_barrier(0);
+        }
+      }
       if (!full) {   // (the branch touches P only)
+        const int j0 = tile_of(t);
+        const int tb = tq + j0;   // window offset of key j0 + 4 lg for this lane's row
 #pragma unroll
         for (int r = 0; r < 16; ++r) {
           const int c = 8 * (r >> 2) + (r & 3);
@@ -1379,9 +1395,7 @@ __global__ __launch_bounds__(NT, 2) void k_dq2(Params p, BwdArgs a) {
       __syncthreads();  // tile t complete; tile t - 2's buffer free
       const bool more = t + 2 < n_it;
       if (more) issue(t + 2, (j + 2) % NBQ);
-      const int j0 = tile_of(t);
-      const bool full = (j0 + BK3 <= Sk) && msk.tile_full(wr0, wr0 + 32, j0, j0 + BK3);
-      tilec(t, jc, full);
+      tilec(t, jc, tile_full(tile_of(t)));
       // tile t + 1 complete before the next barrier (tile t + 2 may stay in flight)
       wait_vm(more ? NI : 0);
     };
