@@ -271,7 +271,7 @@ def main():
         "clock_settle": {"ms": args.settle_ms, "steps": n_settle},
         "roofline": {"bound": "mfma", "achieved": round(achieved, 2), "peak": PEAK_BF16_TFLOPS,
                      "unit": "TFLOP/s", "frac": round(achieved / PEAK_BF16_TFLOPS, 4),
-                     "traffic": traffic_record(kernel_key), "kernel": "attn_bwd (k_dkdv2/k_dkdv + k_dq)",
+                     "traffic": traffic_record(kernel_key), "kernel": "attn_bwd (k_dkdv2/k_dkdv + k_dq2/k_dq)",
                      "kernel_ms_mean": round(main_ms, 4), "kernel_ms_median": round(main_med, 4)},
     }
     if not args.no_extras:
