@@ -1159,7 +1159,7 @@ __global__ __launch_bounds__(NT, 2) void k_dq2(Params p, BwdArgs a) {
 
   const int tid = threadIdx.x, l = tid & 63, lr = l & 31, lg = l >> 5;
   const int w = __builtin_amdgcn_readfirstlane(tid >> 6);   // wave-uniform
-  const BlockXYZ blk = xcd_block();
+  const BlockXYZ blk = xcd_block_xmajor();
   // under a causal mask later row blocks see more keys: deal them first
   const bool heavy_last = p.mask.kind != kMaskNone && p.mask.wl < 0;
   const int i0 = (heavy_last ? (int)gridDim.x - 1 - blk.x : blk.x) * BQ3;

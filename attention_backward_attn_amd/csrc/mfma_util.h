@@ -197,6 +197,20 @@ __device__ inline BlockXYZ xcd_block() {
   return {L - zy * nx, zy / nz, zy % nz};
 }
 
+// As xcd_block, for grids whose x index ranks the blocks by work (heaviest
+// first): when the (y, z) units divide evenly over the XCDs, XCD k takes
+// units [k U / 8, (k + 1) U / 8) (their K / V stay in its L2) and walks them
+// x-major, so every XCD starts its heaviest blocks first.
+__device__ inline BlockXYZ xcd_block_xmajor() {
+  const int nx = gridDim.x, ny = gridDim.y, nz = gridDim.z;
+  const int U = ny * nz;
+  if (U % 8 != 0) return xcd_block();
+  const int id = blockIdx.x + nx * (blockIdx.y + ny * blockIdx.z);
+  const int k = id & 7, i = id >> 3, per = U / 8;
+  const int unit = k * per + i % per;
+  return {i / per, unit / nz, unit % nz};
+}
+
 // Raw buffer resource over [base, base + bytes): a load at an offset past the
 // end returns zero without touching memory, so ragged tiles need no clamping.
 __device__ inline __amdgpu_buffer_rsrc_t buf_rsrc(const void* base, int bytes) {
