@@ -15,6 +15,7 @@ struct FwdArgs {
   const float* sinks;  // nullable [Hq]
   void* o;
   float* lse;
+  int xmajor;           // set by the launcher: walk row blocks heaviest first per XCD
 };
 
 struct BwdArgs {
@@ -32,7 +33,13 @@ struct BwdArgs {
   int accumulate_dq;    // add into dq instead of overwriting
   int deterministic;
   int accumulate_dkdv;  // add into dk / dv instead of overwriting
+  int xmajor;           // set by the launcher: walk row blocks heaviest first per XCD
 };
+
+// Whether the query-block kernels may walk each XCD's (head, batch) units
+// row-block-major (heaviest blocks first): only when the K / V rows those
+// units read at once fit well within the XCD's 4 MiB L2.
+bool xmajor_fits(const Params& p, int ny, int nz);
 
 // A strided [B, H, S, D] fp32 tensor (D contiguous) to be zeroed.
 struct ZeroRows {

@@ -112,7 +112,7 @@ __global__ __launch_bounds__(NTF, 2) void k_fwd(Params p, FwdArgs a) {
 
   const int tid = threadIdx.x, l = tid & 63, lr = l & 31, lg = l >> 5;
   const int w = __builtin_amdgcn_readfirstlane(tid >> 6);   // wave-uniform
-  const BlockXYZ blk = xcd_block();
+  const BlockXYZ blk = a.xmajor ? xcd_block_xmajor() : xcd_block();
   // under a causal mask later row blocks see more keys: deal them first
   const bool heavy_last = p.mask.kind != kMaskNone && p.mask.wl < 0;
   const int i0 = (heavy_last ? (int)gridDim.x - 1 - blk.x : blk.x) * BQF;
@@ -295,8 +295,10 @@ bool mfma_fwd_supported(const Params& p, const FwdArgs& a, bool o_bf16) {
   return true;
 }
 
-hipError_t launch_fwd_mfma(const Params& p, const FwdArgs& a, bool o_bf16, hipStream_t st) {
+hipError_t launch_fwd_mfma(const Params& p, const FwdArgs& a0, bool o_bf16, hipStream_t st) {
   if (p.Sq == 0 || p.B == 0 || p.Hq == 0) return hipSuccess;
+  FwdArgs a = a0;
+  a.xmajor = xmajor_fits(p, p.Hq, p.B) ? 1 : 0;   // grid (row blocks, Hq, B)
   const bool bias = a.bias != nullptr;
   if (p.Dqk == 64)
     return bias ? launch_fwd_d<64, 32, true>(p, a, o_bf16, st) : launch_fwd_d<64, 64, false>(p, a, o_bf16, st);

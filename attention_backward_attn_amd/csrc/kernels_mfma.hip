@@ -994,7 +994,7 @@ __global__ __launch_bounds__(NT, 2) void k_dq(Params p, BwdArgs a) {
 
   const int tid = threadIdx.x, l = tid & 63, lr = l & 31, lg = l >> 5;
   const int w = __builtin_amdgcn_readfirstlane(tid >> 6);   // wave-uniform
-  const BlockXYZ blk = xcd_block();
+  const BlockXYZ blk = a.xmajor ? xcd_block_xmajor() : xcd_block();
   // under a causal mask later row blocks see more keys: deal them first
   const bool heavy_last = p.mask.kind != kMaskNone && p.mask.wl < 0;
   const int i0 = (heavy_last ? (int)gridDim.x - 1 - blk.x : blk.x) * BQ3;
@@ -1159,7 +1159,7 @@ __global__ __launch_bounds__(NT, 2) void k_dq2(Params p, BwdArgs a) {
 
   const int tid = threadIdx.x, l = tid & 63, lr = l & 31, lg = l >> 5;
   const int w = __builtin_amdgcn_readfirstlane(tid >> 6);   // wave-uniform
-  const BlockXYZ blk = xcd_block_xmajor();
+  const BlockXYZ blk = a.xmajor ? xcd_block_xmajor() : xcd_block();
   // under a causal mask later row blocks see more keys: deal them first
   const bool heavy_last = p.mask.kind != kMaskNone && p.mask.wl < 0;
   const int i0 = (heavy_last ? (int)gridDim.x - 1 - blk.x : blk.x) * BQ3;
@@ -1439,8 +1439,10 @@ __global__ __launch_bounds__(NT, 2) void k_dq2(Params p, BwdArgs a) {
 }
 
 template <int D>
-hipError_t launch_dq(const Params& p, const BwdArgs& a, hipStream_t st) {
+hipError_t launch_dq(const Params& p, const BwdArgs& a0, hipStream_t st) {
   const dim3 grid((p.Sq + BQ3 - 1) / BQ3, p.Hq, p.B);
+  BwdArgs a = a0;
+  a.xmajor = xmajor_fits(p, grid.y, grid.z) ? 1 : 0;
   if (a.bias)
     hipLaunchKernelGGL((k_dq<D, true>), grid, dim3(NT), 0, st, p, a);
   else
@@ -1460,6 +1462,22 @@ bool mfma_bwd_supported(const Params& p) {
     for (int i = 0; i < 3; ++i)
       if (x[i] % 8 != 0) return false;
   return true;
+}
+
+bool xmajor_fits(const Params& p, int ny, int nz) {
+  const int U = ny * nz;
+  if (U % 8 != 0) return false;
+  const int per = U / 8;   // units of XCD 0: unit u is head u / nz, batch entry u % nz
+  int pairs = 0, last_z = -1, last_g = -1;
+  for (int u = 0; u < per; ++u) {
+    const int z = u % nz, g = (u / nz) / p.G;
+    if (z != last_z || g != last_g) ++pairs;   // consecutive units share a K / V head when both match
+    last_z = z;
+    last_g = g;
+  }
+  // distinct (batch entry, KV head) pairs are at most `pairs` (runs of equal ones counted once)
+  const double bytes = (double)pairs * p.Sk * (p.Dqk + p.Dv) * 2.0;
+  return bytes <= 3.0 * 1024 * 1024;
 }
 
 hipError_t launch_bwd_mfma(const Params& p, const BwdArgs& a, hipStream_t st) {
