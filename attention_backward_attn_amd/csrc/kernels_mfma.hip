@@ -727,6 +727,21 @@ __global__ __launch_bounds__(NT2) void k_dkdv2(Params p, BwdArgs a, DkdvGrid gd)
       }
 
       // one tile: t the tile index, j = t % NB2 (a constant)
+      // Operands of the next tile read before its barrier, from buffers that
+      // are complete (and not rewritten) since an earlier one: B of its
+      // dV / dK products and, for the dP wave, A of its dP chain.  Their
+      // latency then overlaps the end of the current tile.
+      bf16x8 bq_n[AHEAD], xa_n[AHEAD];
+      auto prefetch = [&](auto jc) {   // jc: buffer of the next tile
+        constexpr int j = decltype(jc)::value, j1 = (j + 1) % NB2;
+#pragma unroll
+        for (int i = 0; i < AHEAD; ++i) bq_n[i] = read_b(j, i);
+        if (!SW) {
+#pragma unroll
+          for (int i = 0; i < AHEAD; ++i) xa_n[i] = read_a(j1, i);
+        }
+      };
+      prefetch(std::integral_constant<int, 0>{});
       auto tile = [&](int t, auto jc) {
         constexpr int j = decltype(jc)::value;
         constexpr int j1 = (j + 1) % NB2, j2 = (j + 2) % NB2;
@@ -741,7 +756,7 @@ __global__ __launch_bounds__(NT2) void k_dkdv2(Params p, BwdArgs a, DkdvGrid gd)
           f32x4 L4[4];
           row_vals(L4, sm.lse[j1]);
 #pragma unroll
-          for (int i = 0; i < AHEAD; ++i) { bq[i] = read_b(j, i); xa[i] = read_a(j2, i); }
+          for (int i = 0; i < AHEAD; ++i) { bq[i] = bq_n[i]; xa[i] = read_a(j2, i); }
           __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
           for (int i = 0; i < NS; ++i) {
@@ -766,7 +781,7 @@ __global__ __launch_bounds__(NT2) void k_dkdv2(Params p, BwdArgs a, DkdvGrid gd)
 #pragma unroll
           for (int k = 0; k < 4; ++k) P4[k] = sm.px[t & 1][pr][k][l];
 #pragma unroll
-          for (int i = 0; i < AHEAD; ++i) { bq[i] = read_b(j, i); xa[i] = read_a(j1, i); }
+          for (int i = 0; i < AHEAD; ++i) { bq[i] = bq_n[i]; xa[i] = xa_n[i]; }
           __builtin_amdgcn_sched_barrier(0);
           float dsv[16];
           bf16x8 A0, A1;
@@ -788,6 +803,7 @@ __global__ __launch_bounds__(NT2) void k_dkdv2(Params p, BwdArgs a, DkdvGrid gd)
           for (int i = NS / 2; i < NS; ++i) og[i % NC] = mfma(A1, bq[i], og[i % NC]);
         }
         acc = accn;
+        prefetch(std::integral_constant<int, j1>{});   // (past the last tile: stale, unused)
         // tile t + 3 complete before the next barrier (tile t + 4 may stay in flight)
         wait_vm(more ? stg.n_loads : 0);
       };
