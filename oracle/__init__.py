@@ -45,4 +45,6 @@ from .attention import (  # noqa: F401
     allowed_pair_count,
     forward_varlen,
     backward_varlen,
+    backward_shared_kv,
+    backward_shared_kv_varlen,
 )

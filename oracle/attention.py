@@ -36,6 +36,10 @@ How each function is pinned (tests/test_oracle_*.py):
                     identity with an empty partial; commutativity
 ``dq_rows`` /       equality with the corresponding rows / keys of
 ``dkdv_keys``       ``backward`` on small inputs
+``backward_shared_  central finite differences of L = sum(O * dO) with the one
+kv`` (+ ``_varlen``)  tensor perturbed in both roles; torch fp64 autograd
+                    with one leaf tensor passed as keys and values; dK alone
+                    (the dV term dropped) fails the finite-difference pin
 ==================  =========================================================
 
 Readings of the pages that the code takes (each is listed with its reason in
@@ -386,3 +390,23 @@ def backward_varlen(q, k, v, o, do, lse, cu_q, cu_k, scale: float, spec: MaskSpe
         if dsinks is not None and n > 0:
             dsinks += g["dsinks"]
     return {"dq": dq, "dk": dk, "dv": dv, "dsinks": dsinks, "delta": delta}
+
+
+def backward_shared_kv(q, kv, o, do, lse, scale: float, spec: MaskSpec = MaskSpec(), sinks=None,
+                       row_block: int = 512):
+    """Backward when one tensor ``kv`` [B, Hk, Sk, D] serves as keys and
+    values ([SFMG] "Formula", sliding-window case: the selected KV is the
+    original KV, used in Q KV^T, dO KV^T and dS KV).  Its gradient collects
+    both uses, dKV = scale * dS^T Q + P^T dO ([SFMG] Phase 3): by the chain
+    rule, the dK plus the dV of ``backward`` with k = v = kv.  Returns a dict
+    with dq, dkv, dsinks (or None) and delta."""
+    g = backward(q, kv, kv, o, do, lse, scale, spec, None, sinks, row_block)
+    return {"dq": g["dq"], "dkv": g["dk"] + g["dv"], "dsinks": g["dsinks"], "delta": g["delta"]}
+
+
+def backward_shared_kv_varlen(q, kv, o, do, lse, cu_q, cu_k, scale: float, spec: MaskSpec = MaskSpec(),
+                              sinks=None):
+    """``backward_shared_kv`` of a variable-length packed batch (TND, see
+    ``forward_varlen``): packed dq [Tq, Hq, D] and dkv [Tk, Hk, D]."""
+    g = backward_varlen(q, kv, kv, o, do, lse, cu_q, cu_k, scale, spec, sinks)
+    return {"dq": g["dq"], "dkv": g["dk"] + g["dv"], "dsinks": g["dsinks"], "delta": g["delta"]}
