@@ -19,7 +19,7 @@ LIB_PATH = os.path.join(HERE, "libattnbwd.so")
 ATTN_OK, ATTN_EINVAL, ATTN_EUNSUPPORTED, ATTN_EHIP = 0, -1, -2, -3
 ATTN_F32, ATTN_BF16 = 0, 1
 MASKS = {"none": 0, "top_left": 1, "bottom_right": 2}
-ATTN_DETERMINISTIC, ATTN_ACCUMULATE_DQ, ATTN_ACCUMULATE_DKDV = 1, 2, 4
+ATTN_DETERMINISTIC, ATTN_ACCUMULATE_DQ, ATTN_ACCUMULATE_DKDV, ATTN_SHARED_KV = 1, 2, 4, 8
 
 EXPORTED = ("attn_problem_init", "attn_fwd_lse", "attn_bwd_preprocess", "attn_bwd",
             "attn_lse_merge", "attn_status_string")
@@ -231,7 +231,9 @@ def forward(q, k, v, *, bias=None, sinks=None, o_dtype=None, stream=None, **mask
 def backward(q, k, v, o, do, lse, *, bias=None, sinks=None, want_dbias=False, flags=0, stream=None,
              dq=None, **mask_kw):
     """Full backward: preprocess then the main pass.  Returns a dict with
-    dq, dk, dv (fp32), dbias and dsinks (or None) and delta."""
+    dq, dk, dv (fp32), dbias and dsinks (or None) and delta.  With
+    ATTN_SHARED_KV in flags (k is v) dk is the gradient of the shared tensor
+    and dv is None."""
     import torch
     dev = q.device
     if mask_kw.get("cu_seqlens_q") is not None:
@@ -240,7 +242,8 @@ def backward(q, k, v, o, do, lse, *, bias=None, sinks=None, want_dbias=False, fl
         B, Hq, Sq, _ = q.shape
     dq = torch.empty(q.shape, device=dev, dtype=torch.float32) if dq is None else dq
     dk = torch.empty(k.shape, device=dev, dtype=torch.float32)
-    dv = torch.empty(v.shape, device=dev, dtype=torch.float32)
+    # one tensor as keys and values: dk is the gradient of that tensor
+    dv = None if flags & ATTN_SHARED_KV else torch.empty(v.shape, device=dev, dtype=torch.float32)
     delta = torch.empty(B, Hq, Sq, device=dev, dtype=torch.float32)
     dsinks = torch.empty(Hq, device=dev, dtype=torch.float32) if sinks is not None else None
     dbias = torch.empty(bias.shape, device=dev, dtype=torch.float32) if (want_dbias and bias is not None) else None

@@ -18,7 +18,7 @@ HERE = os.path.dirname(os.path.abspath(__file__))
 ROOT = os.path.dirname(HERE)
 CSRC = os.path.join(HERE, "csrc")
 LIB = os.path.join(HERE, "libattnbwd.so")
-SOURCES = ["api.cpp", "kernels_aux.hip", "kernels_simt.hip", "kernels_mfma.hip", "kernels_fwd_mfma.hip"]
+SOURCES = ["api.cpp", "kernels_aux.hip", "kernels_simt.hip", "kernels_mfma.hip", "kernels_fwd_mfma.hip", "kernels_mla.hip"]
 ARCH = "gfx950"
 
 

@@ -14,7 +14,7 @@ using attn::Params;
 
 namespace {
 
-constexpr int kMaxHeadDim = 256;
+constexpr int kMaxHeadDim = 512;
 
 bool strides_ok(const int64_t* s) { return s[0] >= 0 && s[1] >= 0 && s[2] >= 0; }
 
@@ -88,6 +88,38 @@ attn::ZeroRows ksite_rows(const attn_problem_t* p, float* x, int D, const int64_
 
 attn_status_t hip_status(hipError_t e) { return e == hipSuccess ? ATTN_OK : ATTN_EHIP; }
 
+// k and v name the same tensor: one pointer, one set of strides
+bool same_kv(const attn_problem_t* p, const void* k, const void* v) {
+  return k == v && p->k_str[0] == p->v_str[0] && p->k_str[1] == p->v_str[1] && p->k_str[2] == p->v_str[2];
+}
+
+// attn_bwd with one tensor as keys and values (ATTN_SHARED_KV): head dim 512,
+// bf16, no bias; dk receives the gradient of the shared tensor.
+attn_status_t bwd_shared_kv(const attn_problem_t* p, const void* q, const void* k, const void* v,
+                            const void* dout, const float* lse, const float* delta, const float* bias,
+                            float* dq, float* dk, float* dv, float* dbias, uint32_t flags, void* stream) {
+  if (!(flags & ATTN_SHARED_KV) || p->Dqk != attn::kSharedKvD || p->Dv != attn::kSharedKvD ||
+      p->in_dtype != ATTN_BF16 || bias || dbias)
+    return ATTN_EUNSUPPORTED;
+  if (dv || !same_kv(p, k, v)) return ATTN_EINVAL;
+  if (!strides_ok(p->q_str) || !strides_ok(p->k_str) || !strides_ok(p->do_str) || !strides_ok(p->dq_str) ||
+      !strides_ok(p->dk_str))
+    return ATTN_EINVAL;
+  const bool no_rows = p->B == 0 || p->Sq == 0;
+  const bool no_keys = p->B == 0 || p->Sk == 0;
+  if (!no_rows && (!q || !dout || !lse || !delta || !dq)) return ATTN_EINVAL;
+  if (!no_keys && (!k || !dk)) return ATTN_EINVAL;
+  Params kp = make_params(p);
+  if (!attn::mla_supported(kp) || (!no_rows && (!aligned16(q) || !aligned16(dout) || !aligned16(dq))) ||
+      (!no_keys && (!aligned16(k) || !aligned16(dk))))
+    return ATTN_EUNSUPPORTED;
+  if (no_rows && no_keys) return ATTN_OK;
+  attn::BwdArgs a{q, k, k, dout, lse, delta, nullptr, dq, dk, nullptr, nullptr,
+                  (flags & ATTN_ACCUMULATE_DQ) ? 1 : 0, (flags & ATTN_DETERMINISTIC) ? 1 : 0,
+                  (flags & ATTN_ACCUMULATE_DKDV) ? 1 : 0, 0};
+  return hip_status(attn::launch_bwd512(kp, a, (hipStream_t)stream));
+}
+
 }  // namespace
 
 extern "C" {
@@ -137,11 +169,21 @@ attn_status_t attn_fwd_lse(const attn_problem_t* p, const void* q, const void* k
   if (!empty && (!q || !o || !lse)) return ATTN_EINVAL;
   if (!empty && p->Sk > 0 && (!k || !v)) return ATTN_EINVAL;
   if (bias && (p->bias_str[0] < 0 || p->bias_str[1] < 0)) return ATTN_EINVAL;
+  const bool o_bf16 = p->o_dtype == ATTN_BF16;
+  if (p->Dqk == attn::kSharedKvD || p->Dv == attn::kSharedKvD) {
+    // head dim 512: one tensor as keys and values, bf16, no bias
+    if (p->Dqk != p->Dv || p->in_dtype != ATTN_BF16 || bias || !same_kv(p, k, v)) return ATTN_EUNSUPPORTED;
+    Params kp = make_params(p);
+    if (!attn::mla_supported(kp) || !aligned16(q) || !aligned16(k) || ((uintptr_t)o & (o_bf16 ? 7u : 15u)))
+      return ATTN_EUNSUPPORTED;
+    if (empty) return ATTN_OK;
+    attn::FwdArgs a{q, k, v, bias, sinks, o, lse};
+    return hip_status(attn::launch_fwd512(kp, a, o_bf16, (hipStream_t)stream));
+  }
   if (p->Dqk > attn::kSimtMaxD || p->Dv > attn::kSimtMaxD) return ATTN_EUNSUPPORTED;
   if (empty) return ATTN_OK;
   Params kp = make_params(p);
   attn::FwdArgs a{q, k, v, bias, sinks, o, lse};
-  const bool o_bf16 = p->o_dtype == ATTN_BF16;
   const bool mfma = p->in_dtype == ATTN_BF16 && attn::mfma_fwd_supported(kp, a, o_bf16);
   if (packed(p) && (!mfma || bias)) return ATTN_EUNSUPPORTED;
   if (mfma) return hip_status(attn::launch_fwd_mfma(kp, a, o_bf16, (hipStream_t)stream));
@@ -184,8 +226,10 @@ attn_status_t attn_bwd(const attn_problem_t* p, const void* q, const void* k, co
                        float* dq, float* dk, float* dv, float* dbias, uint32_t flags, void* stream) {
   attn_status_t st = check_problem(p);
   if (st != ATTN_OK) return st;
-  if ((flags & ~(uint32_t)(ATTN_DETERMINISTIC | ATTN_ACCUMULATE_DQ | ATTN_ACCUMULATE_DKDV)) != 0)
+  if ((flags & ~(uint32_t)(ATTN_DETERMINISTIC | ATTN_ACCUMULATE_DQ | ATTN_ACCUMULATE_DKDV | ATTN_SHARED_KV)) != 0)
     return ATTN_EINVAL;
+  if ((flags & ATTN_SHARED_KV) || p->Dqk == attn::kSharedKvD || p->Dv == attn::kSharedKvD)
+    return bwd_shared_kv(p, q, k, v, dout, lse, delta, bias, dq, dk, dv, dbias, flags, stream);
   if (!strides_ok(p->q_str) || !strides_ok(p->k_str) || !strides_ok(p->v_str) || !strides_ok(p->do_str) ||
       !strides_ok(p->dq_str) || !strides_ok(p->dk_str) || !strides_ok(p->dv_str))
     return ATTN_EINVAL;

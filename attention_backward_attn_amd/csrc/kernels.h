@@ -86,4 +86,13 @@ hipError_t launch_fwd_mfma(const Params& p, const FwdArgs& a, bool o_bf16, hipSt
 bool mfma_bwd_supported(const Params& p);
 hipError_t launch_bwd_mfma(const Params& p, const BwdArgs& a, hipStream_t st);
 
+// bf16 matrix-core kernels for head dim 512 with one tensor as keys and
+// values (k == v): forward, and the backward whose dk output is the gradient
+// of the shared tensor (dK + dV).  Row strides multiples of 8 elements,
+// 16-byte aligned operands.
+constexpr int kSharedKvD = 512;
+bool mla_supported(const Params& p);
+hipError_t launch_fwd512(const Params& p, const FwdArgs& a, bool o_bf16, hipStream_t st);
+hipError_t launch_bwd512(const Params& p, const BwdArgs& a, hipStream_t st);
+
 }  // namespace attn

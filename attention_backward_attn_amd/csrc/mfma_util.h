@@ -173,6 +173,15 @@ __device__ inline void wait_vm(int n) {
     case 4: __builtin_amdgcn_s_waitcnt(0x0F74); break;
     case 5: __builtin_amdgcn_s_waitcnt(0x0F75); break;
     case 6: __builtin_amdgcn_s_waitcnt(0x0F76); break;
+    case 7: __builtin_amdgcn_s_waitcnt(0x0F77); break;
+    case 8: __builtin_amdgcn_s_waitcnt(0x0F78); break;
+    case 9: __builtin_amdgcn_s_waitcnt(0x0F79); break;
+    case 10: __builtin_amdgcn_s_waitcnt(0x0F7A); break;
+    case 11: __builtin_amdgcn_s_waitcnt(0x0F7B); break;
+    case 12: __builtin_amdgcn_s_waitcnt(0x0F7C); break;
+    case 13: __builtin_amdgcn_s_waitcnt(0x0F7D); break;
+    case 14: __builtin_amdgcn_s_waitcnt(0x0F7E); break;
+    case 15: __builtin_amdgcn_s_waitcnt(0x0F7F); break;
     default: __builtin_amdgcn_s_waitcnt(0x0F70); break;
   }
 }

@@ -167,3 +167,61 @@ def make_varlen_inputs(w: VarlenWorkload) -> dict:
     draw = lambda *s: round_bf16(rng.standard_normal(s).astype(np.float32))
     return {"q": draw(T, w.Hq, w.D), "k": draw(T, w.Hk, w.D), "v": draw(T, w.Hk, w.D),
             "do": draw(T, w.Hq, w.D), "cu_seqlens": cu}
+
+
+@dataclass(frozen=True)
+class SharedKvWorkload:
+    """Attention with one tensor as keys and values, head dim 512, in the
+    packed TND layout of the CANN sparse_flash_mla_grad page ("Prototype",
+    "Example": q and dO [T1, N1, D], kv [T2, N2, D], per-head sink logits,
+    cumulative sequence lengths).  ``seqs`` lists each sequence's (query,
+    key) lengths; the mask is a bottom-right sliding window of
+    ``window_left + 1`` keys (the sliding-window case of that page)."""
+    name: str
+    seqs: tuple
+    N1: int
+    N2: int
+    D: int
+    window_left: int
+    sinks: bool
+    seed: int
+
+    @property
+    def scale(self) -> float:
+        return 1.0 / float(np.sqrt(self.D))
+
+    def cu_seqlens(self):
+        cu_q = np.concatenate([[0], np.cumsum([a for a, _ in self.seqs])]).astype(np.int32)
+        cu_k = np.concatenate([[0], np.cumsum([b for _, b in self.seqs])]).astype(np.int32)
+        return cu_q, cu_k
+
+    @property
+    def max_q(self) -> int:
+        return max(a for a, _ in self.seqs)
+
+    @property
+    def max_k(self) -> int:
+        return max(b for _, b in self.seqs)
+
+
+SHARED_KV_WORKLOADS = {
+    # the example's sizes: S1 = 256 queries, S2 = 1024 keys, N1 = 64, N2 = 1, D = 512
+    "mla_swa512_s256x1024": SharedKvWorkload("mla_swa512_s256x1024", seqs=((256, 1024),), N1=64, N2=1,
+                                             D=512, window_left=511, sinks=True, seed=1007),
+    # one 4096-token sequence with the same heads
+    "mla_swa512_s4096": SharedKvWorkload("mla_swa512_s4096", seqs=((4096, 4096),), N1=64, N2=1, D=512,
+                                         window_left=511, sinks=True, seed=1008),
+}
+
+
+def make_shared_kv_inputs(w: SharedKvWorkload) -> dict:
+    """Packed q, do [T1, N1, D], kv [T2, N2, D] (bf16-rounded float32), the
+    sink logits [N1] and the prefix sums of the query and key lengths."""
+    cu_q, cu_k = w.cu_seqlens()
+    rng = np.random.default_rng(w.seed)
+    draw = lambda *s: round_bf16(rng.standard_normal(s).astype(np.float32))  # noqa: E731
+    out = {"q": draw(int(cu_q[-1]), w.N1, w.D), "kv": draw(int(cu_k[-1]), w.N2, w.D),
+           "do": draw(int(cu_q[-1]), w.N1, w.D), "cu_q": cu_q, "cu_k": cu_k, "sinks": None}
+    if w.sinks:
+        out["sinks"] = rng.standard_normal(w.N1).astype(np.float32)
+    return out

@@ -88,14 +88,26 @@ typedef enum {
  *   ring use, [RING] _ring_bwd accumulates dq over the K/V chunks).
  * ATTN_ACCUMULATE_DKDV: add into dK and dV instead of overwriting them
  *   ([RING] _ring_bwd adds each chunk's dk/dv into travelling
- *   accumulators). */
-enum { ATTN_DETERMINISTIC = 1u, ATTN_ACCUMULATE_DQ = 2u, ATTN_ACCUMULATE_DKDV = 4u };
+ *   accumulators).
+ * ATTN_SHARED_KV: one tensor serves as keys and values ([SFMG] "Formula",
+ *   sliding-window case: the selected KV is the original KV, used in
+ *   Q KV^T, dO KV^T and dS KV).  k and v must be the same pointer with the
+ *   same strides and Dqk == Dv; dk receives the gradient of the shared
+ *   tensor, dKV = scale * dS^T Q + P^T dO ([SFMG] Phase 3), and dv must be
+ *   null.  Covered for head dim 512 (the page's D) with bf16 inputs and no
+ *   bias; head dim 512 requires the flag (else ATTN_EUNSUPPORTED). */
+enum {
+  ATTN_DETERMINISTIC = 1u,
+  ATTN_ACCUMULATE_DQ = 2u,
+  ATTN_ACCUMULATE_DKDV = 4u,
+  ATTN_SHARED_KV = 8u
+};
 
 /* Problem description ([GQA-BWD] FmhaProblem; [SFMG] "Prototype"). */
 typedef struct attn_problem {
   int32_t B, Hq, Hk;        /* batch, query heads, KV heads; Hq % Hk == 0        */
   int32_t Sq, Sk;           /* local sequence lengths (this call's rows / keys)  */
-  int32_t Dqk, Dv;          /* head dims of Q/K and of V/O                       */
+  int32_t Dqk, Dv;          /* head dims of Q/K and of V/O (at most 512)         */
   float scale;              /* softmax scale, applied to Q K^T before bias       */
   int32_t in_dtype;         /* attn_dtype_t of Q, K, V and dO                    */
   int32_t o_dtype;          /* attn_dtype_t of O                                 */
@@ -142,7 +154,9 @@ void attn_problem_init(attn_problem_t* p, int32_t B, int32_t Hq, int32_t Hk, int
  * excluded); the optional sink logit of each query head joins the softmax
  * normaliser without a value row.  Writes O (o_dtype, strides o_str) and
  * LSE (fp32 [B, Hq, Sq]).
- *   bias:  nullable fp32 [Hq, Sq, Sk];  sinks: nullable fp32 [Hq]. */
+ *   bias:  nullable fp32 [Hq, Sq, Sk];  sinks: nullable fp32 [Hq].
+ * Head dim 512 ([SFMG] shared KV): k and v must be the same tensor (same
+ * pointer and strides), bf16, no bias (else ATTN_EUNSUPPORTED). */
 attn_status_t attn_fwd_lse(const attn_problem_t* p, const void* q, const void* k,
                            const void* v, const float* bias, const float* sinks, void* o,
                            float* lse, void* stream);

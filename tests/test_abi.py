@@ -59,7 +59,7 @@ FAKE = ctypes.c_void_p(0x1000)  # never dereferenced: validation fails first
 BAD = [
     dict(Hk=3),                 # Hq % Hk != 0
     dict(Dqk=0),
-    dict(Dv=300),
+    dict(Dv=600),               # above the largest head dim (512)
     dict(scale=0.0),
     dict(scale=float("nan")),
     dict(in_dtype=7),
@@ -115,7 +115,7 @@ def test_bwd_rejects_null_pointers_and_flags():
                       0, None) == B.ATTN_EINVAL
     # unknown flag bit
     assert L.attn_bwd(ctypes.byref(p), FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, None, FAKE, FAKE, FAKE, None,
-                      8, None) == B.ATTN_EINVAL
+                      16, None) == B.ATTN_EINVAL
     assert L.attn_bwd(None, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, None, FAKE, FAKE, FAKE, None, 0,
                       None) == B.ATTN_EINVAL
 
@@ -148,3 +148,52 @@ def test_status_strings():
     assert B.status_string(B.ATTN_OK) == "ok"
     assert "invalid" in B.status_string(B.ATTN_EINVAL)
     assert "unsupported" in B.status_string(B.ATTN_EUNSUPPORTED)
+
+
+FAKE2 = ctypes.c_void_p(0x2000)
+
+
+def shared_problem(**kw):
+    p = B.attn_problem_t()
+    B.lib().attn_problem_init(ctypes.byref(p), 1, 8, 1, 64, 64, 512, 512)
+    for k, v in kw.items():
+        setattr(p, k, v)
+    return p
+
+
+def bwd(p, k, v, dv, bias=None, flags=B.ATTN_SHARED_KV):
+    return B.lib().attn_bwd(ctypes.byref(p), FAKE, k, v, FAKE, FAKE, FAKE, bias, FAKE, FAKE, dv, None, flags,
+                            None)
+
+
+def test_shared_kv_validation():
+    p = shared_problem()
+    # head dim 512 needs the shared-KV flag
+    assert bwd(p, FAKE, FAKE, None, flags=0) == B.ATTN_EUNSUPPORTED
+    # the flag needs one tensor: same pointer, same strides
+    assert bwd(p, FAKE, FAKE2, None) == B.ATTN_EINVAL
+    p2 = shared_problem()
+    p2.v_str[2] = 1024
+    assert bwd(p2, FAKE, FAKE, None) == B.ATTN_EINVAL
+    # dk is the shared gradient: dv must be null
+    assert bwd(p, FAKE, FAKE, FAKE) == B.ATTN_EINVAL
+    # no bias, bf16 only, head dim 512 only
+    assert bwd(p, FAKE, FAKE, None, bias=FAKE) == B.ATTN_EUNSUPPORTED
+    assert bwd(shared_problem(in_dtype=B.ATTN_F32), FAKE, FAKE, None) == B.ATTN_EUNSUPPORTED
+    assert bwd(problem(), FAKE, FAKE, None) == B.ATTN_EUNSUPPORTED
+    # unaligned operand
+    assert bwd(p, ctypes.c_void_p(0x1008), ctypes.c_void_p(0x1008), None) == B.ATTN_EUNSUPPORTED
+    # nothing to do: no device access
+    assert bwd(shared_problem(B=0), FAKE, FAKE, None) == B.ATTN_OK
+
+
+def test_shared_kv_forward_validation():
+    L = B.lib()
+    p = shared_problem()
+    fwd = lambda p, k, v, bias=None: L.attn_fwd_lse(ctypes.byref(p), FAKE, k, v, bias, None, FAKE, FAKE,  # noqa: E731
+                                                    None)
+    assert fwd(p, FAKE, FAKE2) == B.ATTN_EUNSUPPORTED           # separate K and V at head dim 512
+    assert fwd(p, FAKE, FAKE, bias=FAKE) == B.ATTN_EUNSUPPORTED
+    assert fwd(shared_problem(in_dtype=B.ATTN_F32), FAKE, FAKE) == B.ATTN_EUNSUPPORTED
+    assert fwd(shared_problem(Dv=256), FAKE, FAKE) == B.ATTN_EUNSUPPORTED
+    assert fwd(shared_problem(Sq=0), FAKE, FAKE) == B.ATTN_OK
