@@ -229,27 +229,38 @@ __global__ __launch_bounds__(XNT, 1) void k_fwd512(Params p, FwdArgs a) {
     } else {
       wait_vm(0);
     }
-    for (int t = 0; t <= n_it; ++t) {
+    // One tile step: the S^T chains of tile t (when HC) among the O^T
+    // products of tile t - 1 (when HP), operands two product steps ahead,
+    // then the online softmax of tile t.  First and last steps peeled.
+    auto step = [&](int t, auto hc_, auto hp_) {
+      constexpr bool HC = decltype(hc_)::value, HP = decltype(hp_)::value;
+      constexpr int AH = 2;
       __syncthreads();   // tile t complete; tile t - 3's buffer free
       if (t + 2 < n_it) issue(t + 2);
       TileAddr cur, prv;
-      cur.set(sm_base + (t % XNB) * XTS, a_lane, t_lane);
-      prv.set(sm_base + ((t + XNB - 1) % XNB) * XTS, a_lane, t_lane);
-      const bool has_cur = t < n_it, has_prv = t > 0;
-      // S^T of tile t among the O^T products of tile t - 1
+      if (HC) cur.set(sm_base + (t % XNB) * XTS, a_lane, t_lane);
+      if (HP) prv.set(sm_base + ((t + XNB - 1) % XNB) * XTS, a_lane, t_lane);
       f32x4 sacc[2] = {zero4(), zero4()};
+      bf16x8 k0[XNS], k1[XNS], bt[XNC];
+#pragma unroll
+      for (int i = 0; i < AH; ++i) {
+        if (HC) { k0[i] = cur.row(0, i); k1[i] = cur.row(1, i); }
+        if (HP) { bt[2 * i] = prv.tr(2 * i); bt[2 * i + 1] = prv.tr(2 * i + 1); }
+      }
+      __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
       for (int s = 0; s < XNS; ++s) {
-        if (has_cur) {
-          sacc[0] = mfma16(cur.row(0, s), qB[s], sacc[0]);
-          sacc[1] = mfma16(cur.row(1, s), qB[s], sacc[1]);
+        if (HC) sacc[0] = mfma16(k0[s], qB[s], sacc[0]);
+        if (HP) o[2 * s] = mfma16(bt[2 * s], Pb, o[2 * s]);
+        if (HC) sacc[1] = mfma16(k1[s], qB[s], sacc[1]);
+        if (HP) o[2 * s + 1] = mfma16(bt[2 * s + 1], Pb, o[2 * s + 1]);
+        if (s + AH < XNS) {
+          if (HC) { k0[s + AH] = cur.row(0, s + AH); k1[s + AH] = cur.row(1, s + AH); }
+          if (HP) { bt[2 * (s + AH)] = prv.tr(2 * (s + AH)); bt[2 * (s + AH) + 1] = prv.tr(2 * (s + AH) + 1); }
         }
-        if (has_prv) {
-          o[2 * s] = mfma16(prv.tr(2 * s), Pb, o[2 * s]);
-          o[2 * s + 1] = mfma16(prv.tr(2 * s + 1), Pb, o[2 * s + 1]);
-        }
+        __builtin_amdgcn_sched_barrier(0);
       }
-      if (has_cur) {
+      if (HC) {
         const int j0 = kt.j0(t);
         float sv8[8];
 #pragma unroll
@@ -280,8 +291,11 @@ __global__ __launch_bounds__(XNT, 1) void k_fwd512(Params p, FwdArgs a) {
         }
         Pb = pack_halves(pv);
       }
-      if (t + 1 < n_it) wait_vm(t + 2 < n_it ? 8 : 0);
-    }
+      if (t + 1 < n_it) wait_vm(t + 2 < n_it ? 8 : 0);   // tile t + 1 complete before the next barrier
+    };
+    step(0, std::true_type{}, std::false_type{});
+    for (int t = 1; t < n_it; ++t) step(t, std::true_type{}, std::true_type{});
+    step(n_it, std::false_type{}, std::true_type{});
   }
   // normaliser of the row over its four lane groups
   float lt = l_run + __shfl_xor(l_run, 16);
@@ -371,44 +385,67 @@ __global__ __launch_bounds__(XNT, 1) void k_dq512(Params p, BwdArgs a) {
     } else {
       wait_vm(0);
     }
-    for (int t = 0; t <= n_it; ++t) {
+    // One tile step: the S^T / dP^T chains of tile t (when HC) among the dQ^T
+    // products of tile t - 1 (when HP, first half of the columns), then the
+    // second half of those products among the exponentials and dS arithmetic
+    // of tile t.  Operands are read two product steps ahead.  The first and
+    // last steps are peeled, so the main loop has no branches.
+    auto step = [&](int t, auto hc_, auto hp_) {
+      constexpr bool HC = decltype(hc_)::value, HP = decltype(hp_)::value;
+      constexpr int AH = 2;
       __syncthreads();   // tile t complete; tile t - 3's buffer free
       if (t + 2 < n_it) issue(t + 2);
       TileAddr cur, prv;
-      cur.set(sm_base + (t % XNB) * XTS, a_lane, t_lane);
-      prv.set(sm_base + ((t + XNB - 1) % XNB) * XTS, a_lane, t_lane);
-      const bool has_cur = t < n_it, has_prv = t > 0;
+      if (HC) cur.set(sm_base + (t % XNB) * XTS, a_lane, t_lane);
+      if (HP) prv.set(sm_base + ((t + XNB - 1) % XNB) * XTS, a_lane, t_lane);
       f32x4 sacc[2] = {zero4(), zero4()}, pacc[2] = {zero4(), zero4()};
+      bf16x8 k0[XNS], k1[XNS], bt[XNC];
+#pragma unroll
+      for (int i = 0; i < AH; ++i) {
+        if (HC) { k0[i] = cur.row(0, i); k1[i] = cur.row(1, i); }
+        if (HP) bt[i] = prv.tr(i);
+      }
+      __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
       for (int s = 0; s < XNS; ++s) {
-        if (has_cur) {
-          const bf16x8 k0 = cur.row(0, s), k1 = cur.row(1, s);
-          sacc[0] = mfma16(k0, qB[s], sacc[0]);
-          pacc[0] = mfma16(k0, doB[s], pacc[0]);
-          sacc[1] = mfma16(k1, qB[s], sacc[1]);
-          pacc[1] = mfma16(k1, doB[s], pacc[1]);
+        if (HC) {
+          sacc[0] = mfma16(k0[s], qB[s], sacc[0]);
+          pacc[0] = mfma16(k0[s], doB[s], pacc[0]);
         }
-        if (has_prv) {
-          dq[2 * s] = mfma16(prv.tr(2 * s), Db, dq[2 * s]);
-          dq[2 * s + 1] = mfma16(prv.tr(2 * s + 1), Db, dq[2 * s + 1]);
+        if (HP) dq[s] = mfma16(bt[s], Db, dq[s]);
+        if (HC) {
+          sacc[1] = mfma16(k1[s], qB[s], sacc[1]);
+          pacc[1] = mfma16(k1[s], doB[s], pacc[1]);
         }
+        if (HC && s + AH < XNS) { k0[s + AH] = cur.row(0, s + AH); k1[s + AH] = cur.row(1, s + AH); }
+        if (HP) bt[s + AH] = prv.tr(s + AH);
+        __builtin_amdgcn_sched_barrier(0);
       }
-      if (has_cur) {
-        const int j0 = kt.j0(t);
-        float pv[8];
+      float pv[8], dsv[8];
 #pragma unroll
-        for (int e = 0; e < 8; ++e) pv[e] = __builtin_amdgcn_exp2f(fmaf(sacc[e >> 2][e & 3], scale_log2, -lse2));
-        if (!rm.full(j0)) {
-#pragma unroll
-          for (int e = 0; e < 8; ++e) pv[e] = rm.ok(j0, g, e >> 2, e & 3) ? pv[e] : 0.f;
+      for (int i = 0; i < XNC - XNS; ++i) {
+        const int nb = XNS + i;
+        if (HP) dq[nb] = mfma16(bt[nb], Db, dq[nb]);
+        if (HC) {
+          if (i < 8) pv[i] = __builtin_amdgcn_exp2f(fmaf(sacc[i >> 2][i & 3], scale_log2, -lse2));
+          else dsv[i - 8] = pv[i - 8] * fmaf(pacc[(i - 8) >> 2][(i - 8) & 3], scale, -dls);
         }
-        float dsv[8];
+        if (HP && nb + AH < XNC) bt[nb + AH] = prv.tr(nb + AH);
+        __builtin_amdgcn_sched_barrier(0);
+      }
+      if (HC) {
+        const int j0 = kt.j0(t);
+        if (!rm.full(j0)) {   // (the branch touches dS only)
 #pragma unroll
-        for (int e = 0; e < 8; ++e) dsv[e] = pv[e] * fmaf(pacc[e >> 2][e & 3], scale, -dls);
+          for (int e = 0; e < 8; ++e) dsv[e] = rm.ok(j0, g, e >> 2, e & 3) ? dsv[e] : 0.f;
+        }
         Db = pack_halves(dsv);
       }
-      if (t + 1 < n_it) wait_vm(t + 2 < n_it ? 8 : 0);
-    }
+      if (t + 1 < n_it) wait_vm(t + 2 < n_it ? 8 : 0);   // tile t + 1 complete before the next barrier
+    };
+    step(0, std::true_type{}, std::false_type{});
+    for (int t = 1; t < n_it; ++t) step(t, std::true_type{}, std::true_type{});
+    step(n_it, std::false_type{}, std::true_type{});
   }
   if (irow < Sq) {
     float* dst = a.dq + sv.q_off(p.dq_str, b) + h * p.dq_str[1] + (int64_t)irow * p.dq_str[2];
@@ -532,18 +569,37 @@ __global__ __launch_bounds__(XNT, 1) void k_dkv512(Params p, BwdArgs a, int part
       TileAddr tq, td;
       tq.set(sm_base + offsetof(SmemY, q) + buf * YTS, a_lane, t_lane);
       td.set(sm_base + offsetof(SmemY, d) + buf * YTS, a_lane, t_lane);
-      f32x4 sacc[2] = {zero4(), zero4()}, pacc[2] = {zero4(), zero4()};
-#pragma unroll
-      for (int s = 0; s < XNS; ++s) {
-        sacc[0] = mfma16(tq.row(0, s), kB[s], sacc[0]);
-        pacc[0] = mfma16(td.row(0, s), kB[s], pacc[0]);
-        sacc[1] = mfma16(tq.row(1, s), kB[s], sacc[1]);
-        pacc[1] = mfma16(td.row(1, s), kB[s], pacc[1]);
-      }
-      // rows 16 h + 4 g + r of the tile: LSE (log2 units, +inf for a row
-      // without keys) and delta * scale
+      // rows 16 h + 4 g + r of the tile: raw LSE and delta
       const f32x4 L0 = *(const f32x4*)&sm.lse[buf][4 * g], L1 = *(const f32x4*)&sm.lse[buf][16 + 4 * g];
       const f32x4 D0 = *(const f32x4*)&sm.dl[buf][4 * g], D1 = *(const f32x4*)&sm.dl[buf][16 + 4 * g];
+      // S = Q KV^T and dP = dO KV^T: four chains, operands two steps ahead;
+      // the products' first operands are read during the last steps
+      constexpr int AH = 2, AHB = 4;
+      f32x4 sacc[2] = {zero4(), zero4()}, pacc[2] = {zero4(), zero4()};
+      bf16x8 xq0[XNS], xq1[XNS], xd0[XNS], xd1[XNS], bd[XNC], bq[XNC];
+#pragma unroll
+      for (int i = 0; i < AH; ++i) {
+        xq0[i] = tq.row(0, i); xd0[i] = td.row(0, i); xq1[i] = tq.row(1, i); xd1[i] = td.row(1, i);
+      }
+      __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+      for (int s = 0; s < XNS; ++s) {
+        sacc[0] = mfma16(xq0[s], kB[s], sacc[0]);
+        pacc[0] = mfma16(xd0[s], kB[s], pacc[0]);
+        sacc[1] = mfma16(xq1[s], kB[s], sacc[1]);
+        pacc[1] = mfma16(xd1[s], kB[s], pacc[1]);
+        if (s + AH < XNS) {
+          xq0[s + AH] = tq.row(0, s + AH); xd0[s + AH] = td.row(0, s + AH);
+          xq1[s + AH] = tq.row(1, s + AH); xd1[s + AH] = td.row(1, s + AH);
+        } else {
+          const int n = s + AH - XNS;   // 0 .. AH - 1
+          bd[n] = td.tr(n); bq[n] = tq.tr(n);
+          if (AHB > AH) { bd[n + AH] = td.tr(n + AH); bq[n + AH] = tq.tr(n + AH); }
+        }
+        __builtin_amdgcn_sched_barrier(0);
+      }
+      // P = exp2(S scale log2 e - LSE log2 e) (LSE -inf: a row without keys,
+      // P = 0); dS = P (dP - delta) scale
       float pv[8], dsv[8];
 #pragma unroll
       for (int e = 0; e < 8; ++e) {
@@ -565,10 +621,14 @@ __global__ __launch_bounds__(XNT, 1) void k_dkv512(Params p, BwdArgs a, int part
         dsv[e] = pv[e] * (pacc[e >> 2][e & 3] - dv) * scale;
       }
       const bf16x8 Pb = pack_halves(pv), Sb = pack_halves(dsv);
+      __builtin_amdgcn_sched_barrier(0);
+      // dKV^T += dO^T P + Q^T (scale dS), operands four steps ahead
 #pragma unroll
       for (int n = 0; n < XNC; ++n) {
-        acc[n] = mfma16(td.tr(n), Pb, acc[n]);
-        acc[n] = mfma16(tq.tr(n), Sb, acc[n]);
+        acc[n] = mfma16(bd[n], Pb, acc[n]);
+        acc[n] = mfma16(bq[n], Sb, acc[n]);
+        if (n + AHB < XNC) { bd[n + AHB] = td.tr(n + AHB); bq[n + AHB] = tq.tr(n + AHB); }
+        __builtin_amdgcn_sched_barrier(0);
       }
       if (t + 1 < n_it) wait_vm(0);
     }

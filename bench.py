@@ -21,7 +21,8 @@ Rank 0 prints one JSON line.  It also carries
   * ``cpu_baseline``: the fp64 CPU oracle timed on a bounded sample of the
     same workload (a subset of the KV head groups),
   * extra timings (deterministic mode, the 4-chunk K/V split with the lse
-    merge, the forward).
+    merge, the forward, a packed variable-length batch, and the shared-KV
+    head-dim-512 path).
 """
 
 from __future__ import annotations
@@ -131,6 +132,63 @@ def bench_varlen(stream, name: str = "varlen16_gqa4_causal_br", steps: int = 10)
             "tflops": round(flops / (ms * 1e-3) / 1e12, 2)}
 
 
+def bench_shared_kv(stream, name: str = "mla_swa512_s4096", steps: int = 10, warmup: int = 3) -> dict:
+    """One tensor as keys and values at head dim 512 (packed TND, bottom-right
+    sliding window, sink logits): preprocess + attn_bwd with ATTN_SHARED_KV
+    per step, and the forward.  Counted FLOPs as for the other workloads,
+    10 * D per allowed pair per query head (dK and dV of the shared tensor
+    are both counted; they are both computed)."""
+    import numpy as np
+    import torch
+
+    from attention_backward_attn_amd import binding as ab
+    from attention_backward_attn_amd.inputs import SHARED_KV_WORKLOADS, make_shared_kv_inputs
+    from attention_backward_attn_amd.mask import allowed_pairs
+    w = SHARED_KV_WORKLOADS[name]
+    x = make_shared_kv_inputs(w)
+    dev = torch.device("cuda:0")
+    q, kv, do = (torch.from_numpy(x[n]).to(dev, torch.bfloat16) for n in ("q", "kv", "do"))
+    sinks = None if x["sinks"] is None else torch.from_numpy(x["sinks"]).to(dev)
+    kw = dict(mask="bottom_right", window_left=w.window_left, cu_seqlens_q=torch.from_numpy(x["cu_q"]).to(dev),
+              cu_seqlens_k=torch.from_numpy(x["cu_k"]).to(dev), max_seqlen_q=w.max_q, max_seqlen_k=w.max_k)
+    # O in the inputs' dtype (the page requires attn_out to match q)
+    o, lse = ab.forward(q, kv, kv, sinks=sinks, scale=w.scale, o_dtype=torch.bfloat16, stream=stream, **kw)
+    dq = torch.empty(q.shape, device=dev)
+    dkv = torch.empty(kv.shape, device=dev)
+    delta = torch.empty(lse.shape, device=dev)
+    dsinks = torch.empty(w.N1, device=dev) if sinks is not None else None
+    p = ab.make_problem(q, kv, kv, o=o, do=do, dq=dq, dk=dkv, scale=w.scale, **kw)
+
+    def step():
+        ab.attn_bwd_preprocess(p, o, do, lse, sinks, delta, dsinks, None, None, None, stream)
+        ab.attn_bwd(p, q, kv, kv, do, lse, delta, None, dq, dkv, None, None, ab.ATTN_SHARED_KV, stream)
+
+    def fwd():
+        ab.attn_fwd_lse(p, q, kv, kv, None, sinks, o, lse, stream)
+
+    def time_it(fn, n):
+        for _ in range(warmup):
+            fn()
+        torch.cuda.synchronize()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record(stream)
+        for _ in range(n):
+            fn()
+        e1.record(stream)
+        torch.cuda.synchronize()
+        return e0.elapsed_time(e1) / n
+    ms = time_it(step, steps)
+    fwd_ms = time_it(fwd, steps)
+    pairs = sum(allowed_pairs(a, b, "bottom_right", w.window_left) for a, b in w.seqs)
+    flops = 10.0 * w.D * pairs * w.N1
+    return {"workload": name, "T1": int(x["cu_q"][-1]), "T2": int(x["cu_k"][-1]), "N1": w.N1, "N2": w.N2,
+            "D": w.D, "window_left": w.window_left, "allowed_pairs_per_head": pairs, "counted_flop": flops,
+            "ms_per_step": round(ms, 4), "tflops": round(flops / (ms * 1e-3) / 1e12, 2),
+            "pct_peak": round(100.0 * flops / (ms * 1e-3) / 1e12 / PEAK_BF16_TFLOPS, 2),
+            "forward_ms": round(fwd_ms, 4),
+            "forward_tflops": round(4.0 * w.D * pairs * w.N1 / (fwd_ms * 1e-3) / 1e12, 2)}
+
+
 def cpu_baseline(w, x, groups: int):
     """Time the fp64 oracle backward on KV groups [0, groups) of batch 0."""
     import numpy as np
@@ -180,6 +238,16 @@ def main():
     if not torch.cuda.is_available():
         print("bench.py needs a GPU", file=sys.stderr)
         sys.exit(1)
+    from attention_backward_attn_amd.inputs import SHARED_KV_WORKLOADS
+    if args.workload in SHARED_KV_WORKLOADS:
+        # the shared-KV (head dim 512) path alone, on its own line
+        r = bench_shared_kv(torch.cuda.current_stream(), args.workload, steps=args.steps, warmup=args.warmup)
+        print(json.dumps({"metric": "shared-KV attention-backward TFLOP/s (D=512)", "value": r["tflops"],
+                          "unit": "TFLOP/s", "n_gpus": 1, "steps": args.steps, "warmup": args.warmup,
+                          "ms_per_step": r["ms_per_step"], "higher_is_better": True, "scaling": "weak",
+                          "vs_baseline": None, "dtype": "bf16", "data": "synthetic (seeded N(0,1) inputs)",
+                          "config": {"workload": args.workload}, "shared_kv": r}), flush=True)
+        return
     w = WORKLOADS[args.workload or HEADLINE]
     dev = torch.device("cuda:0")
     x = make_inputs(w)
@@ -313,6 +381,7 @@ def main():
             out["chunked_kv4"] = {"ms_per_step": round(ch_ms, 4), "tflops": round(flops / (ch_ms * 1e-3) / 1e12, 2)}
         if w.name == HEADLINE:
             out["varlen"] = bench_varlen(stream)
+            out["shared_kv"] = bench_shared_kv(stream)
     if not args.no_cpu_baseline:
         out["cpu_baseline"] = cpu_baseline(w, x, args.cpu_groups)
     print(json.dumps(out), flush=True)
