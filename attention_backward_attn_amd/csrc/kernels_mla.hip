@@ -8,7 +8,7 @@
 //             shared tensor summed, per that page's Phase 3)
 // All use v_mfma_f32_16x16x32_bf16 at one wave per SIMD.  At D = 512 a wave
 // keeps 16 rows (or keys) of fragments and a 16 x 512 fp32 accumulator in
-// registers; the other operand streams through LDS in 1 KB swizzled rows.
+// registers; the other operand streams through LDS in padded 1 KB rows.
 //
 // MFMA 16x16x32 bf16 operand layout (lane l, g = l / 16, r = 0..3):
 //   A[m][k]: lane holds m = l % 16, k = 8 g + 0..7
@@ -34,11 +34,11 @@ constexpr int XNS = XD / 32;     // k-steps over the head dim (16)
 constexpr int XNC = XD / 16;     // 16-column blocks of the head dim (32)
 constexpr int XBK = 32;          // keys per tile (forward, dQ)
 constexpr int XBQ = 64;          // query rows per workgroup (forward, dQ)
-constexpr int XTS = XBK * XRB;   // key tile bytes (32 KB)
+constexpr int XTS = XBK * (XRB + 32);   // key tile bytes (32 padded rows)
 constexpr int XNB = 4;           // key tile buffers (forward, dQ)
 constexpr int YBK = 64;          // keys per workgroup (dKV)
 constexpr int YBQ = 32;          // query rows per tile (dKV)
-constexpr int YTS = YBQ * XRB;   // Q or dO tile bytes (32 KB)
+constexpr int YTS = YBQ * (XRB + 32);   // Q or dO tile bytes (32 padded rows)
 
 __device__ inline f32x4 mfma16(bf16x8 a, bf16x8 b, f32x4 c) {
   return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
@@ -46,45 +46,34 @@ __device__ inline f32x4 mfma16(bf16x8 a, bf16x8 b, f32x4 c) {
 
 __device__ inline f32x4 zero4() { return f32x4{0.f, 0.f, 0.f, 0.f}; }
 
-// Swizzled 1 KB rows: 16-byte chunk c of row r sits at chunk position
-// c ^ f(r).  f permutes 0..15 over every 16 aligned rows, so the 16 lanes of
-// a ds_read_b128 (one chunk of 16 consecutive rows) hit 16 distinct bank
-// groups; f / 2 permutes 0..7 over every 8 aligned rows, so a transposing
-// read (two adjacent chunks of 8 consecutive rows per 32 lanes) does too.
-// f(r + 16) = f(r): the second 16-row half of a tile is the first plus 16 KB.
-struct Swz512 {
-  __host__ __device__ static constexpr int f(int r) { return 2 * (r & 7) + ((r >> 3) & 1); }
-  // row-read lane base: row l % 16, chunk l / 16; k-step s reads
-  // (base ^ 64 (s % 4)) + 256 (s / 4)
-  __device__ static int a_lane(int l) {
-    const int r = l & 15;
-    return r * XRB + 16 * ((l >> 4) ^ f(r));
-  }
-  // transposing-read lane base: lane 4 e + q of 16-lane group g addresses
-  // row 4 g + e, columns 4 q .. 4 q + 3; column block nb reads
-  // (base ^ 32 (nb % 8)) + 256 (nb / 8), rows + 16 at + 16 KB
-  __device__ static int t_lane(int l) {
-    const int j = l & 15, r = 4 * (l >> 4) + (j >> 2), q = j & 3;
-    return r * XRB + 16 * ((q >> 1) ^ f(r)) + 8 * (q & 1);
-  }
-};
+// LDS rows of 1 KB padded to 1056 bytes.  Measured on gfx950 with the two
+// operand read patterns below (in-bounds probe), this stride serves both at
+// full speed -- ds_read_b128 of one 16-byte chunk of 16 consecutive rows at
+// 2.7 cycles per wave instruction per CU, ds_read_b64_tr_b16 of 4 x 8 bytes
+// of 16 consecutive rows at 1.67 -- while unpadded 1 KB rows with chunks
+// XOR-permuted per row run the row reads at 4.5.  Every operand address is
+// then a lane base plus a constant.
+constexpr int XRS = XRB + 32;      // LDS row stride (bytes)
+constexpr int XHS = 16 * XRS;      // second 16-row half of a tile
+// row-read lane base: row l % 16, chunk l / 16 (k-step s at + 64 s)
+__device__ inline int a_lane_of(int l) { return (l & 15) * XRS + 16 * (l >> 4); }
+// transposing-read lane base: lane 4 e + q of 16-lane group g addresses row
+// 4 g + e, columns 4 q .. 4 q + 3 (column block nb at + 32 nb)
+__device__ inline int t_lane_of(int l) { return (4 * (l >> 4) + ((l & 15) >> 2)) * XRS + 8 * (l & 3); }
 
-// Per-lane read addresses of one swizzled tile: the four row-read bases and
-// the eight transposing-read bases, offset to the tile's buffer.
+// Per-lane read addresses of one tile: row reads and transposing reads.
 struct TileAddr {
-  unsigned int a[4], t[8];
+  unsigned int a, t;
   __device__ inline void set(unsigned int tile, int a_lane, int t_lane) {
-#pragma unroll
-    for (int i = 0; i < 4; ++i) a[i] = tile + (a_lane ^ (64 * i));
-#pragma unroll
-    for (int i = 0; i < 8; ++i) t[i] = tile + (t_lane ^ (32 * i));
+    a = tile + a_lane;
+    t = tile + t_lane;
   }
   // A operand: rows 16 h + l % 16, head-dim step s
-  __device__ inline bf16x8 row(int h, int s) const { return lds_b128_at(a[s & 3] + 256 * (s >> 2) + 16384 * h); }
+  __device__ inline bf16x8 row(int h, int s) const { return lds_b128_at(a + 64 * s + XHS * h); }
   // transposed operand of column block nb over the tile's 32 rows in slot order
   __device__ inline bf16x8 tr(int nb) const {
-    const unsigned int x = t[nb & 7] + 256 * (nb >> 3);
-    return cat44(lds_tr4_at(x), lds_tr4_at(x + 16384));
+    const unsigned int x = t + 32 * nb;
+    return cat44(lds_tr4_at(x), lds_tr4_at(x + XHS));
   }
 };
 
@@ -94,15 +83,15 @@ __device__ inline bf16x8 pack_halves(const float* v) {   // v[0..3]: half 0, v[4
   return pack8(v);
 }
 
-// Direct loads of a tile of rows (1 KB each) into swizzled LDS: lane l of the
-// load of row r brings global chunk l ^ f(r) to chunk position l.  Rows past
-// `rows` (the buffer resource's extent) arrive as zeros.
+// Direct loads of a tile of rows (1 KB each) into padded LDS rows: one load
+// per row, lane l bringing its 16-byte chunk l.  Rows past `rows` (the buffer
+// resource's extent) arrive as zeros.
 __device__ inline void stage_rows(const unsigned short* src, int64_t row_str, int rows, unsigned int lds_tile,
                                   int r0, int nrows, int l) {
   const __amdgpu_buffer_rsrc_t rs = buf_rsrc(src, rows * (int)(2 * row_str));
   for (int k = 0; k < nrows; ++k) {
     const int r = r0 + k;
-    lds_dma16(rs, __builtin_amdgcn_readfirstlane(lds_tile + r * XRB), r * (int)(2 * row_str) + 16 * (l ^ Swz512::f(r)));
+    lds_dma16(rs, __builtin_amdgcn_readfirstlane(lds_tile + r * XRS), r * (int)(2 * row_str) + 16 * l);
   }
 }
 
@@ -192,6 +181,20 @@ __global__ __launch_bounds__(XNT, 1) void k_fwd512(Params p, FwdArgs a) {
 
   const unsigned short* q = (const unsigned short*)a.q + sv.q_off(p.q_str, b) + h * p.q_str[1];
   const unsigned short* kv = (const unsigned short*)a.k + sv.k_off(p.k_str, b) + hk * p.k_str[1];
+  const KeyTiles kt = key_tiles(msk, i0, min(i0 + XBQ, Sq), Sk);
+  RowMask rm;
+  rm.init(msk, irow, i0 + 16 * w, g, Sk);
+  const unsigned int sm_base = __builtin_amdgcn_readfirstlane(lds_addr(&sm));
+  const int a_lane = a_lane_of(l), t_lane = t_lane_of(l);
+  auto issue = [&](int it) {
+    const int j0 = kt.j0(it);
+    stage_rows(kv + (int64_t)j0 * p.k_str[2], p.k_str[2], min(Sk - j0, XBK), sm_base + (it % XNB) * XTS, 8 * w, 8, l);
+  };
+
+  const int n_it = kt.n_it;
+  // key tiles 0 and 1 in flight before the fragment loads
+  if (n_it > 0) issue(0);
+  if (n_it > 1) issue(1);
   bf16x8 qB[XNS];
   {
     const int64_t ic = min(irow, Sq - 1);
@@ -204,37 +207,20 @@ __global__ __launch_bounds__(XNT, 1) void k_fwd512(Params p, FwdArgs a) {
     m_run = a.sinks[h] * kLog2e;
     l_run = g == 0 ? 1.f : 0.f;
   }
-  wait_vm_loads();
 
-  const KeyTiles kt = key_tiles(msk, i0, min(i0 + XBQ, Sq), Sk);
-  RowMask rm;
-  rm.init(msk, irow, i0 + 16 * w, g, Sk);
-  const unsigned int sm_base = __builtin_amdgcn_readfirstlane(lds_addr(&sm));
-  const int a_lane = Swz512::a_lane(l), t_lane = Swz512::t_lane(l);
-  auto issue = [&](int it) {
-    const int j0 = kt.j0(it);
-    stage_rows(kv + (int64_t)j0 * p.k_str[2], p.k_str[2], min(Sk - j0, XBK), sm_base + (it % XNB) * XTS, 8 * w, 8, l);
-  };
+  wait_vm_loads();   // fragments and both key tiles
 
   f32x4 o[XNC];
 #pragma unroll
   for (int n = 0; n < XNC; ++n) o[n] = zero4();
   bf16x8 Pb = as_bf16x8(u16x8{0, 0, 0, 0, 0, 0, 0, 0});
-  const int n_it = kt.n_it;
   if (n_it > 0) {
-    issue(0);
-    if (n_it > 1) {
-      issue(1);
-      wait_vm(8);
-    } else {
-      wait_vm(0);
-    }
     // One tile step: the S^T chains of tile t (when HC) among the O^T
     // products of tile t - 1 (when HP), operands two product steps ahead,
     // then the online softmax of tile t.  First and last steps peeled.
     auto step = [&](int t, auto hc_, auto hp_) {
       constexpr bool HC = decltype(hc_)::value, HP = decltype(hp_)::value;
-      constexpr int AH = 2;
+      constexpr int AH = 3;
       __syncthreads();   // tile t complete; tile t - 3's buffer free
       if (t + 2 < n_it) issue(t + 2);
       TileAddr cur, prv;
@@ -345,6 +331,21 @@ __global__ __launch_bounds__(XNT, 1) void k_dq512(Params p, BwdArgs a) {
   const unsigned short* q = (const unsigned short*)a.q + sv.q_off(p.q_str, b) + h * p.q_str[1];
   const unsigned short* dout = (const unsigned short*)a.dout + sv.q_off(p.do_str, b) + h * p.do_str[1];
   const unsigned short* kv = (const unsigned short*)a.k + sv.k_off(p.k_str, b) + hk * p.k_str[1];
+  const KeyTiles kt = key_tiles(msk, i0, min(i0 + XBQ, Sq), Sk);
+  RowMask rm;
+  rm.init(msk, irow, i0 + 16 * w, g, Sk);
+  const unsigned int sm_base = __builtin_amdgcn_readfirstlane(lds_addr(&sm));
+  const int a_lane = a_lane_of(l), t_lane = t_lane_of(l);
+  auto issue = [&](int it) {
+    const int j0 = kt.j0(it);
+    stage_rows(kv + (int64_t)j0 * p.k_str[2], p.k_str[2], min(Sk - j0, XBK), sm_base + (it % XNB) * XTS, 8 * w, 8, l);
+  };
+
+  const int n_it = kt.n_it;
+  // key tiles 0 and 1 in flight before the fragment loads, so that their
+  // latencies overlap
+  if (n_it > 0) issue(0);
+  if (n_it > 1) issue(1);
   bf16x8 qB[XNS], doB[XNS];
   {
     const int64_t ic = min(irow, Sq - 1);
@@ -360,31 +361,14 @@ __global__ __launch_bounds__(XNT, 1) void k_dq512(Params p, BwdArgs a) {
     lse2 = lv == -INFINITY ? INFINITY : lv * kLog2e;
     dls = a.delta[((int64_t)b * p.Hq + h) * p.Sq + irow] * scale;
   }
-  wait_vm_loads();
 
-  const KeyTiles kt = key_tiles(msk, i0, min(i0 + XBQ, Sq), Sk);
-  RowMask rm;
-  rm.init(msk, irow, i0 + 16 * w, g, Sk);
-  const unsigned int sm_base = __builtin_amdgcn_readfirstlane(lds_addr(&sm));
-  const int a_lane = Swz512::a_lane(l), t_lane = Swz512::t_lane(l);
-  auto issue = [&](int it) {
-    const int j0 = kt.j0(it);
-    stage_rows(kv + (int64_t)j0 * p.k_str[2], p.k_str[2], min(Sk - j0, XBK), sm_base + (it % XNB) * XTS, 8 * w, 8, l);
-  };
+  wait_vm_loads();   // fragments, LSE / delta and both key tiles
 
   f32x4 dq[XNC];
 #pragma unroll
   for (int n = 0; n < XNC; ++n) dq[n] = zero4();
   bf16x8 Db = as_bf16x8(u16x8{0, 0, 0, 0, 0, 0, 0, 0});
-  const int n_it = kt.n_it;
   if (n_it > 0) {
-    issue(0);
-    if (n_it > 1) {
-      issue(1);
-      wait_vm(8);
-    } else {
-      wait_vm(0);
-    }
     // One tile step: the S^T / dP^T chains of tile t (when HC) among the dQ^T
     // products of tile t - 1 (when HP, first half of the columns), then the
     // second half of those products among the exponentials and dS arithmetic
@@ -392,7 +376,9 @@ __global__ __launch_bounds__(XNT, 1) void k_dq512(Params p, BwdArgs a) {
     // last steps are peeled, so the main loop has no branches.
     auto step = [&](int t, auto hc_, auto hp_) {
       constexpr bool HC = decltype(hc_)::value, HP = decltype(hp_)::value;
-      constexpr int AH = 2;
+      // read-ahead: three steps of the chains; ten dQ product operands in
+      // flight when the second region (one product per step) starts
+      constexpr int AH = 3, BAH = 10, XTRA = BAH - AH;
       __syncthreads();   // tile t complete; tile t - 3's buffer free
       if (t + 2 < n_it) issue(t + 2);
       TileAddr cur, prv;
@@ -419,6 +405,7 @@ __global__ __launch_bounds__(XNT, 1) void k_dq512(Params p, BwdArgs a) {
         }
         if (HC && s + AH < XNS) { k0[s + AH] = cur.row(0, s + AH); k1[s + AH] = cur.row(1, s + AH); }
         if (HP) bt[s + AH] = prv.tr(s + AH);
+        if (HP && s >= XNS - XTRA) bt[XNS + AH + s - (XNS - XTRA)] = prv.tr(XNS + AH + s - (XNS - XTRA));
         __builtin_amdgcn_sched_barrier(0);
       }
       float pv[8], dsv[8];
@@ -430,7 +417,7 @@ __global__ __launch_bounds__(XNT, 1) void k_dq512(Params p, BwdArgs a) {
           if (i < 8) pv[i] = __builtin_amdgcn_exp2f(fmaf(sacc[i >> 2][i & 3], scale_log2, -lse2));
           else dsv[i - 8] = pv[i - 8] * fmaf(pacc[(i - 8) >> 2][(i - 8) & 3], scale, -dls);
         }
-        if (HP && nb + AH < XNC) bt[nb + AH] = prv.tr(nb + AH);
+        if (HP && nb + BAH < XNC) bt[nb + BAH] = prv.tr(nb + BAH);
         __builtin_amdgcn_sched_barrier(0);
       }
       if (HC) {
@@ -463,7 +450,7 @@ __global__ __launch_bounds__(XNT, 1) void k_dq512(Params p, BwdArgs a) {
 // 16 w .. 16 w + 15 with their KV fragments and a 16 x 512 fp32 dKV^T
 // accumulator (one key per lane) in registers.  The workgroup walks the
 // part's (head, 32-row tile) iterations; Q and dO tiles come straight into
-// two swizzled LDS buffers, one tile ahead.  Per tile: S = Q KV^T and
+// two padded LDS buffers, one tile ahead.  Per tile: S = Q KV^T and
 // dP = dO KV^T (one key per lane), P and dS, then
 // dKV^T += dO^T P + Q^T (scale dS), whose reduction over the tile's rows
 // uses the accumulators' slot order.  Several parts add into zeroed dKV.
@@ -530,7 +517,7 @@ __global__ __launch_bounds__(XNT, 1) void k_dkv512(Params p, BwdArgs a, int part
   }
 
   const unsigned int sm_base = __builtin_amdgcn_readfirstlane(lds_addr(&sm));
-  const int a_lane = Swz512::a_lane(l), t_lane = Swz512::t_lane(l);
+  const int a_lane = a_lane_of(l), t_lane = t_lane_of(l);
   const int64_t lrow = (int64_t)p.Sq;   // rows per (batch, head) of LSE / delta
   auto tile_rows = [&](int it, int* hh, int* i0) {
     *hh = h_begin + it / nqb;
@@ -574,7 +561,7 @@ __global__ __launch_bounds__(XNT, 1) void k_dkv512(Params p, BwdArgs a, int part
       const f32x4 D0 = *(const f32x4*)&sm.dl[buf][4 * g], D1 = *(const f32x4*)&sm.dl[buf][16 + 4 * g];
       // S = Q KV^T and dP = dO KV^T: four chains, operands two steps ahead;
       // the products' first operands are read during the last steps
-      constexpr int AH = 2, AHB = 4;
+      constexpr int AH = 3, AHB = 2 * AH;
       f32x4 sacc[2] = {zero4(), zero4()}, pacc[2] = {zero4(), zero4()};
       bf16x8 xq0[XNS], xq1[XNS], xd0[XNS], xd1[XNS], bd[XNC], bq[XNC];
 #pragma unroll
