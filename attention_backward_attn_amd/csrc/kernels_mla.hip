@@ -311,10 +311,18 @@ __global__ __launch_bounds__(XNT, 1) void k_fwd512(Params p, FwdArgs a) {
 // keeps Q and dO fragments of its 16 rows.  Per 32-key tile t (one barrier):
 // S^T = KV Q^T and dP^T = KV dO^T as four chains sharing each KV row read,
 // among the dQ^T products of tile t - 1; then P = exp2(S - LSE) and
-// dS = P (dP - delta) (scale folded in) for tile t.
+// dS = P (dP - delta) (scale folded in) for tile t, published in LDS.  The
+// products split the head dim: wave w accumulates dQ^T columns
+// 128 w .. 128 w + 127 of all 64 rows, from the four waves' dS -- so each
+// KV^T block is read once per workgroup rather than once per wave.
 // ---------------------------------------------------------------------------
+struct __attribute__((aligned(1024))) SmemXD {
+  unsigned char k[XNB][XTS];
+  bf16x8 ds[2][4][64];   // dS operands of the previous two tiles, per wave and lane
+};
+
 __global__ __launch_bounds__(XNT, 1) void k_dq512(Params p, BwdArgs a) {
-  __shared__ SmemX sm;
+  __shared__ SmemXD sm;
   const int tid = threadIdx.x, l = tid & 63, lr = l & 15, g = l >> 4;
   const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
   const BlockXYZ blk = a.xmajor ? xcd_block_xmajor() : xcd_block();
@@ -364,60 +372,74 @@ __global__ __launch_bounds__(XNT, 1) void k_dq512(Params p, BwdArgs a) {
 
   wait_vm_loads();   // fragments, LSE / delta and both key tiles
 
-  f32x4 dq[XNC];
+  // dQ^T of columns 128 w + 16 c + 4 g + r for rows 16 rb + lane % 16:
+  // dq[4 c + rb], c = 0..7, rb = 0..3
+  constexpr int NCW = XNC / 4;   // 16-column blocks per wave
+  f32x4 dq[4 * NCW];
 #pragma unroll
-  for (int n = 0; n < XNC; ++n) dq[n] = zero4();
-  bf16x8 Db = as_bf16x8(u16x8{0, 0, 0, 0, 0, 0, 0, 0});
+  for (int n = 0; n < 4 * NCW; ++n) dq[n] = zero4();
+  const unsigned int ds_base = sm_base + offsetof(SmemXD, ds);
   if (n_it > 0) {
-    // One tile step: the S^T / dP^T chains of tile t (when HC) among the dQ^T
-    // products of tile t - 1 (when HP, first half of the columns), then the
-    // second half of those products among the exponentials and dS arithmetic
-    // of tile t.  Operands are read two product steps ahead.  The first and
-    // last steps are peeled, so the main loop has no branches.
+    // One tile step: the S^T / dP^T chains of tile t (when HC) among the
+    // first half of the dQ^T products of tile t - 1 (when HP), then the
+    // second half among the exponentials and dS arithmetic of tile t.
+    // Operands are read ahead; the first and last steps are peeled, so the
+    // main loop has no branches.
     auto step = [&](int t, auto hc_, auto hp_) {
       constexpr bool HC = decltype(hc_)::value, HP = decltype(hp_)::value;
-      // read-ahead: three steps of the chains; ten dQ product operands in
-      // flight when the second region (one product per step) starts
-      constexpr int AH = 3, BAH = 10, XTRA = BAH - AH;
-      __syncthreads();   // tile t complete; tile t - 3's buffer free
+      constexpr int AH = 3;
+      __syncthreads();   // tile t complete, dS of tile t - 1 published; tile t - 3's buffer free
       if (t + 2 < n_it) issue(t + 2);
       TileAddr cur, prv;
       if (HC) cur.set(sm_base + (t % XNB) * XTS, a_lane, t_lane);
-      if (HP) prv.set(sm_base + ((t + XNB - 1) % XNB) * XTS, a_lane, t_lane);
+      // (transposing reads of this wave's column blocks: base offset to block NCW w)
+      if (HP) prv.set(sm_base + ((t + XNB - 1) % XNB) * XTS, a_lane, t_lane + 32 * NCW * w);
       f32x4 sacc[2] = {zero4(), zero4()}, pacc[2] = {zero4(), zero4()};
-      bf16x8 k0[XNS], k1[XNS], bt[XNC];
+      bf16x8 k0[XNS], k1[XNS], kt_[NCW], dsb[4];
+      const unsigned int dsp = ds_base + ((t + 1) & 1) * (4 * 64 * 16) + 16 * l;   // dS of tile t - 1
 #pragma unroll
-      for (int i = 0; i < AH; ++i) {
+      for (int i = 0; i < AH; ++i)
         if (HC) { k0[i] = cur.row(0, i); k1[i] = cur.row(1, i); }
-        if (HP) bt[i] = prv.tr(i);
+      if (HP) {
+#pragma unroll
+        for (int rb = 0; rb < 4; ++rb) dsb[rb] = lds_b128_at(dsp + rb * 64 * 16);
+        kt_[0] = prv.tr(0);
+        kt_[1] = prv.tr(1);
       }
       __builtin_amdgcn_sched_barrier(0);
+      // dQ^T product n = 4 c + rb (column block c, row block rb); the K^T
+      // operand of block c + 2 is read when block c starts
+      auto product = [&](int n) {
+        if ((n & 3) == 0 && (n >> 2) + 2 < NCW) kt_[(n >> 2) + 2] = prv.tr((n >> 2) + 2);
+        dq[n] = mfma16(kt_[n >> 2], dsb[n & 3], dq[n]);
+      };
+      // region 1: 64 chain products among dQ^T products 0 .. XNS - 3 (the
+      // first two steps wait only for their own rows' reads)
+      constexpr int D1 = 2;
 #pragma unroll
       for (int s = 0; s < XNS; ++s) {
         if (HC) {
           sacc[0] = mfma16(k0[s], qB[s], sacc[0]);
           pacc[0] = mfma16(k0[s], doB[s], pacc[0]);
         }
-        if (HP) dq[s] = mfma16(bt[s], Db, dq[s]);
+        if (HP && s >= D1) product(s - D1);
         if (HC) {
           sacc[1] = mfma16(k1[s], qB[s], sacc[1]);
           pacc[1] = mfma16(k1[s], doB[s], pacc[1]);
         }
         if (HC && s + AH < XNS) { k0[s + AH] = cur.row(0, s + AH); k1[s + AH] = cur.row(1, s + AH); }
-        if (HP) bt[s + AH] = prv.tr(s + AH);
-        if (HP && s >= XNS - XTRA) bt[XNS + AH + s - (XNS - XTRA)] = prv.tr(XNS + AH + s - (XNS - XTRA));
         __builtin_amdgcn_sched_barrier(0);
       }
+      // region 2: the remaining dQ^T products among the exponentials and dS
+      // of tile t
       float pv[8], dsv[8];
 #pragma unroll
-      for (int i = 0; i < XNC - XNS; ++i) {
-        const int nb = XNS + i;
-        if (HP) dq[nb] = mfma16(bt[nb], Db, dq[nb]);
-        if (HC) {
+      for (int i = 0; i < XNC - (XNS - D1); ++i) {
+        if (HP) product(XNS - D1 + i);
+        if (HC && i < 16) {
           if (i < 8) pv[i] = __builtin_amdgcn_exp2f(fmaf(sacc[i >> 2][i & 3], scale_log2, -lse2));
           else dsv[i - 8] = pv[i - 8] * fmaf(pacc[(i - 8) >> 2][(i - 8) & 3], scale, -dls);
         }
-        if (HP && nb + BAH < XNC) bt[nb + BAH] = prv.tr(nb + BAH);
         __builtin_amdgcn_sched_barrier(0);
       }
       if (HC) {
@@ -426,7 +448,9 @@ __global__ __launch_bounds__(XNT, 1) void k_dq512(Params p, BwdArgs a) {
 #pragma unroll
           for (int e = 0; e < 8; ++e) dsv[e] = rm.ok(j0, g, e >> 2, e & 3) ? dsv[e] : 0.f;
         }
-        Db = pack_halves(dsv);
+        // publish dS of tile t (read by every wave in the next step)
+        *(lds_u16x8*)(size_t)(ds_base + (t & 1) * (4 * 64 * 16) + w * 64 * 16 + 16 * l) =
+            __builtin_bit_cast(u16x8, pack_halves(dsv));
       }
       if (t + 1 < n_it) wait_vm(t + 2 < n_it ? 8 : 0);   // tile t + 1 complete before the next barrier
     };
@@ -434,12 +458,17 @@ __global__ __launch_bounds__(XNT, 1) void k_dq512(Params p, BwdArgs a) {
     for (int t = 1; t < n_it; ++t) step(t, std::true_type{}, std::true_type{});
     step(n_it, std::false_type{}, std::true_type{});
   }
-  if (irow < Sq) {
-    float* dst = a.dq + sv.q_off(p.dq_str, b) + h * p.dq_str[1] + (int64_t)irow * p.dq_str[2];
+  // dQ rows i0 + 16 rb + lane % 16, columns 128 w + 16 c + 4 g .. + 3
+  float* dqp = a.dq + sv.q_off(p.dq_str, b) + h * p.dq_str[1];
 #pragma unroll
-    for (int n = 0; n < XNC; ++n) {
-      f32x4* d4 = (f32x4*)(dst + 16 * n + 4 * g);
-      *d4 = a.accumulate_dq ? *d4 + dq[n] : dq[n];
+  for (int rb = 0; rb < 4; ++rb) {
+    const int i = i0 + 16 * rb + lr;
+    if (i < Sq) {
+#pragma unroll
+      for (int c = 0; c < NCW; ++c) {
+        f32x4* d4 = (f32x4*)(dqp + (int64_t)i * p.dq_str[2] + 128 * w + 16 * c + 4 * g);
+        *d4 = a.accumulate_dq ? *d4 + dq[4 * c + rb] : dq[4 * c + rb];
+      }
     }
   }
 }
@@ -447,17 +476,22 @@ __global__ __launch_bounds__(XNT, 1) void k_dq512(Params p, BwdArgs a) {
 // ---------------------------------------------------------------------------
 // k_dkv512: the dKV pass.  One workgroup of four waves per (64-key block,
 // part of a KV head's query group, batch entry); wave w owns keys
-// 16 w .. 16 w + 15 with their KV fragments and a 16 x 512 fp32 dKV^T
-// accumulator (one key per lane) in registers.  The workgroup walks the
+// 16 w .. 16 w + 15 with their KV fragments, and a 64 x 128 fp32 slice of
+// dKV^T in registers.  The workgroup walks the
 // part's (head, 32-row tile) iterations; Q and dO tiles come straight into
 // two padded LDS buffers, one tile ahead.  Per tile: S = Q KV^T and
-// dP = dO KV^T (one key per lane), P and dS, then
-// dKV^T += dO^T P + Q^T (scale dS), whose reduction over the tile's rows
-// uses the accumulators' slot order.  Several parts add into zeroed dKV.
+// dP = dO KV^T for the wave's keys (one key per lane), P and dS, published
+// in LDS; in the next step dKV^T += dO^T P + Q^T (scale dS) runs under the
+// next tile's S / dP, split over the head dim: wave w accumulates columns
+// 128 w .. 128 w + 127 for all 64 keys, from the four waves' P and dS, with
+// its dO^T / Q^T operands read into registers during the tile's own step.
+// The reduction over the tile's rows uses the accumulators' slot order.
+// Several parts add into zeroed dKV.
 // ---------------------------------------------------------------------------
 struct __attribute__((aligned(1024))) SmemY {
   unsigned char q[2][YTS];
   unsigned char d[2][YTS];
+  bf16x8 px[2][2][4][64];   // [tile parity][P, dS][wave][lane]: B operands of the dKV^T products
   float lse[2][64];   // raw LSE / delta rows (a wave-wide load fills 64 entries)
   float dl[2][64];
 };
@@ -519,119 +553,203 @@ __global__ __launch_bounds__(XNT, 1) void k_dkv512(Params p, BwdArgs a, int part
   const unsigned int sm_base = __builtin_amdgcn_readfirstlane(lds_addr(&sm));
   const int a_lane = a_lane_of(l), t_lane = t_lane_of(l);
   const int64_t lrow = (int64_t)p.Sq;   // rows per (batch, head) of LSE / delta
-  auto tile_rows = [&](int it, int* hh, int* i0) {
-    *hh = h_begin + it / nqb;
-    *i0 = lo_al + YBQ * (it % nqb);
-  };
+  // tile walk of the loads: heads outer, 32-row tiles inner; pointers to the
+  // next tile's Q, dO, LSE and delta rows advance by one tile, and wrap to
+  // the next head after the last row tile
+  int ld_i0 = lo_al, cur_i0 = lo_al;
+  const int i_end = lo_al + YBQ * nqb;
+  const unsigned short* ld_q = (const unsigned short*)a.q + sv.q_off(p.q_str, b) + h_begin * p.q_str[1] + (int64_t)lo_al * p.q_str[2];
+  const unsigned short* ld_d = (const unsigned short*)a.dout + sv.q_off(p.do_str, b) + h_begin * p.do_str[1] + (int64_t)lo_al * p.do_str[2];
+  const int64_t rb0 = ((int64_t)b * p.Hq + h_begin) * lrow + lo_al;
+  const float* ld_l = a.lse + rb0;
+  const float* ld_dl = a.delta + rb0;
+  const int64_t q_step = YBQ * p.q_str[2], d_step = YBQ * p.do_str[2];
+  const int64_t q_wrap = p.q_str[1] - nqb * q_step, d_wrap = p.do_str[1] - nqb * d_step;
+  const int64_t l_wrap = lrow - (int64_t)nqb * YBQ;
   auto issue = [&](int it) {
-    int hh, i0;
-    tile_rows(it, &hh, &i0);
+    const int i0 = ld_i0;
     const int rows = min(Sq - i0, YBQ);
     const int buf = it & 1;
-    const unsigned short* qs = (const unsigned short*)a.q + sv.q_off(p.q_str, b) + hh * p.q_str[1] + (int64_t)i0 * p.q_str[2];
-    const unsigned short* ds = (const unsigned short*)a.dout + sv.q_off(p.do_str, b) + hh * p.do_str[1] + (int64_t)i0 * p.do_str[2];
-    stage_rows(qs, p.q_str[2], rows, sm_base + offsetof(SmemY, q) + buf * YTS, 8 * w, 8, l);
-    stage_rows(ds, p.do_str[2], rows, sm_base + offsetof(SmemY, d) + buf * YTS, 8 * w, 8, l);
+    stage_rows(ld_q, p.q_str[2], rows, sm_base + offsetof(SmemY, q) + buf * YTS, 8 * w, 8, l);
+    stage_rows(ld_d, p.do_str[2], rows, sm_base + offsetof(SmemY, d) + buf * YTS, 8 * w, 8, l);
     if (w == 0) {
       // raw LSE and delta of the tile's rows (zeros past the end)
-      const int64_t rb = ((int64_t)b * p.Hq + hh) * lrow + i0;
-      const __amdgpu_buffer_rsrc_t rl = buf_rsrc(a.lse + rb, rows * 4), rd = buf_rsrc(a.delta + rb, rows * 4);
+      const __amdgpu_buffer_rsrc_t rl = buf_rsrc(ld_l, rows * 4), rd = buf_rsrc(ld_dl, rows * 4);
       // (lanes past the tile's rows read past the resource: zeros)
       lds_dma4(rl, __builtin_amdgcn_readfirstlane(sm_base + offsetof(SmemY, lse) + buf * 256), 4 * l);
       lds_dma4(rd, __builtin_amdgcn_readfirstlane(sm_base + offsetof(SmemY, dl) + buf * 256), 4 * l);
     }
+    ld_i0 += YBQ;
+    ld_q += q_step;
+    ld_d += d_step;
+    ld_l += YBQ;
+    ld_dl += YBQ;
+    if (ld_i0 >= i_end) {
+      ld_i0 = lo_al;
+      ld_q += q_wrap;
+      ld_d += d_wrap;
+      ld_l += l_wrap;
+      ld_dl += l_wrap;
+    }
   };
-  f32x4 acc[XNC];
+  // dKV^T of columns 128 w + 16 c + 4 g + r for keys k0 + 16 kb + lane % 16:
+  // acc[4 c + kb]
+  constexpr int NCW = XNC / 4;   // 16-column blocks per wave
+  f32x4 acc[4 * NCW];
 #pragma unroll
-  for (int n = 0; n < XNC; ++n) acc[n] = zero4();
+  for (int n = 0; n < 4 * NCW; ++n) acc[n] = zero4();
+  // A operands of the products (dO^T, Q^T of this wave's column blocks over
+  // a tile's 32 rows, slot order): read during the step of their tile, used
+  // in the next one; block c is refilled right after its last use
+  bf16x8 ad[NCW], aq[NCW];
+  const unsigned int px_base = sm_base + offsetof(SmemY, px);
   if (n_it > 0) {
     issue(0);
     wait_vm(0);
-    for (int t = 0; t < n_it; ++t) {
-      __syncthreads();   // tile t complete; tile t - 1's buffer free
-      if (t + 1 < n_it) issue(t + 1);
-      const int buf = t & 1;
-      int hh, i0;
-      tile_rows(t, &hh, &i0);
-      TileAddr tq, td;
-      tq.set(sm_base + offsetof(SmemY, q) + buf * YTS, a_lane, t_lane);
-      td.set(sm_base + offsetof(SmemY, d) + buf * YTS, a_lane, t_lane);
-      // rows 16 h + 4 g + r of the tile: raw LSE and delta
-      const f32x4 L0 = *(const f32x4*)&sm.lse[buf][4 * g], L1 = *(const f32x4*)&sm.lse[buf][16 + 4 * g];
-      const f32x4 D0 = *(const f32x4*)&sm.dl[buf][4 * g], D1 = *(const f32x4*)&sm.dl[buf][16 + 4 * g];
-      // S = Q KV^T and dP = dO KV^T: four chains, operands two steps ahead;
-      // the products' first operands are read during the last steps
-      constexpr int AH = 3, AHB = 2 * AH;
-      f32x4 sacc[2] = {zero4(), zero4()}, pacc[2] = {zero4(), zero4()};
-      bf16x8 xq0[XNS], xq1[XNS], xd0[XNS], xd1[XNS], bd[XNC], bq[XNC];
+    // One step u: S = Q KV^T and dP = dO KV^T of tile u (when HC) among the
+    // dKV^T products of tile u - 1 (when HP), which take the four waves' P
+    // and dS from LDS; then P and dS of tile u, published for the next step.
+    auto step = [&](int u, auto hc_, auto hp_) {
+      constexpr bool HC = decltype(hc_)::value, HP = decltype(hp_)::value;
+      constexpr int AH = 2, D1 = 2;
+      __syncthreads();   // tile u complete; P / dS of tile u - 1 published; tile u - 1's buffer free
+      if (HC && u + 1 < n_it) issue(u + 1);
+      const int buf = u & 1;
+      const int i0 = cur_i0;
+      if (HC) {
+        cur_i0 += YBQ;
+        if (cur_i0 >= i_end) cur_i0 = lo_al;
+      }
+      // row reads of the chains; transposing reads of this wave's column
+      // blocks (base offset to block NCW w)
+      TileAddr tq, td, tqw, tdw;
+      if (HC) {
+        tq.set(sm_base + offsetof(SmemY, q) + buf * YTS, a_lane, t_lane);
+        td.set(sm_base + offsetof(SmemY, d) + buf * YTS, a_lane, t_lane);
+        tqw.set(sm_base + offsetof(SmemY, q) + buf * YTS, a_lane, t_lane + 32 * NCW * w);
+        tdw.set(sm_base + offsetof(SmemY, d) + buf * YTS, a_lane, t_lane + 32 * NCW * w);
+      }
+      bf16x8 pb[4], sb[4];
+      if (HP) {
+        const unsigned int pxp = px_base + (buf ^ 1) * (2 * 4 * 64 * 16) + 16 * l;
 #pragma unroll
-      for (int i = 0; i < AH; ++i) {
-        xq0[i] = tq.row(0, i); xd0[i] = td.row(0, i); xq1[i] = tq.row(1, i); xd1[i] = td.row(1, i);
+        for (int kb = 0; kb < 4; ++kb) {
+          pb[kb] = lds_b128_at(pxp + kb * 64 * 16);
+          sb[kb] = lds_b128_at(pxp + 4 * 64 * 16 + kb * 64 * 16);
+        }
+      }
+      f32x4 sacc[2] = {zero4(), zero4()}, pacc[2] = {zero4(), zero4()};
+      bf16x8 xq0[XNS], xq1[XNS], xd0[XNS], xd1[XNS];
+      if (HC) {
+#pragma unroll
+        for (int i = 0; i < AH; ++i) {
+          xq0[i] = tq.row(0, i); xd0[i] = td.row(0, i); xq1[i] = tq.row(1, i); xd1[i] = td.row(1, i);
+        }
       }
       __builtin_amdgcn_sched_barrier(0);
+      // product n of tile u - 1: column block c = n / 8; n % 8 < 4: dO^T P
+      // into key block n % 4, else Q^T dS; after the last product of block c
+      // its operands are refilled from tile u
+      auto product = [&](int n) {
+        const int c = n >> 3, kb = n & 3;
+        if ((n & 4) == 0) acc[4 * c + kb] = mfma16(ad[c], pb[kb], acc[4 * c + kb]);
+        else acc[4 * c + kb] = mfma16(aq[c], sb[kb], acc[4 * c + kb]);
+        if (HC && (n & 7) == 7) { ad[c] = tdw.tr(c); aq[c] = tqw.tr(c); }
+      };
+      constexpr int NP = 4 * NCW * 2;   // 64 products
+      // region 1: the four chains, products 0 .. 2 (XNS - D1) - 1
 #pragma unroll
       for (int s = 0; s < XNS; ++s) {
-        sacc[0] = mfma16(xq0[s], kB[s], sacc[0]);
-        pacc[0] = mfma16(xd0[s], kB[s], pacc[0]);
-        sacc[1] = mfma16(xq1[s], kB[s], sacc[1]);
-        pacc[1] = mfma16(xd1[s], kB[s], pacc[1]);
-        if (s + AH < XNS) {
+        if (HC) {
+          sacc[0] = mfma16(xq0[s], kB[s], sacc[0]);
+          pacc[0] = mfma16(xd0[s], kB[s], pacc[0]);
+        }
+        if (HP && s >= D1) product(2 * (s - D1));
+        if (HC) {
+          sacc[1] = mfma16(xq1[s], kB[s], sacc[1]);
+          pacc[1] = mfma16(xd1[s], kB[s], pacc[1]);
+        }
+        if (HP && s >= D1) product(2 * (s - D1) + 1);
+        if (HC && s + AH < XNS) {
           xq0[s + AH] = tq.row(0, s + AH); xd0[s + AH] = td.row(0, s + AH);
           xq1[s + AH] = tq.row(1, s + AH); xd1[s + AH] = td.row(1, s + AH);
-        } else {
-          const int n = s + AH - XNS;   // 0 .. AH - 1
-          bd[n] = td.tr(n); bq[n] = tq.tr(n);
-          if (AHB > AH) { bd[n + AH] = td.tr(n + AH); bq[n + AH] = tq.tr(n + AH); }
         }
         __builtin_amdgcn_sched_barrier(0);
       }
-      // P = exp2(S scale log2 e - LSE log2 e) (LSE -inf: a row without keys,
-      // P = 0); dS = P (dP - delta) scale
+      if (!HP && HC) {   // first step: nothing to refill behind, read every block now
+#pragma unroll
+        for (int c = 0; c < NCW; ++c) { ad[c] = tdw.tr(c); aq[c] = tqw.tr(c); }
+      }
+      // region 2: the remaining products among P = exp2(S scale log2 e -
+      // LSE log2 e) (LSE -inf: a row without keys, P = 0) and
+      // dS = P (dP - delta) scale of tile u
       float pv[8], dsv[8];
-#pragma unroll
-      for (int e = 0; e < 8; ++e) {
-        const float lv = e < 4 ? L0[e & 3] : L1[e & 3];
-        const float l2 = lv == -INFINITY ? INFINITY : lv * kLog2e;
-        pv[e] = __builtin_amdgcn_exp2f(fmaf(sacc[e >> 2][e & 3], scale_log2, -l2));
+      f32x4 L0, L1, D0, D1v;
+      if (HC) {
+        L0 = *(const f32x4*)&sm.lse[buf][4 * g];
+        L1 = *(const f32x4*)&sm.lse[buf][16 + 4 * g];
+        D0 = *(const f32x4*)&sm.dl[buf][4 * g];
+        D1v = *(const f32x4*)&sm.dl[buf][16 + 4 * g];
       }
-      if (!(i0 >= full_a && i0 + YBQ - 1 <= full_c)) {
-        const int tb = tb0 - i0;
+      constexpr int R2 = NP - 2 * (XNS - D1);   // products left for region 2
 #pragma unroll
-        for (int e = 0; e < 8; ++e) {
-          const unsigned int tt = (unsigned int)(tb - (16 * (e >> 2) + (e & 3)));
-          pv[e] = (key_ok & (tt <= (unsigned int)span)) ? pv[e] : 0.f;
+      for (int i = 0; i < R2; ++i) {
+        if (HP) product(2 * (XNS - D1) + i);
+        if (HC && i >= 2 && i < 10) {
+          const int e = i - 2;
+          const float lv = e < 4 ? L0[e & 3] : L1[e & 3];
+          const float l2 = lv == -INFINITY ? INFINITY : lv * kLog2e;
+          pv[e] = __builtin_amdgcn_exp2f(fmaf(sacc[e >> 2][e & 3], scale_log2, -l2));
         }
-      }
-#pragma unroll
-      for (int e = 0; e < 8; ++e) {
-        const float dv = e < 4 ? D0[e & 3] : D1[e & 3];
-        dsv[e] = pv[e] * (pacc[e >> 2][e & 3] - dv) * scale;
-      }
-      const bf16x8 Pb = pack_halves(pv), Sb = pack_halves(dsv);
-      __builtin_amdgcn_sched_barrier(0);
-      // dKV^T += dO^T P + Q^T (scale dS), operands four steps ahead
-#pragma unroll
-      for (int n = 0; n < XNC; ++n) {
-        acc[n] = mfma16(bd[n], Pb, acc[n]);
-        acc[n] = mfma16(bq[n], Sb, acc[n]);
-        if (n + AHB < XNC) { bd[n + AHB] = td.tr(n + AHB); bq[n + AHB] = tq.tr(n + AHB); }
+        if (HC && i >= 10 && i < 18) {
+          const int e = i - 10;
+          const float dv = e < 4 ? D0[e & 3] : D1v[e & 3];
+          dsv[e] = pv[e] * (pacc[e >> 2][e & 3] - dv) * scale;
+        }
         __builtin_amdgcn_sched_barrier(0);
       }
-      if (t + 1 < n_it) wait_vm(0);
-    }
+      if (HC) {
+        if (!(i0 >= full_a && i0 + YBQ - 1 <= full_c)) {   // (the branch touches P and dS only)
+          const int tb = tb0 - i0;
+#pragma unroll
+          for (int e = 0; e < 8; ++e) {
+            const unsigned int tt = (unsigned int)(tb - (16 * (e >> 2) + (e & 3)));
+            const bool ok = key_ok & (tt <= (unsigned int)span);
+            pv[e] = ok ? pv[e] : 0.f;
+            dsv[e] = ok ? dsv[e] : 0.f;
+          }
+        }
+        // publish P and dS of tile u (read by every wave in the next step)
+        const unsigned int pxw = px_base + buf * (2 * 4 * 64 * 16) + w * 64 * 16 + 16 * l;
+        *(lds_u16x8*)(size_t)pxw = __builtin_bit_cast(u16x8, pack_halves(pv));
+        *(lds_u16x8*)(size_t)(pxw + 4 * 64 * 16) = __builtin_bit_cast(u16x8, pack_halves(dsv));
+      }
+      if (HC && u + 1 < n_it) wait_vm(0);   // tile u + 1 complete before the next barrier
+    };
+    step(0, std::true_type{}, std::false_type{});
+    for (int u = 1; u < n_it; ++u) step(u, std::true_type{}, std::true_type{});
+    step(n_it, std::false_type{}, std::true_type{});
   }
-  if (key < Sk) {
-    float* dst = a.dk + sv.k_off(p.dk_str, b) + hk * p.dk_str[1] + (int64_t)key * p.dk_str[2];
+  // dKV rows k0 + 16 kb + lane % 16, columns 128 w + 16 c + 4 g .. + 3
+  // (a part without tiles has nothing to add to the zeroed output)
+  if (n_it == 0 && out_mode == kAtomicAddX) return;
+  float* dkp = a.dk + sv.k_off(p.dk_str, b) + hk * p.dk_str[1];
 #pragma unroll
-    for (int n = 0; n < XNC; ++n) {
-      float* d = dst + 16 * n + 4 * g;
-      if (out_mode == kAtomicAddX) {
+  for (int kb2 = 0; kb2 < 4; ++kb2) {
+    const int kk = k0 + 16 * kb2 + lr;
+    if (kk < Sk) {
 #pragma unroll
-        for (int r = 0; r < 4; ++r) atomic_add_f32(d + r, acc[n][r]);
-      } else if (out_mode == kAddIntoX) {
-        *(f32x4*)d = *(const f32x4*)d + acc[n];
-      } else {
-        *(f32x4*)d = acc[n];
+      for (int c = 0; c < NCW; ++c) {
+        float* d = dkp + (int64_t)kk * p.dk_str[2] + 128 * w + 16 * c + 4 * g;
+        const f32x4 v = acc[4 * c + kb2];
+        if (out_mode == kAtomicAddX) {
+#pragma unroll
+          for (int r = 0; r < 4; ++r) atomic_add_f32(d + r, v[r]);
+        } else if (out_mode == kAddIntoX) {
+          *(f32x4*)d = *(const f32x4*)d + v;
+        } else {
+          *(f32x4*)d = v;
+        }
       }
     }
   }
