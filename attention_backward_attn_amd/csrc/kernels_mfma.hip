@@ -440,7 +440,6 @@ struct StageDma {
   unsigned int dst0[NI];   // LDS byte offset of each load in buffer 0
   bool is_d;               // this wave loads dO (else Q)
   bool rows_too;           // wave 0: also the LSE / delta rows
-  int n_loads;             // loads per tile of this wave
 
   __device__ inline void init(int w, int l, int q_rb, int d_rb) {
 #pragma unroll
@@ -453,22 +452,23 @@ struct StageDma {
       dst0[k] = (is_d ? offsetof(SmemDKDV2<D>, d) : offsetof(SmemDKDV2<D>, q)) + 1024 * slot;
     }
     rows_too = w == 0;
-    n_loads = NI + (rows_too ? 2 : 0);
   }
 
   // q_t / d_t / l_t / dl_t: the tile's first row; rows: rows inside the problem
+  // Wave 0 issues the two small row loads first, so that every wave can
+  // wait for "at most NI loads in flight" to see a whole tile complete.
   __device__ inline void issue(unsigned int sm_base, int buf, const unsigned short* q_t, const unsigned short* d_t,
                                int q_rb, int d_rb, const float* l_t, const float* dl_t, int rows, int l) {
-    const __amdgpu_buffer_rsrc_t rs = is_d ? buf_rsrc(d_t, rows * d_rb) : buf_rsrc(q_t, rows * q_rb);
-#pragma unroll
-    for (int k = 0; k < NI; ++k)
-      lds_dma16(rs, __builtin_amdgcn_readfirstlane(sm_base + dst0[k] + buf * (BQ * 2 * D)), voff[k]);
     if (rows_too) {
       lds_dma4(buf_rsrc(l_t, rows * 4),
                __builtin_amdgcn_readfirstlane(sm_base + offsetof(SmemDKDV2<D>, lse) + buf * (8 * BQ)), 4 * l);
       lds_dma4(buf_rsrc(dl_t, rows * 4),
                __builtin_amdgcn_readfirstlane(sm_base + offsetof(SmemDKDV2<D>, dl) + buf * (8 * BQ)), 4 * l);
     }
+    const __amdgpu_buffer_rsrc_t rs = is_d ? buf_rsrc(d_t, rows * d_rb) : buf_rsrc(q_t, rows * q_rb);
+#pragma unroll
+    for (int k = 0; k < NI; ++k)
+      lds_dma16(rs, __builtin_amdgcn_readfirstlane(sm_base + dst0[k] + buf * (BQ * 2 * D)), voff[k]);
   }
 };
 
@@ -622,9 +622,9 @@ __global__ __launch_bounds__(NT2) void k_dkdv2(Params p, BwdArgs a, DkdvGrid gd)
       if (n_it > j) issue(j);
     if (n_it > NB2 - 2) {
       issue(NB2 - 2);
-      wait_vm(stg.n_loads);
+      wait_vm_c<StageDma<D>::NI>();
     } else {
-      wait_vm(0);
+      wait_vm_c<0>();
     }
     __syncthreads();
     // Wave 0 turns the raw LSE / delta rows of a complete tile into
@@ -805,7 +805,7 @@ __global__ __launch_bounds__(NT2) void k_dkdv2(Params p, BwdArgs a, DkdvGrid gd)
         acc = accn;
         prefetch(std::integral_constant<int, j1>{});   // (past the last tile: stale, unused)
         // tile t + 3 complete before the next barrier (tile t + 4 may stay in flight)
-        wait_vm(more ? stg.n_loads : 0);
+        wait_vm_keep<StageDma<D>::NI>(more);
       };
       static_assert(NB2 == 5, "tile loop unrolled over five buffers");
       for (int t0 = 0; t0 < n_it; t0 += NB2) {
@@ -1351,7 +1351,7 @@ __global__ __launch_bounds__(NT, 2) void k_dq2(Params p, BwdArgs a) {
       if (more) issue(t + 2, (j + 2) % NBQ);
       tile(t, j, tile_full(tile_of(t)));
       // tile t + 1 complete before the next barrier (tile t + 2 may stay in flight)
-      wait_vm(more ? NI : 0);
+      wait_vm_keep<NI>(more);
     };
     auto tilec = [&](int t, auto jc, bool full) {
       constexpr int j = decltype(jc)::value, jp = (j + NBQ - 1) % NBQ;
@@ -1413,7 +1413,7 @@ __global__ __launch_bounds__(NT, 2) void k_dq2(Params p, BwdArgs a) {
       if (more) issue(t + 2, (j + 2) % NBQ);
       tilec(t, jc, tile_full(tile_of(t)));
       // tile t + 1 complete before the next barrier (tile t + 2 may stay in flight)
-      wait_vm(more ? NI : 0);
+      wait_vm_keep<NI>(more);
     };
     // main loop unrolled over the four buffers (constant read offsets), then
     // the remaining tiles

@@ -277,7 +277,7 @@ __global__ __launch_bounds__(XNT, 1) void k_fwd512(Params p, FwdArgs a) {
         }
         Pb = pack_halves(pv);
       }
-      if (t + 1 < n_it) wait_vm(t + 2 < n_it ? 8 : 0);   // tile t + 1 complete before the next barrier
+      if (t + 1 < n_it) wait_vm_keep<8>(t + 2 < n_it);   // tile t + 1 complete before the next barrier
     };
     step(0, std::true_type{}, std::false_type{});
     for (int t = 1; t < n_it; ++t) step(t, std::true_type{}, std::true_type{});
@@ -452,7 +452,7 @@ __global__ __launch_bounds__(XNT, 1) void k_dq512(Params p, BwdArgs a) {
         *(lds_u16x8*)(size_t)(ds_base + (t & 1) * (4 * 64 * 16) + w * 64 * 16 + 16 * l) =
             __builtin_bit_cast(u16x8, pack_halves(dsv));
       }
-      if (t + 1 < n_it) wait_vm(t + 2 < n_it ? 8 : 0);   // tile t + 1 complete before the next barrier
+      if (t + 1 < n_it) wait_vm_keep<8>(t + 2 < n_it);   // tile t + 1 complete before the next barrier
     };
     step(0, std::true_type{}, std::false_type{});
     for (int t = 1; t < n_it; ++t) step(t, std::true_type{}, std::true_type{});

@@ -186,6 +186,19 @@ __device__ inline void wait_vm(int n) {
   }
 }
 
+// wait_vm with a compile-time count: one instruction, no branch.
+template <int N>
+__device__ inline void wait_vm_c() {
+  static_assert(N >= 0 && N < 16, "vmcnt field");
+  __builtin_amdgcn_s_waitcnt(0x0F70 | N);
+}
+// Either N or 0 in flight, chosen at run time by `keep` (two fixed waits).
+template <int N>
+__device__ inline void wait_vm_keep(bool keep) {
+  if (keep) wait_vm_c<N>();
+  else wait_vm_c<0>();
+}
+
 // The hardware deals a launch's workgroups to the eight XCDs round-robin by
 // linear workgroup id.  Renumbering them so that each XCD receives one
 // contiguous range of logical ids (x fastest, then z, then y) keeps the
