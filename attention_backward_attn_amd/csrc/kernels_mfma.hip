@@ -1252,13 +1252,31 @@ __global__ __launch_bounds__(NT, 2) void k_dq2(Params p, BwdArgs a) {
     voff[k] = row * (ld_v ? v_rb : k_rb) + 16 * ((l % CR) ^ Swz<D>::f(row));
     dst0[k] = sm_base + (ld_v ? offsetof(SmemDQ2<D>, v) : offsetof(SmemDQ2<D>, k)) + 1024 * slot;
   }
-  auto issue = [&](int it, int buf) {
-    const int j0 = tile_of(it);
-    const int keys = min(Sk - j0, BK3);
-    const __amdgpu_buffer_rsrc_t rs = ld_v ? buf_rsrc(vp + (int64_t)j0 * p.v_str[2], keys * v_rb)
-                                           : buf_rsrc(kp + (int64_t)j0 * p.k_str[2], keys * k_rb);
+  // tile walk: the next tile to load (its first key and this wave's K or V
+  // pointer) and the tile being formed, advanced one tile at a time (the
+  // step from the last sink tile to the first band tile jumps)
+  const unsigned short* const src0 = ld_v ? vp : kp;
+  const int64_t src_str = ld_v ? p.v_str[2] : p.k_str[2];
+  const int src_rb = ld_v ? v_rb : k_rb;
+  int ld_it = 0, ld_j0 = tile_of(0);
+  const unsigned short* ld_src = src0 + (int64_t)ld_j0 * src_str;
+  auto issue = [&](int buf) {
+    const int keys = min(Sk - ld_j0, BK3);
+    const __amdgpu_buffer_rsrc_t rs = buf_rsrc(ld_src, keys * src_rb);
 #pragma unroll
     for (int k = 0; k < NI; ++k) lds_dma16(rs, __builtin_amdgcn_readfirstlane(dst0[k] + buf * TS), voff[k]);
+    if (++ld_it == n1) {
+      ld_j0 = BK3 * a2;
+      ld_src = src0 + (int64_t)ld_j0 * src_str;
+    } else {
+      ld_j0 += BK3;
+      ld_src += BK3 * src_str;
+    }
+  };
+  int cur_it = 0, cur_j0 = tile_of(0);
+  auto advance_cur = [&]() {
+    if (++cur_it == n1) cur_j0 = BK3 * a2;
+    else cur_j0 += BK3;
   };
 
   f32x16 dq[NC];
@@ -1270,9 +1288,9 @@ __global__ __launch_bounds__(NT, 2) void k_dq2(Params p, BwdArgs a) {
 #pragma unroll
     for (int k = 0; k < TS / (16 * NT); ++k) *(u16x8*)&sm.k[NBQ - 1][16 * (tid + NT * k)] = u16x8{0, 0, 0, 0, 0, 0, 0, 0};
     // tiles 0 and 1 in flight; 0 complete before the first barrier
-    issue(0, 0);
+    issue(0);
     if (n_it > 1) {
-      issue(1, 1);
+      issue(1);
       wait_vm(NI);
     } else {
       wait_vm(0);
@@ -1301,7 +1319,7 @@ __global__ __launch_bounds__(NT, 2) void k_dq2(Params p, BwdArgs a) {
     // tile t in buffer j: the S^T / dP^T chains of tile t among the dQ
     // products of tile t - 1 (when DQ), then the exponentials and dS
     // arithmetic of tile t
-    auto tile = [&](int t, int j, bool full) {
+    auto tile = [&](int t, int j, bool full, int j0) {
       const int jp = (j + NBQ - 1) % NBQ;
       constexpr bool DQ = true;
       bf16x8 xk[NS], xv[NS], bq[NS];
@@ -1325,7 +1343,6 @@ __global__ __launch_bounds__(NT, 2) void k_dq2(Params p, BwdArgs a) {
         }
         __builtin_amdgcn_sched_barrier(0);
       }
-      const int j0 = tile_of(t);
       const int tb = tq + j0;   // window offset of key j0 + 4 lg for this lane's row
       float pp[16], dsv[16];
 #pragma unroll
@@ -1348,12 +1365,13 @@ __global__ __launch_bounds__(NT, 2) void k_dq2(Params p, BwdArgs a) {
       const int j = t % NBQ;
       __syncthreads();  // tile t complete; tile t - 2's buffer free
       const bool more = t + 2 < n_it;
-      if (more) issue(t + 2, (j + 2) % NBQ);
-      tile(t, j, tile_full(tile_of(t)));
+      if (more) issue((j + 2) % NBQ);
+      tile(t, j, tile_full(cur_j0), cur_j0);
+      advance_cur();
       // tile t + 1 complete before the next barrier (tile t + 2 may stay in flight)
       wait_vm_keep<NI>(more);
     };
-    auto tilec = [&](int t, auto jc, bool full) {
+    auto tilec = [&](int t, auto jc, bool full, int j0) {
       constexpr int j = decltype(jc)::value, jp = (j + NBQ - 1) % NBQ;
       // region 1: the S^T / dP^T chains of tile t (two independent chains)
       f32x16 sacc = zero16(), pacc = zero16();
@@ -1391,7 +1409,6 @@ __global__ __launch_bounds__(NT, 2) void k_dq2(Params p, BwdArgs a) {
         }
       }
       if (!full) {   // (the branch touches P only)
-        const int j0 = tile_of(t);
         const int tb = tq + j0;   // window offset of key j0 + 4 lg for this lane's row
 #pragma unroll
         for (int r = 0; r < 16; ++r) {
@@ -1410,8 +1427,9 @@ __global__ __launch_bounds__(NT, 2) void k_dq2(Params p, BwdArgs a) {
       constexpr int j = decltype(jc)::value;
       __syncthreads();  // tile t complete; tile t - 2's buffer free
       const bool more = t + 2 < n_it;
-      if (more) issue(t + 2, (j + 2) % NBQ);
-      tilec(t, jc, tile_full(tile_of(t)));
+      if (more) issue((j + 2) % NBQ);
+      tilec(t, jc, tile_full(cur_j0), cur_j0);
+      advance_cur();
       // tile t + 1 complete before the next barrier (tile t + 2 may stay in flight)
       wait_vm_keep<NI>(more);
     };
