@@ -31,12 +31,17 @@ __global__ __launch_bounds__(256) void k_delta_vec(const OT* __restrict__ o,
                                                    int64_t qh, int64_t qs, Packed pk) {
   const int64_t rows = (int64_t)B * H * Sq;
   const int lane_in_row = threadIdx.x % TPR;
-  const int64_t row = ((int64_t)blockIdx.x * 256 + threadIdx.x) / TPR;
+  const int64_t idx = ((int64_t)blockIdx.x * 256 + threadIdx.x) / TPR;
   float acc = 0.f;
-  bool live = row < rows;
-  const int i = live ? (int)(row % Sq) : 0;
-  const int h = live ? (int)((row / Sq) % H) : 0;
-  const int b = live ? (int)(row / ((int64_t)Sq * H)) : 0;
+  bool live = idx < rows;
+  // Walk the rows in memory order: positions fastest when a head's rows are
+  // contiguous ([B, H, S, D]), heads fastest when the heads of a position are
+  // ([T, H, D] packed).
+  const bool h_fast = oh < os;
+  const int i = !live ? 0 : (h_fast ? (int)((idx / H) % Sq) : (int)(idx % Sq));
+  const int h = !live ? 0 : (h_fast ? (int)(idx % H) : (int)((idx / Sq) % H));
+  const int b = live ? (int)(idx / ((int64_t)Sq * H)) : 0;
+  const int64_t row = ((int64_t)b * H + h) * Sq + i;   // delta index
   // dense: (b, i) through the b stride; packed: packed row r0 + i of sequence b
   int64_t ro = 0, rd = 0, rq = 0;
   if (live) {
@@ -62,7 +67,7 @@ __global__ __launch_bounds__(256) void k_delta_vec(const OT* __restrict__ o,
   }
 #pragma unroll
   for (int off = TPR / 2; off > 0; off >>= 1) acc += __shfl_xor(acc, off, TPR);
-  if (row < rows && lane_in_row == 0) delta[row] = acc;   // 0 past a packed sequence's length
+  if (idx < rows && lane_in_row == 0) delta[row] = acc;   // 0 past a packed sequence's length
 }
 
 // Scalar fallback for Dv not a multiple of 8: one thread per row.
@@ -248,13 +253,17 @@ static hipError_t launch_delta_t(const void* o, const void* dout, float* delta, 
                                  const int64_t* qs, Packed pk, hipStream_t st) {
   const int64_t rows = (int64_t)B * H * Sq;
   if (Dv % 8 == 0) {
-    const int tpr = Dv >= 128 ? 16 : (Dv >= 64 ? 8 : (Dv >= 32 ? 4 : (Dv >= 16 ? 2 : 1)));
+    // lanes per row: 8 elements each (one 16-byte load per tensor for head
+    // dims up to 512, so a row's loads are all in flight at once)
+    const int tpr = Dv >= 512 ? 64 : (Dv >= 256 ? 32 : (Dv >= 128 ? 16 : (Dv >= 64 ? 8 : (Dv >= 32 ? 4 : (Dv >= 16 ? 2 : 1)))));
     const int64_t blocks = (rows * tpr + 255) / 256;
 #define ATTN_DELTA_LAUNCH(T)                                                                     \
   hipLaunchKernelGGL((k_delta_vec<OT, DT, T>), dim3((unsigned)blocks), dim3(256), 0, st,           \
                      (const OT*)o, (const DT*)dout, delta, B, H, Sq, Dv, os[0], os[1], os[2],      \
                      ds[0], ds[1], ds[2], dq, Dqk, qs[0], qs[1], qs[2], pk)
     switch (tpr) {
+      case 64: ATTN_DELTA_LAUNCH(64); break;
+      case 32: ATTN_DELTA_LAUNCH(32); break;
       case 16: ATTN_DELTA_LAUNCH(16); break;
       case 8: ATTN_DELTA_LAUNCH(8); break;
       case 4: ATTN_DELTA_LAUNCH(4); break;
