@@ -257,9 +257,6 @@ attn_status_t attn_bwd(const attn_problem_t* p, const void* q, const void* k, co
                     !aligned16(k) || !aligned16(v) || !aligned16(dout)))
     return ATTN_EUNSUPPORTED;
   if (no_rows && no_keys) return ATTN_OK;
-  if (dbias && !no_rows && p->Sk > 0) {
-    if (attn::launch_zero_bias(dbias, p->Hq, p->Sq, p->Sk, p->bias_str, s) != hipSuccess) return ATTN_EHIP;
-  }
   if (p->in_dtype == ATTN_BF16 && attn::mfma_bwd_supported(kp))
     return hip_status(attn::launch_bwd_mfma(kp, a, s));
   // fp32 inputs (and bf16 shapes the matrix-core kernels do not cover)

@@ -1521,6 +1521,13 @@ hipError_t launch_bwd_mfma(const Params& p, const BwdArgs& a, hipStream_t st) {
   if (a.bias && (!aligned16(a.bias) || p.Sk % 4 != 0 || p.bias_str[0] % 4 != 0 || p.bias_str[1] % 4 != 0))
     return launch_bwd_simt(p, a, 1, st);
   const bool bias = a.bias != nullptr;
+  // dbias: the first batch entry stores the dS of every tile it visits;
+  // without a mask every tile is visited, so only masked problems need the
+  // tiles that no key block reaches zeroed first
+  if (a.dbias && p.mask.kind != kMaskNone && p.Sq > 0 && p.Sk > 0 && p.B > 0) {
+    hipError_t e = launch_zero_bias(a.dbias, p.Hq, p.Sq, p.Sk, p.bias_str, st);
+    if (e != hipSuccess) return e;
+  }
   // dK / dV by key blocks (k_dkdv2; k_dkdv with a bias, where dbias is
   // summed over the batch in a fixed order by one workgroup per key block
   // walking the batch), then dQ by query blocks (k_dq): no dQ atomics.

@@ -326,6 +326,11 @@ hipError_t launch_fwd_simt(const Params& p, const FwdArgs& a, int in_bf16, int o
 }
 
 hipError_t launch_bwd_simt(const Params& p, const BwdArgs& a, int in_bf16, hipStream_t st) {
+  // dbias is summed into (every batch entry adds its dS)
+  if (a.dbias && p.Sq > 0 && p.Sk > 0 && p.B > 0) {
+    hipError_t e = launch_zero_bias(a.dbias, p.Hq, p.Sq, p.Sk, p.bias_str, st);
+    if (e != hipSuccess) return e;
+  }
   if (p.Sk > 0 && p.B > 0) {
     const int b_loop = a.dbias != nullptr;
     const dim3 grid((p.Sk + kT - 1) / kT, p.Hk, b_loop ? 1 : p.B);

@@ -317,7 +317,8 @@ def main():
     achieved = flops / (main_ms * 1e-3) / 1e12
     kernel_key = f"bwd_main:{w.name}"
     out = {
-        "metric": "attention-backward TFLOP/s + % bf16 MFMA peak (GQA 32:8, S=4096, D=128, causal)",
+        "metric": ("attention-backward TFLOP/s + % bf16 MFMA peak (GQA 32:8, S=4096, D=128, causal)"
+                   if w.name == HEADLINE else f"attention-backward TFLOP/s + % bf16 MFMA peak ({w.name})"),
         "value": round(value, 2),
         "unit": "TFLOP/s",
         "n_gpus": 1,
