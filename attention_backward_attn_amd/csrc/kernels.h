@@ -63,6 +63,17 @@ hipError_t launch_delta(const void* o, int o_bf16, const void* dout, int do_bf16
 hipError_t launch_dsinks(const float* lse, const float* delta, const float* sinks, float* dsinks,
                          int B, int H, int Sq, Packed pk, hipStream_t st);
 hipError_t launch_zero_rows(float* x, int B, int H, int S, int D, const int64_t* str, hipStream_t st);
+// Up to three strided row tensors zeroed as one flat range: tensor k covers
+// the elements [off[k], off[k + 1]), counted in 4-float groups where vec[k].
+struct ZeroMulti {
+  ZeroRows z[3];
+  int64_t off[4];
+  int vec[3];
+  int dense[3];   // the tensor is one gap-free block from z.p (zeroed flat)
+  int n;          // tensors (0: nothing to zero)
+};
+// The tensors z[0 .. n) with the empty ones dropped.
+ZeroMulti make_zero_multi(const ZeroRows* z, int n);
 // Zero up to three tensors in one launch (n == 0: nothing is launched).
 hipError_t launch_zero_multi(const ZeroRows* z, int n, hipStream_t st);
 hipError_t launch_zero_bias(float* x, int H, int Sq, int Sk, const int64_t* str, hipStream_t st);

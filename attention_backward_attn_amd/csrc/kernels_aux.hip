@@ -1,6 +1,7 @@
 // Memory-bound helper kernels: the backward preprocess (delta = rowsum(dO*O)
 // and the sink-logit gradient), zero fills, and the log-sum-exp merge.
 #include "kernels.h"
+#include "mfma_util.h"
 
 namespace attn {
 
@@ -151,37 +152,11 @@ __global__ __launch_bounds__(256) void k_zero_rows(float* __restrict__ x, int B,
   }
 }
 
-// Zero up to three strided row tensors: the flat element range of tensor k
-// starts at off[k]; rows of D % 4 == 0 tensors are written 4 floats at a time.
-struct ZeroMulti {
-  ZeroRows z[3];
-  int64_t off[4];  // element offsets (in units of 4-float groups where vec)
-  int vec[3];
-  int n;
-};
-
 __global__ __launch_bounds__(256) void k_zero_multi(ZeroMulti m) {
-  const int64_t total = m.off[m.n];
-  for (int64_t e = (int64_t)blockIdx.x * 256 + threadIdx.x; e < total; e += (int64_t)gridDim.x * 256) {
-    int k = 0;
-    while (k + 1 < m.n && e >= m.off[k + 1]) ++k;
-    const ZeroRows& z = m.z[k];
-    const int64_t x = e - m.off[k];
-    const int w = m.vec[k] ? z.D / 4 : z.D;
-    const int d = (int)(x % w);
-    const int64_t r = x / w;
-    const int i = (int)(r % z.S);
-    const int h = (int)((r / z.S) % z.H);
-    const int b = (int)(r / ((int64_t)z.S * z.H));
-    float* row = z.p + b * z.str[0] + h * z.str[1] + i * z.str[2];
-    if (m.vec[k])
-      *(float4*)(row + 4 * d) = make_float4(0.f, 0.f, 0.f, 0.f);
-    else
-      row[d] = 0.f;
-  }
+  zero_multi_range(m, 0, m.off[m.n], blockIdx.x * 256 + threadIdx.x, gridDim.x * 256);
 }
 
-hipError_t launch_zero_multi(const ZeroRows* z, int n, hipStream_t st) {
+ZeroMulti make_zero_multi(const ZeroRows* z, int n) {
   ZeroMulti m{};
   int k = 0;
   m.off[0] = 0;
@@ -192,12 +167,35 @@ hipError_t launch_zero_multi(const ZeroRows* z, int n, hipStream_t st) {
     const bool aligned = ((uintptr_t)z[i].p % 16 == 0) && z[i].str[0] % 4 == 0 && z[i].str[1] % 4 == 0 &&
                          z[i].str[2] % 4 == 0;
     m.vec[k] = (z[i].D % 4 == 0 && aligned) ? 1 : 0;
+    // dense: the (size, stride) pairs of the B, H, S indices (size-1 ones
+    // dropped), in increasing stride, tile the memory after the D floats of a row
+    int64_t dims[3][2] = {{z[i].B, z[i].str[0]}, {z[i].H, z[i].str[1]}, {z[i].S, z[i].str[2]}};
+    for (int a = 0; a < 3; ++a)
+      for (int b = a + 1; b < 3; ++b)
+        if (dims[b][1] < dims[a][1]) {
+          int64_t t0 = dims[a][0], t1 = dims[a][1];
+          dims[a][0] = dims[b][0]; dims[a][1] = dims[b][1];
+          dims[b][0] = t0; dims[b][1] = t1;
+        }
+    int64_t expect = z[i].D;
+    bool dense = true;
+    for (int a = 0; a < 3; ++a) {
+      if (dims[a][0] == 1) continue;
+      if (dims[a][1] != expect) dense = false;
+      expect *= dims[a][0];
+    }
+    m.dense[k] = dense ? 1 : 0;
     m.off[k + 1] = m.off[k] + rows * (m.vec[k] ? z[i].D / 4 : z[i].D);
     ++k;
   }
   m.n = k;
-  if (k == 0) return hipSuccess;
-  hipLaunchKernelGGL(k_zero_multi, dim3(fill_blocks(m.off[k])), dim3(256), 0, st, m);
+  return m;
+}
+
+hipError_t launch_zero_multi(const ZeroRows* z, int n, hipStream_t st) {
+  const ZeroMulti m = make_zero_multi(z, n);
+  if (m.n == 0) return hipSuccess;
+  hipLaunchKernelGGL(k_zero_multi, dim3(fill_blocks(m.off[m.n])), dim3(256), 0, st, m);
   return hipGetLastError();
 }
 

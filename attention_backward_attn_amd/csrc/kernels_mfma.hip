@@ -15,9 +15,10 @@
 //     32-key slice between a pair of waves on one SIMD (two waves per SIMD);
 //     k_dkdv, one wave per 32 keys, serves problems with a bias and walks the
 //     batch so that dbias is summed in a fixed order.
-//   * dQ by query blocks: k_dq, one workgroup per (128-row block, query
-//     head, batch), recomputes S and dP per key tile and keeps dQ in
-//     registers.
+//   * dQ by query blocks: k_dq2 (k_dq with a bias), one workgroup per
+//     (128-row block, query head, batch), recomputes S and dP per key tile
+//     and keeps dQ in registers.  k_dq2 may run first and also zero the
+//     dK / dV that the split key-block parts add into.
 // In every kernel S (or S^T) comes out of v_mfma_f32_32x32x16_bf16 with one
 // row or key per lane, and that accumulator layout is used directly as the
 // operand of the next product once the reduction index is permuted the same
@@ -1163,7 +1164,7 @@ struct __attribute__((aligned(1024))) SmemDQ2 {
 };
 
 template <int D>
-__global__ __launch_bounds__(NT, 2) void k_dq2(Params p, BwdArgs a) {
+__global__ __launch_bounds__(NT, 2) void k_dq2(Params p, BwdArgs a, ZeroMulti zm) {
   constexpr int NS = D / 16;   // k-steps over the head dim
   constexpr int NC = D / 32;   // 32-column blocks of dQ
   constexpr int RB = Swz<D>::RB, CR = Swz<D>::CR;
@@ -1175,6 +1176,17 @@ __global__ __launch_bounds__(NT, 2) void k_dq2(Params p, BwdArgs a) {
 
   const int tid = threadIdx.x, l = tid & 63, lr = l & 31, lg = l >> 5;
   const int w = __builtin_amdgcn_readfirstlane(tid >> 6);   // wave-uniform
+  // Tensors that the key-block pass launched after this one adds into (its
+  // split parts) are zeroed here, an even share per workgroup, once its own
+  // work is done (the stores then overlap other workgroups' products).
+  auto zero_share = [&]() {
+    if (zm.n > 0) {
+      const int64_t nwg = (int64_t)gridDim.x * gridDim.y * gridDim.z;
+      const int64_t wg = blockIdx.x + (int64_t)gridDim.x * (blockIdx.y + (int64_t)gridDim.y * blockIdx.z);
+      const int64_t total = zm.off[zm.n], per = (total + nwg - 1) / nwg;
+      zero_multi_range(zm, wg * per, min(total, (wg + 1) * per), tid, NT);
+    }
+  };
   const BlockXYZ blk = a.xmajor ? xcd_block_xmajor() : xcd_block();
   // under a causal mask later row blocks see more keys: deal them first
   const bool heavy_last = p.mask.kind != kMaskNone && p.mask.wl < 0;
@@ -1183,7 +1195,10 @@ __global__ __launch_bounds__(NT, 2) void k_dq2(Params p, BwdArgs a) {
   const SeqView sv = seq_view(p, b);   // this batch entry (or packed sequence)
   const Mask& msk = sv.mask;
   const int Sq = sv.Sq, Sk = sv.Sk;
-  if (i0 >= Sq) return;   // past this sequence's rows (uniform across the workgroup)
+  if (i0 >= Sq) {   // past this sequence's rows (uniform across the workgroup)
+    zero_share();
+    return;
+  }
   const int irow = i0 + 32 * w + lr;           // this lane's query row
   const float scale = p.scale, scale_log2 = p.scale * kLog2e;
 
@@ -1470,17 +1485,19 @@ __global__ __launch_bounds__(NT, 2) void k_dq2(Params p, BwdArgs a) {
       }
     }
   }
+  zero_share();
 }
 
+// zm: tensors to zero on the way (k_dq2 only; zm.n == 0 with a bias)
 template <int D>
-hipError_t launch_dq(const Params& p, const BwdArgs& a0, hipStream_t st) {
+hipError_t launch_dq(const Params& p, const BwdArgs& a0, const ZeroMulti& zm, hipStream_t st) {
   const dim3 grid((p.Sq + BQ3 - 1) / BQ3, p.Hq, p.B);
   BwdArgs a = a0;
   a.xmajor = xmajor_fits(p, grid.y, grid.z) ? 1 : 0;
   if (a.bias)
     hipLaunchKernelGGL((k_dq<D, true>), grid, dim3(NT), 0, st, p, a);
   else
-    hipLaunchKernelGGL((k_dq2<D>), grid, dim3(NT), 0, st, p, a);
+    hipLaunchKernelGGL((k_dq2<D>), grid, dim3(NT), 0, st, p, a, zm);
   return hipGetLastError();
 }
 
@@ -1530,17 +1547,32 @@ hipError_t launch_bwd_mfma(const Params& p, const BwdArgs& a, hipStream_t st) {
   }
   // dK / dV by key blocks (k_dkdv2; k_dkdv with a bias, where dbias is
   // summed over the batch in a fixed order by one workgroup per key block
-  // walking the batch), then dQ by query blocks (k_dq): no dQ atomics.
+  // walking the batch) and dQ by query blocks (k_dq2; k_dq with a bias): no
+  // dQ atomics.  The passes are independent.  The dK / dV that the split
+  // key-block parts add into are zeroed by the dQ pass, run first, when it is
+  // k_dq2 and reads its K / V mostly from L2 (the stores then cost it little);
+  // otherwise by a zero kernel ahead of the key-block pass.
   const bool bloop = a.dbias != nullptr;
   const DkdvPlan pl = plan_dkdv(p, bloop, a.accumulate_dkdv != 0, a.deterministic != 0);
-  // split parts add into zeroed dK / dV
+  const bool run_dq = p.Sq > 0 && p.B > 0, dq_first = run_dq && !bias && xmajor_fits(p, p.Hq, p.B);
+  auto dq = [&](const ZeroMulti& zm) {
+    return p.Dqk == 64 ? launch_dq<64>(p, a, zm, st) : launch_dq<128>(p, a, zm, st);
+  };
+  ZeroMulti zm{};
   if (pl.g.out_mode == kAtomicAdd && !a.accumulate_dkdv && p.Sk > 0) {
     // dense [B, Hk, Sk] or the packed rows of a variable-length batch
     const bool pk = p.cu_k != nullptr;
     const int zb = pk ? 1 : p.B, zs = pk ? (int)p.tot_k : p.Sk;
     ZeroRows z[2] = {ZeroRows{a.dk, zb, p.Hk, zs, p.Dqk, {pk ? 0 : p.dk_str[0], p.dk_str[1], p.dk_str[2]}},
                      ZeroRows{a.dv, zb, p.Hk, zs, p.Dv, {pk ? 0 : p.dv_str[0], p.dv_str[1], p.dv_str[2]}}};
-    hipError_t e = launch_zero_multi(z, 2, st);
+    zm = make_zero_multi(z, 2);
+    if (!dq_first && zm.n > 0) {
+      hipError_t e = launch_zero_multi(z, 2, st);
+      if (e != hipSuccess) return e;
+    }
+  }
+  if (dq_first) {
+    hipError_t e = dq(zm);
     if (e != hipSuccess) return e;
   }
   if (p.Sk > 0 && p.B > 0) {
@@ -1548,7 +1580,7 @@ hipError_t launch_bwd_mfma(const Params& p, const BwdArgs& a, hipStream_t st) {
                                : dispatch_dkdv<128>(p, a, pl, bias, bloop, st);
     if (e != hipSuccess) return e;
   }
-  if (p.Sq > 0 && p.B > 0) return p.Dqk == 64 ? launch_dq<64>(p, a, st) : launch_dq<128>(p, a, st);
+  if (run_dq && !dq_first) return dq(ZeroMulti{});
   return hipSuccess;
 }
 

@@ -8,7 +8,7 @@
 //   C[m][n]: lane holds n = l % 32, m = 8 (r / 4) + 4 (l / 32) + r % 4
 #pragma once
 
-#include "common.h"
+#include "kernels.h"
 
 namespace attn {
 namespace mfma_util {
@@ -248,4 +248,38 @@ __device__ inline float buf_load_f32(__amdgpu_buffer_rsrc_t r, int off) {
 }
 
 }  // namespace mfma_util
+// Thread t of nt zeroes the flat elements [e0, e1) of m (consecutive
+// threads on consecutive elements).
+__device__ inline void zero_multi_range(const ZeroMulti& m, int64_t e0, int64_t e1, int t, int nt) {
+#pragma unroll
+  for (int k = 0; k < 3; ++k) {
+    if (k >= m.n) break;
+    const ZeroRows& z = m.z[k];
+    const int64_t lo = e0 > m.off[k] ? e0 : m.off[k], hi = e1 < m.off[k + 1] ? e1 : m.off[k + 1];
+    const int w = m.vec[k] ? z.D / 4 : z.D;
+    if (m.dense[k]) {   // flat: no index arithmetic
+      if (m.vec[k]) {
+        float4* q = (float4*)z.p;
+        for (int64_t e = lo + t; e < hi; e += nt) q[e - m.off[k]] = make_float4(0.f, 0.f, 0.f, 0.f);
+      } else {
+        for (int64_t e = lo + t; e < hi; e += nt) z.p[e - m.off[k]] = 0.f;
+      }
+      continue;
+    }
+    for (int64_t e = lo + t; e < hi; e += nt) {
+      const int64_t x = e - m.off[k];
+      const int d = (int)(x % w);
+      const int64_t r = x / w;
+      const int i = (int)(r % z.S);
+      const int h = (int)((r / z.S) % z.H);
+      const int b = (int)(r / ((int64_t)z.S * z.H));
+      float* row = z.p + b * z.str[0] + h * z.str[1] + i * z.str[2];
+      if (m.vec[k])
+        *(float4*)(row + 4 * d) = make_float4(0.f, 0.f, 0.f, 0.f);
+      else
+        row[d] = 0.f;
+    }
+  }
+}
+
 }  // namespace attn
