@@ -1330,12 +1330,24 @@ __global__ __launch_bounds__(NT, 2) void k_dq2(Params p, BwdArgs a, ZeroMulti zm
     // dS of the previous tile (dQ operands); before the first tile zeros,
     // against the K tile buffer 3 zeroed in the prologue
     bf16x8 A0 = as_bf16x8(u16x8{0, 0, 0, 0, 0, 0, 0, 0}), A1 = A0;
+    // P (masked) and dP^T of the previous tile: its dS is formed while the
+    // next tile's chains run; zeros before the first tile (dS = 0)
+    float pp[16], pc[16];
+#pragma unroll
+    for (int r = 0; r < 16; ++r) { pp[r] = 0.f; pc[r] = 0.f; }
+    auto ds_prev = [&]() {
+      float dsv[16];
+#pragma unroll
+      for (int r = 0; r < 16; ++r) dsv[r] = pp[r] * fmaf(pc[r], scale, -dls);
+      A0 = pack8(dsv);
+      A1 = pack8(dsv + 8);
+    };
 
-    // tile t in buffer j: the S^T / dP^T chains of tile t among the dQ
-    // products of tile t - 1 (when DQ), then the exponentials and dS
-    // arithmetic of tile t
+    // tile t in buffer j: dS of tile t - 1, the S^T / dP^T chains of tile t
+    // among the dQ products of tile t - 1, then the exponentials of tile t
     auto tile = [&](int t, int j, bool full, int j0) {
       const int jp = (j + NBQ - 1) % NBQ;
+      ds_prev();
       constexpr bool DQ = true;
       bf16x8 xk[NS], xv[NS], bq[NS];
       f32x16 sacc = zero16(), pacc = zero16();
@@ -1359,7 +1371,6 @@ __global__ __launch_bounds__(NT, 2) void k_dq2(Params p, BwdArgs a, ZeroMulti zm
         __builtin_amdgcn_sched_barrier(0);
       }
       const int tb = tq + j0;   // window offset of key j0 + 4 lg for this lane's row
-      float pp[16], dsv[16];
 #pragma unroll
       for (int r = 0; r < 16; ++r) pp[r] = __builtin_amdgcn_exp2f(fmaf(sacc[r], scale_log2, -lse2));
       if (!full) {   // (the branch touches P only)
@@ -1372,9 +1383,7 @@ __global__ __launch_bounds__(NT, 2) void k_dq2(Params p, BwdArgs a, ZeroMulti zm
         }
       }
 #pragma unroll
-      for (int r = 0; r < 16; ++r) dsv[r] = pp[r] * fmaf(pacc[r], scale, -dls);
-      A0 = pack8(dsv);
-      A1 = pack8(dsv + 8);
+      for (int r = 0; r < 16; ++r) pc[r] = pacc[r];
     };
     auto step = [&](int t) {
       const int j = t % NBQ;
@@ -1388,10 +1397,13 @@ __global__ __launch_bounds__(NT, 2) void k_dq2(Params p, BwdArgs a, ZeroMulti zm
     };
     auto tilec = [&](int t, auto jc, bool full, int j0) {
       constexpr int j = decltype(jc)::value, jp = (j + NBQ - 1) % NBQ;
+      constexpr int EPS = 16 / NS;   // accumulator elements per chain step
       // region 1: the S^T / dP^T chains of tile t (two independent chains)
+      // among the dS arithmetic of tile t - 1
       f32x16 sacc = zero16(), pacc = zero16();
       {
         bf16x8 xk[NS], xv[NS];
+        float dsv[16];
 #pragma unroll
         for (int i = 0; i < AHEAD; ++i) { xk[i] = read_k(j, i); xv[i] = read_v(j, i); }
         __builtin_amdgcn_sched_barrier(0);
@@ -1399,14 +1411,19 @@ __global__ __launch_bounds__(NT, 2) void k_dq2(Params p, BwdArgs a, ZeroMulti zm
         for (int i = 0; i < NS; ++i) {
           sacc = mfma(xk[i], qB[i], sacc);
           pacc = mfma(xv[i], doB[i], pacc);
+#pragma unroll
+          for (int e = 0; e < EPS; ++e) {
+            const int r = EPS * i + e;
+            dsv[r] = pp[r] * fmaf(pc[r], scale, -dls);
+          }
+          if (i == NS / 2 - 1) A0 = pack8(dsv);
           if (i + AHEAD < NS) { xk[i + AHEAD] = read_k(j, i + AHEAD); xv[i + AHEAD] = read_v(j, i + AHEAD); }
           __builtin_amdgcn_sched_barrier(0);
         }
+        A1 = pack8(dsv + 8);
       }
       // region 2: the dQ products of tile t - 1 among the exponentials of tile t
-      float pp[16], dsv[16];
       {
-        constexpr int EPS = 16 / NS;
         bf16x8 bq[NS];
 #pragma unroll
         for (int i = 0; i < AHEAD; ++i) bq[i] = read_kt(jp, i);
@@ -1434,9 +1451,7 @@ __global__ __launch_bounds__(NT, 2) void k_dq2(Params p, BwdArgs a, ZeroMulti zm
         }
       }
 #pragma unroll
-      for (int r = 0; r < 16; ++r) dsv[r] = pp[r] * fmaf(pacc[r], scale, -dls);
-      A0 = pack8(dsv);
-      A1 = pack8(dsv + 8);
+      for (int r = 0; r < 16; ++r) pc[r] = pacc[r];
     };
     auto stepc = [&](int t, auto jc) {
       constexpr int j = decltype(jc)::value;
@@ -1458,7 +1473,8 @@ __global__ __launch_bounds__(NT, 2) void k_dq2(Params p, BwdArgs a, ZeroMulti zm
       stepc(t + 3, std::integral_constant<int, 3>{});
     }
     for (; t < n_it; ++t) step(t);
-    // the dQ products of the last tile
+    // the dS and dQ products of the last tile
+    ds_prev();
     {
       const unsigned int jb = ((n_it - 1) % NBQ) * TS;
       bf16x8 bq[NS];
