@@ -63,6 +63,34 @@ hipError_t launch_delta(const void* o, int o_bf16, const void* dout, int do_bf16
 hipError_t launch_dsinks(const float* lse, const float* delta, const float* sinks, float* dsinks,
                          int B, int H, int Sq, Packed pk, hipStream_t st);
 hipError_t launch_zero_rows(float* x, int B, int H, int S, int D, const int64_t* str, hipStream_t st);
+// Partial dK / dV sums of split key-block units.  Part 0 of a unit writes
+// dK / dV itself; part p >= 1 writes the slot partial_slot(kb, p) of its
+// (batch entry, KV head): 128 keys x (Dqk + Dv) floats, the dK row of a key
+// then its dV row.  Key block 0 has nparts0 parts, every other block nsplit.
+struct Partials {
+  float* base;   // nullptr: no partials (parts add atomically, or no split)
+  int nslot;     // slots per (batch entry, KV head)
+  int nparts0, nsplit;
+};
+__host__ __device__ inline int partial_slot(const Partials& pt, int kb, int part) {
+  return (kb == 0 ? 0 : pt.nparts0 - 1 + (kb - 1) * (pt.nsplit - 1)) + part - 1;
+}
+
+// dK / dV of a dense [B, Hk, Sk, D] problem (strided rows) and the partials
+// still to be added into them, in slot order.
+struct PartialSum {
+  Partials pt;
+  float* dk;
+  float* dv;
+  int64_t dk_str[3], dv_str[3];
+  int B, Hk, Sk, Dk, Dv;
+};
+
+// Stream-ordered device scratch from a memory pool that the library keeps
+// per device (memory returned to the pool stays reserved for later calls).
+hipError_t scratch_alloc(void** ptr, size_t bytes, hipStream_t st);
+hipError_t scratch_free(void* ptr, hipStream_t st);
+
 // Up to three strided row tensors zeroed as one flat range: tensor k covers
 // the elements [off[k], off[k + 1]), counted in 4-float groups where vec[k].
 struct ZeroMulti {

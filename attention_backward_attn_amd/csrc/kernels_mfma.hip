@@ -123,9 +123,12 @@ enum : int { kStore = 0, kAtomicAdd = 1, kAddInto = 2 };
 // kb falls linearly with kb, so block kb and block nkb-1-kb together cost the
 // same for every pair -- one pair per workgroup balances the grid.
 // Splitting: a unit's iteration list may be cut into `nsplit` contiguous
-// parts handled by separate workgroups, each adding its partial dK/dV into
-// zeroed outputs.  With exactly two addends onto zero the fp32 result does
-// not depend on their order, so a two-way split stays deterministic.
+// parts handled by separate workgroups.  With partials (k_dkdv2 on dense
+// problems, more than two parts) part 0 writes dK/dV and the other parts
+// their own slots, which the dQ pass adds in slot order afterwards
+// (deterministic for any split); otherwise every part adds atomically into
+// zeroed outputs (with exactly two addends onto zero the fp32 result does
+// not depend on their order).
 // Sink block: with sink tokens under a sliding window, key block 0 is seen by
 // every query row while the others see only a band; it gets `nsplit0` parts,
 // dealt first (logical block x < nsplit0).
@@ -133,7 +136,8 @@ struct DkdvGrid {
   int pair;      // complementary key blocks per workgroup
   int nsplit;    // parts per unit (logical block y = hk * nsplit + part)
   int nsplit0;   // parts of key block 0 (1 = no separate treatment)
-  int out_mode;  // kStore / kAtomicAdd / kAddInto
+  int out_mode;  // kStore / kAtomicAdd / kAddInto (part 0 with partials)
+  Partials pt;   // slots of parts >= 1 (pt.base nullptr: none)
 };
 
 // Kernel k_dkdv (problems with a bias): four waves, wave w owns keys
@@ -581,9 +585,40 @@ __global__ __launch_bounds__(NT2) void k_dkdv2(Params p, BwdArgs a, DkdvGrid gd)
 #pragma unroll
       for (int s = 0; s < NS; ++s) fB[s] = as_bf16x8(*(const u16x8*)(src + jc * rs + 16 * s + 8 * lg));
     }
+    // where this wave's dV (S wave) or dK (dP wave) rows go: dK / dV, or for
+    // part >= 1 of a split unit with partials the part's slot (rows j - k0,
+    // the dK columns then the dV ones)
+    const bool slot = gd.pt.base != nullptr && part > 0;
+    float* op;
+    int64_t os, jr;
+    if (slot) {
+      const int rw = p.Dqk + p.Dv;
+      op = gd.pt.base + (((int64_t)b * p.Hk + hk) * gd.pt.nslot + partial_slot(gd.pt, kb, part)) * BK * rw +
+           (sw ? p.Dqk : 0);
+      os = rw;
+      jr = k0;
+    } else {
+      op = sw ? a.dv + sv.k_off(p.dv_str, b) + hk * p.dv_str[1] : a.dk + sv.k_off(p.dk_str, b) + hk * p.dk_str[1];
+      os = sw ? p.dv_str[2] : p.dk_str[2];
+      jr = 0;
+    }
+    const int mode = slot ? kStore : out_mode;
     __syncthreads();  // readers of the previous unit's LDS tiles are done
     wait_vm_loads();
-    if (n_it <= 0) continue;
+    if (n_it <= 0) {
+      // no query row reaches this part: stored rows get zeros (rows that
+      // are added into keep their values)
+      if (mode == kStore) {
+#pragma unroll
+        for (int n = 0; n < NC; ++n)
+#pragma unroll
+          for (int r = 0; r < 16; ++r) {
+            const int64_t j = kw + crow(r, lg);
+            if (j < Sk) op[(j - jr) * os + 32 * n + lr] = 0.f;
+          }
+      }
+      continue;
+    }
 
     // tile walks: `ld` runs ahead with the loads, `fr` is the tile whose
     // S / dP is formed next
@@ -822,18 +857,15 @@ __global__ __launch_bounds__(NT2) void k_dkdv2(Params p, BwdArgs a, DkdvGrid gd)
       }
 
       // Epilogue: dV (S wave) or dK (dP wave, scaled through dS) of this pair's keys.
-      float* op = SW ? a.dv + sv.k_off(p.dv_str, b) + hk * p.dv_str[1]
-                     : a.dk + sv.k_off(p.dk_str, b) + hk * p.dk_str[1];
-      const int64_t os = SW ? p.dv_str[2] : p.dk_str[2];
 #pragma unroll
       for (int n = 0; n < NC; ++n) {
 #pragma unroll
         for (int r = 0; r < 16; ++r) {
           const int64_t j = kw + crow(r, lg);
           if (j < Sk) {
-            float* po = op + j * os + 32 * n + lr;
-            if (out_mode == kAtomicAdd) atomic_add_f32(po, og[n][r]);
-            else if (out_mode == kAddInto) *po += og[n][r];
+            float* po = op + (j - jr) * os + 32 * n + lr;
+            if (mode == kAtomicAdd) atomic_add_f32(po, og[n][r]);
+            else if (mode == kAddInto) *po += og[n][r];
             else *po = og[n][r];
           }
         }
@@ -850,7 +882,9 @@ struct DkdvPlan {
   dim3 grid;
 };
 
-DkdvPlan plan_dkdv(const Params& p, bool bloop, bool accumulate_dkdv, bool deterministic) {
+// partials: split parts write slots that the dQ pass adds (k_dkdv2, dense
+// problems); otherwise they add atomically.
+DkdvPlan plan_dkdv(const Params& p, bool bloop, bool accumulate_dkdv, bool deterministic, bool partials) {
   DkdvPlan pl{};
   const int nkb = (p.Sk + BK - 1) / BK;
   const Mask& m = p.mask;
@@ -859,11 +893,12 @@ DkdvPlan plan_dkdv(const Params& p, bool bloop, bool accumulate_dkdv, bool deter
   pl.g.pair = (m.kind != kMaskNone && m.wl < 0 && nkb > 1) ? 1 : 0;
   const int xblocks = pl.g.pair ? (nkb + 1) / 2 : nkb;
   const int64_t units = (int64_t)xblocks * p.Hk * (bloop ? 1 : p.B);
-  // Partial dK/dV go through atomic adds onto zeroed outputs: never with the
-  // batch loop (its dbias is ordered), and only two-way when the result must
-  // be deterministic -- two partials into existing values would not be.
-  const bool can_split = !bloop && !(accumulate_dkdv && deterministic);
-  const int max_parts = deterministic ? 2 : 16;
+  // Atomic partial dK/dV go onto zeroed outputs: never with the batch loop
+  // (its dbias is ordered), and only two-way when the result must be
+  // deterministic -- two partials into existing values would not be.  Slot
+  // partials are summed in a fixed order, so any split is deterministic.
+  const bool can_split = !bloop && (partials || !(accumulate_dkdv && deterministic));
+  const int max_parts = (deterministic && !partials) ? 2 : 16;
   // Split until the grid covers the chip once (one workgroup per CU at one
   // wave per SIMD), keeping at least a few iterations per part; more parts
   // cost more dK/dV atomics than they gain in balance.
@@ -886,7 +921,10 @@ DkdvPlan plan_dkdv(const Params& p, bool bloop, bool accumulate_dkdv, bool deter
     pl.g.nsplit0 = ns0;
   }
   const int nparts_max = pl.g.nsplit * pl.g.nsplit0;
-  pl.g.out_mode = nparts_max > 1 ? kAtomicAdd : (accumulate_dkdv ? kAddInto : kStore);
+  pl.g.out_mode = (nparts_max > 1 && !partials) ? kAtomicAdd : (accumulate_dkdv ? kAddInto : kStore);
+  // slots per (batch entry, KV head) when parts write partials (base set by the launcher)
+  pl.g.pt = Partials{nullptr, 0, nparts_max, pl.g.nsplit};
+  if (partials && nparts_max > 1) pl.g.pt.nslot = (nparts_max - 1) + (nkb - 1) * (pl.g.nsplit - 1);
   pl.grid = dim3(xblocks + pl.g.nsplit0 - 1, p.Hk * pl.g.nsplit, bloop ? 1 : p.B);
   return pl;
 }
@@ -1157,6 +1195,72 @@ __global__ __launch_bounds__(NT, 2) void k_dq(Params p, BwdArgs a) {
 // ---------------------------------------------------------------------------
 constexpr int NBQ = 4;   // K / V tile buffers (k_dq2)
 
+// Rows of a PartialSum that have partials: those of every key when the
+// blocks are split (nsplit > 1), else those of key block 0 only.
+__host__ __device__ inline int partial_rows_per_head(const PartialSum& ps) {
+  return ps.pt.nsplit > 1 ? ps.Sk : (ps.Sk < BK ? ps.Sk : BK);
+}
+
+// Rows [r0, r1) (r = (b Hk + h) nrow + i, nrow from partial_rows_per_head)
+// of a PartialSum, thread t of nt (nt a multiple of (Dk + Dv) / 4): the
+// dK / dV row of key i gets the partials of its block's parts >= 1 added in
+// slot order.  A thread takes one float4 column of every (nt / w)-th row,
+// with the loads of U rows in flight together; row and element counts fit
+// in 32 bits.
+__device__ inline void partial_sum_rows(const PartialSum& ps, int r0, int r1, int t, int nt) {
+  constexpr int U = 4;
+  const int w = (ps.Dk + ps.Dv) / 4, wk = ps.Dk / 4, rw = ps.Dk + ps.Dv;
+  const int c = t % w, rstep = nt / w, nrow = partial_rows_per_head(ps);
+  for (int rb = r0 + t / w; rb < r1; rb += U * rstep) {
+    float4 v[U], x[U];
+    float* dst[U];
+    const float* src[U];
+    int parts[U], kbv[U];
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      const int r = rb + u * rstep;
+      parts[u] = 0;
+      if (r < r1) {
+        const int bh = r / nrow, i = r - bh * nrow;
+        const int b = bh / ps.Hk, h = bh - b * ps.Hk;
+        kbv[u] = i / BK;
+        parts[u] = kbv[u] == 0 ? ps.pt.nparts0 : ps.pt.nsplit;
+        dst[u] = c < wk ? ps.dk + b * ps.dk_str[0] + h * ps.dk_str[1] + i * ps.dk_str[2] + 4 * c
+                        : ps.dv + b * ps.dv_str[0] + h * ps.dv_str[1] + i * ps.dv_str[2] + 4 * (c - wk);
+        src[u] = ps.pt.base + ((int64_t)bh * ps.pt.nslot * BK + (i - kbv[u] * BK)) * rw + 4 * c;
+        if (parts[u] >= 2) {
+          v[u] = *(const float4*)dst[u];
+          x[u] = *(const float4*)(src[u] + (int64_t)partial_slot(ps.pt, kbv[u], 1) * BK * rw);
+        }
+      }
+    }
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      if (parts[u] < 2) continue;
+      v[u].x += x[u].x;
+      v[u].y += x[u].y;
+      v[u].z += x[u].z;
+      v[u].w += x[u].w;
+      for (int q = 2; q < parts[u]; ++q) {
+        const float4 y = *(const float4*)(src[u] + (int64_t)partial_slot(ps.pt, kbv[u], q) * BK * rw);
+        v[u].x += y.x;
+        v[u].y += y.y;
+        v[u].z += y.z;
+        v[u].w += y.w;
+      }
+      *(float4*)dst[u] = v[u];
+    }
+  }
+}
+
+// The sums alone (when no dQ pass follows the key-block pass).
+__global__ __launch_bounds__(256) void k_partial_sum(PartialSum ps) {
+  const int rows = ps.B * ps.Hk * partial_rows_per_head(ps);
+  const int per = (rows + (int)gridDim.x - 1) / (int)gridDim.x;
+  const int r0 = blockIdx.x * per;
+  partial_sum_rows(ps, r0, min(rows, r0 + per), threadIdx.x, 256);
+}
+
 template <int D>
 struct __attribute__((aligned(1024))) SmemDQ2 {
   unsigned char k[NBQ][BK3 * 2 * D];   // K tile, swizzled
@@ -1164,7 +1268,7 @@ struct __attribute__((aligned(1024))) SmemDQ2 {
 };
 
 template <int D>
-__global__ __launch_bounds__(NT, 2) void k_dq2(Params p, BwdArgs a, ZeroMulti zm) {
+__global__ __launch_bounds__(NT, 2) void k_dq2(Params p, BwdArgs a, ZeroMulti zm, PartialSum ps) {
   constexpr int NS = D / 16;   // k-steps over the head dim
   constexpr int NC = D / 32;   // 32-column blocks of dQ
   constexpr int RB = Swz<D>::RB, CR = Swz<D>::CR;
@@ -1176,15 +1280,24 @@ __global__ __launch_bounds__(NT, 2) void k_dq2(Params p, BwdArgs a, ZeroMulti zm
 
   const int tid = threadIdx.x, l = tid & 63, lr = l & 31, lg = l >> 5;
   const int w = __builtin_amdgcn_readfirstlane(tid >> 6);   // wave-uniform
-  // Tensors that the key-block pass launched after this one adds into (its
-  // split parts) are zeroed here, an even share per workgroup, once its own
-  // work is done (the stores then overlap other workgroups' products).
+  // Side duties for the key-block pass, an even share per workgroup once its
+  // own work is done (the memory traffic then overlaps other workgroups'
+  // products): the tensors that a key-block pass launched after this one
+  // adds into (its split parts) are zeroed ...
   auto zero_share = [&]() {
     if (zm.n > 0) {
       const int64_t nwg = (int64_t)gridDim.x * gridDim.y * gridDim.z;
       const int64_t wg = blockIdx.x + (int64_t)gridDim.x * (blockIdx.y + (int64_t)gridDim.y * blockIdx.z);
       const int64_t total = zm.off[zm.n], per = (total + nwg - 1) / nwg;
       zero_multi_range(zm, wg * per, min(total, (wg + 1) * per), tid, NT);
+    }
+    // ... and the partial dK / dV that the key-block pass launched before
+    // this one left in slots are added into dK / dV
+    if (ps.pt.base != nullptr) {
+      const int nwg = (int)(gridDim.x * gridDim.y * gridDim.z);
+      const int wg = (int)(blockIdx.x + gridDim.x * (blockIdx.y + gridDim.y * blockIdx.z));
+      const int rows = ps.B * ps.Hk * partial_rows_per_head(ps), per = (rows + nwg - 1) / nwg;
+      partial_sum_rows(ps, wg * per, min(rows, (wg + 1) * per), tid, NT);
     }
   };
   const BlockXYZ blk = a.xmajor ? xcd_block_xmajor() : xcd_block();
@@ -1504,16 +1617,18 @@ __global__ __launch_bounds__(NT, 2) void k_dq2(Params p, BwdArgs a, ZeroMulti zm
   zero_share();
 }
 
-// zm: tensors to zero on the way (k_dq2 only; zm.n == 0 with a bias)
+// zm / ps: tensors to zero, partials to sum on the way (k_dq2 only: none
+// with a bias)
 template <int D>
-hipError_t launch_dq(const Params& p, const BwdArgs& a0, const ZeroMulti& zm, hipStream_t st) {
+hipError_t launch_dq(const Params& p, const BwdArgs& a0, const ZeroMulti& zm, const PartialSum& ps,
+                     hipStream_t st) {
   const dim3 grid((p.Sq + BQ3 - 1) / BQ3, p.Hq, p.B);
   BwdArgs a = a0;
   a.xmajor = xmajor_fits(p, grid.y, grid.z) ? 1 : 0;
   if (a.bias)
     hipLaunchKernelGGL((k_dq<D, true>), grid, dim3(NT), 0, st, p, a);
   else
-    hipLaunchKernelGGL((k_dq2<D>), grid, dim3(NT), 0, st, p, a, zm);
+    hipLaunchKernelGGL((k_dq2<D>), grid, dim3(NT), 0, st, p, a, zm, ps);
   return hipGetLastError();
 }
 
@@ -1564,16 +1679,54 @@ hipError_t launch_bwd_mfma(const Params& p, const BwdArgs& a, hipStream_t st) {
   // dK / dV by key blocks (k_dkdv2; k_dkdv with a bias, where dbias is
   // summed over the batch in a fixed order by one workgroup per key block
   // walking the batch) and dQ by query blocks (k_dq2; k_dq with a bias): no
-  // dQ atomics.  The passes are independent.  The dK / dV that the split
-  // key-block parts add into are zeroed by the dQ pass, run first, when it is
-  // k_dq2 and reads its K / V mostly from L2 (the stores then cost it little);
-  // otherwise by a zero kernel ahead of the key-block pass.
+  // dQ atomics.  Units of dense problems without a bias split into more than
+  // two parts leave the partial dK / dV of their parts >= 1 in pool scratch,
+  // and the dQ pass, run second, adds them in slot order.  Otherwise split
+  // parts add atomically into zeroed dK / dV; those are zeroed by the dQ
+  // pass, run first, when it is k_dq2 and reads its K / V mostly from L2
+  // (the stores then cost it little), else by a zero kernel ahead of the
+  // key-block pass.
   const bool bloop = a.dbias != nullptr;
-  const DkdvPlan pl = plan_dkdv(p, bloop, a.accumulate_dkdv != 0, a.deterministic != 0);
-  const bool run_dq = p.Sq > 0 && p.B > 0, dq_first = run_dq && !bias && xmajor_fits(p, p.Hq, p.B);
-  auto dq = [&](const ZeroMulti& zm) {
-    return p.Dqk == 64 ? launch_dq<64>(p, a, zm, st) : launch_dq<128>(p, a, zm, st);
+  const bool run_dq = p.Sq > 0 && p.B > 0, run_kv = p.Sk > 0 && p.B > 0;
+  auto dq = [&](const ZeroMulti& zm, const PartialSum& ps) {
+    return p.Dqk == 64 ? launch_dq<64>(p, a, zm, ps, st) : launch_dq<128>(p, a, zm, ps, st);
   };
+  auto dkdv = [&](const DkdvPlan& pl) {
+    return p.Dqk == 64 ? dispatch_dkdv<64>(p, a, pl, bias, bloop, st) : dispatch_dkdv<128>(p, a, pl, bias, bloop, st);
+  };
+  const bool vec_ok = aligned16(a.dk) && aligned16(a.dv) && p.dk_str[0] % 4 == 0 && p.dk_str[1] % 4 == 0 &&
+                      p.dk_str[2] % 4 == 0 && p.dv_str[0] % 4 == 0 && p.dv_str[1] % 4 == 0 && p.dv_str[2] % 4 == 0;
+  const bool fits32 = (int64_t)p.B * p.Hk * p.Sk * ((p.Dqk + p.Dv) / 4) < ((int64_t)1 << 31);
+  const bool partials_ok = !bias && p.cu_k == nullptr && vec_ok && fits32;
+  DkdvPlan pl = plan_dkdv(p, bloop, a.accumulate_dkdv != 0, a.deterministic != 0, partials_ok);
+  // At most two parts per unit: atomic adds onto zeroed outputs cost no
+  // more than partials (the stream-ordered scratch allocation included) and
+  // stay deterministic -- except added into existing values.
+  if (partials_ok && pl.g.pt.nparts0 <= 2 && pl.g.nsplit <= 2 && !(a.deterministic && a.accumulate_dkdv))
+    pl = plan_dkdv(p, bloop, a.accumulate_dkdv != 0, a.deterministic != 0, false);
+  if (partials_ok && pl.g.pt.nslot > 0 && run_kv) {
+    const size_t bytes = (size_t)p.B * p.Hk * pl.g.pt.nslot * BK * (p.Dqk + p.Dv) * sizeof(float);
+    void* scratch = nullptr;
+    if (scratch_alloc(&scratch, bytes, st) == hipSuccess) {
+      pl.g.pt.base = (float*)scratch;
+      PartialSum ps{pl.g.pt, a.dk, a.dv, {p.dk_str[0], p.dk_str[1], p.dk_str[2]},
+                    {p.dv_str[0], p.dv_str[1], p.dv_str[2]}, p.B, p.Hk, p.Sk, p.Dqk, p.Dv};
+      hipError_t e = dkdv(pl);
+      if (e == hipSuccess) {
+        if (run_dq) {
+          e = dq(ZeroMulti{}, ps);
+        } else {
+          hipLaunchKernelGGL(k_partial_sum, dim3(1024), dim3(256), 0, st, ps);
+          e = hipGetLastError();
+        }
+      }
+      const hipError_t ef = scratch_free(scratch, st);
+      return e != hipSuccess ? e : ef;
+    }
+    (void)hipGetLastError();   // no scratch: atomic parts instead
+    pl = plan_dkdv(p, bloop, a.accumulate_dkdv != 0, a.deterministic != 0, false);
+  }
+  const bool dq_first = run_dq && !bias && xmajor_fits(p, p.Hq, p.B);
   ZeroMulti zm{};
   if (pl.g.out_mode == kAtomicAdd && !a.accumulate_dkdv && p.Sk > 0) {
     // dense [B, Hk, Sk] or the packed rows of a variable-length batch
@@ -1588,15 +1741,14 @@ hipError_t launch_bwd_mfma(const Params& p, const BwdArgs& a, hipStream_t st) {
     }
   }
   if (dq_first) {
-    hipError_t e = dq(zm);
+    hipError_t e = dq(zm, PartialSum{});
     if (e != hipSuccess) return e;
   }
-  if (p.Sk > 0 && p.B > 0) {
-    hipError_t e = p.Dqk == 64 ? dispatch_dkdv<64>(p, a, pl, bias, bloop, st)
-                               : dispatch_dkdv<128>(p, a, pl, bias, bloop, st);
+  if (run_kv) {
+    hipError_t e = dkdv(pl);
     if (e != hipSuccess) return e;
   }
-  if (run_dq && !dq_first) return dq(ZeroMulti{});
+  if (run_dq && !dq_first) return dq(ZeroMulti{}, PartialSum{});
   return hipSuccess;
 }
 

@@ -81,9 +81,11 @@ typedef enum {
 /* attn_bwd flags.
  * ATTN_DETERMINISTIC: two calls give bitwise identical results.  dQ always
  *   comes from a query-block-parallel pass that accumulates in registers,
- *   and dbias is summed over the batch in a fixed order; without the flag a
- *   block of dK / dV may be split into more than two parts whose fp32 adds
- *   into the output can come in any order, so the low bits may vary.
+ *   and dbias is summed over the batch in a fixed order.  Without the flag
+ *   the dK / dV of a key block may be split into more than two parts whose
+ *   fp32 adds into the output can come in any order, so the low bits may
+ *   vary -- except for bf16 problems with head dim 64 / 128, no bias and no
+ *   packed batch, whose parts are summed in a fixed order either way.
  * ATTN_ACCUMULATE_DQ: add into dQ instead of overwriting it (chunked /
  *   ring use, [RING] _ring_bwd accumulates dq over the K/V chunks).
  * ATTN_ACCUMULATE_DKDV: add into dK and dV instead of overwriting them
@@ -184,6 +186,12 @@ attn_status_t attn_bwd_preprocess(const attn_problem_t* p, const void* o, const 
  * dq is overwritten (or added into with ATTN_ACCUMULATE_DQ); dk, dv and
  * dbias are overwritten.  bias is nullable; dbias is nullable and requires
  * bias.  delta must come from attn_bwd_preprocess on the same O / dO.
+ * Scratch: when the key blocks are split into more than two parts the call
+ * takes device scratch for their partial sums from a memory pool that the
+ * library keeps per device, allocated and released in the order of
+ * `stream` (hipMallocFromPoolAsync / hipFreeAsync; memory returned to the
+ * pool stays reserved for later calls).  If that allocation fails the parts
+ * add atomically instead; no other error results from it.
  * For a K/V chunk pass the chunk's K/V views with k_offset / sk_total and
  * the GLOBAL O, LSE and delta ([RING] _ring_bwd). */
 attn_status_t attn_bwd(const attn_problem_t* p, const void* q, const void* k, const void* v,

@@ -389,6 +389,53 @@ def test_accumulate_into_existing(flags):
         check(n, got, ref[n], 2e-2)
 
 
+@pytest.mark.parametrize("shape", [(1, 4, 1, 200, 700), (4, 8, 8, 256, 2048)], ids=["split", "unsplit"])
+@pytest.mark.parametrize("flags", [0, ab.ATTN_DETERMINISTIC], ids=["atomic", "determ"])
+def test_unseen_keys_overwritten(shape, flags):
+    """Keys that no query row sees (top-left mask with Sk > Sq) get zero
+    dK / dV, and every other output its oracle value, when the output
+    buffers start out holding NaN: no row of dQ / dK / dV is left unwritten,
+    whether the key blocks are split over workgroups or not."""
+    B, Hq, Hk, Sq, Sk = shape
+    D = 128
+    say(f"[unseen keys] {shape} flags={flags}")
+    x = random_case(B, Hq, Hk, Sq, Sk, D, D, "bf16", 31, False, False)
+    spec = MaskSpec("top_left")
+    scale = 1 / np.sqrt(D)
+    o64, lse64 = oracle.forward(x["q"], x["k"], x["v"], scale, spec)
+    o32, lse32 = o64.astype(np.float32), lse64.astype(np.float32)
+    ref = oracle.backward(x["q"], x["k"], x["v"], o32, x["do"], lse32, scale, spec)
+    q, k, v, do = (dev(x[n], torch.bfloat16) for n in ("q", "k", "v", "do"))
+    o, lse = dev(o32, torch.float32), dev(lse32, torch.float32)
+    dq, dk, dv = (torch.full(t.shape, float("nan"), device="cuda") for t in (q, k, v))
+    delta = torch.empty_like(lse)
+    p = ab.make_problem(q, k, v, o=o, do=do, dq=dq, dk=dk, dv=dv, scale=scale, mask="top_left")
+    ab.attn_bwd_preprocess(p, o, do, lse, None, delta, None, None, None, None)
+    ab.attn_bwd(p, q, k, v, do, lse, delta, None, dq, dk, dv, None, flags)
+    torch.cuda.synchronize()
+    for n, t in (("dq", dq), ("dk", dk), ("dv", dv)):
+        check(n, t, ref[n], 2e-2)
+    assert (dk[:, :, Sq:] == 0).all() and (dv[:, :, Sq:] == 0).all()
+
+
+def test_split_units_bitwise_repeatable():
+    """Without a bias the key-block parts of a split unit leave partial sums
+    that are added in a fixed order: repeated calls agree bit for bit, with
+    or without ATTN_DETERMINISTIC (the small GQA workload splits each unit
+    eight ways)."""
+    w = WORKLOADS["gqa4_causal_tl_s1024"]
+    x = make_inputs(w)
+    q, k, v, do = (dev(x[n], torch.bfloat16) for n in ("q", "k", "v", "do"))
+    o, lse = ab.forward(q, k, v, scale=w.scale, mask=w.mask)
+    outs = []
+    for flags in (0, 0, ab.ATTN_DETERMINISTIC):
+        g = ab.backward(q, k, v, o, do, lse, flags=flags, scale=w.scale, mask=w.mask)
+        torch.cuda.synchronize()
+        outs.append({n: g[n].clone() for n in ("dq", "dk", "dv")})
+    for n in ("dq", "dk", "dv"):
+        assert torch.equal(outs[0][n], outs[1][n]) and torch.equal(outs[0][n], outs[2][n]), n
+
+
 def test_preprocess_zeroes_gradients():
     x = random_case(2, 4, 2, 130, 150, 64, 64, "bf16", 8, False, False)
     dt = torch.bfloat16
