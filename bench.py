@@ -270,32 +270,47 @@ def main():
     dbias = torch.empty(bias.shape, device=dev, dtype=torch.float32) if bias is not None else None
     p = ab.make_problem(q, k, v, o=o, do=do, dq=dq, dk=dk, dv=dv, bias=bias, scale=w.scale, **mask_kw)
 
-    def step(flags, ev=None):
+    def pre():
+        ab.attn_bwd_preprocess(p, o, do, lse, sinks, delta, dsinks, None, None, None, stream)
+
+    def main(flags):
         # attn_bwd overwrites dQ, dK, dV (and dbias); it zeroes by itself
         # whatever its split parts add into.
-        if ev is not None:
-            ev[0].record(stream)
-        ab.attn_bwd_preprocess(p, o, do, lse, sinks, delta, dsinks, None, None, None, stream)
-        if ev is not None:
-            ev[1].record(stream)
         ab.attn_bwd(p, q, k, v, do, lse, delta, bias, dq, dk, dv, dbias, flags, stream)
-        if ev is not None:
-            ev[2].record(stream)
+
+    def step(flags):
+        pre()
+        main(flags)
+
+    def region(fn, n):
+        """Mean ms of n back-to-back calls of fn on the bench stream, between
+        two HIP events on that stream (no event between the calls: a
+        recorded event costs the stream several microseconds)."""
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        torch.cuda.synchronize()
+        e0.record(stream)
+        for _ in range(n):
+            fn()
+        e1.record(stream)
+        torch.cuda.synchronize()
+        return e0.elapsed_time(e1) / n
 
     def timed(flags, steps, warmup):
+        """The timed region: exactly `steps` steps between a synchronize and
+        a HIP event on each side; then the two calls of a step on their own
+        (back-to-back regions of the same length) for the per-call times."""
         for _ in range(warmup):
             step(flags)
         torch.cuda.synchronize()
-        evs = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(steps)]
         t0 = time.perf_counter()
-        for i in range(steps):
-            step(flags, evs[i])
-        torch.cuda.synchronize()
-        wall = (time.perf_counter() - t0) / steps
-        pre = [e[0].elapsed_time(e[1]) for e in evs]
-        main_k = [e[1].elapsed_time(e[2]) for e in evs]
-        span = evs[0][0].elapsed_time(evs[-1][2]) / steps
-        return wall * 1e3, span, float(np.mean(pre)), float(np.mean(main_k)), float(np.median(main_k))
+        span = region(lambda: step(flags), steps)
+        wall = time.perf_counter() - t0
+        pre_ms = region(pre, steps)
+        # attn_bwd alone: the mean over one region, the median of five shorter ones
+        main_ms = region(lambda: main(flags), steps)
+        n5 = max(1, steps // 5)
+        subs = [region(lambda: main(flags), n5) for _ in range(5)]
+        return wall * 1e3 / steps, span, pre_ms, main_ms, float(np.median(subs))
 
     flops = backward_flops(w)
     pairs = allowed_pairs(w.Sq, w.Sk, w.mask, w.window_left, w.window_right, w.num_sink)
