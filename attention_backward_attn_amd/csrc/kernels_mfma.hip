@@ -1697,7 +1697,10 @@ hipError_t launch_bwd_mfma(const Params& p, const BwdArgs& a, hipStream_t st) {
   const bool vec_ok = aligned16(a.dk) && aligned16(a.dv) && p.dk_str[0] % 4 == 0 && p.dk_str[1] % 4 == 0 &&
                       p.dk_str[2] % 4 == 0 && p.dv_str[0] % 4 == 0 && p.dv_str[1] % 4 == 0 && p.dv_str[2] % 4 == 0;
   const bool fits32 = (int64_t)p.B * p.Hk * p.Sk * ((p.Dqk + p.Dv) / 4) < ((int64_t)1 << 31);
-  const bool partials_ok = !bias && p.cu_k == nullptr && vec_ok && fits32;
+  // (no scratch allocation while the stream is being captured into a graph)
+  hipStreamCaptureStatus cap = hipStreamCaptureStatusNone;
+  const bool capturing = hipStreamIsCapturing(st, &cap) == hipSuccess && cap != hipStreamCaptureStatusNone;
+  const bool partials_ok = !bias && p.cu_k == nullptr && vec_ok && fits32 && !capturing;
   DkdvPlan pl = plan_dkdv(p, bloop, a.accumulate_dkdv != 0, a.deterministic != 0, partials_ok);
   // At most two parts per unit: atomic adds onto zeroed outputs cost no
   // more than partials (the stream-ordered scratch allocation included) and

@@ -190,8 +190,10 @@ attn_status_t attn_bwd_preprocess(const attn_problem_t* p, const void* o, const 
  * takes device scratch for their partial sums from a memory pool that the
  * library keeps per device, allocated and released in the order of
  * `stream` (hipMallocFromPoolAsync / hipFreeAsync; memory returned to the
- * pool stays reserved for later calls).  If that allocation fails the parts
- * add atomically instead; no other error results from it.
+ * pool stays reserved for later calls).  If that allocation fails, or
+ * `stream` is being captured into a graph, the parts add atomically
+ * instead; no error results from it.  The call records no memset, so it
+ * can be captured.
  * For a K/V chunk pass the chunk's K/V views with k_offset / sk_total and
  * the GLOBAL O, LSE and delta ([RING] _ring_bwd). */
 attn_status_t attn_bwd(const attn_problem_t* p, const void* q, const void* k, const void* v,

@@ -436,6 +436,56 @@ def test_split_units_bitwise_repeatable():
         assert torch.equal(outs[0][n], outs[1][n]) and torch.equal(outs[0][n], outs[2][n]), n
 
 
+@pytest.mark.parametrize("name", ["gqa4_causal_tl_s1024", "gqa4_causal_br_s4096"])
+def test_graph_capture_replays(name):
+    """attn_bwd_preprocess + attn_bwd captured into a HIP graph: every
+    replay, with eager calls and synchronizations between the replays,
+    reproduces the eager result (no memset nodes and no scratch allocation
+    inside the capture; the small workload, whose eager call sums eight
+    parts in slot order, sums them atomically under capture, so it is
+    compared within fp32 rounding, the headline bit for bit)."""
+    w = WORKLOADS[name]
+    say(f"[graph] {name}")
+    x = make_inputs(w)
+    q, k, v, do = (dev(x[n], torch.bfloat16) for n in ("q", "k", "v", "do"))
+    o, lse = ab.forward(q, k, v, scale=w.scale, mask=w.mask)
+    dq, dk, dv = (torch.empty(t.shape, device="cuda") for t in (q, k, v))
+    delta = torch.empty_like(lse)
+    p = ab.make_problem(q, k, v, o=o, do=do, dq=dq, dk=dk, dv=dv, scale=w.scale, mask=w.mask)
+
+    def step(st):
+        ab.attn_bwd_preprocess(p, o, do, lse, None, delta, None, None, None, None, st)
+        ab.attn_bwd(p, q, k, v, do, lse, delta, None, dq, dk, dv, None, 0, st)
+
+    main = torch.cuda.current_stream()
+    step(main)
+    torch.cuda.synchronize()
+    ref = [t.clone() for t in (dq, dk, dv)]
+    side = torch.cuda.Stream()
+    side.wait_stream(main)
+    with torch.cuda.stream(side):
+        step(side)
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g, stream=side):
+        step(torch.cuda.current_stream())
+    torch.cuda.synchronize()
+    exact = name == "gqa4_causal_br_s4096"
+    for i in range(3):
+        for t in (dq, dk, dv):
+            t.fill_(float("nan"))
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        for n, a, b in zip(("dq", "dk", "dv"), (dq, dk, dv), ref):
+            if exact:
+                assert torch.equal(a, b), f"replay {i}: {n}"
+            else:
+                check(f"replay {i}: {n}", a, b.cpu().numpy(), 1e-5)
+        step(main)   # eager work between the replays
+        torch.cuda.synchronize()
+
+
 def test_preprocess_zeroes_gradients():
     x = random_case(2, 4, 2, 130, 150, 64, 64, "bf16", 8, False, False)
     dt = torch.bfloat16
