@@ -486,6 +486,28 @@ def test_graph_capture_replays(name):
         torch.cuda.synchronize()
 
 
+def test_no_query_rows_split_parts():
+    """No query rows (Sq = 0) with 64 query heads on one KV head: the key
+    blocks still split into eight parts, every part stores zeros, and with no
+    dQ pass to follow, a kernel of its own sums the partial slots: dK and dV
+    (NaN-filled before) come out zero."""
+    B, Hq, Hk, Sk, D = 1, 64, 1, 512, 128
+    say("[no rows] Sq=0, Hq=64, Hk=1, Sk=512")
+    g = torch.Generator().manual_seed(5)
+    k, v = (torch.randn(B, Hk, Sk, D, generator=g).to("cuda", torch.bfloat16) for _ in range(2))
+    q = torch.empty(B, Hq, 0, D, device="cuda", dtype=torch.bfloat16)
+    do = torch.empty_like(q)
+    o = torch.empty(B, Hq, 0, D, device="cuda")
+    lse = torch.empty(B, Hq, 0, device="cuda")
+    delta = torch.empty_like(lse)
+    dq = torch.empty(B, Hq, 0, D, device="cuda")
+    dk, dv = (torch.full(t.shape, float("nan"), device="cuda") for t in (k, v))
+    p = ab.make_problem(q, k, v, o=o, do=do, dq=dq, dk=dk, dv=dv, scale=D ** -0.5, mask="none")
+    ab.attn_bwd(p, q, k, v, do, lse, delta, None, dq, dk, dv, None, 0)
+    torch.cuda.synchronize()
+    assert (dk == 0).all() and (dv == 0).all()
+
+
 def test_preprocess_zeroes_gradients():
     x = random_case(2, 4, 2, 130, 150, 64, 64, "bf16", 8, False, False)
     dt = torch.bfloat16
