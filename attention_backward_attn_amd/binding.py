@@ -22,7 +22,7 @@ MASKS = {"none": 0, "top_left": 1, "bottom_right": 2}
 ATTN_DETERMINISTIC, ATTN_ACCUMULATE_DQ, ATTN_ACCUMULATE_DKDV, ATTN_SHARED_KV = 1, 2, 4, 8
 
 EXPORTED = ("attn_problem_init", "attn_fwd_lse", "attn_bwd_preprocess", "attn_bwd",
-            "attn_lse_merge", "attn_status_string")
+            "attn_bwd_workspace_size", "attn_lse_merge", "attn_status_string")
 
 
 class AttnError(RuntimeError):
@@ -48,6 +48,7 @@ class attn_problem_t(ctypes.Structure):
         ("bias_str", ctypes.c_int64 * 2),
         ("cu_seqlens_q", ctypes.c_void_p), ("cu_seqlens_k", ctypes.c_void_p),
         ("total_q", ctypes.c_int64), ("total_k", ctypes.c_int64),
+        ("workspace", ctypes.c_void_p), ("workspace_bytes", ctypes.c_int64),
     ]
 
 
@@ -72,6 +73,8 @@ def lib() -> ctypes.CDLL:
         L.attn_bwd_preprocess.restype = i32
         L.attn_bwd.argtypes = [P, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, ctypes.c_uint32, vp]
         L.attn_bwd.restype = i32
+        L.attn_bwd_workspace_size.argtypes = [P, ctypes.c_uint32, ctypes.POINTER(i64)]
+        L.attn_bwd_workspace_size.restype = i32
         L.attn_lse_merge.argtypes = [i32, i32, i32, i32, vp, vp, vp, vp, vp]
         L.attn_lse_merge.restype = i32
         L.attn_status_string.argtypes = [i32]
@@ -199,6 +202,28 @@ def attn_bwd(p: attn_problem_t, q, k, v, do, lse, delta, bias, dq, dk, dv, dbias
                                       flags, _stream(stream)))
 
 
+def attn_bwd_workspace_size(p: attn_problem_t, flags: int = 0) -> int:
+    """Bytes of caller workspace with which attn_bwd keeps split key blocks'
+    partial sums (0: none used)."""
+    n = ctypes.c_int64(0)
+    _check("attn_bwd_workspace_size", lib().attn_bwd_workspace_size(ctypes.byref(p), flags, ctypes.byref(n)))
+    return int(n.value)
+
+
+def set_workspace(p: attn_problem_t, flags: int = 0, device=None):
+    """Attach a workspace of attn_bwd_workspace_size bytes to p (a torch
+    uint8 tensor, returned so that the caller keeps it alive; None when the
+    call needs none)."""
+    n = attn_bwd_workspace_size(p, flags)
+    if n == 0:
+        p.workspace, p.workspace_bytes = None, 0
+        return None
+    import torch
+    ws = torch.empty(n, dtype=torch.uint8, device=device or "cuda")
+    p.workspace, p.workspace_bytes = ws.data_ptr(), n
+    return ws
+
+
 def attn_lse_merge(o_acc, lse_acc, o_part, lse_part, stream=None):
     B, H, Sq, Dv = o_acc.shape
     for t in (o_acc, lse_acc, o_part, lse_part):
@@ -248,6 +273,11 @@ def backward(q, k, v, o, do, lse, *, bias=None, sinks=None, want_dbias=False, fl
     dsinks = torch.empty(Hq, device=dev, dtype=torch.float32) if sinks is not None else None
     dbias = torch.empty(bias.shape, device=dev, dtype=torch.float32) if (want_dbias and bias is not None) else None
     p = make_problem(q, k, v, o=o, do=do, dq=dq, dk=dk, dv=dv, bias=bias, **mask_kw)
+    # workspace for split key blocks' partial sums: released after the call is
+    # enqueued (torch's caching allocator reuses it only in the order of the
+    # current stream, which is the call's stream unless one is given)
+    ws = set_workspace(p, flags, dev)
     attn_bwd_preprocess(p, o, do, lse, sinks, delta, dsinks, None, None, None, stream)
     attn_bwd(p, q, k, v, do, lse, delta, bias, dq, dk, dv, dbias, flags, stream)
+    del ws
     return {"dq": dq, "dk": dk, "dv": dv, "dbias": dbias, "dsinks": dsinks, "delta": delta}

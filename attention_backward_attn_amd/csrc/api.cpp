@@ -246,6 +246,8 @@ attn_status_t attn_bwd(const attn_problem_t* p, const void* q, const void* k, co
   attn::BwdArgs a{q, k, v, dout, lse, delta, bias, dq, dk, dv, dbias,
                   (flags & ATTN_ACCUMULATE_DQ) ? 1 : 0, (flags & ATTN_DETERMINISTIC) ? 1 : 0,
                   (flags & ATTN_ACCUMULATE_DKDV) ? 1 : 0};
+  a.workspace = p->workspace_bytes > 0 ? p->workspace : nullptr;
+  a.workspace_bytes = p->workspace_bytes;
   hipStream_t s = (hipStream_t)stream;
   if (p->in_dtype == ATTN_BF16) {
     if (!attn::mfma_bwd_supported(kp)) {
@@ -265,6 +267,21 @@ attn_status_t attn_bwd(const attn_problem_t* p, const void* q, const void* k, co
     return ATTN_OK;
   }
   return hip_status(attn::launch_bwd_simt(kp, a, p->in_dtype == ATTN_BF16, s));
+}
+
+attn_status_t attn_bwd_workspace_size(const attn_problem_t* p, uint32_t flags, int64_t* bytes) {
+  if (!bytes) return ATTN_EINVAL;
+  *bytes = 0;
+  attn_status_t st = check_problem(p);
+  if (st != ATTN_OK) return st;
+  if ((flags & ~(uint32_t)(ATTN_DETERMINISTIC | ATTN_ACCUMULATE_DQ | ATTN_ACCUMULATE_DKDV | ATTN_SHARED_KV)) != 0)
+    return ATTN_EINVAL;
+  // only the bf16 matrix-core path of attn_bwd keeps partial sums
+  if ((flags & ATTN_SHARED_KV) || p->Dqk == attn::kSharedKvD || p->Dv == attn::kSharedKvD) return ATTN_OK;
+  const Params kp = make_params(p);
+  if (p->in_dtype != ATTN_BF16 || !attn::mfma_bwd_supported(kp)) return ATTN_OK;
+  *bytes = attn::bwd_workspace_bytes(kp, (flags & ATTN_ACCUMULATE_DKDV) != 0, (flags & ATTN_DETERMINISTIC) != 0);
+  return ATTN_OK;
 }
 
 attn_status_t attn_lse_merge(int32_t B, int32_t H, int32_t Sq, int32_t Dv, float* o_acc, float* lse_acc,

@@ -34,6 +34,8 @@ struct BwdArgs {
   int deterministic;
   int accumulate_dkdv;  // add into dk / dv instead of overwriting
   int xmajor;           // set by the launcher: walk row blocks heaviest first per XCD
+  void* workspace;      // caller scratch for partial dK / dV sums (nullable)
+  int64_t workspace_bytes;
 };
 
 // Whether the query-block kernels may walk each XCD's (head, batch) units
@@ -86,10 +88,6 @@ struct PartialSum {
   int B, Hk, Sk, Dk, Dv;
 };
 
-// Stream-ordered device scratch from a memory pool that the library keeps
-// per device (memory returned to the pool stays reserved for later calls).
-hipError_t scratch_alloc(void** ptr, size_t bytes, hipStream_t st);
-hipError_t scratch_free(void* ptr, hipStream_t st);
 
 // Up to three strided row tensors zeroed as one flat range: tensor k covers
 // the elements [off[k], off[k + 1]), counted in 4-float groups where vec[k].
@@ -124,6 +122,9 @@ hipError_t launch_fwd_mfma(const Params& p, const FwdArgs& a, bool o_bf16, hipSt
 // bf16 matrix-core backward (gfx950 MFMA), head dims 64 and 128.
 bool mfma_bwd_supported(const Params& p);
 hipError_t launch_bwd_mfma(const Params& p, const BwdArgs& a, hipStream_t st);
+// Workspace bytes with which launch_bwd_mfma keeps split parts' partial
+// sums (0: none used); host-only.
+int64_t bwd_workspace_bytes(const Params& p, bool accumulate_dkdv, bool deterministic);
 
 // bf16 matrix-core kernels for head dim 512 with one tensor as keys and
 // values (k == v): forward, and the backward whose dk output is the gradient

@@ -1,7 +1,5 @@
 // Memory-bound helper kernels: the backward preprocess (delta = rowsum(dO*O)
 // and the sink-logit gradient), zero fills, and the log-sum-exp merge.
-#include <mutex>
-
 #include "kernels.h"
 #include "mfma_util.h"
 
@@ -193,40 +191,6 @@ ZeroMulti make_zero_multi(const ZeroRows* z, int n) {
   m.n = k;
   return m;
 }
-
-namespace {
-std::mutex g_pool_mu;
-constexpr int kMaxDevices = 64;
-hipMemPool_t g_pool[kMaxDevices] = {};
-}  // namespace
-
-hipError_t scratch_alloc(void** ptr, size_t bytes, hipStream_t st) {
-  int dev = 0;
-  hipError_t e = hipGetDevice(&dev);
-  if (e != hipSuccess) return e;
-  if (dev < 0 || dev >= kMaxDevices) return hipErrorInvalidDevice;
-  hipMemPool_t pool;
-  {
-    std::lock_guard<std::mutex> lock(g_pool_mu);
-    if (g_pool[dev] == nullptr) {
-      hipMemPoolProps props{};
-      props.allocType = hipMemAllocationTypePinned;
-      props.location.type = hipMemLocationTypeDevice;
-      props.location.id = dev;
-      hipMemPool_t np = nullptr;
-      e = hipMemPoolCreate(&np, &props);
-      if (e != hipSuccess) return e;
-      uint64_t keep = UINT64_MAX;   // freed blocks stay in the pool
-      e = hipMemPoolSetAttribute(np, hipMemPoolAttrReleaseThreshold, &keep);
-      if (e != hipSuccess) return e;
-      g_pool[dev] = np;
-    }
-    pool = g_pool[dev];
-  }
-  return hipMallocFromPoolAsync(ptr, bytes, pool, st);
-}
-
-hipError_t scratch_free(void* ptr, hipStream_t st) { return hipFreeAsync(ptr, st); }
 
 hipError_t launch_zero_multi(const ZeroRows* z, int n, hipStream_t st) {
   const ZeroMulti m = make_zero_multi(z, n);

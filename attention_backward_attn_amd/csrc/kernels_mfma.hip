@@ -1662,6 +1662,28 @@ bool xmajor_fits(const Params& p, int ny, int nz) {
   return bytes <= 3.0 * 1024 * 1024;
 }
 
+// Partial sums are kept for dense problems whose row and element counts
+// fit in 32 bits.
+static bool partials_fit(const Params& p) {
+  return p.cu_k == nullptr && (int64_t)p.B * p.Hk * p.Sk * ((p.Dqk + p.Dv) / 4) < ((int64_t)1 << 31);
+}
+
+// The key-block plan of a call: with partial sums when `partials` allows
+// them and a unit splits into more than two parts (or into two added into
+// existing values in deterministic mode); otherwise with atomic parts,
+// which for at most two parts onto zeroed outputs cost no more (measured)
+// and stay deterministic.
+static DkdvPlan plan_bwd(const Params& p, bool bloop, bool accumulate_dkdv, bool deterministic, bool partials) {
+  DkdvPlan pl = plan_dkdv(p, bloop, accumulate_dkdv, deterministic, partials);
+  if (partials && pl.g.pt.nparts0 <= 2 && pl.g.nsplit <= 2 && !(deterministic && accumulate_dkdv))
+    pl = plan_dkdv(p, bloop, accumulate_dkdv, deterministic, false);
+  return pl;
+}
+
+static int64_t partial_bytes(const Params& p, const DkdvPlan& pl) {
+  return (int64_t)p.B * p.Hk * pl.g.pt.nslot * BK * (p.Dqk + p.Dv) * (int64_t)sizeof(float);
+}
+
 hipError_t launch_bwd_mfma(const Params& p, const BwdArgs& a, hipStream_t st) {
   if (!aligned16(a.q) || !aligned16(a.k) || !aligned16(a.v) || !aligned16(a.dout))
     return launch_bwd_simt(p, a, 1, st);
@@ -1680,8 +1702,8 @@ hipError_t launch_bwd_mfma(const Params& p, const BwdArgs& a, hipStream_t st) {
   // summed over the batch in a fixed order by one workgroup per key block
   // walking the batch) and dQ by query blocks (k_dq2; k_dq with a bias): no
   // dQ atomics.  Units of dense problems without a bias split into more than
-  // two parts leave the partial dK / dV of their parts >= 1 in pool scratch,
-  // and the dQ pass, run second, adds them in slot order.  Otherwise split
+  // two parts leave the partial dK / dV of their parts >= 1 in the caller's
+  // workspace, and the dQ pass, run second, adds them in slot order.  Otherwise split
   // parts add atomically into zeroed dK / dV; those are zeroed by the dQ
   // pass, run first, when it is k_dq2 and reads its K / V mostly from L2
   // (the stores then cost it little), else by a zero kernel ahead of the
@@ -1696,37 +1718,20 @@ hipError_t launch_bwd_mfma(const Params& p, const BwdArgs& a, hipStream_t st) {
   };
   const bool vec_ok = aligned16(a.dk) && aligned16(a.dv) && p.dk_str[0] % 4 == 0 && p.dk_str[1] % 4 == 0 &&
                       p.dk_str[2] % 4 == 0 && p.dv_str[0] % 4 == 0 && p.dv_str[1] % 4 == 0 && p.dv_str[2] % 4 == 0;
-  const bool fits32 = (int64_t)p.B * p.Hk * p.Sk * ((p.Dqk + p.Dv) / 4) < ((int64_t)1 << 31);
-  // (no scratch allocation while the stream is being captured into a graph)
-  hipStreamCaptureStatus cap = hipStreamCaptureStatusNone;
-  const bool capturing = hipStreamIsCapturing(st, &cap) == hipSuccess && cap != hipStreamCaptureStatusNone;
-  const bool partials_ok = !bias && p.cu_k == nullptr && vec_ok && fits32 && !capturing;
-  DkdvPlan pl = plan_dkdv(p, bloop, a.accumulate_dkdv != 0, a.deterministic != 0, partials_ok);
-  // At most two parts per unit: atomic adds onto zeroed outputs cost no
-  // more than partials (the stream-ordered scratch allocation included) and
-  // stay deterministic -- except added into existing values.
-  if (partials_ok && pl.g.pt.nparts0 <= 2 && pl.g.nsplit <= 2 && !(a.deterministic && a.accumulate_dkdv))
-    pl = plan_dkdv(p, bloop, a.accumulate_dkdv != 0, a.deterministic != 0, false);
-  if (partials_ok && pl.g.pt.nslot > 0 && run_kv) {
-    const size_t bytes = (size_t)p.B * p.Hk * pl.g.pt.nslot * BK * (p.Dqk + p.Dv) * sizeof(float);
-    void* scratch = nullptr;
-    if (scratch_alloc(&scratch, bytes, st) == hipSuccess) {
-      pl.g.pt.base = (float*)scratch;
+  const bool partials_ok = !bias && vec_ok && partials_fit(p);
+  DkdvPlan pl = plan_bwd(p, bloop, a.accumulate_dkdv != 0, a.deterministic != 0, partials_ok);
+  if (pl.g.pt.nslot > 0 && run_kv) {
+    if (a.workspace != nullptr && aligned16(a.workspace) && a.workspace_bytes >= partial_bytes(p, pl)) {
+      pl.g.pt.base = (float*)a.workspace;
       PartialSum ps{pl.g.pt, a.dk, a.dv, {p.dk_str[0], p.dk_str[1], p.dk_str[2]},
                     {p.dv_str[0], p.dv_str[1], p.dv_str[2]}, p.B, p.Hk, p.Sk, p.Dqk, p.Dv};
       hipError_t e = dkdv(pl);
-      if (e == hipSuccess) {
-        if (run_dq) {
-          e = dq(ZeroMulti{}, ps);
-        } else {
-          hipLaunchKernelGGL(k_partial_sum, dim3(1024), dim3(256), 0, st, ps);
-          e = hipGetLastError();
-        }
-      }
-      const hipError_t ef = scratch_free(scratch, st);
-      return e != hipSuccess ? e : ef;
+      if (e != hipSuccess) return e;
+      if (run_dq) return dq(ZeroMulti{}, ps);
+      hipLaunchKernelGGL(k_partial_sum, dim3(1024), dim3(256), 0, st, ps);
+      return hipGetLastError();
     }
-    (void)hipGetLastError();   // no scratch: atomic parts instead
+    // no (or too small a) workspace: the parts add atomically
     pl = plan_dkdv(p, bloop, a.accumulate_dkdv != 0, a.deterministic != 0, false);
   }
   const bool dq_first = run_dq && !bias && xmajor_fits(p, p.Hq, p.B);
@@ -1753,6 +1758,12 @@ hipError_t launch_bwd_mfma(const Params& p, const BwdArgs& a, hipStream_t st) {
   }
   if (run_dq && !dq_first) return dq(ZeroMulti{}, PartialSum{});
   return hipSuccess;
+}
+
+int64_t bwd_workspace_bytes(const Params& p, bool accumulate_dkdv, bool deterministic) {
+  if (p.Sk <= 0 || p.B <= 0 || !partials_fit(p)) return 0;
+  const DkdvPlan pl = plan_bwd(p, false, accumulate_dkdv, deterministic, true);
+  return pl.g.pt.nslot > 0 ? partial_bytes(p, pl) : 0;
 }
 
 }  // namespace attn

@@ -269,6 +269,9 @@ def main():
     dsinks = torch.empty(w.Hq, device=dev, dtype=torch.float32) if sinks is not None else None
     dbias = torch.empty(bias.shape, device=dev, dtype=torch.float32) if bias is not None else None
     p = ab.make_problem(q, k, v, o=o, do=do, dq=dq, dk=dk, dv=dv, bias=bias, scale=w.scale, **mask_kw)
+    # caller-owned workspace for split key blocks' partial sums (none when
+    # the call needs none), allocated before any timing
+    ws = ab.set_workspace(p, 0)  # noqa: F841
 
     def pre():
         ab.attn_bwd_preprocess(p, o, do, lse, sinks, delta, dsinks, None, None, None, stream)
@@ -378,6 +381,7 @@ def main():
             probs = [ab.make_problem(q, k[:, :, i * c:(i + 1) * c], v[:, :, i * c:(i + 1) * c], o=o, do=do, dq=dq,
                                      dk=dk[:, :, i * c:(i + 1) * c], dv=dv[:, :, i * c:(i + 1) * c], scale=w.scale,
                                      k_offset=i * c, sk_total=w.Sk, **mask_kw) for i in range(n)]
+            ws_c = [ab.set_workspace(pc, ab.ATTN_ACCUMULATE_DQ) for pc in probs]  # noqa: F841
 
             def chunked():
                 ab.attn_bwd_preprocess(p, o, do, lse, None, delta, None, dq, None, None, stream)

@@ -85,7 +85,8 @@ typedef enum {
  *   the dK / dV of a key block may be split into more than two parts whose
  *   fp32 adds into the output can come in any order, so the low bits may
  *   vary -- except for bf16 problems with head dim 64 / 128, no bias and no
- *   packed batch, whose parts are summed in a fixed order either way.
+ *   packed batch given a workspace of attn_bwd_workspace_size bytes, whose
+ *   parts are summed in a fixed order either way.
  * ATTN_ACCUMULATE_DQ: add into dQ instead of overwriting it (chunked /
  *   ring use, [RING] _ring_bwd accumulates dq over the K/V chunks).
  * ATTN_ACCUMULATE_DKDV: add into dK and dV instead of overwriting them
@@ -142,6 +143,17 @@ typedef struct attn_problem {
   const int32_t* cu_seqlens_q;
   const int32_t* cu_seqlens_k;
   int64_t total_q, total_k;
+  /* Optional device scratch of attn_bwd, owned by the caller (nullable;
+   * zero-filled by attn_problem_init).  When the dK / dV of key blocks are
+   * split over workgroups into more than two parts, a call with at least
+   * attn_bwd_workspace_size bytes here (16-byte aligned) keeps the parts'
+   * partial sums in it and adds them into dK / dV in a fixed order; with
+   * less, or none, the parts add atomically into the output.  A call uses
+   * the buffer in the order of its stream until it completes there, so calls
+   * that may overlap need buffers of their own.  Its contents on entry do
+   * not matter. */
+  void* workspace;
+  int64_t workspace_bytes;
 } attn_problem_t;
 
 /* Fill *p with contiguous [B, H, S, D] strides and defaults: scale =
@@ -186,20 +198,23 @@ attn_status_t attn_bwd_preprocess(const attn_problem_t* p, const void* o, const 
  * dq is overwritten (or added into with ATTN_ACCUMULATE_DQ); dk, dv and
  * dbias are overwritten.  bias is nullable; dbias is nullable and requires
  * bias.  delta must come from attn_bwd_preprocess on the same O / dO.
- * Scratch: when the key blocks are split into more than two parts the call
- * takes device scratch for their partial sums from a memory pool that the
- * library keeps per device, allocated and released in the order of
- * `stream` (hipMallocFromPoolAsync / hipFreeAsync; memory returned to the
- * pool stays reserved for later calls).  If that allocation fails, or
- * `stream` is being captured into a graph, the parts add atomically
- * instead; no error results from it.  The call records no memset, so it
- * can be captured.
+ * The library allocates nothing: scratch for the partial sums of split key
+ * blocks comes from p->workspace when the caller provides one (see
+ * attn_problem_t).  The call records no memset, so it can be captured
+ * into a graph.
  * For a K/V chunk pass the chunk's K/V views with k_offset / sk_total and
  * the GLOBAL O, LSE and delta ([RING] _ring_bwd). */
 attn_status_t attn_bwd(const attn_problem_t* p, const void* q, const void* k, const void* v,
                        const void* dout, const float* lse, const float* delta,
                        const float* bias, float* dq, float* dk, float* dv, float* dbias,
                        uint32_t flags, void* stream);
+
+/* Bytes of p->workspace with which attn_bwd(p, ..., flags) keeps the
+ * partial sums of split key blocks instead of adding them atomically (a
+ * bias problem does not use it; 0: the call splits no block into more than
+ * two parts, or takes a path without partial sums).  Host-only: makes no
+ * HIP call.  ATTN_EINVAL for an invalid problem or a null `bytes`. */
+attn_status_t attn_bwd_workspace_size(const attn_problem_t* p, uint32_t flags, int64_t* bytes);
 
 /* In-place log-sum-exp merge of a partial result into an accumulator
  * ([RING] _ring_fwd):  lse = logaddexp(lse_acc, lse_part),

@@ -197,3 +197,37 @@ def test_shared_kv_forward_validation():
     assert fwd(shared_problem(in_dtype=B.ATTN_F32), FAKE, FAKE) == B.ATTN_EUNSUPPORTED
     assert fwd(shared_problem(Dv=256), FAKE, FAKE) == B.ATTN_EUNSUPPORTED
     assert fwd(shared_problem(Sq=0), FAKE, FAKE) == B.ATTN_OK
+
+
+def sized_problem(B_, Hq, Hk, Sq, Sk, D, mask, **kw):
+    p = B.attn_problem_t()
+    B.lib().attn_problem_init(ctypes.byref(p), B_, Hq, Hk, Sq, Sk, D, D)
+    p.mask = B.MASKS[mask]
+    for k, v in kw.items():
+        setattr(p, k, v)
+    return p
+
+
+def test_workspace_size_query():
+    """attn_bwd_workspace_size is host-only: 0 when no key block splits into
+    more than two parts (the headline: two parts add onto zero), whole
+    slots of 128 keys x (Dqk + Dv) floats per (batch entry, KV head) when
+    one does (the small GQA workload splits eight ways), and 0 for paths
+    without partial sums (fp32 inputs, a packed batch is not asked here)."""
+    head = sized_problem(1, 32, 8, 4096, 4096, 128, "bottom_right")
+    assert B.attn_bwd_workspace_size(head, 0) == 0
+    # two parts added into existing values deterministically need slots
+    assert B.attn_bwd_workspace_size(head, B.ATTN_DETERMINISTIC | B.ATTN_ACCUMULATE_DKDV) > 0
+    small = sized_problem(2, 16, 4, 1024, 1024, 128, "top_left")
+    n = B.attn_bwd_workspace_size(small, 0)
+    slot = 128 * (128 + 128) * 4
+    assert n > 0 and n % (2 * 4 * slot) == 0
+    assert B.attn_bwd_workspace_size(small, B.ATTN_DETERMINISTIC) == n
+    f32 = sized_problem(2, 16, 4, 1024, 1024, 128, "top_left", in_dtype=B.ATTN_F32)
+    assert B.attn_bwd_workspace_size(f32, 0) == 0
+    L = B.lib()
+    assert L.attn_bwd_workspace_size(ctypes.byref(small), 0, None) == B.ATTN_EINVAL
+    bad = sized_problem(2, 16, 3, 1024, 1024, 128, "top_left")   # Hq % Hk != 0
+    x = ctypes.c_int64(7)
+    assert L.attn_bwd_workspace_size(ctypes.byref(bad), 0, ctypes.byref(x)) == B.ATTN_EINVAL and x.value == 0
+    assert L.attn_bwd_workspace_size(ctypes.byref(small), 64, ctypes.byref(x)) == B.ATTN_EINVAL
