@@ -320,15 +320,18 @@ def main():
     # Clock settle: the GPU takes a few hundred milliseconds of load to reach
     # its steady clock; run the step (untimed) for that long before the
     # warmup steps, so the timed steps see the steady state.
-    settle_s = args.settle_ms * 1e-3
-    t_end = time.perf_counter() + settle_s
-    n_settle = 0
-    while time.perf_counter() < t_end:
-        step(0)
-        n_settle += 1
-        if n_settle % 8 == 0:
-            torch.cuda.synchronize()
-    torch.cuda.synchronize()
+    def settle(flags, ms):
+        t_end = time.perf_counter() + ms * 1e-3
+        n = 0
+        while time.perf_counter() < t_end:
+            step(flags)
+            n += 1
+            if n % 8 == 0:
+                torch.cuda.synchronize()
+        torch.cuda.synchronize()
+        return n
+
+    n_settle = settle(0, args.settle_ms)
     wall_ms, span_ms, pre_ms, main_ms, main_med = timed(0, args.steps, args.warmup)
     ms_per_step = span_ms
     value = flops / (ms_per_step * 1e-3) / 1e12
@@ -362,7 +365,9 @@ def main():
                      "kernel_ms_mean": round(main_ms, 4), "kernel_ms_median": round(main_med, 4)},
     }
     if not args.no_extras:
-        _, span_d, _, main_d, _ = timed(ab.ATTN_DETERMINISTIC, max(3, args.steps // 2), 2)
+        # (its own clock settle and as many steps as the headline line)
+        settle(ab.ATTN_DETERMINISTIC, min(args.settle_ms, 200.0))
+        _, span_d, _, main_d, _ = timed(ab.ATTN_DETERMINISTIC, args.steps, args.warmup)
         out["deterministic"] = {"ms_per_step": round(span_d, 4),
                                 "tflops": round(flops / (span_d * 1e-3) / 1e12, 2)}
         # forward (input producer), timed for context
