@@ -117,6 +117,8 @@ attn_status_t bwd_shared_kv(const attn_problem_t* p, const void* q, const void* 
   attn::BwdArgs a{q, k, k, dout, lse, delta, nullptr, dq, dk, nullptr, nullptr,
                   (flags & ATTN_ACCUMULATE_DQ) ? 1 : 0, (flags & ATTN_DETERMINISTIC) ? 1 : 0,
                   (flags & ATTN_ACCUMULATE_DKDV) ? 1 : 0, 0};
+  a.workspace = p->workspace_bytes > 0 ? p->workspace : nullptr;
+  a.workspace_bytes = p->workspace_bytes;
   return hip_status(attn::launch_bwd512(kp, a, (hipStream_t)stream));
 }
 
@@ -276,9 +278,15 @@ attn_status_t attn_bwd_workspace_size(const attn_problem_t* p, uint32_t flags, i
   if (st != ATTN_OK) return st;
   if ((flags & ~(uint32_t)(ATTN_DETERMINISTIC | ATTN_ACCUMULATE_DQ | ATTN_ACCUMULATE_DKDV | ATTN_SHARED_KV)) != 0)
     return ATTN_EINVAL;
-  // only the bf16 matrix-core path of attn_bwd keeps partial sums
-  if ((flags & ATTN_SHARED_KV) || p->Dqk == attn::kSharedKvD || p->Dv == attn::kSharedKvD) return ATTN_OK;
+  // the bf16 matrix-core paths of attn_bwd keep partial sums
   const Params kp = make_params(p);
+  if ((flags & ATTN_SHARED_KV) || p->Dqk == attn::kSharedKvD || p->Dv == attn::kSharedKvD) {
+    if ((flags & ATTN_SHARED_KV) && p->in_dtype == ATTN_BF16 && p->Dqk == attn::kSharedKvD &&
+        p->Dv == attn::kSharedKvD && attn::mla_supported(kp))
+      *bytes = attn::bwd512_workspace_bytes(kp, (flags & ATTN_DETERMINISTIC) != 0,
+                                            (flags & ATTN_ACCUMULATE_DKDV) != 0);
+    return ATTN_OK;
+  }
   if (p->in_dtype != ATTN_BF16 || !attn::mfma_bwd_supported(kp)) return ATTN_OK;
   *bytes = attn::bwd_workspace_bytes(kp, (flags & ATTN_ACCUMULATE_DKDV) != 0, (flags & ATTN_DETERMINISTIC) != 0);
   return ATTN_OK;

@@ -134,5 +134,8 @@ constexpr int kSharedKvD = 512;
 bool mla_supported(const Params& p);
 hipError_t launch_fwd512(const Params& p, const FwdArgs& a, bool o_bf16, hipStream_t st);
 hipError_t launch_bwd512(const Params& p, const BwdArgs& a, hipStream_t st);
+// Workspace bytes with which launch_bwd512 keeps its head-split parts'
+// partial sums (0: none used); host-only.
+int64_t bwd512_workspace_bytes(const Params& p, bool deterministic, bool accumulate);
 
 }  // namespace attn

@@ -498,7 +498,10 @@ struct __attribute__((aligned(1024))) SmemY {
 
 enum : int { kStoreX = 0, kAddIntoX = 1, kAtomicAddX = 2 };
 
-__global__ __launch_bounds__(XNT, 1) void k_dkv512(Params p, BwdArgs a, int parts, int out_mode) {
+// slots: with partial sums, part q >= 1 stores its dKV into slots + (q - 1)
+// slot_elems, at the element offsets dKV has from a.dk (nullptr: none)
+__global__ __launch_bounds__(XNT, 1) void k_dkv512(Params p, BwdArgs a, int parts, int out_mode, float* slots,
+                                                    int64_t slot_elems) {
   __shared__ SmemY sm;
   const int tid = threadIdx.x, l = tid & 63, lr = l & 15, g = l >> 4;
   const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -731,9 +734,13 @@ __global__ __launch_bounds__(XNT, 1) void k_dkv512(Params p, BwdArgs a, int part
     step(n_it, std::false_type{}, std::true_type{});
   }
   // dKV rows k0 + 16 kb + lane % 16, columns 128 w + 16 c + 4 g .. + 3
-  // (a part without tiles has nothing to add to the zeroed output)
-  if (n_it == 0 && out_mode == kAtomicAddX) return;
-  float* dkp = a.dk + sv.k_off(p.dk_str, b) + hk * p.dk_str[1];
+  // (a part without tiles has nothing to add to the zeroed output; a part
+  // with a slot stores it, zeros included)
+  const bool slot = slots != nullptr && part > 0;
+  if (n_it == 0 && out_mode == kAtomicAddX && !slot) return;
+  const int64_t dko = sv.k_off(p.dk_str, b) + hk * p.dk_str[1];
+  float* dkp = slot ? slots + (part - 1) * slot_elems + dko : a.dk + dko;
+  const int mode = slot ? kStoreX : out_mode;
 #pragma unroll
   for (int kb2 = 0; kb2 < 4; ++kb2) {
     const int kk = k0 + 16 * kb2 + lr;
@@ -742,16 +749,38 @@ __global__ __launch_bounds__(XNT, 1) void k_dkv512(Params p, BwdArgs a, int part
       for (int c = 0; c < NCW; ++c) {
         float* d = dkp + (int64_t)kk * p.dk_str[2] + 128 * w + 16 * c + 4 * g;
         const f32x4 v = acc[4 * c + kb2];
-        if (out_mode == kAtomicAddX) {
+        if (mode == kAtomicAddX) {
 #pragma unroll
           for (int r = 0; r < 4; ++r) atomic_add_f32(d + r, v[r]);
-        } else if (out_mode == kAddIntoX) {
+        } else if (mode == kAddIntoX) {
           *(f32x4*)d = *(const f32x4*)d + v;
         } else {
           *(f32x4*)d = v;
         }
       }
     }
+  }
+}
+
+// dKV (+)= the slots of parts 1 .. nslot, in slot order: 128 threads per
+// 512-float row, rows r of [tot_k, Hk] (packed) or [B, Hk, Sk] (dense).
+__global__ __launch_bounds__(256) void k_slot_sum512(Params p, float* dk, const float* slots, int64_t slot_elems,
+                                                     int nslot) {
+  const bool pk = p.cu_k != nullptr;
+  const int64_t rows = pk ? p.tot_k * p.Hk : (int64_t)p.B * p.Hk * p.Sk;
+  const int c = threadIdx.x & 127;
+  for (int64_t r = (int64_t)blockIdx.x * 2 + (threadIdx.x >> 7); r < rows; r += (int64_t)gridDim.x * 2) {
+    int64_t off;
+    if (pk) {
+      off = (r / p.Hk) * p.dk_str[2] + (r % p.Hk) * p.dk_str[1];
+    } else {
+      const int64_t i = r % p.Sk, bh = r / p.Sk;
+      off = (bh / p.Hk) * p.dk_str[0] + (bh % p.Hk) * p.dk_str[1] + i * p.dk_str[2];
+    }
+    float* d = dk + off + 4 * c;
+    f32x4 v = *(const f32x4*)d;
+    for (int q = 0; q < nslot; ++q) v += *(const f32x4*)(slots + q * slot_elems + off + 4 * c);
+    *(f32x4*)d = v;
   }
 }
 
@@ -781,41 +810,73 @@ hipError_t launch_fwd512(const Params& p, const FwdArgs& a0, bool o_bf16, hipStr
 }
 
 // Parts per KV head's query group: split the group until the grid covers the
-// chip (a part must divide the group); at most two when the result must be
-// deterministic.
-static int dkv512_parts(const Params& p, bool deterministic, bool accumulate) {
+// chip (a part must divide the group).  Atomic parts: at most two when the
+// result must be deterministic (one when adding into existing values);
+// parts that keep partial sums are summed in a fixed order, at most 16.
+static int dkv512_parts(const Params& p, bool deterministic, bool accumulate, bool partials) {
   const int nkb = (p.Sk + YBK - 1) / YBK;
   const int64_t units = (int64_t)nkb * p.Hk * p.B;
-  const int max_parts = deterministic ? (accumulate ? 1 : 2) : 64;
+  const int max_parts = partials ? 16 : deterministic ? (accumulate ? 1 : 2) : 64;
   int parts = 1;
   while (units * parts < 256 && parts * 2 <= max_parts && p.G % (parts * 2) == 0) parts *= 2;
   return parts;
 }
 
+// Elements of the dKV tensor's extent (one slot of partial sums).
+static int64_t dkv512_extent(const Params& p) {
+  if (p.cu_k) return (p.tot_k - 1) * p.dk_str[2] + (p.Hk - 1) * p.dk_str[1] + p.Dqk;
+  return (int64_t)(p.B - 1) * p.dk_str[0] + (p.Hk - 1) * p.dk_str[1] + (int64_t)(p.Sk - 1) * p.dk_str[2] + p.Dqk;
+}
+
+int64_t bwd512_workspace_bytes(const Params& p, bool deterministic, bool accumulate) {
+  if (p.Sk <= 0 || p.B <= 0 || (p.cu_k && p.tot_k <= 0)) return 0;
+  const int parts = dkv512_parts(p, deterministic, accumulate, true);
+  const int atomic_parts = dkv512_parts(p, deterministic, accumulate, false);
+  // partial sums when they split further or keep a fixed order where atomics could not
+  if (parts < 2 || (parts <= 2 && atomic_parts == parts && !(deterministic && accumulate))) return 0;
+  return (int64_t)(parts - 1) * dkv512_extent(p) * (int64_t)sizeof(float);
+}
+
 hipError_t launch_bwd512(const Params& p, const BwdArgs& a0, hipStream_t st) {
   BwdArgs a = a0;
   if (p.Sk > 0) {
-    const int parts = dkv512_parts(p, a.deterministic != 0, a.accumulate_dkdv != 0);
-    int mode = kStoreX;
-    if (parts > 1) {
-      mode = kAtomicAddX;
-      if (!a.accumulate_dkdv) {
-        ZeroRows z{a.dk, p.B, p.Hk, p.Sk, p.Dqk, {p.dk_str[0], p.dk_str[1], p.dk_str[2]}};
-        if (p.cu_k) {   // packed: every row of the packed tensor
-          z.B = 1;
-          z.S = (int)p.tot_k;
-          z.str[0] = 0;
+    const bool det = a.deterministic != 0, acc = a.accumulate_dkdv != 0;
+    const int64_t need = bwd512_workspace_bytes(p, det, acc);
+    if (need > 0 && a.workspace != nullptr && ((uintptr_t)a.workspace & 15u) == 0 && a.workspace_bytes >= need) {
+      // parts >= 1 store slots of partial sums that are then added in order
+      const int parts = dkv512_parts(p, det, acc, true);
+      const int64_t ext = dkv512_extent(p);
+      float* slots = (float*)a.workspace;
+      const dim3 grid((p.Sk + YBK - 1) / YBK, p.Hk * parts, p.B);
+      hipLaunchKernelGGL(k_dkv512, grid, dim3(XNT), 0, st, p, a, parts, acc ? kAddIntoX : kStoreX, slots, ext);
+      hipError_t e = hipGetLastError();
+      if (e != hipSuccess) return e;
+      hipLaunchKernelGGL(k_slot_sum512, dim3(1024), dim3(256), 0, st, p, a.dk, slots, ext, parts - 1);
+      e = hipGetLastError();
+      if (e != hipSuccess) return e;
+    } else {
+      const int parts = dkv512_parts(p, det, acc, false);
+      int mode = kStoreX;
+      if (parts > 1) {
+        mode = kAtomicAddX;
+        if (!acc) {
+          ZeroRows z{a.dk, p.B, p.Hk, p.Sk, p.Dqk, {p.dk_str[0], p.dk_str[1], p.dk_str[2]}};
+          if (p.cu_k) {   // packed: every row of the packed tensor
+            z.B = 1;
+            z.S = (int)p.tot_k;
+            z.str[0] = 0;
+          }
+          hipError_t e = launch_zero_multi(&z, 1, st);
+          if (e != hipSuccess) return e;
         }
-        hipError_t e = launch_zero_multi(&z, 1, st);
-        if (e != hipSuccess) return e;
+      } else if (acc) {
+        mode = kAddIntoX;
       }
-    } else if (a.accumulate_dkdv) {
-      mode = kAddIntoX;
+      const dim3 grid((p.Sk + YBK - 1) / YBK, p.Hk * parts, p.B);
+      hipLaunchKernelGGL(k_dkv512, grid, dim3(XNT), 0, st, p, a, parts, mode, (float*)nullptr, (int64_t)0);
+      hipError_t e = hipGetLastError();
+      if (e != hipSuccess) return e;
     }
-    const dim3 grid((p.Sk + YBK - 1) / YBK, p.Hk * parts, p.B);
-    hipLaunchKernelGGL(k_dkv512, grid, dim3(XNT), 0, st, p, a, parts, mode);
-    hipError_t e = hipGetLastError();
-    if (e != hipSuccess) return e;
   }
   if (p.Sq > 0) {
     const dim3 grid((p.Sq + XBQ - 1) / XBQ, p.Hq, p.B);

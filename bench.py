@@ -158,6 +158,8 @@ def bench_shared_kv(stream, name: str = "mla_swa512_s4096", steps: int = 10, war
     delta = torch.empty(lse.shape, device=dev)
     dsinks = torch.empty(w.N1, device=dev) if sinks is not None else None
     p = ab.make_problem(q, kv, kv, o=o, do=do, dq=dq, dk=dkv, scale=w.scale, **kw)
+    # caller-owned workspace for the query-head parts' partial sums
+    ws = ab.set_workspace(p, ab.ATTN_SHARED_KV)  # noqa: F841
 
     def step():
         ab.attn_bwd_preprocess(p, o, do, lse, sinks, delta, dsinks, None, None, None, stream)

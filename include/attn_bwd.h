@@ -210,10 +210,11 @@ attn_status_t attn_bwd(const attn_problem_t* p, const void* q, const void* k, co
                        uint32_t flags, void* stream);
 
 /* Bytes of p->workspace with which attn_bwd(p, ..., flags) keeps the
- * partial sums of split key blocks instead of adding them atomically (a
- * bias problem does not use it; 0: the call splits no block into more than
- * two parts, or takes a path without partial sums).  Host-only: makes no
- * HIP call.  ATTN_EINVAL for an invalid problem or a null `bytes`. */
+ * partial sums of split key blocks (with ATTN_SHARED_KV: of the query-head
+ * parts of a KV head) instead of adding them atomically (a bias problem
+ * does not use it; 0: the call splits nothing into more than two parts, or
+ * takes a path without partial sums).  Host-only: makes no HIP call.
+ * ATTN_EINVAL for an invalid problem or a null `bytes`. */
 attn_status_t attn_bwd_workspace_size(const attn_problem_t* p, uint32_t flags, int64_t* bytes);
 
 /* In-place log-sum-exp merge of a partial result into an accumulator
