@@ -12,8 +12,10 @@
 // with the wave's Q fragments in registers as the B operand and K rows from
 // LDS as the A operand, so each lane holds one query row (and the lane
 // l ^ 32 holds the row's other keys).  Online softmax in log2 units: the
-// running row maximum is shared by the two lanes of a row with one shuffle;
-// each lane keeps its own share of the normaliser, added up once at the end.
+// running row maximum is shared by the two lanes of a row with one shuffle
+// and raised only when a tile's exceeds it by more than 8 (P < 2^8, rare O
+// rescales); each lane keeps its own share of the normaliser, added up once
+// at the end.
 // O^T += V^T P^T uses the P values straight from the S^T accumulator as the
 // B operand (reduction slots in accumulator order) and V^T from transposing
 // LDS reads in the same slot order, so O^T's accumulator also has one query
@@ -188,10 +190,13 @@ __global__ __launch_bounds__(NTF, 2) void k_fwd(Params p, FwdArgs a) {
     // t = j' - i' - diag for key j0 + 4 lg + c
     const int tb = j0 + (int)msk.k_off + 4 * lg - (irow + (int)msk.q_off) - (int)msk.diag;
     float mt = -INFINITY;
+    // x: the logit in log2 units with a bias; the raw S without one (the
+    // scale, positive, is applied in the exponential's fma and to the tile
+    // maximum)
     auto elem = [&](int hh, int r, bool masked) {
       const int c = 32 * hh + 8 * (r >> 2) + (r & 3);
-      float x = sacc[hh][r] * scale_log2;
-      if (BIAS) x = fmaf(sm.bias[cur][(32 * w + lr) * BS + 4 * lg + c], kLog2e, x);
+      float x = sacc[hh][r];
+      if (BIAS) x = fmaf(sm.bias[cur][(32 * w + lr) * BS + 4 * lg + c], kLog2e, x * scale_log2);
       if (masked) {
         const int j = j0 + 4 * lg + c;
         const int t = tb + c;
@@ -213,23 +218,27 @@ __global__ __launch_bounds__(NTF, 2) void k_fwd(Params p, FwdArgs a) {
         for (int r = 0; r < 16; ++r) elem(hh, r, true);
     }
     mt = fmaxf(mt, __shfl_xor(mt, 32));
-    const float mn = fmaxf(m, mt);
-    const float mu = mn == -INFINITY ? 0.f : mn;   // no finite logit yet: every P is 0
-    const float alpha = __builtin_amdgcn_exp2f(m - mu);
-    m = mn;
-    if (__any(alpha != 1.f)) {
+    if (!BIAS) mt *= scale_log2;
+    // The running maximum is raised only when the tile's exceeds it by more
+    // than 8 (log2 units): P stays below 2^8 and the O rescale is rare.
+    const bool raise = mt > m + 8.f;   // (m = -inf: any allowed key)
+    if (__builtin_amdgcn_ballot_w64(raise)) {
+      const float mn = raise ? mt : m;
+      const float alpha = raise ? __builtin_amdgcn_exp2f(m - mn) : 1.f;
       lsum *= alpha;
 #pragma unroll
       for (int n = 0; n < NB; ++n)
 #pragma unroll
         for (int r = 0; r < 16; ++r) o[n][r] *= alpha;
+      m = mn;
     }
+    const float mu = m == -INFINITY ? 0.f : m;   // no finite logit yet: every P is 0
 #pragma unroll
     for (int hh = 0; hh < NH; ++hh) {
       float pv[16];
 #pragma unroll
       for (int r = 0; r < 16; ++r) {
-        pv[r] = __builtin_amdgcn_exp2f(sacc[hh][r] - mu);
+        pv[r] = __builtin_amdgcn_exp2f(BIAS ? sacc[hh][r] - mu : fmaf(sacc[hh][r], scale_log2, -mu));
         lsum += pv[r];
       }
       const bf16x8 p0 = pack8(pv), p1 = pack8(pv + 8);
