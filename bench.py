@@ -372,15 +372,15 @@ def main():
         _, span_d, _, main_d, _ = timed(ab.ATTN_DETERMINISTIC, args.steps, args.warmup)
         out["deterministic"] = {"ms_per_step": round(span_d, 4),
                                 "tflops": round(flops / (span_d * 1e-3) / 1e12, 2)}
-        # forward (input producer), timed for context
-        torch.cuda.synchronize()
-        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-        e0.record(stream)
+        # forward (input producer), timed for context: attn_fwd_lse into
+        # buffers of its own, warmed up, then a region of back-to-back calls
+        o_f, lse_f = torch.empty_like(o), torch.empty_like(lse)
+
+        def fwd():
+            ab.attn_fwd_lse(p, q, k, v, bias, sinks, o_f, lse_f, stream)
         for _ in range(3):
-            ab.forward(q, k, v, bias=bias, sinks=sinks, scale=w.scale, stream=stream, **mask_kw)
-        e1.record(stream)
-        torch.cuda.synchronize()
-        fwd_ms = e0.elapsed_time(e1) / 3
+            fwd()
+        fwd_ms = region(fwd, args.steps)
         out["forward"] = {"ms": round(fwd_ms, 4),
                           "tflops": round(2 * (w.Dqk + w.Dv) * pairs * w.B * w.Hq / (fwd_ms * 1e-3) / 1e12, 2)}
         if w.kv_chunks > 1 and bias is None and sinks is None:
@@ -398,13 +398,7 @@ def main():
                                 dv[:, :, sl], None, ab.ATTN_ACCUMULATE_DQ, stream)
             for _ in range(2):
                 chunked()
-            torch.cuda.synchronize()
-            e0.record(stream)
-            for _ in range(5):
-                chunked()
-            e1.record(stream)
-            torch.cuda.synchronize()
-            ch_ms = e0.elapsed_time(e1) / 5
+            ch_ms = region(chunked, 5)
             out["chunked_kv4"] = {"ms_per_step": round(ch_ms, 4), "tflops": round(flops / (ch_ms * 1e-3) / 1e12, 2)}
         if w.name == HEADLINE:
             out["varlen"] = bench_varlen(stream)
