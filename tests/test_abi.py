@@ -231,3 +231,24 @@ def test_workspace_size_query():
     x = ctypes.c_int64(7)
     assert L.attn_bwd_workspace_size(ctypes.byref(bad), 0, ctypes.byref(x)) == B.ATTN_EINVAL and x.value == 0
     assert L.attn_bwd_workspace_size(ctypes.byref(small), 64, ctypes.byref(x)) == B.ATTN_EINVAL
+
+
+def test_workspace_size_other_paths():
+    """The window + sink workload splits only its sink key block (parts
+    summed through slots of that block alone); a packed batch and a bias
+    problem keep atomic parts (0); the shared-KV head-dim-512 path sizes
+    one dKV-shaped slot per query-head part beyond the first."""
+    from attention_backward_attn_amd.inputs import WORKLOADS
+    w = WORKLOADS["gqa8_swa1024_sink4_s8192"]
+    p = sized_problem(w.B, w.Hq, w.Hk, w.Sq, w.Sk, w.Dqk, w.mask, window_left=w.window_left,
+                      window_right=w.window_right, num_sink_tokens=w.num_sink)
+    n = B.attn_bwd_workspace_size(p, 0)
+    slot = 128 * (w.Dqk + w.Dv) * 4
+    assert n > 0 and n % (w.B * w.Hk * slot) == 0
+    # only the sink block's parts beyond the first (never more than 15 slots per head)
+    assert n // (w.B * w.Hk * slot) <= 15
+    # shared KV at head dim 512: (parts - 1) copies of the [Sk, Hk, 512] fp32 tensor
+    kv = sized_problem(1, 64, 1, 4096, 4096, 512, "bottom_right", window_left=511)
+    m = B.attn_bwd_workspace_size(kv, B.ATTN_SHARED_KV)
+    one = 4096 * 512 * 4
+    assert m > 0 and m % one == 0 and m // one in (1, 3, 7, 15)
