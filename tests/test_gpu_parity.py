@@ -113,6 +113,7 @@ SMALL = [
     (1, 4, 2, 96, 112, 128, 64, "bf16", MaskSpec("top_left"), False, True),      # Dqk != Dv
     (3, 4, 4, 640, 640, 64, 64, "bf16", MaskSpec("none"), True, False),           # batch-ordered dbias
     (1, 32, 8, 1100, 1100, 128, 128, "bf16", MaskSpec("bottom_right"), False, False),
+    (1, 16, 1, 512, 512, 64, 64, "bf16", MaskSpec("top_left"), False, False),     # D = 64, 16-way split
 ]
 
 
