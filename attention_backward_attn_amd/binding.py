@@ -176,6 +176,8 @@ def make_problem(q, k, v, *, o=None, do=None, dq=None, dk=None, dv=None, bias=No
     if dv is not None:
         p.dv_str[:] = st(dv)
     if bias is not None:
+        if tuple(bias.shape) != (Hq, Sq, Sk):
+            raise ValueError(f"bias must be [Hq, Sq, Sk] = {(Hq, Sq, Sk)}, got {tuple(bias.shape)}")
         if bias.stride(-1) != 1:
             raise ValueError("bias: the key dimension must be contiguous")
         p.bias_str[:] = (bias.stride(0), bias.stride(1))
@@ -222,6 +224,17 @@ def set_workspace(p: attn_problem_t, flags: int = 0, device=None):
     ws = torch.empty(n, dtype=torch.uint8, device=device or "cuda")
     p.workspace, p.workspace_bytes = ws.data_ptr(), n
     return ws
+
+
+def _torch_stream(stream, device):
+    """The torch stream object of a stream argument (None: the current one;
+    a raw handle is wrapped)."""
+    import torch
+    if stream is None:
+        return torch.cuda.current_stream(device)
+    if isinstance(stream, torch.cuda.Stream):
+        return stream
+    return torch.cuda.ExternalStream(int(stream), device=device)
 
 
 def attn_lse_merge(o_acc, lse_acc, o_part, lse_part, stream=None):
@@ -271,12 +284,20 @@ def backward(q, k, v, o, do, lse, *, bias=None, sinks=None, want_dbias=False, fl
     dv = None if flags & ATTN_SHARED_KV else torch.empty(v.shape, device=dev, dtype=torch.float32)
     delta = torch.empty(B, Hq, Sq, device=dev, dtype=torch.float32)
     dsinks = torch.empty(Hq, device=dev, dtype=torch.float32) if sinks is not None else None
-    dbias = torch.empty(bias.shape, device=dev, dtype=torch.float32) if (want_dbias and bias is not None) else None
+    dbias = None
+    if want_dbias and bias is not None:
+        # dbias is written through the bias strides: give a strided or
+        # broadcast bias a dense copy, so that dbias has the same layout
+        if not bias.is_contiguous():
+            bias = bias.contiguous()
+        dbias = torch.empty(bias.shape, device=dev, dtype=torch.float32)
     p = make_problem(q, k, v, o=o, do=do, dq=dq, dk=dk, dv=dv, bias=bias, **mask_kw)
-    # workspace for split key blocks' partial sums: released after the call is
-    # enqueued (torch's caching allocator reuses it only in the order of the
-    # current stream, which is the call's stream unless one is given)
+    # workspace for split key blocks' partial sums, marked as in use on the
+    # call's stream: torch's caching allocator then hands the block to no
+    # other allocation before that stream has finished the call
     ws = set_workspace(p, flags, dev)
+    if ws is not None:
+        ws.record_stream(_torch_stream(stream, dev))
     attn_bwd_preprocess(p, o, do, lse, sinks, delta, dsinks, None, None, None, stream)
     attn_bwd(p, q, k, v, do, lse, delta, bias, dq, dk, dv, dbias, flags, stream)
     del ws

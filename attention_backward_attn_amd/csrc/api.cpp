@@ -49,6 +49,16 @@ attn_status_t check_problem(const attn_problem_t* p) {
 
 bool packed(const attn_problem_t* p) { return p->cu_seqlens_q != nullptr; }
 
+// dbias is written through the bias strides: its rows (and heads) must not
+// overlap, or two query rows (heads) would write one element -- a broadcast
+// (stride 0) bias is fine to read but has no room for its gradient.
+bool dbias_strides_ok(const attn_problem_t* p) {
+  const int64_t row_span = (p->Sq > 0 ? (int64_t)(p->Sq - 1) * p->bias_str[1] : 0) + p->Sk;
+  if (p->Sq > 1 && p->bias_str[1] < p->Sk) return false;
+  if (p->Hq > 1 && p->bias_str[0] < row_span) return false;
+  return true;
+}
+
 bool aligned16(const void* x) { return ((uintptr_t)x & 15u) == 0; }
 
 Params make_params(const attn_problem_t* p) {
@@ -237,6 +247,7 @@ attn_status_t attn_bwd(const attn_problem_t* p, const void* q, const void* k, co
     return ATTN_EINVAL;
   if (dbias && !bias) return ATTN_EINVAL;
   if (bias && (p->bias_str[0] < 0 || p->bias_str[1] < 0)) return ATTN_EINVAL;
+  if (dbias && !dbias_strides_ok(p)) return ATTN_EINVAL;
   const bool no_rows = p->B == 0 || p->Sq == 0;
   const bool no_keys = p->B == 0 || p->Sk == 0;
   if (!no_rows && (!q || !dout || !lse || !delta || !dq)) return ATTN_EINVAL;

@@ -63,3 +63,19 @@ def backward_flops(w, pairs_per_head: Optional[int] = None) -> float:
     if pairs_per_head is None:
         pairs_per_head = allowed_pairs(w.Sq, w.Sk, w.mask, w.window_left, w.window_right, w.num_sink)
     return float(2 * (3 * w.Dqk + 2 * w.Dv)) * pairs_per_head * w.B * w.Hq
+
+
+def backward_bytes(w) -> int:
+    """Algorithmic HBM bytes of one attn_bwd call (the main pass, without the
+    preprocess): every input read once and every output written once --
+    Q, dO (B Hq Sq D) and K, V (B Hk Sk D) in the input dtype, LSE and delta
+    (4 bytes per query row), the fp32 bias [Hq, Sq, Sk] when there is one;
+    dQ, dK, dV in fp32 and dbias [Hq, Sq, Sk] in fp32 when there is a bias."""
+    e = 2 if w.dtype == "bf16" else 4
+    rows = w.B * w.Hq * w.Sq
+    reads = e * (rows * (w.Dqk + w.Dv) + w.B * w.Hk * w.Sk * (w.Dqk + w.Dv)) + 8 * rows
+    writes = 4 * (rows * w.Dqk + w.B * w.Hk * w.Sk * (w.Dqk + w.Dv))
+    if w.bias:
+        reads += 4 * w.Hq * w.Sq * w.Sk
+        writes += 4 * w.Hq * w.Sq * w.Sk
+    return int(reads + writes)

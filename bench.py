@@ -88,6 +88,30 @@ def traffic_record(kernel_key: str):
     return None
 
 
+def roofline(w, flops: float, main_ms: float, main_med: float, traffic) -> dict:
+    """Roofline of the attn_bwd call.  The ALiBi + dbias workload (fp32 bias
+    and dbias of [Hq, Sq, Sk] dominate its bytes) is bound by HBM: achieved =
+    algorithmic bytes / time against 8 TB/s.  The fp32 workload runs on the
+    vector ALU (fp32 FMA peak).  The others are bound by the bf16 matrix
+    cores: achieved = counted FLOPs / time."""
+    from attention_backward_attn_amd.mask import backward_bytes
+    out = {"kernel": "attn_bwd (k_dkdv2/k_dkdv + k_dq2/k_dq)" if w.dtype == "bf16" else
+           "attn_bwd (k_dkdv_simt + k_dq_simt)", "kernel_ms_mean": round(main_ms, 4),
+           "kernel_ms_median": round(main_med, 4), "algorithmic_bytes": backward_bytes(w)}
+    if w.bias:
+        gbs = backward_bytes(w) / (main_ms * 1e-3) / 1e9
+        out.update({"bound": "hbm", "achieved": round(gbs, 1), "peak": HBM_GBS, "unit": "GB/s",
+                    "frac": round(gbs / HBM_GBS, 4), "traffic": traffic})
+        out["mfma_tflops"] = round(flops / (main_ms * 1e-3) / 1e12, 2)
+    else:
+        peak = PEAK_BF16_TFLOPS if w.dtype == "bf16" else PEAK_F32_TFLOPS
+        achieved = flops / (main_ms * 1e-3) / 1e12
+        out.update({"bound": "mfma" if w.dtype == "bf16" else "alu", "achieved": round(achieved, 2),
+                    "peak": peak, "unit": "TFLOP/s", "frac": round(achieved / peak, 4), "traffic": traffic})
+    return {k: out[k] for k in ("bound", "achieved", "peak", "unit", "frac", "traffic")} | \
+        {k: v for k, v in out.items() if k not in ("bound", "achieved", "peak", "unit", "frac", "traffic")}
+
+
 def bench_varlen(stream, name: str = "varlen16_gqa4_causal_br", steps: int = 10):
     """Backward of a packed variable-length batch (TND with cumulative
     sequence lengths): preprocess + attn_bwd per step, counted FLOPs summed
@@ -337,7 +361,6 @@ def main():
     wall_ms, span_ms, pre_ms, main_ms, main_med = timed(0, args.steps, args.warmup)
     ms_per_step = span_ms
     value = flops / (ms_per_step * 1e-3) / 1e12
-    achieved = flops / (main_ms * 1e-3) / 1e12
     kernel_key = f"bwd_main:{w.name}"
     out = {
         "metric": ("attention-backward TFLOP/s + % bf16 MFMA peak (GQA 32:8, S=4096, D=128, causal)"
@@ -361,10 +384,7 @@ def main():
         "wall_ms_per_step": round(wall_ms, 4),
         "preprocess_ms": round(pre_ms, 4),
         "clock_settle": {"ms": args.settle_ms, "steps": n_settle},
-        "roofline": {"bound": "mfma", "achieved": round(achieved, 2), "peak": PEAK_BF16_TFLOPS,
-                     "unit": "TFLOP/s", "frac": round(achieved / PEAK_BF16_TFLOPS, 4),
-                     "traffic": traffic_record(kernel_key), "kernel": "attn_bwd (k_dkdv2/k_dkdv + k_dq2/k_dq)",
-                     "kernel_ms_mean": round(main_ms, 4), "kernel_ms_median": round(main_med, 4)},
+        "roofline": roofline(w, flops, main_ms, main_med, traffic_record(kernel_key)),
     }
     if not args.no_extras:
         # (its own clock settle and as many steps as the headline line)

@@ -197,7 +197,12 @@ attn_status_t attn_bwd_preprocess(const attn_problem_t* p, const void* o, const 
  *   each KV head's query group), dbias = sum over batch of dS.
  * dq is overwritten (or added into with ATTN_ACCUMULATE_DQ); dk, dv and
  * dbias are overwritten.  bias is nullable; dbias is nullable and requires
- * bias.  delta must come from attn_bwd_preprocess on the same O / dO.
+ * bias.  dbias is written through bias_str, so with dbias the strides must
+ * keep rows and heads apart (bias_str[1] >= Sk when Sq > 1, and
+ * bias_str[0] >= (Sq - 1) * bias_str[1] + Sk when Hq > 1; a broadcast bias
+ * with zero strides is readable but has no room for its gradient):
+ * ATTN_EINVAL otherwise.  delta must come from attn_bwd_preprocess on the
+ * same O / dO.
  * The library allocates nothing: scratch for the partial sums of split key
  * blocks comes from p->workspace when the caller provides one (see
  * attn_problem_t).  The call records no memset, so it can be captured

@@ -252,3 +252,40 @@ def test_workspace_size_other_paths():
     m = B.attn_bwd_workspace_size(kv, B.ATTN_SHARED_KV)
     one = 4096 * 512 * 4
     assert m > 0 and m % one == 0 and m // one in (1, 3, 7, 15)
+
+
+def test_bwd_rejects_overlapping_dbias_strides():
+    """dbias is written through the bias strides: rows or heads that overlap
+    (a broadcast bias with stride 0, or a row stride below Sk) are rejected
+    when dbias is asked for, and accepted for reading a bias alone."""
+    L = B.lib()
+
+    def call(bias_str, dbias):
+        p = problem()
+        p.bias_str[:] = bias_str
+        # Sk = 0 and B = 0: no kernel would run even if validation passed
+        return L.attn_bwd(ctypes.byref(p), FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE,
+                          FAKE if dbias else None, 0, None)
+
+    for bad in ((0, 0), (64 * 64, 0), (0, 64), (64 * 63, 64), (64 * 64, 63)):
+        assert call(bad, True) == B.ATTN_EINVAL, bad
+    # a padded layout keeps rows and heads apart
+    for good in ((64 * 64, 64), (65 * 72, 72)):
+        p = problem(B=0)
+        p.bias_str[:] = good
+        assert L.attn_bwd(ctypes.byref(p), FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, 0,
+                          None) == B.ATTN_OK, good
+    # reading a broadcast bias without its gradient is fine
+    p = problem(B=0)
+    p.bias_str[:] = (0, 0)
+    assert L.attn_bwd(ctypes.byref(p), FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, None, 0,
+                      None) == B.ATTN_OK
+
+
+def test_binding_checks_bias_shape():
+    torch = pytest.importorskip("torch")
+    q = torch.empty(1, 4, 64, 64, dtype=torch.bfloat16)
+    k = torch.empty(1, 2, 64, 64, dtype=torch.bfloat16)
+    with pytest.raises(ValueError):
+        B.make_problem(q, k, k, bias=torch.empty(4, 64, 32))
+    B.make_problem(q, k, k, bias=torch.empty(4, 64, 64))

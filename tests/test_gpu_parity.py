@@ -3,9 +3,14 @@ on the same seeded inputs.
 
 Tolerance (per output tensor): max|gpu - ref| <= tol * max|ref|, with
 tol = 1e-4 for fp32 inputs and 2e-2 for bf16 inputs (fp32 accumulation).
-The backward on both sides consumes the same fp32 O and LSE, produced by the
-oracle forward, so parity measures the backward kernels alone; the GPU
-forward is checked separately.
+There is no absolute term except for references that are zero in exact
+arithmetic (see parity_util).  The backward on both sides consumes the same
+fp32 O and LSE, produced by the oracle forward, so parity measures the
+backward kernels alone; the GPU forward is checked separately.  The three
+large workloads (headline, ALiBi + dbias, window + sink) and the 4-chunk
+headline are compared element by element on every output, with oracle
+references computed over (batch entry, KV head) units in a forked worker
+pool (oracle_pool).
 """
 import sys
 
@@ -15,17 +20,13 @@ import pytest
 import oracle
 from oracle import MaskSpec
 from attention_backward_attn_amd.inputs import WORKLOADS, make_inputs, round_bf16
+from parity_util import TOL, check
 
 torch = pytest.importorskip("torch")
 pytestmark = pytest.mark.gpu
 
 from attention_backward_attn_amd import binding as ab  # noqa: E402
 
-TOL = {"f32": 1e-4, "bf16": 2e-2}
-# Absolute floor for outputs whose reference is (nearly) all zeros -- e.g.
-# dQ when every row has a single key, where fp32 rounding of delta leaves
-# ~1e-7 * |dO| |V| behind.
-ATOL = 1e-5
 
 
 def say(msg):
@@ -46,17 +47,6 @@ def dev(x, dtype):
 
 def tdtype(name):
     return torch.bfloat16 if name == "bf16" else torch.float32
-
-
-def check(name, got, ref, tol):
-    got = got.detach().float().cpu().numpy().astype(np.float64) if torch.is_tensor(got) else np.asarray(got)
-    ref = np.asarray(ref, dtype=np.float64)
-    assert got.shape == ref.shape, (name, got.shape, ref.shape)
-    assert np.isfinite(got).all(), f"{name}: non-finite values"
-    scale = np.abs(ref).max()
-    err = np.abs(got - ref).max()
-    assert err <= tol * scale + ATOL, f"{name}: max err {err:.3e} > {tol:g} * {scale:.3e} + {ATOL:g}"
-    return err / max(scale, 1e-30)
 
 
 def mask_kw(spec: MaskSpec):
@@ -137,85 +127,77 @@ def test_workload_full_parity(name):
     say(f"  rel errs {errs}")
 
 
-def sampled_workload(name, groups, rows_per_head=48, n_keys=48, flags=0):
-    """Full-size run of a workload; compare sampled outputs with the oracle.
-
-    The oracle forward runs for the query heads of the sampled KV groups
-    (every batch entry for bias workloads, whose dbias sums the batch); the
-    other heads take O/LSE from the GPU forward and are only checked for
-    finite values."""
-    w = WORKLOADS[name]
-    x = make_inputs(w)
+def gpu_backward_full(w, x, ref, flags=0):
+    """GPU preprocess + attn_bwd of workload ``w`` on the oracle's fp32 O / LSE."""
     spec = MaskSpec(w.mask, w.window_left, w.window_right, w.num_sink)
     dt = tdtype(w.dtype)
     q, k, v, do = (dev(x[n], dt) for n in ("q", "k", "v", "do"))
     bias, sinks = dev(x["bias"], torch.float32), dev(x["sinks"], torch.float32)
-    say(f"[workload sampled] {name}: GPU forward")
-    o, lse = ab.forward(q, k, v, bias=bias, sinks=sinks, scale=w.scale, **mask_kw(spec))
-    torch.cuda.synchronize()
-    o_np = o.cpu().numpy()
-    lse_np = lse.cpu().numpy()
-    G = w.G
-    bs = range(w.B) if (w.bias or w.sinks) else [0]
-    for g in groups:
-        heads = list(range(g * G, (g + 1) * G))
-        for b in bs:
-            sl = (slice(b, b + 1), slice(heads[0], heads[-1] + 1))
-            bias_h = None if x["bias"] is None else x["bias"][heads[0]:heads[-1] + 1]
-            sinks_h = None if x["sinks"] is None else x["sinks"][heads[0]:heads[-1] + 1]
-            o64, l64 = oracle.forward(x["q"][sl], x["k"][b:b + 1, g:g + 1], x["v"][b:b + 1, g:g + 1],
-                                      w.scale, spec, bias_h, sinks_h, row_block=1024)
-            o_np[sl] = o64.astype(np.float32)
-            lse_np[sl] = l64.astype(np.float32)
-    o = dev(o_np, torch.float32)
-    lse = dev(lse_np, torch.float32)
-    say(f"[workload sampled] {name}: GPU backward flags={flags}")
+    o, lse = dev(ref["o"], torch.float32), dev(ref["lse"], torch.float32)
+    say(f"[full] {w.name}: GPU backward flags={flags}")
     got = ab.backward(q, k, v, o, do, lse, bias=bias, sinks=sinks, want_dbias=bias is not None,
                       flags=flags, scale=w.scale, **mask_kw(spec))
     torch.cuda.synchronize()
-    for key in ("dq", "dk", "dv"):
-        assert torch.isfinite(got[key]).all(), key
-    rng = np.random.default_rng(77)
+    return got, (q, k, v, do, bias, sinks, o, lse)
+
+
+def compare_full(w, got, ref):
     tol = TOL[w.dtype]
     errs = {}
-    for g in groups:
-        heads = list(range(g * G, (g + 1) * G))
-        b = 0
-        edge = [0, 1, 2, 3, 4, w.Sk // 4 - 1, w.Sk // 4, w.Sk // 2, w.Sk - 1]
-        keys = np.unique(np.concatenate([edge, rng.choice(w.Sk, n_keys, replace=False)]))
-        dk_ref, dv_ref = oracle.dkdv_keys(x["q"], x["k"], x["v"], o_np, x["do"], lse_np, w.scale, spec,
-                                          b, g, keys, x["bias"])
-        errs[f"dk[g{g}]"] = check("dk", got["dk"][b, g, keys], dk_ref, tol)
-        errs[f"dv[g{g}]"] = check("dv", got["dv"][b, g, keys], dv_ref, tol)
-        for h in heads[:2] + heads[-1:]:
-            rows = np.unique(np.concatenate([[0, 1, w.Sq - 1], rng.choice(w.Sq, rows_per_head, replace=False)]))
-            ref = oracle.dq_rows(x["q"], x["k"], x["v"], o_np, x["do"], lse_np, w.scale, spec, b, h, rows,
-                                 x["bias"])
-            errs[f"dq[h{h}]"] = check("dq", got["dq"][b, h, rows], ref, tol)
-            if w.bias:
-                rows_b = rows[:12]
-                ref_b = sum(oracle.ds_rows(x["q"], x["k"], x["v"], o_np, x["do"], lse_np, w.scale, spec, bb,
-                                           h, rows_b, x["bias"]) for bb in range(w.B))
-                errs[f"dbias[h{h}]"] = check("dbias", got["dbias"][h, rows_b], ref_b, tol)
-        if w.sinks:
-            ref_d, ref_s = oracle.preprocess(o_np[:, heads], x["do"][:, heads], lse_np[:, heads],
-                                             x["sinks"][heads])
-            errs[f"dsinks[g{g}]"] = check("dsinks", got["dsinks"][heads], ref_s, tol)
-            check("delta", got["delta"][:, heads], ref_d, 1e-5)
+    for n in ("dq", "dk", "dv", "dbias", "dsinks"):
+        if ref[n] is not None:
+            errs[n] = check(n, got[n], ref[n], tol)
+    check("delta", got["delta"], ref["delta"], 1e-5)
     say(f"  rel errs {errs}")
-    return got, x, o_np, lse_np
+    return errs
 
 
-def test_headline_sampled():
-    sampled_workload("gqa4_causal_br_s4096", groups=[0, 7])
+def full_workload(name):
+    """Full-size run of a workload, every element of every output compared
+    with the oracle: the GPU forward (O, LSE) against the oracle forward,
+    and the GPU backward on the oracle's fp32 O / LSE against the oracle
+    backward (dQ, dK, dV, dbias over all [Hq, Sq, Sk], dsinks over all Hq,
+    delta)."""
+    import oracle_pool
+    w = WORKLOADS[name]
+    x = make_inputs(w)
+    spec = MaskSpec(w.mask, w.window_left, w.window_right, w.num_sink)
+    say(f"[full] {name}: oracle references")
+    ref = oracle_pool.reference(name, w, x, spec, say)
+    got, t = gpu_backward_full(w, x, ref)
+    compare_full(w, got, ref)
+    del got
+    q, k, v, do, bias, sinks, _, _ = t
+    say(f"[full] {name}: GPU forward")
+    o_g, lse_g = ab.forward(q, k, v, bias=bias, sinks=sinks, scale=w.scale, **mask_kw(spec))
+    torch.cuda.synchronize()
+    lse_g = lse_g.cpu().numpy()
+    assert not np.isneginf(ref["lse"]).any() and np.isfinite(lse_g).all()
+    check("lse", lse_g, ref["lse"], 1e-5)
+    check("o", o_g, ref["o64"], TOL[w.dtype])
+    return w, x, ref
 
 
-def test_alibi_dbias_sampled():
-    sampled_workload("mha_alibi_dbias_s2048", groups=[0, 15], rows_per_head=16, n_keys=24)
+@pytest.mark.full_oracle
+@pytest.mark.timeout(900)
+def test_headline_full():
+    full_workload("gqa4_causal_br_s4096")
 
 
-def test_window_sink_sampled():
-    sampled_workload("gqa8_swa1024_sink4_s8192", groups=[0], rows_per_head=32, n_keys=32)
+@pytest.mark.full_oracle
+@pytest.mark.timeout(900)
+def test_alibi_dbias_full():
+    import oracle_pool
+    full_workload("mha_alibi_dbias_s2048")
+    oracle_pool.drop("mha_alibi_dbias_s2048")
+
+
+@pytest.mark.full_oracle
+@pytest.mark.timeout(1200)
+def test_window_sink_full():
+    import oracle_pool
+    full_workload("gqa8_swa1024_sink4_s8192")
+    oracle_pool.drop("gqa8_swa1024_sink4_s8192")
 
 
 def test_dsinks_full_batch():
@@ -294,55 +276,56 @@ def test_lse_merge_parity():
     np.testing.assert_allclose(lg[fin], l_ref[fin], atol=1e-6)
 
 
+@pytest.mark.full_oracle
+@pytest.mark.timeout(900)
 def test_headline_chunked():
-    """The headline workload run as 4 K/V chunks of 1024: forward partials
-    joined by attn_lse_merge, then the backward of each chunk against the
-    global O / LSE / delta with dQ accumulated ("Ring attention for PyTorch",
-    _ring_fwd / _ring_bwd on one GPU).  Compared with the unchunked GPU run
-    and, on sampled outputs, with the oracle."""
+    """The headline workload run as 4 K/V chunks of 1024 ("Ring attention for
+    PyTorch", _ring_fwd / _ring_bwd on one GPU): forward partials joined by
+    attn_lse_merge, compared with the oracle forward in full; then the
+    backward of each chunk against the global O / LSE / delta (the oracle's
+    fp32 O / LSE) with dQ accumulated over the chunks and each chunk's dK /
+    dV written into its slice, compared in full with the oracle backward."""
+    import oracle_pool
     w = WORKLOADS["gqa4_causal_br_s4096"]
     x = make_inputs(w)
     spec = MaskSpec(w.mask)
+    ref = oracle_pool.reference(w.name, w, x, spec, say)
     dt = torch.bfloat16
     q, k, v, do = (dev(x[n], dt) for n in ("q", "k", "v", "do"))
     say("[chunked] forward")
-    o_full, lse_full = ab.forward(q, k, v, scale=w.scale, mask=w.mask)
     n, c = w.kv_chunks, w.Sk // w.kv_chunks
-    o = torch.zeros_like(o_full)
-    lse = torch.full_like(lse_full, -np.inf)
+    o = torch.zeros(w.B, w.Hq, w.Sq, w.Dv, device="cuda")
+    lse = torch.full((w.B, w.Hq, w.Sq), -np.inf, device="cuda")
     for i in range(n):
         kc, vc = k[:, :, i * c:(i + 1) * c], v[:, :, i * c:(i + 1) * c]
         o2, l2 = ab.forward(q, kc, vc, scale=w.scale, mask=w.mask, k_offset=i * c, sk_total=w.Sk)
         ab.attn_lse_merge(o, lse, o2, l2)
     torch.cuda.synchronize()
     assert (lse == -np.inf).sum() == 0
-    # each chunk rounds its own P to bf16 as a matrix-core operand
-    check("o merged vs unchunked", o, o_full.cpu().numpy(), TOL["bf16"])
-    # oracle forward on one group
-    o64, l64 = oracle.forward(x["q"][:, :4], x["k"][:, :1], x["v"][:, :1], w.scale, spec, row_block=1024)
-    check("o merged vs oracle", o[:, :4], o64, TOL["bf16"])
+    check("o merged", o, ref["o64"], TOL["bf16"])
+    check("lse merged", lse, ref["lse"], 1e-5)
     say("[chunked] backward")
-    full = ab.backward(q, k, v, o, do, lse, scale=w.scale, mask=w.mask)
-    dq = torch.zeros_like(full["dq"])
-    delta = torch.empty_like(full["delta"])
-    dk = torch.empty_like(full["dk"])
-    dv = torch.empty_like(full["dv"])
+    o, lse = dev(ref["o"], torch.float32), dev(ref["lse"], torch.float32)
+    dq = torch.full((w.B, w.Hq, w.Sq, w.Dqk), float("nan"), device="cuda")
+    dk = torch.full((w.B, w.Hk, w.Sk, w.Dqk), float("nan"), device="cuda")
+    dv = torch.full((w.B, w.Hk, w.Sk, w.Dv), float("nan"), device="cuda")
+    delta = torch.empty(w.B, w.Hq, w.Sq, device="cuda")
     p = ab.make_problem(q, k, v, o=o, do=do, dq=dq, dk=dk, dv=dv, scale=w.scale, mask=w.mask)
-    ab.attn_bwd_preprocess(p, o, do, lse, None, delta, None, None, None, None)
+    # delta, and dQ zeroed for the chunks to accumulate into
+    ab.attn_bwd_preprocess(p, o, do, lse, None, delta, None, dq, None, None)
+    keep = []
     for i in range(n):
         sl = slice(i * c, (i + 1) * c)
         pc = ab.make_problem(q, k[:, :, sl], v[:, :, sl], o=o, do=do, dq=dq, dk=dk[:, :, sl], dv=dv[:, :, sl],
                              scale=w.scale, mask=w.mask, k_offset=i * c, sk_total=w.Sk)
+        keep.append(ab.set_workspace(pc, ab.ATTN_ACCUMULATE_DQ))
         ab.attn_bwd(pc, q, k[:, :, sl], v[:, :, sl], do, lse, delta, None, dq, dk[:, :, sl], dv[:, :, sl],
                     None, ab.ATTN_ACCUMULATE_DQ)
     torch.cuda.synchronize()
-    for name, a, b in (("dq", dq, full["dq"]), ("dk", dk, full["dk"]), ("dv", dv, full["dv"])):
-        check(f"chunked {name} vs unchunked", a, b.cpu().numpy(), 1e-3)
-    # sampled oracle check on group 0 with the oracle's own O / LSE
-    rows = np.array([0, 1, 1023, 1024, 2047, 3000, 4095])
-    o_np, lse_np = o.cpu().numpy(), lse.cpu().numpy()
-    ref = oracle.dq_rows(x["q"], x["k"], x["v"], o_np, x["do"], lse_np, w.scale, spec, 0, 1, rows)
-    check("chunked dq vs oracle", dq[0, 1, rows], ref, 2e-2)
+    del keep
+    for name, t in (("dq", dq), ("dk", dk), ("dv", dv)):
+        check(f"chunked {name}", t, ref[name], TOL["bf16"])
+    check("delta", delta, ref["delta"], 1e-5)
 
 
 def test_deterministic_is_bitwise_repeatable():

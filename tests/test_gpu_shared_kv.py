@@ -20,10 +20,11 @@ from attention_backward_attn_amd.inputs import SHARED_KV_WORKLOADS, make_shared_
 torch = pytest.importorskip("torch")
 pytestmark = pytest.mark.gpu
 
+from parity_util import check as _check  # noqa: E402
+
 from attention_backward_attn_amd import binding as ab  # noqa: E402
 
 TOL = 2e-2
-ATOL = 1e-5
 D = 512
 
 
@@ -44,14 +45,7 @@ def dev(x, dtype):
 
 
 def check(name, got, ref, tol=TOL):
-    got = got.detach().float().cpu().numpy().astype(np.float64) if torch.is_tensor(got) else np.asarray(got)
-    ref = np.asarray(ref, dtype=np.float64)
-    assert got.shape == ref.shape, (name, got.shape, ref.shape)
-    assert np.isfinite(got).all(), f"{name}: non-finite values"
-    scale = np.abs(ref).max()
-    err = np.abs(got - ref).max()
-    assert err <= tol * scale + ATOL, f"{name}: max err {err:.3e} > {tol:g} * {scale:.3e} + {ATOL:g}"
-    return err / max(scale, 1e-30)
+    return _check(name, got, ref, tol)
 
 
 def mask_kw(spec: MaskSpec):

@@ -16,10 +16,11 @@ from attention_backward_attn_amd.inputs import round_bf16
 
 pytestmark = pytest.mark.gpu
 
+from parity_util import check as _check  # noqa: E402
+
 from attention_backward_attn_amd import binding as ab  # noqa: E402
 
 TOL = 2e-2      # bf16 matrix-core operands, fp32 accumulation
-ATOL = 1e-5
 
 
 def say(msg):
@@ -35,13 +36,7 @@ def _gpu():
 
 
 def check(name, got, ref, tol):
-    got = got.detach().float().cpu().numpy().astype(np.float64) if torch.is_tensor(got) else np.asarray(got)
-    ref = np.asarray(ref, dtype=np.float64)
-    assert got.shape == ref.shape, (name, got.shape, ref.shape)
-    assert np.isfinite(got).all(), f"{name}: non-finite values"
-    err = np.abs(got - ref).max() if ref.size else 0.0
-    scale = np.abs(ref).max() if ref.size else 0.0
-    assert err <= tol * scale + ATOL, f"{name}: max err {err:.3e} > {tol:g} * {scale:.3e} + {ATOL:g}"
+    return _check(name, got, ref, tol)
 
 
 CASES = [
