@@ -16,12 +16,13 @@ from typing import Optional
 HERE = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(HERE, "libattnbwd.so")
 
-ATTN_OK, ATTN_EINVAL, ATTN_EUNSUPPORTED, ATTN_EHIP = 0, -1, -2, -3
+ATTN_OK, ATTN_EINVAL, ATTN_EUNSUPPORTED, ATTN_EHIP, ATTN_ENOSCRATCH = 0, -1, -2, -3, -4
+ATTN_STATIC_SCRATCH_BYTES = 64 * 1024 * 1024
 ATTN_F32, ATTN_BF16 = 0, 1
 MASKS = {"none": 0, "top_left": 1, "bottom_right": 2}
 ATTN_DETERMINISTIC, ATTN_ACCUMULATE_DQ, ATTN_ACCUMULATE_DKDV, ATTN_SHARED_KV = 1, 2, 4, 8
 
-EXPORTED = ("attn_problem_init", "attn_fwd_lse", "attn_bwd_preprocess", "attn_bwd",
+EXPORTED = ("attn_problem_init", "attn_fwd_lse", "attn_bwd_preprocess", "attn_bwd", "attn_bwd_static",
             "attn_bwd_workspace_size", "attn_lse_merge", "attn_status_string")
 
 
@@ -73,6 +74,8 @@ def lib() -> ctypes.CDLL:
         L.attn_bwd_preprocess.restype = i32
         L.attn_bwd.argtypes = [P, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, ctypes.c_uint32, vp]
         L.attn_bwd.restype = i32
+        L.attn_bwd_static.argtypes = [P, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, ctypes.c_uint32, vp]
+        L.attn_bwd_static.restype = i32
         L.attn_bwd_workspace_size.argtypes = [P, ctypes.c_uint32, ctypes.POINTER(i64)]
         L.attn_bwd_workspace_size.restype = i32
         L.attn_lse_merge.argtypes = [i32, i32, i32, i32, vp, vp, vp, vp, vp]
@@ -202,6 +205,15 @@ def attn_bwd(p: attn_problem_t, q, k, v, do, lse, delta, bias, dq, dk, dv, dbias
     _check("attn_bwd", lib().attn_bwd(ctypes.byref(p), _ptr(q), _ptr(k), _ptr(v), _ptr(do), _ptr(lse),
                                       _ptr(delta), _ptr(bias), _ptr(dq), _ptr(dk), _ptr(dv), _ptr(dbias),
                                       flags, _stream(stream)))
+
+
+def attn_bwd_static(p: attn_problem_t, q, k, v, do, lse, delta, bias, dq, dk, dv, dbias, flags: int = 0,
+                    stream=None):
+    """attn_bwd with the library's static device scratch in place of
+    p.workspace (allocates nothing)."""
+    _check("attn_bwd_static",
+           lib().attn_bwd_static(ctypes.byref(p), _ptr(q), _ptr(k), _ptr(v), _ptr(do), _ptr(lse), _ptr(delta),
+                                 _ptr(bias), _ptr(dq), _ptr(dk), _ptr(dv), _ptr(dbias), flags, _stream(stream)))
 
 
 def attn_bwd_workspace_size(p: attn_problem_t, flags: int = 0) -> int:

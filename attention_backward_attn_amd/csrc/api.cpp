@@ -7,12 +7,49 @@
 #include <math.h>
 #include <stdint.h>
 
+#include <mutex>
+
 #include "../../include/attn_bwd.h"
 #include "kernels.h"
 
 using attn::Params;
 
+// Device scratch of attn_bwd_static: the partial dK / dV sums of split key
+// blocks (or query-head parts) that attn_bwd keeps in a caller workspace.
+// Each GPU the library runs on holds its own copy until the process ends.
+// In host code `scratch` is only a stand-in for the symbol: its device
+// address on a GPU comes from hipGetSymbolAddress with that GPU current
+// (static_scratch below), and only that address is ever handed to a kernel.
+static __device__ __align__(256) unsigned char scratch[ATTN_STATIC_SCRATCH_BYTES];
+
 namespace {
+
+// Per-device address of `scratch`, looked up once per device.
+constexpr int kMaxDevices = 64;
+std::once_flag g_scratch_once[kMaxDevices];
+void* g_scratch_ptr[kMaxDevices];
+hipError_t g_scratch_err[kMaxDevices];
+
+// The scratch of the device that `stream` runs on (the current device for
+// the null stream), looked up with that device current.
+attn_status_t static_scratch(void* stream, void** out) {
+  int cur = -1, dev = -1;
+  if (hipGetDevice(&cur) != hipSuccess) return ATTN_EHIP;
+  dev = cur;
+  if (stream != nullptr && hipStreamGetDevice((hipStream_t)stream, &dev) != hipSuccess) return ATTN_EHIP;
+  if (dev < 0 || dev >= kMaxDevices) return ATTN_EUNSUPPORTED;
+  std::call_once(g_scratch_once[dev], [dev, cur]() {
+    void* ptr = nullptr;
+    hipError_t e = dev == cur ? hipSuccess : hipSetDevice(dev);
+    if (e == hipSuccess) e = hipGetSymbolAddress(&ptr, HIP_SYMBOL(scratch));
+    if (dev != cur && hipSetDevice(cur) != hipSuccess && e == hipSuccess) e = hipErrorInvalidDevice;
+    g_scratch_err[dev] = e;
+    g_scratch_ptr[dev] = e == hipSuccess ? ptr : nullptr;
+  });
+  if (g_scratch_err[dev] != hipSuccess || g_scratch_ptr[dev] == nullptr) return ATTN_EHIP;
+  *out = g_scratch_ptr[dev];
+  return ATTN_OK;
+}
 
 constexpr int kMaxHeadDim = 512;
 
@@ -107,7 +144,8 @@ bool same_kv(const attn_problem_t* p, const void* k, const void* v) {
 // bf16, no bias; dk receives the gradient of the shared tensor.
 attn_status_t bwd_shared_kv(const attn_problem_t* p, const void* q, const void* k, const void* v,
                             const void* dout, const float* lse, const float* delta, const float* bias,
-                            float* dq, float* dk, float* dv, float* dbias, uint32_t flags, void* stream) {
+                            float* dq, float* dk, float* dv, float* dbias, uint32_t flags, void* stream,
+                            bool launch) {
   if (!(flags & ATTN_SHARED_KV) || p->Dqk != attn::kSharedKvD || p->Dv != attn::kSharedKvD ||
       p->in_dtype != ATTN_BF16 || bias || dbias)
     return ATTN_EUNSUPPORTED;
@@ -124,12 +162,66 @@ attn_status_t bwd_shared_kv(const attn_problem_t* p, const void* q, const void* 
       (!no_keys && (!aligned16(k) || !aligned16(dk))))
     return ATTN_EUNSUPPORTED;
   if (no_rows && no_keys) return ATTN_OK;
+  if (!launch) return ATTN_OK;
   attn::BwdArgs a{q, k, k, dout, lse, delta, nullptr, dq, dk, nullptr, nullptr,
                   (flags & ATTN_ACCUMULATE_DQ) ? 1 : 0, (flags & ATTN_DETERMINISTIC) ? 1 : 0,
                   (flags & ATTN_ACCUMULATE_DKDV) ? 1 : 0, 0};
   a.workspace = p->workspace_bytes > 0 ? p->workspace : nullptr;
   a.workspace_bytes = p->workspace_bytes;
   return hip_status(attn::launch_bwd512(kp, a, (hipStream_t)stream));
+}
+
+// attn_bwd: validation, then (when `launch`) the kernels.  With launch false
+// the call only validates: no HIP call is made.
+attn_status_t bwd_impl(const attn_problem_t* p, const void* q, const void* k, const void* v,
+                       const void* dout, const float* lse, const float* delta, const float* bias,
+                       float* dq, float* dk, float* dv, float* dbias, uint32_t flags, void* stream,
+                       bool launch) {
+  attn_status_t st = check_problem(p);
+  if (st != ATTN_OK) return st;
+  if ((flags & ~(uint32_t)(ATTN_DETERMINISTIC | ATTN_ACCUMULATE_DQ | ATTN_ACCUMULATE_DKDV | ATTN_SHARED_KV)) != 0)
+    return ATTN_EINVAL;
+  if ((flags & ATTN_SHARED_KV) || p->Dqk == attn::kSharedKvD || p->Dv == attn::kSharedKvD)
+    return bwd_shared_kv(p, q, k, v, dout, lse, delta, bias, dq, dk, dv, dbias, flags, stream, launch);
+  if (!strides_ok(p->q_str) || !strides_ok(p->k_str) || !strides_ok(p->v_str) || !strides_ok(p->do_str) ||
+      !strides_ok(p->dq_str) || !strides_ok(p->dk_str) || !strides_ok(p->dv_str))
+    return ATTN_EINVAL;
+  if (dbias && !bias) return ATTN_EINVAL;
+  if (bias && (p->bias_str[0] < 0 || p->bias_str[1] < 0)) return ATTN_EINVAL;
+  if (dbias && !dbias_strides_ok(p)) return ATTN_EINVAL;
+  const bool no_rows = p->B == 0 || p->Sq == 0;
+  const bool no_keys = p->B == 0 || p->Sk == 0;
+  if (!no_rows && (!q || !dout || !lse || !delta || !dq)) return ATTN_EINVAL;
+  if (!no_keys && (!k || !v || !dk || !dv)) return ATTN_EINVAL;
+  if (p->in_dtype == ATTN_F32 && (p->Dqk > attn::kSimtMaxD || p->Dv > attn::kSimtMaxD))
+    return ATTN_EUNSUPPORTED;
+
+  Params kp = make_params(p);
+  attn::BwdArgs a{q, k, v, dout, lse, delta, bias, dq, dk, dv, dbias,
+                  (flags & ATTN_ACCUMULATE_DQ) ? 1 : 0, (flags & ATTN_DETERMINISTIC) ? 1 : 0,
+                  (flags & ATTN_ACCUMULATE_DKDV) ? 1 : 0};
+  a.workspace = p->workspace_bytes > 0 ? p->workspace : nullptr;
+  a.workspace_bytes = p->workspace_bytes;
+  hipStream_t s = (hipStream_t)stream;
+  if (p->in_dtype == ATTN_BF16) {
+    if (!attn::mfma_bwd_supported(kp)) {
+      if (p->Dqk > attn::kSimtMaxD || p->Dv > attn::kSimtMaxD) return ATTN_EUNSUPPORTED;
+    }
+  }
+  // a packed batch runs on the matrix-core kernels only
+  if (packed(p) && (bias || p->in_dtype != ATTN_BF16 || !attn::mfma_bwd_supported(kp) || !aligned16(q) ||
+                    !aligned16(k) || !aligned16(v) || !aligned16(dout)))
+    return ATTN_EUNSUPPORTED;
+  if (no_rows && no_keys) return ATTN_OK;
+  if (!launch) return ATTN_OK;
+  if (p->in_dtype == ATTN_BF16 && attn::mfma_bwd_supported(kp))
+    return hip_status(attn::launch_bwd_mfma(kp, a, s));
+  // fp32 inputs (and bf16 shapes the matrix-core kernels do not cover)
+  if (no_keys) {  // no keys: dK/dV are empty, dQ gets nothing added
+    if (!a.accumulate_dq) return hip_status(attn::launch_zero_rows(dq, p->B, p->Hq, p->Sq, p->Dqk, p->dq_str, s));
+    return ATTN_OK;
+  }
+  return hip_status(attn::launch_bwd_simt(kp, a, p->in_dtype == ATTN_BF16, s));
 }
 
 }  // namespace
@@ -167,6 +259,7 @@ const char* attn_status_string(attn_status_t s) {
     case ATTN_EINVAL: return "invalid argument";
     case ATTN_EUNSUPPORTED: return "unsupported problem";
     case ATTN_EHIP: return "HIP runtime error";
+    case ATTN_ENOSCRATCH: return "problem needs more device scratch than attn_bwd_static holds";
   }
   return "unknown status";
 }
@@ -236,50 +329,29 @@ attn_status_t attn_bwd_preprocess(const attn_problem_t* p, const void* o, const 
 attn_status_t attn_bwd(const attn_problem_t* p, const void* q, const void* k, const void* v,
                        const void* dout, const float* lse, const float* delta, const float* bias,
                        float* dq, float* dk, float* dv, float* dbias, uint32_t flags, void* stream) {
-  attn_status_t st = check_problem(p);
-  if (st != ATTN_OK) return st;
-  if ((flags & ~(uint32_t)(ATTN_DETERMINISTIC | ATTN_ACCUMULATE_DQ | ATTN_ACCUMULATE_DKDV | ATTN_SHARED_KV)) != 0)
-    return ATTN_EINVAL;
-  if ((flags & ATTN_SHARED_KV) || p->Dqk == attn::kSharedKvD || p->Dv == attn::kSharedKvD)
-    return bwd_shared_kv(p, q, k, v, dout, lse, delta, bias, dq, dk, dv, dbias, flags, stream);
-  if (!strides_ok(p->q_str) || !strides_ok(p->k_str) || !strides_ok(p->v_str) || !strides_ok(p->do_str) ||
-      !strides_ok(p->dq_str) || !strides_ok(p->dk_str) || !strides_ok(p->dv_str))
-    return ATTN_EINVAL;
-  if (dbias && !bias) return ATTN_EINVAL;
-  if (bias && (p->bias_str[0] < 0 || p->bias_str[1] < 0)) return ATTN_EINVAL;
-  if (dbias && !dbias_strides_ok(p)) return ATTN_EINVAL;
-  const bool no_rows = p->B == 0 || p->Sq == 0;
-  const bool no_keys = p->B == 0 || p->Sk == 0;
-  if (!no_rows && (!q || !dout || !lse || !delta || !dq)) return ATTN_EINVAL;
-  if (!no_keys && (!k || !v || !dk || !dv)) return ATTN_EINVAL;
-  if (p->in_dtype == ATTN_F32 && (p->Dqk > attn::kSimtMaxD || p->Dv > attn::kSimtMaxD))
-    return ATTN_EUNSUPPORTED;
+  return bwd_impl(p, q, k, v, dout, lse, delta, bias, dq, dk, dv, dbias, flags, stream, true);
+}
 
-  Params kp = make_params(p);
-  attn::BwdArgs a{q, k, v, dout, lse, delta, bias, dq, dk, dv, dbias,
-                  (flags & ATTN_ACCUMULATE_DQ) ? 1 : 0, (flags & ATTN_DETERMINISTIC) ? 1 : 0,
-                  (flags & ATTN_ACCUMULATE_DKDV) ? 1 : 0};
-  a.workspace = p->workspace_bytes > 0 ? p->workspace : nullptr;
-  a.workspace_bytes = p->workspace_bytes;
-  hipStream_t s = (hipStream_t)stream;
-  if (p->in_dtype == ATTN_BF16) {
-    if (!attn::mfma_bwd_supported(kp)) {
-      if (p->Dqk > attn::kSimtMaxD || p->Dv > attn::kSimtMaxD) return ATTN_EUNSUPPORTED;
-    }
+attn_status_t attn_bwd_static(const attn_problem_t* p, const void* q, const void* k, const void* v,
+                              const void* dout, const float* lse, const float* delta, const float* bias,
+                              float* dq, float* dk, float* dv, float* dbias, uint32_t flags, void* stream) {
+  // every host-side check first: no HIP call for an invalid or oversized problem
+  attn_status_t st = bwd_impl(p, q, k, v, dout, lse, delta, bias, dq, dk, dv, dbias, flags, stream, false);
+  if (st != ATTN_OK) return st;
+  int64_t need = 0;
+  st = attn_bwd_workspace_size(p, flags, &need);
+  if (st != ATTN_OK) return st;
+  if (need > (int64_t)ATTN_STATIC_SCRATCH_BYTES) return ATTN_ENOSCRATCH;
+  attn_problem_t ps = *p;
+  ps.workspace = nullptr;
+  ps.workspace_bytes = 0;
+  if (need > 0) {
+    // every slot a call reads is stored by that call first: no zeroing
+    st = static_scratch(stream, &ps.workspace);
+    if (st != ATTN_OK) return st;
+    ps.workspace_bytes = (int64_t)ATTN_STATIC_SCRATCH_BYTES;
   }
-  // a packed batch runs on the matrix-core kernels only
-  if (packed(p) && (bias || p->in_dtype != ATTN_BF16 || !attn::mfma_bwd_supported(kp) || !aligned16(q) ||
-                    !aligned16(k) || !aligned16(v) || !aligned16(dout)))
-    return ATTN_EUNSUPPORTED;
-  if (no_rows && no_keys) return ATTN_OK;
-  if (p->in_dtype == ATTN_BF16 && attn::mfma_bwd_supported(kp))
-    return hip_status(attn::launch_bwd_mfma(kp, a, s));
-  // fp32 inputs (and bf16 shapes the matrix-core kernels do not cover)
-  if (no_keys) {  // no keys: dK/dV are empty, dQ gets nothing added
-    if (!a.accumulate_dq) return hip_status(attn::launch_zero_rows(dq, p->B, p->Hq, p->Sq, p->Dqk, p->dq_str, s));
-    return ATTN_OK;
-  }
-  return hip_status(attn::launch_bwd_simt(kp, a, p->in_dtype == ATTN_BF16, s));
+  return bwd_impl(&ps, q, k, v, dout, lse, delta, bias, dq, dk, dv, dbias, flags, stream, true);
 }
 
 attn_status_t attn_bwd_workspace_size(const attn_problem_t* p, uint32_t flags, int64_t* bytes) {

@@ -56,7 +56,8 @@ typedef enum {
   ATTN_OK = 0,
   ATTN_EINVAL = -1,        /* inconsistent or out-of-range argument          */
   ATTN_EUNSUPPORTED = -2,  /* valid problem outside what the kernels cover   */
-  ATTN_EHIP = -3           /* a HIP launch or runtime call failed            */
+  ATTN_EHIP = -3,          /* a HIP launch or runtime call failed            */
+  ATTN_ENOSCRATCH = -4     /* attn_bwd_static: needs more than its scratch   */
 } attn_status_t;
 
 typedef enum { ATTN_F32 = 0, ATTN_BF16 = 1 } attn_dtype_t;
@@ -213,6 +214,29 @@ attn_status_t attn_bwd(const attn_problem_t* p, const void* q, const void* k, co
                        const void* dout, const float* lse, const float* delta,
                        const float* bias, float* dq, float* dk, float* dv, float* dbias,
                        uint32_t flags, void* stream);
+
+/* Size of the device scratch array of attn_bwd_static, per GPU. */
+#define ATTN_STATIC_SCRATCH_BYTES (64u * 1024u * 1024u)
+
+/* attn_bwd for callers that cannot allocate device memory (code under HIP
+ * graph capture, tight serving loops, harnesses that forbid allocation):
+ * the same arguments, results and validation as attn_bwd, but the partial
+ * sums that attn_bwd keeps in p->workspace live in a static device array
+ * of ATTN_STATIC_SCRATCH_BYTES (64 MiB) that the library holds on each GPU
+ * it runs on until the process ends; p->workspace and p->workspace_bytes
+ * are ignored.  The call allocates nothing.  A problem whose
+ * attn_bwd_workspace_size exceeds ATTN_STATIC_SCRATCH_BYTES returns
+ * ATTN_ENOSCRATCH before any HIP call (it fits attn_bwd with a caller
+ * workspace, or without one).  Every call on a GPU shares that GPU's array
+ * and leaves its contents behind; a call stores every element of it that it
+ * reads first, so nothing needs to be cleared, but calls that overlap on one
+ * GPU (on different streams, or concurrent host threads) race on it and
+ * must be serialised by the caller.  The first call on a GPU looks up the
+ * array's device address there (hipGetSymbolAddress). */
+attn_status_t attn_bwd_static(const attn_problem_t* p, const void* q, const void* k, const void* v,
+                              const void* dout, const float* lse, const float* delta,
+                              const float* bias, float* dq, float* dk, float* dv, float* dbias,
+                              uint32_t flags, void* stream);
 
 /* Bytes of p->workspace with which attn_bwd(p, ..., flags) keeps the
  * partial sums of split key blocks (with ATTN_SHARED_KV: of the query-head

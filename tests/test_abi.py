@@ -289,3 +289,22 @@ def test_binding_checks_bias_shape():
     with pytest.raises(ValueError):
         B.make_problem(q, k, k, bias=torch.empty(4, 64, 32))
     B.make_problem(q, k, k, bias=torch.empty(4, 64, 64))
+
+
+def test_static_entry_point_rejects_oversized_problem():
+    """attn_bwd_static refuses, before any HIP call, a problem whose partial
+    sums need more than its static scratch (here 84 MiB: one KV head of
+    12288 keys split eight ways); invalid arguments fail as in attn_bwd."""
+    L = B.lib()
+    p = B.attn_problem_t()
+    L.attn_problem_init(ctypes.byref(p), 1, 8, 1, 12288, 12288, 128, 128)
+    p.mask = 1
+    n = ctypes.c_int64(0)
+    assert L.attn_bwd_workspace_size(ctypes.byref(p), 0, ctypes.byref(n)) == B.ATTN_OK
+    assert n.value > B.ATTN_STATIC_SCRATCH_BYTES
+    args = [FAKE] * 7 + [FAKE, FAKE, FAKE, None, 0, None]
+    assert L.attn_bwd_static(ctypes.byref(p), *args) == B.ATTN_ENOSCRATCH
+    assert B.status_string(B.ATTN_ENOSCRATCH) != "unknown status"
+    # validation comes first: a null dq is ATTN_EINVAL whatever the size
+    bad = [FAKE] * 7 + [None, FAKE, FAKE, None, 0, None]
+    assert L.attn_bwd_static(ctypes.byref(p), *bad) == B.ATTN_EINVAL
