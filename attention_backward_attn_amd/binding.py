@@ -224,11 +224,11 @@ def attn_bwd_workspace_size(p: attn_problem_t, flags: int = 0) -> int:
     return int(n.value)
 
 
-def set_workspace(p: attn_problem_t, flags: int = 0, device=None):
+def set_workspace(p: attn_problem_t, flags: int = 0, device=None, bias=None):
     """Attach a workspace of attn_bwd_workspace_size bytes to p (a torch
     uint8 tensor, returned so that the caller keeps it alive; None when the
-    call needs none)."""
-    n = attn_bwd_workspace_size(p, flags)
+    call needs none -- a problem with a bias uses none)."""
+    n = 0 if bias is not None else attn_bwd_workspace_size(p, flags)
     if n == 0:
         p.workspace, p.workspace_bytes = None, 0
         return None
@@ -279,11 +279,12 @@ def forward(q, k, v, *, bias=None, sinks=None, o_dtype=None, stream=None, **mask
 
 
 def backward(q, k, v, o, do, lse, *, bias=None, sinks=None, want_dbias=False, flags=0, stream=None,
-             dq=None, **mask_kw):
+             dq=None, workspace: bool = True, **mask_kw):
     """Full backward: preprocess then the main pass.  Returns a dict with
     dq, dk, dv (fp32), dbias and dsinks (or None) and delta.  With
     ATTN_SHARED_KV in flags (k is v) dk is the gradient of the shared tensor
-    and dv is None."""
+    and dv is None.  ``workspace`` False runs attn_bwd without a caller
+    workspace (the parts of split key blocks then add atomically)."""
     import torch
     dev = q.device
     if mask_kw.get("cu_seqlens_q") is not None:
@@ -307,7 +308,7 @@ def backward(q, k, v, o, do, lse, *, bias=None, sinks=None, want_dbias=False, fl
     # workspace for split key blocks' partial sums, marked as in use on the
     # call's stream: torch's caching allocator then hands the block to no
     # other allocation before that stream has finished the call
-    ws = set_workspace(p, flags, dev)
+    ws = set_workspace(p, flags, dev, bias) if workspace else None
     if ws is not None:
         ws.record_stream(_torch_stream(stream, dev))
     attn_bwd_preprocess(p, o, do, lse, sinks, delta, dsinks, None, None, None, stream)

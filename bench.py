@@ -297,7 +297,7 @@ def main():
     p = ab.make_problem(q, k, v, o=o, do=do, dq=dq, dk=dk, dv=dv, bias=bias, scale=w.scale, **mask_kw)
     # caller-owned workspace for split key blocks' partial sums (none when
     # the call needs none), allocated before any timing
-    ws = ab.set_workspace(p, 0)  # noqa: F841
+    ws = ab.set_workspace(p, 0, bias=bias)  # noqa: F841
 
     def pre():
         ab.attn_bwd_preprocess(p, o, do, lse, sinks, delta, dsinks, None, None, None, stream)

@@ -65,7 +65,7 @@ def random_case(B, Hq, Hk, Sq, Sk, D, Dv, dtype, seed, bias, sinks):
     return x
 
 
-def run_full_parity(x, dtype, spec, scale, flags=0):
+def run_full_parity(x, dtype, spec, scale, flags=0, workspace=True):
     """Oracle forward -> fp32 O/LSE -> GPU and oracle backward; compare all."""
     o64, lse64 = oracle.forward(x["q"], x["k"], x["v"], scale, spec, x["bias"], x["sinks"])
     o32, lse32 = o64.astype(np.float32), lse64.astype(np.float32)
@@ -75,7 +75,7 @@ def run_full_parity(x, dtype, spec, scale, flags=0):
     bias, sinks = dev(x["bias"], torch.float32), dev(x["sinks"], torch.float32)
     o, lse = dev(o32, torch.float32), dev(lse32, torch.float32)
     got = ab.backward(q, k, v, o, do, lse, bias=bias, sinks=sinks, want_dbias=bias is not None,
-                      flags=flags, scale=scale, **mask_kw(spec))
+                      flags=flags, scale=scale, workspace=workspace, **mask_kw(spec))
     torch.cuda.synchronize()
     tol = TOL[dtype]
     errs = {}
@@ -110,11 +110,15 @@ SMALL = [
 @pytest.mark.parametrize("case", SMALL, ids=lambda c: f"{c[7]}-B{c[0]}H{c[1]}:{c[2]}-S{c[3]}x{c[4]}-D{c[5]}-"
                          f"{c[8].kind}{'-bias' if c[9] else ''}{'-sinks' if c[10] else ''}")
 @pytest.mark.parametrize("flags", [0, ab.ATTN_DETERMINISTIC], ids=["atomic", "determ"])
-def test_small_parity(case, flags):
+@pytest.mark.parametrize("workspace", [True, False], ids=["ws", "nows"])
+def test_small_parity(case, flags, workspace):
+    """With a workspace, the parts of split key blocks keep partial dK / dV
+    sums that are added in slot order; without one they add atomically into
+    zeroed outputs."""
     B, Hq, Hk, Sq, Sk, D, Dv, dtype, spec, bias, sinks = case
-    say(f"[parity] {case} flags={flags}")
+    say(f"[parity] {case} flags={flags} workspace={workspace}")
     x = random_case(B, Hq, Hk, Sq, Sk, D, Dv, dtype, 100 + Sq + Sk, bias, sinks)
-    run_full_parity(x, dtype, spec, 1.0 / np.sqrt(D), flags)
+    run_full_parity(x, dtype, spec, 1.0 / np.sqrt(D), flags, workspace)
 
 
 @pytest.mark.parametrize("name", ["mha_f32_s64", "gqa4_causal_tl_s1024"])
