@@ -430,6 +430,13 @@ struct __attribute__((aligned(1024))) SmemDKDV2 {
   f32x4 px[2][4][4][64];              // P (fp32) by tile parity, pair w % 4: [4 values][lane]
 };
 
+// With a bias (head dim 64): the bias tile [32 rows][128 keys] (fp32) of each
+// buffer, after the members above (the S wave adds it to S).
+template <int D>
+struct __attribute__((aligned(1024))) SmemDKDV2B : SmemDKDV2<D> {
+  float bias[NB2][BQ * BK];
+};
+
 // Staging of one 32-row Q / dO tile straight from global memory into LDS:
 // wave w issues CR / 8 64-lane loads, each filling 1 KB (64 / CR rows) of
 // one tensor's tile in the swizzled layout, so every lane has one fixed
@@ -483,14 +490,16 @@ struct StageDma {
 struct TileWalk {
   const unsigned short *q, *d;
   const float *l, *dl;
+  const float* bz;   // bias of the tile's first row and the block's first key (with a bias)
   int qb, nqb, i0, lo_al;
-  int64_t q_step, d_step, q_wrap, d_wrap, l_wrap;
+  int64_t q_step, d_step, q_wrap, d_wrap, l_wrap, b_step, b_wrap;
 
   __device__ inline void next() {
     q += q_step;
     d += d_step;
     l += BQ;
     dl += BQ;
+    bz += b_step;
     i0 += BQ;
     if (++qb == nqb) {
       qb = 0;
@@ -499,17 +508,25 @@ struct TileWalk {
       d += d_wrap;
       l += l_wrap;
       dl += l_wrap;
+      bz += b_wrap;
     }
   }
 };
 
-template <int D>
+// BIAS (head dim 64): S gets the elementwise bias [Hq, Sq, Sk] (shared over
+// the batch), staged per tile into LDS next to Q / dO; the S wave adds it
+// before the exponentials.  No dbias here (the dQ pass sums it).
+template <int D, bool BIAS>
 __global__ __launch_bounds__(NT2) void k_dkdv2(Params p, BwdArgs a, DkdvGrid gd) {
   static_assert(D == 64 || D == 128, "head dim");
+  static_assert(!BIAS || D == 64, "the bias tiles fit LDS at head dim 64");
   constexpr int NS = D / 16;          // k-steps over the head dim
   constexpr int NC = D / 32;          // 32-column blocks of dK / dV
   constexpr int RB = Swz<D>::RB;
-  __shared__ SmemDKDV2<D> sm;
+  constexpr int NIW = StageDma<D>::NI + (BIAS ? 2 : 0);   // loads per wave per tile
+  constexpr int BIAS_OFF = (int)sizeof(SmemDKDV2<D>);      // byte offset of the bias tiles
+  constexpr int BTS = BQ * BK * 4;                         // bias tile bytes
+  __shared__ std::conditional_t<BIAS, SmemDKDV2B<D>, SmemDKDV2<D>> sm;
 
   const int tid = threadIdx.x, l = tid & 63, lr = l & 31, lg = l >> 5;
   const int w = __builtin_amdgcn_readfirstlane(tid >> 6);   // wave-uniform
@@ -641,14 +658,30 @@ __global__ __launch_bounds__(NT2) void k_dkdv2(Params p, BwdArgs a, DkdvGrid gd)
       ld.q_wrap = p.q_str[1] - nqb * ld.q_step;
       ld.d_wrap = p.do_str[1] - nqb * ld.d_step;
       ld.l_wrap = (int64_t)p.Sq - (int64_t)nqb * BQ;
+      ld.bz = BIAS ? a.bias + h0 * p.bias_str[0] + (int64_t)i00 * p.bias_str[1] + k0 : nullptr;
+      ld.b_step = BIAS ? BQ * p.bias_str[1] : 0;
+      ld.b_wrap = BIAS ? p.bias_str[0] - nqb * ld.b_step : 0;
     }
     int fr_i0 = ld.i0, fr_qb = ld.qb;   // tile whose P the S wave forms next
     auto fr_next = [&]() {
       fr_i0 += BQ;
       if (++fr_qb == nqb) { fr_qb = 0; fr_i0 = lo_al; }
     };
+    // bias tile: wave w loads rows 4 w .. 4 w + 3 (two 1 KB loads of two rows each);
+    // the resource ends at the tile's last valid element (rows past the end read zeros)
+    const int b_rb = BIAS ? 4 * (int)p.bias_str[1] : 0, bkeys = min(Sk - k0, BK);
     auto issue = [&](int buf) {
-      stg.issue(sm_base, buf, ld.q, ld.d, q_rb, d_rb, ld.l, ld.dl, min(Sq - ld.i0, BQ), l);
+      const int rows = min(Sq - ld.i0, BQ);
+      stg.issue(sm_base, buf, ld.q, ld.d, q_rb, d_rb, ld.l, ld.dl, rows, l);
+      if (BIAS) {
+        const __amdgpu_buffer_rsrc_t rb_ = buf_rsrc(ld.bz, (rows - 1) * b_rb + 4 * bkeys);
+#pragma unroll
+        for (int k = 0; k < 2; ++k) {
+          const int g = 2 * w + k;   // rows 2 g, 2 g + 1
+          lds_dma16(rb_, __builtin_amdgcn_readfirstlane(sm_base + BIAS_OFF + buf * BTS + 1024 * g),
+                    (2 * g + (l >> 5)) * b_rb + 16 * (l & 31));
+        }
+      }
       ld.next();
     };
     // Prologue: tiles 0..3 in flight; 0..2 complete before the first barrier.
@@ -658,7 +691,7 @@ __global__ __launch_bounds__(NT2) void k_dkdv2(Params p, BwdArgs a, DkdvGrid gd)
       if (n_it > j) issue(j);
     if (n_it > NB2 - 2) {
       issue(NB2 - 2);
-      wait_vm_c<StageDma<D>::NI>();
+      wait_vm_c<NIW>();
     } else {
       wait_vm_c<0>();
     }
@@ -690,6 +723,23 @@ __global__ __launch_bounds__(NT2) void k_dkdv2(Params p, BwdArgs a, DkdvGrid gd)
     auto row_vals = [&](f32x4* x, const float* v) {
 #pragma unroll
       for (int m = 0; m < 4; ++m) x[m] = *(const f32x4*)&v[8 * m + 4 * lg];
+    };
+    // bias (log2 units) of the 16 pairs this lane holds for the tile in
+    // buffer j: rows crow(r, lg), key 32 pr + lane of the block
+    const unsigned int b_lane = sm_base + BIAS_OFF + (4 * lg) * (BK * 4) + (32 * pr + lr) * 4;
+    auto bias_vals = [&](float* bv, int j) {
+      if (BIAS) {
+        typedef __attribute__((address_space(3))) const float lds_f32;
+        const unsigned int base = b_lane + j * BTS;
+#pragma unroll
+        for (int r = 0; r < 16; ++r)
+          bv[r] = *(lds_f32*)(size_t)(base + (8 * (r >> 2) + (r & 3)) * (BK * 4)) * kLog2e;
+      }
+    };
+    // exponent (log2 units) of P = exp(S scale + bias - LSE)
+    auto expo = [&](float s_, float l2, float b2) {
+      const float x = fmaf(s_, scale_log2, -l2);
+      return BIAS ? x + b2 : x;
     };
     constexpr int EPS = 16 / NS;   // accumulator elements handled per chain step
     constexpr int AHEAD = 2;       // chain steps whose operands are in flight
@@ -755,8 +805,11 @@ __global__ __launch_bounds__(NT2) void k_dkdv2(Params p, BwdArgs a, DkdvGrid gd)
       if (SW) {
         f32x4 L4[4];
         row_vals(L4, sm.lse[0]);
+        float bv[16];
+        bias_vals(bv, 0);
 #pragma unroll
-        for (int r = 0; r < 16; ++r) pv[r] = __builtin_amdgcn_exp2f(fmaf(acc[r], scale_log2, -L4[r >> 2][r & 3]));
+        for (int r = 0; r < 16; ++r)
+          pv[r] = __builtin_amdgcn_exp2f(expo(acc[r], L4[r >> 2][r & 3], bv[r]));
         publish(0);
         fr_next();
         acc = chain(1);   // S(1) (stale when there is no tile 1; then unused)
@@ -791,6 +844,8 @@ __global__ __launch_bounds__(NT2) void k_dkdv2(Params p, BwdArgs a, DkdvGrid gd)
           // region: dV(t) products, S(t + 2) chain, exponentials of S(t + 1)
           f32x4 L4[4];
           row_vals(L4, sm.lse[j1]);
+          float bv[16];
+          bias_vals(bv, j1);
 #pragma unroll
           for (int i = 0; i < AHEAD; ++i) { bq[i] = bq_n[i]; xa[i] = read_a(j2, i); }
           __builtin_amdgcn_sched_barrier(0);
@@ -801,7 +856,7 @@ __global__ __launch_bounds__(NT2) void k_dkdv2(Params p, BwdArgs a, DkdvGrid gd)
 #pragma unroll
             for (int e = 0; e < EPS; ++e) {
               const int r = EPS * i + e;
-              pv[r] = __builtin_amdgcn_exp2f(fmaf(acc[r], scale_log2, -L4[r >> 2][r & 3]));
+              pv[r] = __builtin_amdgcn_exp2f(expo(acc[r], L4[r >> 2][r & 3], bv[r]));
             }
             if (i + AHEAD < NS) { bq[i + AHEAD] = read_b(j, i + AHEAD); xa[i + AHEAD] = read_a(j2, i + AHEAD); }
             __builtin_amdgcn_sched_barrier(0);
@@ -841,7 +896,7 @@ __global__ __launch_bounds__(NT2) void k_dkdv2(Params p, BwdArgs a, DkdvGrid gd)
         acc = accn;
         prefetch(std::integral_constant<int, j1>{});   // (past the last tile: stale, unused)
         // tile t + 3 complete before the next barrier (tile t + 4 may stay in flight)
-        wait_vm_keep<StageDma<D>::NI>(more);
+        wait_vm_keep<NIW>(more);
       };
       static_assert(NB2 == 5, "tile loop unrolled over five buffers");
       for (int t0 = 0; t0 < n_it; t0 += NB2) {
@@ -939,7 +994,11 @@ template <int D>
 hipError_t dispatch_dkdv(const Params& p, const BwdArgs& a, const DkdvPlan& pl, bool bias, bool bloop,
                          hipStream_t st) {
   if (!bias) {
-    hipLaunchKernelGGL((k_dkdv2<D>), pl.grid, dim3(NT2), 0, st, p, a, pl.g);
+    hipLaunchKernelGGL((k_dkdv2<D, false>), pl.grid, dim3(NT2), 0, st, p, a, pl.g);
+    return hipGetLastError();
+  }
+  if (D == 64 && !bloop) {
+    hipLaunchKernelGGL((k_dkdv2<64, true>), pl.grid, dim3(NT2), 0, st, p, a, pl.g);
     return hipGetLastError();
   }
   return bloop ? launch_dkdv<D, true, true>(p, a, pl, st) : launch_dkdv<D, true, false>(p, a, pl, st);
@@ -1617,6 +1676,273 @@ __global__ __launch_bounds__(NT, 2) void k_dq2(Params p, BwdArgs a, ZeroMulti zm
   zero_share();
 }
 
+// ---------------------------------------------------------------------------
+// Kernel k_dqb (dQ and dbias, head dim 64): one workgroup of four waves per
+// (128-row block, query head); wave w owns rows 32 w .. 32 w + 31.  The
+// batch is walked innermost, in groups of up to BGB entries: for each key
+// tile the workgroup stages the group's K / V tiles and the [128 x 32] fp32
+// bias tile (one copy for all entries: the bias is shared over the batch)
+// straight into LDS, two tiles ahead, and each wave forms, entry by entry,
+// S^T = K Q^T and dP^T = V dO^T (keys on accumulator rows, one query row per
+// lane, Q / dO fragments of every entry in registers), P, dS, dQ += dS K,
+// and adds dS into a register dbias tile.  After the group's entries the
+// dbias tile is stored (the first group) or added to (later groups), so
+// dbias = sum_b dS is read from and written to memory once per group, in a
+// fixed order.  One wave per SIMD (the group's fragments and accumulators
+// take most of the register file).
+// ---------------------------------------------------------------------------
+constexpr int BGB = 4;   // batch entries per group (k_dqb)
+constexpr int NQB = 3;   // tile buffers (k_dqb)
+
+template <int D>
+struct __attribute__((aligned(1024))) SmemDQB {
+  unsigned char kv[NQB][2 * BGB][BK3 * 2 * D];   // K then V tile of each entry, swizzled
+  float bias[NQB][BQ3 * BK3];                   // bias[i0 + r][j0 + c], 16-byte chunks swizzled by row
+};
+
+template <int D>
+__global__ __launch_bounds__(NT, 1) void k_dqb(Params p, BwdArgs a) {
+  static_assert(D == 64, "head dim 64");
+  constexpr int NS = D / 16;                 // k-steps over the head dim
+  constexpr int NC = D / 32;                 // 32-column blocks of dQ
+  constexpr int RB = Swz<D>::RB, CR = Swz<D>::CR;
+  constexpr int TS = BK3 * 2 * D;            // K or V tile bytes
+  constexpr int PER_T = BK3 * CR / 64;       // 1 KB loads per K or V tile
+  constexpr int BTB = BQ3 * BK3 * 4;         // bias tile bytes
+  constexpr int BIAS_OFF = NQB * 2 * BGB * TS;
+  static_assert(PER_T == 4 && BTB == 16384, "loads per wave: one entry's K and V, 32 bias rows");
+  __shared__ SmemDQB<D> sm;
+
+  const int tid = threadIdx.x, l = tid & 63, lr = l & 31, lg = l >> 5;
+  const int w = __builtin_amdgcn_readfirstlane(tid >> 6);   // wave-uniform
+  const BlockXYZ blk = xcd_block();
+  const int i0 = blk.x * BQ3, h = blk.y, g = h / p.G;
+  const Mask& msk = p.mask;
+  const int Sq = p.Sq, Sk = p.Sk;
+  if (i0 >= Sq) return;
+  const int irow = i0 + 32 * w + lr;   // this lane's query row
+  const bool row_ok = irow < Sq;
+  const float scale = p.scale, scale_log2 = p.scale * kLog2e, inv_scale = 1.f / p.scale;
+
+  // key tiles: the sink tiles [0, a1) and the band tiles [a2, a3)
+  int64_t s_hi, b_lo, b_hi;
+  msk.keys_for_rows(i0, min(i0 + BQ3, Sq), Sk, &s_hi, &b_lo, &b_hi);
+  const int a1 = (int)((s_hi + BK3 - 1) / BK3);
+  int a2 = (int)(b_lo / BK3);
+  const int a3 = b_hi > b_lo ? (int)((b_hi + BK3 - 1) / BK3) : a2;
+  if (a2 < a1) a2 = a1;
+  const int n1 = a1, n2 = a3 > a2 ? a3 - a2 : 0, n_it = n1 + n2;
+  auto tile_of = [&](int it) { return BK3 * (it < n1 ? it : a2 + (it - n1)); };
+  const bool no_mask = msk.kind == kMaskNone;
+  int lo_l = msk.wl < 0 ? -0x3fffffff : -msk.wl, span = msk.wr - lo_l;
+  if (no_mask) { lo_l = -0x3fffffff; span = 0x7ffffffe; }
+  // window offset of key 4 lg (+ c) of a tile for this lane's row
+  const int tq = (int)msk.k_off - (irow + (int)msk.q_off) - (int)msk.diag + 4 * lg - lo_l;
+  const int sink_lim = (int)min<int64_t>(max<int64_t>(msk.n_sink - msk.k_off, 0), 0x3fffffff);
+  const int wr0 = i0 + 32 * w;
+  auto clamp_i = [](int64_t x) { return (int)max<int64_t>(min<int64_t>(x, 0x3fffffff), -0x3fffffff); };
+  const int64_t band = (int64_t)wr0 + msk.q_off + msk.diag - msk.k_off;
+  const int fl_hi = no_mask ? 0x3fffffff : clamp_i(band + msk.wr - 31);
+  const int fl_lo = (no_mask || msk.wl < 0) ? -0x3fffffff : clamp_i(band + 31 - msk.wl);
+  const int fl_sink = no_mask ? -0x3fffffff : clamp_i((int64_t)msk.n_sink - 31 - msk.k_off);
+  auto tile_full = [&](int j0) { return (j0 + BK3 <= Sk) & ((j0 < fl_sink) | ((j0 <= fl_hi) & (j0 >= fl_lo))); };
+
+  const unsigned int sm_base = __builtin_amdgcn_readfirstlane(lds_addr(&sm));
+  const int k_rb = 2 * (int)p.k_str[2], v_rb = 2 * (int)p.v_str[2], b_rb = 4 * (int)p.bias_str[1];
+  const int brows = min(Sq - i0, BQ3);
+  const float* bias_h = a.bias + h * p.bias_str[0] + (int64_t)i0 * p.bias_str[1];
+  // staging: wave w loads entry w's K and V tiles (four 1 KB loads each, when
+  // the group has that entry) and bias rows 32 w .. 32 w + 31 (four 1 KB loads
+  // of 8 rows; 16-byte chunk c of row r lands at chunk c ^ (r % 8))
+  auto issue = [&](int it, int buf, int b0, int nb) {
+    const int j0 = tile_of(it);
+    const int keys = min(Sk - j0, BK3);
+    if (w < nb) {
+      const int b = b0 + w;
+      const unsigned short* kt = (const unsigned short*)a.k + b * p.k_str[0] + g * p.k_str[1] + (int64_t)j0 * p.k_str[2];
+      const unsigned short* vt = (const unsigned short*)a.v + b * p.v_str[0] + g * p.v_str[1] + (int64_t)j0 * p.v_str[2];
+      const __amdgpu_buffer_rsrc_t rk = buf_rsrc(kt, keys * k_rb), rv = buf_rsrc(vt, keys * v_rb);
+#pragma unroll
+      for (int k = 0; k < PER_T; ++k) {
+        const int row = (64 * k + l) / CR, c = (l % CR) ^ Swz<D>::f(row);
+        lds_dma16(rk, __builtin_amdgcn_readfirstlane(sm_base + (buf * 2 * BGB + w) * TS + 1024 * k),
+                  row * k_rb + 16 * c);
+        lds_dma16(rv, __builtin_amdgcn_readfirstlane(sm_base + (buf * 2 * BGB + BGB + w) * TS + 1024 * k),
+                  row * v_rb + 16 * c);
+      }
+    }
+    const __amdgpu_buffer_rsrc_t rb_ = buf_rsrc(bias_h + j0, (brows - 1) * b_rb + 4 * keys);
+#pragma unroll
+    for (int k = 0; k < 4; ++k) {
+      const int row = 32 * w + 8 * k + (l >> 3), c = (l & 7) ^ (row & 7);
+      lds_dma16(rb_, __builtin_amdgcn_readfirstlane(sm_base + BIAS_OFF + buf * BTB + (32 * w + 8 * k) * 128),
+                row * b_rb + 16 * c);
+    }
+  };
+
+  // operand read addresses (buffer 0, entry 0)
+  const int a_lane = Swz<D>::a_lane(l), t_lane = Swz<D>::t_lane(l);
+  unsigned int br[NC];
+#pragma unroll
+  for (int n = 0; n < NC; ++n) br[n] = sm_base + (t_lane ^ (64 * n));
+  const unsigned int ka = sm_base + a_lane;
+  // this lane's bias row, chunks 2 m + lg (keys 8 m + 4 lg + 0..3), swizzled
+  const int brow = 32 * w + lr;
+  const unsigned int b_lane = sm_base + BIAS_OFF + brow * 128;
+
+  float* dbias_h = a.dbias + h * p.bias_str[0] + (int64_t)i0 * p.bias_str[1];
+  const int db_off = (32 * w + lr) * b_rb + 16 * lg;   // this lane's row, keys 4 lg + 0..3 of a tile
+  for (int b0 = 0; b0 < p.B; b0 += BGB) {
+    const int nb = min(BGB, p.B - b0);
+    const bool first = b0 == 0;
+    // this group's Q / dO fragments (B operands, one query row per lane), LSE, delta
+    bf16x8 qB[BGB][NS], doB[BGB][NS];
+    float lse2[BGB], dls[BGB];
+    f32x16 dq[BGB][NC];
+#pragma unroll
+    for (int e = 0; e < BGB; ++e) {
+      const int b = b0 + (e < nb ? e : 0);
+      const int64_t ic = min(irow, Sq - 1);
+      const unsigned short* q = (const unsigned short*)a.q + b * p.q_str[0] + h * p.q_str[1] + ic * p.q_str[2];
+      const unsigned short* d = (const unsigned short*)a.dout + b * p.do_str[0] + h * p.do_str[1] + ic * p.do_str[2];
+#pragma unroll
+      for (int s = 0; s < NS; ++s) {
+        qB[e][s] = as_bf16x8(*(const u16x8*)(q + 16 * s + 8 * lg));
+        doB[e][s] = as_bf16x8(*(const u16x8*)(d + 16 * s + 8 * lg));
+      }
+      lse2[e] = INFINITY;
+      dls[e] = 0.f;
+      if (row_ok) {
+        const float lv = a.lse[((int64_t)b * p.Hq + h) * p.Sq + irow];
+        lse2[e] = (lv == -INFINITY) ? INFINITY : lv * kLog2e;
+        dls[e] = a.delta[((int64_t)b * p.Hq + h) * p.Sq + irow] * scale;
+      }
+#pragma unroll
+      for (int n = 0; n < NC; ++n) dq[e][n] = zero16();
+    }
+    wait_vm_loads();
+    __syncthreads();   // the previous group's readers of the tile buffers are done
+    if (n_it > 0) {
+      issue(0, 0, b0, nb);
+      if (n_it > 1) issue(1, 1, b0, nb);
+    }
+    const int ni = (w < nb ? 2 * PER_T : 0) + 4;   // this wave's loads per tile
+    if (n_it > 1) wait_vm(ni);
+    else wait_vm(0);
+    for (int t = 0; t < n_it; ++t) {
+      const int buf = t % NQB;
+      __syncthreads();   // tile t complete for every wave; tile t - 1's buffer free
+      if (t + 2 < n_it) issue(t + 2, (t + 2) % NQB, b0, nb);
+      const int j0 = tile_of(t);
+      const bool full = tile_full(j0);
+      float db[16];
+#pragma unroll
+      for (int r = 0; r < 16; ++r) db[r] = 0.f;
+      const int tb = tq + j0;
+#pragma unroll
+      for (int e = 0; e < BGB; ++e) {
+        if (e >= nb) break;
+        const unsigned int kt = (buf * 2 * BGB + e) * TS, vt = (buf * 2 * BGB + BGB + e) * TS;
+        // S^T starts from bias / scale (this lane's row, keys 8 m + 4 lg + 0..3),
+        // so the chain ends at (S scale + bias) / scale
+        f32x16 sacc, pacc = zero16();
+#pragma unroll
+        for (int m = 0; m < 4; ++m) {
+          const f32x4 bz = *(const __attribute__((address_space(3))) f32x4*)(size_t)(
+              b_lane + buf * BTB + 16 * ((2 * m + lg) ^ (brow & 7)));
+#pragma unroll
+          for (int c = 0; c < 4; ++c) sacc[4 * m + c] = bz[c] * inv_scale;
+        }
+#pragma unroll
+        for (int s = 0; s < NS; ++s) {
+          sacc = mfma(lds_b128_at((ka ^ (32 * s)) + kt), qB[e][s], sacc);
+          pacc = mfma(lds_b128_at((ka ^ (32 * s)) + vt), doB[e][s], pacc);
+        }
+        float dsv[16];
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+          const int c = 8 * (r >> 2) + (r & 3);   // key 4 lg + c of the tile
+          float pp = __builtin_amdgcn_exp2f(fmaf(sacc[r], scale_log2, -lse2[e]));
+          if (!full) {
+            const int jj = j0 + 4 * lg + c;
+            const bool ok = (jj < Sk) & (((unsigned int)(tb + c) <= (unsigned int)span) | (jj < sink_lim));
+            pp = ok ? pp : 0.f;
+          }
+          dsv[r] = pp * fmaf(pacc[r], scale, -dls[e]);
+          db[r] += dsv[r];
+        }
+        const bf16x8 A0 = pack8(dsv), A1 = pack8(dsv + 8);
+#pragma unroll
+        for (int i = 0; i < NS; ++i) {
+          const int n = i % NC, r0 = 16 * (i / NC);
+          const bf16x8 bq = cat44(lds_tr4_at(br[n] + kt + r0 * RB), lds_tr4_at((br[n] ^ 32) + kt + (r0 + 8) * RB));
+          dq[e][n] = mfma(i < NC ? A0 : A1, bq, dq[e][n]);
+        }
+      }
+      // dbias of this tile (unscaled dS summed over the group): this lane's
+      // row, keys j0 + 8 m + 4 lg + 0..3.  A whole key tile is stored by four
+      // buffer stores from every lane (rows past the end fall outside the
+      // resource and are dropped), so the count of memory operations is the
+      // same in every wave; the ragged last tile stores lane by lane.
+      const bool whole = j0 + BK3 <= Sk;
+      if (whole) {
+        const __amdgpu_buffer_rsrc_t rd = buf_rsrc(dbias_h + j0, (brows - 1) * b_rb + 4 * BK3);
+#pragma unroll
+        for (int m = 0; m < 4; ++m) {
+          f32x4 v = {db[4 * m] * inv_scale, db[4 * m + 1] * inv_scale, db[4 * m + 2] * inv_scale,
+                     db[4 * m + 3] * inv_scale};
+          if (!first) v += __builtin_bit_cast(f32x4, __builtin_amdgcn_raw_buffer_load_b128(rd, db_off + 32 * m, 0, 0));
+          __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u32x4, v), rd, db_off + 32 * m, 0, 0);
+        }
+      } else if (row_ok) {
+#pragma unroll
+        for (int m = 0; m < 4; ++m) {
+          const int j = j0 + 8 * m + 4 * lg;
+          if (j < Sk) {
+            f32x4* dst = (f32x4*)(dbias_h + (int64_t)(irow - i0) * p.bias_str[1] + j);
+            f32x4 v = {db[4 * m] * inv_scale, db[4 * m + 1] * inv_scale, db[4 * m + 2] * inv_scale,
+                       db[4 * m + 3] * inv_scale};
+            if (!first) v += *dst;
+            *dst = v;
+          }
+        }
+      }
+      // Tile t + 1 complete before the next barrier (tile t + 2 may stay in
+      // flight).  Behind tile t + 1's loads come the dbias stores of tile t - 1,
+      // tile t + 2's loads and this tile's dbias stores (vector memory
+      // operations complete in issue order).
+      if (t + 2 < n_it && whole && first) {
+        if (t > 0) {
+          if (ni == 12) wait_vm_n<20>();
+          else wait_vm_n<12>();
+        } else {
+          if (ni == 12) wait_vm_n<16>();
+          else wait_vm_n<8>();
+        }
+      } else {
+        wait_vm_n<0>();
+      }
+    }
+    // dQ of the group: rows i0 + 32 w + crow(r, lg), columns 32 n + lane
+#pragma unroll
+    for (int e = 0; e < BGB; ++e) {
+      if (e >= nb) break;
+      float* dqp = a.dq + (b0 + e) * p.dq_str[0] + h * p.dq_str[1];
+#pragma unroll
+      for (int n = 0; n < NC; ++n) {
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+          const int64_t i = i0 + 32 * w + crow(r, lg);
+          if (i < Sq) {
+            float* dst = dqp + i * p.dq_str[2] + 32 * n + lr;
+            *dst = a.accumulate_dq ? *dst + dq[e][n][r] : dq[e][n][r];
+          }
+        }
+      }
+    }
+  }
+}
+
 // zm / ps: tensors to zero, partials to sum on the way (k_dq2 only: none
 // with a bias)
 template <int D>
@@ -1625,7 +1951,9 @@ hipError_t launch_dq(const Params& p, const BwdArgs& a0, const ZeroMulti& zm, co
   const dim3 grid((p.Sq + BQ3 - 1) / BQ3, p.Hq, p.B);
   BwdArgs a = a0;
   a.xmajor = xmajor_fits(p, grid.y, grid.z) ? 1 : 0;
-  if (a.bias)
+  if (a.bias && a.dbias && D == 64)   // dQ and dbias, the batch walked inside
+    hipLaunchKernelGGL((k_dqb<64>), dim3(grid.x, grid.y, 1), dim3(NT), 0, st, p, a);
+  else if (a.bias)
     hipLaunchKernelGGL((k_dq<D, true>), grid, dim3(NT), 0, st, p, a);
   else
     hipLaunchKernelGGL((k_dq2<D>), grid, dim3(NT), 0, st, p, a, zm, ps);
@@ -1708,7 +2036,9 @@ hipError_t launch_bwd_mfma(const Params& p, const BwdArgs& a, hipStream_t st) {
   // pass, run first, when it is k_dq2 and reads its K / V mostly from L2
   // (the stores then cost it little), else by a zero kernel ahead of the
   // key-block pass.
-  const bool bloop = a.dbias != nullptr;
+  // head dim 64: k_dkdv2 takes the bias (dbias, if asked, comes from k_dqb);
+  // head dim 128: k_dkdv, walking the batch when dbias is asked
+  const bool bloop = a.dbias != nullptr && p.Dqk != 64;
   const bool run_dq = p.Sq > 0 && p.B > 0, run_kv = p.Sk > 0 && p.B > 0;
   auto dq = [&](const ZeroMulti& zm, const PartialSum& ps) {
     return p.Dqk == 64 ? launch_dq<64>(p, a, zm, ps, st) : launch_dq<128>(p, a, zm, ps, st);

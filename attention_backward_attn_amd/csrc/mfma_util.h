@@ -155,11 +155,16 @@ __device__ inline unsigned int lds_addr(const void* p) {
 // Issued as inline assembly, which the compiler does not count: the caller
 // waits for completion (vmcnt) itself.  The compiler would otherwise make
 // every transposing LDS read wait for all such loads in flight.
+// The compiler's hazard checks do not look inside inline assembly, so the
+// wait states that the hardware needs before a vector memory instruction
+// reads an SGPR just written by a VALU instruction (5: the compiler may
+// restore the resource from a VGPR lane with v_readlane right before) and
+// before an LDS DMA reads M0 just written (1) are inserted here.
 __device__ inline void lds_dma16(__amdgpu_buffer_rsrc_t r, unsigned int lds, int voff) {
-  asm volatile("buffer_load_dwordx4 %0, %1, 0 offen lds" ::"v"(voff), "s"(r), "{m0}"(lds) : "memory");
+  asm volatile("s_nop 4\n\tbuffer_load_dwordx4 %0, %1, 0 offen lds" ::"v"(voff), "s"(r), "{m0}"(lds) : "memory");
 }
 __device__ inline void lds_dma4(__amdgpu_buffer_rsrc_t r, unsigned int lds, int voff) {
-  asm volatile("buffer_load_dword %0, %1, 0 offen lds" ::"v"(voff), "s"(r), "{m0}"(lds) : "memory");
+  asm volatile("s_nop 4\n\tbuffer_load_dword %0, %1, 0 offen lds" ::"v"(voff), "s"(r), "{m0}"(lds) : "memory");
 }
 
 // Wait until at most n vector-memory operations of this wave are in flight
@@ -191,6 +196,13 @@ template <int N>
 __device__ inline void wait_vm_c() {
   static_assert(N >= 0 && N < 16, "vmcnt field");
   __builtin_amdgcn_s_waitcnt(0x0F70 | N);
+}
+// wait_vm_c for counts up to 63 (the count's two high bits sit in bits 15:14
+// of the s_waitcnt immediate).
+template <int N>
+__device__ inline void wait_vm_n() {
+  static_assert(N >= 0 && N < 64, "vmcnt field");
+  __builtin_amdgcn_s_waitcnt(0x0F70 | (N & 15) | ((N >> 4) << 14));
 }
 // Either N or 0 in flight, chosen at run time by `keep` (two fixed waits).
 template <int N>
