@@ -1677,50 +1677,63 @@ __global__ __launch_bounds__(NT, 2) void k_dq2(Params p, BwdArgs a, ZeroMulti zm
 }
 
 // ---------------------------------------------------------------------------
-// Kernel k_dqb (dQ and dbias, head dim 64): one workgroup of four waves per
-// (128-row block, query head); wave w owns rows 32 w .. 32 w + 31.  The
-// batch is walked innermost, in groups of up to BGB entries: for each key
-// tile the workgroup stages the group's K / V tiles and the [128 x 32] fp32
-// bias tile (one copy for all entries: the bias is shared over the batch)
-// straight into LDS, two tiles ahead, and each wave forms, entry by entry,
-// S^T = K Q^T and dP^T = V dO^T (keys on accumulator rows, one query row per
-// lane, Q / dO fragments of every entry in registers), P, dS, dQ += dS K,
-// and adds dS into a register dbias tile.  After the group's entries the
-// dbias tile is stored (the first group) or added to (later groups), so
-// dbias = sum_b dS is read from and written to memory once per group, in a
-// fixed order.  One wave per SIMD (the group's fragments and accumulators
-// take most of the register file).
+// Kernel k_dqb (dQ and dbias, head dim 64): one workgroup of eight waves per
+// (128-row block, query head), two waves per SIMD.  Waves w and w + 4 own
+// rows 32 (w % 4) .. 32 (w % 4) + 31.  The batch is walked innermost, in
+// groups of up to BGB entries, wave w taking entries 2 (w / 4) and
+// 2 (w / 4) + 1 of the group.  For each key tile the workgroup stages the
+// group's K / V tiles and the [128 x 32] fp32 bias tile (one copy for all
+// entries: the bias is shared over the batch) straight into LDS, two tiles
+// ahead; each wave forms, entry by entry, S^T = K Q^T (the chain starting
+// from bias / scale) and dP^T = V dO^T (keys on accumulator rows, one query
+// row per lane, the Q / dO fragments of its entries in registers), P, dS,
+// dQ += dS K, and adds dS into a register dbias tile.  Wave w + 4 hands its
+// dbias tile to wave w through LDS (a second barrier per tile), which adds
+// it and stores the tile (the first group) or adds it to dbias (later
+// groups): dbias = sum_b dS is written once per group, in a fixed order.
+// The tile loop is unrolled over the three buffers, so every LDS operand
+// address is a lane base plus an immediate offset.
 // ---------------------------------------------------------------------------
-constexpr int BGB = 4;   // batch entries per group (k_dqb)
-constexpr int NQB = 3;   // tile buffers (k_dqb)
+constexpr int BGB = 4;     // batch entries per group (k_dqb)
+constexpr int EPW = 2;     // entries per wave (k_dqb)
+constexpr int NQB = 3;     // tile buffers (k_dqb)
+constexpr int NTB = 512;   // threads per workgroup (k_dqb)
 
 template <int D>
 struct __attribute__((aligned(1024))) SmemDQB {
-  unsigned char kv[NQB][2 * BGB][BK3 * 2 * D];   // K then V tile of each entry, swizzled
-  float bias[NQB][BQ3 * BK3];                   // bias[i0 + r][j0 + c], 16-byte chunks swizzled by row
+  // K / V tiles, swizzled: [entry pair][buffer][entry of the pair][K, V]
+  // (one pair's tiles span 48 KB, inside the reach of an LDS offset field)
+  unsigned char kv[BGB / EPW][NQB][EPW][2][BK3 * 2 * D];
+  float bias[NQB][BQ3 * BK3];   // bias[i0 + r][j0 + c], 16-byte chunks swizzled by row
+  f32x4 x[4][4][64];            // handed-over dbias tiles: [row slot][chunk m][lane]
 };
+static_assert(sizeof(SmemDQB<64>) <= 160 * 1024, "k_dqb LDS");
 
 template <int D>
-__global__ __launch_bounds__(NT, 1) void k_dqb(Params p, BwdArgs a) {
+__global__ __launch_bounds__(NTB, 1) void k_dqb(Params p, BwdArgs a) {
   static_assert(D == 64, "head dim 64");
   constexpr int NS = D / 16;                 // k-steps over the head dim
   constexpr int NC = D / 32;                 // 32-column blocks of dQ
   constexpr int RB = Swz<D>::RB, CR = Swz<D>::CR;
   constexpr int TS = BK3 * 2 * D;            // K or V tile bytes
   constexpr int PER_T = BK3 * CR / 64;       // 1 KB loads per K or V tile
+  constexpr int BUF_B = EPW * 2 * TS;        // one buffer of an entry pair
+  constexpr int PAIR_B = NQB * BUF_B;        // an entry pair's region
   constexpr int BTB = BQ3 * BK3 * 4;         // bias tile bytes
-  constexpr int BIAS_OFF = NQB * 2 * BGB * TS;
-  static_assert(PER_T == 4 && BTB == 16384, "loads per wave: one entry's K and V, 32 bias rows");
+  constexpr int BIAS_OFF = (int)offsetof(SmemDQB<D>, bias);
+  static_assert(PER_T == 4 && BTB == 16384, "loads per wave: one K or V tile, 16 bias rows");
+  static_assert(PAIR_B <= 65536 && NQB * BTB <= 65536, "immediate LDS offsets");
   __shared__ SmemDQB<D> sm;
 
   const int tid = threadIdx.x, l = tid & 63, lr = l & 31, lg = l >> 5;
   const int w = __builtin_amdgcn_readfirstlane(tid >> 6);   // wave-uniform
+  const int ws = w & 3, half = w >> 2;                      // row slot, entry pair
   const BlockXYZ blk = xcd_block();
   const int i0 = blk.x * BQ3, h = blk.y, g = h / p.G;
   const Mask& msk = p.mask;
   const int Sq = p.Sq, Sk = p.Sk;
   if (i0 >= Sq) return;
-  const int irow = i0 + 32 * w + lr;   // this lane's query row
+  const int irow = i0 + 32 * ws + lr;   // this lane's query row
   const bool row_ok = irow < Sq;
   const float scale = p.scale, scale_log2 = p.scale * kLog2e, inv_scale = 1.f / p.scale;
 
@@ -1739,7 +1752,7 @@ __global__ __launch_bounds__(NT, 1) void k_dqb(Params p, BwdArgs a) {
   // window offset of key 4 lg (+ c) of a tile for this lane's row
   const int tq = (int)msk.k_off - (irow + (int)msk.q_off) - (int)msk.diag + 4 * lg - lo_l;
   const int sink_lim = (int)min<int64_t>(max<int64_t>(msk.n_sink - msk.k_off, 0), 0x3fffffff);
-  const int wr0 = i0 + 32 * w;
+  const int wr0 = i0 + 32 * ws;
   auto clamp_i = [](int64_t x) { return (int)max<int64_t>(min<int64_t>(x, 0x3fffffff), -0x3fffffff); };
   const int64_t band = (int64_t)wr0 + msk.q_off + msk.diag - msk.k_off;
   const int fl_hi = no_mask ? 0x3fffffff : clamp_i(band + msk.wr - 31);
@@ -1748,194 +1761,217 @@ __global__ __launch_bounds__(NT, 1) void k_dqb(Params p, BwdArgs a) {
   auto tile_full = [&](int j0) { return (j0 + BK3 <= Sk) & ((j0 < fl_sink) | ((j0 <= fl_hi) & (j0 >= fl_lo))); };
 
   const unsigned int sm_base = __builtin_amdgcn_readfirstlane(lds_addr(&sm));
-  const int k_rb = 2 * (int)p.k_str[2], v_rb = 2 * (int)p.v_str[2], b_rb = 4 * (int)p.bias_str[1];
+  const int b_rb = 4 * (int)p.bias_str[1];
   const int brows = min(Sq - i0, BQ3);
   const float* bias_h = a.bias + h * p.bias_str[0] + (int64_t)i0 * p.bias_str[1];
-  // staging: wave w loads entry w's K and V tiles (four 1 KB loads each, when
-  // the group has that entry) and bias rows 32 w .. 32 w + 31 (four 1 KB loads
-  // of 8 rows; 16-byte chunk c of row r lands at chunk c ^ (r % 8))
-  auto issue = [&](int it, int buf, int b0, int nb) {
+  // staging: wave w loads the K (w < 4) or V tile of entry w % 4 (four 1 KB
+  // loads, when the group has that entry) and bias rows 16 w .. 16 w + 15
+  // (two 1 KB loads of 8 rows; 16-byte chunk c of row r lands at chunk
+  // c ^ (r % 8))
+  const int64_t* kv_str = half == 0 ? p.k_str : p.v_str;
+  const int kv_rb = 2 * (int)kv_str[2];
+  const unsigned char* kv_head =
+      (const unsigned char*)((half == 0 ? (const unsigned short*)a.k : (const unsigned short*)a.v) + g * kv_str[1]);
+  const int64_t kv_bbytes = 2 * kv_str[0];
+  const unsigned int kv_dst = sm_base + (ws >> 1) * PAIR_B + (ws & 1) * 2 * TS + half * TS;
+  const unsigned char* kv_grp = kv_head;   // the group's entry ws
+  auto issue = [&](int it, int buf, int nb) {
     const int j0 = tile_of(it);
     const int keys = min(Sk - j0, BK3);
-    if (w < nb) {
-      const int b = b0 + w;
-      const unsigned short* kt = (const unsigned short*)a.k + b * p.k_str[0] + g * p.k_str[1] + (int64_t)j0 * p.k_str[2];
-      const unsigned short* vt = (const unsigned short*)a.v + b * p.v_str[0] + g * p.v_str[1] + (int64_t)j0 * p.v_str[2];
-      const __amdgpu_buffer_rsrc_t rk = buf_rsrc(kt, keys * k_rb), rv = buf_rsrc(vt, keys * v_rb);
+    if (ws < nb) {
+      const __amdgpu_buffer_rsrc_t rs = buf_rsrc(kv_grp + j0 * kv_rb, keys * kv_rb);
 #pragma unroll
       for (int k = 0; k < PER_T; ++k) {
         const int row = (64 * k + l) / CR, c = (l % CR) ^ Swz<D>::f(row);
-        lds_dma16(rk, __builtin_amdgcn_readfirstlane(sm_base + (buf * 2 * BGB + w) * TS + 1024 * k),
-                  row * k_rb + 16 * c);
-        lds_dma16(rv, __builtin_amdgcn_readfirstlane(sm_base + (buf * 2 * BGB + BGB + w) * TS + 1024 * k),
-                  row * v_rb + 16 * c);
+        lds_dma16(rs, __builtin_amdgcn_readfirstlane(kv_dst + buf * BUF_B + 1024 * k), row * kv_rb + 16 * c);
       }
     }
     const __amdgpu_buffer_rsrc_t rb_ = buf_rsrc(bias_h + j0, (brows - 1) * b_rb + 4 * keys);
 #pragma unroll
-    for (int k = 0; k < 4; ++k) {
-      const int row = 32 * w + 8 * k + (l >> 3), c = (l & 7) ^ (row & 7);
-      lds_dma16(rb_, __builtin_amdgcn_readfirstlane(sm_base + BIAS_OFF + buf * BTB + (32 * w + 8 * k) * 128),
+    for (int k = 0; k < 2; ++k) {
+      const int row = 16 * w + 8 * k + (l >> 3), c = (l & 7) ^ (row & 7);
+      lds_dma16(rb_, __builtin_amdgcn_readfirstlane(sm_base + BIAS_OFF + buf * BTB + (16 * w + 8 * k) * 128),
                 row * b_rb + 16 * c);
     }
   };
 
-  // operand read addresses (buffer 0, entry 0)
+  // operand lane addresses in this wave's pair region (buffer 0, entry 0's
+  // K tile); tiles are reached by immediate offsets
+  const unsigned int pair_base = sm_base + half * PAIR_B;
   const int a_lane = Swz<D>::a_lane(l), t_lane = Swz<D>::t_lane(l);
-  unsigned int br[NC];
+  unsigned int ka[NS], br[NC], br2[NC];
 #pragma unroll
-  for (int n = 0; n < NC; ++n) br[n] = sm_base + (t_lane ^ (64 * n));
-  const unsigned int ka = sm_base + a_lane;
-  // this lane's bias row, chunks 2 m + lg (keys 8 m + 4 lg + 0..3), swizzled
-  const int brow = 32 * w + lr;
-  const unsigned int b_lane = sm_base + BIAS_OFF + brow * 128;
+  for (int s = 0; s < NS; ++s) ka[s] = (pair_base + a_lane) ^ (32 * s);
+#pragma unroll
+  for (int n = 0; n < NC; ++n) {
+    br[n] = pair_base + (t_lane ^ (64 * n));
+    br2[n] = br[n] ^ 32;
+  }
+  // this lane's bias row: chunk 2 m + lg (keys 8 m + 4 lg + 0..3) sits at
+  // position (2 m + lg) ^ (row % 8), i.e. at  b_lane ^ (32 m)  (the row
+  // start is 128-byte aligned)
+  const int brow = 32 * ws + lr;
+  const unsigned int b_lane = sm_base + BIAS_OFF + brow * 128 + 16 * (lg ^ (brow & 1)) + 32 * ((brow >> 1) & 3);
+  unsigned int bl[4];
+#pragma unroll
+  for (int m = 0; m < 4; ++m) bl[m] = b_lane ^ (32 * m);
 
   float* dbias_h = a.dbias + h * p.bias_str[0] + (int64_t)i0 * p.bias_str[1];
-  const int db_off = (32 * w + lr) * b_rb + 16 * lg;   // this lane's row, keys 4 lg + 0..3 of a tile
+  const int db_off = brow * b_rb + 16 * lg;   // this lane's row, keys 4 lg + 0..3 of a tile
   for (int b0 = 0; b0 < p.B; b0 += BGB) {
     const int nb = min(BGB, p.B - b0);
     const bool first = b0 == 0;
-    // this group's Q / dO fragments (B operands, one query row per lane), LSE, delta
-    bf16x8 qB[BGB][NS], doB[BGB][NS];
-    float lse2[BGB], dls[BGB];
-    f32x16 dq[BGB][NC];
+    // this wave's entries of the group: 2 half + ee for ee < ne
+    const int ne = max(0, min(EPW, nb - 2 * half));
+    const bool hand = nb > 2;   // waves 4..7 have entries: their dbias tiles are handed over
+    bf16x8 qB[EPW][NS], doB[EPW][NS];
+    float lse2[EPW], dls[EPW];
+    f32x16 dq[EPW][NC];
 #pragma unroll
-    for (int e = 0; e < BGB; ++e) {
-      const int b = b0 + (e < nb ? e : 0);
+    for (int ee = 0; ee < EPW; ++ee) {
+      const int b = b0 + min(2 * half + ee, nb - 1);
       const int64_t ic = min(irow, Sq - 1);
       const unsigned short* q = (const unsigned short*)a.q + b * p.q_str[0] + h * p.q_str[1] + ic * p.q_str[2];
       const unsigned short* d = (const unsigned short*)a.dout + b * p.do_str[0] + h * p.do_str[1] + ic * p.do_str[2];
 #pragma unroll
       for (int s = 0; s < NS; ++s) {
-        qB[e][s] = as_bf16x8(*(const u16x8*)(q + 16 * s + 8 * lg));
-        doB[e][s] = as_bf16x8(*(const u16x8*)(d + 16 * s + 8 * lg));
+        qB[ee][s] = as_bf16x8(*(const u16x8*)(q + 16 * s + 8 * lg));
+        doB[ee][s] = as_bf16x8(*(const u16x8*)(d + 16 * s + 8 * lg));
       }
-      lse2[e] = INFINITY;
-      dls[e] = 0.f;
+      lse2[ee] = INFINITY;
+      dls[ee] = 0.f;
       if (row_ok) {
         const float lv = a.lse[((int64_t)b * p.Hq + h) * p.Sq + irow];
-        lse2[e] = (lv == -INFINITY) ? INFINITY : lv * kLog2e;
-        dls[e] = a.delta[((int64_t)b * p.Hq + h) * p.Sq + irow] * scale;
+        lse2[ee] = (lv == -INFINITY) ? INFINITY : lv * kLog2e;
+        dls[ee] = a.delta[((int64_t)b * p.Hq + h) * p.Sq + irow] * scale;
       }
 #pragma unroll
-      for (int n = 0; n < NC; ++n) dq[e][n] = zero16();
+      for (int n = 0; n < NC; ++n) dq[ee][n] = zero16();
     }
+    kv_grp = kv_head + (b0 + ws) * kv_bbytes;
     wait_vm_loads();
     __syncthreads();   // the previous group's readers of the tile buffers are done
     if (n_it > 0) {
-      issue(0, 0, b0, nb);
-      if (n_it > 1) issue(1, 1, b0, nb);
+      issue(0, 0, nb);
+      if (n_it > 1) issue(1, 1, nb);
     }
-    const int ni = (w < nb ? 2 * PER_T : 0) + 4;   // this wave's loads per tile
+    const int ni = (ws < nb ? PER_T : 0) + 2;   // this wave's loads per tile
     if (n_it > 1) wait_vm(ni);
     else wait_vm(0);
-    for (int t = 0; t < n_it; ++t) {
-      const int buf = t % NQB;
+
+    // tile t in buffer J
+    auto tile = [&](int t, auto Jc) {
+      constexpr int J = decltype(Jc)::value;
       __syncthreads();   // tile t complete for every wave; tile t - 1's buffer free
-      if (t + 2 < n_it) issue(t + 2, (t + 2) % NQB, b0, nb);
+      if (t + 2 < n_it) issue(t + 2, (J + 2) % NQB, nb);
       const int j0 = tile_of(t);
       const bool full = tile_full(j0);
+      const int tb = tq + j0;
       float db[16];
 #pragma unroll
       for (int r = 0; r < 16; ++r) db[r] = 0.f;
-      const int tb = tq + j0;
 #pragma unroll
-      for (int e = 0; e < BGB; ++e) {
-        if (e >= nb) break;
-        const unsigned int kt = (buf * 2 * BGB + e) * TS, vt = (buf * 2 * BGB + BGB + e) * TS;
+      for (int ee = 0; ee < EPW; ++ee) {
+        if (ee >= ne) break;
+        constexpr int kt0 = J * BUF_B;
+        const int kt = kt0 + ee * 2 * TS, vt = kt + TS;
         // S^T starts from bias / scale (this lane's row, keys 8 m + 4 lg + 0..3),
         // so the chain ends at (S scale + bias) / scale
         f32x16 sacc, pacc = zero16();
 #pragma unroll
         for (int m = 0; m < 4; ++m) {
-          const f32x4 bz = *(const __attribute__((address_space(3))) f32x4*)(size_t)(
-              b_lane + buf * BTB + 16 * ((2 * m + lg) ^ (brow & 7)));
+          const f32x4 v = *(const __attribute__((address_space(3))) f32x4*)(size_t)(bl[m] + J * BTB);
 #pragma unroll
-          for (int c = 0; c < 4; ++c) sacc[4 * m + c] = bz[c] * inv_scale;
+          for (int c = 0; c < 4; ++c) sacc[4 * m + c] = v[c] * inv_scale;
         }
 #pragma unroll
         for (int s = 0; s < NS; ++s) {
-          sacc = mfma(lds_b128_at((ka ^ (32 * s)) + kt), qB[e][s], sacc);
-          pacc = mfma(lds_b128_at((ka ^ (32 * s)) + vt), doB[e][s], pacc);
+          sacc = mfma(lds_b128_at(ka[s] + kt), qB[ee][s], sacc);
+          pacc = mfma(lds_b128_at(ka[s] + vt), doB[ee][s], pacc);
         }
         float dsv[16];
 #pragma unroll
         for (int r = 0; r < 16; ++r) {
           const int c = 8 * (r >> 2) + (r & 3);   // key 4 lg + c of the tile
-          float pp = __builtin_amdgcn_exp2f(fmaf(sacc[r], scale_log2, -lse2[e]));
+          float pp = __builtin_amdgcn_exp2f(fmaf(sacc[r], scale_log2, -lse2[ee]));
           if (!full) {
             const int jj = j0 + 4 * lg + c;
             const bool ok = (jj < Sk) & (((unsigned int)(tb + c) <= (unsigned int)span) | (jj < sink_lim));
             pp = ok ? pp : 0.f;
           }
-          dsv[r] = pp * fmaf(pacc[r], scale, -dls[e]);
+          dsv[r] = pp * fmaf(pacc[r], scale, -dls[ee]);
           db[r] += dsv[r];
         }
         const bf16x8 A0 = pack8(dsv), A1 = pack8(dsv + 8);
 #pragma unroll
         for (int i = 0; i < NS; ++i) {
           const int n = i % NC, r0 = 16 * (i / NC);
-          const bf16x8 bq = cat44(lds_tr4_at(br[n] + kt + r0 * RB), lds_tr4_at((br[n] ^ 32) + kt + (r0 + 8) * RB));
-          dq[e][n] = mfma(i < NC ? A0 : A1, bq, dq[e][n]);
+          const bf16x8 bq = cat44(lds_tr4_at(br[n] + kt + r0 * RB), lds_tr4_at(br2[n] + kt + (r0 + 8) * RB));
+          dq[ee][n] = mfma(i < NC ? A0 : A1, bq, dq[ee][n]);
         }
       }
-      // dbias of this tile (unscaled dS summed over the group): this lane's
-      // row, keys j0 + 8 m + 4 lg + 0..3.  A whole key tile is stored by four
-      // buffer stores from every lane (rows past the end fall outside the
-      // resource and are dropped), so the count of memory operations is the
-      // same in every wave; the ragged last tile stores lane by lane.
+      if (half == 1 && hand) {
+#pragma unroll
+        for (int m = 0; m < 4; ++m) sm.x[ws][m][l] = f32x4{db[4 * m], db[4 * m + 1], db[4 * m + 2], db[4 * m + 3]};
+      }
+      __syncthreads();   // the handed-over tiles are in LDS
       const bool whole = j0 + BK3 <= Sk;
-      if (whole) {
-        const __amdgpu_buffer_rsrc_t rd = buf_rsrc(dbias_h + j0, (brows - 1) * b_rb + 4 * BK3);
+      if (half == 0) {
+        if (hand) {
 #pragma unroll
-        for (int m = 0; m < 4; ++m) {
-          f32x4 v = {db[4 * m] * inv_scale, db[4 * m + 1] * inv_scale, db[4 * m + 2] * inv_scale,
-                     db[4 * m + 3] * inv_scale};
-          if (!first) v += __builtin_bit_cast(f32x4, __builtin_amdgcn_raw_buffer_load_b128(rd, db_off + 32 * m, 0, 0));
-          __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u32x4, v), rd, db_off + 32 * m, 0, 0);
+          for (int m = 0; m < 4; ++m) {
+            const f32x4 v = sm.x[ws][m][l];
+#pragma unroll
+            for (int c = 0; c < 4; ++c) db[4 * m + c] += v[c];
+          }
         }
-      } else if (row_ok) {
+        // dbias of this tile (unscaled dS summed over the group): this lane's
+        // row, keys j0 + 8 m + 4 lg + 0..3.  A whole key tile is stored by
+        // four buffer stores from every lane (rows past the end fall outside
+        // the resource and are dropped), so the count of memory operations
+        // is the same in every such wave; the ragged last tile stores the
+        // chunks inside the problem only.
+        const __amdgpu_buffer_rsrc_t rd = buf_rsrc(dbias_h + j0, (brows - 1) * b_rb + 4 * min(BK3, Sk - j0));
 #pragma unroll
         for (int m = 0; m < 4; ++m) {
-          const int j = j0 + 8 * m + 4 * lg;
-          if (j < Sk) {
-            f32x4* dst = (f32x4*)(dbias_h + (int64_t)(irow - i0) * p.bias_str[1] + j);
+          if (whole || (row_ok && j0 + 8 * m + 4 * lg < Sk)) {
             f32x4 v = {db[4 * m] * inv_scale, db[4 * m + 1] * inv_scale, db[4 * m + 2] * inv_scale,
                        db[4 * m + 3] * inv_scale};
-            if (!first) v += *dst;
-            *dst = v;
+            if (!first) v += __builtin_bit_cast(f32x4, __builtin_amdgcn_raw_buffer_load_b128(rd, db_off + 32 * m, 0, 0));
+            __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u32x4, v), rd, db_off + 32 * m, 0, 0);
           }
         }
       }
       // Tile t + 1 complete before the next barrier (tile t + 2 may stay in
-      // flight).  Behind tile t + 1's loads come the dbias stores of tile t - 1,
-      // tile t + 2's loads and this tile's dbias stores (vector memory
-      // operations complete in issue order).
-      if (t + 2 < n_it && whole && first) {
-        if (t > 0) {
-          if (ni == 12) wait_vm_n<20>();
-          else wait_vm_n<12>();
-        } else {
-          if (ni == 12) wait_vm_n<16>();
-          else wait_vm_n<8>();
-        }
-      } else {
-        wait_vm_n<0>();
-      }
+      // flight).  Behind tile t + 1's loads come, in waves 0..3, the dbias
+      // stores of tile t - 1, then tile t + 2's loads and this tile's dbias
+      // stores (vector memory operations complete in issue order).  Only the
+      // last tile can be ragged, so tile t - 1 was whole here.
+      if (t + 2 < n_it && whole && first) wait_vm((half == 0 ? (t > 0 ? 8 : 4) : 0) + ni);
+      else wait_vm(0);
+    };
+    int t = 0;
+    for (; t + NQB <= n_it; t += NQB) {
+      tile(t, std::integral_constant<int, 0>{});
+      tile(t + 1, std::integral_constant<int, 1>{});
+      tile(t + 2, std::integral_constant<int, 2>{});
     }
-    // dQ of the group: rows i0 + 32 w + crow(r, lg), columns 32 n + lane
+    if (t < n_it) tile(t, std::integral_constant<int, 0>{});
+    if (t + 1 < n_it) tile(t + 1, std::integral_constant<int, 1>{});
+
+    // dQ of this wave's entries: rows i0 + 32 ws + crow(r, lg), columns 32 n + lane
 #pragma unroll
-    for (int e = 0; e < BGB; ++e) {
-      if (e >= nb) break;
-      float* dqp = a.dq + (b0 + e) * p.dq_str[0] + h * p.dq_str[1];
+    for (int ee = 0; ee < EPW; ++ee) {
+      if (ee >= ne) break;
+      float* dqp = a.dq + (b0 + 2 * half + ee) * p.dq_str[0] + h * p.dq_str[1];
 #pragma unroll
       for (int n = 0; n < NC; ++n) {
 #pragma unroll
         for (int r = 0; r < 16; ++r) {
-          const int64_t i = i0 + 32 * w + crow(r, lg);
+          const int64_t i = i0 + 32 * ws + crow(r, lg);
           if (i < Sq) {
             float* dst = dqp + i * p.dq_str[2] + 32 * n + lr;
-            *dst = a.accumulate_dq ? *dst + dq[e][n][r] : dq[e][n][r];
+            *dst = a.accumulate_dq ? *dst + dq[ee][n][r] : dq[ee][n][r];
           }
         }
       }
@@ -1952,7 +1988,7 @@ hipError_t launch_dq(const Params& p, const BwdArgs& a0, const ZeroMulti& zm, co
   BwdArgs a = a0;
   a.xmajor = xmajor_fits(p, grid.y, grid.z) ? 1 : 0;
   if (a.bias && a.dbias && D == 64)   // dQ and dbias, the batch walked inside
-    hipLaunchKernelGGL((k_dqb<64>), dim3(grid.x, grid.y, 1), dim3(NT), 0, st, p, a);
+    hipLaunchKernelGGL((k_dqb<64>), dim3(grid.x, grid.y, 1), dim3(NTB), 0, st, p, a);
   else if (a.bias)
     hipLaunchKernelGGL((k_dq<D, true>), grid, dim3(NT), 0, st, p, a);
   else
