@@ -103,15 +103,18 @@ __global__ __launch_bounds__(256) void k_delta_scalar(const OT* __restrict__ o,
 
 // dsinks[h] = -sum_{b,i} exp(sink_h - lse[b,h,i]) * delta[b,h,i]
 // (CANN sparse_flash_mla_grad Phase 3 dSinks reduced over rows and batch).
-// One block per head; fixed-order strided partial sums and a fixed tree, so
-// the result does not depend on scheduling.
-__global__ __launch_bounds__(256) void k_dsinks(const float* __restrict__ lse,
-                                                const float* __restrict__ delta,
-                                                const float* __restrict__ sinks,
-                                                float* __restrict__ dsinks, int B, int H, int Sq,
-                                                Packed pk) {
-  __shared__ float red[256];
-  const int h = blockIdx.x;
+// One block of DS_NT threads per head; each thread sums the rows
+// i = t + DS_NT k in a fixed order, with DS_U rows' loads in flight before
+// their use, then a fixed tree adds the threads' sums: the result does not
+// depend on scheduling.
+constexpr int DS_NT = 1024, DS_U = 4;
+__global__ __launch_bounds__(DS_NT) void k_dsinks(const float* __restrict__ lse,
+                                                  const float* __restrict__ delta,
+                                                  const float* __restrict__ sinks,
+                                                  float* __restrict__ dsinks, int B, int H, int Sq,
+                                                  Packed pk) {
+  __shared__ float red[DS_NT];
+  const int h = blockIdx.x, t = threadIdx.x;
   const float s = sinks[h];
   float acc = 0.f;
   for (int b = 0; b < B; ++b) {
@@ -119,18 +122,26 @@ __global__ __launch_bounds__(256) void k_dsinks(const float* __restrict__ lse,
     const float* d = delta + ((int64_t)b * H + h) * Sq;
     int64_t r0;
     const int n = pk.cu ? packed_seq(pk, b, Sq, &r0) : Sq;   // rows of this sequence
-    for (int i = threadIdx.x; i < n; i += 256) {
-      const float li = l[i];
-      if (li != -INFINITY) acc += expf(s - li) * d[i];
+    for (int i0 = t; i0 < n; i0 += DS_NT * DS_U) {
+      float lv[DS_U], dv[DS_U];
+#pragma unroll
+      for (int u = 0; u < DS_U; ++u) {
+        const int i = i0 + DS_NT * u;
+        lv[u] = i < n ? l[i] : -INFINITY;
+        dv[u] = i < n ? d[i] : 0.f;
+      }
+#pragma unroll
+      for (int u = 0; u < DS_U; ++u)
+        if (lv[u] != -INFINITY) acc += expf(s - lv[u]) * dv[u];
     }
   }
-  red[threadIdx.x] = acc;
+  red[t] = acc;
   __syncthreads();
-  for (int w = 128; w > 0; w >>= 1) {
-    if (threadIdx.x < w) red[threadIdx.x] += red[threadIdx.x + w];
+  for (int w = DS_NT / 2; w > 0; w >>= 1) {
+    if (t < w) red[t] += red[t + w];
     __syncthreads();
   }
-  if (threadIdx.x == 0) dsinks[h] = -red[0];
+  if (t == 0) dsinks[h] = -red[0];
 }
 
 static unsigned fill_blocks(int64_t n) {
@@ -292,7 +303,7 @@ hipError_t launch_delta(const void* o, int o_bf16, const void* dout, int do_bf16
 
 hipError_t launch_dsinks(const float* lse, const float* delta, const float* sinks, float* dsinks,
                          int B, int H, int Sq, Packed pk, hipStream_t st) {
-  hipLaunchKernelGGL(k_dsinks, dim3(H), dim3(256), 0, st, lse, delta, sinks, dsinks, B, H, Sq, pk);
+  hipLaunchKernelGGL(k_dsinks, dim3(H), dim3(DS_NT), 0, st, lse, delta, sinks, dsinks, B, H, Sq, pk);
   return hipGetLastError();
 }
 

@@ -532,7 +532,9 @@ __global__ __launch_bounds__(NT2) void k_dkdv2(Params p, BwdArgs a, DkdvGrid gd)
   const int w = __builtin_amdgcn_readfirstlane(tid >> 6);   // wave-uniform
   const int pr = w & 3;               // pair: keys [32 pr, 32 pr + 32) of the block
   const bool sw = w < 4;              // S wave (else dP wave)
-  const BlockXYZ blk = xcd_block();
+  // with a bias (shared over the batch) the batch entries of a unit run side
+  // by side, so each bias tile comes from HBM about once
+  const BlockXYZ blk = BIAS ? xcd_block_zfast() : xcd_block();
   const int b = blk.z;
   const SeqView sv = seq_view(p, b);   // this batch entry (or packed sequence)
   const Mask& msk = sv.mask;
@@ -1767,7 +1769,9 @@ __global__ __launch_bounds__(NTB, 1) void k_dqb(Params p, BwdArgs a) {
   // staging: wave w loads the K (w < 4) or V tile of entry w % 4 (four 1 KB
   // loads, when the group has that entry) and bias rows 16 w .. 16 w + 15
   // (two 1 KB loads of 8 rows; 16-byte chunk c of row r lands at chunk
-  // c ^ (r % 8))
+  // c ^ ((r / 2) % 8): a 128-byte row covers half the banks, row parity picks
+  // the half, and the 16 rows that one read serves at a time fall on
+  // distinct banks)
   const int64_t* kv_str = half == 0 ? p.k_str : p.v_str;
   const int kv_rb = 2 * (int)kv_str[2];
   const unsigned char* kv_head =
@@ -1789,9 +1793,21 @@ __global__ __launch_bounds__(NTB, 1) void k_dqb(Params p, BwdArgs a) {
     const __amdgpu_buffer_rsrc_t rb_ = buf_rsrc(bias_h + j0, (brows - 1) * b_rb + 4 * keys);
 #pragma unroll
     for (int k = 0; k < 2; ++k) {
-      const int row = 16 * w + 8 * k + (l >> 3), c = (l & 7) ^ (row & 7);
+      const int row = 16 * w + 8 * k + (l >> 3), c = (l & 7) ^ ((row >> 1) & 7);
       lds_dma16(rb_, __builtin_amdgcn_readfirstlane(sm_base + BIAS_OFF + buf * BTB + (16 * w + 8 * k) * 128),
                 row * b_rb + 16 * c);
+    }
+  };
+
+  // bias / scale in place: each wave scales the 16 rows it loaded itself
+  // (complete once its own loads are), before the barrier that publishes them
+  typedef __attribute__((address_space(3))) f32x4 lds_f32x4;
+  auto scale_bias = [&](int buf) {
+    const unsigned int o = sm_base + BIAS_OFF + buf * BTB + 16 * w * 128 + 16 * l;
+#pragma unroll
+    for (int k = 0; k < 2; ++k) {
+      lds_f32x4* x = (lds_f32x4*)(size_t)(o + 1024 * k);
+      *x = *x * inv_scale;
     }
   };
 
@@ -1808,10 +1824,11 @@ __global__ __launch_bounds__(NTB, 1) void k_dqb(Params p, BwdArgs a) {
     br2[n] = br[n] ^ 32;
   }
   // this lane's bias row: chunk 2 m + lg (keys 8 m + 4 lg + 0..3) sits at
-  // position (2 m + lg) ^ (row % 8), i.e. at  b_lane ^ (32 m)  (the row
-  // start is 128-byte aligned)
+  // position (2 m + lg) ^ ((row / 2) % 8), i.e. at  b_lane ^ (32 m)  (the
+  // row start is 128-byte aligned)
   const int brow = 32 * ws + lr;
-  const unsigned int b_lane = sm_base + BIAS_OFF + brow * 128 + 16 * (lg ^ (brow & 1)) + 32 * ((brow >> 1) & 3);
+  const unsigned int b_lane =
+      sm_base + BIAS_OFF + brow * 128 + 16 * (lg ^ ((brow >> 1) & 1)) + 32 * ((brow >> 2) & 3);
   unsigned int bl[4];
 #pragma unroll
   for (int m = 0; m < 4; ++m) bl[m] = b_lane ^ (32 * m);
@@ -1825,7 +1842,7 @@ __global__ __launch_bounds__(NTB, 1) void k_dqb(Params p, BwdArgs a) {
     const int ne = max(0, min(EPW, nb - 2 * half));
     const bool hand = nb > 2;   // waves 4..7 have entries: their dbias tiles are handed over
     bf16x8 qB[EPW][NS], doB[EPW][NS];
-    float lse2[EPW], dls[EPW];
+    float lse2[EPW], ndl[EPW];   // LSE * log2(e) and -delta of this lane's row
     f32x16 dq[EPW][NC];
 #pragma unroll
     for (int ee = 0; ee < EPW; ++ee) {
@@ -1839,11 +1856,11 @@ __global__ __launch_bounds__(NTB, 1) void k_dqb(Params p, BwdArgs a) {
         doB[ee][s] = as_bf16x8(*(const u16x8*)(d + 16 * s + 8 * lg));
       }
       lse2[ee] = INFINITY;
-      dls[ee] = 0.f;
+      ndl[ee] = 0.f;
       if (row_ok) {
         const float lv = a.lse[((int64_t)b * p.Hq + h) * p.Sq + irow];
         lse2[ee] = (lv == -INFINITY) ? INFINITY : lv * kLog2e;
-        dls[ee] = a.delta[((int64_t)b * p.Hq + h) * p.Sq + irow] * scale;
+        ndl[ee] = -a.delta[((int64_t)b * p.Hq + h) * p.Sq + irow];
       }
 #pragma unroll
       for (int n = 0; n < NC; ++n) dq[ee][n] = zero16();
@@ -1858,6 +1875,7 @@ __global__ __launch_bounds__(NTB, 1) void k_dqb(Params p, BwdArgs a) {
     const int ni = (ws < nb ? PER_T : 0) + 2;   // this wave's loads per tile
     if (n_it > 1) wait_vm(ni);
     else wait_vm(0);
+    if (n_it > 0) scale_bias(0);
 
     // tile t in buffer J
     auto tile = [&](int t, auto Jc) {
@@ -1875,14 +1893,15 @@ __global__ __launch_bounds__(NTB, 1) void k_dqb(Params p, BwdArgs a) {
         if (ee >= ne) break;
         constexpr int kt0 = J * BUF_B;
         const int kt = kt0 + ee * 2 * TS, vt = kt + TS;
-        // S^T starts from bias / scale (this lane's row, keys 8 m + 4 lg + 0..3),
-        // so the chain ends at (S scale + bias) / scale
+        // S^T starts from bias / scale (this lane's row, keys 8 m + 4 lg + 0..3;
+        // the tile holds bias / scale), so the chain ends at (S scale + bias) /
+        // scale
         f32x16 sacc, pacc = zero16();
 #pragma unroll
         for (int m = 0; m < 4; ++m) {
           const f32x4 v = *(const __attribute__((address_space(3))) f32x4*)(size_t)(bl[m] + J * BTB);
 #pragma unroll
-          for (int c = 0; c < 4; ++c) sacc[4 * m + c] = v[c] * inv_scale;
+          for (int c = 0; c < 4; ++c) sacc[4 * m + c] = v[c];
         }
 #pragma unroll
         for (int s = 0; s < NS; ++s) {
@@ -1891,15 +1910,20 @@ __global__ __launch_bounds__(NTB, 1) void k_dqb(Params p, BwdArgs a) {
         }
         float dsv[16];
 #pragma unroll
-        for (int r = 0; r < 16; ++r) {
-          const int c = 8 * (r >> 2) + (r & 3);   // key 4 lg + c of the tile
-          float pp = __builtin_amdgcn_exp2f(fmaf(sacc[r], scale_log2, -lse2[ee]));
-          if (!full) {
+        for (int r = 0; r < 16; ++r) dsv[r] = __builtin_amdgcn_exp2f(fmaf(sacc[r], scale_log2, -lse2[ee]));
+        if (!full) {   // (one branch, touching P only)
+#pragma unroll
+          for (int r = 0; r < 16; ++r) {
+            const int c = 8 * (r >> 2) + (r & 3);   // key 4 lg + c of the tile
             const int jj = j0 + 4 * lg + c;
             const bool ok = (jj < Sk) & (((unsigned int)(tb + c) <= (unsigned int)span) | (jj < sink_lim));
-            pp = ok ? pp : 0.f;
+            dsv[r] = ok ? dsv[r] : 0.f;
           }
-          dsv[r] = pp * fmaf(pacc[r], scale, -dls[ee]);
+        }
+        // dS = P (dP - delta), unscaled (dQ takes the scale once at the end)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+          dsv[r] *= pacc[r] + ndl[ee];
           db[r] += dsv[r];
         }
         const bf16x8 A0 = pack8(dsv), A1 = pack8(dsv + 8);
@@ -1935,8 +1959,7 @@ __global__ __launch_bounds__(NTB, 1) void k_dqb(Params p, BwdArgs a) {
 #pragma unroll
         for (int m = 0; m < 4; ++m) {
           if (whole || (row_ok && j0 + 8 * m + 4 * lg < Sk)) {
-            f32x4 v = {db[4 * m] * inv_scale, db[4 * m + 1] * inv_scale, db[4 * m + 2] * inv_scale,
-                       db[4 * m + 3] * inv_scale};
+            f32x4 v = {db[4 * m], db[4 * m + 1], db[4 * m + 2], db[4 * m + 3]};
             if (!first) v += __builtin_bit_cast(f32x4, __builtin_amdgcn_raw_buffer_load_b128(rd, db_off + 32 * m, 0, 0));
             __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u32x4, v), rd, db_off + 32 * m, 0, 0);
           }
@@ -1949,6 +1972,7 @@ __global__ __launch_bounds__(NTB, 1) void k_dqb(Params p, BwdArgs a) {
       // last tile can be ragged, so tile t - 1 was whole here.
       if (t + 2 < n_it && whole && first) wait_vm((half == 0 ? (t > 0 ? 8 : 4) : 0) + ni);
       else wait_vm(0);
+      if (t + 1 < n_it) scale_bias((J + 1) % NQB);   // (own rows of tile t + 1, complete)
     };
     int t = 0;
     for (; t + NQB <= n_it; t += NQB) {
@@ -1971,7 +1995,8 @@ __global__ __launch_bounds__(NTB, 1) void k_dqb(Params p, BwdArgs a) {
           const int64_t i = i0 + 32 * ws + crow(r, lg);
           if (i < Sq) {
             float* dst = dqp + i * p.dq_str[2] + 32 * n + lr;
-            *dst = a.accumulate_dq ? *dst + dq[ee][n][r] : dq[ee][n][r];
+            const float v = dq[ee][n][r] * scale;
+            *dst = a.accumulate_dq ? *dst + v : v;
           }
         }
       }

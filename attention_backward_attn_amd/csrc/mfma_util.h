@@ -231,6 +231,20 @@ __device__ inline BlockXYZ xcd_block() {
   return {L - zy * nx, zy / nz, zy % nz};
 }
 
+// As xcd_block, with the logical order batch (z) fastest, then x, then y:
+// the batch entries of one (x, y) unit run side by side on one XCD, so
+// tensors broadcast over the batch (a bias) are read from its L2 by all of
+// them at about the same time.
+__device__ inline BlockXYZ xcd_block_zfast() {
+  const int nx = gridDim.x, ny = gridDim.y, nz = gridDim.z;
+  const int n = nx * ny * nz;
+  const int id = blockIdx.x + nx * (blockIdx.y + ny * blockIdx.z);
+  const int q = n >> 3, r = n & 7, k = id & 7;
+  const int L = k * q + min(k, r) + (id >> 3);
+  const int xy = L / nz;
+  return {xy % nx, xy / nx, L - xy * nz};
+}
+
 // As xcd_block, for grids whose x index ranks the blocks by work (heaviest
 // first): when the (y, z) units divide evenly over the XCDs, XCD k takes
 // units [k U / 8, (k + 1) U / 8) (their K / V stay in its L2) and walks them
