@@ -1373,6 +1373,20 @@ __global__ __launch_bounds__(NT, 2) void k_dq2(Params p, BwdArgs a, ZeroMulti zm
     zero_share();
     return;
   }
+  // key tiles: the sink tiles [0, a1) and the band tiles [a2, a3)
+  int64_t s_hi, b_lo, b_hi;
+  const int i1 = min(i0 + BQ3, Sq);
+  msk.keys_for_rows(i0, i1, Sk, &s_hi, &b_lo, &b_hi);
+  const int a1 = (int)((s_hi + BK3 - 1) / BK3);
+  int a2 = (int)(b_lo / BK3);
+  const int a3 = b_hi > b_lo ? (int)((b_hi + BK3 - 1) / BK3) : a2;
+  if (a2 < a1) a2 = a1;
+  const int n1 = a1, n2 = a3 > a2 ? a3 - a2 : 0;
+  const int n_it = n1 + n2;
+  if (n_it == 0 && a.accumulate_dq) {   // no key reaches these rows: dQ keeps its values
+    zero_share();
+    return;
+  }
   const int irow = i0 + 32 * w + lr;           // this lane's query row
   const float scale = p.scale, scale_log2 = p.scale * kLog2e;
 
@@ -1398,16 +1412,6 @@ __global__ __launch_bounds__(NT, 2) void k_dq2(Params p, BwdArgs a, ZeroMulti zm
   }
   wait_vm_loads();
 
-  // key tiles: the sink tiles [0, a1) and the band tiles [a2, a3)
-  int64_t s_hi, b_lo, b_hi;
-  const int i1 = min(i0 + BQ3, Sq);
-  msk.keys_for_rows(i0, i1, Sk, &s_hi, &b_lo, &b_hi);
-  const int a1 = (int)((s_hi + BK3 - 1) / BK3);
-  int a2 = (int)(b_lo / BK3);
-  const int a3 = b_hi > b_lo ? (int)((b_hi + BK3 - 1) / BK3) : a2;
-  if (a2 < a1) a2 = a1;
-  const int n1 = a1, n2 = a3 > a2 ? a3 - a2 : 0;
-  const int n_it = n1 + n2;
   auto tile_of = [&](int it) { return BK3 * (it < n1 ? it : a2 + (it - n1)); };
   // this wave's rows: a tile [j0, j0 + 32) is full when every key is
   // allowed for all 32 rows
@@ -1680,62 +1684,57 @@ __global__ __launch_bounds__(NT, 2) void k_dq2(Params p, BwdArgs a, ZeroMulti zm
 
 // ---------------------------------------------------------------------------
 // Kernel k_dqb (dQ and dbias, head dim 64): one workgroup of eight waves per
-// (128-row block, query head), two waves per SIMD.  Waves w and w + 4 own
-// rows 32 (w % 4) .. 32 (w % 4) + 31.  The batch is walked innermost, in
-// groups of up to BGB entries, wave w taking entries 2 (w / 4) and
-// 2 (w / 4) + 1 of the group.  For each key tile the workgroup stages the
-// group's K / V tiles and the [128 x 32] fp32 bias tile (one copy for all
+// (128-row block, query head), two waves per SIMD; wave w owns rows
+// 16 w .. 16 w + 15 for every batch entry.  The batch is walked innermost,
+// in groups of up to BGB entries.  For each 32-key tile the workgroup stages
+// the group's K / V tiles and the [128 x 32] fp32 bias tile (one copy for all
 // entries: the bias is shared over the batch) straight into LDS, two tiles
-// ahead; each wave forms, entry by entry, S^T = K Q^T (the chain starting
-// from bias / scale) and dP^T = V dO^T (keys on accumulator rows, one query
-// row per lane, the Q / dO fragments of its entries in registers), P, dS,
-// dQ += dS K, and adds dS into a register dbias tile.  Wave w + 4 hands its
-// dbias tile to wave w through LDS (a second barrier per tile), which adds
-// it and stores the tile (the first group) or adds it to dbias (later
-// groups): dbias = sum_b dS is written once per group, in a fixed order.
-// The tile loop is unrolled over the three buffers, so every LDS operand
-// address is a lane base plus an immediate offset.
+// ahead, and each wave, entry by entry, forms S^T = K Q^T (16x16x32 products;
+// the chain starts from bias / scale) and dP^T = V dO^T (keys on accumulator
+// rows, one query row per lane, the Q / dO fragments of the group's entries
+// in registers), P, dS, dQ += dS K, and adds dS into a register dbias tile,
+// which it stores (the first group) or adds to dbias (later groups) once per
+// tile: dbias = sum_b dS is written once per group, in a fixed order.  A
+// lane holds keys 4 g + 0..3 and 16 + 4 g + 0..3 (g = lane / 16) of its row:
+// two 16-byte chunks of the bias and dbias rows, and directly the eight
+// reduction slots of its dQ = dS K operand.  A group with fewer than BGB
+// entries fills the rest with copies of its last entry whose P is zero.
 // ---------------------------------------------------------------------------
 constexpr int BGB = 4;     // batch entries per group (k_dqb)
-constexpr int EPW = 2;     // entries per wave (k_dqb)
 constexpr int NQB = 3;     // tile buffers (k_dqb)
 constexpr int NTB = 512;   // threads per workgroup (k_dqb)
+struct DbTile {   // a lane's two dbias chunks of a tile
+  f32x4 c0, c1;
+};
 
 template <int D>
 struct __attribute__((aligned(1024))) SmemDQB {
-  // K / V tiles, swizzled: [entry pair][buffer][entry of the pair][K, V]
-  // (one pair's tiles span 48 KB, inside the reach of an LDS offset field)
-  unsigned char kv[BGB / EPW][NQB][EPW][2][BK3 * 2 * D];
-  float bias[NQB][BQ3 * BK3];   // bias[i0 + r][j0 + c], 16-byte chunks swizzled by row
-  f32x4 x[4][4][64];            // handed-over dbias tiles: [row slot][chunk m][lane]
+  unsigned char kv[NQB][BGB][2][BK3 * 2 * D];   // K then V tile of each entry, swizzled
+  float bias[NQB][BQ3 * BK3];                   // bias[i0 + r][j0 + c] / scale, 16-byte chunks swizzled by row
 };
 static_assert(sizeof(SmemDQB<64>) <= 160 * 1024, "k_dqb LDS");
 
 template <int D>
 __global__ __launch_bounds__(NTB, 1) void k_dqb(Params p, BwdArgs a) {
   static_assert(D == 64, "head dim 64");
-  constexpr int NS = D / 16;                 // k-steps over the head dim
-  constexpr int NC = D / 32;                 // 32-column blocks of dQ
   constexpr int RB = Swz<D>::RB, CR = Swz<D>::CR;
   constexpr int TS = BK3 * 2 * D;            // K or V tile bytes
   constexpr int PER_T = BK3 * CR / 64;       // 1 KB loads per K or V tile
-  constexpr int BUF_B = EPW * 2 * TS;        // one buffer of an entry pair
-  constexpr int PAIR_B = NQB * BUF_B;        // an entry pair's region
+  constexpr int BUF_B = BGB * 2 * TS;        // one buffer of K / V tiles
   constexpr int BTB = BQ3 * BK3 * 4;         // bias tile bytes
   constexpr int BIAS_OFF = (int)offsetof(SmemDQB<D>, bias);
-  static_assert(PER_T == 4 && BTB == 16384, "loads per wave: one K or V tile, 16 bias rows");
-  static_assert(PAIR_B <= 65536 && NQB * BTB <= 65536, "immediate LDS offsets");
+  constexpr int NI = PER_T + 2;              // loads per wave per tile
+  static_assert(PER_T == 4 && BTB == 16384 && RB == 128, "one K or V tile and 16 bias rows per wave");
   __shared__ SmemDQB<D> sm;
 
-  const int tid = threadIdx.x, l = tid & 63, lr = l & 31, lg = l >> 5;
+  const int tid = threadIdx.x, l = tid & 63, j = l & 15, g = l >> 4;
   const int w = __builtin_amdgcn_readfirstlane(tid >> 6);   // wave-uniform
-  const int ws = w & 3, half = w >> 2;                      // row slot, entry pair
   const BlockXYZ blk = xcd_block();
-  const int i0 = blk.x * BQ3, h = blk.y, g = h / p.G;
+  const int i0 = blk.x * BQ3, h = blk.y, hk = h / p.G;
   const Mask& msk = p.mask;
   const int Sq = p.Sq, Sk = p.Sk;
   if (i0 >= Sq) return;
-  const int irow = i0 + 32 * ws + lr;   // this lane's query row
+  const int irow = i0 + 16 * w + j;   // this lane's query row
   const bool row_ok = irow < Sq;
   const float scale = p.scale, scale_log2 = p.scale * kLog2e, inv_scale = 1.f / p.scale;
 
@@ -1751,14 +1750,16 @@ __global__ __launch_bounds__(NTB, 1) void k_dqb(Params p, BwdArgs a) {
   const bool no_mask = msk.kind == kMaskNone;
   int lo_l = msk.wl < 0 ? -0x3fffffff : -msk.wl, span = msk.wr - lo_l;
   if (no_mask) { lo_l = -0x3fffffff; span = 0x7ffffffe; }
-  // window offset of key 4 lg (+ c) of a tile for this lane's row
-  const int tq = (int)msk.k_off - (irow + (int)msk.q_off) - (int)msk.diag + 4 * lg - lo_l;
+  // window offset of key 4 g (+ 16 mt + i) of a tile for this lane's row
+  const int tq = (int)msk.k_off - (irow + (int)msk.q_off) - (int)msk.diag + 4 * g - lo_l;
   const int sink_lim = (int)min<int64_t>(max<int64_t>(msk.n_sink - msk.k_off, 0), 0x3fffffff);
-  const int wr0 = i0 + 32 * ws;
+  // a tile is full for this wave when every key is inside the problem and
+  // allowed for all 16 of its rows
+  const int wr0 = i0 + 16 * w;
   auto clamp_i = [](int64_t x) { return (int)max<int64_t>(min<int64_t>(x, 0x3fffffff), -0x3fffffff); };
   const int64_t band = (int64_t)wr0 + msk.q_off + msk.diag - msk.k_off;
   const int fl_hi = no_mask ? 0x3fffffff : clamp_i(band + msk.wr - 31);
-  const int fl_lo = (no_mask || msk.wl < 0) ? -0x3fffffff : clamp_i(band + 31 - msk.wl);
+  const int fl_lo = (no_mask || msk.wl < 0) ? -0x3fffffff : clamp_i(band + 15 - msk.wl);
   const int fl_sink = no_mask ? -0x3fffffff : clamp_i((int64_t)msk.n_sink - 31 - msk.k_off);
   auto tile_full = [&](int j0) { return (j0 + BK3 <= Sk) & ((j0 < fl_sink) | ((j0 <= fl_hi) & (j0 >= fl_lo))); };
 
@@ -1766,29 +1767,33 @@ __global__ __launch_bounds__(NTB, 1) void k_dqb(Params p, BwdArgs a) {
   const int b_rb = 4 * (int)p.bias_str[1];
   const int brows = min(Sq - i0, BQ3);
   const float* bias_h = a.bias + h * p.bias_str[0] + (int64_t)i0 * p.bias_str[1];
-  // staging: wave w loads the K (w < 4) or V tile of entry w % 4 (four 1 KB
-  // loads, when the group has that entry) and bias rows 16 w .. 16 w + 15
-  // (two 1 KB loads of 8 rows; 16-byte chunk c of row r lands at chunk
-  // c ^ ((r / 2) % 8): a 128-byte row covers half the banks, row parity picks
-  // the half, and the 16 rows that one read serves at a time fall on
-  // distinct banks)
-  const int64_t* kv_str = half == 0 ? p.k_str : p.v_str;
+  // staging: wave w loads the K (w < 4) or V tile of entry w % 4 of the group
+  // (four 1 KB loads; a group with fewer entries loads its last entry's
+  // instead) and bias rows 16 w .. 16 w + 15 (two 1 KB loads of 8 rows;
+  // 16-byte chunk c of row r lands at chunk c ^ ((r / 2) % 8): a 128-byte row
+  // covers half the banks, row parity picks the half, and the 16 rows that one
+  // read serves at a time fall on distinct banks)
+  const int we = w & 3, wkv = w >> 2;
+  const int64_t* kv_str = wkv == 0 ? p.k_str : p.v_str;
   const int kv_rb = 2 * (int)kv_str[2];
   const unsigned char* kv_head =
-      (const unsigned char*)((half == 0 ? (const unsigned short*)a.k : (const unsigned short*)a.v) + g * kv_str[1]);
+      (const unsigned char*)((wkv == 0 ? (const unsigned short*)a.k : (const unsigned short*)a.v) + hk * kv_str[1]);
   const int64_t kv_bbytes = 2 * kv_str[0];
-  const unsigned int kv_dst = sm_base + (ws >> 1) * PAIR_B + (ws & 1) * 2 * TS + half * TS;
-  const unsigned char* kv_grp = kv_head;   // the group's entry ws
-  auto issue = [&](int it, int buf, int nb) {
+  const unsigned int kv_dst = sm_base + (we * 2 + wkv) * TS;
+  // K / V tiles: 16-byte chunk c of row r sits at chunk c ^ fq(r).  Both read
+  // patterns -- one chunk of 16 consecutive rows (the A operands) and two
+  // chunks of 8 consecutive rows (the transposing reads of dQ's B operand,
+  // 32 lanes a pass) -- then fall on distinct banks.
+  auto fq = [](int r) { return 4 * ((r >> 2) & 1) + 2 * ((r >> 1) & 1) + ((r >> 3) & 1); };
+  const unsigned char* kv_grp = kv_head;   // the group's entry w % 4 (or its last)
+  auto issue = [&](int it, int buf) {
     const int j0 = tile_of(it);
     const int keys = min(Sk - j0, BK3);
-    if (ws < nb) {
-      const __amdgpu_buffer_rsrc_t rs = buf_rsrc(kv_grp + j0 * kv_rb, keys * kv_rb);
+    const __amdgpu_buffer_rsrc_t rs = buf_rsrc(kv_grp + j0 * kv_rb, keys * kv_rb);
 #pragma unroll
-      for (int k = 0; k < PER_T; ++k) {
-        const int row = (64 * k + l) / CR, c = (l % CR) ^ Swz<D>::f(row);
-        lds_dma16(rs, __builtin_amdgcn_readfirstlane(kv_dst + buf * BUF_B + 1024 * k), row * kv_rb + 16 * c);
-      }
+    for (int k = 0; k < PER_T; ++k) {
+      const int row = (64 * k + l) / CR, c = (l % CR) ^ fq(row);
+      lds_dma16(rs, __builtin_amdgcn_readfirstlane(kv_dst + buf * BUF_B + 1024 * k), row * kv_rb + 16 * c);
     }
     const __amdgpu_buffer_rsrc_t rb_ = buf_rsrc(bias_h + j0, (brows - 1) * b_rb + 4 * keys);
 #pragma unroll
@@ -1798,9 +1803,8 @@ __global__ __launch_bounds__(NTB, 1) void k_dqb(Params p, BwdArgs a) {
                 row * b_rb + 16 * c);
     }
   };
-
   // bias / scale in place: each wave scales the 16 rows it loaded itself
-  // (complete once its own loads are), before the barrier that publishes them
+  // (complete once its own loads are; only this wave reads them)
   typedef __attribute__((address_space(3))) f32x4 lds_f32x4;
   auto scale_bias = [&](int buf) {
     const unsigned int o = sm_base + BIAS_OFF + buf * BTB + 16 * w * 128 + 16 * l;
@@ -1811,167 +1815,160 @@ __global__ __launch_bounds__(NTB, 1) void k_dqb(Params p, BwdArgs a) {
     }
   };
 
-  // operand lane addresses in this wave's pair region (buffer 0, entry 0's
-  // K tile); tiles are reached by immediate offsets
-  const unsigned int pair_base = sm_base + half * PAIR_B;
-  const int a_lane = Swz<D>::a_lane(l), t_lane = Swz<D>::t_lane(l);
-  unsigned int ka[NS], br[NC], br2[NC];
+  // operand lane addresses (buffer 0, entry 0's K tile; tiles are reached by
+  // immediate offsets):
+  //  * A of S^T / dP^T: K / V row 16 mt + j, chunk g + 4 s  ->  (a16 ^ 64 s) + 2048 mt
+  //  * B of dQ (transposing reads): lane 4 r + cc of group g addresses K row
+  //    16 h + 4 g + r, columns 16 nt + 4 cc ..  ->  (tb16 ^ 32 nt) + 2048 h
+  //  * bias row 16 w + j, chunk 4 mt + g  ->  bb ^ 64 mt
+  const unsigned int a16 = sm_base + j * RB + 16 * (g ^ fq(j));
+  const int tr = j >> 2, tc = j & 3;
+  const int ftr = fq(4 * g + tr);
+  const unsigned int tb16 = sm_base + (4 * g + tr) * RB + 16 * ((tc >> 1) ^ ftr) + 8 * (tc & 1);
+  unsigned int ta[4];
 #pragma unroll
-  for (int s = 0; s < NS; ++s) ka[s] = (pair_base + a_lane) ^ (32 * s);
-#pragma unroll
-  for (int n = 0; n < NC; ++n) {
-    br[n] = pair_base + (t_lane ^ (64 * n));
-    br2[n] = br[n] ^ 32;
-  }
-  // this lane's bias row: chunk 2 m + lg (keys 8 m + 4 lg + 0..3) sits at
-  // position (2 m + lg) ^ ((row / 2) % 8), i.e. at  b_lane ^ (32 m)  (the
-  // row start is 128-byte aligned)
-  const int brow = 32 * ws + lr;
-  const unsigned int b_lane =
-      sm_base + BIAS_OFF + brow * 128 + 16 * (lg ^ ((brow >> 1) & 1)) + 32 * ((brow >> 2) & 3);
-  unsigned int bl[4];
-#pragma unroll
-  for (int m = 0; m < 4; ++m) bl[m] = b_lane ^ (32 * m);
+  for (int nt = 0; nt < 4; ++nt) ta[nt] = tb16 ^ (32 * nt);
+  const unsigned int aa[2] = {a16, a16 ^ 64};
+  const int brow = 16 * w + j;
+  const unsigned int bb = sm_base + BIAS_OFF + brow * 128 + 16 * (g ^ ((brow >> 1) & 7));
+  const unsigned int bl[2] = {bb, bb ^ 64};
 
   float* dbias_h = a.dbias + h * p.bias_str[0] + (int64_t)i0 * p.bias_str[1];
-  const int db_off = brow * b_rb + 16 * lg;   // this lane's row, keys 4 lg + 0..3 of a tile
+  const int db_off = brow * b_rb + 16 * g;   // this lane's row, keys 4 g + 0..3 of a tile
   for (int b0 = 0; b0 < p.B; b0 += BGB) {
     const int nb = min(BGB, p.B - b0);
     const bool first = b0 == 0;
-    // this wave's entries of the group: 2 half + ee for ee < ne
-    const int ne = max(0, min(EPW, nb - 2 * half));
-    const bool hand = nb > 2;   // waves 4..7 have entries: their dbias tiles are handed over
-    bf16x8 qB[EPW][NS], doB[EPW][NS];
-    float lse2[EPW], ndl[EPW];   // LSE * log2(e) and -delta of this lane's row
-    f32x16 dq[EPW][NC];
+    // the group's Q / dO fragments (B operands: row j, head-dim columns
+    // 8 g + 32 s ..), LSE * log2(e) and -delta of this lane's row
+    bf16x8 qB[BGB][2], doB[BGB][2];
+    float lse2[BGB], ndl[BGB];
+    f32x4 dq[BGB][4];
 #pragma unroll
-    for (int ee = 0; ee < EPW; ++ee) {
-      const int b = b0 + min(2 * half + ee, nb - 1);
+    for (int e = 0; e < BGB; ++e) {
+      const int b = b0 + min(e, nb - 1);
       const int64_t ic = min(irow, Sq - 1);
       const unsigned short* q = (const unsigned short*)a.q + b * p.q_str[0] + h * p.q_str[1] + ic * p.q_str[2];
       const unsigned short* d = (const unsigned short*)a.dout + b * p.do_str[0] + h * p.do_str[1] + ic * p.do_str[2];
 #pragma unroll
-      for (int s = 0; s < NS; ++s) {
-        qB[ee][s] = as_bf16x8(*(const u16x8*)(q + 16 * s + 8 * lg));
-        doB[ee][s] = as_bf16x8(*(const u16x8*)(d + 16 * s + 8 * lg));
+      for (int s = 0; s < 2; ++s) {
+        qB[e][s] = as_bf16x8(*(const u16x8*)(q + 32 * s + 8 * g));
+        doB[e][s] = as_bf16x8(*(const u16x8*)(d + 32 * s + 8 * g));
       }
-      lse2[ee] = INFINITY;
-      ndl[ee] = 0.f;
-      if (row_ok) {
+      lse2[e] = INFINITY;   // P = 0: rows past the end and the filler entries
+      ndl[e] = 0.f;
+      if (row_ok && e < nb) {
         const float lv = a.lse[((int64_t)b * p.Hq + h) * p.Sq + irow];
-        lse2[ee] = (lv == -INFINITY) ? INFINITY : lv * kLog2e;
-        ndl[ee] = -a.delta[((int64_t)b * p.Hq + h) * p.Sq + irow];
+        lse2[e] = (lv == -INFINITY) ? INFINITY : lv * kLog2e;
+        ndl[e] = -a.delta[((int64_t)b * p.Hq + h) * p.Sq + irow];
       }
 #pragma unroll
-      for (int n = 0; n < NC; ++n) dq[ee][n] = zero16();
+      for (int nt = 0; nt < 4; ++nt) dq[e][nt] = f32x4{0.f, 0.f, 0.f, 0.f};
     }
-    kv_grp = kv_head + (b0 + ws) * kv_bbytes;
+    kv_grp = kv_head + (b0 + min(we, nb - 1)) * kv_bbytes;
     wait_vm_loads();
     __syncthreads();   // the previous group's readers of the tile buffers are done
     if (n_it > 0) {
-      issue(0, 0, nb);
-      if (n_it > 1) issue(1, 1, nb);
+      issue(0, 0);
+      if (n_it > 1) issue(1, 1);
     }
-    const int ni = (ws < nb ? PER_T : 0) + 2;   // this wave's loads per tile
-    if (n_it > 1) wait_vm(ni);
-    else wait_vm(0);
+    if (n_it > 1) wait_vm_c<NI>();
+    else wait_vm_c<0>();
     if (n_it > 0) scale_bias(0);
+
+    // the products and arithmetic of one tile in buffer J; full: no key of
+    // the tile is masked for this wave's rows.  A masked pair starts its S^T
+    // chain from -inf instead of bias / scale: the products are finite, so the
+    // chain ends at -inf and P = 0 for every entry (LSE is never -inf here).
+    // The mask is applied once per tile, before any product, and the entries
+    // form one straight block.
+    auto body = [&](int j0, auto Jc, bool full) {
+      constexpr int J = decltype(Jc)::value;
+      const int tb = tq + j0;
+      f32x4 bz[2];
+#pragma unroll
+      for (int mt = 0; mt < 2; ++mt) bz[mt] = *(const lds_f32x4*)(size_t)(bl[mt] + J * BTB);
+      if (!full) {
+#pragma unroll
+        for (int r = 0; r < 8; ++r) {
+          const int c = 16 * (r >> 2) + (r & 3);   // key 4 g + c of the tile
+          const int jj = j0 + 4 * g + c;
+          const bool ok = (jj < Sk) & (((unsigned int)(tb + c) <= (unsigned int)span) | (jj < sink_lim));
+          bz[r >> 2][r & 3] = ok ? bz[r >> 2][r & 3] : -INFINITY;
+        }
+      }
+      f32x4 db[2] = {f32x4{0.f, 0.f, 0.f, 0.f}, f32x4{0.f, 0.f, 0.f, 0.f}};
+#pragma unroll
+      for (int e = 0; e < BGB; ++e) {
+        const int kt = J * BUF_B + e * 2 * TS, vt = kt + TS;
+        // S^T starts from bias / scale, so it ends at (S scale + bias) / scale
+        f32x4 sacc[2] = {bz[0], bz[1]};
+        f32x4 pacc[2] = {f32x4{0.f, 0.f, 0.f, 0.f}, f32x4{0.f, 0.f, 0.f, 0.f}};
+#pragma unroll
+        for (int s = 0; s < 2; ++s) {
+#pragma unroll
+          for (int mt = 0; mt < 2; ++mt) {
+            sacc[mt] = mfma16(lds_b128_at(aa[s] + kt + 2048 * mt), qB[e][s], sacc[mt]);
+            pacc[mt] = mfma16(lds_b128_at(aa[s] + vt + 2048 * mt), doB[e][s], pacc[mt]);
+          }
+        }
+        // P, then dS = P (dP - delta), unscaled (dQ takes the scale once at the end)
+        float dsv[8];
+#pragma unroll
+        for (int mt = 0; mt < 2; ++mt)
+#pragma unroll
+          for (int i = 0; i < 4; ++i) dsv[4 * mt + i] = __builtin_amdgcn_exp2f(fmaf(sacc[mt][i], scale_log2, -lse2[e]));
+#pragma unroll
+        for (int mt = 0; mt < 2; ++mt)
+#pragma unroll
+          for (int i = 0; i < 4; ++i) {
+            dsv[4 * mt + i] *= pacc[mt][i] + ndl[e];
+            db[mt][i] += dsv[4 * mt + i];
+          }
+        const bf16x8 A = pack8(dsv);
+#pragma unroll
+        for (int nt = 0; nt < 4; ++nt) {
+          const bf16x8 bq = cat44(lds_tr4_at(ta[nt] + kt), lds_tr4_at(ta[nt] + kt + 2048));
+          dq[e][nt] = mfma16(A, bq, dq[e][nt]);
+        }
+      }
+      return DbTile{db[0], db[1]};
+    };
 
     // tile t in buffer J
     auto tile = [&](int t, auto Jc) {
       constexpr int J = decltype(Jc)::value;
       __syncthreads();   // tile t complete for every wave; tile t - 1's buffer free
-      if (t + 2 < n_it) issue(t + 2, (J + 2) % NQB, nb);
+      if (t + 2 < n_it) issue(t + 2, (J + 2) % NQB);
       const int j0 = tile_of(t);
-      const bool full = tile_full(j0);
-      const int tb = tq + j0;
-      float db[16];
-#pragma unroll
-      for (int r = 0; r < 16; ++r) db[r] = 0.f;
-#pragma unroll
-      for (int ee = 0; ee < EPW; ++ee) {
-        if (ee >= ne) break;
-        constexpr int kt0 = J * BUF_B;
-        const int kt = kt0 + ee * 2 * TS, vt = kt + TS;
-        // S^T starts from bias / scale (this lane's row, keys 8 m + 4 lg + 0..3;
-        // the tile holds bias / scale), so the chain ends at (S scale + bias) /
-        // scale
-        f32x16 sacc, pacc = zero16();
-#pragma unroll
-        for (int m = 0; m < 4; ++m) {
-          const f32x4 v = *(const __attribute__((address_space(3))) f32x4*)(size_t)(bl[m] + J * BTB);
-#pragma unroll
-          for (int c = 0; c < 4; ++c) sacc[4 * m + c] = v[c];
-        }
-#pragma unroll
-        for (int s = 0; s < NS; ++s) {
-          sacc = mfma(lds_b128_at(ka[s] + kt), qB[ee][s], sacc);
-          pacc = mfma(lds_b128_at(ka[s] + vt), doB[ee][s], pacc);
-        }
-        float dsv[16];
-#pragma unroll
-        for (int r = 0; r < 16; ++r) dsv[r] = __builtin_amdgcn_exp2f(fmaf(sacc[r], scale_log2, -lse2[ee]));
-        if (!full) {   // (one branch, touching P only)
-#pragma unroll
-          for (int r = 0; r < 16; ++r) {
-            const int c = 8 * (r >> 2) + (r & 3);   // key 4 lg + c of the tile
-            const int jj = j0 + 4 * lg + c;
-            const bool ok = (jj < Sk) & (((unsigned int)(tb + c) <= (unsigned int)span) | (jj < sink_lim));
-            dsv[r] = ok ? dsv[r] : 0.f;
-          }
-        }
-        // dS = P (dP - delta), unscaled (dQ takes the scale once at the end)
-#pragma unroll
-        for (int r = 0; r < 16; ++r) {
-          dsv[r] *= pacc[r] + ndl[ee];
-          db[r] += dsv[r];
-        }
-        const bf16x8 A0 = pack8(dsv), A1 = pack8(dsv + 8);
-#pragma unroll
-        for (int i = 0; i < NS; ++i) {
-          const int n = i % NC, r0 = 16 * (i / NC);
-          const bf16x8 bq = cat44(lds_tr4_at(br[n] + kt + r0 * RB), lds_tr4_at(br2[n] + kt + (r0 + 8) * RB));
-          dq[ee][n] = mfma(i < NC ? A0 : A1, bq, dq[ee][n]);
-        }
-      }
-      if (half == 1 && hand) {
-#pragma unroll
-        for (int m = 0; m < 4; ++m) sm.x[ws][m][l] = f32x4{db[4 * m], db[4 * m + 1], db[4 * m + 2], db[4 * m + 3]};
-      }
-      __syncthreads();   // the handed-over tiles are in LDS
+      const DbTile dbt = body(j0, Jc, tile_full(j0));
+      const f32x4 db[2] = {dbt.c0, dbt.c1};
+      // dbias of this tile (unscaled dS summed over the group): this lane's
+      // row, keys j0 + 16 mt + 4 g + 0..3.  A whole key tile is stored by two
+      // buffer stores from every lane (rows past the end fall outside the
+      // resource and are dropped), so the count of memory operations is the
+      // same in every wave; the ragged last tile stores the chunks inside the
+      // problem only.
       const bool whole = j0 + BK3 <= Sk;
-      if (half == 0) {
-        if (hand) {
+      const __amdgpu_buffer_rsrc_t rd = buf_rsrc(dbias_h + j0, (brows - 1) * b_rb + 4 * min(BK3, Sk - j0));
 #pragma unroll
-          for (int m = 0; m < 4; ++m) {
-            const f32x4 v = sm.x[ws][m][l];
-#pragma unroll
-            for (int c = 0; c < 4; ++c) db[4 * m + c] += v[c];
-          }
-        }
-        // dbias of this tile (unscaled dS summed over the group): this lane's
-        // row, keys j0 + 8 m + 4 lg + 0..3.  A whole key tile is stored by
-        // four buffer stores from every lane (rows past the end fall outside
-        // the resource and are dropped), so the count of memory operations
-        // is the same in every such wave; the ragged last tile stores the
-        // chunks inside the problem only.
-        const __amdgpu_buffer_rsrc_t rd = buf_rsrc(dbias_h + j0, (brows - 1) * b_rb + 4 * min(BK3, Sk - j0));
-#pragma unroll
-        for (int m = 0; m < 4; ++m) {
-          if (whole || (row_ok && j0 + 8 * m + 4 * lg < Sk)) {
-            f32x4 v = {db[4 * m], db[4 * m + 1], db[4 * m + 2], db[4 * m + 3]};
-            if (!first) v += __builtin_bit_cast(f32x4, __builtin_amdgcn_raw_buffer_load_b128(rd, db_off + 32 * m, 0, 0));
-            __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u32x4, v), rd, db_off + 32 * m, 0, 0);
-          }
+      for (int mt = 0; mt < 2; ++mt) {
+        if (whole || (row_ok && j0 + 16 * mt + 4 * g < Sk)) {
+          f32x4 v = db[mt];
+          if (!first) v += __builtin_bit_cast(f32x4, __builtin_amdgcn_raw_buffer_load_b128(rd, db_off + 64 * mt, 0, 0));
+          __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u32x4, v), rd, db_off + 64 * mt, 0, 0);
         }
       }
       // Tile t + 1 complete before the next barrier (tile t + 2 may stay in
-      // flight).  Behind tile t + 1's loads come, in waves 0..3, the dbias
-      // stores of tile t - 1, then tile t + 2's loads and this tile's dbias
-      // stores (vector memory operations complete in issue order).  Only the
-      // last tile can be ragged, so tile t - 1 was whole here.
-      if (t + 2 < n_it && whole && first) wait_vm((half == 0 ? (t > 0 ? 8 : 4) : 0) + ni);
-      else wait_vm(0);
+      // flight).  Behind tile t + 1's loads come the dbias stores of tile
+      // t - 1, then tile t + 2's loads and this tile's dbias stores (vector
+      // memory operations complete in issue order).  Only the last tile can
+      // be ragged, so tile t - 1 was whole here.
+      if (t + 2 < n_it && whole && first) {
+        if (t > 0) wait_vm_c<NI + 4>();
+        else wait_vm_c<NI + 2>();
+      } else {
+        wait_vm_c<0>();
+      }
       if (t + 1 < n_it) scale_bias((J + 1) % NQB);   // (own rows of tile t + 1, complete)
     };
     int t = 0;
@@ -1983,19 +1980,19 @@ __global__ __launch_bounds__(NTB, 1) void k_dqb(Params p, BwdArgs a) {
     if (t < n_it) tile(t, std::integral_constant<int, 0>{});
     if (t + 1 < n_it) tile(t + 1, std::integral_constant<int, 1>{});
 
-    // dQ of this wave's entries: rows i0 + 32 ws + crow(r, lg), columns 32 n + lane
+    // dQ of the group's entries: rows i0 + 16 w + 4 g + i, columns 16 nt + j
 #pragma unroll
-    for (int ee = 0; ee < EPW; ++ee) {
-      if (ee >= ne) break;
-      float* dqp = a.dq + (b0 + 2 * half + ee) * p.dq_str[0] + h * p.dq_str[1];
+    for (int e = 0; e < BGB; ++e) {
+      if (e >= nb) break;
+      float* dqp = a.dq + (b0 + e) * p.dq_str[0] + h * p.dq_str[1];
 #pragma unroll
-      for (int n = 0; n < NC; ++n) {
+      for (int nt = 0; nt < 4; ++nt) {
 #pragma unroll
-        for (int r = 0; r < 16; ++r) {
-          const int64_t i = i0 + 32 * ws + crow(r, lg);
-          if (i < Sq) {
-            float* dst = dqp + i * p.dq_str[2] + 32 * n + lr;
-            const float v = dq[ee][n][r] * scale;
+        for (int i = 0; i < 4; ++i) {
+          const int64_t r = i0 + 16 * w + 4 * g + i;
+          if (r < Sq) {
+            float* dst = dqp + r * p.dq_str[2] + 16 * nt + j;
+            const float v = dq[e][nt][i] * scale;
             *dst = a.accumulate_dq ? *dst + v : v;
           }
         }

@@ -104,6 +104,11 @@ SMALL = [
     (3, 4, 4, 640, 640, 64, 64, "bf16", MaskSpec("none"), True, False),           # batch-ordered dbias
     (1, 32, 8, 1100, 1100, 128, 128, "bf16", MaskSpec("bottom_right"), False, False),
     (1, 16, 1, 512, 512, 64, 64, "bf16", MaskSpec("top_left"), False, False),     # D = 64, 16-way split
+    # head dim 64 with a bias and dbias under masks (masked tiles of both passes)
+    (2, 4, 2, 200, 333, 64, 64, "bf16", MaskSpec("bottom_right", window_left=63, window_right=5,
+                                                  num_sink=3), True, True),
+    (5, 2, 2, 160, 160, 64, 64, "bf16", MaskSpec("top_left"), True, False),       # two batch groups
+    (1, 4, 4, 256, 200, 64, 64, "bf16", MaskSpec("bottom_right"), True, False),
 ]
 
 
@@ -332,17 +337,18 @@ def test_headline_chunked():
     check("delta", delta, ref["delta"], 1e-5)
 
 
-def test_deterministic_is_bitwise_repeatable():
-    x = random_case(1, 8, 2, 512, 512, 128, 128, "bf16", 9, True, True)
+@pytest.mark.parametrize("D", [128, 64])
+def test_deterministic_is_bitwise_repeatable(D):
+    x = random_case(5 if D == 64 else 1, 8, 2, 512, 512, D, D, "bf16", 9, True, True)
     spec = MaskSpec("top_left", window_left=200, num_sink=4)
     dt = torch.bfloat16
     q, k, v, do = (dev(x[n], dt) for n in ("q", "k", "v", "do"))
     bias, sinks = dev(x["bias"], torch.float32), dev(x["sinks"], torch.float32)
-    o, lse = ab.forward(q, k, v, bias=bias, sinks=sinks, scale=1 / np.sqrt(128), **mask_kw(spec))
+    o, lse = ab.forward(q, k, v, bias=bias, sinks=sinks, scale=1 / np.sqrt(D), **mask_kw(spec))
     outs = []
     for _ in range(3):
         g = ab.backward(q, k, v, o, do, lse, bias=bias, sinks=sinks, want_dbias=True,
-                        flags=ab.ATTN_DETERMINISTIC, scale=1 / np.sqrt(128), **mask_kw(spec))
+                        flags=ab.ATTN_DETERMINISTIC, scale=1 / np.sqrt(D), **mask_kw(spec))
         torch.cuda.synchronize()
         outs.append({kk: vv.clone() for kk, vv in g.items() if vv is not None})
     for kk in outs[0]:
