@@ -999,11 +999,12 @@ hipError_t dispatch_dkdv(const Params& p, const BwdArgs& a, const DkdvPlan& pl, 
     hipLaunchKernelGGL((k_dkdv2<D, false>), pl.grid, dim3(NT2), 0, st, p, a, pl.g);
     return hipGetLastError();
   }
-  if (D == 64 && !bloop) {
+  if constexpr (D == 64) {   // with a bias, head dim 64 always takes k_dkdv2 (dbias comes from k_dqb)
     hipLaunchKernelGGL((k_dkdv2<64, true>), pl.grid, dim3(NT2), 0, st, p, a, pl.g);
     return hipGetLastError();
+  } else {
+    return bloop ? launch_dkdv<D, true, true>(p, a, pl, st) : launch_dkdv<D, true, false>(p, a, pl, st);
   }
-  return bloop ? launch_dkdv<D, true, true>(p, a, pl, st) : launch_dkdv<D, true, false>(p, a, pl, st);
 }
 
 // ---------------------------------------------------------------------------
