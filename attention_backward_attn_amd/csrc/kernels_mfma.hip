@@ -376,6 +376,10 @@ __global__ __launch_bounds__(NT, 1) void k_dkdv(Params p, BwdArgs a, DkdvGrid gd
       // Epilogue: dK (scaled through dS) and dV for this wave's keys.
       float* dkp = a.dk + b * p.dk_str[0] + hk * p.dk_str[1];
       float* dvp = a.dv + b * p.dv_str[0] + hk * p.dv_str[1];
+      if (out_mode == kAddInto) {
+        add_loaded<NB>(dk, dkp, p.dk_str[2], kw, Sk, lg, lr);
+        add_loaded<NB>(dv, dvp, p.dv_str[2], kw, Sk, lg, lr);
+      }
 #pragma unroll
       for (int n = 0; n < NB; ++n) {
 #pragma unroll
@@ -387,9 +391,6 @@ __global__ __launch_bounds__(NT, 1) void k_dkdv(Params p, BwdArgs a, DkdvGrid gd
             if (out_mode == kAtomicAdd) {
               atomic_add_f32(pk, dk[n][r]);
               atomic_add_f32(pvv, dv[n][r]);
-            } else if (out_mode == kAddInto) {
-              *pk += dk[n][r];
-              *pvv += dv[n][r];
             } else {
               *pk = dk[n][r];
               *pvv = dv[n][r];
@@ -1230,15 +1231,13 @@ __global__ __launch_bounds__(NT, 2) void k_dq(Params p, BwdArgs a) {
 
   // dQ rows i0 + 32 w + crow(r, lg), columns 32 n + lr (already scaled through dS).
   float* dqp = a.dq + sv.q_off(p.dq_str, b) + h * p.dq_str[1];
+  if (a.accumulate_dq) add_loaded<NB>(dq, dqp, p.dq_str[2], i0 + 32 * w, Sq, lg, lr);
 #pragma unroll
   for (int n = 0; n < NB; ++n) {
 #pragma unroll
     for (int r = 0; r < 16; ++r) {
       const int64_t i = i0 + 32 * w + crow(r, lg);
-      if (i < Sq) {
-        float* dst = dqp + i * p.dq_str[2] + 32 * n + lr;
-        *dst = a.accumulate_dq ? *dst + dq[n][r] : dq[n][r];
-      }
+      if (i < Sq) dqp[i * p.dq_str[2] + 32 * n + lr] = dq[n][r];
     }
   }
 }
@@ -1669,15 +1668,13 @@ __global__ __launch_bounds__(NT, 2) void k_dq2(Params p, BwdArgs a, ZeroMulti zm
 
   // dQ rows i0 + 32 w + crow(r, lg), columns 32 n + lr (already scaled through dS).
   float* dqp = a.dq + sv.q_off(p.dq_str, b) + h * p.dq_str[1];
+  if (a.accumulate_dq) add_loaded<NC>(dq, dqp, p.dq_str[2], i0 + 32 * w, Sq, lg, lr);
 #pragma unroll
   for (int n = 0; n < NC; ++n) {
 #pragma unroll
     for (int r = 0; r < 16; ++r) {
       const int64_t i = i0 + 32 * w + crow(r, lg);
-      if (i < Sq) {
-        float* dst = dqp + i * p.dq_str[2] + 32 * n + lr;
-        *dst = a.accumulate_dq ? *dst + dq[n][r] : dq[n][r];
-      }
+      if (i < Sq) dqp[i * p.dq_str[2] + 32 * n + lr] = dq[n][r];
     }
   }
   zero_share();
@@ -1992,13 +1989,27 @@ __global__ __launch_bounds__(NTB, 1) void k_dqb(Params p, BwdArgs a) {
 #pragma unroll
       for (int nt = 0; nt < 4; ++nt) {
 #pragma unroll
+        for (int i = 0; i < 4; ++i) dq[e][nt][i] *= scale;
+      }
+      if (a.accumulate_dq) {   // every load ahead of the adds (in flight together)
+        f32x4 old[4];
+#pragma unroll
+        for (int nt = 0; nt < 4; ++nt) {
+#pragma unroll
+          for (int i = 0; i < 4; ++i) {
+            const int64_t r = i0 + 16 * w + 4 * g + i;
+            old[nt][i] = r < Sq ? dqp[r * p.dq_str[2] + 16 * nt + j] : 0.f;
+          }
+        }
+#pragma unroll
+        for (int nt = 0; nt < 4; ++nt) dq[e][nt] = old[nt] + dq[e][nt];
+      }
+#pragma unroll
+      for (int nt = 0; nt < 4; ++nt) {
+#pragma unroll
         for (int i = 0; i < 4; ++i) {
           const int64_t r = i0 + 16 * w + 4 * g + i;
-          if (r < Sq) {
-            float* dst = dqp + r * p.dq_str[2] + 16 * nt + j;
-            const float v = dq[e][nt][i] * scale;
-            *dst = a.accumulate_dq ? *dst + v : v;
-          }
+          if (r < Sq) dqp[r * p.dq_str[2] + 16 * nt + j] = dq[e][nt][i];
         }
       }
     }

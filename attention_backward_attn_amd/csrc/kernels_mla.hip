@@ -460,15 +460,26 @@ __global__ __launch_bounds__(XNT, 1) void k_dq512(Params p, BwdArgs a) {
   }
   // dQ rows i0 + 16 rb + lane % 16, columns 128 w + 16 c + 4 g .. + 3
   float* dqp = a.dq + sv.q_off(p.dq_str, b) + h * p.dq_str[1];
+  if (a.accumulate_dq) {   // every load ahead of the adds (in flight together)
+    f32x4 old[4 * NCW];
+#pragma unroll
+    for (int rb = 0; rb < 4; ++rb) {
+      const int i = i0 + 16 * rb + lr;
+#pragma unroll
+      for (int c = 0; c < NCW; ++c)
+        old[4 * c + rb] = i < Sq ? *(const f32x4*)(dqp + (int64_t)i * p.dq_str[2] + 128 * w + 16 * c + 4 * g)
+                                 : f32x4{0.f, 0.f, 0.f, 0.f};
+    }
+#pragma unroll
+    for (int x = 0; x < 4 * NCW; ++x) dq[x] = old[x] + dq[x];
+  }
 #pragma unroll
   for (int rb = 0; rb < 4; ++rb) {
     const int i = i0 + 16 * rb + lr;
     if (i < Sq) {
 #pragma unroll
-      for (int c = 0; c < NCW; ++c) {
-        f32x4* d4 = (f32x4*)(dqp + (int64_t)i * p.dq_str[2] + 128 * w + 16 * c + 4 * g);
-        *d4 = a.accumulate_dq ? *d4 + dq[4 * c + rb] : dq[4 * c + rb];
-      }
+      for (int c = 0; c < NCW; ++c)
+        *(f32x4*)(dqp + (int64_t)i * p.dq_str[2] + 128 * w + 16 * c + 4 * g) = dq[4 * c + rb];
     }
   }
 }
@@ -741,6 +752,19 @@ __global__ __launch_bounds__(XNT, 1) void k_dkv512(Params p, BwdArgs a, int part
   const int64_t dko = sv.k_off(p.dk_str, b) + hk * p.dk_str[1];
   float* dkp = slot ? slots + (part - 1) * slot_elems + dko : a.dk + dko;
   const int mode = slot ? kStoreX : out_mode;
+  if (mode == kAddIntoX) {   // every load ahead of the adds (in flight together)
+    f32x4 old[4 * NCW];
+#pragma unroll
+    for (int kb2 = 0; kb2 < 4; ++kb2) {
+      const int kk = k0 + 16 * kb2 + lr;
+#pragma unroll
+      for (int c = 0; c < NCW; ++c)
+        old[4 * c + kb2] = kk < Sk ? *(const f32x4*)(dkp + (int64_t)kk * p.dk_str[2] + 128 * w + 16 * c + 4 * g)
+                                   : f32x4{0.f, 0.f, 0.f, 0.f};
+    }
+#pragma unroll
+    for (int x = 0; x < 4 * NCW; ++x) acc[x] = old[x] + acc[x];
+  }
 #pragma unroll
   for (int kb2 = 0; kb2 < 4; ++kb2) {
     const int kk = k0 + 16 * kb2 + lr;
@@ -752,8 +776,6 @@ __global__ __launch_bounds__(XNT, 1) void k_dkv512(Params p, BwdArgs a, int part
         if (mode == kAtomicAddX) {
 #pragma unroll
           for (int r = 0; r < 4; ++r) atomic_add_f32(d + r, v[r]);
-        } else if (mode == kAddIntoX) {
-          *(f32x4*)d = *(const f32x4*)d + v;
         } else {
           *(f32x4*)d = v;
         }

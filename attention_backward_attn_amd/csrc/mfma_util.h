@@ -58,6 +58,28 @@ __device__ inline f32x16 zero16() {
 // Row (within a 32-row accumulator block) held by lane group lg in register r.
 __device__ inline int crow(int r, int lg) { return 8 * (r >> 2) + 4 * lg + (r & 3); }
 
+// Accumulating epilogue of N 32 x 32 accumulator blocks: acc[n][r] += the
+// fp32 value at base[(row0 + crow(r, lg)) stride + 32 n + lr] for the rows
+// below nrows, ahead of the stores.  The loads of a block are issued
+// together; written as one load-add-store per element, every store must
+// stay ahead of the next load (their addresses may alias), and each load's
+// full memory latency is paid in turn.
+template <int N>
+__device__ inline void add_loaded(f32x16 (&acc)[N], const float* base, int64_t stride, int64_t row0,
+                                  int64_t nrows, int lg, int lr) {
+#pragma unroll
+  for (int n = 0; n < N; ++n) {
+    float v[16];
+#pragma unroll
+    for (int r = 0; r < 16; ++r) {
+      const int64_t i = row0 + crow(r, lg);
+      v[r] = i < nrows ? base[i * stride + 32 * n + lr] : 0.f;
+    }
+#pragma unroll
+    for (int r = 0; r < 16; ++r) acc[n][r] += v[r];
+  }
+}
+
 // LDS layouts.  Every tile is row-major bf16 with a padded row stride, and
 // each access pattern gets a copy whose padding makes it bank-conflict-free
 // with per-lane addresses of the form  lane_base + compile-time offset:
