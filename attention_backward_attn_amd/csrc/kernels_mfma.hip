@@ -1266,14 +1266,15 @@ __host__ __device__ inline int partial_rows_per_head(const PartialSum& ps) {
 // of a PartialSum, thread t of nt (nt a multiple of (Dk + Dv) / 4): the
 // dK / dV row of key i gets the partials of its block's parts >= 1 added in
 // slot order.  A thread takes one float4 column of every (nt / w)-th row,
-// with the loads of U rows in flight together; row and element counts fit
+// U rows at a time with the loads of up to MS slots of each in flight
+// together (further slots follow one at a time); row and element counts fit
 // in 32 bits.
 __device__ inline void partial_sum_rows(const PartialSum& ps, int r0, int r1, int t, int nt) {
-  constexpr int U = 4;
+  constexpr int U = 2, MS = 8;
   const int w = (ps.Dk + ps.Dv) / 4, wk = ps.Dk / 4, rw = ps.Dk + ps.Dv;
   const int c = t % w, rstep = nt / w, nrow = partial_rows_per_head(ps);
   for (int rb = r0 + t / w; rb < r1; rb += U * rstep) {
-    float4 v[U], x[U];
+    float4 v[U], y[U][MS];
     float* dst[U];
     const float* src[U];
     int parts[U], kbv[U];
@@ -1291,23 +1292,30 @@ __device__ inline void partial_sum_rows(const PartialSum& ps, int r0, int r1, in
         src[u] = ps.pt.base + ((int64_t)bh * ps.pt.nslot * BK + (i - kbv[u] * BK)) * rw + 4 * c;
         if (parts[u] >= 2) {
           v[u] = *(const float4*)dst[u];
-          x[u] = *(const float4*)(src[u] + (int64_t)partial_slot(ps.pt, kbv[u], 1) * BK * rw);
+#pragma unroll
+          for (int q = 1; q <= MS; ++q)
+            if (q < parts[u]) y[u][q - 1] = *(const float4*)(src[u] + (int64_t)partial_slot(ps.pt, kbv[u], q) * BK * rw);
         }
       }
     }
 #pragma unroll
     for (int u = 0; u < U; ++u) {
       if (parts[u] < 2) continue;
-      v[u].x += x[u].x;
-      v[u].y += x[u].y;
-      v[u].z += x[u].z;
-      v[u].w += x[u].w;
-      for (int q = 2; q < parts[u]; ++q) {
-        const float4 y = *(const float4*)(src[u] + (int64_t)partial_slot(ps.pt, kbv[u], q) * BK * rw);
-        v[u].x += y.x;
-        v[u].y += y.y;
-        v[u].z += y.z;
-        v[u].w += y.w;
+#pragma unroll
+      for (int q = 1; q <= MS; ++q) {
+        if (q < parts[u]) {
+          v[u].x += y[u][q - 1].x;
+          v[u].y += y[u][q - 1].y;
+          v[u].z += y[u][q - 1].z;
+          v[u].w += y[u][q - 1].w;
+        }
+      }
+      for (int q = MS + 1; q < parts[u]; ++q) {
+        const float4 z = *(const float4*)(src[u] + (int64_t)partial_slot(ps.pt, kbv[u], q) * BK * rw);
+        v[u].x += z.x;
+        v[u].y += z.y;
+        v[u].z += z.z;
+        v[u].w += z.w;
       }
       *(float4*)dst[u] = v[u];
     }
@@ -1395,22 +1403,10 @@ __global__ __launch_bounds__(NT, 2) void k_dq2(Params p, BwdArgs a, ZeroMulti zm
   const unsigned short* kp = (const unsigned short*)a.k + sv.k_off(p.k_str, b) + g * p.k_str[1];
   const unsigned short* vp = (const unsigned short*)a.v + sv.k_off(p.v_str, b) + g * p.v_str[1];
 
+  // Q / dO fragments (B operands) and the row's LSE and delta: loaded after
+  // the first K / V tiles are issued, so that all arrive in one round trip
   bf16x8 qB[NS], doB[NS];
-  {
-    const int64_t ic = min(irow, Sq - 1);
-#pragma unroll
-    for (int s = 0; s < NS; ++s) {
-      qB[s] = as_bf16x8(*(const u16x8*)(q + ic * p.q_str[2] + 16 * s + 8 * lg));
-      doB[s] = as_bf16x8(*(const u16x8*)(dout + ic * p.do_str[2] + 16 * s + 8 * lg));
-    }
-  }
   float lse2 = INFINITY, dls = 0.f;
-  if (irow < Sq) {
-    const float lv = a.lse[((int64_t)b * p.Hq + h) * p.Sq + irow];
-    lse2 = (lv == -INFINITY) ? INFINITY : lv * kLog2e;
-    dls = a.delta[((int64_t)b * p.Hq + h) * p.Sq + irow] * scale;
-  }
-  wait_vm_loads();
 
   auto tile_of = [&](int it) { return BK3 * (it < n1 ? it : a2 + (it - n1)); };
   // this wave's rows: a tile [j0, j0 + 32) is full when every key is
@@ -1480,14 +1476,24 @@ __global__ __launch_bounds__(NT, 2) void k_dq2(Params p, BwdArgs a, ZeroMulti zm
     // K tile buffer 3 zeroed (read by the zero dQ products ahead of tile 0)
 #pragma unroll
     for (int k = 0; k < TS / (16 * NT); ++k) *(u16x8*)&sm.k[NBQ - 1][16 * (tid + NT * k)] = u16x8{0, 0, 0, 0, 0, 0, 0, 0};
-    // tiles 0 and 1 in flight; 0 complete before the first barrier
+    // tiles 0 and 1, the Q / dO fragments, LSE and delta in flight together,
+    // all complete before the first barrier
     issue(0);
-    if (n_it > 1) {
-      issue(1);
-      wait_vm(NI);
-    } else {
-      wait_vm(0);
+    if (n_it > 1) issue(1);
+    {
+      const int64_t ic = min(irow, Sq - 1);
+#pragma unroll
+      for (int s = 0; s < NS; ++s) {
+        qB[s] = as_bf16x8(*(const u16x8*)(q + ic * p.q_str[2] + 16 * s + 8 * lg));
+        doB[s] = as_bf16x8(*(const u16x8*)(dout + ic * p.do_str[2] + 16 * s + 8 * lg));
+      }
     }
+    if (irow < Sq) {
+      const float lv = a.lse[((int64_t)b * p.Hq + h) * p.Sq + irow];
+      lse2 = (lv == -INFINITY) ? INFINITY : lv * kLog2e;
+      dls = a.delta[((int64_t)b * p.Hq + h) * p.Sq + irow] * scale;
+    }
+    wait_vm_loads();
 
     // operand read addresses in tile buffer 0
     const int a_lane = Swz<D>::a_lane(l), t_lane = Swz<D>::t_lane(l);
