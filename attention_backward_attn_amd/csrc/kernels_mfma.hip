@@ -624,7 +624,6 @@ __global__ __launch_bounds__(NT2) void k_dkdv2(Params p, BwdArgs a, DkdvGrid gd)
     }
     const int mode = slot ? kStore : out_mode;
     __syncthreads();  // readers of the previous unit's LDS tiles are done
-    wait_vm_loads();
     if (n_it <= 0) {
       // no query row reaches this part: stored rows get zeros (rows that
       // are added into keep their values)
@@ -687,17 +686,13 @@ __global__ __launch_bounds__(NT2) void k_dkdv2(Params p, BwdArgs a, DkdvGrid gd)
       }
       ld.next();
     };
-    // Prologue: tiles 0..3 in flight; 0..2 complete before the first barrier.
+    // Prologue: tiles 0..3 in flight together with the K / V fragments, all
+    // complete before the first barrier.
     issue(0);
 #pragma unroll
-    for (int j = 1; j < NB2 - 2; ++j)
+    for (int j = 1; j < NB2 - 1; ++j)
       if (n_it > j) issue(j);
-    if (n_it > NB2 - 2) {
-      issue(NB2 - 2);
-      wait_vm_c<NIW>();
-    } else {
-      wait_vm_c<0>();
-    }
+    wait_vm_loads();
     __syncthreads();
     // Wave 0 turns the raw LSE / delta rows of a complete tile into
     // LSE * log2(e) (+inf for a row without keys) and delta * scale, in place.
