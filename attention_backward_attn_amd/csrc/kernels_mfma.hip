@@ -12,19 +12,24 @@
 //     batch) loops over the G query heads of the group and the 32-row query
 //     tiles that can see the block, keeping dK and dV for its keys in
 //     registers (GQA group sums without atomics).  k_dkdv2 splits each
-//     32-key slice between a pair of waves on one SIMD (two waves per SIMD);
-//     k_dkdv, one wave per 32 keys, serves problems with a bias and walks the
-//     batch so that dbias is summed in a fixed order.
+//     32-key slice between a pair of waves on one SIMD (two waves per SIMD),
+//     with a bias at head dim 64 as well; k_dkdv, one wave per 32 keys,
+//     serves a bias at head dim 128 and walks the batch when dbias is asked,
+//     so that dbias is summed in a fixed order.
 //   * dQ by query blocks: k_dq2 (k_dq with a bias), one workgroup per
 //     (128-row block, query head, batch), recomputes S and dP per key tile
 //     and keeps dQ in registers.  k_dq2 may run first and also zero the
-//     dK / dV that the split key-block parts add into.
-// In every kernel S (or S^T) comes out of v_mfma_f32_32x32x16_bf16 with one
-// row or key per lane, and that accumulator layout is used directly as the
-// operand of the next product once the reduction index is permuted the same
-// way on both operands; the other operand is read from row-major LDS tiles,
-// with the gfx950 transposing read ds_read_b64_tr_b16 where the tile row is
-// the reduction index.
+//     dK / dV that the split key-block parts add into.  With a bias and
+//     dbias at head dim 64, k_dqb forms dQ and dbias together, walking the
+//     batch inside the workgroup (dbias summed in a fixed order, written
+//     once per group of entries).
+// In the 32x32 kernels S (or S^T) comes out of v_mfma_f32_32x32x16_bf16 with
+// one row or key per lane, and that accumulator layout is used directly as
+// the operand of the next product once the reduction index is permuted the
+// same way on both operands; the other operand is read from row-major LDS
+// tiles, with the gfx950 transposing read ds_read_b64_tr_b16 where the tile
+// row is the reduction index.  k_dqb does the same with
+// v_mfma_f32_16x16x32_bf16.
 //
 // MFMA 32x32x16 bf16 operand layout (lane l, r = 0..15):
 //   A[m][k]: lane holds m = l % 32, k = 8 (l / 32) + 0..7
