@@ -355,32 +355,45 @@ def test_deterministic_is_bitwise_repeatable(D):
         assert torch.equal(outs[0][kk], outs[1][kk]) and torch.equal(outs[0][kk], outs[2][kk]), kk
 
 
+# (B, Hq, Hk, S, D, bias): no bias (k_dkdv2 / k_dq2); a bias with dbias at
+# head dim 64 (k_dkdv2 with the bias, k_dqb) and at head dim 128 (k_dkdv
+# walking the batch, k_dq with the bias)
+ACC_CASES = [(1, 8, 2, 300, 128, False), (2, 4, 4, 200, 64, True), (2, 2, 2, 160, 128, True)]
+
+
+@pytest.mark.parametrize("case", ACC_CASES, ids=["nobias", "bias_d64", "bias_d128"])
 @pytest.mark.parametrize("flags", [0, ab.ATTN_DETERMINISTIC], ids=["atomic", "determ"])
-def test_accumulate_into_existing(flags):
+def test_accumulate_into_existing(flags, case):
     """ATTN_ACCUMULATE_DQ / ATTN_ACCUMULATE_DKDV add into the caller's
-    buffers: start from random contents and compare with contents + oracle."""
-    x = random_case(1, 8, 2, 300, 300, 128, 128, "bf16", 21, False, False)
+    buffers: start from random contents and compare with contents + oracle
+    (dbias, when asked, is written, not added)."""
+    B, Hq, Hk, S, D, with_bias = case
+    x = random_case(B, Hq, Hk, S, S, D, D, "bf16", 21, with_bias, False)
     spec = MaskSpec("top_left")
-    scale = 1 / np.sqrt(128)
-    say(f"[accumulate] flags={flags}")
-    o64, lse64 = oracle.forward(x["q"], x["k"], x["v"], scale, spec)
+    scale = 1 / np.sqrt(D)
+    say(f"[accumulate] case={case} flags={flags}")
+    o64, lse64 = oracle.forward(x["q"], x["k"], x["v"], scale, spec, x["bias"])
     o32, lse32 = o64.astype(np.float32), lse64.astype(np.float32)
-    ref = oracle.backward(x["q"], x["k"], x["v"], o32, x["do"], lse32, scale, spec)
+    ref = oracle.backward(x["q"], x["k"], x["v"], o32, x["do"], lse32, scale, spec, x["bias"])
     dt = torch.bfloat16
     q, k, v, do = (dev(x[n], dt) for n in ("q", "k", "v", "do"))
     o, lse = dev(o32, torch.float32), dev(lse32, torch.float32)
+    bias = dev(x["bias"], torch.float32)
+    dbias = None if bias is None else torch.full_like(bias, float("nan"))
     rng = np.random.default_rng(3)
     init = {n: rng.standard_normal(ref[n].shape).astype(np.float32) for n in ("dq", "dk", "dv")}
     dq, dk, dv = (dev(init[n], torch.float32) for n in ("dq", "dk", "dv"))
     delta = torch.empty_like(lse)
-    p = ab.make_problem(q, k, v, o=o, do=do, dq=dq, dk=dk, dv=dv, scale=scale, mask="top_left")
+    p = ab.make_problem(q, k, v, o=o, do=do, dq=dq, dk=dk, dv=dv, bias=bias, scale=scale, mask="top_left")
     ab.attn_bwd_preprocess(p, o, do, lse, None, delta, None, None, None, None)
-    ab.attn_bwd(p, q, k, v, do, lse, delta, None, dq, dk, dv, None,
+    ab.attn_bwd(p, q, k, v, do, lse, delta, bias, dq, dk, dv, dbias,
                 flags | ab.ATTN_ACCUMULATE_DQ | ab.ATTN_ACCUMULATE_DKDV)
     torch.cuda.synchronize()
     for n, t in (("dq", dq), ("dk", dk), ("dv", dv)):
         got = t.cpu().numpy().astype(np.float64) - init[n]
         check(n, got, ref[n], 2e-2)
+    if dbias is not None:
+        check("dbias", dbias.cpu().numpy().astype(np.float64), ref["dbias"], 2e-2)
 
 
 @pytest.mark.parametrize("shape", [(1, 4, 1, 200, 700), (4, 8, 8, 256, 2048)], ids=["split", "unsplit"])
