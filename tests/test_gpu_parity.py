@@ -264,6 +264,57 @@ def test_forward_bf16_output():
     check("o", o, o_ref, TOL["bf16"])
 
 
+# (B, Hq, Hk, S, D, dtype, mask, bias): the matrix-core path (head dims 128
+# and 64 with a bias) and the fp32 path
+BSHD_CASES = [(2, 8, 2, 200, 128, "bf16", MaskSpec("bottom_right"), False),
+              (2, 4, 4, 160, 64, "bf16", MaskSpec("top_left"), True),
+              (1, 4, 2, 96, 64, "f32", MaskSpec("none"), False)]
+
+
+def bshd_view(a, dtype):
+    """numpy [B, H, S, D] -> device memory in [B, S, H, D] order, returned as
+    its [B, H, S, D] view (row stride H D, head stride D)."""
+    t = torch.from_numpy(np.ascontiguousarray(a.transpose(0, 2, 1, 3))).to("cuda", dtype)
+    return t.transpose(1, 2)
+
+
+@pytest.mark.parametrize("case", BSHD_CASES, ids=["gqa_d128", "bias_d64", "f32"])
+def test_bshd_layout(case):
+    """Tensors stored [B, S, H, D] (native BSHD, the Ascend interface's
+    layout option) pass through the ABI as strides: the forward O and every
+    gradient match the oracle as for [B, H, S, D] storage."""
+    B, Hq, Hk, S, D, dtype, spec, with_bias = case
+    say(f"[bshd] {case}")
+    x = random_case(B, Hq, Hk, S, S, D, D, dtype, 41, with_bias, False)
+    scale = 1 / np.sqrt(D)
+    o64, lse64 = oracle.forward(x["q"], x["k"], x["v"], scale, spec, x["bias"])
+    o32, lse32 = o64.astype(np.float32), lse64.astype(np.float32)
+    ref = oracle.backward(x["q"], x["k"], x["v"], o32, x["do"], lse32, scale, spec, x["bias"])
+    dt = tdtype(dtype)
+    q, k, v, do = (bshd_view(x[n], dt) for n in ("q", "k", "v", "do"))
+    nan = lambda a: bshd_view(np.full(a.shape, np.nan, np.float32), torch.float32)
+    o = nan(o32)
+    lse = torch.empty(B, Hq, S, device="cuda")
+    dq, dk, dv = nan(ref["dq"]), nan(ref["dk"]), nan(ref["dv"])
+    bias = dev(x["bias"], torch.float32)
+    dbias = None if bias is None else torch.full_like(bias, float("nan"))
+    p = ab.make_problem(q, k, v, o=o, do=do, dq=dq, dk=dk, dv=dv, bias=bias, scale=scale, **mask_kw(spec))
+    assert tuple(p.q_str) == (S * Hq * D, D, Hq * D)
+    ab.attn_fwd_lse(p, q, k, v, bias, None, o, lse)
+    torch.cuda.synchronize()
+    tol = 1e-4 if dtype == "f32" else TOL["bf16"]
+    check("o", o.cpu().numpy().astype(np.float64), o64, tol)
+    # the backward from the oracle's O / LSE, O stored [B, S, H, D] too
+    o_in, lse_in = bshd_view(o32, torch.float32), dev(lse32, torch.float32)
+    delta = torch.empty_like(lse_in)
+    ab.attn_bwd_preprocess(p, o_in, do, lse_in, None, delta, None, None, None, None)
+    ab.attn_bwd(p, q, k, v, do, lse_in, delta, bias, dq, dk, dv, dbias, 0)
+    torch.cuda.synchronize()
+    for n, t in (("dq", dq), ("dk", dk), ("dv", dv), ("dbias", dbias)):
+        if t is not None:
+            check(n, t.cpu().numpy().astype(np.float64), ref[n], tol)
+
+
 def test_lse_merge_parity():
     say("[merge]")
     rng = np.random.default_rng(12)
