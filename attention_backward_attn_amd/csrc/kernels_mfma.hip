@@ -541,7 +541,38 @@ __global__ __launch_bounds__(NT2) void k_dkdv2(Params p, BwdArgs a, DkdvGrid gd)
   // with a bias (shared over the batch) the batch entries of a unit run side
   // by side, so each bias tile comes from HBM about once
   const BlockXYZ blk = BIAS ? xcd_block_zfast() : xcd_block();
-  const int b = blk.z;
+  // a packed batch takes its sequences by decreasing work (query rows x
+  // keys, ties by index): each XCD walks its logical blocks with the key
+  // blocks fastest, then the batch index, so the longest sequences' units
+  // start first and the short ones fill the end (batch index z stands for
+  // the sequence of rank z; the P exchange area, unused until the first
+  // tile, holds the prefix sums meanwhile)
+  int b = blk.z;
+  if (p.cu_k != nullptr && p.B <= NT2) {
+    int* cu = (int*)&sm.px;   // cu_q[0 .. B], cu_k[0 .. B], the answer
+    for (int i = tid; i <= p.B; i += NT2) {
+      cu[i] = p.cu_q[i];
+      cu[p.B + 1 + i] = p.cu_k[i];
+    }
+    __syncthreads();
+    if (tid < p.B) {
+      auto work = [&](int s_) {
+        const int lq = min(max(cu[s_ + 1] - cu[s_], 0), p.Sq);
+        const int lk = min(max(cu[p.B + 2 + s_] - cu[p.B + 1 + s_], 0), p.Sk);
+        return (int64_t)lq * lk;
+      };
+      const int64_t wt = work(tid);
+      int rank = 0;
+      for (int s_ = 0; s_ < p.B; ++s_) {
+        const int64_t ws = work(s_);
+        rank += (ws > wt) | ((ws == wt) & (s_ < tid));
+      }
+      if (rank == blk.z) cu[2 * p.B + 2] = tid;
+    }
+    __syncthreads();
+    b = __builtin_amdgcn_readfirstlane(cu[2 * p.B + 2]);
+    __syncthreads();   // every wave has read it before the area is reused
+  }
   const SeqView sv = seq_view(p, b);   // this batch entry (or packed sequence)
   const Mask& msk = sv.mask;
   const int Sq = sv.Sq, Sk = sv.Sk;
