@@ -7,6 +7,10 @@
 //   O = exp(S - LSE) V.  Rows with no allowed key and no sink: O = 0,
 //   LSE = -inf.
 //
+// Without a bias the forward runs k_fwd2 (below: buffer-to-LDS tiles in one
+// swizzled copy, the S chain among the previous tile's O products); k_fwd
+// serves problems with a bias.
+//
 // Kernel k_fwd: one workgroup per (128-row query block, query head, batch);
 // wave w owns rows [32 w, 32 w + 32).  Per tile of KT keys, S^T = K Q^T
 // with the wave's Q fragments in registers as the B operand and K rows from
