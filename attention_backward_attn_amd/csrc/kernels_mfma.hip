@@ -965,6 +965,602 @@ __global__ __launch_bounds__(NT2) void k_dkdv2(Params p, BwdArgs a, DkdvGrid gd)
   }
 }
 
+// ---------------------------------------------------------------------------
+// Kernel k_dkdv3 (dK / dV without a bias, head dim 128): the wave pairs of
+// k_dkdv2 on 64-row query tiles.  Per tile each wave issues 32 products --
+// two independent S (or dP) chains of 8 over the head dim and 16 dV (or dK)
+// products -- where a 32-row tile gives it 16, so the barrier, the hand-over
+// of P and the operand reads that follow the barrier are paid once per 64
+// rows, and no wave waits on a single dependent chain.
+// LDS (130 KB): the Q and dO tiles in three swizzled buffers each, loaded
+// two tiles ahead; the rows' LSE and delta in four buffers, loaded three
+// tiles ahead and prepared in place (LSE * log2(e), delta * scale) by wave 0
+// two tiles before their use; P handed from the S wave to the dP wave as the
+// bf16 operand registers the S wave itself multiplies with, in two buffers by
+// tile parity.  Per tile t, one barrier:
+//   S wave:  S(t + 1) = Q K^T as two chains (rows 0..31 and 32..63,
+//            alternating), then dV += P(t)^T dO(t) with the exponentials,
+//            masking and bf16 rounding of P(t + 1) = exp2(S - LSE) among
+//            those products; P(t + 1) published before the next barrier.
+//   dP wave: dP(t + 1) = dO V^T as two alternating chains, with
+//            dS(t) = P(t) (dP(t) scale - delta scale) of rows 0..31 among
+//            the first eight; dK += dS(t)^T Q(t) for rows 0..31 among the
+//            last eight (with the dS of rows 32..63), then for rows 32..63.
+// ---------------------------------------------------------------------------
+constexpr int BQ4 = 64;   // query rows per tile (k_dkdv3)
+constexpr int NB4 = 3;    // Q / dO tile buffers
+constexpr int NL4 = 4;    // LSE / delta row buffers
+
+template <int D>
+struct __attribute__((aligned(1024))) SmemDKDV3 {
+  unsigned char q[NB4][BQ4 * 2 * D];   // Q tile, swizzled (A of S = Q K^T; tr B of dK += dS^T Q)
+  unsigned char d[NB4][BQ4 * 2 * D];   // dO tile, swizzled (A of dP = dO V^T; tr B of dV += P^T dO)
+  u16x8 px[2][4][4][64];               // P as bf16 operands: [tile % 2][pair][operand][lane]
+  float lse[NL4][BQ4];                 // LSE of the tile's rows, then LSE * log2(e) (+inf: no keys)
+  float dl[NL4][BQ4];                  // delta of the tile's rows, then delta * scale
+};
+
+// Walk over the (query head, 64-row tile) sequence of a unit part: Q / dO
+// tile pointers, or LSE / delta row pointers, one tile at a time.
+struct Walk64 {
+  const void *x, *y;   // Q and dO (bytes), or LSE and delta (floats)
+  int qb, i0;
+  __device__ inline void next(int nqb, int lo_al, int64_t x_step, int64_t y_step, int64_t x_wrap, int64_t y_wrap) {
+    x = (const char*)x + x_step;
+    y = (const char*)y + y_step;
+    i0 += BQ4;
+    if (++qb == nqb) {
+      qb = 0;
+      i0 = lo_al;
+      x = (const char*)x + x_wrap;
+      y = (const char*)y + y_wrap;
+    }
+  }
+};
+
+template <int D>
+__global__ __launch_bounds__(NT2) void k_dkdv3(Params p, BwdArgs a, DkdvGrid gd) {
+  static_assert(D == 128, "head dim");
+  constexpr int NS = D / 16;                   // k-steps over the head dim
+  constexpr int NC = D / 32;                   // 32-column blocks of dK / dV
+  constexpr int RB = Swz<D>::RB, CR = Swz<D>::CR;
+  constexpr int TS = BQ4 * RB;                 // tile bytes
+  constexpr int SLW = BQ4 * CR / 64 / 8;       // 1 KB slots of each tile loaded per wave
+  constexpr int HB = 32 * RB;                  // byte offset of rows 32..63
+  __shared__ SmemDKDV3<D> sm;
+
+  const int tid = threadIdx.x, l = tid & 63, lr = l & 31, lg = l >> 5;
+  const int w = __builtin_amdgcn_readfirstlane(tid >> 6);   // wave-uniform
+  const int pr = w & 3;               // pair: keys [32 pr, 32 pr + 32) of the block
+  const bool sw = w < 4;              // S wave (else dP wave)
+  const BlockXYZ blk = xcd_block();
+  // packed batch: batch index z stands for the sequence of rank z by work
+  // (query rows x keys, ties by index), longest first (as in k_dkdv2)
+  int b = blk.z;
+  if (p.cu_k != nullptr && p.B <= NT2) {
+    int* cu = (int*)&sm.px;   // cu_q[0 .. B], cu_k[0 .. B], the answer
+    for (int i = tid; i <= p.B; i += NT2) {
+      cu[i] = p.cu_q[i];
+      cu[p.B + 1 + i] = p.cu_k[i];
+    }
+    __syncthreads();
+    if (tid < p.B) {
+      auto work = [&](int s_) {
+        const int lq = min(max(cu[s_ + 1] - cu[s_], 0), p.Sq);
+        const int lk = min(max(cu[p.B + 2 + s_] - cu[p.B + 1 + s_], 0), p.Sk);
+        return (int64_t)lq * lk;
+      };
+      const int64_t wt = work(tid);
+      int rank = 0;
+      for (int s_ = 0; s_ < p.B; ++s_) {
+        const int64_t ws = work(s_);
+        rank += (ws > wt) | ((ws == wt) & (s_ < tid));
+      }
+      if (rank == blk.z) cu[2 * p.B + 2] = tid;
+    }
+    __syncthreads();
+    b = __builtin_amdgcn_readfirstlane(cu[2 * p.B + 2]);
+    __syncthreads();   // every wave has read it before the area is reused
+  }
+  const SeqView sv = seq_view(p, b);
+  const Mask& msk = sv.mask;
+  const int Sq = sv.Sq, Sk = sv.Sk;
+  const int nkb = (Sk + BK - 1) / BK;
+  const int hk = blk.y / gd.nsplit;
+  int part = blk.y % gd.nsplit, nparts = gd.nsplit;
+  int kbx = blk.x;
+  if (gd.nsplit0 > 1) {
+    if (kbx < gd.nsplit0) {
+      part = kbx * gd.nsplit + part;
+      nparts = gd.nsplit0 * gd.nsplit;
+      kbx = 0;
+    } else {
+      kbx -= gd.nsplit0 - 1;
+    }
+  }
+  const int h_begin = hk * p.G;
+  const float scale = p.scale, scale_log2 = p.scale * kLog2e;
+  const bool unit_in = gd.pair ? 2 * kbx < nkb : kbx < nkb;
+  const int n_units = !unit_in ? 0 : ((gd.pair && nkb - 1 - kbx != kbx) ? 2 : 1);
+  const int out_mode = gd.out_mode;
+  const bool no_mask = msk.kind == kMaskNone;
+  const int lo_t = msk.wl < 0 ? -0x3fffffff : -msk.wl;
+  const int wr_t = msk.wr;
+  const int a_lane = Swz<D>::a_lane(l), t_lane = Swz<D>::t_lane(l);
+  const int q_rb = 2 * (int)p.q_str[2], d_rb = 2 * (int)p.do_str[2];
+  const unsigned int sm_base = __builtin_amdgcn_readfirstlane(lds_addr(&sm));
+  // staging: wave w fills the 1 KB slots SLW w .. SLW w + SLW - 1 (rows
+  // 4 slot .. 4 slot + 3) of each Q and dO tile; one fixed source offset per
+  // lane and slot, the chunk order swizzled
+  int qv[SLW], dv_[SLW];
+#pragma unroll
+  for (int k = 0; k < SLW; ++k) {
+    const int slot = SLW * w + k, row = (64 * slot + l) / CR, c = l % CR;
+    qv[k] = row * q_rb + 16 * (c ^ Swz<D>::f(row));
+    dv_[k] = row * d_rb + 16 * (c ^ Swz<D>::f(row));
+  }
+
+  for (int u = 0; u < n_units; ++u) {
+    const int kb = u == 0 ? kbx : nkb - 1 - kbx;
+    const int k0 = kb * BK;
+    const int kw = k0 + 32 * pr;
+    const int jkey = kw + lr;
+    const bool key_ok = jkey < Sk;
+    const int jg = jkey + (int)msk.k_off;
+    const bool sink_key = jg < msk.n_sink;
+    int64_t lo64, hi64;
+    msk.rows_for_keys(k0, min(k0 + BK, Sk), Sq, &lo64, &hi64);
+    const int lo = (int)lo64, hi = (int)hi64;
+    const int lo_al = lo & ~(BQ4 - 1);
+    const int nqb = hi > lo ? (hi - lo_al + BQ4 - 1) / BQ4 : 0;
+    const int n_all = p.G * nqb;
+    const int it_lo = (int)((int64_t)n_all * part / nparts);
+    const int n_it = (int)((int64_t)n_all * (part + 1) / nparts) - it_lo;
+    // 32-row halves [i, i + 32) in which every row sees all 32 keys of this
+    // wave: i >= full_a and i + 31 <= full_c
+    int full_a = -0x3fffffff, full_c = 0x3fffffff;
+    if (kw + 32 > Sk) {
+      full_a = 0x3fffffff;
+    } else if (!no_mask && kw + 31 + msk.k_off >= msk.n_sink) {
+      const int64_t base = (int64_t)kw + msk.k_off - msk.q_off - msk.diag;
+      full_a = (int)max<int64_t>(min<int64_t>(base + 31 - msk.wr, 0x3fffffff), -0x3fffffff);
+      if (msk.wl >= 0) full_c = (int)max<int64_t>(min<int64_t>(base + msk.wl, 0x3fffffff), -0x3fffffff);
+    }
+
+    // K (S wave) or V (dP wave) fragments of this pair's keys: B operands
+    bf16x8 fB[NS];
+    {
+      const unsigned short* src = sw ? (const unsigned short*)a.k + sv.k_off(p.k_str, b) + hk * p.k_str[1]
+                                     : (const unsigned short*)a.v + sv.k_off(p.v_str, b) + hk * p.v_str[1];
+      const int64_t rs = sw ? p.k_str[2] : p.v_str[2];
+      const int64_t jc = min(jkey, Sk - 1);
+#pragma unroll
+      for (int s = 0; s < NS; ++s) fB[s] = as_bf16x8(*(const u16x8*)(src + jc * rs + 16 * s + 8 * lg));
+    }
+    // where this wave's dV (S wave) or dK (dP wave) rows go (as in k_dkdv2)
+    const bool slot = gd.pt.base != nullptr && part > 0;
+    float* op;
+    int64_t os, jr;
+    if (slot) {
+      const int rw = p.Dqk + p.Dv;
+      op = gd.pt.base + (((int64_t)b * p.Hk + hk) * gd.pt.nslot + partial_slot(gd.pt, kb, part)) * BK * rw +
+           (sw ? p.Dqk : 0);
+      os = rw;
+      jr = k0;
+    } else {
+      op = sw ? a.dv + sv.k_off(p.dv_str, b) + hk * p.dv_str[1] : a.dk + sv.k_off(p.dk_str, b) + hk * p.dk_str[1];
+      os = sw ? p.dv_str[2] : p.dk_str[2];
+      jr = 0;
+    }
+    const int mode = slot ? kStore : out_mode;
+    __syncthreads();  // readers of the previous unit's LDS tiles are done
+    if (n_it <= 0) {
+      if (mode == kStore) {
+#pragma unroll
+        for (int n = 0; n < NC; ++n)
+#pragma unroll
+          for (int r = 0; r < 16; ++r) {
+            const int64_t j = kw + crow(r, lg);
+            if (j < Sk) op[(j - jr) * os + 32 * n + lr] = 0.f;
+          }
+      }
+      continue;
+    }
+
+    // tile walks: `wqd` issues the Q / dO tiles (two ahead), `wl` the LSE /
+    // delta rows (three ahead)
+    Walk64 wqd, wl;
+    const int64_t q_step = (int64_t)BQ4 * p.q_str[2] * 2, d_step = (int64_t)BQ4 * p.do_str[2] * 2;
+    const int64_t q_wrap = p.q_str[1] * 2 - nqb * q_step, d_wrap = p.do_str[1] * 2 - nqb * d_step;
+    const int64_t l_step = BQ4 * 4, l_wrap = ((int64_t)p.Sq - (int64_t)nqb * BQ4) * 4;
+    {
+      const int h0 = h_begin + it_lo / nqb, qb0 = it_lo % nqb;
+      const int i00 = lo_al + BQ4 * qb0;
+      wqd.x = (const unsigned short*)a.q + sv.q_off(p.q_str, b) + h0 * p.q_str[1] + (int64_t)i00 * p.q_str[2];
+      wqd.y = (const unsigned short*)a.dout + sv.q_off(p.do_str, b) + h0 * p.do_str[1] + (int64_t)i00 * p.do_str[2];
+      const int64_t rb = ((int64_t)b * p.Hq + h0) * p.Sq + i00;
+      wl.x = a.lse + rb;
+      wl.y = a.delta + rb;
+      wqd.qb = wl.qb = qb0;
+      wqd.i0 = wl.i0 = i00;
+    }
+    int fr_i0 = wqd.i0, fr_qb = wqd.qb;   // first row of the tile whose P the S wave forms next
+    auto fr_next = [&]() {
+      fr_i0 += BQ4;
+      if (++fr_qb == nqb) { fr_qb = 0; fr_i0 = lo_al; }
+    };
+    auto issue_qd = [&](int buf) {
+      const int rows = min(Sq - wqd.i0, BQ4);
+      const __amdgpu_buffer_rsrc_t rq = buf_rsrc(wqd.x, rows * q_rb), rd = buf_rsrc(wqd.y, rows * d_rb);
+      const unsigned int mq = sm_base + offsetof(SmemDKDV3<D>, q) + buf * TS + 1024 * SLW * w;
+      const unsigned int md = sm_base + offsetof(SmemDKDV3<D>, d) + buf * TS + 1024 * SLW * w;
+#pragma unroll
+      for (int k = 0; k < SLW; ++k) lds_dma16(rq, mq + 1024 * k, qv[k]);
+#pragma unroll
+      for (int k = 0; k < SLW; ++k) lds_dma16(rd, md + 1024 * k, dv_[k]);
+      wqd.next(nqb, lo_al, q_step, d_step, q_wrap, d_wrap);
+    };
+    auto issue_l = [&](int lb) {
+      if (w == 0) {
+        const int rows = min(Sq - wl.i0, BQ4);
+        lds_dma4(buf_rsrc(wl.x, rows * 4), sm_base + offsetof(SmemDKDV3<D>, lse) + lb * (4 * BQ4), 4 * l);
+        lds_dma4(buf_rsrc(wl.y, rows * 4), sm_base + offsetof(SmemDKDV3<D>, dl) + lb * (4 * BQ4), 4 * l);
+      }
+      wl.next(nqb, lo_al, l_step, l_step, l_wrap, l_wrap);
+    };
+    // wave 0 turns the raw rows of a complete buffer into LSE * log2(e)
+    // (+inf for a row without keys) and delta * scale; rows past the end
+    // hold zeros (P = 1 there, against zero Q / dO rows)
+    auto prep = [&](int lb) {
+      if (w == 0) {
+        const float x = sm.lse[lb][l], y = sm.dl[lb][l];
+        sm.lse[lb][l] = x == -INFINITY ? INFINITY : x * kLog2e;
+        sm.dl[lb][l] = y * scale;
+      }
+    };
+    // Prologue: Q / dO tiles 0, 1 and LSE / delta rows 0..2 in flight
+    // together with the K / V fragments, all complete before the barrier.
+    issue_qd(0);
+    if (n_it > 1) issue_qd(1);
+    issue_l(0);
+    if (n_it > 1) issue_l(1);
+    if (n_it > 2) issue_l(2);
+    wait_vm_loads();
+    __syncthreads();
+    prep(0);
+    if (n_it > 1) prep(1);
+    __syncthreads();
+
+    // Per-lane key window of the masked exponentials (as in k_dkdv2).
+    int lo_l = lo_t, span = wr_t - lo_t;
+    if (no_mask | sink_key) { lo_l = -0x3fffffff; span = 0x7ffffffe; }
+    if (!key_ok) { lo_l = 0x3fffffff; span = 0; }
+    const int tb0 = jg - (int)msk.q_off - (int)msk.diag - 4 * lg - lo_l;
+
+    // The loads of Q / dO tile t + 2 (into the buffer of tile t - 1), set up
+    // at barrier t and issued one 1 KB slot at a time among the wave's first
+    // products: issued together right after the barrier, the eight waves'
+    // loads queue for the vector memory unit and hold up every wave's
+    // products behind them.  Past the last tile they load nothing (zeros).
+    struct DmaSet {
+      __amdgpu_buffer_rsrc_t rq, rd;
+      unsigned int mq, md;
+    };
+    auto dma_set = [&](int t, int buf) {
+      DmaSet d;
+      const bool on = t + 2 < n_it;
+      const int rows = on ? min(Sq - wqd.i0, BQ4) : 0;
+      d.rq = buf_rsrc(wqd.x, rows * q_rb);
+      d.rd = buf_rsrc(wqd.y, rows * d_rb);
+      d.mq = sm_base + offsetof(SmemDKDV3<D>, q) + buf * TS + 1024 * SLW * w;
+      d.md = sm_base + offsetof(SmemDKDV3<D>, d) + buf * TS + 1024 * SLW * w;
+      if (on) wqd.next(nqb, lo_al, q_step, d_step, q_wrap, d_wrap);
+      return d;
+    };
+    auto dma_one = [&](const DmaSet& d, int k) {   // k < SLW: Q slot k, else dO slot k - SLW
+      if (k < SLW) lds_dma16(d.rq, d.mq + 1024 * k, qv[k]);
+      else lds_dma16(d.rd, d.md + 1024 * (k - SLW), dv_[k - SLW]);
+    };
+    // one tile's common start: barrier t, the loads of the rows of tile
+    // t + 3, the rows of tile t + 2 prepared
+    auto tile_head = [&](int t) {
+      __syncthreads();  // P(t) published; tile t + 1 and rows t + 2 complete; tile t - 1's buffers free
+      if (t + 3 < n_it) issue_l((t + 3) & 3);
+      if (t + 2 < n_it) prep((t + 2) & 3);
+    };
+
+    if (sw) {
+      // ------------------------------------------------------------------ S wave
+      f32x16 og[NC];   // dV, columns 32 n + lane
+#pragma unroll
+      for (int n = 0; n < NC; ++n) og[n] = zero16();
+      unsigned int ar[NS], br[NC];
+#pragma unroll
+      for (int s = 0; s < NS; ++s) ar[s] = sm_base + offsetof(SmemDKDV3<D>, q) + (a_lane ^ (32 * s));
+#pragma unroll
+      for (int n = 0; n < NC; ++n) br[n] = sm_base + offsetof(SmemDKDV3<D>, d) + (t_lane ^ (64 * n));
+      // chain step c of S: rows 32 (c % 2) .., k-step c / 2
+      auto read_a = [&](int j, int c) { return lds_b128_at(ar[c >> 1] + j * TS + (c & 1) * HB); };
+      // dV product i: accumulator i % NC, tile rows 16 (i / NC) .. (reduction slots)
+      auto read_v = [&](int j, int i) {
+        const int n = i % NC, r0 = 16 * (i / NC);
+        return cat44(lds_tr4_at(br[n] + j * TS + r0 * RB), lds_tr4_at((br[n] ^ 32) + j * TS + (r0 + 8) * RB));
+      };
+      // exponent, mask and bf16 rounding of half h of S (rows 32 h ..) of the
+      // tile whose first row is i0, with the prepared LSE rows lrow
+      auto lse_vals = [&](f32x4* L4, const float* lrow, int h) {
+#pragma unroll
+        for (int m = 0; m < 4; ++m) L4[m] = *(const f32x4*)&lrow[32 * h + 8 * m + 4 * lg];
+      };
+      auto mask_pack = [&](float* pv, int i0h, bf16x8* dst2) {
+        if (!(i0h >= full_a && i0h + 31 <= full_c)) {
+          const int tb = tb0 - i0h;
+#pragma unroll
+          for (int r = 0; r < 16; ++r) {
+            const unsigned int tt = (unsigned int)(tb - (8 * (r >> 2) + (r & 3)));
+            pv[r] = tt <= (unsigned int)span ? pv[r] : 0.f;
+          }
+        }
+        dst2[0] = pack8(pv);
+        dst2[1] = pack8(pv + 8);
+      };
+      auto publish = [&](const bf16x8* pn, int par) {
+#pragma unroll
+        for (int k = 0; k < 4; ++k) sm.px[par][pr][k][l] = __builtin_bit_cast(u16x8, pn[k]);
+      };
+      bf16x8 pa[4];   // P(t) as dV operands: rows 16 k .. 16 k + 15 in slot order
+      {
+        // P(0): both chains on Q tile 0, then the exponentials
+        f32x16 s0 = zero16(), s1 = zero16();
+#pragma unroll
+        for (int s = 0; s < NS; ++s) {
+          s0 = mfma(read_a(0, 2 * s), fB[s], s0);
+          s1 = mfma(read_a(0, 2 * s + 1), fB[s], s1);
+        }
+        f32x4 L4[4];
+        float pv[16];
+        lse_vals(L4, sm.lse[0], 0);
+#pragma unroll
+        for (int r = 0; r < 16; ++r) pv[r] = __builtin_amdgcn_exp2f(fmaf(s0[r], scale_log2, -L4[r >> 2][r & 3]));
+        mask_pack(pv, fr_i0, pa);
+        lse_vals(L4, sm.lse[0], 1);
+#pragma unroll
+        for (int r = 0; r < 16; ++r) pv[r] = __builtin_amdgcn_exp2f(fmaf(s1[r], scale_log2, -L4[r >> 2][r & 3]));
+        mask_pack(pv, fr_i0 + 32, pa + 2);
+        publish(pa, 0);
+        fr_next();
+      }
+      constexpr int VPRE = 2;   // dV operands read before the barrier
+      bf16x8 vn[VPRE];
+#pragma unroll
+      for (int i = 0; i < VPRE; ++i) vn[i] = read_v(0, i);
+      constexpr int AH = 2;     // operand reads in flight ahead of their product
+      auto tile = [&](int t, auto jc) {
+        constexpr int j = decltype(jc)::value, j1 = (j + 1) % NB4;
+        tile_head(t);
+        const DmaSet dma = dma_set(t, (j + 2) % NB4);
+        const float* lrow = sm.lse[(t + 1) & 3];
+        f32x16 s0 = zero16(), s1 = zero16();
+        bf16x8 xa[2 * NS], bv[16];
+#pragma unroll
+        for (int i = 0; i < VPRE; ++i) bv[i] = vn[i];
+#pragma unroll
+        for (int c = 0; c < AH; ++c) xa[c] = read_a(j1, c);
+        __builtin_amdgcn_sched_barrier(0);
+        // dV products 0, 1 (operands already here) cover the first reads
+#pragma unroll
+        for (int i = 0; i < VPRE; ++i) og[i % NC] = mfma(pa[i / NC], bv[i], og[i % NC]);
+#pragma unroll
+        for (int i = VPRE; i < VPRE + AH; ++i) bv[i] = read_v(j, i);
+        __builtin_amdgcn_sched_barrier(0);
+        // the two S chains, alternating
+#pragma unroll
+        for (int c = 0; c < 2 * NS; ++c) {
+          if (c & 1) s1 = mfma(xa[c], fB[c >> 1], s1);
+          else s0 = mfma(xa[c], fB[c >> 1], s0);
+          if (c + AH < 2 * NS) xa[c + AH] = read_a(j1, c + AH);
+          if (c % 3 == 0 && c / 3 < 2 * SLW) dma_one(dma, c / 3);
+          __builtin_amdgcn_sched_barrier(0);
+        }
+        // the remaining dV products, among the exponentials of both halves
+        // (element r: half r / 16, its LSE in the four-row group r / 4,
+        // read one product ahead of the group's first exponential)
+        float pv[32];
+        constexpr int NV = 16 - VPRE;          // products in this region
+        auto r_lo = [](int k) { return (32 * k + NV - 1) / NV; };   // first element of product k
+        auto lse4 = [&](int g) {   // rows of four-element group g
+          return *(const f32x4*)&lrow[32 * (g >> 2) + 8 * (g & 3) + 4 * lg];
+        };
+        f32x4 L4[8];
+        L4[0] = lse4(0);
+#pragma unroll
+        for (int k = 0; k < NV; ++k) {
+          const int i = VPRE + k;
+          og[i % NC] = mfma(pa[i / NC], bv[i], og[i % NC]);
+#pragma unroll
+          for (int r = r_lo(k); r < r_lo(k + 1); ++r) {
+            const float sv_ = r < 16 ? s0[r] : s1[r - 16];
+            pv[r] = __builtin_amdgcn_exp2f(fmaf(sv_, scale_log2, -L4[r >> 2][r & 3]));
+            // (kept here: otherwise the compiler sinks them below the products)
+            asm volatile("" : "+v"(pv[r]));
+          }
+#pragma unroll
+          for (int g = 1; g < 8; ++g)
+            if (4 * g >= r_lo(k + 1) && 4 * g < r_lo(k + 2)) L4[g] = lse4(g);
+          if (i + AH < 16) bv[i + AH] = read_v(j, i + AH);
+          __builtin_amdgcn_sched_barrier(0);
+        }
+        bf16x8 pn[4];
+        mask_pack(pv, fr_i0, pn);
+        mask_pack(pv + 16, fr_i0 + 32, pn + 2);
+        // (unconditional: past the last tile it writes an unread buffer)
+        publish(pn, (t + 1) & 1);
+        fr_next();
+#pragma unroll
+        for (int k = 0; k < 4; ++k) pa[k] = pn[k];
+        // dV operands of tile t + 1 (complete since barrier t)
+#pragma unroll
+        for (int i = 0; i < VPRE; ++i) vn[i] = read_v(j1, i);
+        wait_vm_loads();   // this wave's loads of tile t + 2 done before the next barrier
+      };
+      for (int t0 = 0; t0 < n_it; t0 += NB4) {
+        tile(t0, std::integral_constant<int, 0>{});
+        if (t0 + 1 >= n_it) break;
+        tile(t0 + 1, std::integral_constant<int, 1>{});
+        if (t0 + 2 >= n_it) break;
+        tile(t0 + 2, std::integral_constant<int, 2>{});
+      }
+#pragma unroll
+      for (int n = 0; n < NC; ++n) {
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+          const int64_t j = kw + crow(r, lg);
+          if (j < Sk) {
+            float* po = op + (j - jr) * os + 32 * n + lr;
+            if (mode == kAtomicAdd) atomic_add_f32(po, og[n][r]);
+            else if (mode == kAddInto) *po += og[n][r];
+            else *po = og[n][r];
+          }
+        }
+      }
+    } else {
+      // ----------------------------------------------------------------- dP wave
+      f32x16 og[NC];   // dK, columns 32 n + lane (scaled through dS)
+#pragma unroll
+      for (int n = 0; n < NC; ++n) og[n] = zero16();
+      unsigned int ar[NS], br[NC];
+#pragma unroll
+      for (int s = 0; s < NS; ++s) ar[s] = sm_base + offsetof(SmemDKDV3<D>, d) + (a_lane ^ (32 * s));
+#pragma unroll
+      for (int n = 0; n < NC; ++n) br[n] = sm_base + offsetof(SmemDKDV3<D>, q) + (t_lane ^ (64 * n));
+      auto read_a = [&](int j, int c) { return lds_b128_at(ar[c >> 1] + j * TS + (c & 1) * HB); };
+      auto read_k = [&](int j, int i) {
+        const int n = i % NC, r0 = 16 * (i / NC);
+        return cat44(lds_tr4_at(br[n] + j * TS + r0 * RB), lds_tr4_at((br[n] ^ 32) + j * TS + (r0 + 8) * RB));
+      };
+      // dP(0): both chains on dO tile 0
+      f32x16 p0 = zero16(), p1 = zero16();
+#pragma unroll
+      for (int s = 0; s < NS; ++s) {
+        p0 = mfma(read_a(0, 2 * s), fB[s], p0);
+        p1 = mfma(read_a(0, 2 * s + 1), fB[s], p1);
+      }
+      constexpr int AH = 2;
+      // dS of one half: P (bf16 operands k0, k0 + 1 of the published P) times
+      // dP scale - delta scale, rounded to the bf16 operands of dK
+      auto ds_half = [&](const u32x4* pw, const f32x16& acc, const f32x4* D4, int r, float* dsv) {
+        const unsigned int wd = pw[r >> 3][(r & 7) >> 1];
+        const float pval = __uint_as_float((r & 1) ? (wd & 0xffff0000u) : (wd << 16));
+        dsv[r] = pval * fmaf(acc[r], scale, -D4[r >> 2][r & 3]);
+      };
+      auto tile = [&](int t, auto jc) {
+        constexpr int j = decltype(jc)::value, j1 = (j + 1) % NB4;
+        tile_head(t);
+        const DmaSet dma = dma_set(t, (j + 2) % NB4);
+        const int par = t & 1;
+        const float* drow = sm.dl[t & 3];
+        u32x4 pw[4];   // P(t), bf16 pairs (operands 2, 3: rows 32..63, read later)
+#pragma unroll
+        for (int k = 0; k < 2; ++k) pw[k] = __builtin_bit_cast(u32x4, sm.px[par][pr][k][l]);
+        f32x4 Da[4], Db[4];
+#pragma unroll
+        for (int m = 0; m < 2; ++m) Da[m] = *(const f32x4*)&drow[8 * m + 4 * lg];
+        f32x16 n0 = zero16(), n1 = zero16();
+        bf16x8 xa[2 * NS], bk[16];
+#pragma unroll
+        for (int c = 0; c < AH; ++c) xa[c] = read_a(j1, c);
+        __builtin_amdgcn_sched_barrier(0);
+        float dsv[32];
+        bf16x8 ds[4];
+        // chain steps 0..7 among the dS of rows 0..31
+        constexpr int EP = 2;   // dS elements per product
+#pragma unroll
+        for (int c = 0; c < NS; ++c) {
+          if (c & 1) n1 = mfma(xa[c], fB[c >> 1], n1);
+          else n0 = mfma(xa[c], fB[c >> 1], n0);
+          if (c >= 2) {   // (P arrives after the first products)
+#pragma unroll
+            for (int e = 0; e < EP + 1; ++e) {
+              const int r = (EP + 1) * (c - 2) + e;
+              if (r < 16) ds_half(pw, p0, Da, r, dsv);
+            }
+          }
+          if (c == 2) {
+#pragma unroll
+            for (int m = 2; m < 4; ++m) Da[m] = *(const f32x4*)&drow[8 * m + 4 * lg];
+          }
+          if (c == 5) {
+#pragma unroll
+            for (int k = 2; k < 4; ++k) pw[k] = __builtin_bit_cast(u32x4, sm.px[par][pr][k][l]);
+#pragma unroll
+            for (int m = 0; m < 2; ++m) Db[m] = *(const f32x4*)&drow[32 + 8 * m + 4 * lg];
+          }
+          if (c + AH < 2 * NS) xa[c + AH] = read_a(j1, c + AH);
+          if (c >= NS - AH) bk[c - (NS - AH)] = read_k(j, c - (NS - AH));
+          if ((c & 1) == 0 && c / 2 < 2 * SLW) dma_one(dma, c / 2);
+          __builtin_amdgcn_sched_barrier(0);
+        }
+        ds[0] = pack8(dsv);
+        ds[1] = pack8(dsv + 8);
+        // chain steps 8..15 among the dK products of rows 0..31 and the dS of rows 32..63
+#pragma unroll
+        for (int c = NS; c < 2 * NS; ++c) {
+          const int i = c - NS;   // dK product 0..7
+          og[i % NC] = mfma(ds[i / NC], bk[i], og[i % NC]);
+          if (c & 1) n1 = mfma(xa[c], fB[c >> 1], n1);
+          else n0 = mfma(xa[c], fB[c >> 1], n0);
+#pragma unroll
+          for (int e = 0; e < EP; ++e) {
+            const int r = EP * i + e;
+            const unsigned int wd = pw[2 + (r >> 3)][(r & 7) >> 1];
+            const float pval = __uint_as_float((r & 1) ? (wd & 0xffff0000u) : (wd << 16));
+            dsv[16 + r] = pval * fmaf(p1[r], scale, -Db[r >> 2][r & 3]);
+          }
+          if (i == 1) {
+#pragma unroll
+            for (int m = 2; m < 4; ++m) Db[m] = *(const f32x4*)&drow[32 + 8 * m + 4 * lg];
+          }
+          if (c + AH < 2 * NS) xa[c + AH] = read_a(j1, c + AH);
+          if (i + AH < 16) bk[i + AH] = read_k(j, i + AH);
+          __builtin_amdgcn_sched_barrier(0);
+        }
+        ds[2] = pack8(dsv + 16);
+        ds[3] = pack8(dsv + 24);
+        // dK products of rows 32..63
+#pragma unroll
+        for (int i = 8; i < 16; ++i) {
+          og[i % NC] = mfma(ds[i / NC], bk[i], og[i % NC]);
+          if (i + AH < 16) bk[i + AH] = read_k(j, i + AH);
+          __builtin_amdgcn_sched_barrier(0);
+        }
+        p0 = n0;
+        p1 = n1;
+        wait_vm_loads();
+      };
+      for (int t0 = 0; t0 < n_it; t0 += NB4) {
+        tile(t0, std::integral_constant<int, 0>{});
+        if (t0 + 1 >= n_it) break;
+        tile(t0 + 1, std::integral_constant<int, 1>{});
+        if (t0 + 2 >= n_it) break;
+        tile(t0 + 2, std::integral_constant<int, 2>{});
+      }
+#pragma unroll
+      for (int n = 0; n < NC; ++n) {
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+          const int64_t j = kw + crow(r, lg);
+          if (j < Sk) {
+            float* po = op + (j - jr) * os + 32 * n + lr;
+            if (mode == kAtomicAdd) atomic_add_f32(po, og[n][r]);
+            else if (mode == kAddInto) *po += og[n][r];
+            else *po = og[n][r];
+          }
+        }
+      }
+    }
+  }
+}
+
 // Grid shape of k_dkdv for a problem (host side).
 struct DkdvPlan {
   DkdvGrid g;
@@ -1028,7 +1624,10 @@ template <int D>
 hipError_t dispatch_dkdv(const Params& p, const BwdArgs& a, const DkdvPlan& pl, bool bias, bool bloop,
                          hipStream_t st) {
   if (!bias) {
-    hipLaunchKernelGGL((k_dkdv2<D, false>), pl.grid, dim3(NT2), 0, st, p, a, pl.g);
+    if constexpr (D == 128)
+      hipLaunchKernelGGL((k_dkdv3<128>), pl.grid, dim3(NT2), 0, st, p, a, pl.g);
+    else
+      hipLaunchKernelGGL((k_dkdv2<D, false>), pl.grid, dim3(NT2), 0, st, p, a, pl.g);
     return hipGetLastError();
   }
   if constexpr (D == 64) {   // with a bias, head dim 64 always takes k_dkdv2 (dbias comes from k_dqb)
