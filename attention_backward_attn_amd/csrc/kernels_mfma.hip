@@ -9,11 +9,12 @@
 //
 // The backward runs as two passes, neither with atomic dQ updates:
 //   * dK / dV by key blocks: one workgroup per (128-key block, KV head,
-//     batch) loops over the G query heads of the group and the 32-row query
-//     tiles that can see the block, keeping dK and dV for its keys in
-//     registers (GQA group sums without atomics).  k_dkdv2 splits each
-//     32-key slice between a pair of waves on one SIMD (two waves per SIMD),
-//     with a bias at head dim 64 as well; k_dkdv, one wave per 32 keys,
+//     batch) loops over the G query heads of the group and the query tiles
+//     that can see the block, keeping dK and dV for its keys in registers
+//     (GQA group sums without atomics).  k_dkdv3 (head dim 128) and k_dkdv2
+//     (head dim 64, also with a bias) split each 32-key slice between a pair
+//     of waves on one SIMD (two waves per SIMD), on 64-row and 32-row query
+//     tiles respectively; k_dkdv, one wave per 32 keys,
 //     serves a bias at head dim 128 and walks the batch when dbias is asked,
 //     so that dbias is summed in a fixed order.
 //   * dQ by query blocks: k_dq2 (k_dq with a bias), one workgroup per
