@@ -408,14 +408,17 @@ def main():
             probs = [ab.make_problem(q, k[:, :, i * c:(i + 1) * c], v[:, :, i * c:(i + 1) * c], o=o, do=do, dq=dq,
                                      dk=dk[:, :, i * c:(i + 1) * c], dv=dv[:, :, i * c:(i + 1) * c], scale=w.scale,
                                      k_offset=i * c, sk_total=w.Sk, **mask_kw) for i in range(n)]
-            ws_c = [ab.set_workspace(pc, ab.ATTN_ACCUMULATE_DQ) for pc in probs]  # noqa: F841
+            # the first chunk writes dQ, the others add to it (the same sum as
+            # zeroed dQ plus every chunk, without the zero fill and one read)
+            fl_c = [0] + [ab.ATTN_ACCUMULATE_DQ] * (n - 1)
+            ws_c = [ab.set_workspace(pc, f) for pc, f in zip(probs, fl_c)]  # noqa: F841
 
             def chunked():
-                ab.attn_bwd_preprocess(p, o, do, lse, None, delta, None, dq, None, None, stream)
+                ab.attn_bwd_preprocess(p, o, do, lse, None, delta, None, None, None, None, stream)
                 for i in range(n):
                     sl = slice(i * c, (i + 1) * c)
                     ab.attn_bwd(probs[i], q, k[:, :, sl], v[:, :, sl], do, lse, delta, None, dq, dk[:, :, sl],
-                                dv[:, :, sl], None, ab.ATTN_ACCUMULATE_DQ, stream)
+                                dv[:, :, sl], None, fl_c[i], stream)
             for _ in range(2):
                 chunked()
             ch_ms = region(chunked, 5)

@@ -371,16 +371,18 @@ def test_headline_chunked():
     dv = torch.full((w.B, w.Hk, w.Sk, w.Dv), float("nan"), device="cuda")
     delta = torch.empty(w.B, w.Hq, w.Sq, device="cuda")
     p = ab.make_problem(q, k, v, o=o, do=do, dq=dq, dk=dk, dv=dv, scale=w.scale, mask=w.mask)
-    # delta, and dQ zeroed for the chunks to accumulate into
-    ab.attn_bwd_preprocess(p, o, do, lse, None, delta, None, dq, None, None)
+    # delta only: the first chunk writes every dQ row (over the NaNs), the
+    # others add to it -- the page's zeroed dq plus each chunk's share
+    ab.attn_bwd_preprocess(p, o, do, lse, None, delta, None, None, None, None)
     keep = []
     for i in range(n):
         sl = slice(i * c, (i + 1) * c)
         pc = ab.make_problem(q, k[:, :, sl], v[:, :, sl], o=o, do=do, dq=dq, dk=dk[:, :, sl], dv=dv[:, :, sl],
                              scale=w.scale, mask=w.mask, k_offset=i * c, sk_total=w.Sk)
-        keep.append(ab.set_workspace(pc, ab.ATTN_ACCUMULATE_DQ))
+        fl = ab.ATTN_ACCUMULATE_DQ if i > 0 else 0
+        keep.append(ab.set_workspace(pc, fl))
         ab.attn_bwd(pc, q, k[:, :, sl], v[:, :, sl], do, lse, delta, None, dq, dk[:, :, sl], dv[:, :, sl],
-                    None, ab.ATTN_ACCUMULATE_DQ)
+                    None, fl)
     torch.cuda.synchronize()
     del keep
     for name, t in (("dq", dq), ("dk", dk), ("dv", dv)):
