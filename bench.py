@@ -95,7 +95,7 @@ def roofline(w, flops: float, main_ms: float, main_med: float, traffic) -> dict:
     vector ALU (fp32 FMA peak).  The others are bound by the bf16 matrix
     cores: achieved = counted FLOPs / time."""
     from attention_backward_attn_amd.mask import backward_bytes
-    out = {"kernel": "attn_bwd (k_dkdv2/k_dkdv + k_dq2/k_dq/k_dqb)" if w.dtype == "bf16" else
+    out = {"kernel": "attn_bwd (k_dkdv3/k_dkdv2/k_dkdv + k_dq2/k_dq/k_dqb)" if w.dtype == "bf16" else
            "attn_bwd (k_dkdv_simt + k_dq_simt)", "kernel_ms_mean": round(main_ms, 4),
            "kernel_ms_median": round(main_med, 4), "algorithmic_bytes": backward_bytes(w)}
     if w.bias:
