@@ -2424,22 +2424,39 @@ __global__ __launch_bounds__(NTB, 1) void k_dqb(Params p, BwdArgs a) {
   // operand) -- fall on distinct banks.
   auto fq = [](int r) { return 2 * ((r >> 2) & 3) + ((r >> 1) & 1); };
   const unsigned char* kv_grp = kv_head;   // the group's entry w % 4 (or its last)
-  auto issue = [&](int it, int buf) {
-    const int j0 = tile_of(it);
-    const int keys = min(Sk - j0, BK3);
-    const __amdgpu_buffer_rsrc_t rs = buf_rsrc(kv_grp + j0 * kv_rb, keys * kv_rb);
-#pragma unroll
-    for (int k = 0; k < PER_T; ++k) {
+  struct DmaB {
+    __amdgpu_buffer_rsrc_t rs, rb;
+    int buf;
+  };
+  auto dma_set = [&](int it, int buf, bool on) {
+    DmaB d;
+    const int j0 = tile_of(on ? it : 0);
+    const int keys = on ? min(Sk - j0, BK3) : 0;
+    d.rs = buf_rsrc(kv_grp + j0 * kv_rb, keys * kv_rb);
+    d.rb = buf_rsrc(bias_h + j0, on ? (brows - 1) * b_rb + 4 * keys : 0);
+    d.buf = buf;
+    return d;
+  };
+  // A tile's loads are set up at the barrier and issued two at a time after
+  // the first entries' products: issued together right after the barrier,
+  // the eight waves' 48 KB queue for the vector memory unit and hold up the
+  // products behind them.  With `on` false they load nothing (zeros into a
+  // buffer no later tile reads).
+  auto dma_one = [&](const DmaB& d, int k) {   // k < PER_T: K / V slot k, else bias rows
+    if (k < PER_T) {
       const int row = (64 * k + l) / CR, c = (l % CR) ^ fq(row);
-      lds_dma16(rs, __builtin_amdgcn_readfirstlane(kv_dst + buf * BUF_B + 1024 * k), row * kv_rb + 16 * c);
-    }
-    const __amdgpu_buffer_rsrc_t rb_ = buf_rsrc(bias_h + j0, (brows - 1) * b_rb + 4 * keys);
-#pragma unroll
-    for (int k = 0; k < 2; ++k) {
-      const int row = 16 * w + 8 * k + (l >> 3), c = (l & 7) ^ ((row >> 1) & 7);
-      lds_dma16(rb_, __builtin_amdgcn_readfirstlane(sm_base + BIAS_OFF + buf * BTB + (16 * w + 8 * k) * 128),
+      lds_dma16(d.rs, __builtin_amdgcn_readfirstlane(kv_dst + d.buf * BUF_B + 1024 * k), row * kv_rb + 16 * c);
+    } else {
+      const int kb = k - PER_T;
+      const int row = 16 * w + 8 * kb + (l >> 3), c = (l & 7) ^ ((row >> 1) & 7);
+      lds_dma16(d.rb, __builtin_amdgcn_readfirstlane(sm_base + BIAS_OFF + d.buf * BTB + (16 * w + 8 * kb) * 128),
                 row * b_rb + 16 * c);
     }
+  };
+  auto issue = [&](int it, int buf) {
+    const DmaB d = dma_set(it, buf, true);
+#pragma unroll
+    for (int k = 0; k < NI; ++k) dma_one(d, k);
   };
   // bias / scale in place: each wave scales the 16 rows it loaded itself
   // (complete once its own loads are; only this wave reads them)
@@ -2519,7 +2536,7 @@ __global__ __launch_bounds__(NTB, 1) void k_dqb(Params p, BwdArgs a) {
     // chain ends at -inf and P = 0 for every entry (LSE is never -inf here).
     // The mask is applied once per tile, before any product, and the entries
     // form one straight block.
-    auto body = [&](int j0, auto Jc, bool full) {
+    auto body = [&](int j0, auto Jc, bool full, const DmaB& dm) {
       constexpr int J = decltype(Jc)::value;
       const int tb = tq + j0;
       f32x4 bz[2];
@@ -2563,6 +2580,9 @@ __global__ __launch_bounds__(NTB, 1) void k_dqb(Params p, BwdArgs a) {
             db[mt][i] += dsv[4 * mt + i];
           }
         const bf16x8 A = pack8(dsv);
+        // two of the next-but-one tile's loads after each of the first entries
+        if (2 * e < NI) dma_one(dm, 2 * e);
+        if (2 * e + 1 < NI) dma_one(dm, 2 * e + 1);
 #pragma unroll
         for (int nt = 0; nt < 4; ++nt) {
           const bf16x8 bq = cat44(lds_tr4_at(ta[nt] + kt), lds_tr4_at(ta[nt] + kt + 2048));
@@ -2576,9 +2596,9 @@ __global__ __launch_bounds__(NTB, 1) void k_dqb(Params p, BwdArgs a) {
     auto tile = [&](int t, auto Jc) {
       constexpr int J = decltype(Jc)::value;
       __syncthreads();   // tile t complete for every wave; tile t - 1's buffer free
-      if (t + 2 < n_it) issue(t + 2, (J + 2) % NQB);
+      const DmaB dm = dma_set(t + 2, (J + 2) % NQB, t + 2 < n_it);
       const int j0 = tile_of(t);
-      const DbTile dbt = body(j0, Jc, tile_full(j0));
+      const DbTile dbt = body(j0, Jc, tile_full(j0), dm);
       const f32x4 db[2] = {dbt.c0, dbt.c1};
       // dbias of this tile (unscaled dS summed over the group): this lane's
       // row, keys j0 + 16 mt + 4 g + 0..3.  A whole key tile is stored by two
