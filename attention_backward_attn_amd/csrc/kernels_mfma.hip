@@ -967,26 +967,31 @@ __global__ __launch_bounds__(NT2) void k_dkdv2(Params p, BwdArgs a, DkdvGrid gd)
 }
 
 // ---------------------------------------------------------------------------
-// Kernel k_dkdv3 (dK / dV without a bias, head dim 128): the wave pairs of
-// k_dkdv2 on 64-row query tiles.  Per tile each wave issues 32 products --
-// two independent S (or dP) chains of 8 over the head dim and 16 dV (or dK)
-// products -- where a 32-row tile gives it 16, so the barrier, the hand-over
-// of P and the operand reads that follow the barrier are paid once per 64
-// rows, and no wave waits on a single dependent chain.
-// LDS (130 KB): the Q and dO tiles in three swizzled buffers each, loaded
-// two tiles ahead; the rows' LSE and delta in four buffers, loaded three
-// tiles ahead and prepared in place (LSE * log2(e), delta * scale) by wave 0
-// two tiles before their use; P handed from the S wave to the dP wave as the
-// bf16 operand registers the S wave itself multiplies with, in two buffers by
-// tile parity.  Per tile t, one barrier:
+// Kernel k_dkdv3 (dK / dV on 64-row query tiles: head dim 128 without a
+// bias, head dim 64 with one): the wave pairs of k_dkdv2 on 64-row tiles.
+// Per tile each wave issues two independent S (or dP) chains over the head
+// dim (8 products each at head dim 128) and the dV (or dK) products (16),
+// twice what a 32-row tile gives it, so the barrier, the hand-over of P and
+// the operand reads that follow the barrier are paid once per 64 rows, and
+// no wave waits on a single dependent chain.
+// LDS (130 KB at head dim 128): the Q and dO tiles in three swizzled
+// buffers each, loaded two tiles ahead; the rows' LSE and delta in four
+// buffers, loaded three tiles ahead and prepared in place (LSE * log2(e),
+// delta * scale) by wave 0 two tiles before their use; P handed from the S
+// wave to the dP wave as the bf16 operand registers the S wave itself
+// multiplies with, in two buffers by tile parity.  With a bias (head dim 64,
+// 146 KB) the [64 rows x 128 keys] fp32 bias tile of each Q / dO tile comes
+// into LDS beside it (two buffers) and the S wave adds it to S before the
+// exponentials.  Every wave issues its share of a tile's loads one 1 KB
+// slot at a time among its first products.  Per tile t, one barrier:
 //   S wave:  S(t + 1) = Q K^T as two chains (rows 0..31 and 32..63,
 //            alternating), then dV += P(t)^T dO(t) with the exponentials,
 //            masking and bf16 rounding of P(t + 1) = exp2(S - LSE) among
 //            those products; P(t + 1) published before the next barrier.
 //   dP wave: dP(t + 1) = dO V^T as two alternating chains, with
 //            dS(t) = P(t) (dP(t) scale - delta scale) of rows 0..31 among
-//            the first eight; dK += dS(t)^T Q(t) for rows 0..31 among the
-//            last eight (with the dS of rows 32..63), then for rows 32..63.
+//            the first half; dK += dS(t)^T Q(t) for rows 0..31 among the
+//            second half (with the dS of rows 32..63), then for rows 32..63.
 // ---------------------------------------------------------------------------
 constexpr int BQ4 = 64;   // query rows per tile (k_dkdv3)
 constexpr int NB4 = 3;    // Q / dO tile buffers
@@ -1001,40 +1006,56 @@ struct __attribute__((aligned(1024))) SmemDKDV3 {
   float dl[NL4][BQ4];                  // delta of the tile's rows, then delta * scale
 };
 
+// With a bias: the bias tile [64 rows][128 keys] (fp32) of Q / dO tile t in
+// buffer t % 2, after the members above.
+template <int D>
+struct __attribute__((aligned(1024))) SmemDKDV3B : SmemDKDV3<D> {
+  float bias[2][BQ4 * BK];
+};
+
 // Walk over the (query head, 64-row tile) sequence of a unit part: Q / dO
 // tile pointers, or LSE / delta row pointers, one tile at a time.
 struct Walk64 {
-  const void *x, *y;   // Q and dO (bytes), or LSE and delta (floats)
+  const void *x, *y, *z;   // Q, dO and bias (bytes), or LSE and delta (floats)
   int qb, i0;
-  __device__ inline void next(int nqb, int lo_al, int64_t x_step, int64_t y_step, int64_t x_wrap, int64_t y_wrap) {
+  __device__ inline void next(int nqb, int lo_al, int64_t x_step, int64_t y_step, int64_t x_wrap, int64_t y_wrap,
+                              int64_t z_step = 0, int64_t z_wrap = 0) {
     x = (const char*)x + x_step;
     y = (const char*)y + y_step;
+    z = (const char*)z + z_step;
     i0 += BQ4;
     if (++qb == nqb) {
       qb = 0;
       i0 = lo_al;
       x = (const char*)x + x_wrap;
       y = (const char*)y + y_wrap;
+      z = (const char*)z + z_wrap;
     }
   }
 };
 
-template <int D>
+template <int D, bool BIAS>
 __global__ __launch_bounds__(NT2) void k_dkdv3(Params p, BwdArgs a, DkdvGrid gd) {
-  static_assert(D == 128, "head dim");
+  static_assert((D == 128 && !BIAS) || (D == 64 && BIAS), "head dim 128 without a bias, 64 with one");
   constexpr int NS = D / 16;                   // k-steps over the head dim
   constexpr int NC = D / 32;                   // 32-column blocks of dK / dV
+  constexpr int NVT = 4 * NC;                  // dV (or dK) products per tile
   constexpr int RB = Swz<D>::RB, CR = Swz<D>::CR;
   constexpr int TS = BQ4 * RB;                 // tile bytes
   constexpr int SLW = BQ4 * CR / 64 / 8;       // 1 KB slots of each tile loaded per wave
   constexpr int HB = 32 * RB;                  // byte offset of rows 32..63
-  __shared__ SmemDKDV3<D> sm;
+  constexpr int NDMA = 2 * SLW + (BIAS ? 4 : 0);   // 1 KB loads per wave per tile
+  constexpr int BIAS_OFF = (int)sizeof(SmemDKDV3<D>);   // byte offset of the bias tiles
+  constexpr int BTS = BQ4 * BK * 4;                      // bias tile bytes
+  __shared__ std::conditional_t<BIAS, SmemDKDV3B<D>, SmemDKDV3<D>> sm;
 
   const int tid = threadIdx.x, l = tid & 63, lr = l & 31, lg = l >> 5;
   const int w = __builtin_amdgcn_readfirstlane(tid >> 6);   // wave-uniform
   const int pr = w & 3;               // pair: keys [32 pr, 32 pr + 32) of the block
   const bool sw = w < 4;              // S wave (else dP wave)
-  const BlockXYZ blk = xcd_block();
+  // with a bias (shared over the batch) the batch entries of a unit run side
+  // by side, so each bias tile comes from HBM about once
+  const BlockXYZ blk = BIAS ? xcd_block_zfast() : xcd_block();
   // packed batch: batch index z stands for the sequence of rank z by work
   // (query rows x keys, ties by index), longest first (as in k_dkdv2)
   int b = blk.z;
@@ -1174,6 +1195,10 @@ __global__ __launch_bounds__(NT2) void k_dkdv3(Params p, BwdArgs a, DkdvGrid gd)
     const int64_t q_step = (int64_t)BQ4 * p.q_str[2] * 2, d_step = (int64_t)BQ4 * p.do_str[2] * 2;
     const int64_t q_wrap = p.q_str[1] * 2 - nqb * q_step, d_wrap = p.do_str[1] * 2 - nqb * d_step;
     const int64_t l_step = BQ4 * 4, l_wrap = ((int64_t)p.Sq - (int64_t)nqb * BQ4) * 4;
+    // bias rows of a tile (bytes): the tile's first row, the block's first key
+    const int64_t z_step = BIAS ? (int64_t)BQ4 * p.bias_str[1] * 4 : 0;
+    const int64_t z_wrap = BIAS ? (p.bias_str[0] - (int64_t)nqb * BQ4 * p.bias_str[1]) * 4 : 0;
+    const int b_rb = BIAS ? 4 * (int)p.bias_str[1] : 0, bkeys = min(Sk - k0, BK);
     {
       const int h0 = h_begin + it_lo / nqb, qb0 = it_lo % nqb;
       const int i00 = lo_al + BQ4 * qb0;
@@ -1182,6 +1207,8 @@ __global__ __launch_bounds__(NT2) void k_dkdv3(Params p, BwdArgs a, DkdvGrid gd)
       const int64_t rb = ((int64_t)b * p.Hq + h0) * p.Sq + i00;
       wl.x = a.lse + rb;
       wl.y = a.delta + rb;
+      wqd.z = BIAS ? a.bias + h0 * p.bias_str[0] + (int64_t)i00 * p.bias_str[1] + k0 : nullptr;
+      wl.z = nullptr;
       wqd.qb = wl.qb = qb0;
       wqd.i0 = wl.i0 = i00;
     }
@@ -1190,7 +1217,12 @@ __global__ __launch_bounds__(NT2) void k_dkdv3(Params p, BwdArgs a, DkdvGrid gd)
       fr_i0 += BQ4;
       if (++fr_qb == nqb) { fr_qb = 0; fr_i0 = lo_al; }
     };
-    auto issue_qd = [&](int buf) {
+    // bias tile slot g (1 KB: rows 2 g, 2 g + 1) of wave w: g = 4 w + k
+    auto bias_dma = [&](__amdgpu_buffer_rsrc_t rz, int bbuf, int k) {
+      const int g = 4 * w + k;
+      lds_dma16(rz, sm_base + BIAS_OFF + bbuf * BTS + 1024 * g, (2 * g + (l >> 5)) * b_rb + 16 * (l & 31));
+    };
+    auto issue_qd = [&](int buf, int bbuf) {
       const int rows = min(Sq - wqd.i0, BQ4);
       const __amdgpu_buffer_rsrc_t rq = buf_rsrc(wqd.x, rows * q_rb), rd = buf_rsrc(wqd.y, rows * d_rb);
       const unsigned int mq = sm_base + offsetof(SmemDKDV3<D>, q) + buf * TS + 1024 * SLW * w;
@@ -1199,7 +1231,13 @@ __global__ __launch_bounds__(NT2) void k_dkdv3(Params p, BwdArgs a, DkdvGrid gd)
       for (int k = 0; k < SLW; ++k) lds_dma16(rq, mq + 1024 * k, qv[k]);
 #pragma unroll
       for (int k = 0; k < SLW; ++k) lds_dma16(rd, md + 1024 * k, dv_[k]);
-      wqd.next(nqb, lo_al, q_step, d_step, q_wrap, d_wrap);
+      if (BIAS) {
+        // (the resource ends at the tile's last valid element: rows past the end read zeros)
+        const __amdgpu_buffer_rsrc_t rz = buf_rsrc(wqd.z, (rows - 1) * b_rb + 4 * bkeys);
+#pragma unroll
+        for (int k = 0; k < 4; ++k) bias_dma(rz, bbuf, k);
+      }
+      wqd.next(nqb, lo_al, q_step, d_step, q_wrap, d_wrap, z_step, z_wrap);
     };
     auto issue_l = [&](int lb) {
       if (w == 0) {
@@ -1221,8 +1259,8 @@ __global__ __launch_bounds__(NT2) void k_dkdv3(Params p, BwdArgs a, DkdvGrid gd)
     };
     // Prologue: Q / dO tiles 0, 1 and LSE / delta rows 0..2 in flight
     // together with the K / V fragments, all complete before the barrier.
-    issue_qd(0);
-    if (n_it > 1) issue_qd(1);
+    issue_qd(0, 0);
+    if (n_it > 1) issue_qd(1, 1);
     issue_l(0);
     if (n_it > 1) issue_l(1);
     if (n_it > 2) issue_l(2);
@@ -1244,8 +1282,9 @@ __global__ __launch_bounds__(NT2) void k_dkdv3(Params p, BwdArgs a, DkdvGrid gd)
     // loads queue for the vector memory unit and hold up every wave's
     // products behind them.  Past the last tile they load nothing (zeros).
     struct DmaSet {
-      __amdgpu_buffer_rsrc_t rq, rd;
+      __amdgpu_buffer_rsrc_t rq, rd, rz;
       unsigned int mq, md;
+      int bbuf;
     };
     auto dma_set = [&](int t, int buf) {
       DmaSet d;
@@ -1253,14 +1292,18 @@ __global__ __launch_bounds__(NT2) void k_dkdv3(Params p, BwdArgs a, DkdvGrid gd)
       const int rows = on ? min(Sq - wqd.i0, BQ4) : 0;
       d.rq = buf_rsrc(wqd.x, rows * q_rb);
       d.rd = buf_rsrc(wqd.y, rows * d_rb);
+      d.rz = buf_rsrc(wqd.z, on && BIAS ? (rows - 1) * b_rb + 4 * bkeys : 0);
       d.mq = sm_base + offsetof(SmemDKDV3<D>, q) + buf * TS + 1024 * SLW * w;
       d.md = sm_base + offsetof(SmemDKDV3<D>, d) + buf * TS + 1024 * SLW * w;
-      if (on) wqd.next(nqb, lo_al, q_step, d_step, q_wrap, d_wrap);
+      d.bbuf = t & 1;   // tile t + 2's bias buffer
+      if (on) wqd.next(nqb, lo_al, q_step, d_step, q_wrap, d_wrap, z_step, z_wrap);
       return d;
     };
-    auto dma_one = [&](const DmaSet& d, int k) {   // k < SLW: Q slot k, else dO slot k - SLW
+    // k < SLW: Q slot k; k < 2 SLW: dO slot k - SLW; then the bias slots
+    auto dma_one = [&](const DmaSet& d, int k) {
       if (k < SLW) lds_dma16(d.rq, d.mq + 1024 * k, qv[k]);
-      else lds_dma16(d.rd, d.md + 1024 * (k - SLW), dv_[k - SLW]);
+      else if (k < 2 * SLW) lds_dma16(d.rd, d.md + 1024 * (k - SLW), dv_[k - SLW]);
+      else if (BIAS) bias_dma(d.rz, d.bbuf, k - 2 * SLW);
     };
     // one tile's common start: barrier t, the loads of the rows of tile
     // t + 3, the rows of tile t + 2 prepared
@@ -1293,6 +1336,24 @@ __global__ __launch_bounds__(NT2) void k_dkdv3(Params p, BwdArgs a, DkdvGrid gd)
 #pragma unroll
         for (int m = 0; m < 4; ++m) L4[m] = *(const f32x4*)&lrow[32 * h + 8 * m + 4 * lg];
       };
+      // bias of the four-element group g (rows 32 (g / 4) + 8 (g % 4) + 4 lg
+      // + 0..3, this lane's key) of the tile in bias buffer bbuf
+      typedef __attribute__((address_space(3))) const float lds_f32;
+      const unsigned int b_lane = sm_base + BIAS_OFF + (4 * lg) * (BK * 4) + (32 * pr + lr) * 4;
+      auto bias4 = [&](int g, int bbuf) {
+        f32x4 v{0.f, 0.f, 0.f, 0.f};
+        if (BIAS) {
+          const unsigned int base = b_lane + bbuf * BTS + (32 * (g >> 2) + 8 * (g & 3)) * (BK * 4);
+#pragma unroll
+          for (int e = 0; e < 4; ++e) v[e] = *(lds_f32*)(size_t)(base + e * (BK * 4));
+        }
+        return v;
+      };
+      // exponent (log2 units) of P = exp(S scale + bias - LSE)
+      auto expo = [&](float s_, float l2, float bz) {
+        const float x = fmaf(s_, scale_log2, -l2);
+        return BIAS ? fmaf(bz, kLog2e, x) : x;
+      };
       auto mask_pack = [&](float* pv, int i0h, bf16x8* dst2) {
         if (!(i0h >= full_a && i0h + 31 <= full_c)) {
           const int tb = tb0 - i0h;
@@ -1318,15 +1379,19 @@ __global__ __launch_bounds__(NT2) void k_dkdv3(Params p, BwdArgs a, DkdvGrid gd)
           s0 = mfma(read_a(0, 2 * s), fB[s], s0);
           s1 = mfma(read_a(0, 2 * s + 1), fB[s], s1);
         }
-        f32x4 L4[4];
+        f32x4 L4[4], B4[4];
         float pv[16];
         lse_vals(L4, sm.lse[0], 0);
 #pragma unroll
-        for (int r = 0; r < 16; ++r) pv[r] = __builtin_amdgcn_exp2f(fmaf(s0[r], scale_log2, -L4[r >> 2][r & 3]));
+        for (int m = 0; m < 4; ++m) B4[m] = bias4(m, 0);
+#pragma unroll
+        for (int r = 0; r < 16; ++r) pv[r] = __builtin_amdgcn_exp2f(expo(s0[r], L4[r >> 2][r & 3], B4[r >> 2][r & 3]));
         mask_pack(pv, fr_i0, pa);
         lse_vals(L4, sm.lse[0], 1);
 #pragma unroll
-        for (int r = 0; r < 16; ++r) pv[r] = __builtin_amdgcn_exp2f(fmaf(s1[r], scale_log2, -L4[r >> 2][r & 3]));
+        for (int m = 0; m < 4; ++m) B4[m] = bias4(4 + m, 0);
+#pragma unroll
+        for (int r = 0; r < 16; ++r) pv[r] = __builtin_amdgcn_exp2f(expo(s1[r], L4[r >> 2][r & 3], B4[r >> 2][r & 3]));
         mask_pack(pv, fr_i0 + 32, pa + 2);
         publish(pa, 0);
         fr_next();
@@ -1342,7 +1407,7 @@ __global__ __launch_bounds__(NT2) void k_dkdv3(Params p, BwdArgs a, DkdvGrid gd)
         const DmaSet dma = dma_set(t, (j + 2) % NB4);
         const float* lrow = sm.lse[(t + 1) & 3];
         f32x16 s0 = zero16(), s1 = zero16();
-        bf16x8 xa[2 * NS], bv[16];
+        bf16x8 xa[2 * NS], bv[NVT];
 #pragma unroll
         for (int i = 0; i < VPRE; ++i) bv[i] = vn[i];
 #pragma unroll
@@ -1360,20 +1425,31 @@ __global__ __launch_bounds__(NT2) void k_dkdv3(Params p, BwdArgs a, DkdvGrid gd)
           if (c & 1) s1 = mfma(xa[c], fB[c >> 1], s1);
           else s0 = mfma(xa[c], fB[c >> 1], s0);
           if (c + AH < 2 * NS) xa[c + AH] = read_a(j1, c + AH);
-          if (c % 3 == 0 && c / 3 < 2 * SLW) dma_one(dma, c / 3);
+          if constexpr (NS == 8) {
+            if (c % 3 == 0 && c / 3 < NDMA) dma_one(dma, c / 3);
+          } else {
+#pragma unroll
+            for (int q_ = (c * NDMA) / (2 * NS); q_ < ((c + 1) * NDMA) / (2 * NS); ++q_) dma_one(dma, q_);
+          }
           __builtin_amdgcn_sched_barrier(0);
         }
         // the remaining dV products, among the exponentials of both halves
         // (element r: half r / 16, its LSE in the four-row group r / 4,
         // read one product ahead of the group's first exponential)
         float pv[32];
-        constexpr int NV = 16 - VPRE;          // products in this region
+        constexpr int NV = NVT - VPRE;         // products in this region
         auto r_lo = [](int k) { return (32 * k + NV - 1) / NV; };   // first element of product k
         auto lse4 = [&](int g) {   // rows of four-element group g
           return *(const f32x4*)&lrow[32 * (g >> 2) + 8 * (g & 3) + 4 * lg];
         };
-        f32x4 L4[8];
-        L4[0] = lse4(0);
+        const int bbuf = (t + 1) & 1;   // bias of tile t + 1
+        f32x4 L4[8], B4[8];
+#pragma unroll
+        for (int g = 0; g < 8; ++g)   // the groups that product 0 starts
+          if (4 * g < r_lo(1)) {
+            L4[g] = lse4(g);
+            B4[g] = bias4(g, bbuf);
+          }
 #pragma unroll
         for (int k = 0; k < NV; ++k) {
           const int i = VPRE + k;
@@ -1381,14 +1457,17 @@ __global__ __launch_bounds__(NT2) void k_dkdv3(Params p, BwdArgs a, DkdvGrid gd)
 #pragma unroll
           for (int r = r_lo(k); r < r_lo(k + 1); ++r) {
             const float sv_ = r < 16 ? s0[r] : s1[r - 16];
-            pv[r] = __builtin_amdgcn_exp2f(fmaf(sv_, scale_log2, -L4[r >> 2][r & 3]));
+            pv[r] = __builtin_amdgcn_exp2f(expo(sv_, L4[r >> 2][r & 3], B4[r >> 2][r & 3]));
             // (kept here: otherwise the compiler sinks them below the products)
             asm volatile("" : "+v"(pv[r]));
           }
 #pragma unroll
           for (int g = 1; g < 8; ++g)
-            if (4 * g >= r_lo(k + 1) && 4 * g < r_lo(k + 2)) L4[g] = lse4(g);
-          if (i + AH < 16) bv[i + AH] = read_v(j, i + AH);
+            if (4 * g >= r_lo(k + 1) && 4 * g < r_lo(k + 2)) {
+              L4[g] = lse4(g);
+              B4[g] = bias4(g, bbuf);
+            }
+          if (i + AH < NVT) bv[i + AH] = read_v(j, i + AH);
           __builtin_amdgcn_sched_barrier(0);
         }
         bf16x8 pn[4];
@@ -1460,14 +1539,21 @@ __global__ __launch_bounds__(NT2) void k_dkdv3(Params p, BwdArgs a, DkdvGrid gd)
         const DmaSet dma = dma_set(t, (j + 2) % NB4);
         const int par = t & 1;
         const float* drow = sm.dl[t & 3];
-        u32x4 pw[4];   // P(t), bf16 pairs (operands 2, 3: rows 32..63, read later)
-#pragma unroll
-        for (int k = 0; k < 2; ++k) pw[k] = __builtin_bit_cast(u32x4, sm.px[par][pr][k][l]);
+        // P(t) as bf16 pairs and the delta rows; at head dim 128 those of
+        // rows 32..63 (and part of rows 0..31) are read during the products
+        constexpr bool LATE = NS == 8;
+        u32x4 pw[4];
         f32x4 Da[4], Db[4];
 #pragma unroll
-        for (int m = 0; m < 2; ++m) Da[m] = *(const f32x4*)&drow[8 * m + 4 * lg];
+        for (int k = 0; k < (LATE ? 2 : 4); ++k) pw[k] = __builtin_bit_cast(u32x4, sm.px[par][pr][k][l]);
+#pragma unroll
+        for (int m = 0; m < (LATE ? 2 : 4); ++m) Da[m] = *(const f32x4*)&drow[8 * m + 4 * lg];
+        if (!LATE) {
+#pragma unroll
+          for (int m = 0; m < 4; ++m) Db[m] = *(const f32x4*)&drow[32 + 8 * m + 4 * lg];
+        }
         f32x16 n0 = zero16(), n1 = zero16();
-        bf16x8 xa[2 * NS], bk[16];
+        bf16x8 xa[2 * NS], bk[NVT];
 #pragma unroll
         for (int c = 0; c < AH; ++c) xa[c] = read_a(j1, c);
         __builtin_amdgcn_sched_barrier(0);
@@ -1480,17 +1566,19 @@ __global__ __launch_bounds__(NT2) void k_dkdv3(Params p, BwdArgs a, DkdvGrid gd)
           if (c & 1) n1 = mfma(xa[c], fB[c >> 1], n1);
           else n0 = mfma(xa[c], fB[c >> 1], n0);
           if (c >= 2) {   // (P arrives after the first products)
+            // elements of step c: 3 a step at head dim 128, else spread evenly
+            constexpr int ES = LATE ? EP + 1 : (16 + NS - 3) / (NS - 2);
 #pragma unroll
-            for (int e = 0; e < EP + 1; ++e) {
-              const int r = (EP + 1) * (c - 2) + e;
+            for (int e = 0; e < ES; ++e) {
+              const int r = ES * (c - 2) + e;
               if (r < 16) ds_half(pw, p0, Da, r, dsv);
             }
           }
-          if (c == 2) {
+          if (LATE && c == 2) {
 #pragma unroll
             for (int m = 2; m < 4; ++m) Da[m] = *(const f32x4*)&drow[8 * m + 4 * lg];
           }
-          if (c == 5) {
+          if (LATE && c == 5) {
 #pragma unroll
             for (int k = 2; k < 4; ++k) pw[k] = __builtin_bit_cast(u32x4, sm.px[par][pr][k][l]);
 #pragma unroll
@@ -1498,7 +1586,12 @@ __global__ __launch_bounds__(NT2) void k_dkdv3(Params p, BwdArgs a, DkdvGrid gd)
           }
           if (c + AH < 2 * NS) xa[c + AH] = read_a(j1, c + AH);
           if (c >= NS - AH) bk[c - (NS - AH)] = read_k(j, c - (NS - AH));
-          if ((c & 1) == 0 && c / 2 < 2 * SLW) dma_one(dma, c / 2);
+          if constexpr (LATE) {
+            if ((c & 1) == 0 && c / 2 < NDMA) dma_one(dma, c / 2);
+          } else {
+#pragma unroll
+            for (int q_ = (c * NDMA) / NS; q_ < ((c + 1) * NDMA) / NS; ++q_) dma_one(dma, q_);
+          }
           __builtin_amdgcn_sched_barrier(0);
         }
         ds[0] = pack8(dsv);
@@ -1510,28 +1603,29 @@ __global__ __launch_bounds__(NT2) void k_dkdv3(Params p, BwdArgs a, DkdvGrid gd)
           og[i % NC] = mfma(ds[i / NC], bk[i], og[i % NC]);
           if (c & 1) n1 = mfma(xa[c], fB[c >> 1], n1);
           else n0 = mfma(xa[c], fB[c >> 1], n0);
+          constexpr int EB = 16 / NS;   // dS elements of rows 32..63 per step
 #pragma unroll
-          for (int e = 0; e < EP; ++e) {
-            const int r = EP * i + e;
+          for (int e = 0; e < EB; ++e) {
+            const int r = EB * i + e;
             const unsigned int wd = pw[2 + (r >> 3)][(r & 7) >> 1];
             const float pval = __uint_as_float((r & 1) ? (wd & 0xffff0000u) : (wd << 16));
             dsv[16 + r] = pval * fmaf(p1[r], scale, -Db[r >> 2][r & 3]);
           }
-          if (i == 1) {
+          if (LATE && i == 1) {
 #pragma unroll
             for (int m = 2; m < 4; ++m) Db[m] = *(const f32x4*)&drow[32 + 8 * m + 4 * lg];
           }
           if (c + AH < 2 * NS) xa[c + AH] = read_a(j1, c + AH);
-          if (i + AH < 16) bk[i + AH] = read_k(j, i + AH);
+          if (i + AH < NVT) bk[i + AH] = read_k(j, i + AH);
           __builtin_amdgcn_sched_barrier(0);
         }
         ds[2] = pack8(dsv + 16);
         ds[3] = pack8(dsv + 24);
         // dK products of rows 32..63
 #pragma unroll
-        for (int i = 8; i < 16; ++i) {
+        for (int i = NS; i < NVT; ++i) {
           og[i % NC] = mfma(ds[i / NC], bk[i], og[i % NC]);
-          if (i + AH < 16) bk[i + AH] = read_k(j, i + AH);
+          if (i + AH < NVT) bk[i + AH] = read_k(j, i + AH);
           __builtin_amdgcn_sched_barrier(0);
         }
         p0 = n0;
@@ -1626,13 +1720,13 @@ hipError_t dispatch_dkdv(const Params& p, const BwdArgs& a, const DkdvPlan& pl, 
                          hipStream_t st) {
   if (!bias) {
     if constexpr (D == 128)
-      hipLaunchKernelGGL((k_dkdv3<128>), pl.grid, dim3(NT2), 0, st, p, a, pl.g);
+      hipLaunchKernelGGL((k_dkdv3<128, false>), pl.grid, dim3(NT2), 0, st, p, a, pl.g);
     else
       hipLaunchKernelGGL((k_dkdv2<D, false>), pl.grid, dim3(NT2), 0, st, p, a, pl.g);
     return hipGetLastError();
   }
-  if constexpr (D == 64) {   // with a bias, head dim 64 always takes k_dkdv2 (dbias comes from k_dqb)
-    hipLaunchKernelGGL((k_dkdv2<64, true>), pl.grid, dim3(NT2), 0, st, p, a, pl.g);
+  if constexpr (D == 64) {   // with a bias, head dim 64 always takes k_dkdv3 (dbias comes from k_dqb)
+    hipLaunchKernelGGL((k_dkdv3<64, true>), pl.grid, dim3(NT2), 0, st, p, a, pl.g);
     return hipGetLastError();
   } else {
     return bloop ? launch_dkdv<D, true, true>(p, a, pl, st) : launch_dkdv<D, true, false>(p, a, pl, st);
