@@ -408,8 +408,8 @@ def test_deterministic_is_bitwise_repeatable(D):
         assert torch.equal(outs[0][kk], outs[1][kk]) and torch.equal(outs[0][kk], outs[2][kk]), kk
 
 
-# (B, Hq, Hk, S, D, bias): no bias (k_dkdv2 / k_dq2); a bias with dbias at
-# head dim 64 (k_dkdv2 with the bias, k_dqb) and at head dim 128 (k_dkdv
+# (B, Hq, Hk, S, D, bias): no bias (k_dkdv3 / k_dq2); a bias with dbias at
+# head dim 64 (k_dkdv3 with the bias, k_dqb) and at head dim 128 (k_dkdv
 # walking the batch, k_dq with the bias)
 ACC_CASES = [(1, 8, 2, 300, 128, False), (2, 4, 4, 200, 64, True), (2, 2, 2, 160, 128, True)]
 
