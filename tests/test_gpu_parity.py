@@ -109,6 +109,10 @@ SMALL = [
                                                   num_sink=3), True, True),
     (5, 2, 2, 160, 160, 64, 64, "bf16", MaskSpec("top_left"), True, False),       # two batch groups
     (1, 4, 4, 256, 200, 64, 64, "bf16", MaskSpec("bottom_right"), True, False),
+    # 64-row query tiles of the dK/dV pass: one partial tile with a bias at
+    # head dim 64; three tiles with a 2-row tail at head dim 128
+    (1, 2, 2, 40, 96, 64, 64, "bf16", MaskSpec("bottom_right"), True, False),
+    (2, 4, 1, 130, 70, 128, 128, "bf16", MaskSpec("top_left"), False, True),
 ]
 
 
