@@ -129,8 +129,8 @@ enum : int { kStore = 0, kAtomicAdd = 1, kAddInto = 2 };
 // kb falls linearly with kb, so block kb and block nkb-1-kb together cost the
 // same for every pair -- one pair per workgroup balances the grid.
 // Splitting: a unit's iteration list may be cut into `nsplit` contiguous
-// parts handled by separate workgroups.  With partials (k_dkdv2 on dense
-// problems, more than two parts) part 0 writes dK/dV and the other parts
+// parts handled by separate workgroups.  With partials (k_dkdv3 / k_dkdv2
+// without a bias on dense problems, more than two parts) part 0 writes dK/dV and the other parts
 // their own slots, which the dQ pass adds in slot order afterwards
 // (deterministic for any split); otherwise every part adds atomically into
 // zeroed outputs (with exactly two addends onto zero the fp32 result does
@@ -1662,7 +1662,7 @@ struct DkdvPlan {
   dim3 grid;
 };
 
-// partials: split parts write slots that the dQ pass adds (k_dkdv2, dense
+// partials: split parts write slots that the dQ pass adds (no bias, dense
 // problems); otherwise they add atomically.
 DkdvPlan plan_dkdv(const Params& p, bool bloop, bool accumulate_dkdv, bool deterministic, bool partials) {
   DkdvPlan pl{};
@@ -2850,7 +2850,7 @@ hipError_t launch_bwd_mfma(const Params& p, const BwdArgs& a, hipStream_t st) {
     hipError_t e = launch_zero_bias(a.dbias, p.Hq, p.Sq, p.Sk, p.bias_str, st);
     if (e != hipSuccess) return e;
   }
-  // dK / dV by key blocks (k_dkdv2; k_dkdv with a bias, where dbias is
+  // dK / dV by key blocks (k_dkdv3 / k_dkdv2; k_dkdv with a bias, where dbias is
   // summed over the batch in a fixed order by one workgroup per key block
   // walking the batch) and dQ by query blocks (k_dq2; k_dq with a bias): no
   // dQ atomics.  Units of dense problems without a bias split into more than
@@ -2860,7 +2860,7 @@ hipError_t launch_bwd_mfma(const Params& p, const BwdArgs& a, hipStream_t st) {
   // pass, run first, when it is k_dq2 and reads its K / V mostly from L2
   // (the stores then cost it little), else by a zero kernel ahead of the
   // key-block pass.
-  // head dim 64: k_dkdv2 takes the bias (dbias, if asked, comes from k_dqb);
+  // head dim 64: k_dkdv3 takes the bias (dbias, if asked, comes from k_dqb);
   // head dim 128: k_dkdv, walking the batch when dbias is asked
   const bool bloop = a.dbias != nullptr && p.Dqk != 64;
   const bool run_dq = p.Sq > 0 && p.B > 0, run_kv = p.Sk > 0 && p.B > 0;
