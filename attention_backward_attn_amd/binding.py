@@ -106,9 +106,18 @@ def _stream(stream) -> Optional[int]:
     return getattr(stream, "cuda_stream", stream)
 
 
+def _dense_strides(shape):
+    st = [1] * len(shape)
+    for i in range(len(shape) - 2, -1, -1):
+        st[i] = st[i + 1] * max(int(shape[i + 1]), 1)
+    return st
+
+
 def _strides3(t):
     if t is None:
         return (0, 0, 0)
+    if t.numel() == 0:   # no element is addressed: any strides (numpy gives zeros) read as dense
+        return tuple(_dense_strides(t.shape)[:3])
     if t.stride(-1) != 1:
         raise ValueError("the last dimension must be contiguous")
     return tuple(t.stride()[:3])
@@ -118,6 +127,9 @@ def _strides_packed(t):
     """{b, h, s} strides of a packed [T, H, D] tensor (the b stride is unused)."""
     if t is None:
         return (0, 0, 0)
+    if t.numel() == 0:
+        st = _dense_strides(t.shape)
+        return (0, st[1], st[0])
     if t.stride(-1) != 1:
         raise ValueError("the last dimension must be contiguous")
     return (0, t.stride(1), t.stride(0))

@@ -6,6 +6,7 @@ import glob
 import os
 import re
 
+import numpy as np
 import pytest
 
 from attention_backward_attn_amd import binding as B
@@ -308,3 +309,19 @@ def test_static_entry_point_rejects_oversized_problem():
     # validation comes first: a null dq is ATTN_EINVAL whatever the size
     bad = [FAKE] * 7 + [None, FAKE, FAKE, None, 0, None]
     assert L.attn_bwd_static(ctypes.byref(p), *bad) == B.ATTN_EINVAL
+
+
+def test_empty_tensor_strides_read_as_dense():
+    """Tensors with no elements (numpy gives them zero strides) are marshalled
+    with dense strides, so an empty batch passes validation: attn_bwd with
+    B = 0 returns ATTN_OK without touching the GPU."""
+    torch = pytest.importorskip("torch")
+    q = torch.from_numpy(np.zeros((0, 4, 70, 64), np.float32))
+    k = torch.from_numpy(np.zeros((0, 2, 50, 64), np.float32))
+    assert q.stride() == (0, 0, 0, 0)
+    p = B.make_problem(q, k, k.clone(), o=q, do=q, dq=q, dk=k, dv=k, scale=0.125, mask="top_left")
+    assert tuple(p.q_str) == (4 * 70 * 64, 70 * 64, 64) and tuple(p.k_str) == (2 * 50 * 64, 50 * 64, 64)
+    assert B.lib().attn_bwd(ctypes.byref(p), None, None, None, None, None, None, None, None, None, None,
+                            None, 0, None) == B.ATTN_OK
+    t = torch.from_numpy(np.zeros((0, 4, 64), np.float32))   # packed [T, H, D]
+    assert B._strides_packed(t) == (0, 64, 4 * 64)

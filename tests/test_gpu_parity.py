@@ -575,6 +575,44 @@ def test_no_query_rows_split_parts():
     assert (dk == 0).all() and (dv == 0).all()
 
 
+
+@pytest.mark.parametrize("dtype,D", [("f32", 64), ("bf16", 64), ("bf16", 128)])
+@pytest.mark.parametrize("with_sinks", [False, True], ids=["nosinks", "sinks"])
+def test_no_keys_and_empty_batch(dtype, D, with_sinks):
+    """No keys (Sk = 0): every row's O is 0 and its LSE is -inf, or the sink
+    logit when the head has one (the oracle's values); the backward gives
+    dQ = 0 (NaN-filled before), delta = 0 and dsinks = 0.  An empty batch
+    (B = 0) runs the forward and the backward without error."""
+    say(f"[no keys] {dtype} D={D} sinks={with_sinks}")
+    dt = tdtype(dtype)
+    x = random_case(2, 4, 2, 70, 0, D, D, dtype, 21, False, with_sinks)
+    spec = MaskSpec("top_left")
+    o64, lse64 = oracle.forward(x["q"], x["k"], x["v"], D ** -0.5, spec, None, x["sinks"])
+    q, k, v, do = (dev(x[n], dt) for n in ("q", "k", "v", "do"))
+    sinks = dev(x["sinks"], torch.float32)
+    o, lse = ab.forward(q, k, v, sinks=sinks, **mask_kw(spec))
+    torch.cuda.synchronize()
+    assert (o == 0).all()
+    lse_g, lse_r = lse.cpu().numpy(), lse64.astype(np.float32)
+    assert (np.isneginf(lse_g) == np.isneginf(lse_r)).all()
+    fin = ~np.isneginf(lse_r)
+    np.testing.assert_allclose(lse_g[fin], lse_r[fin], rtol=0, atol=1e-5)
+    dq = torch.full(q.shape, float("nan"), device="cuda")
+    got = ab.backward(q, k, v, o, do, lse, sinks=sinks, dq=dq, **mask_kw(spec))
+    torch.cuda.synchronize()
+    assert (got["dq"] == 0).all() and (got["delta"] == 0).all()
+    if with_sinks:
+        assert (got["dsinks"] == 0).all()
+    # empty batch
+    e = random_case(0, 4, 2, 70, 50, D, D, dtype, 22, False, with_sinks)
+    qe, ke, ve, doe = (dev(e[n], dt) for n in ("q", "k", "v", "do"))
+    oe, lsee = ab.forward(qe, ke, ve, sinks=sinks, **mask_kw(spec))
+    ge = ab.backward(qe, ke, ve, oe, doe, lsee, sinks=sinks, **mask_kw(spec))
+    torch.cuda.synchronize()
+    assert ge["dq"].numel() == 0 and ge["dk"].numel() == 0
+    if with_sinks:
+        assert (ge["dsinks"] == 0).all()
+
 def test_preprocess_zeroes_gradients():
     x = random_case(2, 4, 2, 130, 150, 64, 64, "bf16", 8, False, False)
     dt = torch.bfloat16
