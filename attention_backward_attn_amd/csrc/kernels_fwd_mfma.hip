@@ -435,6 +435,12 @@ __global__ __launch_bounds__(NTF, 2) void k_fwd2(Params p, FwdArgs a) {
     // tile t - 1 (buffer jp), then the softmax of tile t
     auto tile = [&](auto jc, bool full, int j0) {
       constexpr int j = decltype(jc)::value, jp = (j + NBF - 1) % NBF;
+      // Issue priority low over the products, raised over the softmax: the
+      // two waves sharing a SIMD come from different workgroups and run in
+      // any phase, and the one in its softmax then issues first while the
+      // other's products keep the matrix pipe busy (measured on GQA 32:8,
+      // S = 4096, D = 128, causal: 0.156 -> 0.154 ms).
+      __builtin_amdgcn_s_setprio(0);
       f32x16 sacc = zero16();
       {
         bf16x8 xk[NS], bv[NS];
@@ -449,6 +455,7 @@ __global__ __launch_bounds__(NTF, 2) void k_fwd2(Params p, FwdArgs a) {
           __builtin_amdgcn_sched_barrier(0);
         }
       }
+      __builtin_amdgcn_s_setprio(1);
       // softmax of tile t: masked logits to -inf, the tile maximum over the
       // row's two lanes, the running maximum raised (and O rescaled) only by
       // more than 8, then P = 2^(S scale log2(e) - m)
