@@ -113,6 +113,9 @@ SMALL = [
     # head dim 64; three tiles with a 2-row tail at head dim 128
     (1, 2, 2, 40, 96, 64, 64, "bf16", MaskSpec("bottom_right"), True, False),
     (2, 4, 1, 130, 70, 128, 128, "bf16", MaskSpec("top_left"), False, True),
+    # head dim 64 without a bias on a grid of 512 dQ workgroups (two per CU:
+    # the dQ pass with issue priorities)
+    (1, 32, 8, 2048, 2048, 64, 64, "bf16", MaskSpec("bottom_right"), False, False),
 ]
 
 
